@@ -1,0 +1,185 @@
+"""Python handle on the CPU oracle (libpa_oracle.so).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg.  The product package never imports it.
+
+``Oracle(path)`` wraps one build of the library (the shipped one, or a copy
+with a planted mistake).  Every call takes CPU tensors/arrays (bf16 tensors
+are passed as their raw 16-bit patterns) and returns float64 numpy arrays.
+``precision`` selects the _f64 (gate) or _f32 instantiation.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+import numpy as np
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+DEFAULT_LIB = os.path.join(HERE, "libpa_oracle.so")
+
+
+class _Pool(C.Structure):
+    _fields_ = [("num_pages", C.c_int32), ("page_size", C.c_int32),
+                ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32),
+                ("page_stride", C.c_int64), ("head_stride", C.c_int64),
+                ("token_stride", C.c_int64)]
+
+
+def _bits(t: torch.Tensor) -> np.ndarray:
+    """Raw bf16 bit patterns of a CPU tensor, as a uint16 array (no copy of
+    values through any arithmetic).  Non-contiguous views keep their strides
+    only through the pool descriptor, so the base storage is passed."""
+    assert t.dtype == torch.bfloat16
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def _i32(t) -> np.ndarray:
+    if isinstance(t, torch.Tensor):
+        t = t.detach().cpu().numpy()
+    return np.ascontiguousarray(t, dtype=np.int32)
+
+
+def _ptr(a: np.ndarray, ctype):
+    return a.ctypes.data_as(C.POINTER(ctype))
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+class Oracle:
+    def __init__(self, path: Optional[str] = None):
+        path = path or DEFAULT_LIB
+        if not os.path.exists(path):
+            raise OracleError(f"oracle library {path} is not built (run oracle/build.py)")
+        self.path = path
+        self.lib = C.CDLL(path)
+        u16p, i32p, f64p = C.POINTER(C.c_uint16), C.POINTER(C.c_int32), C.POINTER(C.c_double)
+        pool = C.POINTER(_Pool)
+        for sfx in ("_f64", "_f32"):
+            f = getattr(self.lib, "oracle_pa_decode" + sfx)
+            f.argtypes = [u16p, u16p, u16p, pool, i32p, C.c_int32, i32p, C.c_int32, C.c_int32,
+                          C.c_double, C.c_int32, f64p, f64p]
+            f.restype = C.c_int
+            f = getattr(self.lib, "oracle_pa_partials" + sfx)
+            f.argtypes = [u16p, u16p, u16p, pool, i32p, C.c_int32, i32p, C.c_int32, C.c_int32,
+                          C.c_double, C.c_int32, C.c_int32, C.c_int32, f64p, f64p, f64p]
+            f.restype = C.c_int
+            f = getattr(self.lib, "oracle_pa_merge" + sfx)
+            f.argtypes = [f64p, f64p, f64p, i32p, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                          C.c_int32, C.c_int32, f64p, f64p]
+            f.restype = C.c_int
+            f = getattr(self.lib, "oracle_mla_decode" + sfx)
+            f.argtypes = [u16p, u16p, u16p, pool, u16p, u16p, i32p, C.c_int32, i32p, C.c_int32,
+                          C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_double,
+                          f64p, f64p, f64p]
+            f.restype = C.c_int
+        self.lib.oracle_set_num_threads.argtypes = [C.c_int32]
+        self.lib.oracle_max_threads.restype = C.c_int32
+        self.lib.oracle_mutation.restype = C.c_int32
+
+    # ---- helpers ---------------------------------------------------------
+    def set_threads(self, n: int) -> None:
+        self.lib.oracle_set_num_threads(int(n))
+
+    def max_threads(self) -> int:
+        return int(self.lib.oracle_max_threads())
+
+    @property
+    def mutation(self) -> int:
+        return int(self.lib.oracle_mutation())
+
+    @staticmethod
+    def _pool_of(case) -> _Pool:
+        ps, hs, ts = case.strides()
+        return _Pool(case.num_pages, case.page_size, case.num_kv_heads, case.head_dim, ps, hs, ts)
+
+    def _check(self, rc: int, what: str) -> None:
+        if rc != 0:
+            raise OracleError(f"{what} returned {rc}")
+
+    # ---- GQA paged decode --------------------------------------------------
+    def decode(self, case, precision: str = "f64", window: Optional[int] = None):
+        """(out [B,Hq,D] float64, lse [B,Hq] float64) for a GqaCase."""
+        B, H, D = case.batch, case.num_q_heads, case.head_dim
+        q, k, v = _bits(case.q), _bits(case.k_pool), _bits(case.v_pool)
+        bt, ctx = _i32(case.block_table), _i32(case.context_lens)
+        out = np.zeros((B, H, D), np.float64)
+        lse = np.zeros((B, H), np.float64)
+        pool = self._pool_of(case)
+        w = case.window if window is None else window
+        u16, i32, f64 = C.c_uint16, C.c_int32, C.c_double
+        rc = getattr(self.lib, "oracle_pa_decode_" + precision)(
+            _ptr(q, u16), _ptr(k, u16), _ptr(v, u16), C.byref(pool), _ptr(bt, i32),
+            bt.shape[1], _ptr(ctx, i32), B, H, float(case.scale), int(w),
+            _ptr(out, f64), _ptr(lse, f64))
+        self._check(rc, "oracle_pa_decode")
+        return out, lse
+
+    def partials(self, case, partition_size: int, max_parts: int, precision: str = "f64"):
+        """(part_out [B,Hq,max_parts,D], part_max, part_sum [B,Hq,max_parts])."""
+        B, H, D = case.batch, case.num_q_heads, case.head_dim
+        q, k, v = _bits(case.q), _bits(case.k_pool), _bits(case.v_pool)
+        bt, ctx = _i32(case.block_table), _i32(case.context_lens)
+        po = np.zeros((B, H, max_parts, D), np.float64)
+        pm = np.zeros((B, H, max_parts), np.float64)
+        pl = np.zeros((B, H, max_parts), np.float64)
+        pool = self._pool_of(case)
+        u16, i32, f64 = C.c_uint16, C.c_int32, C.c_double
+        rc = getattr(self.lib, "oracle_pa_partials_" + precision)(
+            _ptr(q, u16), _ptr(k, u16), _ptr(v, u16), C.byref(pool), _ptr(bt, i32),
+            bt.shape[1], _ptr(ctx, i32), B, H, float(case.scale), int(case.window),
+            int(partition_size), int(max_parts), _ptr(po, f64), _ptr(pm, f64), _ptr(pl, f64))
+        self._check(rc, "oracle_pa_partials")
+        return po, pm, pl
+
+    def merge(self, part_out, part_max, part_sum, context_lens, partition_size: int,
+              window: int, precision: str = "f64"):
+        po = np.ascontiguousarray(part_out, np.float64)
+        pm = np.ascontiguousarray(part_max, np.float64)
+        pl = np.ascontiguousarray(part_sum, np.float64)
+        B, H, P, D = po.shape
+        ctx = _i32(context_lens)
+        out = np.zeros((B, H, D), np.float64)
+        lse = np.zeros((B, H), np.float64)
+        i32, f64 = C.c_int32, C.c_double
+        rc = getattr(self.lib, "oracle_pa_merge_" + precision)(
+            _ptr(po, f64), _ptr(pm, f64), _ptr(pl, f64), _ptr(ctx, i32), B, H, D,
+            int(partition_size), P, int(window), _ptr(out, f64), _ptr(lse, f64))
+        self._check(rc, "oracle_pa_merge")
+        return out, lse
+
+    # ---- absorbed MLA --------------------------------------------------------
+    def mla(self, case, precision: str = "f64", want_q_abs: bool = False):
+        """(out [B,H,d_v], lse [B,H], q_abs [B,H,d_lat] or None) for an MlaCase."""
+        B, H = case.batch, case.num_heads
+        qn, qr, cache = _bits(case.q_nope), _bits(case.q_rope), _bits(case.cache)
+        wuk, wuv = _bits(case.w_uk), _bits(case.w_uv)
+        bt, ctx = _i32(case.block_table), _i32(case.context_lens)
+        row = case.d_lat + case.d_rope
+        s = case.cache.stride()
+        pool = _Pool(case.num_pages, case.page_size, 1, row, s[0], 0, s[1])
+        out = np.zeros((B, H, case.d_v), np.float64)
+        lse = np.zeros((B, H), np.float64)
+        qa = np.zeros((B, H, case.d_lat), np.float64) if want_q_abs else None
+        u16, i32, f64 = C.c_uint16, C.c_int32, C.c_double
+        rc = getattr(self.lib, "oracle_mla_decode_" + precision)(
+            _ptr(qn, u16), _ptr(qr, u16), _ptr(cache, u16), C.byref(pool), _ptr(wuk, u16),
+            _ptr(wuv, u16), _ptr(bt, i32), bt.shape[1], _ptr(ctx, i32), B, H, case.d_nope,
+            case.d_rope, case.d_lat, case.d_v, float(case.scale), _ptr(out, f64),
+            _ptr(qa, f64) if qa is not None else None, _ptr(lse, f64))
+        self._check(rc, "oracle_mla_decode")
+        return out, lse, qa
+
+
+_DEFAULT: Optional[Oracle] = None
+
+
+def default() -> Oracle:
+    global _DEFAULT
+    if _DEFAULT is None:
+        _DEFAULT = Oracle()
+    return _DEFAULT

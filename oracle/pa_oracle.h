@@ -1,0 +1,124 @@
+/*
+ * pa_oracle.h -- the CPU oracle for decode-time paged attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, includes or
+ * calls this code; only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg load it.  It shares no source with the GPU path.
+ *
+ * Every routine exists twice, with suffix _f64 (all arithmetic in double) and
+ * _f32 (all arithmetic in float).  _f64 is the parity gate; _f32 is the plain
+ * fp32 formulation and is checked against _f64.  Inputs are raw bf16 bit
+ * patterns (uint16_t); outputs are double arrays holding the value the
+ * routine computed (an f32 result is widened exactly).
+ *
+ * Definitions followed (sources are cited by page title and section):
+ *  - Paged gather: token t of a sequence lives in page block_table[t / ps],
+ *    slot t % ps; a block table and per-request lengths are device metadata
+ *    read in place [vllm.cpp kernel matrix, row KERNEL-ATTN-DFLASH-PAGED-BLOCK].
+ *  - Softmax attention of one query over the gathered keys, computed two-pass
+ *    (max, then sums) in ascending token order; the online (streamed) softmax
+ *    that the decode kernels use reaches the same value up to rounding order
+ *    [vllm.cpp PR #425, commit message: the warp-strided online softmax and
+ *    the per-tile loop differ only in reduction order].
+ *  - GQA: q head h reads KV head h / (Hq / Hkv) [vllm.cpp PR #49, commit body:
+ *    the q heads of one KV group form one work item].
+ *  - Split-KV partials (max, sum, normalised partial out) and their merge with
+ *    both -inf edge cases, ascending split order, no atomics [vllm.cpp kernel
+ *    matrix, row KERNEL-ATTN-MLA-SPARSE, W4/W5].
+ *  - Absorbed MLA: q_abs = q_nope . W_UK[h] (W_UK indexed [d][j]); score over
+ *    the 576-wide latent row (512 latent ++ 64 rope); V is the latent itself;
+ *    out = W_UV[h] . o_lat (W_UV indexed [dv][j]) [pegainfer PR #938, review
+ *    quote of the kernel's "Schedule" comment, steps 1-7; vllm.cpp kernel
+ *    matrix, row KERNEL-ATTN-MLA-SPARSE, W6 absorption and W4 "v is the
+ *    transposed k"].
+ *
+ * Return codes: 0 on success, ORACLE_ERR_ARGS for bad sizes or pointers,
+ * ORACLE_ERR_PAGE when a block-table entry needed for a live token lies
+ * outside [0, num_pages).
+ */
+#ifndef PA_ORACLE_H
+#define PA_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ORACLE_OK 0
+#define ORACLE_ERR_ARGS (-1)
+#define ORACLE_ERR_PAGE (-2)
+
+/* Geometry of one KV page pool (all strides in elements). */
+typedef struct oracle_pool {
+  int32_t num_pages;
+  int32_t page_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int64_t page_stride;
+  int64_t head_stride;
+  int64_t token_stride;
+} oracle_pool;
+
+/* Full decode: out[b,h,:] (unrounded), lse[b,h] (natural log).  window <= 0
+ * means no window; otherwise only keys t >= ctx - window are attended. */
+#define ORACLE_DECL_DECODE(SFX)                                                 \
+  int oracle_pa_decode##SFX(                                                   \
+      const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,       \
+      const oracle_pool* pool, const int32_t* block_table, int32_t bt_stride,  \
+      const int32_t* context_lens, int32_t batch, int32_t num_q_heads,         \
+      double scale, int32_t window, double* out, double* lse);
+
+/* Split-KV partials: partition j of sequence b covers
+ * [lo + j*P, min(lo + (j+1)*P, ctx)); empty -> max=-inf, sum=0, out=0.
+ * part_out [B,Hq,max_parts,D], part_max/part_sum [B,Hq,max_parts]. */
+#define ORACLE_DECL_PARTIALS(SFX)                                               \
+  int oracle_pa_partials##SFX(                                                 \
+      const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,       \
+      const oracle_pool* pool, const int32_t* block_table, int32_t bt_stride,  \
+      const int32_t* context_lens, int32_t batch, int32_t num_q_heads,         \
+      double scale, int32_t window, int32_t partition_size,                    \
+      int32_t max_parts, double* part_out, double* part_max,                   \
+      double* part_sum);
+
+/* LSE merge of partials (inputs as double, read at the routine's precision). */
+#define ORACLE_DECL_MERGE(SFX)                                                  \
+  int oracle_pa_merge##SFX(                                                    \
+      const double* part_out, const double* part_max, const double* part_sum,  \
+      const int32_t* context_lens, int32_t batch, int32_t num_q_heads,         \
+      int32_t head_dim, int32_t partition_size, int32_t max_parts,             \
+      int32_t window, double* out, double* lse);
+
+/* Absorbed MLA decode over a single-head latent cache whose rows hold
+ * d_lat latent values followed by d_rope rope values.
+ * q_nope [B,H,d_nope], q_rope [B,H,d_rope], w_uk [H,d_nope,d_lat],
+ * w_uv [H,d_v,d_lat]; out [B,H,d_v]; q_abs_out [B,H,d_lat] may be NULL;
+ * lse [B,H] may be NULL. */
+#define ORACLE_DECL_MLA(SFX)                                                    \
+  int oracle_mla_decode##SFX(                                                  \
+      const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* cache,   \
+      const oracle_pool* pool, const uint16_t* w_uk, const uint16_t* w_uv,     \
+      const int32_t* block_table, int32_t bt_stride,                           \
+      const int32_t* context_lens, int32_t batch, int32_t num_heads,           \
+      int32_t d_nope, int32_t d_rope, int32_t d_lat, int32_t d_v,              \
+      double scale, double* out, double* q_abs_out, double* lse);
+
+ORACLE_DECL_DECODE(_f64)
+ORACLE_DECL_DECODE(_f32)
+ORACLE_DECL_PARTIALS(_f64)
+ORACLE_DECL_PARTIALS(_f32)
+ORACLE_DECL_MERGE(_f64)
+ORACLE_DECL_MERGE(_f32)
+ORACLE_DECL_MLA(_f64)
+ORACLE_DECL_MLA(_f32)
+
+/* Thread control for the (b, h) loop; results do not depend on it. */
+void oracle_set_num_threads(int32_t n);
+int32_t oracle_max_threads(void);
+/* Which planted mistake (0 = none) this build carries; see pa_oracle.c. */
+int32_t oracle_mutation(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PA_ORACLE_H */

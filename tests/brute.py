@@ -1,0 +1,89 @@
+"""Independent float64 brute force used to pin the oracle.
+
+Written separately from the oracle (numpy fancy indexing instead of pointer
+and stride arithmetic, BLAS products instead of ascending loops), so a
+mistake in the oracle's gather, head map, window or softmax shows up as a
+disagreement here.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+
+def pool_f64(pool: torch.Tensor) -> np.ndarray:
+    return pool.detach().cpu().to(torch.float64).numpy()
+
+
+def gather_rows(pool: np.ndarray, layout: str, bt_row: np.ndarray, t: np.ndarray,
+                page_size: int, g: int) -> np.ndarray:
+    """Rows of KV head g for logical tokens t: [len(t), D]."""
+    pages = bt_row[t // page_size]
+    slots = t % page_size
+    if layout == "PHSD":
+        return pool[pages, g, slots, :]
+    return pool[pages, slots, g, :]
+
+
+def key_range(n: int, window: int) -> tuple[int, int]:
+    return (max(0, n - window) if window > 0 else 0), n
+
+
+def dense_attention(case, window=None):
+    """(out [B,Hq,D], lse [B,Hq]) in float64 over materialised K/V."""
+    w = case.window if window is None else window
+    K = pool_f64(case.k_pool)
+    V = pool_f64(case.v_pool)
+    q = case.q.to(torch.float64).numpy()
+    bt = case.block_table.numpy()
+    ctx = case.context_lens.numpy()
+    B, H, D = q.shape
+    G = H // case.num_kv_heads
+    out = np.zeros((B, H, D))
+    lse = np.full((B, H), -np.inf)
+    for b in range(B):
+        lo, n = key_range(int(ctx[b]), w)
+        if n <= lo:
+            continue
+        t = np.arange(lo, n)
+        for g in range(case.num_kv_heads):
+            Kb = gather_rows(K, case.layout, bt[b], t, case.page_size, g)
+            Vb = gather_rows(V, case.layout, bt[b], t, case.page_size, g)
+            for h in range(g * G, (g + 1) * G):
+                s = case.scale * (Kb @ q[b, h])
+                mx = s.max()
+                e = np.exp(s - mx)
+                out[b, h] = (e @ Vb) / e.sum()
+                lse[b, h] = mx + np.log(e.sum())
+    return out, lse
+
+
+def mla_unabsorbed(case):
+    """MLA evaluated without absorption: per head, materialise
+    k_t = [W_UK[h] c_t[:d_lat] ; c_t[d_lat:]] and v_t = W_UV[h] c_t[:d_lat],
+    then plain softmax attention of q = [q_nope ; q_rope]."""
+    C = case.cache.detach().cpu().to(torch.float64).numpy()
+    qn = case.q_nope.to(torch.float64).numpy()
+    qr = case.q_rope.to(torch.float64).numpy()
+    Wuk = case.w_uk.to(torch.float64).numpy()   # [H, d_nope, d_lat]
+    Wuv = case.w_uv.to(torch.float64).numpy()   # [H, d_v, d_lat]
+    bt = case.block_table.numpy()
+    ctx = case.context_lens.numpy()
+    B, H = qn.shape[:2]
+    out = np.zeros((B, H, case.d_v))
+    for b in range(B):
+        n = int(ctx[b])
+        if n == 0:
+            continue
+        t = np.arange(n)
+        rows = C[bt[b][t // case.page_size], t % case.page_size, :]    # [n, 576]
+        lat, rope = rows[:, :case.d_lat], rows[:, case.d_lat:]
+        for h in range(H):
+            k_nope = lat @ Wuk[h].T          # [n, d_nope]
+            v = lat @ Wuv[h].T               # [n, d_v]
+            k = np.concatenate([k_nope, rope], axis=1)
+            q = np.concatenate([qn[b, h], qr[b, h]])
+            s = case.scale * (k @ q)
+            e = np.exp(s - s.max())
+            out[b, h] = (e @ v) / e.sum()
+    return out

@@ -1,0 +1,37 @@
+"""RED-first: every planted mistake in the oracle must fail at least one pin.
+
+The mistakes are compiled into copies of the oracle (ORACLE_MUTATION=k) on
+the CPU; the shipped build carries none.  This is the pages' practice of
+perturbing the code under test and showing the gate turns red [vllm.cpp
+kernel matrix: RED-first mutation proofs in several rows].
+"""
+import os
+
+import pytest
+
+import oracle_pins
+from oracle import build as obuild
+from oracle.oracle import Oracle
+
+MUTATIONS = {
+    1: "window one key short",
+    2: "interleaved GQA head map",
+    3: "slot mirrored inside a page",
+    4: "W_UK read as [j][d]",
+    5: "lse without the max",
+    6: "merge weight without l_j",
+    7: "softmax scale dropped",
+    8: "MLA value row shifted",
+    9: "MLA rope term dropped",
+    10: "split partitions counted from key 0",
+}
+
+
+@pytest.mark.parametrize("k", sorted(MUTATIONS))
+def test_mutation_is_caught(tmp_path, k):
+    lib = obuild.build(mutation=k, out=os.path.join(tmp_path, f"libpa_oracle_m{k}.so"))
+    o = Oracle(lib)
+    assert o.mutation == k
+    res = oracle_pins.run_all(o)
+    failed = [n for n, r in res.items() if r is not None]
+    assert failed, f"mutation {k} ({MUTATIONS[k]}) passed every pin"
