@@ -1,0 +1,215 @@
+/*
+ * pa_decode.h -- C ABI of the MI355X (gfx950) decode-time paged-attention
+ * library (libpa_decode.so).
+ *
+ * One new query token per sequence attends over that sequence's KV cache,
+ * which lives in fixed-size pages of a shared pool and is found through a
+ * per-sequence block table: logical token t sits in page block_table[b][t /
+ * page_size] at slot t % page_size.  The block table and the context lengths
+ * are device arrays read in place, so every entry point is safe to record in
+ * a HIP graph [vllm.cpp kernel matrix, row KERNEL-ATTN-DFLASH-PAGED-BLOCK:
+ * paged K/V with per-request lengths and block table as persistent device
+ * tensors, static grid].
+ *
+ * Conventions for every entry point:
+ *  - Pointers named as tensors are DEVICE pointers owned by the caller; the
+ *    library never allocates, frees, copies between host and device, or
+ *    synchronises.  Work is enqueued on `stream` (a hipStream_t; NULL = the
+ *    default stream) and the call returns before it finishes.
+ *  - bf16 is IEEE-754 binary32 truncated to its upper 16 bits; every bf16
+ *    output is rounded to nearest, ties to even.
+ *  - Arguments are validated on the host before anything is enqueued; on a
+ *    non-zero status nothing was launched and pa_last_error() describes why.
+ *  - Device-side contract, not checked: 0 <= context_lens[b] <=
+ *    max_pages_per_seq * page_size, and block_table[b][i] lies in
+ *    [0, num_pages) for every page i that holds a live key.  Block-table
+ *    entries past a sequence's last live page are never read.
+ *  - Results are bitwise reproducible run to run and independent of which
+ *    physical pages hold the keys: every reduction runs in a fixed order
+ *    over logical token positions and there are no floating-point atomics.
+ */
+#ifndef PA_DECODE_H
+#define PA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Only the entry points below are exported from the shared library. */
+#ifndef PA_API
+#define PA_API __attribute__((visibility("default")))
+#endif
+
+/* Status codes. */
+#define PA_OK 0
+#define PA_ERR_NULL (-1)        /* a required pointer is NULL */
+#define PA_ERR_SHAPE (-2)       /* sizes inconsistent or out of range */
+#define PA_ERR_UNSUPPORTED (-3) /* head_dim / group / page size not built */
+#define PA_ERR_ALIGN (-4)       /* stride not a multiple of 8 elements or pointer not 16-byte aligned */
+#define PA_ERR_WORKSPACE (-5)   /* workspace missing or too small */
+#define PA_ERR_LAUNCH (-6)      /* the HIP runtime refused a launch */
+
+/* Geometry of a K or V page pool of bf16 elements.  Strides are in ELEMENTS;
+ * the innermost (head_dim) axis is contiguous.  The layout [page][kv head]
+ * [slot][dim] (head_stride = page_size*head_dim, token_stride = head_dim)
+ * makes each (page, KV head) tile one contiguous block and is the layout this
+ * library is tuned for; the layout [page][slot][kv head][dim] works through
+ * the same code.  All three strides must be multiples of 8 and the pool
+ * 16-byte aligned.  For the MLA latent cache num_kv_heads = 1, head_dim = 576
+ * and head_stride is ignored. */
+typedef struct pa_kv_layout {
+  int32_t num_pages;
+  int32_t page_size;    /* 16, 32 or 64 */
+  int32_t num_kv_heads;
+  int32_t head_dim;     /* 128 or 256 (576 for the MLA cache) */
+  int64_t page_stride;
+  int64_t head_stride;
+  int64_t token_stride;
+} pa_kv_layout;
+
+/* ---------------------------------------------------------------------------
+ * pa_decode_splitkv -- stage 1 of split-KV decode.
+ *
+ * Softmax attention of q head h of sequence b over keys of KV head
+ * g = h / (num_q_heads / num_kv_heads) (contiguous groups; each KV page tile
+ * is read once per KV head and serves all of its q heads) [vllm.cpp PR #49,
+ * commit body: the decode grid over batch x KV heads with the q heads of a
+ * group processed together].  Scores s_t = scale * q . k_t in fp32.
+ * With window > 0 only keys t >= ctx - window are attended (the newest
+ * `window` keys); window <= 0 attends every key [vllm.cpp PR #425,
+ * LIMITATIONS: windowed instantiation].
+ *
+ * The attended range [lo, ctx) is cut into partitions of partition_size
+ * keys counted from lo: partition j = [lo + j*P, min(lo + (j+1)*P, ctx)).
+ * For every b, h and j < max_partitions it writes, in fp32,
+ *   part_max[b][h][j] = m_j = max_t s_t          (natural-log domain)
+ *   part_sum[b][h][j] = l_j = sum_t exp(s_t - m_j)
+ *   part_out[b][h][j][:] = sum_t exp(s_t - m_j) v_t / l_j
+ * and for an empty partition m_j = -inf, l_j = 0, part_out = 0
+ * [vllm.cpp kernel matrix, row KERNEL-ATTN-MLA-SPARSE, W4: per-split partial
+ * results and a second merge stage; row KERNEL-ATTN-FA2: split-KV decode].
+ *
+ * q            [batch][num_q_heads][head_dim] bf16, contiguous
+ * k_pool/v_pool  pools described by *kv (host pointer to the descriptor)
+ * block_table  [batch][block_table_stride] int32, device
+ * context_lens [batch] int32, device
+ * part_out     [batch][num_q_heads][max_partitions][head_dim] fp32
+ * part_max, part_sum [batch][num_q_heads][max_partitions] fp32
+ * Requires partition_size >= 1 and max_partitions * partition_size >= the
+ * largest possible attended range (min(window, max_pages_per_seq *
+ * page_size) with a window, else max_pages_per_seq * page_size); supported
+ * head_dim 128 with 1/2/4/8/16 q heads per KV head, head_dim 256 with
+ * 1/2/4/8; page_size 16/32/64.
+ * ------------------------------------------------------------------------- */
+PA_API int pa_decode_splitkv(const void* q, const void* k_pool, const void* v_pool,
+                      const pa_kv_layout* kv, const int32_t* block_table,
+                      int32_t block_table_stride, const int32_t* context_lens,
+                      int32_t batch, int32_t num_q_heads,
+                      int32_t max_pages_per_seq, float scale, int32_t window,
+                      int32_t partition_size, int32_t max_partitions,
+                      float* part_out, float* part_max, float* part_sum,
+                      void* stream);
+
+/* ---------------------------------------------------------------------------
+ * pa_merge_lse -- stage 2: log-sum-exp merge of split partials.
+ *
+ * For each (b, h), over the live partitions j < ceil((ctx - lo) / P) in
+ * ascending j:  M = max_j m_j,  w_j = l_j exp(m_j - M),  W = sum_j w_j,
+ *   out[b][h][:] = bf16( sum_j (w_j / W) part_out[j][:] ),
+ *   lse_out[b][h] = M + ln W.
+ * Empty partitions (m_j = -inf) weigh nothing; no live partition, or all
+ * empty, gives out = 0 and lse = -inf [vllm.cpp kernel matrix, row
+ * KERNEL-ATTN-MLA-SPARSE, W5: merge of attention states with both -inf edge
+ * cases; W4: fixed ascending split order, no atomics].
+ *
+ * Arguments as written by pa_decode_splitkv with the same partition_size,
+ * max_partitions and window; max_partitions must cover every sequence's live
+ * partitions (not checked: the context lengths live on the device).  out [batch][num_q_heads][head_dim] bf16;
+ * lse_out [batch][num_q_heads] fp32 or NULL.  head_dim 128 or 256.
+ * ------------------------------------------------------------------------- */
+PA_API int pa_merge_lse(const float* part_out, const float* part_max,
+                 const float* part_sum, const int32_t* context_lens,
+                 int32_t batch, int32_t num_q_heads, int32_t head_dim,
+                 int32_t partition_size, int32_t max_partitions,
+                 int32_t window, void* out, float* lse_out, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * pa_decode -- complete decode attention: pa_decode_splitkv followed by
+ * pa_merge_lse, with the partition size chosen from host-known shapes only
+ * (batch, heads, head_dim, max_pages_per_seq, page_size, window), so the
+ * result never depends on the device-side context lengths' values.
+ *
+ * out [batch][num_q_heads][head_dim] bf16; lse_out [batch][num_q_heads] fp32
+ * or NULL.  workspace: device memory of at least
+ * pa_decode_workspace_size(...) bytes, 256-byte aligned, owned by the caller
+ * and clobbered by the call (no state is kept between calls).
+ * ------------------------------------------------------------------------- */
+PA_API int pa_decode(const void* q, const void* k_pool, const void* v_pool,
+              const pa_kv_layout* kv, const int32_t* block_table,
+              int32_t block_table_stride, const int32_t* context_lens,
+              int32_t batch, int32_t num_q_heads, int32_t max_pages_per_seq,
+              float scale, int32_t window, void* out, float* lse_out,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace pa_decode needs for these shapes (0 on invalid shapes). */
+PA_API size_t pa_decode_workspace_size(int32_t batch, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t head_dim,
+                                int32_t max_pages_per_seq, int32_t page_size,
+                                int32_t window);
+
+/* Partition size pa_decode uses for these shapes (0 on invalid shapes). */
+PA_API int32_t pa_decode_partition_size(int32_t batch, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t max_pages_per_seq, int32_t page_size,
+                                 int32_t window);
+
+/* ---------------------------------------------------------------------------
+ * mla_absorbed_decode -- absorbed multi-head latent attention decode.
+ *
+ * The cache holds one 576-wide bf16 row per token: 512 latent values c[0:512]
+ * followed by 64 rope values c[512:576], shared by all heads.  For sequence b
+ * and head h [pegainfer PR #938, review quote of the kernel's "Schedule"
+ * comment, steps 1-7; vllm.cpp kernel matrix, row KERNEL-ATTN-MLA-SPARSE:
+ * absorption as a load-time weight transform plus two batched products, and
+ * V equal to the latent part of the cache]:
+ *   q_abs[j]  = sum_d q_nope[b][h][d] * w_uk[h][d][j]          (d < 128, j < 512)
+ *   s_t       = scale * (q_abs . c_t[0:512] + q_rope[b][h] . c_t[512:576])
+ *   o_lat[j]  = sum_t softmax(s)_t * c_t[j]
+ *   out[b][h][dv] = bf16( sum_j w_uv[h][dv][j] * o_lat[j] )    (dv < 128)
+ * with every intermediate kept at (near-)fp32 precision.
+ *
+ * q_nope [batch][num_heads][128] bf16; q_rope [batch][num_heads][64] bf16;
+ * kv_cache: pool described by *cache (num_kv_heads 1, head_dim 576,
+ * page_size 16/32/64, token_stride >= 576 and a multiple of 8);
+ * w_uk, w_uv [num_heads][128][512] bf16; out [batch][num_heads][128] bf16.
+ * num_heads must be a multiple of 16.  partition_size: keys per split
+ * (multiple of 64, or 0 to let the library choose from host-known shapes).
+ * workspace: at least mla_absorbed_decode_workspace_size(...) bytes,
+ * 256-byte aligned, clobbered by the call.
+ * ------------------------------------------------------------------------- */
+PA_API int mla_absorbed_decode(const void* q_nope, const void* q_rope,
+                        const void* kv_cache, const pa_kv_layout* cache,
+                        const void* w_uk, const void* w_uv,
+                        const int32_t* block_table, int32_t block_table_stride,
+                        const int32_t* context_lens, int32_t batch,
+                        int32_t num_heads, int32_t max_pages_per_seq,
+                        float scale, int32_t partition_size, void* out,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace mla_absorbed_decode needs (0 on invalid shapes). */
+PA_API size_t mla_absorbed_decode_workspace_size(int32_t batch, int32_t num_heads,
+                                          int32_t max_pages_per_seq,
+                                          int32_t page_size,
+                                          int32_t partition_size);
+
+/* Text describing the last non-zero status returned on the calling thread
+ * ("" if none).  The pointer stays valid until the next call on that thread. */
+PA_API const char* pa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PA_DECODE_H */

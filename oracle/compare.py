@@ -129,7 +129,8 @@ def close_f32(gpu: np.ndarray, ref: np.ndarray, rtol: float = 1e-5, atol: float 
     inf = np.isinf(r) | np.isinf(g)
     same_inf = np.where(inf, g == r, True)
     fin = ~inf
-    err = np.abs(g - r)
+    with np.errstate(invalid="ignore"):
+        err = np.abs(g - r)
     bound = atol + rtol * np.abs(r)
     ok = bool(same_inf.all() and (err[fin] <= bound[fin]).all() and not np.isnan(g).any())
     return ok, float(err[fin].max()) if fin.any() else 0.0

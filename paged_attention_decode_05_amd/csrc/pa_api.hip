@@ -1,0 +1,184 @@
+// pa_api.hip -- extern "C" entry points of libpa_decode.so.  Each one checks
+// its arguments on the host (pa_validate.cpp), fills a parameter block and
+// enqueues kernels on the caller's stream.  Nothing here allocates, copies or
+// synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <string>
+
+#include "pa_decode.h"
+#include "pa_validate.h"
+
+#include "pa_params.h"
+
+namespace pa {
+
+hipError_t launch_split(const SplitParams& p, int head_dim, int group, int batch,
+                        int num_kv_heads, hipStream_t stream);
+hipError_t launch_merge(const MergeParams& p, int head_dim, int batch, hipStream_t stream);
+
+}  // namespace pa
+
+namespace {
+
+int launch_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return PA_OK;
+  return pa::fail(PA_ERR_LAUNCH, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+int ilog2(int v) {
+  int s = 0;
+  while ((1 << s) < v) ++s;
+  return s;
+}
+
+pa::SplitParams split_params(const void* q, const void* k_pool, const void* v_pool,
+                             const pa_kv_layout* kv, const int32_t* block_table,
+                             int32_t block_table_stride, const int32_t* context_lens,
+                             int32_t num_q_heads, float scale, int32_t window,
+                             int32_t partition_size, int32_t max_partitions, float* part_out,
+                             float* part_max, float* part_sum, int32_t write_empty) {
+  pa::SplitParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k_pool);
+  p.v = static_cast<const uint16_t*>(v_pool);
+  p.block_table = block_table;
+  p.context_lens = context_lens;
+  p.part_out = part_out;
+  p.part_max = part_max;
+  p.part_sum = part_sum;
+  p.page_stride = kv->page_stride;
+  p.head_stride = kv->head_stride;
+  p.token_stride = static_cast<int32_t>(kv->token_stride);
+  p.bt_stride = block_table_stride;
+  p.num_q_heads = num_q_heads;
+  p.page_size = kv->page_size;
+  p.page_shift = ilog2(kv->page_size);
+  p.window = window;
+  p.partition_size = partition_size;
+  p.max_parts = max_partitions;
+  p.write_empty = write_empty;
+  p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_decode_splitkv(const void* q, const void* k_pool, const void* v_pool,
+                      const pa_kv_layout* kv, const int32_t* block_table,
+                      int32_t block_table_stride, const int32_t* context_lens, int32_t batch,
+                      int32_t num_q_heads, int32_t max_pages_per_seq, float scale,
+                      int32_t window, int32_t partition_size, int32_t max_partitions,
+                      float* part_out, float* part_max, float* part_sum, void* stream) {
+  int rc = pa::check_gqa(q, k_pool, v_pool, kv, block_table, block_table_stride, context_lens,
+                         batch, num_q_heads, max_pages_per_seq, scale);
+  if (rc) return rc;
+  rc = pa::check_split(partition_size, max_partitions, max_pages_per_seq, kv->page_size, window,
+                       part_out, part_max, part_sum);
+  if (rc) return rc;
+  const pa::SplitParams p = split_params(q, k_pool, v_pool, kv, block_table, block_table_stride,
+                                         context_lens, num_q_heads, scale, window, partition_size,
+                                         max_partitions, part_out, part_max, part_sum, 1);
+  pa::clear_error();
+  return launch_status(pa::launch_split(p, kv->head_dim, num_q_heads / kv->num_kv_heads, batch,
+                                        kv->num_kv_heads, static_cast<hipStream_t>(stream)),
+                       "split kernel");
+}
+
+int pa_merge_lse(const float* part_out, const float* part_max, const float* part_sum,
+                 const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                 int32_t head_dim, int32_t partition_size, int32_t max_partitions,
+                 int32_t window, void* out, float* lse_out, void* stream) {
+  int rc = pa::check_merge(part_out, part_max, part_sum, context_lens, batch, num_q_heads,
+                           head_dim, partition_size, max_partitions, out);
+  if (rc) return rc;
+  pa::MergeParams p{};
+  p.part_out = part_out;
+  p.part_max = part_max;
+  p.part_sum = part_sum;
+  p.context_lens = context_lens;
+  p.out = static_cast<uint16_t*>(out);
+  p.lse = lse_out;
+  p.num_q_heads = num_q_heads;
+  p.partition_size = partition_size;
+  p.max_parts = max_partitions;
+  p.window = window;
+  pa::clear_error();
+  return launch_status(pa::launch_merge(p, head_dim, batch, static_cast<hipStream_t>(stream)),
+                       "merge kernel");
+}
+
+size_t pa_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t max_pages_per_seq, int32_t page_size,
+                                int32_t window) {
+  pa::DecodePlan plan;
+  if (!pa::plan_decode(batch, num_q_heads, num_kv_heads, head_dim, max_pages_per_seq, page_size,
+                       window, &plan))
+    return 0;
+  return plan.bytes;
+}
+
+int32_t pa_decode_partition_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_pages_per_seq, int32_t page_size,
+                                 int32_t window) {
+  pa::DecodePlan plan;
+  if (!pa::plan_decode(batch, num_q_heads, num_kv_heads, head_dim, max_pages_per_seq, page_size,
+                       window, &plan))
+    return 0;
+  return plan.partition_size;
+}
+
+int pa_decode(const void* q, const void* k_pool, const void* v_pool, const pa_kv_layout* kv,
+              const int32_t* block_table, int32_t block_table_stride,
+              const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+              int32_t max_pages_per_seq, float scale, int32_t window, void* out,
+              float* lse_out, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = pa::check_gqa(q, k_pool, v_pool, kv, block_table, block_table_stride, context_lens,
+                         batch, num_q_heads, max_pages_per_seq, scale);
+  if (rc) return rc;
+  if (!out) return pa::fail(PA_ERR_NULL, "out must not be NULL");
+  if (reinterpret_cast<uintptr_t>(out) & 15u)
+    return pa::fail(PA_ERR_ALIGN, "out must be 16-byte aligned");
+  pa::DecodePlan plan;
+  if (!pa::plan_decode(batch, num_q_heads, kv->num_kv_heads, kv->head_dim, max_pages_per_seq,
+                       kv->page_size, window, &plan))
+    return pa::fail(PA_ERR_SHAPE, "no launch plan for these shapes");
+  if (!workspace || workspace_bytes < plan.bytes)
+    return pa::fail(PA_ERR_WORKSPACE, "workspace must hold pa_decode_workspace_size() = " +
+                                          std::to_string(plan.bytes) + " bytes");
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return pa::fail(PA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  float* part_out = reinterpret_cast<float*>(ws + plan.off_out);
+  float* part_max = reinterpret_cast<float*>(ws + plan.off_max);
+  float* part_sum = reinterpret_cast<float*>(ws + plan.off_sum);
+  const pa::SplitParams sp = split_params(q, k_pool, v_pool, kv, block_table, block_table_stride,
+                                          context_lens, num_q_heads, scale, window,
+                                          plan.partition_size, plan.max_partitions, part_out,
+                                          part_max, part_sum, 0);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  pa::clear_error();
+  rc = launch_status(pa::launch_split(sp, kv->head_dim, num_q_heads / kv->num_kv_heads, batch,
+                                      kv->num_kv_heads, s),
+                     "split kernel");
+  if (rc) return rc;
+  pa::MergeParams mp{};
+  mp.part_out = part_out;
+  mp.part_max = part_max;
+  mp.part_sum = part_sum;
+  mp.context_lens = context_lens;
+  mp.out = static_cast<uint16_t*>(out);
+  mp.lse = lse_out;
+  mp.num_q_heads = num_q_heads;
+  mp.partition_size = plan.partition_size;
+  mp.max_parts = plan.max_partitions;
+  mp.window = window;
+  return launch_status(pa::launch_merge(mp, kv->head_dim, batch, s), "merge kernel");
+}
+
+const char* pa_last_error(void) { return pa::last_error(); }
+
+}  // extern "C"

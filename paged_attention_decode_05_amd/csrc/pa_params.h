@@ -1,0 +1,45 @@
+// pa_params.h -- kernel parameter blocks shared by the launchers and the
+// C-ABI entry points (passed to the kernels by value).
+#pragma once
+
+#include <stdint.h>
+
+namespace pa {
+
+struct SplitParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  float* part_out;
+  float* part_max;
+  float* part_sum;
+  int64_t page_stride;
+  int64_t head_stride;
+  int32_t token_stride;
+  int32_t bt_stride;
+  int32_t num_q_heads;
+  int32_t page_size;
+  int32_t page_shift;   // log2(page_size)
+  int32_t window;
+  int32_t partition_size;
+  int32_t max_parts;
+  int32_t write_empty;
+  float scale_log2;
+};
+
+struct MergeParams {
+  const float* part_out;
+  const float* part_max;
+  const float* part_sum;
+  const int32_t* context_lens;
+  uint16_t* out;
+  float* lse;
+  int32_t num_q_heads;
+  int32_t partition_size;
+  int32_t max_parts;
+  int32_t window;
+};
+
+}  // namespace pa

@@ -1,0 +1,212 @@
+// pa_validate.cpp -- host-side checks and launch planning (no HIP).
+#include "pa_validate.h"
+
+#include <cmath>
+#include <cstdio>
+
+namespace pa {
+
+namespace {
+thread_local std::string g_last_error;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool mult8(int64_t s) { return s > 0 && (s % 8) == 0; }
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+}  // namespace
+
+int fail(int status, const std::string& msg) {
+  g_last_error = msg;
+  return status;
+}
+void clear_error() { g_last_error.clear(); }
+const char* last_error() { return g_last_error.c_str(); }
+
+bool head_dim_supported(int32_t d) { return d == 128 || d == 256; }
+
+// q heads per KV head built per head_dim: the accumulator of one lane holds
+// group * 8 fp32 values, so head_dim 256 stops at 8.
+bool group_supported(int32_t head_dim, int32_t group) {
+  if (group == 1 || group == 2 || group == 4 || group == 8) return true;
+  return group == 16 && head_dim == 128;
+}
+
+bool page_size_supported(int32_t ps) { return ps == 16 || ps == 32 || ps == 64; }
+
+int64_t max_keys(int32_t max_pages_per_seq, int32_t page_size, int32_t window) {
+  int64_t k = static_cast<int64_t>(max_pages_per_seq) * page_size;
+  if (window > 0 && window < k) k = window;
+  return k;
+}
+
+int check_gqa(const void* q, const void* k_pool, const void* v_pool, const pa_kv_layout* kv,
+              const int32_t* block_table, int32_t block_table_stride,
+              const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+              int32_t max_pages_per_seq, float scale) {
+  if (!q || !k_pool || !v_pool || !kv || !block_table || !context_lens)
+    return fail(PA_ERR_NULL, "a required pointer (q, k_pool, v_pool, kv, block_table, "
+                             "context_lens) is NULL");
+  if (batch < 1 || num_q_heads < 1 || max_pages_per_seq < 1)
+    return fail(PA_ERR_SHAPE, "batch, num_q_heads and max_pages_per_seq must be >= 1");
+  if (batch > 65535 || num_q_heads > 65535)
+    return fail(PA_ERR_SHAPE, "batch and num_q_heads must be <= 65535 (grid limits)");
+  if (kv->num_pages < 1 || kv->num_kv_heads < 1 || kv->page_size < 1 || kv->head_dim < 1)
+    return fail(PA_ERR_SHAPE, "kv layout: num_pages, num_kv_heads, page_size, head_dim must be >= 1");
+  if (num_q_heads % kv->num_kv_heads != 0)
+    return fail(PA_ERR_SHAPE, "num_q_heads must be a multiple of num_kv_heads");
+  if (block_table_stride < max_pages_per_seq)
+    return fail(PA_ERR_SHAPE, "block_table_stride must be >= max_pages_per_seq");
+  if (!std::isfinite(scale) || !(scale > 0.0f))
+    return fail(PA_ERR_SHAPE, "scale must be finite and > 0");
+  if (static_cast<int64_t>(max_pages_per_seq) * kv->page_size > INT32_MAX / 2)
+    return fail(PA_ERR_SHAPE, "max_pages_per_seq * page_size is too large");
+  if (!head_dim_supported(kv->head_dim))
+    return fail(PA_ERR_UNSUPPORTED, "head_dim must be 128 or 256");
+  const int32_t group = num_q_heads / kv->num_kv_heads;
+  if (!group_supported(kv->head_dim, group))
+    return fail(PA_ERR_UNSUPPORTED, "q heads per KV head must be 1, 2, 4, 8 (or 16 at head_dim 128)");
+  if (!page_size_supported(kv->page_size))
+    return fail(PA_ERR_UNSUPPORTED, "page_size must be 16, 32 or 64");
+  if (!mult8(kv->page_stride) || !mult8(kv->head_stride) || !mult8(kv->token_stride))
+    return fail(PA_ERR_ALIGN, "kv strides must be positive multiples of 8 elements");
+  if (kv->token_stride < kv->head_dim)
+    return fail(PA_ERR_SHAPE, "token_stride must be >= head_dim");
+  if (static_cast<int64_t>(kv->page_size - 1) * kv->token_stride + kv->head_dim > INT32_MAX / 4)
+    return fail(PA_ERR_SHAPE, "token_stride too large");
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
+    return fail(PA_ERR_ALIGN, "q, k_pool and v_pool must be 16-byte aligned");
+  return PA_OK;
+}
+
+int check_split(int32_t partition_size, int32_t max_partitions, int32_t max_pages_per_seq,
+                int32_t page_size, int32_t window, const float* part_out, const float* part_max,
+                const float* part_sum) {
+  if (!part_out || !part_max || !part_sum)
+    return fail(PA_ERR_NULL, "part_out, part_max and part_sum must not be NULL");
+  if (partition_size < 1 || max_partitions < 1)
+    return fail(PA_ERR_SHAPE, "partition_size and max_partitions must be >= 1");
+  const int64_t need = ceil_div(max_keys(max_pages_per_seq, page_size, window), partition_size);
+  if (max_partitions < need) {
+    char buf[160];
+    std::snprintf(buf, sizeof buf,
+                  "max_partitions %d cannot cover %lld keys in partitions of %d (need %lld)",
+                  max_partitions, (long long)max_keys(max_pages_per_seq, page_size, window),
+                  partition_size, (long long)need);
+    return fail(PA_ERR_SHAPE, buf);
+  }
+  if (!aligned16(part_out) || !aligned16(part_max) || !aligned16(part_sum))
+    return fail(PA_ERR_ALIGN, "partial buffers must be 16-byte aligned");
+  return PA_OK;
+}
+
+int check_merge(const float* part_out, const float* part_max, const float* part_sum,
+                const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                int32_t head_dim, int32_t partition_size, int32_t max_partitions, const void* out) {
+  if (!part_out || !part_max || !part_sum || !context_lens || !out)
+    return fail(PA_ERR_NULL, "part_out, part_max, part_sum, context_lens and out must not be NULL");
+  if (batch < 1 || num_q_heads < 1 || partition_size < 1 || max_partitions < 1)
+    return fail(PA_ERR_SHAPE, "batch, num_q_heads, partition_size, max_partitions must be >= 1");
+  if (batch > 65535 || num_q_heads > 65535)
+    return fail(PA_ERR_SHAPE, "batch and num_q_heads must be <= 65535 (grid limits)");
+  if (!head_dim_supported(head_dim))
+    return fail(PA_ERR_UNSUPPORTED, "head_dim must be 128 or 256");
+  if (!aligned16(part_out) || !aligned16(out))
+    return fail(PA_ERR_ALIGN, "part_out and out must be 16-byte aligned");
+  return PA_OK;
+}
+
+// Partition size for pa_decode.  Aim at about 4096 work items of (sequence,
+// KV head, partition) when contexts average half the maximum, but never below
+// 256 keys for head_dim 128 (128 for 256): a partition's fp32 partial output
+// (group * (head_dim + 2) floats) must stay small next to the K/V bytes it
+// summarises.  Depends on host-known shapes only.
+bool plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                 int32_t max_pages_per_seq, int32_t page_size, int32_t window, DecodePlan* plan) {
+  if (batch < 1 || num_q_heads < 1 || num_kv_heads < 1 || max_pages_per_seq < 1 ||
+      page_size < 1 || !head_dim_supported(head_dim) || num_q_heads % num_kv_heads)
+    return false;
+  const int64_t keys = max_keys(max_pages_per_seq, page_size, window);
+  const int64_t work = static_cast<int64_t>(batch) * num_kv_heads * keys;
+  int64_t p = 1;
+  while (p * 2 * 4096 < work) p *= 2;
+  const int64_t pmin = head_dim == 128 ? 256 : 128;
+  if (p < pmin) p = pmin;
+  if (p > 4096) p = 4096;
+  plan->partition_size = static_cast<int32_t>(p);
+  plan->max_partitions = static_cast<int32_t>(ceil_div(keys, p));
+  const size_t rows = static_cast<size_t>(batch) * num_q_heads * plan->max_partitions;
+  plan->off_out = 0;
+  plan->off_max = round_up(rows * head_dim * sizeof(float), 256);
+  plan->off_sum = plan->off_max + round_up(rows * sizeof(float), 256);
+  plan->bytes = plan->off_sum + round_up(rows * sizeof(float), 256);
+  return true;
+}
+
+// MLA split plan: partition size a multiple of the 64-key granule; by default
+// about 2 * 256 work items of (sequence, head tile, partition).
+bool plan_mla(int32_t batch, int32_t num_heads, int32_t max_pages_per_seq, int32_t page_size,
+              int32_t partition_size, MlaPlan* plan) {
+  if (batch < 1 || num_heads < 1 || num_heads % kMlaHeadTile || max_pages_per_seq < 1 ||
+      !page_size_supported(page_size) || partition_size < 0 || partition_size % kMlaKeyTile)
+    return false;
+  const int64_t keys = static_cast<int64_t>(max_pages_per_seq) * page_size;
+  int64_t p = partition_size;
+  if (p == 0) {
+    const int64_t tiles = static_cast<int64_t>(batch) * (num_heads / kMlaHeadTile);
+    p = kMlaKeyTile;
+    while (tiles * ceil_div(keys, p) / 2 > 512 && p < 8192) p *= 2;
+  }
+  plan->partition_size = static_cast<int32_t>(p);
+  plan->max_partitions = static_cast<int32_t>(ceil_div(keys, p));
+  const size_t bh = static_cast<size_t>(batch) * num_heads;
+  const size_t rows = bh * plan->max_partitions;
+  plan->off_qabs = 0;                                               // q_abs hi/lo, bf16 [B][H][576][2]
+  plan->off_out = round_up(bh * kMlaRow * 2 * sizeof(uint16_t), 256);
+  plan->off_max = plan->off_out + round_up(rows * kMlaLat * sizeof(float), 256);
+  plan->off_sum = plan->off_max + round_up(rows * sizeof(float), 256);
+  plan->off_lat = plan->off_sum + round_up(rows * sizeof(float), 256);  // merged o_lat fp32 [B][H][512]
+  plan->bytes = plan->off_lat + round_up(bh * kMlaLat * sizeof(float), 256);
+  return true;
+}
+
+int check_mla(const void* q_nope, const void* q_rope, const void* kv_cache,
+              const pa_kv_layout* cache, const void* w_uk, const void* w_uv,
+              const int32_t* block_table, int32_t block_table_stride,
+              const int32_t* context_lens, int32_t batch, int32_t num_heads,
+              int32_t max_pages_per_seq, float scale, int32_t partition_size, const void* out) {
+  if (!q_nope || !q_rope || !kv_cache || !cache || !w_uk || !w_uv || !block_table ||
+      !context_lens || !out)
+    return fail(PA_ERR_NULL, "a required pointer is NULL");
+  if (batch < 1 || num_heads < 1 || max_pages_per_seq < 1)
+    return fail(PA_ERR_SHAPE, "batch, num_heads and max_pages_per_seq must be >= 1");
+  if (batch > 65535 || num_heads > 65535)
+    return fail(PA_ERR_SHAPE, "batch and num_heads must be <= 65535 (grid limits)");
+  if (cache->num_pages < 1 || cache->page_size < 1)
+    return fail(PA_ERR_SHAPE, "cache: num_pages and page_size must be >= 1");
+  if (block_table_stride < max_pages_per_seq)
+    return fail(PA_ERR_SHAPE, "block_table_stride must be >= max_pages_per_seq");
+  if (!std::isfinite(scale) || !(scale > 0.0f))
+    return fail(PA_ERR_SHAPE, "scale must be finite and > 0");
+  if (static_cast<int64_t>(max_pages_per_seq) * cache->page_size > INT32_MAX / 2)
+    return fail(PA_ERR_SHAPE, "max_pages_per_seq * page_size is too large");
+  if (cache->num_kv_heads != 1 || cache->head_dim != kMlaRow)
+    return fail(PA_ERR_UNSUPPORTED, "MLA cache must have num_kv_heads 1 and head_dim 576");
+  if (num_heads % kMlaHeadTile)
+    return fail(PA_ERR_UNSUPPORTED, "num_heads must be a multiple of 16");
+  if (!page_size_supported(cache->page_size))
+    return fail(PA_ERR_UNSUPPORTED, "page_size must be 16, 32 or 64");
+  if (partition_size < 0 || partition_size % kMlaKeyTile)
+    return fail(PA_ERR_SHAPE, "partition_size must be 0 or a positive multiple of 64");
+  if (!mult8(cache->page_stride) || !mult8(cache->token_stride))
+    return fail(PA_ERR_ALIGN, "cache strides must be positive multiples of 8 elements");
+  if (cache->token_stride < kMlaRow)
+    return fail(PA_ERR_SHAPE, "cache token_stride must be >= 576");
+  if (static_cast<int64_t>(cache->page_size) * cache->token_stride > INT32_MAX / 4)
+    return fail(PA_ERR_SHAPE, "cache token_stride too large");
+  if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(kv_cache) || !aligned16(w_uk) ||
+      !aligned16(w_uv) || !aligned16(out))
+    return fail(PA_ERR_ALIGN, "q_nope, q_rope, kv_cache, w_uk, w_uv and out must be 16-byte aligned");
+  return PA_OK;
+}
+
+}  // namespace pa

@@ -1,0 +1,75 @@
+// pa_validate.h -- host-side argument checks and launch planning for the
+// paged-decode C ABI.  Pure C++ (no HIP headers), so the checks build and
+// run on a machine without a GPU.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "pa_decode.h"
+
+namespace pa {
+
+// Records `msg` as the calling thread's last error and returns `status`.
+int fail(int status, const std::string& msg);
+void clear_error();
+const char* last_error();
+
+// Supported compile-time shapes.
+bool head_dim_supported(int32_t d);
+bool group_supported(int32_t head_dim, int32_t group);
+bool page_size_supported(int32_t ps);
+
+// Largest number of keys one sequence can attend to.
+int64_t max_keys(int32_t max_pages_per_seq, int32_t page_size, int32_t window);
+
+// Checks shared by pa_decode and pa_decode_splitkv.
+int check_gqa(const void* q, const void* k_pool, const void* v_pool, const pa_kv_layout* kv,
+              const int32_t* block_table, int32_t block_table_stride,
+              const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+              int32_t max_pages_per_seq, float scale);
+
+// Checks for explicit split parameters.
+int check_split(int32_t partition_size, int32_t max_partitions, int32_t max_pages_per_seq,
+                int32_t page_size, int32_t window, const float* part_out, const float* part_max,
+                const float* part_sum);
+
+int check_merge(const float* part_out, const float* part_max, const float* part_sum,
+                const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                int32_t head_dim, int32_t partition_size, int32_t max_partitions, const void* out);
+
+// Launch plan of pa_decode: partition size and workspace carve-up, a pure
+// function of host-known shapes.
+struct DecodePlan {
+  int32_t partition_size = 0;
+  int32_t max_partitions = 0;
+  size_t off_out = 0, off_max = 0, off_sum = 0, bytes = 0;
+};
+bool plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                 int32_t max_pages_per_seq, int32_t page_size, int32_t window, DecodePlan* plan);
+
+// MLA geometry fixed by the absorbed-MLA entry point.
+constexpr int32_t kMlaNope = 128;
+constexpr int32_t kMlaRope = 64;
+constexpr int32_t kMlaLat = 512;
+constexpr int32_t kMlaRow = kMlaLat + kMlaRope;  // 576
+constexpr int32_t kMlaDv = 128;
+constexpr int32_t kMlaHeadTile = 16;             // heads per MFMA tile
+constexpr int32_t kMlaKeyTile = 64;              // keys per split granule
+
+struct MlaPlan {
+  int32_t partition_size = 0;
+  int32_t max_partitions = 0;
+  size_t off_qabs = 0, off_out = 0, off_max = 0, off_sum = 0, off_lat = 0, bytes = 0;
+};
+bool plan_mla(int32_t batch, int32_t num_heads, int32_t max_pages_per_seq, int32_t page_size,
+              int32_t partition_size, MlaPlan* plan);
+
+int check_mla(const void* q_nope, const void* q_rope, const void* kv_cache,
+              const pa_kv_layout* cache, const void* w_uk, const void* w_uv,
+              const int32_t* block_table, int32_t block_table_stride,
+              const int32_t* context_lens, int32_t batch, int32_t num_heads,
+              int32_t max_pages_per_seq, float scale, int32_t partition_size, const void* out);
+
+}  // namespace pa

@@ -1,0 +1,58 @@
+"""Helpers for the GPU parity tests: run a seeded case through the C ABI
+(via the thin binding) and hand back CPU tensors."""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from paged_attention_decode_05_amd import binding as pb
+
+
+def dev_case(case):
+    return case.to("cuda")
+
+
+def run_decode(dc, with_lse=True, workspace=None):
+    B, H, D = dc.q.shape
+    out = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda") if with_lse else None
+    kv = pb.kv_layout(dc.k_pool, dc.layout)
+    if workspace is None:
+        nbytes = pb.pa_decode_workspace_size(B, H, dc.num_kv_heads, D, dc.max_pages, dc.page_size,
+                                             dc.window)
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    pb.pa_decode(dc.q, dc.k_pool, dc.v_pool, kv, dc.block_table, dc.context_lens, dc.scale,
+                 dc.window, out, lse, workspace)
+    torch.cuda.synchronize()
+    return out.cpu(), (lse.cpu() if lse is not None else None)
+
+
+def max_parts_for(dc, partition_size):
+    keys = dc.max_pages * dc.page_size
+    if dc.window > 0:
+        keys = min(keys, dc.window)
+    return max(1, math.ceil(keys / partition_size))
+
+
+def run_splitkv(dc, partition_size, max_parts=None, poison=True):
+    B, H, D = dc.q.shape
+    mp = max_parts or max_parts_for(dc, partition_size)
+    fill = float("nan") if poison else 0.0
+    po = torch.full((B, H, mp, D), fill, dtype=torch.float32, device="cuda")
+    pm = torch.full((B, H, mp), fill, dtype=torch.float32, device="cuda")
+    ps = torch.full((B, H, mp), fill, dtype=torch.float32, device="cuda")
+    pb.pa_decode_splitkv(dc.q, dc.k_pool, dc.v_pool, pb.kv_layout(dc.k_pool, dc.layout),
+                         dc.block_table, dc.context_lens, dc.scale, dc.window, partition_size, mp,
+                         po, pm, ps)
+    torch.cuda.synchronize()
+    return po, pm, ps
+
+
+def run_merge(po, pm, ps, context_lens, partition_size, window):
+    B, H, P, D = po.shape
+    out = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    pb.pa_merge_lse(po, pm, ps, context_lens, partition_size, window, out, lse)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu()
