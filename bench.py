@@ -1,0 +1,215 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark: µs per call and KV-read bandwidth on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama]
+
+One step = one pa_decode call (split-KV partial kernel + LSE merge kernel)
+over one batch of the synthetic workload, inputs resident in HBM.  The timed
+region is bracketed by torch.cuda.synchronize() on both sides and measured
+with HIP events on the stream the kernels are launched on (torch's current
+stream, whose handle is passed through the C ABI).
+
+value = algorithmic K+V bytes per call / mean time per call  (GB/s, 1e9 B/s)
+  algorithmic bytes = sum over sequences of attended keys * 2 (K and V)
+                      * num_kv_heads * head_dim * 2 B
+roofline (dominant kernel = the split-KV partial kernel): the same bytes /
+  that kernel's mean duration, from HIP events around each of K launches of
+  the kernel through pa_decode_splitkv with pa_decode's partition size.
+cpu_baseline: the CPU oracle (float64, the parity reference) on the whole
+  workload, all host threads, on the same byte definition.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+METRIC = "decode-attn µs/call + KV-read GB/s (% of MI355X HBM peak), d128 GQA bs64"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama", choices=["tiny", "llama", "d256w", "long"])
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--rotate", type=int, default=1,
+                    help="input sets to rotate through (for workloads that fit in the 256 MB "
+                         "Infinity Cache)")
+    return ap.parse_args()
+
+
+def main() -> int:
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        return 2
+    import torch
+
+    from paged_attention_decode_05_amd import binding as pb
+    from paged_attention_decode_05_amd import workload as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+
+    log(f"generating workload {a.workload} (seeded) ...")
+    t0 = time.time()
+    cases = [wl.NAMED[a.workload](poison=False, seed=wl.SEED_BASE + 100 * i + {
+        "tiny": 1, "llama": 2, "d256w": 3, "long": 4}[a.workload]) for i in range(a.rotate)]
+    dcs = [c.to(dev) for c in cases]
+    log(f"  {time.time() - t0:.1f}s; pool pages {cases[0].num_pages}, "
+        f"sum ctx {int(cases[0].context_lens.sum())}")
+    c0 = cases[0]
+    B, H, D = c0.q.shape
+    Hkv = c0.num_kv_heads
+    kv_bytes = [c.kv_bytes() for c in cases]
+    P = pb.pa_decode_partition_size(B, H, Hkv, D, c0.max_pages, c0.page_size, c0.window)
+    ws_bytes = pb.pa_decode_workspace_size(B, H, Hkv, D, c0.max_pages, c0.page_size, c0.window)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
+    kvl = [pb.kv_layout(d.k_pool, d.layout) for d in dcs]
+
+    def step(i):
+        d = dcs[i % len(dcs)]
+        pb.pa_decode(d.q, d.k_pool, d.v_pool, kvl[i % len(dcs)], d.block_table, d.context_lens,
+                     d.scale, d.window, out, None, ws)
+
+    stream = torch.cuda.current_stream()
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"timing {a.steps} pa_decode calls (partition {P}) ...")
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(a.steps):
+        step(i)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / a.steps
+    mean_bytes = sum(kv_bytes[i % len(cases)] for i in range(a.steps)) / a.steps
+    gbs = mean_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # Dominant kernel alone: the split-KV partial kernel, HIP events around each launch.
+    maxp = -(-min(c0.max_pages * c0.page_size, c0.window if c0.window > 0 else 1 << 30) // P)
+    po = torch.empty((B, H, maxp, D), dtype=torch.float32, device=dev)
+    pm = torch.empty((B, H, maxp), dtype=torch.float32, device=dev)
+    ps = torch.empty((B, H, maxp), dtype=torch.float32, device=dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+    for i in range(min(a.warmup, 5)):
+        d = dcs[i % len(dcs)]
+        pb.pa_decode_splitkv(d.q, d.k_pool, d.v_pool, kvl[i % len(dcs)], d.block_table,
+                             d.context_lens, d.scale, d.window, P, maxp, po, pm, ps)
+    torch.cuda.synchronize()
+    log("timing the split-KV kernel and the merge kernel separately ...")
+    for i in range(a.steps):
+        d = dcs[i % len(dcs)]
+        ev[i][0].record(stream)
+        pb.pa_decode_splitkv(d.q, d.k_pool, d.v_pool, kvl[i % len(dcs)], d.block_table,
+                             d.context_lens, d.scale, d.window, P, maxp, po, pm, ps)
+        ev[i][1].record(stream)
+        pb.pa_merge_lse(po, pm, ps, d.context_lens, P, d.window, out)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    split_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    merge_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    split_mean = statistics.fmean(split_ms)
+    merge_mean = statistics.fmean(merge_ms)
+    achieved = mean_bytes / (split_mean * 1e-3) / 1e9
+
+    cpu = None
+    if not a.no_cpu:
+        cpu = cpu_baseline(cases[0])
+
+    res = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_call": round(ms_per_step * 1e3, 2),
+        "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "storage_dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": {"llama": "llama3-8b-shaped decode, bs64, 32q/8kv heads, d128, page 32, "
+                                  "ctx U[512,8192]",
+                         "tiny": "tiny paged decode, 8 seqs, 8q/2kv, d128, page 32",
+                         "d256w": "d256 GQA-8 sliding window 4096, bs32",
+                         "long": "long context bs4, ctx 32K-128K, d128"}[a.workload],
+            "batch": B, "num_q_heads": H, "num_kv_heads": Hkv, "head_dim": D,
+            "page_size": c0.page_size, "window": c0.window,
+            "sum_context": int(c0.context_lens.sum()), "pool_pages": c0.num_pages,
+            "partition_size": P, "kv_bytes_per_call": int(mean_bytes),
+            "input_sets_rotated": a.rotate, "layout": c0.layout,
+        },
+        "kernels_us": {"split": round(split_mean * 1e3, 2), "merge": round(merge_mean * 1e3, 2)},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "split_kernel",
+            "algorithmic_bytes_per_launch": int(mean_bytes),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def cpu_baseline(case):
+    """The CPU oracle (float64 gate instantiation, unmodified) on the whole
+    workload with every host thread, repeated until about 10 s of wall time or
+    3 runs; reports the median on the same byte definition as the GPU."""
+    from oracle.oracle import Oracle
+    o = Oracle()
+    threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    # the GPU machine grants 16 host threads per GPU (OMP_NUM_THREADS)
+    threads = max(1, min(threads, int(os.environ.get("OMP_NUM_THREADS", "16") or 16)))
+    o.set_threads(threads)
+    times = []
+    t_all = time.time()
+    while len(times) < 3 or (time.time() - t_all < 10 and len(times) < 10):
+        t = time.time()
+        o.decode(case, "f64")
+        times.append(time.time() - t)
+    med = statistics.median(times)
+    return {"value": round(case.kv_bytes() / med / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"whole workload ({case.batch} seqs, {int(case.context_lens.sum())} keys), "
+                      f"float64 oracle, median of {len(times)} runs",
+            "seconds_per_call": round(med, 3)}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

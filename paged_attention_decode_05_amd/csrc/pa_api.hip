@@ -51,6 +51,9 @@ pa::SplitParams split_params(const void* q, const void* k_pool, const void* v_po
   p.page_stride = kv->page_stride;
   p.head_stride = kv->head_stride;
   p.token_stride = static_cast<int32_t>(kv->token_stride);
+  p.tile_bytes = static_cast<int32_t>(((kv->page_size - 1) * kv->token_stride + kv->head_dim) * 2);
+  p.token_bytes = static_cast<int32_t>(kv->token_stride * 2);
+  p.page_bytes = static_cast<uint32_t>(kv->page_stride * 2);
   p.bt_stride = block_table_stride;
   p.num_q_heads = num_q_heads;
   p.page_size = kv->page_size;

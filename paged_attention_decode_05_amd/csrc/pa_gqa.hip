@@ -30,34 +30,226 @@ namespace pa {
 constexpr int kWaves = 4;
 constexpr int kBlock = 64 * kWaves;
 
-// Loads per lane per chunk: fewer for wide groups to bound registers.
-template <int G>
-constexpr int chunk_loads() { return G <= 4 ? 8 : (G == 8 ? 4 : 2); }
+// ---- lane-level exchange helpers (partner = lane ^ W) ---------------------------
+
+template <int W>
+__device__ __forceinline__ float xor_lane(float x) {
+  if constexpr (W == 1) return dpp<0xB1>(x);       // quad_perm [1,0,3,2]
+  else if constexpr (W == 2) return dpp<0x4E>(x);  // quad_perm [2,3,0,1]
+  else if constexpr (W == 4)
+    return u2f(static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(f2u(x)), 0x101f)));
+  else if constexpr (W == 8) return dpp<kRowRor8>(x);   // i -> i+8 mod 16 == i ^ 8
+  else if constexpr (W == 16) return xor16(x);
+  else return xor32(x);
+}
+
+// Sum (kMax = false) or max over the lanes that differ in bits [lo, hi) of
+// the lane id; every such lane gets the result.
+template <int LO, int HI, bool kMax>
+__device__ __forceinline__ float reduce_bits(float x) {
+  if constexpr (LO < HI) {
+    const float y = xor_lane<(1 << LO)>(x);
+    x = kMax ? fmaxf(x, y) : x + y;
+    return reduce_bits<LO + 1, HI, kMax>(x);
+  } else {
+    return x;
+  }
+}
+
+constexpr int ilog2c(int v) { return v <= 1 ? 0 : 1 + ilog2c(v / 2); }
+
+// Compile-time geometry of the split kernel for head_dim D and group G.
+//
+// Score layout: LQ lanes share one key row, each holding D/LQ of its dims
+// (NQL 16-byte pieces); a pass covers TQ = 64/LQ keys.  The LQ partial dot
+// products of every head are combined by a reduce-scatter: at step s lanes
+// j and j ^ (LQ >> (s+1)) trade halves of their remaining head slots, and the
+// q rows are pre-permuted per lane (slot h of lane j holds head h ^ pi(j)) so
+// each step is one uniform "own[k] + partner[k + half]".  After NSCAT steps a
+// lane owns VH heads (slot k = head k ^ pi(j)); leftover steps, when G < LQ,
+// are plain sums.
+//
+// Value layout: LV = D/8 lanes per key row, 8 dims each, TV = 64/LV keys per
+// load; the accumulator of a lane holds its 8 dims for all G heads.
+template <int D, int G>
+struct Geo {
+  static constexpr int LQ = (G * D / 128) > 4 ? G * D / 128 : 4;
+  static constexpr int LOG_LQ = ilog2c(LQ);
+  static constexpr int NQL = D / (8 * LQ);
+  static constexpr int TQ = 64 / LQ;
+  static constexpr int LV = D / 8;
+  static constexpr int TV = 64 / LV;
+  static constexpr int CH = (G >= 16) ? 16 : (D == 128 ? 32 : 16);   // keys per chunk
+  static constexpr int NTQ = CH / TQ;
+  static constexpr int NV = CH / TV;
+  static constexpr int LOG_G = ilog2c(G);
+  static constexpr int NSCAT = LOG_G < LOG_LQ ? LOG_G : LOG_LQ;
+  static constexpr int VH = G >> NSCAT;
+  static_assert(NTQ >= 1 && NV >= 1 && NQL >= 1, "geometry");
+};
+
+// pi(j): which head sits in slot 0 of lane j (within its LQ-lane key group).
+template <int D, int G>
+__device__ __forceinline__ int head_perm(int j) {
+  using g = Geo<D, G>;
+  int pi = 0;
+#pragma unroll
+  for (int s = 0; s < g::NSCAT; ++s) pi |= ((j >> (g::LOG_LQ - 1 - s)) & 1) * (G >> (s + 1));
+  return pi;
+}
+
+// Reduce-scatter of v[0..G) over the LQ lanes of a key group; returns with
+// v[0..VH) holding complete sums for heads k ^ pi(j).
+template <int D, int G, int S>
+__device__ __forceinline__ void scatter_step(float (&v)[G]) {
+  using g = Geo<D, G>;
+  if constexpr (S < g::NSCAT) {
+    constexpr int W = g::LQ >> (S + 1);
+    constexpr int HALF = G >> (S + 1);
+#pragma unroll
+    for (int k = 0; k < HALF; ++k) v[k] += xor_lane<W>(v[k + HALF]);
+    scatter_step<D, G, S + 1>(v);
+  } else if constexpr (S < g::LOG_LQ) {
+    constexpr int W = g::LQ >> (S + 1);
+    v[0] += xor_lane<W>(v[0]);
+    scatter_step<D, G, S + 1>(v);
+  }
+}
+
+// Page table of one wave: the partition [begin, end) is cut into aligned
+// chunks of CH keys and wave w takes chunks c0 = first + w, c0 + 4, ...  The
+// physical page of every page those chunks touch sits in one lane of `ptab`
+// (lane = chunk-in-group << ppc_shift | page-in-chunk), loaded from the block
+// table once per group of 64 >> ppc_shift chunks and read back with
+// v_readlane, so no K/V load waits on a block-table read.
+struct WaveKeys {
+  const int32_t* bt;
+  int begin, end;
+  int c0, nk;
+  int ppc_shift;
+  int ptab;
+  int group;
+};
+
+template <int CH>
+__device__ __forceinline__ void load_page_table(WaveKeys& wk, int grp, int lane, int page_shift) {
+  const int per_group = 64 >> wk.ppc_shift;
+  const int k = grp * per_group + (lane >> wk.ppc_shift);
+  const int sub = lane & ((1 << wk.ppc_shift) - 1);
+  const int c = wk.c0 + k * kWaves;
+  const int pi = ((c * CH) >> page_shift) + sub;
+  const bool live = k < wk.nk && pi >= (wk.begin >> page_shift) && pi <= ((wk.end - 1) >> page_shift);
+  wk.ptab = live ? wk.bt[pi] : 0;
+  wk.group = grp;
+}
+
+// Make sure `ptab` covers chunk k of the wave (reloads once per group).
+template <int CH>
+__device__ __forceinline__ void ensure_pages(WaveKeys& wk, int k, int lane, int page_shift) {
+  const int grp = k >> (6 - wk.ppc_shift);
+  if (grp != wk.group) load_page_table<CH>(wk, grp, lane, page_shift);
+}
+
+// Physical page of key t of the wave's k-th chunk (table already loaded).
+template <int CH>
+__device__ __forceinline__ int page_of(const WaveKeys& wk, int k, int t, int page_shift) {
+  const int kk = k & ((64 >> wk.ppc_shift) - 1);
+  const int tchunk = (wk.c0 + k * kWaves) * CH;
+  const int slot = (kk << wk.ppc_shift) + ((t >> page_shift) - (tchunk >> page_shift));
+  return __builtin_amdgcn_readlane(wk.ptab, slot);
+}
+
+// Buffer descriptor over one (page, KV head) tile; reads at offsets past
+// `tile_bytes` return zeros, which is how dead keys are masked without
+// branching or touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base, int page,
+                                                            uint32_t page_bytes, int tile_bytes) {
+  const char* tile = reinterpret_cast<const char*>(base) +
+                     static_cast<uint64_t>(static_cast<uint32_t>(page)) * page_bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(tile), static_cast<short>(0),
+                                           tile_bytes, 0x00020000);
+}
+
+constexpr int kDeadBit = 0x40000000;   // OR-ed into a dead key's offset: past any tile
+
+__device__ __forceinline__ uint4 tile_load(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// 1 when key t lies outside [begin, end), as the dead-offset bit.
+__device__ __forceinline__ int dead_bit(int t, int begin, int end) {
+  return (static_cast<uint32_t>(t - begin) >= static_cast<uint32_t>(end - begin)) ? kDeadBit : 0;
+}
+
+template <int D, int G>
+struct KRegs {
+  uint4 v[Geo<D, G>::NTQ][Geo<D, G>::NQL];
+};
+template <int D, int G>
+struct VRegs {
+  uint4 v[Geo<D, G>::NV];
+};
+
+// K pieces of chunk k in the score layout; dead keys hold 0.  `koff` is this
+// lane's byte offset inside a tile for slot 0 (slot row r plus its dims); the
+// slot of the first key of a pass is added through the scalar offset.
+template <int D, int G>
+__device__ __forceinline__ void load_k(KRegs<D, G>& kr, const WaveKeys& wk, int k, int lane,
+                                       const uint16_t* kbase, const SplitParams& p, int koff) {
+  using g = Geo<D, G>;
+  const int tchunk = (wk.c0 + k * kWaves) * g::CH;
+  const int r = lane / g::LQ;
+#pragma unroll
+  for (int u = 0; u < g::NTQ; ++u) {
+    const int t0 = tchunk + u * g::TQ;                 // keys t0 .. t0+TQ-1 share one page
+    const int page = page_of<g::CH>(wk, k, t0, p.page_shift);
+    const auto rs = tile_rsrc(kbase, page, p.page_bytes, p.tile_bytes);
+    const int soff = (t0 & (p.page_size - 1)) * p.token_bytes;
+    const int voff = koff | dead_bit(t0 + r, wk.begin, wk.end);
+#pragma unroll
+    for (int s = 0; s < g::NQL; ++s) kr.v[u][s] = tile_load(rs, voff + s * 16 * g::LQ, soff);
+  }
+}
+
+// V rows of chunk k in the value layout; dead keys hold 0.
+template <int D, int G>
+__device__ __forceinline__ void load_v(VRegs<D, G>& vr, const WaveKeys& wk, int k, int lane,
+                                       const uint16_t* vbase, const SplitParams& p, int voff0) {
+  using g = Geo<D, G>;
+  const int tchunk = (wk.c0 + k * kWaves) * g::CH;
+  const int r = lane / g::LV;
+#pragma unroll
+  for (int i = 0; i < g::NV; ++i) {
+    const int t0 = tchunk + i * g::TV;
+    const int page = page_of<g::CH>(wk, k, t0, p.page_shift);
+    const auto rs = tile_rsrc(vbase, page, p.page_bytes, p.tile_bytes);
+    const int soff = (t0 & (p.page_size - 1)) * p.token_bytes;
+    vr.v[i] = tile_load(rs, voff0 | dead_bit(t0 + r, wk.begin, wk.end), soff);
+  }
+}
 
 template <int D, int G>
 __global__ __launch_bounds__(kBlock) void split_kernel(const SplitParams p) {
-  constexpr int LPT = D / 8;         // lanes per key row
-  constexpr int TPI = 64 / LPT;      // keys per wave load
-  constexpr int NI = chunk_loads<G>();
-  constexpr int CH = TPI * NI;       // keys per chunk
+  using g = Geo<D, G>;
+  constexpr int CH = g::CH;
 
   __shared__ float red_acc[kWaves][G][D];
   __shared__ float red_m[kWaves][G];
   __shared__ float red_l[kWaves][G];
+  __shared__ float p_lds[kWaves][CH][G];     // probabilities, key-major
+  __shared__ float a_lds[kWaves][G];         // per-head rescale factor of the chunk
 
   const int j = blockIdx.x;
-  const int g = blockIdx.y;
+  const int gk = blockIdx.y;
   const int b = blockIdx.z;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r = lane / LPT;          // key slot within a wave load
-  const int e0 = (lane % LPT) * 8;   // first of this lane's 8 dims
 
   const int n = p.context_lens[b];
   const int lo = p.window > 0 ? max(0, n - p.window) : 0;
   const int64_t begin64 = static_cast<int64_t>(lo) + static_cast<int64_t>(j) * p.partition_size;
-  const int64_t rowbase = (static_cast<int64_t>(b) * p.num_q_heads + static_cast<int64_t>(g) * G) *
-                          p.max_parts + j;   // index of (b, h = g*G, j)
+  const int64_t rowbase = (static_cast<int64_t>(b) * p.num_q_heads + static_cast<int64_t>(gk) * G) *
+                          p.max_parts + j;   // index of (b, h = gk*G, j)
 
   if (begin64 >= n) {
     if (p.write_empty) {
@@ -72,136 +264,178 @@ __global__ __launch_bounds__(kBlock) void split_kernel(const SplitParams p) {
     }
     return;
   }
-  const int begin = static_cast<int>(begin64);
-  const int end = static_cast<int>(min(begin64 + p.partition_size, static_cast<int64_t>(n)));
 
-  // q rows of the group: 8 bf16 per lane per head.
-  uint4 qv[G];
-  {
-    const uint16_t* qb = p.q + (static_cast<int64_t>(b) * p.num_q_heads + g * G) * D + e0;
-#pragma unroll
-    for (int h = 0; h < G; ++h) qv[h] = load16(qb + h * D);
+  WaveKeys wk;
+  wk.bt = p.block_table + static_cast<int64_t>(b) * p.bt_stride;
+  wk.begin = static_cast<int>(begin64);
+  wk.end = static_cast<int>(min(begin64 + p.partition_size, static_cast<int64_t>(n)));
+  const int c_first = wk.begin / CH;
+  const int c_last = (wk.end - 1) / CH;
+  wk.c0 = c_first + wave;
+  wk.nk = (wk.c0 <= c_last) ? (c_last - wk.c0) / kWaves + 1 : 0;
+  wk.ppc_shift = (CH > p.page_size) ? (ilog2c(CH) - p.page_shift) : 0;
+  wk.ptab = 0;
+  wk.group = -1;
+
+  const uint16_t* kbase = p.k + static_cast<int64_t>(gk) * p.head_stride;
+  const uint16_t* vbase = p.v + static_cast<int64_t>(gk) * p.head_stride;
+
+  const int jq = lane % g::LQ;               // lane within its key group (score layout)
+  const int pi = head_perm<D, G>(jq);
+  // this lane writes p for its heads if it is the first copy among the
+  // lanes that a trailing plain-sum step left holding the same values
+  const bool p_writer = (jq & ((g::LQ >> g::NSCAT) - 1)) == 0;
+
+  // per-lane byte offsets inside a tile (slot row + dims); keys of one
+  // pass are consecutive slots of one page, so the pass adds a scalar
+  const int koff = (lane / g::LQ) * p.token_bytes + 16 * (lane % g::LQ);
+  const int voff0 = (lane / g::LV) * p.token_bytes + 16 * (lane % g::LV);
+
+  KRegs<D, G> kr;
+  VRegs<D, G> vr;
+  if (wk.nk > 0) {
+    ensure_pages<CH>(wk, 0, lane, p.page_shift);
+    load_k<D, G>(kr, wk, 0, lane, kbase, p, koff);
+    load_v<D, G>(vr, wk, 0, lane, vbase, p, voff0);
   }
 
-  float m[G], l[G], acc[G][8];
+  // q pieces, pre-permuted per lane: slot h holds head h ^ pi.
+  uint4 qv[G][g::NQL];
+  {
+    const uint16_t* qb = p.q + (static_cast<int64_t>(b) * p.num_q_heads + gk * G) * D + 8 * jq;
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = -INFINITY;
-    l[h] = 0.0f;
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int s = 0; s < g::NQL; ++s) qv[h][s] = load16(qb + (h ^ pi) * D + s * 8 * g::LQ);
+  }
+
+  float m_own[g::VH], l_own[g::VH];
+#pragma unroll
+  for (int v = 0; v < g::VH; ++v) {
+    m_own[v] = -INFINITY;
+    l_own[v] = 0.0f;
+  }
+  float acc[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
-  }
 
-  const int32_t* bt = p.block_table + static_cast<int64_t>(b) * p.bt_stride;
-  const uint16_t* kbase = p.k + static_cast<int64_t>(g) * p.head_stride;
-  const uint16_t* vbase = p.v + static_cast<int64_t>(g) * p.head_stride;
-  const int c_first = begin / CH;
-  const int c_last = (end - 1) / CH;
+  const int rq = lane / g::LQ;
+  for (int k = 0; k < wk.nk; ++k) {
+    const int tchunk = (wk.c0 + k * kWaves) * CH;
 
-  for (int c = c_first + wave; c <= c_last; c += kWaves) {
-    const int tchunk = c * CH;
-    uint4 kr[NI], vr[NI];
-    bool valid[NI];
+    // scores of this lane's keys, then reduce-scatter over the key group
+    float s_own[g::NTQ][g::VH];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int t0 = tchunk + i * TPI;               // first key of this load (wave-uniform)
-      const int t = t0 + r;
-      valid[i] = (t >= begin) && (t < end);
-      kr[i] = make_uint4(0, 0, 0, 0);
-      vr[i] = make_uint4(0, 0, 0, 0);
-      if (t0 + TPI > begin && t0 < end) {            // some key of this load is live
-        const int page = bt[t0 >> p.page_shift];     // page_size % TPI == 0: one page per load
-        const int64_t pbase = static_cast<int64_t>(page) * p.page_stride;
-        const int off = (t & (p.page_size - 1)) * p.token_stride + e0;
-        if (valid[i]) {
-          kr[i] = load16(kbase + pbase + off);
-          vr[i] = load16(vbase + pbase + off);
+    for (int u = 0; u < g::NTQ; ++u) {
+      float v[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float a = 0.0f;
+#pragma unroll
+        for (int s = 0; s < g::NQL; ++s) {
+          a = dot2_bf16(kr.v[u][s].x, qv[h][s].x, a);
+          a = dot2_bf16(kr.v[u][s].y, qv[h][s].y, a);
+          a = dot2_bf16(kr.v[u][s].z, qv[h][s].z, a);
+          a = dot2_bf16(kr.v[u][s].w, qv[h][s].w, a);
         }
+        v[h] = a;
       }
+      scatter_step<D, G, 0>(v);
+      const int t = tchunk + u * g::TQ + rq;
+      const bool live = t >= wk.begin && t < wk.end;
+#pragma unroll
+      for (int vh = 0; vh < g::VH; ++vh) s_own[u][vh] = live ? v[vh] * p.scale_log2 : -INFINITY;
     }
 
-    // scores s[i][h] (log2 domain), replicated over the LPT lanes of a key
-    float s[NI][G];
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float a = dot2_bf16(kr[i].x, qv[h].x, 0.0f);
-        a = dot2_bf16(kr[i].y, qv[h].y, a);
-        a = dot2_bf16(kr[i].z, qv[h].z, a);
-        a = dot2_bf16(kr[i].w, qv[h].w, a);
-        a = row_sum16(a);
-        if constexpr (LPT == 32) a += xor16(a);
-        s[i][h] = valid[i] ? a * p.scale_log2 : -INFINITY;
-      }
+    // K registers are free: start streaming the next chunk's K now (the
+    // scheduling barriers keep the compiler from hoisting these loads above
+    // the last reads of the registers they overwrite)
+    __builtin_amdgcn_sched_barrier(0);
+    if (k + 1 < wk.nk) {
+      ensure_pages<CH>(wk, k + 1, lane, p.page_shift);
+      load_k<D, G>(kr, wk, k + 1, lane, kbase, p, koff);
     }
 
-    // online softmax update, then P.V
+    // online softmax for the heads this lane owns; the running max of a head
+    // is the same on every lane that owns it (max over all keys of the chunk)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float cm = s[0][h];
+    for (int vh = 0; vh < g::VH; ++vh) {
+      float cm = s_own[0][vh];
 #pragma unroll
-      for (int i = 1; i < NI; ++i) cm = fmaxf(cm, s[i][h]);
-      const float mn = fmaxf(m[h], cm);
+      for (int u = 1; u < g::NTQ; ++u) cm = fmaxf(cm, s_own[u][vh]);
+      cm = reduce_bits<g::LOG_LQ, 6, true>(cm);
+      const float mn = fmaxf(m_own[vh], cm);
       const float base = (mn == -INFINITY) ? 0.0f : mn;
-      const float alpha = fast_exp2(m[h] - base);
-      m[h] = mn;
-      l[h] *= alpha;
+      const float alpha = fast_exp2(m_own[vh] - base);
+      m_own[vh] = mn;
+      float ls = 0.0f;
+      const int h = vh ^ pi;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        s[i][h] = fast_exp2(s[i][h] - base);
-        l[h] += s[i][h];
+      for (int u = 0; u < g::NTQ; ++u) {
+        const float pr = fast_exp2(s_own[u][vh] - base);
+        ls += pr;
+        if (p_writer) p_lds[wave][u * g::TQ + rq][h] = pr;
       }
+      l_own[vh] = l_own[vh] * alpha + ls;
+      if (p_writer && rq == 0) a_lds[wave][h] = alpha;
     }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // rescale the accumulators, then P.V in the value layout
+    {
+      float al[G];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
+      for (int h = 0; h < G; ++h) al[h] = a_lds[wave][h];
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] *= al[h];
+    }
+    const int rv = lane / g::LV;
+#pragma unroll
+    for (int i = 0; i < g::NV; ++i) {
+      float pr[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) pr[h] = p_lds[wave][i * g::TV + rv][h];
       float vf[8];
-      vf[0] = bf16_lo(vr[i].x); vf[1] = bf16_hi(vr[i].x);
-      vf[2] = bf16_lo(vr[i].y); vf[3] = bf16_hi(vr[i].y);
-      vf[4] = bf16_lo(vr[i].z); vf[5] = bf16_hi(vr[i].z);
-      vf[6] = bf16_lo(vr[i].w); vf[7] = bf16_hi(vr[i].w);
+      vf[0] = bf16_lo(vr.v[i].x); vf[1] = bf16_hi(vr.v[i].x);
+      vf[2] = bf16_lo(vr.v[i].y); vf[3] = bf16_hi(vr.v[i].y);
+      vf[4] = bf16_lo(vr.v[i].z); vf[5] = bf16_hi(vr.v[i].z);
+      vf[6] = bf16_lo(vr.v[i].w); vf[7] = bf16_hi(vr.v[i].w);
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
+      for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(s[i][h], vf[e], acc[h][e]);
-      }
+        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pr[h], vf[e], acc[h][e]);
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+
+    __builtin_amdgcn_sched_barrier(0);
+    if (k + 1 < wk.nk) load_v<D, G>(vr, wk, k + 1, lane, vbase, p, voff0);
   }
 
-  // Merge the TPI key-slot groups of this wave (lanes r*LPT + e), fixed order.
+  // Wave totals: l over the key groups that own the same head, the
+  // accumulators over the key slots of the value layout.  All lanes of a
+  // head share one running max, so no rescaling is needed here.
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float M = m[h];
-    if constexpr (TPI == 4) M = fmaxf(M, xor16(M));
-    M = fmaxf(M, xor32(M));
-    const float sc = (M == -INFINITY) ? 0.0f : fast_exp2(m[h] - M);
-    float lw = l[h] * sc;
-    if constexpr (TPI == 4) lw += xor16(lw);
-    lw += xor32(lw);
+  for (int vh = 0; vh < g::VH; ++vh) l_own[vh] = reduce_bits<g::LOG_LQ, 6, false>(l_own[vh]);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float a = acc[h][e] * sc;
-      if constexpr (TPI == 4) a += xor16(a);
-      a += xor32(a);
-      acc[h][e] = a;
-    }
-    m[h] = M;
-    l[h] = lw;
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = reduce_bits<ilog2c(g::LV), 6, false>(acc[h][e]);
+  if (lane < g::LV) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red_acc[wave][h][lane * 8 + e] = acc[h][e];
   }
-  if (lane < LPT) {
+  if (lane < g::LQ && p_writer) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) red_acc[wave][h][e0 + e] = acc[h][e];
-    }
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      red_m[wave][h] = m[h];
-      red_l[wave][h] = l[h];
+    for (int vh = 0; vh < g::VH; ++vh) {
+      red_m[wave][vh ^ pi] = m_own[vh];
+      red_l[wave][vh ^ pi] = l_own[vh];
     }
   }
   __syncthreads();

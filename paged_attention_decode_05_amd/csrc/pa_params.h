@@ -18,6 +18,9 @@ struct SplitParams {
   int64_t page_stride;
   int64_t head_stride;
   int32_t token_stride;
+  int32_t tile_bytes;   // bytes spanned by one (page, KV head) tile: ((ps-1)*token_stride + D)*2
+  int32_t token_bytes;  // token_stride * 2
+  uint32_t page_bytes;  // page_stride * 2
   int32_t bt_stride;
   int32_t num_q_heads;
   int32_t page_size;

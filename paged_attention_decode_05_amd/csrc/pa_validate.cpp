@@ -73,6 +73,9 @@ int check_gqa(const void* q, const void* k_pool, const void* v_pool, const pa_kv
     return fail(PA_ERR_SHAPE, "token_stride must be >= head_dim");
   if (static_cast<int64_t>(kv->page_size - 1) * kv->token_stride + kv->head_dim > INT32_MAX / 4)
     return fail(PA_ERR_SHAPE, "token_stride too large");
+  if (kv->page_stride > static_cast<int64_t>(UINT32_MAX / 2) ||
+      kv->head_stride > static_cast<int64_t>(UINT32_MAX / 2))
+    return fail(PA_ERR_SHAPE, "page_stride and head_stride must stay below 2^31 elements");
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
     return fail(PA_ERR_ALIGN, "q, k_pool and v_pool must be 16-byte aligned");
   return PA_OK;
