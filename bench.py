@@ -3,7 +3,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama]
 
-One step = one pa_decode call (split-KV partial kernel + LSE merge kernel)
+One step = one pa_decode call (plan kernel + balanced split-KV kernel + LSE
+merge kernel)
 over one batch of the synthetic workload, inputs resident in HBM.  The timed
 region is bracketed by torch.cuda.synchronize() on both sides and measured
 with HIP events on the stream the kernels are launched on (torch's current
@@ -12,9 +13,9 @@ stream, whose handle is passed through the C ABI).
 value = algorithmic K+V bytes per call / mean time per call  (GB/s, 1e9 B/s)
   algorithmic bytes = sum over sequences of attended keys * 2 (K and V)
                       * num_kv_heads * head_dim * 2 B
-roofline (dominant kernel = the split-KV partial kernel): the same bytes /
-  that kernel's mean duration, from HIP events around each of K launches of
-  the kernel through pa_decode_splitkv with pa_decode's partition size.
+roofline: the same bytes / the mean duration of one pa_decode call (plan
+  kernel + balanced split-KV kernel + merge kernel), from HIP events around
+  each of K calls on the launch stream; the rocprofv3 kernel trace splits it.
 cpu_baseline: the CPU oracle (float64, the parity reference) on the whole
   workload, all host threads, on the same byte definition.
 
@@ -82,7 +83,6 @@ def main() -> int:
     B, H, D = c0.q.shape
     Hkv = c0.num_kv_heads
     kv_bytes = [c.kv_bytes() for c in cases]
-    P = pb.pa_decode_partition_size(B, H, Hkv, D, c0.max_pages, c0.page_size, c0.window)
     ws_bytes = pb.pa_decode_workspace_size(B, H, Hkv, D, c0.max_pages, c0.page_size, c0.window)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     out = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
@@ -97,7 +97,7 @@ def main() -> int:
     for i in range(a.warmup):
         step(i)
     torch.cuda.synchronize()
-    log(f"timing {a.steps} pa_decode calls (partition {P}) ...")
+    log(f"timing {a.steps} pa_decode calls ...")
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
@@ -110,33 +110,21 @@ def main() -> int:
     mean_bytes = sum(kv_bytes[i % len(cases)] for i in range(a.steps)) / a.steps
     gbs = mean_bytes / (ms_per_step * 1e-3) / 1e9
 
-    # Dominant kernel alone: the split-KV partial kernel, HIP events around each launch.
-    maxp = -(-min(c0.max_pages * c0.page_size, c0.window if c0.window > 0 else 1 << 30) // P)
-    po = torch.empty((B, H, maxp, D), dtype=torch.float32, device=dev)
-    pm = torch.empty((B, H, maxp), dtype=torch.float32, device=dev)
-    ps = torch.empty((B, H, maxp), dtype=torch.float32, device=dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
-    for i in range(min(a.warmup, 5)):
-        d = dcs[i % len(dcs)]
-        pb.pa_decode_splitkv(d.q, d.k_pool, d.v_pool, kvl[i % len(dcs)], d.block_table,
-                             d.context_lens, d.scale, d.window, P, maxp, po, pm, ps)
+    # The dominant work is the balanced split-KV kernel; pa_decode launches it
+    # between a one-block plan kernel and the merge kernel inside one C call,
+    # so the per-launch figure brackets the whole call with HIP events on the
+    # launch stream (an upper bound on the split kernel's own duration).
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(a.steps)]
     torch.cuda.synchronize()
-    log("timing the split-KV kernel and the merge kernel separately ...")
     for i in range(a.steps):
-        d = dcs[i % len(dcs)]
         ev[i][0].record(stream)
-        pb.pa_decode_splitkv(d.q, d.k_pool, d.v_pool, kvl[i % len(dcs)], d.block_table,
-                             d.context_lens, d.scale, d.window, P, maxp, po, pm, ps)
+        step(i)
         ev[i][1].record(stream)
-        pb.pa_merge_lse(po, pm, ps, d.context_lens, P, d.window, out)
-        ev[i][2].record(stream)
     torch.cuda.synchronize()
-    split_ms = [e[0].elapsed_time(e[1]) for e in ev]
-    merge_ms = [e[1].elapsed_time(e[2]) for e in ev]
-    split_mean = statistics.fmean(split_ms)
-    merge_mean = statistics.fmean(merge_ms)
-    achieved = mean_bytes / (split_mean * 1e-3) / 1e9
+    call_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    call_mean = statistics.fmean(call_ms)
+    achieved = mean_bytes / (call_mean * 1e-3) / 1e9
 
     cpu = None
     if not a.no_cpu:
@@ -167,10 +155,12 @@ def main() -> int:
             "batch": B, "num_q_heads": H, "num_kv_heads": Hkv, "head_dim": D,
             "page_size": c0.page_size, "window": c0.window,
             "sum_context": int(c0.context_lens.sum()), "pool_pages": c0.num_pages,
-            "partition_size": P, "kv_bytes_per_call": int(mean_bytes),
+            "split": "balanced (equal K/V bytes per block)", "kv_bytes_per_call": int(mean_bytes),
             "input_sets_rotated": a.rotate, "layout": c0.layout,
         },
-        "kernels_us": {"split": round(split_mean * 1e3, 2), "merge": round(merge_mean * 1e3, 2)},
+        "call_us": {"mean": round(call_mean * 1e3, 2),
+                    "p10": round(sorted(call_ms)[len(call_ms) // 10] * 1e3, 2),
+                    "p90": round(sorted(call_ms)[(9 * len(call_ms)) // 10] * 1e3, 2)},
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 1),
@@ -178,7 +168,7 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": None,
-            "kernel": "split_kernel",
+            "kernel": "pa_decode call: plan_kernel + balanced_split_kernel + balanced_merge_kernel",
             "algorithmic_bytes_per_launch": int(mean_bytes),
         },
         "cpu_baseline": cpu,

@@ -17,6 +17,9 @@ namespace pa {
 hipError_t launch_split(const SplitParams& p, int head_dim, int group, int batch,
                         int num_kv_heads, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, int head_dim, int batch, hipStream_t stream);
+hipError_t launch_balanced(const SplitParams& sp, const BalancedLayout& bl, int head_dim, int group,
+                           int grid, hipStream_t stream);
+int balanced_grid(int head_dim, int group, int num_cus, int max_blocks);
 
 }  // namespace pa
 
@@ -25,6 +28,20 @@ namespace {
 int launch_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return PA_OK;
   return pa::fail(PA_ERR_LAUNCH, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
 }
 
 int ilog2(int v) {
@@ -127,11 +144,8 @@ size_t pa_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_
 int32_t pa_decode_partition_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_pages_per_seq, int32_t page_size,
                                  int32_t window) {
-  pa::DecodePlan plan;
-  if (!pa::plan_decode(batch, num_q_heads, num_kv_heads, head_dim, max_pages_per_seq, page_size,
-                       window, &plan))
-    return 0;
-  return plan.partition_size;
+  if (num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads) return 0;
+  return pa::suggest_partition(batch, num_kv_heads, head_dim, max_pages_per_seq, page_size, window);
 }
 
 int pa_decode(const void* q, const void* k_pool, const void* v_pool, const pa_kv_layout* kv,
@@ -155,31 +169,28 @@ int pa_decode(const void* q, const void* k_pool, const void* v_pool, const pa_kv
   if (reinterpret_cast<uintptr_t>(workspace) & 255u)
     return pa::fail(PA_ERR_ALIGN, "workspace must be 256-byte aligned");
   char* ws = static_cast<char*>(workspace);
-  float* part_out = reinterpret_cast<float*>(ws + plan.off_out);
-  float* part_max = reinterpret_cast<float*>(ws + plan.off_max);
-  float* part_sum = reinterpret_cast<float*>(ws + plan.off_sum);
+  const int group = num_q_heads / kv->num_kv_heads;
+  const int nbmax = pa::balanced_grid(kv->head_dim, group, device_cus(), pa::kMaxBalancedBlocks);
+  if (nbmax < 1) return pa::fail(PA_ERR_UNSUPPORTED, "no balanced-split kernel for these shapes");
+
+  pa::BalancedLayout bl{};
+  bl.context_lens = context_lens;
+  bl.out = static_cast<uint16_t*>(out);
+  bl.lse = lse_out;
+  bl.seg_out = reinterpret_cast<float*>(ws + plan.off_seg_out);
+  bl.seg_max = reinterpret_cast<float*>(ws + plan.off_seg_max);
+  bl.seg_sum = reinterpret_cast<float*>(ws + plan.off_seg_sum);
+  bl.min_units = pa::kMinUnitsPerBlock;
+  bl.rows = plan.rows;
+  bl.batch = batch;
+
   const pa::SplitParams sp = split_params(q, k_pool, v_pool, kv, block_table, block_table_stride,
-                                          context_lens, num_q_heads, scale, window,
-                                          plan.partition_size, plan.max_partitions, part_out,
-                                          part_max, part_sum, 0);
-  hipStream_t s = static_cast<hipStream_t>(stream);
+                                          context_lens, num_q_heads, scale, window, 1, 1, nullptr,
+                                          nullptr, nullptr, 0);
   pa::clear_error();
-  rc = launch_status(pa::launch_split(sp, kv->head_dim, num_q_heads / kv->num_kv_heads, batch,
-                                      kv->num_kv_heads, s),
-                     "split kernel");
-  if (rc) return rc;
-  pa::MergeParams mp{};
-  mp.part_out = part_out;
-  mp.part_max = part_max;
-  mp.part_sum = part_sum;
-  mp.context_lens = context_lens;
-  mp.out = static_cast<uint16_t*>(out);
-  mp.lse = lse_out;
-  mp.num_q_heads = num_q_heads;
-  mp.partition_size = plan.partition_size;
-  mp.max_parts = plan.max_partitions;
-  mp.window = window;
-  return launch_status(pa::launch_merge(mp, kv->head_dim, batch, s), "merge kernel");
+  return launch_status(pa::launch_balanced(sp, bl, kv->head_dim, group, nbmax,
+                                           static_cast<hipStream_t>(stream)),
+                       "balanced decode");
 }
 
 const char* pa_last_error(void) { return pa::last_error(); }

@@ -27,7 +27,7 @@
 
 namespace pa {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;               // waves of a fixed-partition block
 constexpr int kBlock = 64 * kWaves;
 
 // ---- lane-level exchange helpers (partner = lane ^ W) ---------------------------
@@ -126,6 +126,7 @@ struct WaveKeys {
   const int32_t* bt;
   int begin, end;
   int c0, nk;
+  int step;        // waves sharing the range: chunk k of this wave is c0 + k*step
   int ppc_shift;
   int ptab;
   int group;
@@ -136,7 +137,7 @@ __device__ __forceinline__ void load_page_table(WaveKeys& wk, int grp, int lane,
   const int per_group = 64 >> wk.ppc_shift;
   const int k = grp * per_group + (lane >> wk.ppc_shift);
   const int sub = lane & ((1 << wk.ppc_shift) - 1);
-  const int c = wk.c0 + k * kWaves;
+  const int c = wk.c0 + k * wk.step;
   const int pi = ((c * CH) >> page_shift) + sub;
   const bool live = k < wk.nk && pi >= (wk.begin >> page_shift) && pi <= ((wk.end - 1) >> page_shift);
   wk.ptab = live ? wk.bt[pi] : 0;
@@ -154,7 +155,7 @@ __device__ __forceinline__ void ensure_pages(WaveKeys& wk, int k, int lane, int 
 template <int CH>
 __device__ __forceinline__ int page_of(const WaveKeys& wk, int k, int t, int page_shift) {
   const int kk = k & ((64 >> wk.ppc_shift) - 1);
-  const int tchunk = (wk.c0 + k * kWaves) * CH;
+  const int tchunk = (wk.c0 + k * wk.step) * CH;
   const int slot = (kk << wk.ppc_shift) + ((t >> page_shift) - (tchunk >> page_shift));
   return __builtin_amdgcn_readlane(wk.ptab, slot);
 }
@@ -197,7 +198,7 @@ template <int D, int G>
 __device__ __forceinline__ void load_k(KRegs<D, G>& kr, const WaveKeys& wk, int k, int lane,
                                        const uint16_t* kbase, const SplitParams& p, int koff) {
   using g = Geo<D, G>;
-  const int tchunk = (wk.c0 + k * kWaves) * g::CH;
+  const int tchunk = (wk.c0 + k * wk.step) * g::CH;
   const int r = lane / g::LQ;
 #pragma unroll
   for (int u = 0; u < g::NTQ; ++u) {
@@ -216,7 +217,7 @@ template <int D, int G>
 __device__ __forceinline__ void load_v(VRegs<D, G>& vr, const WaveKeys& wk, int k, int lane,
                                        const uint16_t* vbase, const SplitParams& p, int voff0) {
   using g = Geo<D, G>;
-  const int tchunk = (wk.c0 + k * kWaves) * g::CH;
+  const int tchunk = (wk.c0 + k * wk.step) * g::CH;
   const int r = lane / g::LV;
 #pragma unroll
   for (int i = 0; i < g::NV; ++i) {
@@ -228,51 +229,41 @@ __device__ __forceinline__ void load_v(VRegs<D, G>& vr, const WaveKeys& wk, int 
   }
 }
 
-template <int D, int G>
-__global__ __launch_bounds__(kBlock) void split_kernel(const SplitParams p) {
+// Attention of the G q heads of KV head gk of sequence b over keys
+// [begin, end) (begin < end), by the NW waves of the block: wave w takes
+// chunks w, w + NW, ..., keeps its own running state, and the waves are
+// merged at the end.
+// Writes the fp32 partial of head h (0 <= h < G) to out + h*hstride*D,
+// mx[h*hstride] (natural-log max) and sm[h*hstride] (sum) -- or, when
+// `final_out` is set (the range is the row's only one), the bf16 attention
+// output of head h to final_out + h*D and its log-sum-exp to final_lse[h].
+template <int D, int G, int NW>
+__device__ __forceinline__ void attend_range(const SplitParams& p, int b, int gk, int begin,
+                                             int end, float* out, float* mx, float* sm,
+                                             int64_t hstride, uint16_t* final_out = nullptr,
+                                             float* final_lse = nullptr) {
   using g = Geo<D, G>;
   constexpr int CH = g::CH;
 
-  __shared__ float red_acc[kWaves][G][D];
-  __shared__ float red_m[kWaves][G];
-  __shared__ float red_l[kWaves][G];
-  __shared__ float p_lds[kWaves][CH][G];     // probabilities, key-major
-  __shared__ float a_lds[kWaves][G];         // per-head rescale factor of the chunk
+  constexpr int NT = 64 * NW;
+  __shared__ float red_acc[NW][G][D];
+  __shared__ float red_m[NW][G];
+  __shared__ float red_l[NW][G];
+  __shared__ float p_lds[NW][CH][G];         // probabilities, key-major
+  __shared__ float a_lds[NW][G];             // per-head rescale factor of the chunk
 
-  const int j = blockIdx.x;
-  const int gk = blockIdx.y;
-  const int b = blockIdx.z;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  const int n = p.context_lens[b];
-  const int lo = p.window > 0 ? max(0, n - p.window) : 0;
-  const int64_t begin64 = static_cast<int64_t>(lo) + static_cast<int64_t>(j) * p.partition_size;
-  const int64_t rowbase = (static_cast<int64_t>(b) * p.num_q_heads + static_cast<int64_t>(gk) * G) *
-                          p.max_parts + j;   // index of (b, h = gk*G, j)
-
-  if (begin64 >= n) {
-    if (p.write_empty) {
-      for (int i = threadIdx.x; i < G * D; i += kBlock) {
-        const int h = i / D;
-        p.part_out[(rowbase + static_cast<int64_t>(h) * p.max_parts) * D + (i % D)] = 0.0f;
-      }
-      if (threadIdx.x < G) {
-        p.part_max[rowbase + static_cast<int64_t>(threadIdx.x) * p.max_parts] = -INFINITY;
-        p.part_sum[rowbase + static_cast<int64_t>(threadIdx.x) * p.max_parts] = 0.0f;
-      }
-    }
-    return;
-  }
-
   WaveKeys wk;
   wk.bt = p.block_table + static_cast<int64_t>(b) * p.bt_stride;
-  wk.begin = static_cast<int>(begin64);
-  wk.end = static_cast<int>(min(begin64 + p.partition_size, static_cast<int64_t>(n)));
-  const int c_first = wk.begin / CH;
-  const int c_last = (wk.end - 1) / CH;
+  wk.begin = begin;
+  wk.end = end;
+  const int c_first = begin / CH;
+  const int c_last = (end - 1) / CH;
   wk.c0 = c_first + wave;
-  wk.nk = (wk.c0 <= c_last) ? (c_last - wk.c0) / kWaves + 1 : 0;
+  wk.step = NW;
+  wk.nk = (wk.c0 <= c_last) ? (c_last - wk.c0) / NW + 1 : 0;
   wk.ppc_shift = (CH > p.page_size) ? (ilog2c(CH) - p.page_shift) : 0;
   wk.ptab = 0;
   wk.group = -1;
@@ -290,14 +281,6 @@ __global__ __launch_bounds__(kBlock) void split_kernel(const SplitParams p) {
   // pass are consecutive slots of one page, so the pass adds a scalar
   const int koff = (lane / g::LQ) * p.token_bytes + 16 * (lane % g::LQ);
   const int voff0 = (lane / g::LV) * p.token_bytes + 16 * (lane % g::LV);
-
-  KRegs<D, G> kr;
-  VRegs<D, G> vr;
-  if (wk.nk > 0) {
-    ensure_pages<CH>(wk, 0, lane, p.page_shift);
-    load_k<D, G>(kr, wk, 0, lane, kbase, p, koff);
-    load_v<D, G>(vr, wk, 0, lane, vbase, p, voff0);
-  }
 
   // q pieces, pre-permuted per lane: slot h holds head h ^ pi.
   uint4 qv[G][g::NQL];
@@ -323,7 +306,12 @@ __global__ __launch_bounds__(kBlock) void split_kernel(const SplitParams p) {
 
   const int rq = lane / g::LQ;
   for (int k = 0; k < wk.nk; ++k) {
-    const int tchunk = (wk.c0 + k * kWaves) * CH;
+    const int tchunk = (wk.c0 + k * NW) * CH;
+    KRegs<D, G> kr;
+    VRegs<D, G> vr;
+    ensure_pages<CH>(wk, k, lane, p.page_shift);
+    load_k<D, G>(kr, wk, k, lane, kbase, p, koff);
+    load_v<D, G>(vr, wk, k, lane, vbase, p, voff0);
 
     // scores of this lane's keys, then reduce-scatter over the key group
     float s_own[g::NTQ][g::VH];
@@ -347,15 +335,6 @@ __global__ __launch_bounds__(kBlock) void split_kernel(const SplitParams p) {
       const bool live = t >= wk.begin && t < wk.end;
 #pragma unroll
       for (int vh = 0; vh < g::VH; ++vh) s_own[u][vh] = live ? v[vh] * p.scale_log2 : -INFINITY;
-    }
-
-    // K registers are free: start streaming the next chunk's K now (the
-    // scheduling barriers keep the compiler from hoisting these loads above
-    // the last reads of the registers they overwrite)
-    __builtin_amdgcn_sched_barrier(0);
-    if (k + 1 < wk.nk) {
-      ensure_pages<CH>(wk, k + 1, lane, p.page_shift);
-      load_k<D, G>(kr, wk, k + 1, lane, kbase, p, koff);
     }
 
     // online softmax for the heads this lane owns; the running max of a head
@@ -411,9 +390,6 @@ __global__ __launch_bounds__(kBlock) void split_kernel(const SplitParams p) {
         for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pr[h], vf[e], acc[h][e]);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-
-    __builtin_amdgcn_sched_barrier(0);
-    if (k + 1 < wk.nk) load_v<D, G>(vr, wk, k + 1, lane, vbase, p, voff0);
   }
 
   // Wave totals: l over the key groups that own the same head, the
@@ -440,70 +416,324 @@ __global__ __launch_bounds__(kBlock) void split_kernel(const SplitParams p) {
   }
   __syncthreads();
 
-  // Merge the four waves and write the normalised partial, fp32.
-  for (int i = threadIdx.x; i < G * D; i += kBlock) {
+  // Merge the waves and write the normalised partial, fp32.
+  for (int i = threadIdx.x; i < G * D; i += NT) {
     const int h = i / D;
     const int d = i % D;
     float M = red_m[0][h];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, red_m[w][h]);
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, red_m[w][h]);
     float W = 0.0f, o = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float sc = (red_m[w][h] == -INFINITY) ? 0.0f : fast_exp2(red_m[w][h] - M);
       W += red_l[w][h] * sc;
       o += red_acc[w][h][d] * sc;
     }
-    const int64_t row = rowbase + static_cast<int64_t>(h) * p.max_parts;
-    p.part_out[row * D + d] = o / W;
-    if (d == 0) {
-      p.part_max[row] = M * kLn2;
-      p.part_sum[row] = W;
+    if (final_out) {
+      final_out[h * D + d] = f32_to_bf16_rne(o / W);
+      if (d == 0 && final_lse) final_lse[h] = M * kLn2 + __logf(W);
+    } else {
+      out[h * hstride * D + d] = o / W;
+      if (d == 0) {
+        mx[h * hstride] = M * kLn2;
+        sm[h * hstride] = W;
+      }
     }
+  }
+  __syncthreads();   // the shared buffers are reused by the block's next range
+}
+
+// Fixed partitions: block (j, gk, b) handles keys [lo + j*P, lo + (j+1)*P).
+template <int D, int G>
+__global__ __launch_bounds__(kBlock) void split_kernel(const SplitParams p) {
+  const int j = blockIdx.x;
+  const int gk = blockIdx.y;
+  const int b = blockIdx.z;
+  const int n = p.context_lens[b];
+  const int lo = p.window > 0 ? max(0, n - p.window) : 0;
+  const int64_t begin64 = static_cast<int64_t>(lo) + static_cast<int64_t>(j) * p.partition_size;
+  const int64_t rowbase = (static_cast<int64_t>(b) * p.num_q_heads + static_cast<int64_t>(gk) * G) *
+                          p.max_parts + j;   // index of (b, h = gk*G, j)
+  if (begin64 >= n) {
+    if (p.write_empty) {
+      for (int i = threadIdx.x; i < G * D; i += kBlock) {
+        const int h = i / D;
+        p.part_out[(rowbase + static_cast<int64_t>(h) * p.max_parts) * D + (i % D)] = 0.0f;
+      }
+      if (threadIdx.x < G) {
+        p.part_max[rowbase + static_cast<int64_t>(threadIdx.x) * p.max_parts] = -INFINITY;
+        p.part_sum[rowbase + static_cast<int64_t>(threadIdx.x) * p.max_parts] = 0.0f;
+      }
+    }
+    return;
+  }
+  const int end = static_cast<int>(min(begin64 + p.partition_size, static_cast<int64_t>(n)));
+  attend_range<D, G, kWaves>(p, b, gk, static_cast<int>(begin64), end, p.part_out + rowbase * D,
+                     p.part_max + rowbase, p.part_sum + rowbase, p.max_parts);
+}
+
+// ---- balanced split -----------------------------------------------------------
+//
+// Rows are (sequence b, KV head g), r = b*Hkv + g, with len_b = ctx_b - lo_b
+// attended keys; laid end to end they form T = Hkv * sum_b len_b units of work
+// (one key of one KV head).  Block i of the nb used blocks owns the units
+// [s_i, s_i+1) with s_i = floor(i*T/nb), so every block streams the same number
+// of K/V bytes whatever the mix of context lengths.  A block's share is cut at
+// row ends into segments; segment (r, i) writes its fp32 partial to slot
+// r + i, which is unique (each segment starts at the (r + i)-th boundary of
+// the merged row/block boundary sequence) and makes the slots of one row
+// contiguous, in ascending key order.  A row that lies inside one block's share
+// is written out directly by that block; the others are merged afterwards.
+// Every block, and the merge, derives the split from the context lengths
+// itself (a scan by one wave), so no plan has to be built and read back.  The
+// split points depend on the context lengths of the whole batch and on
+// nothing else (not on where pages live).
+
+__device__ __forceinline__ int64_t seq_len(const int32_t* ctx, int b, int window) {
+  const int n = ctx[b];
+  const int lo = window > 0 ? max(0, n - window) : 0;
+  return static_cast<int64_t>(n - lo);
+}
+
+__device__ __forceinline__ int64_t wave_sum64(int64_t v) {
+#pragma unroll
+  for (int w = 32; w > 0; w >>= 1) v += __shfl_xor(v, w);
+  return v;
+}
+
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ int64_t wave_scan64(int64_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int w = 1; w < 64; w <<= 1) {
+    const int64_t u = __shfl_up(v, w);
+    if (lane >= w) v += u;
+  }
+  return v;
+}
+
+// Keys (per KV head) of all sequences: sum_b len_b.  Called by a whole wave.
+__device__ __forceinline__ int64_t total_keys(const int32_t* ctx, int batch, int window) {
+  const int lane = threadIdx.x & 63;
+  int64_t s = 0;
+  for (int b0 = 0; b0 < batch; b0 += 64) s += (b0 + lane < batch) ? seq_len(ctx, b0 + lane, window) : 0;
+  return wave_sum64(s);
+}
+
+// Sequence b that holds unit x (0 <= x < T) and the keys before it, pre_b =
+// sum_{b' < b} len_b'.  Called by a whole wave; all lanes get the result.
+__device__ __forceinline__ void locate_unit(const int32_t* ctx, int batch, int window, int hkv,
+                                            int64_t x, int& b_out, int64_t& pre_out) {
+  const int lane = threadIdx.x & 63;
+  int64_t base = 0;
+  for (int b0 = 0; b0 < batch; b0 += 64) {
+    const int64_t len = (b0 + lane < batch) ? seq_len(ctx, b0 + lane, window) : 0;
+    const int64_t incl = wave_scan64(len);
+    const uint64_t hit = __ballot(hkv * (base + incl) > x);
+    if (hit) {
+      const int l = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+      b_out = b0 + l;
+      pre_out = base + __shfl(incl, l) - __shfl(len, l);
+      return;
+    }
+    base += __shfl(incl, 63);
+  }
+  b_out = batch;
+  pre_out = base;
+}
+
+// Block holding unit x: the largest i with floor(i*T/nb) <= x.
+__device__ __forceinline__ int block_of(int64_t x, int64_t T, int nb) {
+  return static_cast<int>(((x + 1) * nb - 1) / T);
+}
+
+__device__ __forceinline__ int used_blocks(int64_t T, int grid, int64_t min_units) {
+  const int64_t want = (T + min_units - 1) / min_units;
+  return static_cast<int>(want < 1 ? 1 : (want < grid ? want : grid));
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(kBlock) void balanced_split_kernel(const SplitParams p,
+                                                                const BalancedLayout bl) {
+  __shared__ int64_t sh_total;
+  __shared__ int64_t sh_pre;
+  __shared__ int sh_b;
+  const int i = blockIdx.x;
+  const int hkv = p.num_q_heads / G;
+  if (threadIdx.x < 64) {
+    const int64_t keys = total_keys(p.context_lens, bl.batch, p.window);
+    const int64_t T = keys * hkv;
+    int b = 0;
+    int64_t pre = 0;
+    if (T > 0) {
+      const int nb = used_blocks(T, gridDim.x, bl.min_units);
+      if (i < nb) locate_unit(p.context_lens, bl.batch, p.window, hkv, static_cast<int64_t>(i) * T / nb, b, pre);
+    }
+    if (threadIdx.x == 0) {
+      sh_total = T;
+      sh_b = b;
+      sh_pre = pre;
+    }
+  }
+  __syncthreads();
+  const int64_t T = sh_total;
+  if (T == 0) return;
+  const int nb = used_blocks(T, gridDim.x, bl.min_units);
+  if (i >= nb) return;
+  const int64_t s0 = static_cast<int64_t>(i) * T / nb;
+  const int64_t s1 = static_cast<int64_t>(i + 1) * T / nb;
+  int b = sh_b;
+  int64_t pre = sh_pre;                                  // keys per KV head before sequence b
+  while (b < bl.batch) {
+    const int n = p.context_lens[b];
+    const int lo = p.window > 0 ? max(0, n - p.window) : 0;
+    const int64_t len = n - lo;
+    const int64_t seq0 = pre * hkv;                      // first unit of sequence b
+    if (seq0 >= s1) break;
+    for (int gk = 0; gk < hkv && len > 0; ++gk) {
+      const int64_t off = seq0 + static_cast<int64_t>(gk) * len;   // first unit of row (b, gk)
+      if (off >= s1) break;
+      const int64_t x0 = s0 > off ? s0 : off;
+      const int64_t x1 = (s1 < off + len) ? s1 : off + len;
+      if (x1 <= x0) continue;
+      const int begin = lo + static_cast<int>(x0 - off);
+      const int end = lo + static_cast<int>(x1 - off);
+      // a row that lies inside this block's share gets its final output here
+      const bool whole = off >= s0 && off + len <= s1;
+      const int64_t slot = static_cast<int64_t>(b * hkv + gk) + i;
+      const int64_t h0 = static_cast<int64_t>(b) * p.num_q_heads + static_cast<int64_t>(gk) * G;
+      attend_range<D, G, kWaves>(p, b, gk, begin, end, bl.seg_out + slot * G * D,
+                                 bl.seg_max + slot * G, bl.seg_sum + slot * G, 1,
+                                 whole ? bl.out + h0 * D : nullptr,
+                                 (whole && bl.lse) ? bl.lse + h0 : nullptr);
+    }
+    pre += len;
+    ++b;
   }
 }
 
-// One block per (q head, sequence): M = max m_j, W = sum l_j e^(m_j - M),
-// out = sum_j (l_j e^(m_j - M) / W) o_j over live partitions, ascending j
-// within each of the block's partition groups, groups added in fixed order.
+// Merge of the fp32 partials in slots slot0 .. slot0+count-1 (ascending key
+// order) of one row, all G heads, by the whole block; writes the bf16 output
+// of head h to out + h*D and its log-sum-exp to lse[h].  Up to kBatch slots
+// are read in one go (independent loads), longer rows in rounds of kBatch.
+template <int D, int G>
+__device__ __forceinline__ void merge_segments(const BalancedLayout& bl, int64_t slot0, int count,
+                                               uint16_t* out, float* lse) {
+  constexpr int kBatch = 16;
+  for (int i = threadIdx.x; i < G * D; i += kBlock) {
+    const int h = i / D;
+    const int d = i % D;
+    const float* pm = bl.seg_max + slot0 * G + h;
+    const float* pl = bl.seg_sum + slot0 * G + h;
+    const float* po = bl.seg_out + (slot0 * G + h) * D + d;
+    float M = -INFINITY;
+    for (int k0 = 0; k0 < count; k0 += kBatch) {
+      float mk[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) mk[k] = (k0 + k < count) ? pm[(k0 + k) * G] : -INFINITY;
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) M = fmaxf(M, mk[k]);
+    }
+    float W = 0.0f, o = 0.0f;
+    for (int k0 = 0; k0 < count; k0 += kBatch) {
+      float wk[kBatch], ok[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const bool in = k0 + k < count;
+        wk[k] = in ? pl[(k0 + k) * G] * __expf(pm[(k0 + k) * G] - M) : 0.0f;
+        ok[k] = in ? po[static_cast<int64_t>(k0 + k) * G * D] : 0.0f;
+      }
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) W += wk[k];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) o = fmaf(wk[k], ok[k], o);
+    }
+    out[h * D + d] = f32_to_bf16_rne(o / W);
+    if (d == 0 && lse) lse[h] = M + __logf(W);
+  }
+}
+
+// One block per row (b, g): rows with no key get zeros and lse -inf, rows
+// that one block covered are already written, the rest are merged here.
+template <int D, int G>
+__global__ __launch_bounds__(kBlock) void balanced_merge_kernel(const BalancedLayout bl,
+                                                               int num_q_heads, int window,
+                                                               int split_grid) {
+  __shared__ int64_t sh_total, sh_pre;
+  const int r = blockIdx.x;
+  const int hkv = num_q_heads / G;
+  const int b = r / hkv;
+  const int gk = r - b * hkv;
+  if (threadIdx.x < 64) {
+    const int64_t T = total_keys(bl.context_lens, bl.batch, window) * hkv;
+    int64_t pre = 0;
+    const int lane = threadIdx.x & 63;
+    for (int b0 = 0; b0 < b; b0 += 64)
+      pre += (b0 + lane < b) ? seq_len(bl.context_lens, b0 + lane, window) : 0;
+    pre = wave_sum64(pre);
+    if (threadIdx.x == 0) {
+      sh_total = T;
+      sh_pre = pre;
+    }
+  }
+  __syncthreads();
+  const int64_t T = sh_total;
+  const int64_t len = seq_len(bl.context_lens, b, window);
+  const int64_t h0 = static_cast<int64_t>(b) * num_q_heads + static_cast<int64_t>(gk) * G;
+  if (len == 0) {
+    for (int i = threadIdx.x; i < G * D; i += kBlock) bl.out[h0 * D + i] = 0;
+    if (bl.lse && threadIdx.x < G) bl.lse[h0 + threadIdx.x] = -INFINITY;
+    return;
+  }
+  const int nb = used_blocks(T, split_grid, bl.min_units);
+  const int64_t off = sh_pre * hkv + static_cast<int64_t>(gk) * len;
+  const int i0 = block_of(off, T, nb);
+  const int i1 = block_of(off + len - 1, T, nb);
+  if (i1 == i0) return;                       // written by the split kernel
+  merge_segments<D, G>(bl, static_cast<int64_t>(r) + i0, i1 - i0 + 1, bl.out + h0 * D,
+                       bl.lse ? bl.lse + h0 : nullptr);
+}
+
+// ---- merge -----------------------------------------------------------------------
+
+// Where the partials of one (sequence, q head) live.
+struct FixedSlots {      // partition j at row*max_parts + j
+  const float* po; const float* pm; const float* pl;
+  int count;
+  __device__ int64_t idx(int k) const { return k; }
+};
+
+// One block per (q head, sequence): M = max m_k, W = sum l_k e^(m_k - M),
+// out = sum_k (l_k e^(m_k - M) / W) o_k over the partials k of the row, in
+// ascending k within each of the block's partition groups, the groups added
+// in fixed order.  `stride` is the distance between consecutive partials in
+// elements of m/l (times D for o).
 template <int D>
-__global__ __launch_bounds__(kBlock) void merge_kernel(const MergeParams p) {
+__device__ __forceinline__ void merge_row(const float* pm, const float* pl, const float* po,
+                                          int64_t stride, int count, uint16_t* out, float* lse) {
   constexpr int TPR = D / 4;                  // threads per row (float4 each)
   constexpr int NGRP = kBlock / TPR;          // partition groups per block
-  __shared__ float red[kBlock];
+  __shared__ float red[kWaves];
   __shared__ float4 part[NGRP][TPR];
 
-  const int h = blockIdx.x;
-  const int b = blockIdx.y;
-  const int n = p.context_lens[b];
-  const int lo = p.window > 0 ? max(0, n - p.window) : 0;
-  const int live = (n > lo) ? static_cast<int>((static_cast<int64_t>(n - lo) + p.partition_size - 1) /
-                                               p.partition_size)
-                            : 0;
-  const int64_t row = static_cast<int64_t>(b) * p.num_q_heads + h;
-  const float* pm = p.part_max + row * p.max_parts;
-  const float* pl = p.part_sum + row * p.max_parts;
-  const float* po = p.part_out + row * p.max_parts * D;
-
-  // M over live partitions
   float M = -INFINITY;
-  for (int jj = threadIdx.x; jj < live; jj += kBlock) M = fmaxf(M, pm[jj]);
+  for (int jj = threadIdx.x; jj < count; jj += kBlock) M = fmaxf(M, pm[jj * stride]);
   M = wave_max(M);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = M;
   __syncthreads();
   M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   __syncthreads();
 
-  uint16_t* out = p.out + row * D;
-  if (live == 0 || M == -INFINITY) {
+  if (count == 0 || M == -INFINITY) {
     for (int d = threadIdx.x; d < D; d += kBlock) out[d] = 0;
-    if (p.lse && threadIdx.x == 0) p.lse[row] = -INFINITY;
+    if (lse && threadIdx.x == 0) *lse = -INFINITY;
     return;
   }
   float W = 0.0f;
-  for (int jj = threadIdx.x; jj < live; jj += kBlock) {
-    const float mj = pm[jj];
-    const float lj = pl[jj];
+  for (int jj = threadIdx.x; jj < count; jj += kBlock) {
+    const float mj = pm[jj * stride];
+    const float lj = pl[jj * stride];
     if (mj != -INFINITY && lj != 0.0f) W += lj * __expf(mj - M);
   }
   W = wave_sum(W);
@@ -514,12 +744,12 @@ __global__ __launch_bounds__(kBlock) void merge_kernel(const MergeParams p) {
   const int grp = threadIdx.x / TPR;
   const int d4 = threadIdx.x % TPR;
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int jj = grp; jj < live; jj += NGRP) {
-    const float mj = pm[jj];
-    const float lj = pl[jj];
+  for (int jj = grp; jj < count; jj += NGRP) {
+    const float mj = pm[jj * stride];
+    const float lj = pl[jj * stride];
     if (mj == -INFINITY || lj == 0.0f) continue;
     const float w = lj * __expf(mj - M) / W;
-    const float4 o = reinterpret_cast<const float4*>(po + static_cast<int64_t>(jj) * D)[d4];
+    const float4 o = reinterpret_cast<const float4*>(po + jj * stride * D)[d4];
     a.x = fmaf(w, o.x, a.x);
     a.y = fmaf(w, o.y, a.y);
     a.z = fmaf(w, o.z, a.z);
@@ -539,7 +769,23 @@ __global__ __launch_bounds__(kBlock) void merge_kernel(const MergeParams p) {
     packed.y = static_cast<uint32_t>(f32_to_bf16_rne(t.z)) | (static_cast<uint32_t>(f32_to_bf16_rne(t.w)) << 16);
     reinterpret_cast<uint2*>(out)[d4] = packed;
   }
-  if (p.lse && threadIdx.x == 0) p.lse[row] = M + __logf(W);
+  if (lse && threadIdx.x == 0) *lse = M + __logf(W);
+}
+
+// Fixed partitions: live partitions j < ceil((ctx - lo) / P).
+template <int D>
+__global__ __launch_bounds__(kBlock) void merge_kernel(const MergeParams p) {
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const int n = p.context_lens[b];
+  const int lo = p.window > 0 ? max(0, n - p.window) : 0;
+  const int live = (n > lo) ? static_cast<int>((static_cast<int64_t>(n - lo) + p.partition_size - 1) /
+                                               p.partition_size)
+                            : 0;
+  const int64_t row = static_cast<int64_t>(b) * p.num_q_heads + h;
+  merge_row<D>(p.part_max + row * p.max_parts, p.part_sum + row * p.max_parts,
+               p.part_out + row * p.max_parts * D, 1, live, p.out + row * D,
+               p.lse ? p.lse + row : nullptr);
 }
 
 // ---- launchers -----------------------------------------------------------------
@@ -550,6 +796,30 @@ static hipError_t launch_split_dg(const SplitParams& p, int batch, int num_kv_he
   dim3 grid(p.max_parts, num_kv_heads, batch);
   hipLaunchKernelGGL((split_kernel<D, G>), grid, dim3(kBlock), 0, stream, p);
   return hipGetLastError();
+}
+
+template <int D, int G>
+static hipError_t launch_balanced_dg(const SplitParams& p, const BalancedLayout& bl, int grid,
+                                     hipStream_t stream) {
+  hipLaunchKernelGGL((balanced_split_kernel<D, G>), dim3(grid), dim3(kBlock), 0, stream, p, bl);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((balanced_merge_kernel<D, G>), dim3(bl.rows), dim3(kBlock), 0, stream, bl,
+                     p.num_q_heads, p.window, grid);
+  return hipGetLastError();
+}
+
+template <int D, int G>
+static int blocks_per_cu() {
+  static int cached = -1;
+  if (cached < 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, balanced_split_kernel<D, G>, kBlock, 0) !=
+            hipSuccess || n < 1)
+      n = 1;
+    cached = n;
+  }
+  return cached;
 }
 
 template <int D>
@@ -584,6 +854,56 @@ hipError_t launch_merge(const MergeParams& p, int head_dim, int batch, hipStream
     return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int D, int G>
+static int balanced_blocks(int num_cus, int max_blocks) {
+  const int n = blocks_per_cu<D, G>() * num_cus;
+  return n < max_blocks ? n : max_blocks;
+}
+
+// Blocks the balanced split would use on this device (occupancy x CUs, capped).
+int balanced_grid(int head_dim, int group, int num_cus, int max_blocks) {
+  if (head_dim == 128) {
+    switch (group) {
+      case 1: return balanced_blocks<128, 1>(num_cus, max_blocks);
+      case 2: return balanced_blocks<128, 2>(num_cus, max_blocks);
+      case 4: return balanced_blocks<128, 4>(num_cus, max_blocks);
+      case 8: return balanced_blocks<128, 8>(num_cus, max_blocks);
+      case 16: return balanced_blocks<128, 16>(num_cus, max_blocks);
+    }
+  } else if (head_dim == 256) {
+    switch (group) {
+      case 1: return balanced_blocks<256, 1>(num_cus, max_blocks);
+      case 2: return balanced_blocks<256, 2>(num_cus, max_blocks);
+      case 4: return balanced_blocks<256, 4>(num_cus, max_blocks);
+      case 8: return balanced_blocks<256, 8>(num_cus, max_blocks);
+    }
+  }
+  return 0;
+}
+
+// Balanced split, then the merge of the rows several blocks shared: the whole
+// of pa_decode.
+hipError_t launch_balanced(const SplitParams& sp, const BalancedLayout& bl, int head_dim, int group,
+                           int grid, hipStream_t stream) {
+  if (head_dim == 128) {
+    switch (group) {
+      case 1: return launch_balanced_dg<128, 1>(sp, bl, grid, stream);
+      case 2: return launch_balanced_dg<128, 2>(sp, bl, grid, stream);
+      case 4: return launch_balanced_dg<128, 4>(sp, bl, grid, stream);
+      case 8: return launch_balanced_dg<128, 8>(sp, bl, grid, stream);
+      case 16: return launch_balanced_dg<128, 16>(sp, bl, grid, stream);
+    }
+  } else if (head_dim == 256) {
+    switch (group) {
+      case 1: return launch_balanced_dg<256, 1>(sp, bl, grid, stream);
+      case 2: return launch_balanced_dg<256, 2>(sp, bl, grid, stream);
+      case 4: return launch_balanced_dg<256, 4>(sp, bl, grid, stream);
+      case 8: return launch_balanced_dg<256, 8>(sp, bl, grid, stream);
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pa

@@ -45,4 +45,17 @@ struct MergeParams {
   int32_t window;
 };
 
+// Device buffers of the balanced split and its merge.
+struct BalancedLayout {
+  const int32_t* context_lens;
+  uint16_t* out;         // [batch][num_q_heads][D] bf16
+  float* lse;            // [batch][num_q_heads] or NULL
+  float* seg_out;        // [(rows + grid) * G][D]  partial of segment slot s, head h at s*G + h
+  float* seg_max;        // [(rows + grid) * G]
+  float* seg_sum;
+  int64_t min_units;     // a block owns at least this many units (keys of one KV head)
+  int32_t rows;          // batch * num_kv_heads
+  int32_t batch;
+};
+
 }  // namespace pa

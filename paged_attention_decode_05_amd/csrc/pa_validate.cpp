@@ -73,6 +73,9 @@ int check_gqa(const void* q, const void* k_pool, const void* v_pool, const pa_kv
     return fail(PA_ERR_SHAPE, "token_stride must be >= head_dim");
   if (static_cast<int64_t>(kv->page_size - 1) * kv->token_stride + kv->head_dim > INT32_MAX / 4)
     return fail(PA_ERR_SHAPE, "token_stride too large");
+  if (static_cast<double>(batch) * kv->num_kv_heads *
+          static_cast<double>(max_keys(max_pages_per_seq, kv->page_size, 0)) > 1e15)
+    return fail(PA_ERR_SHAPE, "batch * num_kv_heads * max keys is too large");
   if (kv->page_stride > static_cast<int64_t>(UINT32_MAX / 2) ||
       kv->head_stride > static_cast<int64_t>(UINT32_MAX / 2))
     return fail(PA_ERR_SHAPE, "page_stride and head_stride must stay below 2^31 elements");
@@ -118,16 +121,15 @@ int check_merge(const float* part_out, const float* part_max, const float* part_
   return PA_OK;
 }
 
-// Partition size for pa_decode.  Aim at about 4096 work items of (sequence,
-// KV head, partition) when contexts average half the maximum, but never below
-// 256 keys for head_dim 128 (128 for 256): a partition's fp32 partial output
-// (group * (head_dim + 2) floats) must stay small next to the K/V bytes it
-// summarises.  Depends on host-known shapes only.
-bool plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                 int32_t max_pages_per_seq, int32_t page_size, int32_t window, DecodePlan* plan) {
-  if (batch < 1 || num_q_heads < 1 || num_kv_heads < 1 || max_pages_per_seq < 1 ||
-      page_size < 1 || !head_dim_supported(head_dim) || num_q_heads % num_kv_heads)
-    return false;
+// Partition size suggested for the two-stage API: about 4096 work items of
+// (sequence, KV head, partition) when contexts average half the maximum, at
+// least 256 keys for head_dim 128 (128 for 256) so a partition's fp32 partial
+// output stays small next to the K/V bytes it summarises.
+int32_t suggest_partition(int32_t batch, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t max_pages_per_seq, int32_t page_size, int32_t window) {
+  if (batch < 1 || num_kv_heads < 1 || max_pages_per_seq < 1 || page_size < 1 ||
+      !head_dim_supported(head_dim))
+    return 0;
   const int64_t keys = max_keys(max_pages_per_seq, page_size, window);
   const int64_t work = static_cast<int64_t>(batch) * num_kv_heads * keys;
   int64_t p = 1;
@@ -135,13 +137,22 @@ bool plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32
   const int64_t pmin = head_dim == 128 ? 256 : 128;
   if (p < pmin) p = pmin;
   if (p > 4096) p = 4096;
-  plan->partition_size = static_cast<int32_t>(p);
-  plan->max_partitions = static_cast<int32_t>(ceil_div(keys, p));
-  const size_t rows = static_cast<size_t>(batch) * num_q_heads * plan->max_partitions;
-  plan->off_out = 0;
-  plan->off_max = round_up(rows * head_dim * sizeof(float), 256);
-  plan->off_sum = plan->off_max + round_up(rows * sizeof(float), 256);
-  plan->bytes = plan->off_sum + round_up(rows * sizeof(float), 256);
+  return static_cast<int32_t>(p);
+}
+
+bool plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                 int32_t max_pages_per_seq, int32_t page_size, int32_t window, DecodePlan* plan) {
+  if (batch < 1 || num_q_heads < 1 || num_kv_heads < 1 || max_pages_per_seq < 1 ||
+      page_size < 1 || !head_dim_supported(head_dim) || num_q_heads % num_kv_heads)
+    return false;
+  plan->rows = batch * num_kv_heads;
+  plan->group = num_q_heads / num_kv_heads;
+  const size_t slots = static_cast<size_t>(plan->rows) + kMaxBalancedBlocks;
+  size_t o = 0;
+  plan->off_seg_out = o;    o += round_up(slots * plan->group * head_dim * sizeof(float), 256);
+  plan->off_seg_max = o;    o += round_up(slots * plan->group * sizeof(float), 256);
+  plan->off_seg_sum = o;    o += round_up(slots * plan->group * sizeof(float), 256);
+  plan->bytes = o;
   return true;
 }
 

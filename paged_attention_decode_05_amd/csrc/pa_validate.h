@@ -39,15 +39,23 @@ int check_merge(const float* part_out, const float* part_max, const float* part_
                 const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
                 int32_t head_dim, int32_t partition_size, int32_t max_partitions, const void* out);
 
-// Launch plan of pa_decode: partition size and workspace carve-up, a pure
-// function of host-known shapes.
+// Workspace carve-up of pa_decode (balanced split): the segment partials,
+// one slot per (row, block) segment, rows + kMaxBalancedBlocks slots in all.
+constexpr int32_t kMaxBalancedBlocks = 2048;
+constexpr int64_t kMinUnitsPerBlock = 512;   // keys (of one KV head) below which a block is not worth it
+
 struct DecodePlan {
-  int32_t partition_size = 0;
-  int32_t max_partitions = 0;
-  size_t off_out = 0, off_max = 0, off_sum = 0, bytes = 0;
+  int32_t rows = 0;          // batch * num_kv_heads
+  int32_t group = 0;
+  size_t off_seg_out = 0, off_seg_max = 0, off_seg_sum = 0, bytes = 0;
 };
 bool plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                  int32_t max_pages_per_seq, int32_t page_size, int32_t window, DecodePlan* plan);
+
+// Fixed partition size used by pa_decode_partition_size (the two-stage API's
+// suggestion for these shapes).
+int32_t suggest_partition(int32_t batch, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t max_pages_per_seq, int32_t page_size, int32_t window);
 
 // MLA geometry fixed by the absorbed-MLA entry point.
 constexpr int32_t kMlaNope = 128;
