@@ -3,8 +3,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama]
 
-One step = one pa_decode call (plan kernel + balanced split-KV kernel + LSE
-merge kernel)
+One step = one pa_decode call (balanced split-KV kernel + LSE merge kernel)
 over one batch of the synthetic workload, inputs resident in HBM.  The timed
 region is bracketed by torch.cuda.synchronize() on both sides and measured
 with HIP events on the stream the kernels are launched on (torch's current
@@ -13,9 +12,13 @@ stream, whose handle is passed through the C ABI).
 value = algorithmic K+V bytes per call / mean time per call  (GB/s, 1e9 B/s)
   algorithmic bytes = sum over sequences of attended keys * 2 (K and V)
                       * num_kv_heads * head_dim * 2 B
-roofline: the same bytes / the mean duration of one pa_decode call (plan
-  kernel + balanced split-KV kernel + merge kernel), from HIP events around
-  each of K calls on the launch stream; the rocprofv3 kernel trace splits it.
+roofline: the same bytes / the mean duration of one pa_decode call (balanced
+  split-KV kernel + merge kernel), from HIP events around each of K calls on
+  the launch stream; the rocprofv3 kernel trace splits it.
+
+--workload mla times mla_absorbed_decode on the 128-head latent workload
+instead (absorb + split + merge/W_UV kernels); its bytes are the latent rows
+read plus W_UK, W_UV, q and out, and its flops the four contractions.
 cpu_baseline: the CPU oracle (float64, the parity reference) on the whole
   workload, all host threads, on the same byte definition.
 
@@ -47,7 +50,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="llama", choices=["tiny", "llama", "d256w", "long"])
+    ap.add_argument("--workload", default="llama", choices=["tiny", "llama", "d256w", "long", "mla"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--rotate", type=int, default=1,
                     help="input sets to rotate through (for workloads that fit in the 256 MB "
@@ -72,6 +75,8 @@ def main() -> int:
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
 
+    if a.workload == "mla":
+        return bench_mla(a, torch, pb, wl, dev)
     log(f"generating workload {a.workload} (seeded) ...")
     t0 = time.time()
     cases = [wl.NAMED[a.workload](poison=False, seed=wl.SEED_BASE + 100 * i + {
@@ -168,9 +173,94 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": None,
-            "kernel": "pa_decode call: plan_kernel + balanced_split_kernel + balanced_merge_kernel",
+            "kernel": "pa_decode call: balanced_split_kernel + balanced_merge_kernel",
             "algorithmic_bytes_per_launch": int(mean_bytes),
         },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def _time_calls(torch, stream, step, steps):
+    """Mean per-call ms from HIP events around each call on the launch stream,
+    plus the list of per-call times."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = [e[0].elapsed_time(e[1]) for e in ev]
+    return statistics.fmean(ms), ms
+
+
+def bench_mla(a, torch, pb, wl, dev) -> int:
+    log("generating workload mla (seeded) ...")
+    case = wl.mla(poison=False)
+    dc = case.to(dev)
+    B, H = case.batch, case.num_heads
+    out = torch.empty((B, H, case.d_v), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(pb.mla_absorbed_decode_workspace_size(B, H, case.max_pages, case.page_size, 0),
+                     dtype=torch.uint8, device=dev)
+    layout = pb.kv_layout(dc.cache, "PSR")
+
+    def step(i):
+        pb.mla_absorbed_decode(dc.q_nope, dc.q_rope, dc.cache, layout, dc.w_uk, dc.w_uv,
+                               dc.block_table, dc.context_lens, dc.scale, out, ws)
+
+    stream = torch.cuda.current_stream()
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(a.steps):
+        step(i)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(stop) / a.steps
+    call_mean, call_ms = _time_calls(torch, stream, step, a.steps)
+    nbytes = case.algorithmic_bytes()
+    keys = int(case.context_lens.sum())
+    flops = 2 * B * H * case.d_nope * case.d_lat + 2 * H * keys * (case.d_lat + case.d_rope) \
+        + 2 * H * keys * case.d_lat + 2 * B * H * case.d_lat * case.d_v
+    gbs = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (call_mean * 1e-3) / 1e9
+    cpu = None
+    if not a.no_cpu:
+        from oracle.oracle import Oracle
+        o = Oracle()
+        threads = max(1, min(len(os.sched_getaffinity(0)),
+                             int(os.environ.get("OMP_NUM_THREADS", "16") or 16)))
+        o.set_threads(threads)
+        t = time.time()
+        o.mla(case, "f64")
+        sec = time.time() - t
+        cpu = {"value": round(nbytes / sec / 1e9, 3), "unit": "GB/s", "cores": threads,
+               "kind": "oracle", "sample": f"whole workload ({B} seqs, {keys} keys), float64 "
+                                           "oracle, one run", "seconds_per_call": round(sec, 3)}
+    res = {
+        "metric": "absorbed-MLA decode µs/call + latent GB/s, bs16 h128",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms_per_step, 5),
+        "us_per_call": round(ms_per_step * 1e3, 2),
+        "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "storage_dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "absorbed MLA decode, bs16, 128 heads, 512+64 latent, page 64, "
+                               "ctx U[1024,8192]", "sum_context": keys,
+                   "algorithmic_bytes": nbytes, "algorithmic_flops": flops},
+        "call_us": {"mean": round(call_mean * 1e3, 2),
+                    "p10": round(sorted(call_ms)[len(call_ms) // 10] * 1e3, 2),
+                    "p90": round(sorted(call_ms)[(9 * len(call_ms)) // 10] * 1e3, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "mla_absorbed_decode call: absorb + split + merge/W_UV kernels",
+                     "algorithmic_bytes_per_launch": nbytes,
+                     "mfma_tflops": round(flops / (call_mean * 1e-3) / 1e12, 2)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

@@ -137,15 +137,26 @@ PA_API int pa_merge_lse(const float* part_out, const float* part_max,
                  int32_t window, void* out, float* lse_out, void* stream);
 
 /* ---------------------------------------------------------------------------
- * pa_decode -- complete decode attention: pa_decode_splitkv followed by
- * pa_merge_lse, with the partition size chosen from host-known shapes only
- * (batch, heads, head_dim, max_pages_per_seq, page_size, window), so the
- * result never depends on the device-side context lengths' values.
+ * pa_decode -- complete decode attention: the result pa_decode_splitkv +
+ * pa_merge_lse define, with a balanced split instead of fixed partitions.
+ *
+ * The attended keys of the whole batch, counted once per KV head (rows
+ * (b, kv head) laid end to end), are cut into equal contiguous ranges, one
+ * per workgroup, so every workgroup reads the same number of K/V bytes
+ * whatever the length mix [vllm.cpp kernel matrix, row
+ * KERNEL-ATTN-MLA-SPARSE, W4: split-KV with a fixed, ordered merge].  A row
+ * that one range covers is written directly; a row cut by range boundaries
+ * gets one partial per piece, merged in ascending order as in pa_merge_lse.
+ * The cut points are computed on the device from context_lens, so a row's
+ * result may differ in the last bits when other sequences' lengths change;
+ * for fixed inputs the result is deterministic run to run and does not
+ * depend on where the pages sit in the pool.
  *
  * out [batch][num_q_heads][head_dim] bf16; lse_out [batch][num_q_heads] fp32
- * or NULL.  workspace: device memory of at least
- * pa_decode_workspace_size(...) bytes, 256-byte aligned, owned by the caller
- * and clobbered by the call (no state is kept between calls).
+ * (natural log of the softmax denominator, -inf for an empty row) or NULL.
+ * workspace: device memory of at least pa_decode_workspace_size(...) bytes,
+ * 256-byte aligned, owned by the caller and clobbered by the call (no state
+ * is kept between calls).
  * ------------------------------------------------------------------------- */
 PA_API int pa_decode(const void* q, const void* k_pool, const void* v_pool,
               const pa_kv_layout* kv, const int32_t* block_table,
@@ -160,7 +171,8 @@ PA_API size_t pa_decode_workspace_size(int32_t batch, int32_t num_q_heads,
                                 int32_t max_pages_per_seq, int32_t page_size,
                                 int32_t window);
 
-/* Partition size pa_decode uses for these shapes (0 on invalid shapes). */
+/* Partition size suggested for pa_decode_splitkv / pa_merge_lse with these
+ * shapes (0 on invalid shapes); pa_decode itself splits by balanced ranges. */
 PA_API int32_t pa_decode_partition_size(int32_t batch, int32_t num_q_heads,
                                  int32_t num_kv_heads, int32_t head_dim,
                                  int32_t max_pages_per_seq, int32_t page_size,
@@ -179,7 +191,12 @@ PA_API int32_t pa_decode_partition_size(int32_t batch, int32_t num_q_heads,
  *   s_t       = scale * (q_abs . c_t[0:512] + q_rope[b][h] . c_t[512:576])
  *   o_lat[j]  = sum_t softmax(s)_t * c_t[j]
  *   out[b][h][dv] = bf16( sum_j w_uv[h][dv][j] * o_lat[j] )    (dv < 128)
- * with every intermediate kept at (near-)fp32 precision.
+ * q_abs, the probabilities and o_lat are fp32; they enter the bf16 matrix
+ * products as three bf16 terms that sum to the fp32 value exactly, so only
+ * fp32 accumulation rounds.  Keys are split into partitions of
+ * partition_size (one workgroup per sequence, 64 heads and partition), merged
+ * by log-sum-exp in ascending partition order; an empty context gives 0.
+ * Deterministic run to run and independent of page placement.
  *
  * q_nope [batch][num_heads][128] bf16; q_rope [batch][num_heads][64] bf16;
  * kv_cache: pool described by *cache (num_kv_heads 1, head_dim 576,
@@ -188,7 +205,11 @@ PA_API int32_t pa_decode_partition_size(int32_t batch, int32_t num_q_heads,
  * num_heads must be a multiple of 16.  partition_size: keys per split
  * (multiple of 64, or 0 to let the library choose from host-known shapes).
  * workspace: at least mla_absorbed_decode_workspace_size(...) bytes,
- * 256-byte aligned, clobbered by the call.
+ * 256-byte aligned, clobbered by the call.  Device-side contract as for
+ * pa_decode: 0 <= context_lens[b] <= max_pages_per_seq * page_size and the
+ * block_table entries a sequence uses lie in [0, num_pages).
+ * Returns PA_OK, or an error code with pa_last_error() set; nothing is
+ * launched on error.
  * ------------------------------------------------------------------------- */
 PA_API int mla_absorbed_decode(const void* q_nope, const void* q_rope,
                         const void* kv_cache, const pa_kv_layout* cache,

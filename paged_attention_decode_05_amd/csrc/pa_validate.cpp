@@ -156,8 +156,11 @@ bool plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32
   return true;
 }
 
-// MLA split plan: partition size a multiple of the 64-key granule; by default
-// about 2 * 256 work items of (sequence, head tile, partition).
+// MLA split plan: partition size a multiple of the 64-key granule.  The
+// split kernel runs one block per (sequence, group of 64 heads, partition);
+// by default the partition is the smallest power of two from 64 keys up that
+// keeps the longest sequence at no more than about 2048 / (batch * groups)
+// blocks, so a full batch covers the 256 CUs a few times over.
 bool plan_mla(int32_t batch, int32_t num_heads, int32_t max_pages_per_seq, int32_t page_size,
               int32_t partition_size, MlaPlan* plan) {
   if (batch < 1 || num_heads < 1 || num_heads % kMlaHeadTile || max_pages_per_seq < 1 ||
@@ -166,20 +169,23 @@ bool plan_mla(int32_t batch, int32_t num_heads, int32_t max_pages_per_seq, int32
   const int64_t keys = static_cast<int64_t>(max_pages_per_seq) * page_size;
   int64_t p = partition_size;
   if (p == 0) {
-    const int64_t tiles = static_cast<int64_t>(batch) * (num_heads / kMlaHeadTile);
+    const int64_t groups = static_cast<int64_t>(batch) * ceil_div(num_heads, kMlaBlockHeads);
     p = kMlaKeyTile;
-    while (tiles * ceil_div(keys, p) / 2 > 512 && p < 8192) p *= 2;
+    while (groups * ceil_div(keys, p) > 2048 && p < 8192) p *= 2;
   }
   plan->partition_size = static_cast<int32_t>(p);
   plan->max_partitions = static_cast<int32_t>(ceil_div(keys, p));
+  if (plan->max_partitions > 65535) return false;
   const size_t bh = static_cast<size_t>(batch) * num_heads;
   const size_t rows = bh * plan->max_partitions;
-  plan->off_qabs = 0;                                               // q_abs hi/lo, bf16 [B][H][576][2]
-  plan->off_out = round_up(bh * kMlaRow * 2 * sizeof(uint16_t), 256);
-  plan->off_max = plan->off_out + round_up(rows * kMlaLat * sizeof(float), 256);
-  plan->off_sum = plan->off_max + round_up(rows * sizeof(float), 256);
-  plan->off_lat = plan->off_sum + round_up(rows * sizeof(float), 256);  // merged o_lat fp32 [B][H][512]
-  plan->bytes = plan->off_lat + round_up(bh * kMlaLat * sizeof(float), 256);
+  size_t o = 0;
+  plan->off_qhi = o;  o += round_up(bh * kMlaRow * sizeof(uint16_t), 256);   // q_abs|q_rope, bf16 hi
+  plan->off_qmid = o; o += round_up(bh * kMlaLat * sizeof(uint16_t), 256);   // q_abs, bf16 mid
+  plan->off_qlo = o;  o += round_up(bh * kMlaLat * sizeof(uint16_t), 256);   // q_abs, bf16 lo
+  plan->off_out = o;  o += round_up(rows * kMlaLat * sizeof(float), 256);    // partial o_lat
+  plan->off_max = o;  o += round_up(rows * sizeof(float), 256);
+  plan->off_sum = o;  o += round_up(rows * sizeof(float), 256);
+  plan->bytes = o;
   return true;
 }
 

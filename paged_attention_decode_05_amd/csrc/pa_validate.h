@@ -65,11 +65,12 @@ constexpr int32_t kMlaRow = kMlaLat + kMlaRope;  // 576
 constexpr int32_t kMlaDv = 128;
 constexpr int32_t kMlaHeadTile = 16;             // heads per MFMA tile
 constexpr int32_t kMlaKeyTile = 64;              // keys per split granule
+constexpr int32_t kMlaBlockHeads = 64;           // heads per split-kernel block
 
 struct MlaPlan {
   int32_t partition_size = 0;
   int32_t max_partitions = 0;
-  size_t off_qabs = 0, off_out = 0, off_max = 0, off_sum = 0, off_lat = 0, bytes = 0;
+  size_t off_qhi = 0, off_qmid = 0, off_qlo = 0, off_out = 0, off_max = 0, off_sum = 0, bytes = 0;
 };
 bool plan_mla(int32_t batch, int32_t num_heads, int32_t max_pages_per_seq, int32_t page_size,
               int32_t partition_size, MlaPlan* plan);

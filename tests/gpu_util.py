@@ -56,3 +56,19 @@ def run_merge(po, pm, ps, context_lens, partition_size, window):
     pb.pa_merge_lse(po, pm, ps, context_lens, partition_size, window, out, lse)
     torch.cuda.synchronize()
     return out.cpu(), lse.cpu()
+
+
+def run_mla(dc, partition_size=0, workspace=None, out=None):
+    B, H = dc.q_nope.shape[0], dc.q_nope.shape[1]
+    if out is None:
+        out = torch.full((B, H, dc.d_v), float("nan"), dtype=torch.bfloat16, device="cuda")
+    if workspace is None:
+        nbytes = pb.mla_absorbed_decode_workspace_size(B, H, dc.max_pages, dc.page_size,
+                                                       partition_size)
+        assert nbytes > 0
+        workspace = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")   # NaN fill
+    pb.mla_absorbed_decode(dc.q_nope, dc.q_rope, dc.cache, pb.kv_layout(dc.cache, "PSR"),
+                           dc.w_uk, dc.w_uv, dc.block_table, dc.context_lens, dc.scale, out,
+                           workspace, partition_size=partition_size)
+    torch.cuda.synchronize()
+    return out.cpu()
