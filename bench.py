@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama", choices=["tiny", "llama", "d256w", "long", "mla"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run K device-to-device copies of a 1 GiB buffer instead (reference "
+                         "kernel of known traffic for the HBM byte counters); prints one JSON line")
     ap.add_argument("--rotate", type=int, default=1,
                     help="input sets to rotate through (for workloads that fit in the 256 MB "
                          "Infinity Cache)")
@@ -75,6 +78,15 @@ def main() -> int:
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
 
+    if a.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(a.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": a.steps}), flush=True)
+        return 0
     if a.workload == "mla":
         return bench_mla(a, torch, pb, wl, dev)
     log(f"generating workload {a.workload} (seeded) ...")
@@ -172,7 +184,7 @@ def main() -> int:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": recorded_traffic("pa_decode_llama_bs64") if a.workload == "llama" and a.rotate == 1 else None,
             "kernel": "pa_decode call: balanced_split_kernel + balanced_merge_kernel",
             "algorithmic_bytes_per_launch": int(mean_bytes),
         },
@@ -180,6 +192,31 @@ def main() -> int:
     }
     print(json.dumps(res), flush=True)
     return 0
+
+
+def recorded_traffic(profile: str):
+    """HBM bytes per call from the PMC summary profiles/<profile>.md (FETCH_SIZE
+    and WRITE_SIZE scaled by a 1 GiB copy), or None when the kernel sources
+    it lists have changed since the counters were taken."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", profile + ".md")
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    m_t = re.search(r"^traffic_bytes_per_call: (\d+)$", text, re.M)
+    m_s = re.search(r"^sources: (.+)$", text, re.M)
+    m_h = re.search(r"^sources_sha256: ([0-9a-f]{64})$", text, re.M)
+    if not (m_t and m_s and m_h):
+        return None
+    h = hashlib.sha256()
+    for f in m_s.group(1).split():
+        try:
+            h.update(open(os.path.join(ROOT, "paged_attention_decode_05_amd", "csrc", f), "rb").read())
+        except OSError:
+            return None
+    return int(m_t.group(1)) if h.hexdigest() == m_h.group(1) else None
 
 
 def _time_calls(torch, stream, step, steps):

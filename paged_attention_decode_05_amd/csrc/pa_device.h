@@ -84,4 +84,35 @@ __device__ __forceinline__ uint4 load16(const uint16_t* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
+// ---- balanced splits: T units cut into nb equal contiguous ranges ----------
+// Block i owns units [floor(i*T/nb), floor((i+1)*T/nb)).
+
+__device__ __forceinline__ int64_t wave_sum64(int64_t v) {
+#pragma unroll
+  for (int w = 32; w > 0; w >>= 1) v += __shfl_xor(v, w);
+  return v;
+}
+
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ int64_t wave_scan64(int64_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int w = 1; w < 64; w <<= 1) {
+    const int64_t u = __shfl_up(v, w);
+    if (lane >= w) v += u;
+  }
+  return v;
+}
+
+// Block holding unit x: the largest i with floor(i*T/nb) <= x.
+__device__ __forceinline__ int block_of(int64_t x, int64_t T, int nb) {
+  return static_cast<int>(((x + 1) * nb - 1) / T);
+}
+
+// Blocks used for T units: ceil(T / min_units), at least 1 and at most grid.
+__device__ __forceinline__ int used_blocks(int64_t T, int grid, int64_t min_units) {
+  const int64_t want = (T + min_units - 1) / min_units;
+  return static_cast<int>(want < 1 ? 1 : (want < grid ? want : grid));
+}
+
 }  // namespace pa

@@ -496,22 +496,6 @@ __device__ __forceinline__ int64_t seq_len(const int32_t* ctx, int b, int window
   return static_cast<int64_t>(n - lo);
 }
 
-__device__ __forceinline__ int64_t wave_sum64(int64_t v) {
-#pragma unroll
-  for (int w = 32; w > 0; w >>= 1) v += __shfl_xor(v, w);
-  return v;
-}
-
-// Inclusive prefix sum over the 64 lanes.
-__device__ __forceinline__ int64_t wave_scan64(int64_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int w = 1; w < 64; w <<= 1) {
-    const int64_t u = __shfl_up(v, w);
-    if (lane >= w) v += u;
-  }
-  return v;
-}
 
 // Keys (per KV head) of all sequences: sum_b len_b.  Called by a whole wave.
 __device__ __forceinline__ int64_t total_keys(const int32_t* ctx, int batch, int window) {
@@ -543,15 +527,6 @@ __device__ __forceinline__ void locate_unit(const int32_t* ctx, int batch, int w
   pre_out = base;
 }
 
-// Block holding unit x: the largest i with floor(i*T/nb) <= x.
-__device__ __forceinline__ int block_of(int64_t x, int64_t T, int nb) {
-  return static_cast<int>(((x + 1) * nb - 1) / T);
-}
-
-__device__ __forceinline__ int used_blocks(int64_t T, int grid, int64_t min_units) {
-  const int64_t want = (T + min_units - 1) / min_units;
-  return static_cast<int>(want < 1 ? 1 : (want < grid ? want : grid));
-}
 
 template <int D, int G>
 __global__ __launch_bounds__(kBlock) void balanced_split_kernel(const SplitParams p,

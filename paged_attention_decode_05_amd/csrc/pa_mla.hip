@@ -16,8 +16,18 @@
 // enters as three bf16 terms hi + mid + lo, which represent an fp32 value
 // exactly (3 x 8 significant bits), so the MFMAs multiply the fp32 operands
 // exactly and only the fp32 accumulation rounds, at three MFMAs instead of one.
+//
+// Work split: heads form groups of 64 (one block = 4 waves x 16 heads); a
+// row is (head group, sequence), ordered group-major.  The keys of all rows,
+// laid end to end (T = groups * sum of context lengths), are cut into nb
+// equal contiguous ranges, one per block; a block writes one partial per row
+// piece it covers.  Group-major order puts the two head groups of the same
+// keys T/2 units apart, i.e. in blocks i and i + nb/2, which the dispatcher
+// places on the same XCD (nb a multiple of 16), so the second read of a
+// cache tile is served by that XCD's L2.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <string>
 
 #include "pa_decode.h"
@@ -28,6 +38,8 @@ namespace pa {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 constexpr int kLat = kMlaLat;      // 512
 constexpr int kRow = kMlaRow;      // 576
@@ -39,9 +51,10 @@ constexpr int kKSL = kLat / 32;    // 16 of them over the latent part
 constexpr int kTileKeys = 32;      // keys per LDS tile
 constexpr int kHeadsPerWave = 16;
 constexpr int kMlaWaves = 4;
+constexpr int kGroup = kHeadsPerWave * kMlaWaves;   // heads per block
 constexpr int kMlaThreads = 64 * kMlaWaves;
-constexpr int kRowPad = kRow + 8;          // LDS row stride (elements) of the key-major copy
-constexpr int kTPad = kTileKeys + 8;       // LDS row stride of the latent-major copy
+constexpr int kRowPad = kRow + 8;  // LDS row stride (elements) of a cache tile row
+static_assert(kGroup == kMlaBlockHeads, "head group size");
 
 struct MlaParams {
   const uint16_t* q_nope;
@@ -54,19 +67,20 @@ struct MlaParams {
   uint16_t* q_hi;          // [B][H][576]  q_abs | q_rope
   uint16_t* q_mid;         // [B][H][512]  second and third terms of q_abs
   uint16_t* q_lo;
-  float* part_out;         // [B][H][max_parts][512]
-  float* part_max;         // [B][H][max_parts]  (natural-log domain)
-  float* part_sum;
+  float* seg_out;          // [slots][64][512] normalised partial o_lat
+  float* seg_max;          // [slots][64] natural-log-domain reference max
+  float* seg_sum;          // [slots][64] sum of exp(s - max)
   uint16_t* out;           // [B][H][128]
   int64_t page_stride;
   int32_t token_stride;
   int32_t bt_stride;
   int32_t batch;
   int32_t num_heads;
+  int32_t groups;          // ceil(num_heads / 64)
   int32_t page_size;
   int32_t page_shift;
-  int32_t partition_size;
-  int32_t max_parts;
+  int32_t split_grid;      // blocks launched for the split kernel
+  int32_t min_keys;        // keys per block below which fewer blocks are used
   float scale_log2;
 };
 
@@ -88,95 +102,137 @@ __device__ __forceinline__ void split3_bf16(float x, uint16_t& hi, uint16_t& mid
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+__device__ __forceinline__ f32x4_t mfma(uint4 a, uint4 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// Transposed 64-bit LDS read (ds_read_b64_tr_b16).  Within each 16-lane
+// group, lane j receives element k (k < 4) of the 4 bf16 that lane 4k + j/4
+// addresses, at position j % 4: with lane a pointing at row a/4, columns
+// 4(a%4) .. +4 of a row-major tile, lane j gets column j of rows 0..3.
+__device__ __forceinline__ uint2 lds_read_tr(const uint16_t* p) {
+  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
 // ---- 1. absorption: q_abs = q_nope . W_UK[h], split in three; rope copied ----------
 //
-// Block (h, jc) computes q_abs[b][h][jc*128 .. +128) for every b: thread t
-// owns column j = jc*128 + t%128 and rows b = t/128, t/128 + 2, ...; the
-// q_nope rows of a 16-row batch tile sit in LDS.  fp32 FMAs in ascending d.
+// Block (h, jc, bt) computes q_abs[b][h][jc*128 .. +128) for the 16 sequences
+// b = 16*bt .. +16: thread t owns latent dims j = jc*128 + 8*(t%16) .. +8
+// of sequence 16*bt + t/16 and reads W_UK[h][d][j .. j+8] as one 16-byte
+// load per d.  fp32 FMAs in ascending d.
 __global__ __launch_bounds__(256) void mla_absorb_kernel(const MlaParams p) {
   __shared__ float qs[16][kNope];
   const int h = blockIdx.x;
   const int jc = blockIdx.y;
+  const int b0 = blockIdx.z * 16;
   const int t = threadIdx.x;
-  const int j = jc * 128 + (t & 127);
-  const int par = t >> 7;
-  const uint16_t* wcol = p.w_uk + static_cast<int64_t>(h) * kNope * kLat + j;
-  for (int b0 = 0; b0 < p.batch; b0 += 16) {
-    const int nb = min(16, p.batch - b0);
-    __syncthreads();
-    for (int i = t; i < nb * kNope; i += 256) {
-      const int bb = i / kNope, d = i % kNope;
-      qs[bb][d] = u2f(static_cast<uint32_t>(
-                          p.q_nope[(static_cast<int64_t>(b0 + bb) * p.num_heads + h) * kNope + d])
-                      << 16);
-    }
-    __syncthreads();
-    float acc[8];
+  const int nb = min(16, p.batch - b0);
+  for (int i = t; i < nb * kNope; i += 256) {
+    const int bb = i / kNope, d = i % kNope;
+    qs[bb][d] = bf16_val(p.q_nope[(static_cast<int64_t>(b0 + bb) * p.num_heads + h) * kNope + d]);
+  }
+  __syncthreads();
+  const int c = t & 15;
+  const int bb = t >> 4;
+  const int j = jc * 128 + 8 * c;
+  const uint16_t* w = p.w_uk + static_cast<int64_t>(h) * kNope * kLat + j;
+  float acc[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) acc[k] = 0.0f;
-    for (int d = 0; d < kNope; ++d) {
-      const float w = u2f(static_cast<uint32_t>(wcol[static_cast<int64_t>(d) * kLat]) << 16);
+  for (int k = 0; k < 8; ++k) acc[k] = 0.0f;
+  const int br = min(bb, nb - 1);      // rows past the batch compute a copy and store nothing
+#pragma unroll 8
+  for (int d = 0; d < kNope; ++d) {
+    const uint4 wv = load16(w + static_cast<int64_t>(d) * kLat);
+    const float q = qs[br][d];
+    const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
 #pragma unroll
-      for (int k = 0; k < 8; ++k) acc[k] = fmaf(qs[par + 2 * k][d], w, acc[k]);
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] = fmaf(q, bf16_lo(ww[e]), acc[2 * e]);
+      acc[2 * e + 1] = fmaf(q, bf16_hi(ww[e]), acc[2 * e + 1]);
     }
+  }
+  if (bb < nb) {
+    uint16_t hi[8], mid[8], lo[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int bb = par + 2 * k;
-      if (bb < nb) {
-        uint16_t hi, mid, lo;
-        split3_bf16(acc[k], hi, mid, lo);
-        const int64_t row = static_cast<int64_t>(b0 + bb) * p.num_heads + h;
-        p.q_hi[row * kRow + j] = hi;
-        p.q_mid[row * kLat + j] = mid;
-        p.q_lo[row * kLat + j] = lo;
-      }
-    }
-    if (jc == 0) {   // rope part: exact bf16, one term
-      for (int i = t; i < nb * kRope; i += 256) {
-        const int bb = i / kRope, r = i % kRope;
-        const int64_t row = static_cast<int64_t>(b0 + bb) * p.num_heads + h;
-        p.q_hi[row * kRow + kLat + r] = p.q_rope[row * kRope + r];
-      }
-    }
+    for (int k = 0; k < 8; ++k) split3_bf16(acc[k], hi[k], mid[k], lo[k]);
+    const int64_t row = static_cast<int64_t>(b0 + bb) * p.num_heads + h;
+    *reinterpret_cast<uint4*>(p.q_hi + row * kRow + j) =
+        make_uint4(pack_bf16(hi[0], hi[1]), pack_bf16(hi[2], hi[3]), pack_bf16(hi[4], hi[5]),
+                   pack_bf16(hi[6], hi[7]));
+    *reinterpret_cast<uint4*>(p.q_mid + row * kLat + j) =
+        make_uint4(pack_bf16(mid[0], mid[1]), pack_bf16(mid[2], mid[3]), pack_bf16(mid[4], mid[5]),
+                   pack_bf16(mid[6], mid[7]));
+    *reinterpret_cast<uint4*>(p.q_lo + row * kLat + j) =
+        make_uint4(pack_bf16(lo[0], lo[1]), pack_bf16(lo[2], lo[3]), pack_bf16(lo[4], lo[5]),
+                   pack_bf16(lo[6], lo[7]));
+  }
+  if (jc == 0 && t < nb * (kRope / 8)) {   // rope part: exact bf16, one term
+    const int rb = t / (kRope / 8), rc = t % (kRope / 8);
+    const int64_t row = static_cast<int64_t>(b0 + rb) * p.num_heads + h;
+    *reinterpret_cast<uint4*>(p.q_hi + row * kRow + kLat + 8 * rc) =
+        load16(p.q_rope + row * kRope + 8 * rc);
   }
 }
 
 // ---- 2. split attention over the latent cache ----------------------------------------
-//
-// Block (part, hg, b): keys [part*P, min(part*P + P, ctx)) of sequence b for
-// heads hg*64 .. hg*64+63, wave w taking 16 of them.  Per 32-key tile the
-// block stages the cache rows in LDS twice: key-major (A operand of the
-// score MFMA) and latent-major (B operand of P.V, whose contraction runs over
-// keys).  Score D layout: lane l holds S^T[key 4*(l/16)+i (+16)][head l%16];
-// those 8 values are exactly the A operand of P.V for head l%16 when the P.V
-// k-slots 8g..8g+7 are taken as keys {4g..4g+3, 16+4g..16+4g+3}, which is
-// also the order the latent-major reads use.  The softmax keeps a per-head
-// reference max and rescales the accumulators only when a score exceeds it
-// by more than 2^8 (log2 domain), so P stays below 2^8 and rescaling is rare.
-__global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(const MlaParams p) {
-  __shared__ __align__(16) uint16_t crow[kTileKeys][kRowPad];
-  __shared__ __align__(16) uint16_t ct[kLat][kTPad];
-  __shared__ __align__(16) uint16_t qlo_s[kHeadsPerWave * kMlaWaves][kLat + 8];   // third q term
 
-  const int part = blockIdx.x;
-  const int hg = blockIdx.y;
-  const int b = blockIdx.z;
+// Sum of the context lengths.  Called by a whole wave.
+__device__ __forceinline__ int64_t mla_total(const int32_t* ctx, int batch) {
+  const int lane = threadIdx.x & 63;
+  int64_t s = 0;
+  for (int b0 = 0; b0 < batch; b0 += 64) s += (b0 + lane < batch) ? ctx[b0 + lane] : 0;
+  return wave_sum64(s);
+}
+
+// Sequence b holding key y (0 <= y < S) of a group's key line, and the keys
+// before it.  Called by a whole wave.
+__device__ __forceinline__ void mla_locate(const int32_t* ctx, int batch, int64_t y, int& b_out,
+                                           int64_t& pre_out) {
+  const int lane = threadIdx.x & 63;
+  int64_t base = 0;
+  for (int b0 = 0; b0 < batch; b0 += 64) {
+    const int64_t len = (b0 + lane < batch) ? ctx[b0 + lane] : 0;
+    const int64_t incl = wave_scan64(len);
+    const uint64_t hit = __ballot(base + incl > y);
+    if (hit) {
+      const int l = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+      b_out = b0 + l;
+      pre_out = base + __shfl(incl, l) - __shfl(len, l);
+      return;
+    }
+    base += __shfl(incl, 63);
+  }
+  b_out = batch;
+  pre_out = base;
+}
+
+// Attention of the heads of group hg of sequence b over keys [begin, end);
+// writes the normalised partial, its max and its sum to slot.
+// Score D layout: lane l holds S^T[key 4*(l/16)+i (+16)][head l%16]; those 8
+// values are exactly the A operand of P.V for head l%16 when the P.V k-slots
+// 8g..8g+7 are taken as keys {4g..4g+3, 16+4g..16+4g+3}; the B operand
+// (those keys, 16 latent columns) comes from two transposed LDS reads of the
+// key-major tile.  The softmax keeps a per-head reference max and rescales
+// the accumulators only when a score exceeds it by more than 8 (log2
+// domain), so P stays below 2^8 and rescaling is rare.
+__device__ __forceinline__ void mla_segment(const MlaParams& p, int b, int hg, int begin, int end,
+                                            int64_t slot, uint16_t (*crow)[kRowPad],
+                                            uint16_t (*qlo_s)[kLat + 8]) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int n = p.context_lens[b];
-  const int begin = part * p.partition_size;
-  if (begin >= n) return;
-  const int end = min(begin + p.partition_size, n);
-  const int h0 = hg * (kHeadsPerWave * kMlaWaves) + wave * kHeadsPerWave;
-  const bool active = h0 < p.num_heads;       // waves past the last head only load tiles
   const int g = lane >> 4;
   const int c16 = lane & 15;
+  const int hb = hg * kGroup;
+  const int nh = min(kGroup, p.num_heads - hb);
+  const int h0 = hb + wave * kHeadsPerWave;
+  const bool active = wave * kHeadsPerWave < nh;   // waves past the last head only stage tiles
   const int32_t* bt = p.block_table + static_cast<int64_t>(b) * p.bt_stride;
 
+  __syncthreads();   // the previous segment is done with qlo_s and crow
   // Q^T operand for all 18 k-steps: head h0 + c16, dims 32*ks + 8g .. +8;
-  // hi (18 steps) and mid (16 latent steps) in registers, lo in LDS (read
-  // once per tile); the rope steps have one term.
+  // hi (18 steps) and mid (16 latent steps) in registers, lo in LDS.
   uint4 qh[kKS], qm[kKSL];
   if (active) {
     const int64_t hrow = static_cast<int64_t>(b) * p.num_heads + h0 + c16;
@@ -185,14 +241,10 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(const MlaParams 
 #pragma unroll
     for (int ks = 0; ks < kKSL; ++ks) qm[ks] = load16(p.q_mid + hrow * kLat + 32 * ks + 8 * g);
   }
-  {
-    const int hb = hg * (kHeadsPerWave * kMlaWaves);
-    const int nh = min(kHeadsPerWave * kMlaWaves, p.num_heads - hb);
-    for (int c = tid; c < nh * (kLat / 8); c += kMlaThreads) {
-      const int r = c / (kLat / 8), cc = c % (kLat / 8);
-      *reinterpret_cast<uint4*>(&qlo_s[r][cc * 8]) =
-          load16(p.q_lo + (static_cast<int64_t>(b) * p.num_heads + hb + r) * kLat + cc * 8);
-    }
+  for (int c = tid; c < nh * (kLat / 8); c += kMlaThreads) {
+    const int r = c / (kLat / 8), cc = c % (kLat / 8);
+    *reinterpret_cast<uint4*>(&qlo_s[r][cc * 8]) =
+        load16(p.q_lo + (static_cast<int64_t>(b) * p.num_heads + hb + r) * kLat + cc * 8);
   }
 
   f32x4_t acc[kLat / 16];
@@ -201,41 +253,28 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(const MlaParams 
   float m_ref = -INFINITY;     // per head c16 (same on the 4 lanes of the head)
   float l_sum = 0.0f;          // this lane's share of the head's denominator
 
-  // Staging of one tile: 32 keys x 72 chunks of 16 B, 9 chunks per thread.
-  constexpr int kChunks = kTileKeys * (kRow / 8) / kMlaThreads;   // 9
+  // Staging of one tile: 32 keys x 72 chunks of 16 B.  Wave w stages keys
+  // 8w .. 8w+7, lane l key 8w + l/8 and its chunks l%8 + 8k (k < 9), so each
+  // lane resolves one page per tile and the chunk offsets are constants.
+  constexpr int kChunks = kRow / 8 / 8;   // 9
+  const int skey = wave * 8 + (lane >> 3);
+  const int schunk = lane & 7;
   uint4 stage[kChunks];
   auto load_tile = [&](int t0) {
+    const int t = t0 + skey;
+    const bool live = t >= begin && t < end;
+    const uint16_t* src = p.cache;
+    if (live)
+      src += static_cast<int64_t>(bt[t >> p.page_shift]) * p.page_stride +
+             static_cast<int64_t>(t & (p.page_size - 1)) * p.token_stride + schunk * 8;
 #pragma unroll
-    for (int k = 0; k < kChunks; ++k) {
-      const int c = tid + kMlaThreads * k;
-      const int key = c / (kRow / 8);
-      const int cc = c % (kRow / 8);
-      const int t = t0 + key;
-      if (t >= begin && t < end) {
-        const int page = bt[t >> p.page_shift];
-        stage[k] = load16(p.cache + static_cast<int64_t>(page) * p.page_stride +
-                          static_cast<int64_t>(t & (p.page_size - 1)) * p.token_stride + cc * 8);
-      } else {
-        stage[k] = make_uint4(0, 0, 0, 0);
-      }
-    }
+    for (int k = 0; k < kChunks; ++k)
+      stage[k] = live ? load16(src + 64 * k) : make_uint4(0, 0, 0, 0);
   };
   auto store_tile = [&]() {
 #pragma unroll
-    for (int k = 0; k < kChunks; ++k) {
-      const int c = tid + kMlaThreads * k;
-      const int key = c / (kRow / 8);
-      const int cc = c % (kRow / 8);
-      *reinterpret_cast<uint4*>(&crow[key][cc * 8]) = stage[k];
-      if (cc < kLat / 8) {
-        const uint32_t w[4] = {stage[k].x, stage[k].y, stage[k].z, stage[k].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          ct[cc * 8 + 2 * e][key] = static_cast<uint16_t>(w[e] & 0xffffu);
-          ct[cc * 8 + 2 * e + 1][key] = static_cast<uint16_t>(w[e] >> 16);
-        }
-      }
-    }
+    for (int k = 0; k < kChunks; ++k)
+      *reinterpret_cast<uint4*>(&crow[skey][(schunk + 8 * k) * 8]) = stage[k];
   };
 
   const int first_tile = begin / kTileKeys;
@@ -269,13 +308,13 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(const MlaParams 
         if (ks + 1 < kKSL) nl = *reinterpret_cast<const uint4*>(lrow + 32 * (ks + 1));
       }
       if (ks < kKSL) {
-        sc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a0), as_bf16x8(qlv), sc[0], 0, 0, 0);
-        sc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1), as_bf16x8(qlv), sc[1], 0, 0, 0);
-        sc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a0), as_bf16x8(qm[ks]), sc[0], 0, 0, 0);
-        sc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1), as_bf16x8(qm[ks]), sc[1], 0, 0, 0);
+        sc[0] = mfma(a0, qlv, sc[0]);
+        sc[1] = mfma(a1, qlv, sc[1]);
+        sc[0] = mfma(a0, qm[ks], sc[0]);
+        sc[1] = mfma(a1, qm[ks], sc[1]);
       }
-      sc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a0), as_bf16x8(qh[ks]), sc[0], 0, 0, 0);
-      sc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1), as_bf16x8(qh[ks]), sc[1], 0, 0, 0);
+      sc[0] = mfma(a0, qh[ks], sc[0]);
+      sc[1] = mfma(a1, qh[ks], sc[1]);
       a0 = n0;
       a1 = n1;
       qlv = nl;
@@ -295,7 +334,7 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(const MlaParams 
       }
     cm = fmaxf(cm, xor16(cm));
     cm = fmaxf(cm, xor32(cm));
-    // move the reference max when a score passes it by more than 2^8
+    // move the reference max when a score passes it by more than 8
     const bool bump = cm > m_ref + 8.0f;
     if (__builtin_amdgcn_read_exec() & __ballot(bump)) {
       const float nref = bump ? cm : m_ref;
@@ -325,16 +364,24 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(const MlaParams 
                                     pack_bf16(pm[4], pm[5]), pack_bf16(pm[6], pm[7]));
     const uint4 pa_lo = make_uint4(pack_bf16(pl[0], pl[1]), pack_bf16(pl[2], pl[3]),
                                    pack_bf16(pl[4], pl[5]), pack_bf16(pl[6], pl[7]));
-    // O[heads][latent] += P . C over the 32 keys of the tile
+    // O[heads][latent] += P . C over the 32 keys of the tile; lane (g, a)
+    // points the transposed reads at rows 4g + a/4 and 16 + 4g + a/4,
+    // columns 16*jt + 4*(a%4).
+    const uint16_t* brow0 = &crow[4 * g + (c16 >> 2)][4 * (c16 & 3)];
+    const uint16_t* brow1 = &crow[16 + 4 * g + (c16 >> 2)][4 * (c16 & 3)];
+    uint2 k03 = lds_read_tr(brow0);
+    uint2 k47 = lds_read_tr(brow1);
 #pragma unroll
     for (int jt = 0; jt < kLat / 16; ++jt) {
-      const int jrow = 16 * jt + c16;
-      const uint2 lo4 = *reinterpret_cast<const uint2*>(&ct[jrow][4 * g]);
-      const uint2 hi4 = *reinterpret_cast<const uint2*>(&ct[jrow][16 + 4 * g]);
-      const uint4 bop = make_uint4(lo4.x, lo4.y, hi4.x, hi4.y);
-      acc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(pa_lo), as_bf16x8(bop), acc[jt], 0, 0, 0);
-      acc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(pa_mid), as_bf16x8(bop), acc[jt], 0, 0, 0);
-      acc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(pa_hi), as_bf16x8(bop), acc[jt], 0, 0, 0);
+      const uint4 bop = make_uint4(k03.x, k03.y, k47.x, k47.y);
+      if (jt + 1 < kLat / 16) {
+        k03 = lds_read_tr(brow0 + 16 * (jt + 1));
+        k47 = lds_read_tr(brow1 + 16 * (jt + 1));
+      }
+      acc[jt] = mfma(pa_lo, bop, acc[jt]);
+      acc[jt] = mfma(pa_mid, bop, acc[jt]);
+      acc[jt] = mfma(pa_hi, bop, acc[jt]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   if (!active) return;
@@ -345,114 +392,196 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(const MlaParams 
   float lr[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) lr[i] = __shfl(l_sum, 4 * g + i);
-  const int64_t rows = static_cast<int64_t>(b) * p.num_heads + h0;
+  const int64_t srow = slot * kGroup + wave * kHeadsPerWave;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    float* dst = p.part_out + ((rows + 4 * g + i) * p.max_parts + part) * kLat;
+    float* dst = p.seg_out + (srow + 4 * g + i) * kLat;
     const float inv = 1.0f / lr[i];
 #pragma unroll
     for (int jt = 0; jt < kLat / 16; ++jt) dst[16 * jt + c16] = acc[jt][i] * inv;
   }
   if (g == 0) {
-    const int64_t idx = (rows + c16) * p.max_parts + part;
-    p.part_max[idx] = m_ref * kLn2;
-    p.part_sum[idx] = l_sum;
+    p.seg_max[srow + c16] = m_ref * kLn2;
+    p.seg_sum[srow + c16] = l_sum;
   }
 }
 
-// ---- 3. merge of the partitions, then out = W_UV[h] . o_lat on MFMA ------------------
+__global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(const MlaParams p) {
+  __shared__ __align__(16) uint16_t crow[kTileKeys][kRowPad];
+  __shared__ __align__(16) uint16_t qlo_s[kGroup][kLat + 8];
+  __shared__ int64_t sh[4];
+  __shared__ int sh_b;
+
+  const int i = blockIdx.x;
+  if (threadIdx.x < 64) {
+    const int64_t S = mla_total(p.context_lens, p.batch);
+    const int64_t T = S * p.groups;
+    const int nb = used_blocks(T, p.split_grid, p.min_keys);
+    const int64_t u0 = T * i / nb;
+    int b = p.batch;
+    int64_t pre = 0;
+    if (i < nb && S > 0) mla_locate(p.context_lens, p.batch, u0 % S, b, pre);
+    if (threadIdx.x == 0) {
+      sh[0] = S;
+      sh[1] = (i < nb) ? u0 : 0;
+      sh[2] = (i < nb) ? T * (i + 1) / nb : 0;
+      sh[3] = pre;
+      sh_b = b;
+    }
+  }
+  __syncthreads();
+  const int64_t S = sh[0];
+  const int64_t u1 = sh[2];
+  int64_t u = sh[1];
+  if (u >= u1) return;
+  int hg = static_cast<int>(u / S);
+  int b = sh_b;
+  int64_t pre = sh[3];
+  while (u < u1) {
+    const int64_t row_start = hg * S + pre;
+    const int n = p.context_lens[b];
+    const int begin = static_cast<int>(u - row_start);
+    const int end = static_cast<int>(min(u1 - row_start, static_cast<int64_t>(n)));
+    if (end > begin)
+      mla_segment(p, b, hg, begin, end, static_cast<int64_t>(hg) * p.batch + b + i, crow, qlo_s);
+    u = row_start + n;
+    pre += n;
+    if (++b == p.batch) {
+      b = 0;
+      pre = 0;
+      ++hg;
+    }
+  }
+}
+
+// ---- 3. merge of the partials, then out = W_UV[h] . o_lat on MFMA ---------------------
 //
-// Block h handles all sequences in tiles of 16: o_lat[b][:] is the
-// l_j e^(m_j - M)/W -weighted sum of the live partials (ascending j), written
-// to LDS as three bf16 terms; then out[b][dv] = sum_j o_lat[b][j] W_UV[h][dv][j] with
-// A = o_lat (16 sequences x 32 latent dims per step) and B = W_UV rows, whose
-// 8 consecutive latent dims per lane are contiguous in memory.
+// Block (h, bt) handles sequences 16*bt .. +16 of head h: row (group hg, b)
+// was cut into pieces by blocks i0 .. i1 of the split (recomputed here from
+// the context lengths), whose partials sit in slots r + i0 .. r + i1 with
+// r = hg*batch + b.  o_lat is the l_i e^(m_i - M)/W -weighted sum of those
+// partials in ascending i, written to LDS as three bf16 terms; then
+// out[b][dv] = sum_j o_lat[b][j] W_UV[h][dv][j] with A = o_lat (16 sequences
+// x 32 latent dims per step) and B = W_UV rows, whose 8 consecutive latent
+// dims per lane are contiguous in memory.  An empty context gives 0.
 __global__ __launch_bounds__(kMlaThreads) void mla_merge_uv_kernel(const MlaParams p) {
   __shared__ __align__(16) uint16_t ohi[16][kLat + 8];
   __shared__ __align__(16) uint16_t omid[16][kLat + 8];
   __shared__ __align__(16) uint16_t olo[16][kLat + 8];
-  __shared__ float mx[16], wsum[16];
-  __shared__ int cnt[16];
+  __shared__ int64_t sh_slot[16];
+  __shared__ int sh_cnt[16];
+  __shared__ float sh_m[16], sh_w[16];
   const int h = blockIdx.x;
+  const int b0 = blockIdx.y * 16;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int g = lane >> 4;
   const int c16 = lane & 15;
-  for (int b0 = 0; b0 < p.batch; b0 += 16) {
-    const int nb = min(16, p.batch - b0);
-    __syncthreads();
-    // per sequence: live partitions, max and total weight
-    if (tid < 16) {
-      const int bb = tid;
-      int live = 0;
+  const int hg = h / kGroup;
+  const int hl = h % kGroup;
+  const int nb16 = min(16, p.batch - b0);
+
+  if (tid < 64) {
+    const int64_t S = mla_total(p.context_lens, p.batch);
+    const int64_t T = S * p.groups;
+    const int nb = used_blocks(T, p.split_grid, p.min_keys);
+    // keys of the sequences before b0, then the prefix within the tile
+    int64_t before = 0;
+    for (int c0 = 0; c0 < b0; c0 += 64) before += (c0 + lane < b0) ? p.context_lens[c0 + lane] : 0;
+    before = wave_sum64(before);
+    const int64_t len = (lane < nb16) ? p.context_lens[b0 + lane] : 0;
+    const int64_t pre = before + wave_scan64(len) - len;
+    if (lane < 16) {
+      int64_t slot = 0;
+      int cnt = 0;
+      if (lane < nb16 && len > 0) {
+        const int64_t start = hg * S + pre;
+        const int i0 = block_of(start, T, nb);
+        const int i1 = block_of(start + len - 1, T, nb);
+        slot = static_cast<int64_t>(hg) * p.batch + b0 + lane + i0;
+        cnt = i1 - i0 + 1;
+      }
       float M = -INFINITY, W = 0.0f;
-      if (bb < nb) {
-        const int nctx = p.context_lens[b0 + bb];
-        live = min((nctx + p.partition_size - 1) / p.partition_size, p.max_parts);
-        const int64_t row = (static_cast<int64_t>(b0 + bb) * p.num_heads + h) * p.max_parts;
-        for (int k = 0; k < live; ++k) M = fmaxf(M, p.part_max[row + k]);
-        for (int k = 0; k < live; ++k) W += p.part_sum[row + k] * __expf(p.part_max[row + k] - M);
-      }
-      cnt[bb] = live;
-      mx[bb] = M;
-      wsum[bb] = W;
+      for (int k = 0; k < cnt; ++k) M = fmaxf(M, p.seg_max[(slot + k) * kGroup + hl]);
+      for (int k = 0; k < cnt; ++k)
+        W += p.seg_sum[(slot + k) * kGroup + hl] * __expf(p.seg_max[(slot + k) * kGroup + hl] - M);
+      sh_slot[lane] = slot;
+      sh_cnt[lane] = cnt;
+      sh_m[lane] = M;
+      sh_w[lane] = W;
     }
-    __syncthreads();
-    // o_lat for 16 sequences x 512 dims: thread owns dims (tid % 128) * 4 .. +4 of rows tid / 128 + 2r
-    for (int rr = 0; rr < 8; ++rr) {
-      const int bb = (tid >> 7) + 2 * rr;
-      const int d0 = (tid & 127) * 4;
-      float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (bb < nb && cnt[bb] > 0 && mx[bb] != -INFINITY) {
-        const int64_t row = (static_cast<int64_t>(b0 + bb) * p.num_heads + h) * p.max_parts;
-        for (int k = 0; k < cnt[bb]; ++k) {
-          const float w = p.part_sum[row + k] * __expf(p.part_max[row + k] - mx[bb]) / wsum[bb];
-          const float4 v = *reinterpret_cast<const float4*>(p.part_out + (row + k) * kLat + d0);
-          o.x = fmaf(w, v.x, o.x);
-          o.y = fmaf(w, v.y, o.y);
-          o.z = fmaf(w, v.z, o.z);
-          o.w = fmaf(w, v.w, o.w);
-        }
+  }
+  __syncthreads();
+  // o_lat for 16 sequences x 512 dims: thread owns dims (tid % 128) * 4 .. +4
+  // of rows tid / 128 + 2 rr
+  for (int rr = 0; rr < 8; ++rr) {
+    const int bb = (tid >> 7) + 2 * rr;
+    const int d0 = (tid & 127) * 4;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    const int cnt = sh_cnt[bb];
+    if (cnt > 0) {
+      const int64_t slot = sh_slot[bb];
+      const float M = sh_m[bb], invW = 1.0f / sh_w[bb];
+      for (int k = 0; k < cnt; ++k) {
+        const int64_t srow = (slot + k) * kGroup + hl;
+        const float w = p.seg_sum[srow] * __expf(p.seg_max[srow] - M) * invW;
+        const float4 v = *reinterpret_cast<const float4*>(p.seg_out + srow * kLat + d0);
+        o.x = fmaf(w, v.x, o.x);
+        o.y = fmaf(w, v.y, o.y);
+        o.z = fmaf(w, v.z, o.z);
+        o.w = fmaf(w, v.w, o.w);
       }
-      uint16_t h4[4], m4[4], l4[4];
-      split3_bf16(o.x, h4[0], m4[0], l4[0]);
-      split3_bf16(o.y, h4[1], m4[1], l4[1]);
-      split3_bf16(o.z, h4[2], m4[2], l4[2]);
-      split3_bf16(o.w, h4[3], m4[3], l4[3]);
-      *reinterpret_cast<uint2*>(&ohi[bb][d0]) = make_uint2(pack_bf16(h4[0], h4[1]), pack_bf16(h4[2], h4[3]));
-      *reinterpret_cast<uint2*>(&omid[bb][d0]) = make_uint2(pack_bf16(m4[0], m4[1]), pack_bf16(m4[2], m4[3]));
-      *reinterpret_cast<uint2*>(&olo[bb][d0]) = make_uint2(pack_bf16(l4[0], l4[1]), pack_bf16(l4[2], l4[3]));
     }
-    __syncthreads();
-    // out[b][dv]: wave w takes dv tiles 2w, 2w+1
-    const uint16_t* wuv = p.w_uv + static_cast<int64_t>(h) * kDv * kLat;
+    uint16_t h4[4], m4[4], l4[4];
+    split3_bf16(o.x, h4[0], m4[0], l4[0]);
+    split3_bf16(o.y, h4[1], m4[1], l4[1]);
+    split3_bf16(o.z, h4[2], m4[2], l4[2]);
+    split3_bf16(o.w, h4[3], m4[3], l4[3]);
+    *reinterpret_cast<uint2*>(&ohi[bb][d0]) = make_uint2(pack_bf16(h4[0], h4[1]), pack_bf16(h4[2], h4[3]));
+    *reinterpret_cast<uint2*>(&omid[bb][d0]) = make_uint2(pack_bf16(m4[0], m4[1]), pack_bf16(m4[2], m4[3]));
+    *reinterpret_cast<uint2*>(&olo[bb][d0]) = make_uint2(pack_bf16(l4[0], l4[1]), pack_bf16(l4[2], l4[3]));
+  }
+  __syncthreads();
+  // out[b][dv]: wave w takes dv tiles 2w, 2w+1
+  const uint16_t* wuv = p.w_uv + static_cast<int64_t>(h) * kDv * kLat;
 #pragma unroll
-    for (int nt2 = 0; nt2 < 2; ++nt2) {
-      const int nt = 2 * wave + nt2;
-      f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+  for (int nt2 = 0; nt2 < 2; ++nt2) {
+    const int nt = 2 * wave + nt2;
+    f32x4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
-      for (int ks = 0; ks < kLat / 32; ++ks) {
-        const uint4 a_hi = *reinterpret_cast<const uint4*>(&ohi[c16][32 * ks + 8 * g]);
-        const uint4 a_mid = *reinterpret_cast<const uint4*>(&omid[c16][32 * ks + 8 * g]);
-        const uint4 a_lo = *reinterpret_cast<const uint4*>(&olo[c16][32 * ks + 8 * g]);
-        const uint4 bw = load16(wuv + static_cast<int64_t>(16 * nt + c16) * kLat + 32 * ks + 8 * g);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a_lo), as_bf16x8(bw), c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a_mid), as_bf16x8(bw), c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a_hi), as_bf16x8(bw), c, 0, 0, 0);
-      }
+    for (int ks = 0; ks < kLat / 32; ++ks) {
+      const uint4 a_hi = *reinterpret_cast<const uint4*>(&ohi[c16][32 * ks + 8 * g]);
+      const uint4 a_mid = *reinterpret_cast<const uint4*>(&omid[c16][32 * ks + 8 * g]);
+      const uint4 a_lo = *reinterpret_cast<const uint4*>(&olo[c16][32 * ks + 8 * g]);
+      const uint4 bw = load16(wuv + static_cast<int64_t>(16 * nt + c16) * kLat + 32 * ks + 8 * g);
+      c = mfma(a_lo, bw, c);
+      c = mfma(a_mid, bw, c);
+      c = mfma(a_hi, bw, c);
+    }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int bb = 4 * g + i;
-        if (bb < nb)
-          p.out[(static_cast<int64_t>(b0 + bb) * p.num_heads + h) * kDv + 16 * nt + c16] =
-              f32_to_bf16_rne(c[i]);
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int bb = 4 * g + i;
+      if (bb < nb16)
+        p.out[(static_cast<int64_t>(b0 + bb) * p.num_heads + h) * kDv + 16 * nt + c16] =
+            f32_to_bf16_rne(c[i]);
     }
   }
 }
 
 }  // namespace pa
+
+namespace {
+
+int mla_device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    return 256;
+  return n;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -495,34 +624,45 @@ int mla_absorbed_decode(const void* q_nope, const void* q_rope, const void* kv_c
   p.q_hi = reinterpret_cast<uint16_t*>(ws + plan.off_qhi);
   p.q_mid = reinterpret_cast<uint16_t*>(ws + plan.off_qmid);
   p.q_lo = reinterpret_cast<uint16_t*>(ws + plan.off_qlo);
-  p.part_out = reinterpret_cast<float*>(ws + plan.off_out);
-  p.part_max = reinterpret_cast<float*>(ws + plan.off_max);
-  p.part_sum = reinterpret_cast<float*>(ws + plan.off_sum);
+  p.seg_out = reinterpret_cast<float*>(ws + plan.off_seg_out);
+  p.seg_max = reinterpret_cast<float*>(ws + plan.off_seg_max);
+  p.seg_sum = reinterpret_cast<float*>(ws + plan.off_seg_sum);
   p.out = static_cast<uint16_t*>(out);
   p.page_stride = cache->page_stride;
   p.token_stride = static_cast<int32_t>(cache->token_stride);
   p.bt_stride = block_table_stride;
   p.batch = batch;
   p.num_heads = num_heads;
+  p.groups = plan.groups;
   p.page_size = cache->page_size;
   int shift = 0;
   while ((1 << shift) < cache->page_size) ++shift;
   p.page_shift = shift;
-  p.partition_size = plan.partition_size;
-  p.max_parts = plan.max_partitions;
+  // Explicit partition size: about that many keys per block.  Library choice:
+  // one block per CU (a multiple of 16, so the head groups of a key range
+  // share an XCD), each block at least kMlaMinKeys keys.
+  if (partition_size > 0) {
+    p.split_grid = plan.max_blocks;
+    p.min_keys = partition_size;
+  } else {
+    const int cus = mla_device_cus();
+    p.split_grid = std::max(16, std::min(plan.max_blocks, cus / 16 * 16));
+    p.min_keys = pa::kMlaMinKeys;
+  }
   p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   pa::clear_error();
-  hipLaunchKernelGGL(pa::mla_absorb_kernel, dim3(num_heads, pa::kMlaLat / 128), dim3(256), 0, s, p);
+  const int btiles = (batch + 15) / 16;
+  hipLaunchKernelGGL(pa::mla_absorb_kernel, dim3(num_heads, pa::kMlaLat / 128, btiles), dim3(256),
+                     0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return pa::fail(PA_ERR_LAUNCH, std::string("absorb: ") + hipGetErrorString(e));
-  const int head_groups = (num_heads + 63) / 64;
-  hipLaunchKernelGGL(pa::mla_split_kernel, dim3(plan.max_partitions, head_groups, batch),
-                     dim3(pa::kMlaThreads), 0, s, p);
+  hipLaunchKernelGGL(pa::mla_split_kernel, dim3(p.split_grid), dim3(pa::kMlaThreads), 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return pa::fail(PA_ERR_LAUNCH, std::string("split: ") + hipGetErrorString(e));
-  hipLaunchKernelGGL(pa::mla_merge_uv_kernel, dim3(num_heads), dim3(pa::kMlaThreads), 0, s, p);
+  hipLaunchKernelGGL(pa::mla_merge_uv_kernel, dim3(num_heads, btiles), dim3(pa::kMlaThreads), 0, s,
+                     p);
   e = hipGetLastError();
   if (e != hipSuccess) return pa::fail(PA_ERR_LAUNCH, std::string("merge: ") + hipGetErrorString(e));
   return PA_OK;

@@ -1,6 +1,7 @@
 // pa_validate.cpp -- host-side checks and launch planning (no HIP).
 #include "pa_validate.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 
@@ -156,35 +157,35 @@ bool plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32
   return true;
 }
 
-// MLA split plan: partition size a multiple of the 64-key granule.  The
-// split kernel runs one block per (sequence, group of 64 heads, partition);
-// by default the partition is the smallest power of two from 64 keys up that
-// keeps the longest sequence at no more than about 2048 / (batch * groups)
-// blocks, so a full batch covers the 256 CUs a few times over.
+// MLA split plan.  Heads form groups of 64; the keys of all (group,
+// sequence) rows are cut into at most max_blocks equal ranges, one per split
+// block, and every block writes one partial per row piece it covers, so
+// groups * batch + max_blocks partial slots bound the workspace.  An explicit
+// partition size P asks for about P keys per block (ceil(T / P) blocks for T
+// keys in all, capped); 0 leaves it to the library (one block per CU).
 bool plan_mla(int32_t batch, int32_t num_heads, int32_t max_pages_per_seq, int32_t page_size,
               int32_t partition_size, MlaPlan* plan) {
   if (batch < 1 || num_heads < 1 || num_heads % kMlaHeadTile || max_pages_per_seq < 1 ||
       !page_size_supported(page_size) || partition_size < 0 || partition_size % kMlaKeyTile)
     return false;
   const int64_t keys = static_cast<int64_t>(max_pages_per_seq) * page_size;
-  int64_t p = partition_size;
-  if (p == 0) {
-    const int64_t groups = static_cast<int64_t>(batch) * ceil_div(num_heads, kMlaBlockHeads);
-    p = kMlaKeyTile;
-    while (groups * ceil_div(keys, p) > 2048 && p < 8192) p *= 2;
+  plan->groups = static_cast<int32_t>(ceil_div(num_heads, kMlaBlockHeads));
+  if (partition_size > 0) {
+    const int64_t most = ceil_div(plan->groups * static_cast<int64_t>(batch) * keys, partition_size);
+    plan->max_blocks = static_cast<int32_t>(std::min<int64_t>(std::max<int64_t>(most, 1),
+                                                              kMlaMaxExplicitBlocks));
+  } else {
+    plan->max_blocks = kMlaMaxBlocks;
   }
-  plan->partition_size = static_cast<int32_t>(p);
-  plan->max_partitions = static_cast<int32_t>(ceil_div(keys, p));
-  if (plan->max_partitions > 65535) return false;
   const size_t bh = static_cast<size_t>(batch) * num_heads;
-  const size_t rows = bh * plan->max_partitions;
+  const size_t slots = static_cast<size_t>(plan->groups) * batch + plan->max_blocks;
   size_t o = 0;
-  plan->off_qhi = o;  o += round_up(bh * kMlaRow * sizeof(uint16_t), 256);   // q_abs|q_rope, bf16 hi
-  plan->off_qmid = o; o += round_up(bh * kMlaLat * sizeof(uint16_t), 256);   // q_abs, bf16 mid
-  plan->off_qlo = o;  o += round_up(bh * kMlaLat * sizeof(uint16_t), 256);   // q_abs, bf16 lo
-  plan->off_out = o;  o += round_up(rows * kMlaLat * sizeof(float), 256);    // partial o_lat
-  plan->off_max = o;  o += round_up(rows * sizeof(float), 256);
-  plan->off_sum = o;  o += round_up(rows * sizeof(float), 256);
+  plan->off_qhi = o;      o += round_up(bh * kMlaRow * sizeof(uint16_t), 256);   // q_abs|q_rope, hi
+  plan->off_qmid = o;     o += round_up(bh * kMlaLat * sizeof(uint16_t), 256);   // q_abs, mid
+  plan->off_qlo = o;      o += round_up(bh * kMlaLat * sizeof(uint16_t), 256);   // q_abs, lo
+  plan->off_seg_out = o;  o += round_up(slots * kMlaBlockHeads * kMlaLat * sizeof(float), 256);
+  plan->off_seg_max = o;  o += round_up(slots * kMlaBlockHeads * sizeof(float), 256);
+  plan->off_seg_sum = o;  o += round_up(slots * kMlaBlockHeads * sizeof(float), 256);
   plan->bytes = o;
   return true;
 }

@@ -64,13 +64,17 @@ constexpr int32_t kMlaLat = 512;
 constexpr int32_t kMlaRow = kMlaLat + kMlaRope;  // 576
 constexpr int32_t kMlaDv = 128;
 constexpr int32_t kMlaHeadTile = 16;             // heads per MFMA tile
-constexpr int32_t kMlaKeyTile = 64;              // keys per split granule
-constexpr int32_t kMlaBlockHeads = 64;           // heads per split-kernel block
+constexpr int32_t kMlaKeyTile = 64;              // partition sizes are multiples of this
+constexpr int32_t kMlaBlockHeads = 64;           // heads per split-kernel block (a head group)
+constexpr int32_t kMlaMaxBlocks = 512;           // split blocks at the library's choice (>= CUs)
+constexpr int32_t kMlaMaxExplicitBlocks = 16384; // cap for an explicit partition size
+constexpr int32_t kMlaMinKeys = 128;             // keys per block below which fewer blocks are used
 
 struct MlaPlan {
-  int32_t partition_size = 0;
-  int32_t max_partitions = 0;
-  size_t off_qhi = 0, off_qmid = 0, off_qlo = 0, off_out = 0, off_max = 0, off_sum = 0, bytes = 0;
+  int32_t groups = 0;        // ceil(num_heads / 64)
+  int32_t max_blocks = 0;    // split-kernel blocks the workspace has partial slots for
+  size_t off_qhi = 0, off_qmid = 0, off_qlo = 0;
+  size_t off_seg_out = 0, off_seg_max = 0, off_seg_sum = 0, bytes = 0;
 };
 bool plan_mla(int32_t batch, int32_t num_heads, int32_t max_pages_per_seq, int32_t page_size,
               int32_t partition_size, MlaPlan* plan);
