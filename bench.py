@@ -294,7 +294,8 @@ def bench_mla(a, torch, pb, wl, dev) -> int:
                     "p10": round(sorted(call_ms)[len(call_ms) // 10] * 1e3, 2),
                     "p90": round(sorted(call_ms)[(9 * len(call_ms)) // 10] * 1e3, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic("mla_absorbed_decode_bs16_h128"),
                      "kernel": "mla_absorbed_decode call: absorb + split + merge/W_UV kernels",
                      "algorithmic_bytes_per_launch": nbytes,
                      "mfma_tflops": round(flops / (call_mean * 1e-3) / 1e12, 2)},
