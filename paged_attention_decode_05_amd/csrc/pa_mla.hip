@@ -53,7 +53,8 @@ constexpr int kHeadsPerWave = 16;
 constexpr int kMlaWaves = 4;
 constexpr int kGroup = kHeadsPerWave * kMlaWaves;   // heads per block
 constexpr int kMlaThreads = 64 * kMlaWaves;
-constexpr int kRowPad = kRow + 8;  // LDS row stride (elements) of a cache tile row
+constexpr int kRowPad = kRow + 16; // LDS row stride (elements) of a cache tile row: 296 dwords,
+                                   // conflict-free for the score and transposed reads
 static_assert(kGroup == kMlaBlockHeads, "head group size");
 
 struct MlaParams {
@@ -115,59 +116,74 @@ __device__ __forceinline__ uint2 lds_read_tr(const uint16_t* p) {
   return __builtin_bit_cast(uint2, v);
 }
 
-// ---- 1. absorption: q_abs = q_nope . W_UK[h], split in three; rope copied ----------
+// ---- 1. absorption: q_abs = q_nope . W_UK[h] on MFMA, split in three; rope copied ---
 //
-// Block (h, jc, bt) computes q_abs[b][h][jc*128 .. +128) for the 16 sequences
-// b = 16*bt .. +16: thread t owns latent dims j = jc*128 + 8*(t%16) .. +8
-// of sequence 16*bt + t/16 and reads W_UK[h][d][j .. j+8] as one 16-byte
-// load per d.  fp32 FMAs in ascending d.
+// Block (h, jq, bt): q_abs[b][h][jq*128 .. +128) for the 16 sequences
+// b = 16*bt .. +16, as the product [16 b x 128 d] . [128 d x 128 j] of exact
+// bf16 operands (MFMA, fp32 accumulation).  A = q_nope rows straight from
+// memory (8 consecutive d per lane); B = the W_UK[h] tile staged in LDS
+// row-major ([d][j]) and read with transposed reads, which give each lane
+// 4 consecutive d of one column j.  Wave w computes j tiles 2w and 2w+1.
+constexpr int kWukPad = 128 + 16;  // LDS row stride of the W_UK tile: 72 dwords, conflict-free
+
 __global__ __launch_bounds__(256) void mla_absorb_kernel(const MlaParams p) {
-  __shared__ float qs[16][kNope];
+  __shared__ __align__(16) uint16_t ws[kNope][kWukPad];
   const int h = blockIdx.x;
-  const int jc = blockIdx.y;
+  const int jq = blockIdx.y;
   const int b0 = blockIdx.z * 16;
   const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int g = lane >> 4;
+  const int c16 = lane & 15;
   const int nb = min(16, p.batch - b0);
-  for (int i = t; i < nb * kNope; i += 256) {
-    const int bb = i / kNope, d = i % kNope;
-    qs[bb][d] = bf16_val(p.q_nope[(static_cast<int64_t>(b0 + bb) * p.num_heads + h) * kNope + d]);
+  const uint16_t* wsrc = p.w_uk + static_cast<int64_t>(h) * kNope * kLat + jq * 128;
+  uint4 wst[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {          // 128 rows x 16 chunks of 16 B
+    const int c = t + 256 * k;
+    wst[k] = load16(wsrc + static_cast<int64_t>(c >> 4) * kLat + (c & 15) * 8);
+  }
+  uint4 qa[kNope / 32];                  // A operand: sequence b0 + c16, d = 32ks + 8g .. +8
+#pragma unroll
+  for (int ks = 0; ks < kNope / 32; ++ks)
+    qa[ks] = c16 < nb ? load16(p.q_nope + (static_cast<int64_t>(b0 + c16) * p.num_heads + h) * kNope +
+                               32 * ks + 8 * g)
+                      : make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int c = t + 256 * k;
+    *reinterpret_cast<uint4*>(&ws[c >> 4][(c & 15) * 8]) = wst[k];
   }
   __syncthreads();
-  const int c = t & 15;
-  const int bb = t >> 4;
-  const int j = jc * 128 + 8 * c;
-  const uint16_t* w = p.w_uk + static_cast<int64_t>(h) * kNope * kLat + j;
-  float acc[8];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) acc[k] = 0.0f;
-  const int br = min(bb, nb - 1);      // rows past the batch compute a copy and store nothing
-#pragma unroll 8
-  for (int d = 0; d < kNope; ++d) {
-    const uint4 wv = load16(w + static_cast<int64_t>(d) * kLat);
-    const float q = qs[br][d];
-    const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+  for (int u = 0; u < 2; ++u) {
+    const int nt = 2 * wave + u;
+    f32x4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc[2 * e] = fmaf(q, bf16_lo(ww[e]), acc[2 * e]);
-      acc[2 * e + 1] = fmaf(q, bf16_hi(ww[e]), acc[2 * e + 1]);
+    for (int ks = 0; ks < kNope / 32; ++ks) {
+      // lane (g, a) points at rows 32ks + 8g + a/4 (+4), columns 16nt + 4(a%4)
+      const uint16_t* bp = &ws[32 * ks + 8 * g + (c16 >> 2)][16 * nt + 4 * (c16 & 3)];
+      const uint2 k03 = lds_read_tr(bp);
+      const uint2 k47 = lds_read_tr(bp + 4 * kWukPad);
+      c = mfma(qa[ks], make_uint4(k03.x, k03.y, k47.x, k47.y), c);
+    }
+    // D: lane holds q_abs[b0 + 4g + i][jq*128 + 16nt + c16]
+    const int j = jq * 128 + 16 * nt + c16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int bb = 4 * g + i;
+      if (bb < nb) {
+        uint16_t hi, mid, lo;
+        split3_bf16(c[i], hi, mid, lo);
+        const int64_t row = static_cast<int64_t>(b0 + bb) * p.num_heads + h;
+        p.q_hi[row * kRow + j] = hi;
+        p.q_mid[row * kLat + j] = mid;
+        p.q_lo[row * kLat + j] = lo;
+      }
     }
   }
-  if (bb < nb) {
-    uint16_t hi[8], mid[8], lo[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) split3_bf16(acc[k], hi[k], mid[k], lo[k]);
-    const int64_t row = static_cast<int64_t>(b0 + bb) * p.num_heads + h;
-    *reinterpret_cast<uint4*>(p.q_hi + row * kRow + j) =
-        make_uint4(pack_bf16(hi[0], hi[1]), pack_bf16(hi[2], hi[3]), pack_bf16(hi[4], hi[5]),
-                   pack_bf16(hi[6], hi[7]));
-    *reinterpret_cast<uint4*>(p.q_mid + row * kLat + j) =
-        make_uint4(pack_bf16(mid[0], mid[1]), pack_bf16(mid[2], mid[3]), pack_bf16(mid[4], mid[5]),
-                   pack_bf16(mid[6], mid[7]));
-    *reinterpret_cast<uint4*>(p.q_lo + row * kLat + j) =
-        make_uint4(pack_bf16(lo[0], lo[1]), pack_bf16(lo[2], lo[3]), pack_bf16(lo[4], lo[5]),
-                   pack_bf16(lo[6], lo[7]));
-  }
-  if (jc == 0 && t < nb * (kRope / 8)) {   // rope part: exact bf16, one term
+  if (jq == 0 && t < nb * (kRope / 8)) {   // rope part: exact bf16, one term
     const int rb = t / (kRope / 8), rc = t % (kRope / 8);
     const int64_t row = static_cast<int64_t>(b0 + rb) * p.num_heads + h;
     *reinterpret_cast<uint4*>(p.q_hi + row * kRow + kLat + 8 * rc) =
@@ -176,6 +192,13 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(const MlaParams p) {
 }
 
 // ---- 2. split attention over the latent cache ----------------------------------------
+
+// Tile row of the key that MFMA row m (0..15) of a 16-key half handles.  The
+// transposed P.V reads of one 16-lane group touch the rows of m = 4g .. 4g+3;
+// mapping them to rows 2i + (g&1) + 8(g>>1) (four rows two apart) puts the
+// four 32-byte pieces in disjoint LDS banks (rows are 292 dwords apart),
+// and keeps the score operand reads of rows m = 0..7 conflict-free.
+__device__ __forceinline__ int key_row(int m) { return 2 * (m & 3) + ((m >> 2) & 1) + 8 * (m >> 3); }
 
 // Sum of the context lengths.  Called by a whole wave.
 __device__ __forceinline__ int64_t mla_total(const int32_t* ctx, int batch) {
@@ -209,9 +232,10 @@ __device__ __forceinline__ void mla_locate(const int32_t* ctx, int batch, int64_
 
 // Attention of the heads of group hg of sequence b over keys [begin, end);
 // writes the normalised partial, its max and its sum to slot.
-// Score D layout: lane l holds S^T[key 4*(l/16)+i (+16)][head l%16]; those 8
-// values are exactly the A operand of P.V for head l%16 when the P.V k-slots
-// 8g..8g+7 are taken as keys {4g..4g+3, 16+4g..16+4g+3}; the B operand
+// Score D layout: lane l holds S^T[MFMA row 4*(l/16)+i (+16)][head l%16]; MFMA
+// row m of each 16-key half is tile row key_row(m).  Those 8 values are
+// exactly the A operand of P.V for head l%16 when the P.V k-slots 8g..8g+7
+// are taken as the keys of rows {4g..4g+3, 16+4g..16+4g+3}; the B operand
 // (those keys, 16 latent columns) comes from two transposed LDS reads of the
 // key-major tile.  The softmax keeps a per-head reference max and rescales
 // the accumulators only when a score exceeds it by more than 8 (log2
@@ -231,8 +255,40 @@ __device__ __forceinline__ void mla_segment(const MlaParams& p, int b, int hg, i
   const int32_t* bt = p.block_table + static_cast<int64_t>(b) * p.bt_stride;
 
   __syncthreads();   // the previous segment is done with qlo_s and crow
+
+  // Staging of one tile: 32 keys x 72 chunks of 16 B.  Wave w stages keys
+  // 8w .. 8w+7, lane l key 8w + l/8 and its chunks l%8 + 8k (k < 9), so each
+  // lane resolves one page per tile and the chunk offsets are constants.
+  // The page of the next tile's key is fetched one tile ahead.
+  constexpr int kChunks = kRow / 8 / 8;   // 9
+  const int skey = wave * 8 + (lane >> 3);
+  const int schunk = lane & 7;
+  uint4 stage[kChunks];
+  auto page_of = [&](int t0) -> int {
+    const int t = t0 + skey;
+    return (t >= begin && t < end) ? bt[t >> p.page_shift] : -1;
+  };
+  auto load_tile = [&](int t0, int page) {
+    const uint16_t* src = p.cache + static_cast<int64_t>(max(page, 0)) * p.page_stride +
+                          static_cast<int64_t>((t0 + skey) & (p.page_size - 1)) * p.token_stride +
+                          schunk * 8;
+#pragma unroll
+    for (int k = 0; k < kChunks; ++k)
+      stage[k] = page >= 0 ? load16(src + 64 * k) : make_uint4(0, 0, 0, 0);
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int k = 0; k < kChunks; ++k)
+      *reinterpret_cast<uint4*>(&crow[skey][(schunk + 8 * k) * 8]) = stage[k];
+  };
+  const int first_tile = begin / kTileKeys;
+  const int last_tile = (end - 1) / kTileKeys;
+  load_tile(first_tile * kTileKeys, page_of(first_tile * kTileKeys));
+  int page_next = first_tile < last_tile ? page_of((first_tile + 1) * kTileKeys) : -1;
+
   // Q^T operand for all 18 k-steps: head h0 + c16, dims 32*ks + 8g .. +8;
-  // hi (18 steps) and mid (16 latent steps) in registers, lo in LDS.
+  // hi (18 steps) and mid (16 latent steps) in registers, lo in LDS, where
+  // each 1 KB row is one direct global->LDS load of the wave (64 lanes x 16 B).
   uint4 qh[kKS], qm[kKSL];
   if (active) {
     const int64_t hrow = static_cast<int64_t>(b) * p.num_heads + h0 + c16;
@@ -241,11 +297,11 @@ __device__ __forceinline__ void mla_segment(const MlaParams& p, int b, int hg, i
 #pragma unroll
     for (int ks = 0; ks < kKSL; ++ks) qm[ks] = load16(p.q_mid + hrow * kLat + 32 * ks + 8 * g);
   }
-  for (int c = tid; c < nh * (kLat / 8); c += kMlaThreads) {
-    const int r = c / (kLat / 8), cc = c % (kLat / 8);
-    *reinterpret_cast<uint4*>(&qlo_s[r][cc * 8]) =
-        load16(p.q_lo + (static_cast<int64_t>(b) * p.num_heads + hb + r) * kLat + cc * 8);
-  }
+  for (int r = wave; r < nh; r += kMlaWaves)
+    __builtin_amdgcn_global_load_lds(
+        (const __attribute__((address_space(1))) void*)(p.q_lo + (static_cast<int64_t>(b) * p.num_heads + hb + r) * kLat + 8 * lane),
+        (__attribute__((address_space(3))) void*)(&qlo_s[r][0]), 16, 0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   f32x4_t acc[kLat / 16];
 #pragma unroll
@@ -253,48 +309,28 @@ __device__ __forceinline__ void mla_segment(const MlaParams& p, int b, int hg, i
   float m_ref = -INFINITY;     // per head c16 (same on the 4 lanes of the head)
   float l_sum = 0.0f;          // this lane's share of the head's denominator
 
-  // Staging of one tile: 32 keys x 72 chunks of 16 B.  Wave w stages keys
-  // 8w .. 8w+7, lane l key 8w + l/8 and its chunks l%8 + 8k (k < 9), so each
-  // lane resolves one page per tile and the chunk offsets are constants.
-  constexpr int kChunks = kRow / 8 / 8;   // 9
-  const int skey = wave * 8 + (lane >> 3);
-  const int schunk = lane & 7;
-  uint4 stage[kChunks];
-  auto load_tile = [&](int t0) {
-    const int t = t0 + skey;
-    const bool live = t >= begin && t < end;
-    const uint16_t* src = p.cache;
-    if (live)
-      src += static_cast<int64_t>(bt[t >> p.page_shift]) * p.page_stride +
-             static_cast<int64_t>(t & (p.page_size - 1)) * p.token_stride + schunk * 8;
-#pragma unroll
-    for (int k = 0; k < kChunks; ++k)
-      stage[k] = live ? load16(src + 64 * k) : make_uint4(0, 0, 0, 0);
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int k = 0; k < kChunks; ++k)
-      *reinterpret_cast<uint4*>(&crow[skey][(schunk + 8 * k) * 8]) = stage[k];
-  };
-
-  const int first_tile = begin / kTileKeys;
-  const int last_tile = (end - 1) / kTileKeys;
-  load_tile(first_tile * kTileKeys);
   for (int tile = first_tile; tile <= last_tile; ++tile) {
     const int t0 = tile * kTileKeys;
     __syncthreads();                 // previous tile fully consumed
     store_tile();
     __syncthreads();
-    if (tile < last_tile) load_tile(t0 + kTileKeys);   // next tile streams during the math
-    if (!active) continue;
+    // The next tile's loads are issued inside the score loop, between MFMAs
+    // (waves without heads issue them here).
+    const bool more = tile < last_tile;
+    const int page_now = page_next;
+    if (more) page_next = tile + 1 < last_tile ? page_of(t0 + 2 * kTileKeys) : -1;
+    if (!active) {
+      if (more) load_tile(t0 + kTileKeys, page_now);
+      continue;
+    }
 
     // scores S^T for keys t0 .. t0+31 (two 16-key M tiles), heads h0 .. h0+15.
     // The LDS operands of step ks+1 are read while the MFMAs of step ks run;
     // the scheduling barriers keep the compiler from hoisting all 18 steps'
     // reads (which would need ~200 more registers).
     f32x4_t sc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
-    const uint16_t* arow0 = &crow[c16][8 * g];
-    const uint16_t* arow1 = &crow[16 + c16][8 * g];
+    const uint16_t* arow0 = &crow[key_row(c16)][8 * g];
+    const uint16_t* arow1 = &crow[16 + key_row(c16)][8 * g];
     const uint16_t* lrow = &qlo_s[wave * kHeadsPerWave + c16][8 * g];
     uint4 a0 = *reinterpret_cast<const uint4*>(arow0);
     uint4 a1 = *reinterpret_cast<const uint4*>(arow1);
@@ -315,19 +351,20 @@ __device__ __forceinline__ void mla_segment(const MlaParams& p, int b, int hg, i
       }
       sc[0] = mfma(a0, qh[ks], sc[0]);
       sc[1] = mfma(a1, qh[ks], sc[1]);
+      if (ks == 2 && more) load_tile(t0 + kTileKeys, page_now);
       a0 = n0;
       a1 = n1;
       qlv = nl;
       __builtin_amdgcn_sched_barrier(0);
     }
-    // lane holds keys t0 + 16*mt + 4g + i for head c16
+    // lane holds keys t0 + 16*mt + key_row(4g + i) for head c16
     float pv[8];
     float cm = -INFINITY;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int t = t0 + 16 * mt + 4 * g + i;
+        const int t = t0 + 16 * mt + key_row(4 * g + i);
         const float v = (t >= begin && t < end) ? sc[mt][i] * p.scale_log2 : -INFINITY;
         pv[4 * mt + i] = v;
         cm = fmaxf(cm, v);
@@ -365,22 +402,31 @@ __device__ __forceinline__ void mla_segment(const MlaParams& p, int b, int hg, i
     const uint4 pa_lo = make_uint4(pack_bf16(pl[0], pl[1]), pack_bf16(pl[2], pl[3]),
                                    pack_bf16(pl[4], pl[5]), pack_bf16(pl[6], pl[7]));
     // O[heads][latent] += P . C over the 32 keys of the tile; lane (g, a)
-    // points the transposed reads at rows 4g + a/4 and 16 + 4g + a/4,
-    // columns 16*jt + 4*(a%4).
-    const uint16_t* brow0 = &crow[4 * g + (c16 >> 2)][4 * (c16 & 3)];
-    const uint16_t* brow1 = &crow[16 + 4 * g + (c16 >> 2)][4 * (c16 & 3)];
-    uint2 k03 = lds_read_tr(brow0);
-    uint2 k47 = lds_read_tr(brow1);
+    // points the transposed reads at the rows of keys key_row(4g + a/4) and
+    // 16 + key_row(4g + a/4), columns 16*jt + 4*(a%4).
+    const int krow = key_row(4 * g + (c16 >> 2));
+    const uint16_t* brow0 = &crow[krow][4 * (c16 & 3)];
+    const uint16_t* brow1 = &crow[16 + krow][4 * (c16 & 3)];
+    // Two N-tiles per step, the next pair's transposed reads in flight, the
+    // MFMAs of the pair interleaved so no MFMA waits on the one before it.
+    uint2 ka0 = lds_read_tr(brow0), ka1 = lds_read_tr(brow1);
+    uint2 kb0 = lds_read_tr(brow0 + 16), kb1 = lds_read_tr(brow1 + 16);
 #pragma unroll
-    for (int jt = 0; jt < kLat / 16; ++jt) {
-      const uint4 bop = make_uint4(k03.x, k03.y, k47.x, k47.y);
-      if (jt + 1 < kLat / 16) {
-        k03 = lds_read_tr(brow0 + 16 * (jt + 1));
-        k47 = lds_read_tr(brow1 + 16 * (jt + 1));
+    for (int jt = 0; jt < kLat / 16; jt += 2) {
+      const uint4 bopa = make_uint4(ka0.x, ka0.y, ka1.x, ka1.y);
+      const uint4 bopb = make_uint4(kb0.x, kb0.y, kb1.x, kb1.y);
+      if (jt + 2 < kLat / 16) {
+        ka0 = lds_read_tr(brow0 + 16 * (jt + 2));
+        ka1 = lds_read_tr(brow1 + 16 * (jt + 2));
+        kb0 = lds_read_tr(brow0 + 16 * (jt + 3));
+        kb1 = lds_read_tr(brow1 + 16 * (jt + 3));
       }
-      acc[jt] = mfma(pa_lo, bop, acc[jt]);
-      acc[jt] = mfma(pa_mid, bop, acc[jt]);
-      acc[jt] = mfma(pa_hi, bop, acc[jt]);
+      acc[jt] = mfma(pa_lo, bopa, acc[jt]);
+      acc[jt + 1] = mfma(pa_lo, bopb, acc[jt + 1]);
+      acc[jt] = mfma(pa_mid, bopa, acc[jt]);
+      acc[jt + 1] = mfma(pa_mid, bopb, acc[jt + 1]);
+      acc[jt] = mfma(pa_hi, bopa, acc[jt]);
+      acc[jt + 1] = mfma(pa_hi, bopb, acc[jt + 1]);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -456,23 +502,30 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(const MlaParams 
 
 // ---- 3. merge of the partials, then out = W_UV[h] . o_lat on MFMA ---------------------
 //
-// Block (h, bt) handles sequences 16*bt .. +16 of head h: row (group hg, b)
+// Block (h, bt) handles sequences 8*bt .. +8 of head h: row (group hg, b)
 // was cut into pieces by blocks i0 .. i1 of the split (recomputed here from
 // the context lengths), whose partials sit in slots r + i0 .. r + i1 with
-// r = hg*batch + b.  o_lat is the l_i e^(m_i - M)/W -weighted sum of those
-// partials in ascending i, written to LDS as three bf16 terms; then
-// out[b][dv] = sum_j o_lat[b][j] W_UV[h][dv][j] with A = o_lat (16 sequences
-// x 32 latent dims per step) and B = W_UV rows, whose 8 consecutive latent
-// dims per lane are contiguous in memory.  An empty context gives 0.
-__global__ __launch_bounds__(kMlaThreads) void mla_merge_uv_kernel(const MlaParams p) {
+// r = hg*batch + b.  The max M and the total W = sum l_i e^(m_i - M) of a row
+// are wave reductions over its pieces; o_lat is the (l_i e^(m_i - M) / W)-
+// weighted sum of the pieces in ascending i (eight pieces' loads in flight),
+// written to LDS as three bf16 terms; then out[b][dv] = sum_j o_lat[b][j]
+// W_UV[h][dv][j] on MFMA with A = o_lat (rows 8..15 zero) and B = W_UV rows,
+// whose 8 consecutive latent dims per lane are contiguous in memory; wave w
+// computes dv tile w.  An empty context gives 0.
+constexpr int kMergeThreads = 512;
+constexpr int kMergeRows = 8;
+constexpr int kMergeWts = 64;      // piece weights kept in LDS per row
+
+__global__ __launch_bounds__(kMergeThreads) void mla_merge_uv_kernel(const MlaParams p) {
   __shared__ __align__(16) uint16_t ohi[16][kLat + 8];
   __shared__ __align__(16) uint16_t omid[16][kLat + 8];
   __shared__ __align__(16) uint16_t olo[16][kLat + 8];
-  __shared__ int64_t sh_slot[16];
-  __shared__ int sh_cnt[16];
-  __shared__ float sh_m[16], sh_w[16];
+  __shared__ float wts[kMergeRows][kMergeWts];
+  __shared__ int64_t sh_slot[kMergeRows];
+  __shared__ int sh_cnt[kMergeRows];
+  __shared__ float sh_m[kMergeRows], sh_iw[kMergeRows];
   const int h = blockIdx.x;
-  const int b0 = blockIdx.y * 16;
+  const int b0 = blockIdx.y * kMergeRows;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -480,7 +533,7 @@ __global__ __launch_bounds__(kMlaThreads) void mla_merge_uv_kernel(const MlaPara
   const int c16 = lane & 15;
   const int hg = h / kGroup;
   const int hl = h % kGroup;
-  const int nb16 = min(16, p.batch - b0);
+  const int nrow = min(kMergeRows, p.batch - b0);
 
   if (tid < 64) {
     const int64_t S = mla_total(p.context_lens, p.batch);
@@ -490,82 +543,121 @@ __global__ __launch_bounds__(kMlaThreads) void mla_merge_uv_kernel(const MlaPara
     int64_t before = 0;
     for (int c0 = 0; c0 < b0; c0 += 64) before += (c0 + lane < b0) ? p.context_lens[c0 + lane] : 0;
     before = wave_sum64(before);
-    const int64_t len = (lane < nb16) ? p.context_lens[b0 + lane] : 0;
+    const int64_t len = (lane < nrow) ? p.context_lens[b0 + lane] : 0;
     const int64_t pre = before + wave_scan64(len) - len;
-    if (lane < 16) {
+    if (lane < kMergeRows) {
       int64_t slot = 0;
       int cnt = 0;
-      if (lane < nb16 && len > 0) {
+      if (lane < nrow && len > 0) {
         const int64_t start = hg * S + pre;
         const int i0 = block_of(start, T, nb);
         const int i1 = block_of(start + len - 1, T, nb);
         slot = static_cast<int64_t>(hg) * p.batch + b0 + lane + i0;
         cnt = i1 - i0 + 1;
       }
-      float M = -INFINITY, W = 0.0f;
-      for (int k = 0; k < cnt; ++k) M = fmaxf(M, p.seg_max[(slot + k) * kGroup + hl]);
-      for (int k = 0; k < cnt; ++k)
-        W += p.seg_sum[(slot + k) * kGroup + hl] * __expf(p.seg_max[(slot + k) * kGroup + hl] - M);
       sh_slot[lane] = slot;
       sh_cnt[lane] = cnt;
-      sh_m[lane] = M;
-      sh_w[lane] = W;
+    }
+  }
+  // rows 8..15 of the MFMA A operand stay zero
+  for (int i = tid; i < kMergeRows * (kLat / 8); i += kMergeThreads) {
+    const int r = kMergeRows + i / (kLat / 8), c8 = (i % (kLat / 8)) * 8;
+    *reinterpret_cast<uint4*>(&ohi[r][c8]) = make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(&omid[r][c8]) = make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(&olo[r][c8]) = make_uint4(0, 0, 0, 0);
+  }
+  __syncthreads();
+  // per row: M and W over its pieces, lanes striding over the pieces (max and
+  // sum read together, the first 64 pieces' terms kept); wave w takes row w
+  {
+    const int bb = wave;
+    const int cnt = sh_cnt[bb];
+    const int64_t slot = sh_slot[bb];
+    const bool mine = lane < cnt;
+    const float m0 = mine ? p.seg_max[(slot + lane) * kGroup + hl] : -INFINITY;
+    const float l0 = mine ? p.seg_sum[(slot + lane) * kGroup + hl] : 0.0f;
+    float M = m0;
+    for (int k = lane + 64; k < cnt; k += 64) M = fmaxf(M, p.seg_max[(slot + k) * kGroup + hl]);
+    M = wave_max(M);
+    float wk = mine ? l0 * __expf(m0 - M) : 0.0f;
+    if (mine) wts[bb][lane] = wk;
+    for (int k = lane + 64; k < cnt; k += 64)
+      wk += p.seg_sum[(slot + k) * kGroup + hl] * __expf(p.seg_max[(slot + k) * kGroup + hl] - M);
+    const float W = wave_sum(wk);
+    if (lane == 0) {
+      sh_m[bb] = M;
+      sh_iw[bb] = cnt > 0 ? 1.0f / W : 0.0f;
     }
   }
   __syncthreads();
-  // o_lat for 16 sequences x 512 dims: thread owns dims (tid % 128) * 4 .. +4
-  // of rows tid / 128 + 2 rr
-  for (int rr = 0; rr < 8; ++rr) {
-    const int bb = (tid >> 7) + 2 * rr;
-    const int d0 = (tid & 127) * 4;
-    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  // o_lat for 8 sequences x 512 dims: wave w takes row w, lane l dims 8l .. 8l+8
+  {
+    const int bb = wave;
+    const int d0 = lane * 8;
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = 0.0f;
     const int cnt = sh_cnt[bb];
-    if (cnt > 0) {
-      const int64_t slot = sh_slot[bb];
-      const float M = sh_m[bb], invW = 1.0f / sh_w[bb];
-      for (int k = 0; k < cnt; ++k) {
-        const int64_t srow = (slot + k) * kGroup + hl;
-        const float w = p.seg_sum[srow] * __expf(p.seg_max[srow] - M) * invW;
-        const float4 v = *reinterpret_cast<const float4*>(p.seg_out + srow * kLat + d0);
-        o.x = fmaf(w, v.x, o.x);
-        o.y = fmaf(w, v.y, o.y);
-        o.z = fmaf(w, v.z, o.z);
-        o.w = fmaf(w, v.w, o.w);
+    const int64_t slot = sh_slot[bb];
+    const float M = sh_m[bb], iw = sh_iw[bb];
+    for (int k0 = 0; k0 < cnt; k0 += 8) {
+      float4 v[8][2];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t srow = (slot + min(k0 + u, cnt - 1)) * kGroup + hl;
+        v[u][0] = *reinterpret_cast<const float4*>(p.seg_out + srow * kLat + d0);
+        v[u][1] = *reinterpret_cast<const float4*>(p.seg_out + srow * kLat + d0 + 4);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int k = k0 + u;
+        const int64_t srow = (slot + min(k, cnt - 1)) * kGroup + hl;
+        const float w = k < cnt ? (k < kMergeWts ? wts[bb][k]
+                                                 : p.seg_sum[srow] * __expf(p.seg_max[srow] - M)) * iw
+                                : 0.0f;
+        o[0] = fmaf(w, v[u][0].x, o[0]);
+        o[1] = fmaf(w, v[u][0].y, o[1]);
+        o[2] = fmaf(w, v[u][0].z, o[2]);
+        o[3] = fmaf(w, v[u][0].w, o[3]);
+        o[4] = fmaf(w, v[u][1].x, o[4]);
+        o[5] = fmaf(w, v[u][1].y, o[5]);
+        o[6] = fmaf(w, v[u][1].z, o[6]);
+        o[7] = fmaf(w, v[u][1].w, o[7]);
       }
     }
-    uint16_t h4[4], m4[4], l4[4];
-    split3_bf16(o.x, h4[0], m4[0], l4[0]);
-    split3_bf16(o.y, h4[1], m4[1], l4[1]);
-    split3_bf16(o.z, h4[2], m4[2], l4[2]);
-    split3_bf16(o.w, h4[3], m4[3], l4[3]);
-    *reinterpret_cast<uint2*>(&ohi[bb][d0]) = make_uint2(pack_bf16(h4[0], h4[1]), pack_bf16(h4[2], h4[3]));
-    *reinterpret_cast<uint2*>(&omid[bb][d0]) = make_uint2(pack_bf16(m4[0], m4[1]), pack_bf16(m4[2], m4[3]));
-    *reinterpret_cast<uint2*>(&olo[bb][d0]) = make_uint2(pack_bf16(l4[0], l4[1]), pack_bf16(l4[2], l4[3]));
+    uint16_t h8[8], m8[8], l8[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) split3_bf16(o[e], h8[e], m8[e], l8[e]);
+    *reinterpret_cast<uint4*>(&ohi[bb][d0]) = make_uint4(pack_bf16(h8[0], h8[1]), pack_bf16(h8[2], h8[3]),
+                                                         pack_bf16(h8[4], h8[5]), pack_bf16(h8[6], h8[7]));
+    *reinterpret_cast<uint4*>(&omid[bb][d0]) = make_uint4(pack_bf16(m8[0], m8[1]), pack_bf16(m8[2], m8[3]),
+                                                          pack_bf16(m8[4], m8[5]), pack_bf16(m8[6], m8[7]));
+    *reinterpret_cast<uint4*>(&olo[bb][d0]) = make_uint4(pack_bf16(l8[0], l8[1]), pack_bf16(l8[2], l8[3]),
+                                                         pack_bf16(l8[4], l8[5]), pack_bf16(l8[6], l8[7]));
   }
   __syncthreads();
-  // out[b][dv]: wave w takes dv tiles 2w, 2w+1
-  const uint16_t* wuv = p.w_uv + static_cast<int64_t>(h) * kDv * kLat;
+  // out[b][dv]: wave w takes dv tile w; all 16 W_UV loads in flight
+  const uint16_t* wuv = p.w_uv + static_cast<int64_t>(h) * kDv * kLat +
+                        static_cast<int64_t>(16 * wave + c16) * kLat + 8 * g;
+  uint4 bw[kLat / 32];
 #pragma unroll
-  for (int nt2 = 0; nt2 < 2; ++nt2) {
-    const int nt = 2 * wave + nt2;
-    f32x4_t c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int ks = 0; ks < kLat / 32; ++ks) {
-      const uint4 a_hi = *reinterpret_cast<const uint4*>(&ohi[c16][32 * ks + 8 * g]);
-      const uint4 a_mid = *reinterpret_cast<const uint4*>(&omid[c16][32 * ks + 8 * g]);
-      const uint4 a_lo = *reinterpret_cast<const uint4*>(&olo[c16][32 * ks + 8 * g]);
-      const uint4 bw = load16(wuv + static_cast<int64_t>(16 * nt + c16) * kLat + 32 * ks + 8 * g);
-      c = mfma(a_lo, bw, c);
-      c = mfma(a_mid, bw, c);
-      c = mfma(a_hi, bw, c);
-    }
+  for (int ks = 0; ks < kLat / 32; ++ks) bw[ks] = load16(wuv + 32 * ks);
+  f32x4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int bb = 4 * g + i;
-      if (bb < nb16)
-        p.out[(static_cast<int64_t>(b0 + bb) * p.num_heads + h) * kDv + 16 * nt + c16] =
-            f32_to_bf16_rne(c[i]);
-    }
+  for (int ks = 0; ks < kLat / 32; ++ks) {
+    const uint4 a_hi = *reinterpret_cast<const uint4*>(&ohi[c16][32 * ks + 8 * g]);
+    const uint4 a_mid = *reinterpret_cast<const uint4*>(&omid[c16][32 * ks + 8 * g]);
+    const uint4 a_lo = *reinterpret_cast<const uint4*>(&olo[c16][32 * ks + 8 * g]);
+    c = mfma(a_lo, bw[ks], c);
+    c = mfma(a_mid, bw[ks], c);
+    c = mfma(a_hi, bw[ks], c);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int bb = 4 * g + i;
+    if (bb < nrow)
+      p.out[(static_cast<int64_t>(b0 + bb) * p.num_heads + h) * kDv + 16 * wave + c16] =
+          f32_to_bf16_rne(c[i]);
   }
 }
 
@@ -661,8 +753,9 @@ int mla_absorbed_decode(const void* q_nope, const void* q_rope, const void* kv_c
   hipLaunchKernelGGL(pa::mla_split_kernel, dim3(p.split_grid), dim3(pa::kMlaThreads), 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return pa::fail(PA_ERR_LAUNCH, std::string("split: ") + hipGetErrorString(e));
-  hipLaunchKernelGGL(pa::mla_merge_uv_kernel, dim3(num_heads, btiles), dim3(pa::kMlaThreads), 0, s,
-                     p);
+  hipLaunchKernelGGL(pa::mla_merge_uv_kernel,
+                     dim3(num_heads, (batch + pa::kMergeRows - 1) / pa::kMergeRows),
+                     dim3(pa::kMergeThreads), 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return pa::fail(PA_ERR_LAUNCH, std::string("merge: ") + hipGetErrorString(e));
   return PA_OK;
