@@ -101,7 +101,7 @@ def main() -> int:
     Hkv = c0.num_kv_heads
     kv_bytes = [c.kv_bytes() for c in cases]
     ws_bytes = pb.pa_decode_workspace_size(B, H, Hkv, D, c0.max_pages, c0.page_size, c0.window)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
     out = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
     kvl = [pb.kv_layout(d.k_pool, d.layout) for d in dcs]
 

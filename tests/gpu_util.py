@@ -21,7 +21,7 @@ def run_decode(dc, with_lse=True, workspace=None):
     if workspace is None:
         nbytes = pb.pa_decode_workspace_size(B, H, dc.num_kv_heads, D, dc.max_pages, dc.page_size,
                                              dc.window)
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        workspace = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
     pb.pa_decode(dc.q, dc.k_pool, dc.v_pool, kv, dc.block_table, dc.context_lens, dc.scale,
                  dc.window, out, lse, workspace)
     torch.cuda.synchronize()
