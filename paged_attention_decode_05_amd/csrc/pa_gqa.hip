@@ -79,7 +79,9 @@ struct Geo {
   static constexpr int TQ = 64 / LQ;
   static constexpr int LV = D / 8;
   static constexpr int TV = 64 / LV;
-  static constexpr int CH = (G >= 16) ? 16 : (D == 128 ? 32 : 16);   // keys per chunk
+  // keys per chunk: 8 for D = 256 with G >= 8, which keeps the K/V buffers
+  // small enough for two waves per SIMD
+  static constexpr int CH = (D == 256 && G >= 8) ? 8 : (G >= 16) ? 16 : (D == 128 ? 32 : 16);
   static constexpr int NTQ = CH / TQ;
   static constexpr int NV = CH / TV;
   static constexpr int LOG_G = ilog2c(G);
@@ -601,7 +603,7 @@ template <int D, int G>
 __device__ __forceinline__ void merge_segments(const BalancedLayout& bl, int64_t slot0, int count,
                                                uint16_t* out, float* lse) {
   constexpr int kBatch = 16;
-  for (int i = threadIdx.x; i < G * D; i += kBlock) {
+  for (int i = blockIdx.y * kBlock + threadIdx.x; i < G * D; i += kBlock * gridDim.y) {
     const int h = i / D;
     const int d = i % D;
     const float* pm = bl.seg_max + slot0 * G + h;
@@ -634,8 +636,9 @@ __device__ __forceinline__ void merge_segments(const BalancedLayout& bl, int64_t
   }
 }
 
-// One block per row (b, g): rows with no key get zeros and lse -inf, rows
-// that one block covered are already written, the rest are merged here.
+// Block (r, y) handles outputs y*256 .. +256 of the G*D of row r = (b, g):
+// rows with no key get zeros and lse -inf, rows that one block covered are
+// already written, the rest are merged here.
 template <int D, int G>
 __global__ __launch_bounds__(kBlock) void balanced_merge_kernel(const BalancedLayout bl,
                                                                int num_q_heads, int window,
@@ -662,8 +665,9 @@ __global__ __launch_bounds__(kBlock) void balanced_merge_kernel(const BalancedLa
   const int64_t len = seq_len(bl.context_lens, b, window);
   const int64_t h0 = static_cast<int64_t>(b) * num_q_heads + static_cast<int64_t>(gk) * G;
   if (len == 0) {
-    for (int i = threadIdx.x; i < G * D; i += kBlock) bl.out[h0 * D + i] = 0;
-    if (bl.lse && threadIdx.x < G) bl.lse[h0 + threadIdx.x] = -INFINITY;
+    for (int i = blockIdx.y * kBlock + threadIdx.x; i < G * D; i += kBlock * gridDim.y)
+      bl.out[h0 * D + i] = 0;
+    if (bl.lse && blockIdx.y == 0 && threadIdx.x < G) bl.lse[h0 + threadIdx.x] = -INFINITY;
     return;
   }
   const int nb = used_blocks(T, split_grid, bl.min_units);
@@ -784,8 +788,8 @@ static hipError_t launch_balanced_dg(const SplitParams& p, const BalancedLayout&
   hipLaunchKernelGGL((balanced_split_kernel<D, G>), dim3(grid), dim3(kBlock), 0, stream, p, bl);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((balanced_merge_kernel<D, G>), dim3(bl.rows), dim3(kBlock), 0, stream, bl,
-                     p.num_q_heads, p.window, grid);
+  hipLaunchKernelGGL((balanced_merge_kernel<D, G>), dim3(bl.rows, (G * D + kBlock - 1) / kBlock),
+                     dim3(kBlock), 0, stream, bl, p.num_q_heads, p.window, grid);
   return hipGetLastError();
 }
 

@@ -42,7 +42,7 @@ int check_merge(const float* part_out, const float* part_max, const float* part_
 // Workspace carve-up of pa_decode (balanced split): the segment partials,
 // one slot per (row, block) segment, rows + kMaxBalancedBlocks slots in all.
 constexpr int32_t kMaxBalancedBlocks = 2048;
-constexpr int64_t kMinUnitsPerBlock = 512;   // keys (of one KV head) below which a block is not worth it
+constexpr int64_t kMinUnitsPerBlock = 128;   // keys (of one KV head) below which a block is not worth it
 
 struct DecodePlan {
   int32_t rows = 0;          // batch * num_kv_heads
