@@ -77,6 +77,13 @@ class Oracle:
                           C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_double,
                           f64p, f64p, f64p]
             f.restype = C.c_int
+        i64p = C.POINTER(C.c_int64)
+        self.lib.oracle_kv_insert.argtypes = [u16p, u16p, C.c_int64, C.c_int64, u16p, u16p, pool,
+                                              i64p, C.c_int32]
+        self.lib.oracle_kv_insert.restype = C.c_int
+        self.lib.oracle_mla_cache_insert.argtypes = [u16p, C.c_int64, u16p, C.c_int64, u16p, pool,
+                                                     i64p, C.c_int32, C.c_int32, C.c_int32]
+        self.lib.oracle_mla_cache_insert.restype = C.c_int
         self.lib.oracle_set_num_threads.argtypes = [C.c_int32]
         self.lib.oracle_max_threads.restype = C.c_int32
         self.lib.oracle_mutation.restype = C.c_int32
@@ -151,6 +158,40 @@ class Oracle:
             int(partition_size), P, int(window), _ptr(out, f64), _ptr(lse, f64))
         self._check(rc, "oracle_pa_merge")
         return out, lse
+
+    # ---- cache writes ----------------------------------------------------------
+    def kv_insert(self, k_new: torch.Tensor, v_new: torch.Tensor, k_pool: torch.Tensor,
+                  v_pool: torch.Tensor, pool: _Pool, slots) -> tuple:
+        """Copies of the two pools after inserting k_new / v_new ([T, Hkv, D]
+        bf16, contiguous) at the flat slots (int64); bf16 CPU tensors."""
+        kn, vn = _bits(k_new), _bits(v_new)
+        kp, vp = _bits(k_pool).copy(), _bits(v_pool).copy()
+        sl = np.ascontiguousarray(torch.as_tensor(slots).cpu().numpy(), np.int64)
+        T, Hkv, D = k_new.shape
+        u16, i64 = C.c_uint16, C.c_int64
+        rc = self.lib.oracle_kv_insert(_ptr(kn, u16), _ptr(vn, u16), Hkv * D, D, _ptr(kp, u16),
+                                       _ptr(vp, u16), C.byref(pool), _ptr(sl, i64), T)
+        self._check(rc, "oracle_kv_insert")
+        back = lambda a, like: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).reshape(like.shape)
+        return back(kp, k_pool), back(vp, v_pool)
+
+    def mla_cache_insert(self, kv_c: torch.Tensor, k_pe: torch.Tensor, cache: torch.Tensor,
+                         slots) -> torch.Tensor:
+        """Copy of the latent cache [P, page, d_lat + d_rope] after writing
+        kv_c [T, d_lat] ++ k_pe [T, d_rope] (bf16, contiguous) at the slots."""
+        c, pe = _bits(kv_c), _bits(k_pe)
+        out = _bits(cache).copy()
+        sl = np.ascontiguousarray(torch.as_tensor(slots).cpu().numpy(), np.int64)
+        T, d_lat = kv_c.shape
+        d_rope = k_pe.shape[1]
+        P, S, R = cache.shape
+        pool = _Pool(P, S, 1, R, S * R, 0, R)
+        u16, i64 = C.c_uint16, C.c_int64
+        rc = self.lib.oracle_mla_cache_insert(_ptr(c, u16), d_lat, _ptr(pe, u16), d_rope,
+                                              _ptr(out, u16), C.byref(pool), _ptr(sl, i64), T,
+                                              d_lat, d_rope)
+        self._check(rc, "oracle_mla_cache_insert")
+        return torch.from_numpy(out.view(np.int16)).view(torch.bfloat16).reshape(cache.shape)
 
     # ---- absorbed MLA --------------------------------------------------------
     def mla(self, case, precision: str = "f64", want_q_abs: bool = False):

@@ -13,6 +13,8 @@
  *   3 slot mirrored inside a page   8 MLA value row shifted by d_rope
  *   4 W_UK read as [j][d]           9 MLA rope term dropped
  *   5 lse without the max          10 split partitions counted from key 0
+ *  11 KV insert: page and in-page offset of a slot swapped
+ *  12 MLA insert: rope part written first, latent after it
  */
 #include <math.h>
 #include <stdlib.h>
@@ -77,3 +79,68 @@ int32_t oracle_max_threads(void) {
 }
 
 int32_t oracle_mutation(void) { return ORACLE_MUTATION; }
+
+/* KV insert ("reshape and cache"): token i of the source goes to the flat
+ * slot s = slots[i] = page * page_size + offset of the pool, every KV head,
+ * as a plain copy of the bf16 bits [vllm.cpp kernel matrix, row
+ * KERNEL-KV-CACHE: KV insert into the paged cache, checked exactly since a
+ * copy does not round].  Slots outside [0, num_pages * page_size) -- negative
+ * ones mark padding -- are skipped. */
+int oracle_kv_insert(const uint16_t* k_new, const uint16_t* v_new, int64_t src_token_stride,
+                     int64_t src_head_stride, uint16_t* k_pool, uint16_t* v_pool,
+                     const oracle_pool* pool, const int64_t* slots, int32_t num_tokens) {
+  if (!k_new || !v_new || !k_pool || !v_pool || !pool || !slots || num_tokens < 0 ||
+      pool->num_pages <= 0 || pool->page_size <= 0 || pool->num_kv_heads <= 0 ||
+      pool->head_dim <= 0)
+    return ORACLE_ERR_ARGS;
+  const int64_t total = (int64_t)pool->num_pages * pool->page_size;
+  for (int32_t i = 0; i < num_tokens; ++i) {
+    const int64_t s = slots[i];
+    if (s < 0 || s >= total) continue;
+#if ORACLE_MUTATION == 11
+    const int64_t page = s % pool->page_size, off = s / pool->page_size; /* planted */
+    if (page >= pool->num_pages || off >= pool->page_size) continue;
+#else
+    const int64_t page = s / pool->page_size, off = s % pool->page_size;
+#endif
+    for (int32_t h = 0; h < pool->num_kv_heads; ++h) {
+      const int64_t dst = page * pool->page_stride + h * pool->head_stride + off * pool->token_stride;
+      const int64_t src = i * src_token_stride + h * src_head_stride;
+      for (int32_t d = 0; d < pool->head_dim; ++d) {
+        k_pool[dst + d] = k_new[src + d];
+        v_pool[dst + d] = v_new[src + d];
+      }
+    }
+  }
+  return ORACLE_OK;
+}
+
+/* MLA cache write: row s of the latent cache becomes the latent part kv_c
+ * (d_lat values) followed by the rope part k_pe (d_rope values), copied bit
+ * for bit [vllm.cpp kernel matrix, row KERNEL-KV-CACHE: the MLA cache write
+ * concatenates the two projections into the 576-wide row, exact, with
+ * strided sources].  Slots outside the pool are skipped. */
+int oracle_mla_cache_insert(const uint16_t* kv_c, int64_t c_stride, const uint16_t* k_pe,
+                            int64_t pe_stride, uint16_t* cache, const oracle_pool* pool,
+                            const int64_t* slots, int32_t num_tokens, int32_t d_lat,
+                            int32_t d_rope) {
+  if (!kv_c || !k_pe || !cache || !pool || !slots || num_tokens < 0 || d_lat <= 0 ||
+      d_rope < 0 || pool->num_kv_heads != 1 || pool->head_dim != d_lat + d_rope ||
+      pool->num_pages <= 0 || pool->page_size <= 0)
+    return ORACLE_ERR_ARGS;
+  const int64_t total = (int64_t)pool->num_pages * pool->page_size;
+  for (int32_t i = 0; i < num_tokens; ++i) {
+    const int64_t s = slots[i];
+    if (s < 0 || s >= total) continue;
+    uint16_t* row = cache + (s / pool->page_size) * pool->page_stride +
+                    (s % pool->page_size) * pool->token_stride;
+#if ORACLE_MUTATION == 12
+    for (int32_t r = 0; r < d_rope; ++r) row[r] = k_pe[i * pe_stride + r]; /* planted */
+    for (int32_t j = 0; j < d_lat; ++j) row[d_rope + j] = kv_c[i * c_stride + j];
+#else
+    for (int32_t j = 0; j < d_lat; ++j) row[j] = kv_c[i * c_stride + j];
+    for (int32_t r = 0; r < d_rope; ++r) row[d_lat + r] = k_pe[i * pe_stride + r];
+#endif
+  }
+  return ORACLE_OK;
+}

@@ -118,6 +118,19 @@ int32_t oracle_max_threads(void);
 /* Which planted mistake (0 = none) this build carries; see pa_oracle.c. */
 int32_t oracle_mutation(void);
 
+/* KV insert: token i of k_new / v_new ([token][kv head][dim] with the given
+ * element strides) is copied to flat slot slots[i] = page * page_size + offset
+ * of both pools; slots outside the pool are skipped. */
+int oracle_kv_insert(const uint16_t* k_new, const uint16_t* v_new, int64_t src_token_stride,
+                     int64_t src_head_stride, uint16_t* k_pool, uint16_t* v_pool,
+                     const oracle_pool* pool, const int64_t* slots, int32_t num_tokens);
+
+/* MLA cache write: row slots[i] becomes kv_c[i][0:d_lat] ++ k_pe[i][0:d_rope]. */
+int oracle_mla_cache_insert(const uint16_t* kv_c, int64_t c_stride, const uint16_t* k_pe,
+                            int64_t pe_stride, uint16_t* cache, const oracle_pool* pool,
+                            const int64_t* slots, int32_t num_tokens, int32_t d_lat,
+                            int32_t d_rope);
+
 #ifdef __cplusplus
 }
 #endif

@@ -16,6 +16,12 @@ builds with a planted mistake (at least one must fail).
                        empty -> (0, -inf)
   mla_unabsorbed       absorbed MLA == unabsorbed MLA (float64, < 1e-11)
   nan_canaries         NaN in every slot outside the key ranges changes nothing
+  kv_insert_roundtrip  inserted rows read back bit-exact through independent
+                       page/offset indexing; padding and out-of-range slots and
+                       every other element untouched
+  insert_then_decode   rows knocked out of a pool and inserted again at each
+                       sequence's last position give a bit-identical decode
+  mla_insert_concat    latent ++ rope land in the 576-wide row in that order
 """
 from __future__ import annotations
 
@@ -265,6 +271,94 @@ def nan_canaries(o):
     assert not np.isnan(b).any() and np.array_equal(a, b)
 
 
+def _slot(bt_row, t, page_size):
+    return int(bt_row[t // page_size]) * page_size + t % page_size
+
+
+def _row(pool, layout, slot, page_size, g):
+    page, off = slot // page_size, slot % page_size
+    return pool[page, g, off] if layout == "PHSD" else pool[page, off, g]
+
+
+def kv_insert_roundtrip(o):
+    from oracle.oracle import _Pool
+    gen = torch.Generator().manual_seed(7120)
+    for layout, Hkv, D, ps in (("PHSD", 2, 16, 8), ("PSHD", 3, 8, 16)):
+        case = make_gqa_case(context_lens=(5, 40), num_q_heads=Hkv, num_kv_heads=Hkv, head_dim=D,
+                             page_size=ps, seed=7121, layout=layout, poison=False, pool_pages=12)
+        total = case.num_pages * ps
+        slots = [3, total - 1, -1, 17, total, 40, 2 * ps]       # -1 padding, total out of range
+        T = len(slots)
+        k_new = torch.randn(T, Hkv, D, generator=gen).to(torch.bfloat16)
+        v_new = torch.randn(T, Hkv, D, generator=gen).to(torch.bfloat16)
+        ps_, hs, ts = case.strides()
+        pool = _Pool(case.num_pages, ps, Hkv, D, ps_, hs, ts)
+        k2, v2 = o.kv_insert(k_new, v_new, case.k_pool, case.v_pool, pool, slots)
+        touched = torch.zeros(case.k_pool.shape[:3], dtype=torch.bool)
+        for i, s in enumerate(slots):
+            if not 0 <= s < total:
+                continue
+            for g in range(Hkv):
+                assert torch.equal(_row(k2, layout, s, ps, g).view(torch.int16),
+                                   k_new[i, g].view(torch.int16))
+                assert torch.equal(_row(v2, layout, s, ps, g).view(torch.int16),
+                                   v_new[i, g].view(torch.int16))
+                page, off = s // ps, s % ps
+                if layout == "PHSD":
+                    touched[page, g, off] = True
+                else:
+                    touched[page, off, g] = True
+        keep = ~touched
+        assert torch.equal(k2[keep].view(torch.int16), case.k_pool[keep].view(torch.int16))
+        assert torch.equal(v2[keep].view(torch.int16), case.v_pool[keep].view(torch.int16))
+
+
+def insert_then_decode(o):
+    from oracle.oracle import _Pool
+    for layout in ("PHSD", "PSHD"):
+        case = make_gqa_case(context_lens=(1, 17, 32, 33), num_q_heads=4, num_kv_heads=2,
+                             head_dim=16, page_size=16, seed=7122, layout=layout, poison=False)
+        ref, ref_lse = o.decode(case, "f64")
+        bt = case.block_table.numpy()
+        slots = [_slot(bt[b], int(n) - 1, 16) for b, n in enumerate(case.context_lens.tolist())]
+        k_new = torch.stack([torch.stack([_row(case.k_pool, layout, s, 16, g) for g in range(2)])
+                             for s in slots])
+        v_new = torch.stack([torch.stack([_row(case.v_pool, layout, s, 16, g) for g in range(2)])
+                             for s in slots])
+        damaged = case.to("cpu")
+        damaged.k_pool = case.k_pool.clone()
+        damaged.v_pool = case.v_pool.clone()
+        for s in slots:
+            for g in range(2):
+                _row(damaged.k_pool, layout, s, 16, g).fill_(float("nan"))
+                _row(damaged.v_pool, layout, s, 16, g).fill_(float("nan"))
+        ps_, hs, ts = case.strides()
+        pool = _Pool(case.num_pages, 16, 2, 16, ps_, hs, ts)
+        damaged.k_pool, damaged.v_pool = o.kv_insert(k_new, v_new, damaged.k_pool, damaged.v_pool,
+                                                     pool, slots)
+        out, lse = o.decode(damaged, "f64")
+        assert np.array_equal(out, ref) and np.array_equal(lse, ref_lse)
+
+
+def mla_insert_concat(o):
+    gen = torch.Generator().manual_seed(7123)
+    P, S, dl, dr = 6, 8, 12, 4
+    cache = torch.randn(P, S, dl + dr, generator=gen).to(torch.bfloat16)
+    slots = [0, 13, -1, P * S - 1, P * S]
+    kv_c = torch.randn(len(slots), dl, generator=gen).to(torch.bfloat16)
+    k_pe = torch.randn(len(slots), dr, generator=gen).to(torch.bfloat16)
+    out = o.mla_cache_insert(kv_c, k_pe, cache, slots)
+    touched = torch.zeros(P, S, dtype=torch.bool)
+    for i, s in enumerate(slots):
+        if not 0 <= s < P * S:
+            continue
+        row = out[s // S, s % S]
+        assert torch.equal(row[:dl].view(torch.int16), kv_c[i].view(torch.int16))
+        assert torch.equal(row[dl:].view(torch.int16), k_pe[i].view(torch.int16))
+        touched[s // S, s % S] = True
+    assert torch.equal(out[~touched].view(torch.int16), cache[~touched].view(torch.int16))
+
+
 PINS = {
     "dense_bruteforce": dense_bruteforce,
     "single_token": single_token,
@@ -276,6 +370,9 @@ PINS = {
     "merge_equals_unsplit": merge_equals_unsplit,
     "mla_unabsorbed": mla_unabsorbed,
     "nan_canaries": nan_canaries,
+    "kv_insert_roundtrip": kv_insert_roundtrip,
+    "insert_then_decode": insert_then_decode,
+    "mla_insert_concat": mla_insert_concat,
 }
 
 

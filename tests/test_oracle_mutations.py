@@ -24,6 +24,8 @@ MUTATIONS = {
     8: "MLA value row shifted",
     9: "MLA rope term dropped",
     10: "split partitions counted from key 0",
+    11: "KV insert with page and offset swapped",
+    12: "MLA insert with the rope part first",
 }
 
 
