@@ -226,6 +226,45 @@ PA_API size_t mla_absorbed_decode_workspace_size(int32_t batch, int32_t num_head
                                           int32_t page_size,
                                           int32_t partition_size);
 
+/* ---------------------------------------------------------------------------
+ * pa_kv_insert -- write new tokens' K and V rows into the paged pools.
+ *
+ * Token i of k_new / v_new ([token][kv head][head_dim] bf16, element strides
+ * src_token_stride and src_head_stride, head_dim contiguous) is copied bit
+ * for bit to flat slot s = slots[i] = page * page_size + offset of k_pool /
+ * v_pool (layout *kv), for every KV head [vllm.cpp kernel matrix, row
+ * KERNEL-KV-CACHE: KV insert into the paged cache, an exact copy].  This is
+ * the step before decode: the new token of sequence b goes to slot
+ * block_table[b][t / page_size] * page_size + t % page_size with
+ * t = context_lens[b] - 1.
+ *
+ * slots: num_tokens int64, device.  Slots outside [0, num_pages *
+ * page_size) are skipped (negative marks padding).  Two tokens with the same
+ * slot race.  head_dim any multiple of 8; strides multiples of 8 elements
+ * (a head stride may be 0 for a one-head pool); pointers 16-byte aligned.
+ * num_tokens 0 is a no-op.  Returns PA_OK or an error code (nothing launched).
+ * ------------------------------------------------------------------------- */
+PA_API int pa_kv_insert(const void* k_new, const void* v_new, int64_t src_token_stride,
+                        int64_t src_head_stride, void* k_pool, void* v_pool,
+                        const pa_kv_layout* kv, const int64_t* slots,
+                        int32_t num_tokens, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * mla_cache_insert -- write new tokens' rows into the MLA latent cache.
+ *
+ * Row slots[i] of the cache (layout *cache: num_kv_heads 1, head_dim 576)
+ * becomes kv_c[i][0:512] followed by k_pe[i][0:64], copied bit for bit
+ * [vllm.cpp kernel matrix, row KERNEL-KV-CACHE: the MLA cache write
+ * concatenates the latent and rope projections into the 576-wide row, from
+ * strided sources].  kv_c rows c_stride elements apart, k_pe rows pe_stride
+ * apart (multiples of 8; c_stride >= 512, pe_stride >= 64), bf16, 16-byte
+ * aligned.  Slots outside the cache are skipped.  Returns PA_OK or an error
+ * code (nothing launched).
+ * ------------------------------------------------------------------------- */
+PA_API int mla_cache_insert(const void* kv_c, int64_t c_stride, const void* k_pe,
+                            int64_t pe_stride, void* kv_cache, const pa_kv_layout* cache,
+                            const int64_t* slots, int32_t num_tokens, void* stream);
+
 /* Text describing the last non-zero status returned on the calling thread
  * ("" if none).  The pointer stays valid until the next call on that thread. */
 PA_API const char* pa_last_error(void);

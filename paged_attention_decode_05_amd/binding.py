@@ -23,7 +23,8 @@ STATUS_NAMES = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_U
 
 EXPORTS = ("pa_decode", "pa_decode_splitkv", "pa_merge_lse", "pa_decode_workspace_size",
            "pa_decode_partition_size", "mla_absorbed_decode",
-           "mla_absorbed_decode_workspace_size", "pa_last_error")
+           "mla_absorbed_decode_workspace_size", "pa_kv_insert", "mla_cache_insert",
+           "pa_last_error")
 
 
 class PaError(RuntimeError):
@@ -63,6 +64,11 @@ def _load() -> C.CDLL:
     lib.mla_absorbed_decode.restype = C.c_int
     lib.mla_absorbed_decode_workspace_size.argtypes = [i32] * 5
     lib.mla_absorbed_decode_workspace_size.restype = C.c_size_t
+    i64, i64p = C.c_int64, C.POINTER(C.c_int64)
+    lib.pa_kv_insert.argtypes = [vp, vp, i64, i64, vp, vp, kvp, vp, i32, vp]
+    lib.pa_kv_insert.restype = C.c_int
+    lib.mla_cache_insert.argtypes = [vp, i64, vp, i64, vp, kvp, vp, i32, vp]
+    lib.mla_cache_insert.restype = C.c_int
     lib.pa_last_error.argtypes = []
     lib.pa_last_error.restype = C.c_char_p
     return lib
@@ -211,4 +217,39 @@ def mla_absorbed_decode(q_nope, q_rope, kv_cache, cache: KvLayout, w_uk, w_uv, b
                                  float(scale), int(partition_size),
                                  _ptr(out, torch.bfloat16, "out"), _ptr(workspace), ws_bytes,
                                  _stream(stream))
+    _check(rc)
+
+
+def _rows(t: torch.Tensor, name: str, ndim: int) -> None:
+    if t.dim() != ndim or t.stride(-1) != 1:
+        raise ValueError(f"{name}: expected {ndim} dims with a contiguous last axis")
+
+
+def pa_kv_insert(k_new, v_new, k_pool, v_pool, kv: KvLayout, slots, stream=None) -> None:
+    """k_new / v_new [T, Hkv, D] bf16 (any strides with a contiguous last
+    axis, the same for both); slots [T] int64 flat slot indices."""
+    _rows(k_new, "k_new", 3)
+    _rows(v_new, "v_new", 3)
+    if k_new.shape != v_new.shape or k_new.stride() != v_new.stride():
+        raise ValueError("k_new and v_new must have the same shape and strides")
+    _contig(slots, "slots")
+    rc = LIB.pa_kv_insert(_ptr(k_new, torch.bfloat16, "k_new"), _ptr(v_new, torch.bfloat16, "v_new"),
+                          k_new.stride(0), k_new.stride(1), _ptr(k_pool, torch.bfloat16, "k_pool"),
+                          _ptr(v_pool, torch.bfloat16, "v_pool"), C.byref(kv),
+                          _ptr(slots, torch.int64, "slots"), k_new.shape[0], _stream(stream))
+    _check(rc)
+
+
+def mla_cache_insert(kv_c, k_pe, kv_cache, cache: KvLayout, slots, stream=None) -> None:
+    """kv_c [T, 512] and k_pe [T, 64] bf16 (row strides free, last axis
+    contiguous); slots [T] int64."""
+    _rows(kv_c, "kv_c", 2)
+    _rows(k_pe, "k_pe", 2)
+    if kv_c.shape[0] != k_pe.shape[0]:
+        raise ValueError("kv_c and k_pe must have the same number of rows")
+    _contig(slots, "slots")
+    rc = LIB.mla_cache_insert(_ptr(kv_c, torch.bfloat16, "kv_c"), kv_c.stride(0),
+                              _ptr(k_pe, torch.bfloat16, "k_pe"), k_pe.stride(0),
+                              _ptr(kv_cache, torch.bfloat16, "kv_cache"), C.byref(cache),
+                              _ptr(slots, torch.int64, "slots"), kv_c.shape[0], _stream(stream))
     _check(rc)

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpa_decode.so")
 
-SOURCES = ["pa_api.hip", "pa_gqa.hip", "pa_mla.hip", "pa_validate.cpp"]
+SOURCES = ["pa_api.hip", "pa_gqa.hip", "pa_mla.hip", "pa_cache.hip", "pa_validate.cpp"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

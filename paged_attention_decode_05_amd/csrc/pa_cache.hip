@@ -1,0 +1,156 @@
+// pa_cache.hip -- writes into the paged caches: K/V insert and the MLA
+// latent-cache write.
+//
+// Token i goes to the flat slot s = slots[i] = page * page_size + offset
+// [vllm.cpp kernel matrix, row KERNEL-KV-CACHE: KV insert into the paged
+// cache; the MLA cache write concatenates the latent and rope projections
+// into the 576-wide row; both are exact copies].  One thread moves one
+// 16-byte chunk (8 bf16) from the source row to the cache row; the flat
+// thread index runs over (token, chunk), so a launch covers any number of
+// tokens with full 16-byte accesses.  Slots outside [0, num_pages *
+// page_size) -- negative ones mark padding -- are skipped, so no slot value
+// can make the kernel write outside the pool.
+#include <hip/hip_runtime.h>
+
+#include <string>
+
+#include "pa_decode.h"
+#include "pa_device.h"
+#include "pa_validate.h"
+
+namespace pa {
+
+constexpr int kCopyThreads = 256;
+
+struct KvInsertParams {
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  uint16_t* k_pool;
+  uint16_t* v_pool;
+  const int64_t* slots;
+  int64_t src_token_stride, src_head_stride;
+  int64_t page_stride, head_stride, token_stride;
+  int64_t total_slots;
+  int64_t num_tokens;
+  int32_t page_size;
+  int32_t chunks_per_head;    // head_dim / 8
+  int32_t chunks_per_tensor;  // num_kv_heads * head_dim / 8
+};
+
+// Thread x: token x / (2 * chunks_per_tensor); within it, K chunks first,
+// then V chunks; chunk c of a tensor is head c / chunks_per_head, dims
+// 8 * (c % chunks_per_head) .. +8.
+__global__ __launch_bounds__(kCopyThreads) void kv_insert_kernel(const KvInsertParams p) {
+  const int64_t x = static_cast<int64_t>(blockIdx.x) * kCopyThreads + threadIdx.x;
+  const int64_t per_token = 2 * static_cast<int64_t>(p.chunks_per_tensor);
+  if (x >= p.num_tokens * per_token) return;
+  const int64_t i = x / per_token;
+  int c = static_cast<int>(x - i * per_token);
+  const bool is_v = c >= p.chunks_per_tensor;
+  if (is_v) c -= p.chunks_per_tensor;
+  const int64_t s = p.slots[i];
+  if (s < 0 || s >= p.total_slots) return;
+  const int h = c / p.chunks_per_head;
+  const int d = 8 * (c - h * p.chunks_per_head);
+  const int64_t page = s / p.page_size, off = s - page * p.page_size;
+  const int64_t src = i * p.src_token_stride + h * p.src_head_stride + d;
+  const int64_t dst = page * p.page_stride + h * p.head_stride + off * p.token_stride + d;
+  const uint4 v = load16((is_v ? p.v_new : p.k_new) + src);
+  *reinterpret_cast<uint4*>((is_v ? p.v_pool : p.k_pool) + dst) = v;
+}
+
+struct MlaInsertParams {
+  const uint16_t* kv_c;
+  const uint16_t* k_pe;
+  uint16_t* cache;
+  const int64_t* slots;
+  int64_t c_stride, pe_stride;
+  int64_t page_stride, token_stride;
+  int64_t total_slots;
+  int64_t num_tokens;
+  int32_t page_size;
+};
+
+// Thread x: token x / 72, chunk x % 72 of the 576-wide row: chunks 0..63 come
+// from the latent source, 64..71 from the rope source.
+__global__ __launch_bounds__(kCopyThreads) void mla_insert_kernel(const MlaInsertParams p) {
+  constexpr int kLatChunks = kMlaLat / 8, kRowChunks = kMlaRow / 8;
+  const int64_t x = static_cast<int64_t>(blockIdx.x) * kCopyThreads + threadIdx.x;
+  if (x >= p.num_tokens * kRowChunks) return;
+  const int64_t i = x / kRowChunks;
+  const int c = static_cast<int>(x - i * kRowChunks);
+  const int64_t s = p.slots[i];
+  if (s < 0 || s >= p.total_slots) return;
+  const int64_t page = s / p.page_size, off = s - page * p.page_size;
+  const uint4 v = c < kLatChunks ? load16(p.kv_c + i * p.c_stride + 8 * c)
+                                 : load16(p.k_pe + i * p.pe_stride + 8 * (c - kLatChunks));
+  *reinterpret_cast<uint4*>(p.cache + page * p.page_stride + off * p.token_stride + 8 * c) = v;
+}
+
+}  // namespace pa
+
+extern "C" {
+
+int pa_kv_insert(const void* k_new, const void* v_new, int64_t src_token_stride,
+                 int64_t src_head_stride, void* k_pool, void* v_pool, const pa_kv_layout* kv,
+                 const int64_t* slots, int32_t num_tokens, void* stream) {
+  const int rc = pa::check_kv_insert(k_new, v_new, src_token_stride, src_head_stride, k_pool,
+                                     v_pool, kv, slots, num_tokens);
+  if (rc) return rc;
+  if (num_tokens == 0) return PA_OK;
+  pa::KvInsertParams p{};
+  p.k_new = static_cast<const uint16_t*>(k_new);
+  p.v_new = static_cast<const uint16_t*>(v_new);
+  p.k_pool = static_cast<uint16_t*>(k_pool);
+  p.v_pool = static_cast<uint16_t*>(v_pool);
+  p.slots = slots;
+  p.src_token_stride = src_token_stride;
+  p.src_head_stride = src_head_stride;
+  p.page_stride = kv->page_stride;
+  p.head_stride = kv->head_stride;
+  p.token_stride = kv->token_stride;
+  p.total_slots = static_cast<int64_t>(kv->num_pages) * kv->page_size;
+  p.num_tokens = num_tokens;
+  p.page_size = kv->page_size;
+  p.chunks_per_head = kv->head_dim / 8;
+  p.chunks_per_tensor = kv->num_kv_heads * (kv->head_dim / 8);
+  const int64_t threads = static_cast<int64_t>(num_tokens) * 2 * p.chunks_per_tensor;
+  const int64_t blocks = (threads + pa::kCopyThreads - 1) / pa::kCopyThreads;
+  pa::clear_error();
+  hipLaunchKernelGGL(pa::kv_insert_kernel, dim3(static_cast<unsigned>(blocks)),
+                     dim3(pa::kCopyThreads), 0, static_cast<hipStream_t>(stream), p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return pa::fail(PA_ERR_LAUNCH, std::string("kv insert: ") + hipGetErrorString(e));
+  return PA_OK;
+}
+
+int mla_cache_insert(const void* kv_c, int64_t c_stride, const void* k_pe, int64_t pe_stride,
+                     void* kv_cache, const pa_kv_layout* cache, const int64_t* slots,
+                     int32_t num_tokens, void* stream) {
+  const int rc = pa::check_mla_insert(kv_c, c_stride, k_pe, pe_stride, kv_cache, cache, slots,
+                                      num_tokens);
+  if (rc) return rc;
+  if (num_tokens == 0) return PA_OK;
+  pa::MlaInsertParams p{};
+  p.kv_c = static_cast<const uint16_t*>(kv_c);
+  p.k_pe = static_cast<const uint16_t*>(k_pe);
+  p.cache = static_cast<uint16_t*>(kv_cache);
+  p.slots = slots;
+  p.c_stride = c_stride;
+  p.pe_stride = pe_stride;
+  p.page_stride = cache->page_stride;
+  p.token_stride = cache->token_stride;
+  p.total_slots = static_cast<int64_t>(cache->num_pages) * cache->page_size;
+  p.num_tokens = num_tokens;
+  p.page_size = cache->page_size;
+  const int64_t threads = static_cast<int64_t>(num_tokens) * (pa::kMlaRow / 8);
+  const int64_t blocks = (threads + pa::kCopyThreads - 1) / pa::kCopyThreads;
+  pa::clear_error();
+  hipLaunchKernelGGL(pa::mla_insert_kernel, dim3(static_cast<unsigned>(blocks)),
+                     dim3(pa::kCopyThreads), 0, static_cast<hipStream_t>(stream), p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return pa::fail(PA_ERR_LAUNCH, std::string("mla insert: ") + hipGetErrorString(e));
+  return PA_OK;
+}
+
+}  // extern "C"

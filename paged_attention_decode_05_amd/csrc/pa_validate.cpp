@@ -230,4 +230,51 @@ int check_mla(const void* q_nope, const void* q_rope, const void* kv_cache,
   return PA_OK;
 }
 
+// Checks of the cache writes.  A stride of 0 is allowed for the head axis of
+// a one-head pool; every other stride is a positive multiple of 8 elements.
+static bool stride_ok(int64_t s, bool may_be_zero) { return (may_be_zero && s == 0) || mult8(s); }
+
+int check_kv_insert(const void* k_new, const void* v_new, int64_t src_token_stride,
+                    int64_t src_head_stride, const void* k_pool, const void* v_pool,
+                    const pa_kv_layout* kv, const int64_t* slots, int32_t num_tokens) {
+  if (!k_new || !v_new || !k_pool || !v_pool || !kv || !slots)
+    return fail(PA_ERR_NULL, "a required pointer is NULL");
+  if (num_tokens < 0) return fail(PA_ERR_SHAPE, "num_tokens must be >= 0");
+  if (kv->num_pages < 1 || kv->page_size < 1 || kv->num_kv_heads < 1 || kv->head_dim < 8)
+    return fail(PA_ERR_SHAPE, "pool: num_pages, page_size, num_kv_heads >= 1, head_dim >= 8");
+  if (kv->head_dim % 8) return fail(PA_ERR_UNSUPPORTED, "head_dim must be a multiple of 8");
+  const bool one_head = kv->num_kv_heads == 1;
+  if (!mult8(kv->page_stride) || !stride_ok(kv->head_stride, one_head) || !mult8(kv->token_stride) ||
+      !mult8(src_token_stride) || !stride_ok(src_head_stride, one_head))
+    return fail(PA_ERR_ALIGN, "strides must be positive multiples of 8 elements");
+  if (kv->token_stride < kv->head_dim || (!one_head && src_head_stride < kv->head_dim))
+    return fail(PA_ERR_SHAPE, "rows of one token and head must not overlap");
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool))
+    return fail(PA_ERR_ALIGN, "k_new, v_new, k_pool and v_pool must be 16-byte aligned");
+  const int64_t blocks = ceil_div(static_cast<int64_t>(num_tokens) * 2 * kv->num_kv_heads *
+                                      (kv->head_dim / 8), 256);
+  if (blocks > INT32_MAX) return fail(PA_ERR_SHAPE, "too many tokens for one launch");
+  return PA_OK;
+}
+
+int check_mla_insert(const void* kv_c, int64_t c_stride, const void* k_pe, int64_t pe_stride,
+                     const void* kv_cache, const pa_kv_layout* cache, const int64_t* slots,
+                     int32_t num_tokens) {
+  if (!kv_c || !k_pe || !kv_cache || !cache || !slots)
+    return fail(PA_ERR_NULL, "a required pointer is NULL");
+  if (num_tokens < 0) return fail(PA_ERR_SHAPE, "num_tokens must be >= 0");
+  if (cache->num_pages < 1 || cache->page_size < 1)
+    return fail(PA_ERR_SHAPE, "cache: num_pages and page_size must be >= 1");
+  if (cache->num_kv_heads != 1 || cache->head_dim != kMlaRow)
+    return fail(PA_ERR_UNSUPPORTED, "MLA cache must have num_kv_heads 1 and head_dim 576");
+  if (!mult8(cache->page_stride) || !mult8(cache->token_stride) || !mult8(c_stride) ||
+      !mult8(pe_stride))
+    return fail(PA_ERR_ALIGN, "strides must be positive multiples of 8 elements");
+  if (cache->token_stride < kMlaRow || c_stride < kMlaLat || pe_stride < kMlaRope)
+    return fail(PA_ERR_SHAPE, "token_stride >= 576, c_stride >= 512 and pe_stride >= 64 required");
+  if (!aligned16(kv_c) || !aligned16(k_pe) || !aligned16(kv_cache))
+    return fail(PA_ERR_ALIGN, "kv_c, k_pe and kv_cache must be 16-byte aligned");
+  return PA_OK;
+}
+
 }  // namespace pa

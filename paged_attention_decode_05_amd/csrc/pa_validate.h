@@ -85,4 +85,12 @@ int check_mla(const void* q_nope, const void* q_rope, const void* kv_cache,
               const int32_t* context_lens, int32_t batch, int32_t num_heads,
               int32_t max_pages_per_seq, float scale, int32_t partition_size, const void* out);
 
+int check_kv_insert(const void* k_new, const void* v_new, int64_t src_token_stride,
+                    int64_t src_head_stride, const void* k_pool, const void* v_pool,
+                    const pa_kv_layout* kv, const int64_t* slots, int32_t num_tokens);
+
+int check_mla_insert(const void* kv_c, int64_t c_stride, const void* k_pe, int64_t pe_stride,
+                     const void* kv_cache, const pa_kv_layout* cache, const int64_t* slots,
+                     int32_t num_tokens);
+
 }  // namespace pa

@@ -145,3 +145,45 @@ def test_mla_rejections():
     assert _mla() == PA["WORKSPACE"]
     assert pb.mla_absorbed_decode_workspace_size(16, 128, 128, 64, 0) > 0
     assert pb.mla_absorbed_decode_workspace_size(16, 100, 128, 64, 0) == 0
+
+
+def _ins(kv=None, n=4, ts=256, hs=128, **kw):
+    kv = kv or _kv()
+    a = dict(k=FAKE, v=FAKE, kp=FAKE, vp=FAKE, sl=FAKE)
+    a.update(kw)
+    return pb.LIB.pa_kv_insert(a["k"], a["v"], ts, hs, a["kp"], a["vp"], C.byref(kv), a["sl"], n,
+                               None)
+
+
+def test_kv_insert_rejections():
+    assert _ins(k=None) == PA["NULL"]
+    assert _ins(sl=None) == PA["NULL"]
+    assert _ins(n=-1) == PA["SHAPE"]
+    assert _ins(kv=_kv(head_dim=12, token_stride=16)) == PA["UNSUPPORTED"]
+    assert _ins(ts=260) == PA["ALIGN"]
+    assert _ins(kv=_kv(token_stride=132)) == PA["ALIGN"]           # not a multiple of 8
+    assert _ins(kv=_kv(token_stride=64)) == PA["SHAPE"]            # rows would overlap
+    assert _ins(hs=64) == PA["SHAPE"]
+    assert _ins(vp=FAKE + 8) == PA["ALIGN"]
+    # zero tokens is a valid no-op: nothing is launched
+    assert _ins(n=0) == PA["OK"]
+
+
+def _mins(cache=None, n=4, cs=512, ps=64, **kw):
+    cache = cache or pb.KvLayout(100, 64, 1, 576, 64 * 576, 0, 576)
+    a = dict(c=FAKE, pe=FAKE, kc=FAKE, sl=FAKE)
+    a.update(kw)
+    return pb.LIB.mla_cache_insert(a["c"], cs, a["pe"], ps, a["kc"], C.byref(cache), a["sl"], n,
+                                   None)
+
+
+def test_mla_cache_insert_rejections():
+    assert _mins(c=None) == PA["NULL"]
+    assert _mins(n=-2) == PA["SHAPE"]
+    assert _mins(cache=pb.KvLayout(100, 64, 1, 512, 64 * 512, 0, 512)) == PA["UNSUPPORTED"]
+    assert _mins(cache=pb.KvLayout(100, 64, 2, 576, 64 * 576, 0, 576)) == PA["UNSUPPORTED"]
+    assert _mins(cs=500) == PA["ALIGN"]
+    assert _mins(cs=504) == PA["SHAPE"]
+    assert _mins(ps=56) == PA["SHAPE"]
+    assert _mins(pe=FAKE + 4) == PA["ALIGN"]
+    assert _mins(n=0) == PA["OK"]
