@@ -72,6 +72,10 @@ class Oracle:
             f.argtypes = [f64p, f64p, f64p, i32p, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
                           C.c_int32, C.c_int32, f64p, f64p]
             f.restype = C.c_int
+            f = getattr(self.lib, "oracle_pa_decode_multi" + sfx)
+            f.argtypes = [u16p, u16p, u16p, pool, i32p, C.c_int32, i32p, C.c_int32, C.c_int32,
+                          C.c_int32, C.c_int32, C.c_double, C.c_int32, f64p, f64p]
+            f.restype = C.c_int
             f = getattr(self.lib, "oracle_mla_decode" + sfx)
             f.argtypes = [u16p, u16p, u16p, pool, u16p, u16p, i32p, C.c_int32, i32p, C.c_int32,
                           C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_double,
@@ -124,6 +128,23 @@ class Oracle:
             bt.shape[1], _ptr(ctx, i32), B, H, float(case.scale), int(w),
             _ptr(out, f64), _ptr(lse, f64))
         self._check(rc, "oracle_pa_decode")
+        return out, lse
+
+    def decode_multi(self, case, causal: bool = True, precision: str = "f64"):
+        """(out [B,S,Hq,D], lse [B,S,Hq]) for a GqaCase whose q is [B, S, Hq, D]."""
+        q4 = case.q if case.q.dim() == 4 else case.q[:, None]
+        B, S, H, D = q4.shape
+        q, k, v = _bits(q4), _bits(case.k_pool), _bits(case.v_pool)
+        bt, ctx = _i32(case.block_table), _i32(case.context_lens)
+        out = np.zeros((B, S, H, D), np.float64)
+        lse = np.zeros((B, S, H), np.float64)
+        pool = self._pool_of(case)
+        u16, i32, f64 = C.c_uint16, C.c_int32, C.c_double
+        rc = getattr(self.lib, "oracle_pa_decode_multi_" + precision)(
+            _ptr(q, u16), _ptr(k, u16), _ptr(v, u16), C.byref(pool), _ptr(bt, i32),
+            bt.shape[1], _ptr(ctx, i32), B, H, S, int(bool(causal)), float(case.scale),
+            int(case.window), _ptr(out, f64), _ptr(lse, f64))
+        self._check(rc, "oracle_pa_decode_multi")
         return out, lse
 
     def partials(self, case, partition_size: int, max_parts: int, precision: str = "f64"):

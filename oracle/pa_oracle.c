@@ -15,6 +15,7 @@
  *   5 lse without the max          10 split partitions counted from key 0
  *  11 KV insert: page and in-page offset of a slot swapped
  *  12 MLA insert: rope part written first, latent after it
+ *  13 multi-query decode: causal limit one key too far
  */
 #include <math.h>
 #include <stdlib.h>

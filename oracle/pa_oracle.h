@@ -109,6 +109,19 @@ ORACLE_DECL_PARTIALS(_f64)
 ORACLE_DECL_PARTIALS(_f32)
 ORACLE_DECL_MERGE(_f64)
 ORACLE_DECL_MERGE(_f32)
+/* Multi-query decode: q [B][S][Hq][D], out [B][S][Hq][D], lse [B][S][Hq];
+ * query s sees keys t <= n - S + s (causal) or t < n (not causal), and with
+ * a window only the last `window` of those. */
+#define ORACLE_DECL_MULTI(SFX)                                                  \
+  int oracle_pa_decode_multi##SFX(                                             \
+      const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,       \
+      const oracle_pool* pool, const int32_t* block_table, int32_t bt_stride,  \
+      const int32_t* context_lens, int32_t batch, int32_t num_q_heads,         \
+      int32_t num_queries, int32_t causal, double scale, int32_t window,       \
+      double* out, double* lse);
+
+ORACLE_DECL_MULTI(_f64)
+ORACLE_DECL_MULTI(_f32)
 ORACLE_DECL_MLA(_f64)
 ORACLE_DECL_MLA(_f32)
 

@@ -145,6 +145,62 @@ int NAME(oracle_pa_decode)(const uint16_t* q, const uint16_t* k_pool,
   return err;
 }
 
+/* Multi-query decode (the verify step of speculative decoding): sequence b
+ * carries S query tokens at the last S positions of its context, q laid out
+ * [b][s][h][d].  Query s sees keys up to its own position n - S + s when
+ * causal, or the whole context otherwise; a window counts back from the last
+ * key it sees [pegainfer PR #938, commit message: the b=8 and b=16 verify
+ * steps; vllm.cpp kernel matrix, row KERNEL-ATTN-DFLASH-PAGED-BLOCK: the
+ * (1+k) block queries attend over the paged context that holds their own
+ * block, with an in-block mask that is either causal or not].  A query with
+ * no key gives out = 0, lse = -inf. */
+int NAME(oracle_pa_decode_multi)(const uint16_t* q, const uint16_t* k_pool,
+                                 const uint16_t* v_pool, const oracle_pool* pool,
+                                 const int32_t* block_table, int32_t bt_stride,
+                                 const int32_t* context_lens, int32_t batch,
+                                 int32_t num_q_heads, int32_t num_queries, int32_t causal,
+                                 double scale, int32_t window, double* out, double* lse) {
+  if (!q || !k_pool || !v_pool || !NAME(check_pool)(pool) || !block_table ||
+      !context_lens || !out || !lse || batch < 0 || num_q_heads <= 0 || num_queries <= 0 ||
+      num_q_heads % pool->num_kv_heads != 0)
+    return ORACLE_ERR_ARGS;
+  const int32_t D = pool->head_dim;
+  const int32_t S = num_queries;
+  int err = ORACLE_OK;
+#pragma omp parallel for collapse(3) schedule(dynamic)
+  for (int32_t b = 0; b < batch; ++b) {
+    for (int32_t sq = 0; sq < S; ++sq) {
+      for (int32_t h = 0; h < num_q_heads; ++h) {
+        const int32_t n = context_lens[b];
+#if ORACLE_MUTATION == 13
+        const int32_t last = causal ? n - S + sq + 1 : n - 1; /* planted: one key too far */
+#else
+        const int32_t last = causal ? n - S + sq : n - 1;
+#endif
+        const int32_t hi = last + 1 < n ? last + 1 : n;
+        const int32_t lo = window > 0 ? (hi - window > 0 ? hi - window : 0) : 0;
+        const int64_t row = ((int64_t)b * S + sq) * num_q_heads + h;
+        const int32_t g = NAME(kv_head_of)(h, num_q_heads, pool->num_kv_heads);
+        REAL* o = (REAL*)malloc(sizeof(REAL) * (size_t)D);
+        REAL m = 0, l = 0;
+        int rc = !o ? ORACLE_ERR_ARGS
+                    : NAME(attend_range)(q + row * D, k_pool, v_pool, pool,
+                                         block_table + (int64_t)b * bt_stride, g,
+                                         lo > 0 ? lo : 0, hi > 0 ? hi : 0, (REAL)scale, &m, &l, o);
+        if (rc != ORACLE_OK) {
+#pragma omp atomic write
+          err = rc;
+        } else {
+          for (int32_t d = 0; d < D; ++d) out[row * D + d] = (double)o[d];
+          lse[row] = (l > 0) ? (double)(m + LOGR(l)) : -INFINITY;
+        }
+        free(o);
+      }
+    }
+  }
+  return err;
+}
+
 int NAME(oracle_pa_partials)(const uint16_t* q, const uint16_t* k_pool,
                              const uint16_t* v_pool, const oracle_pool* pool,
                              const int32_t* block_table, int32_t bt_stride,

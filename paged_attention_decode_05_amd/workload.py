@@ -67,7 +67,12 @@ class GqaCase:
 
     @property
     def num_q_heads(self) -> int:
-        return int(self.q.shape[1])
+        return int(self.q.shape[-2])
+
+    @property
+    def num_queries(self) -> int:
+        """Query tokens per sequence: q is [B, Hq, D] (1) or [B, S, Hq, D]."""
+        return int(self.q.shape[1]) if self.q.dim() == 4 else 1
 
     @property
     def max_pages(self) -> int:
@@ -81,10 +86,12 @@ class GqaCase:
         return s[0], s[2], s[1]
 
     def kv_read_tokens(self) -> int:
-        """Keys each KV head streams per call (window-limited)."""
+        """Keys each KV head streams per call (window-limited; with several
+        queries, the union of their key ranges)."""
         tot = 0
+        reach = self.window + self.num_queries - 1
         for n in self.context_lens.tolist():
-            lo = max(0, n - self.window) if self.window > 0 else 0
+            lo = max(0, n - reach) if self.window > 0 else 0
             tot += n - lo
         return tot
 
@@ -213,10 +220,14 @@ def make_gqa_case(*, context_lens: Sequence[int], num_q_heads: int, num_kv_heads
                   pool_pages: Optional[int] = None, layout: str = "PHSD", window: int = 0,
                   q_std: float = 1.0, scale: Optional[float] = None, poison: bool = True,
                   partition_size: Optional[int] = None, name: str = "custom",
-                  ctx_draw: Optional[tuple] = None, batch: Optional[int] = None) -> GqaCase:
+                  ctx_draw: Optional[tuple] = None, batch: Optional[int] = None,
+                  num_queries: int = 1) -> GqaCase:
     """Build one GQA decode case.  ``ctx_draw=(lo, hi)`` draws ``batch`` context
     lengths uniformly from the integers lo..hi (inclusive) instead of using
-    ``context_lens``."""
+    ``context_lens``.  ``num_queries`` > 1 gives q of shape [B, S, Hq, D] (the
+    last S positions of each context), for multi-query decode; the NaN
+    canaries then spare the S - 1 keys the earlier queries' windows reach
+    further back."""
     if layout not in LAYOUTS:
         raise ValueError(layout)
     gen = torch.Generator().manual_seed(int(seed))
@@ -230,7 +241,8 @@ def make_gqa_case(*, context_lens: Sequence[int], num_q_heads: int, num_kv_heads
         max_pages = max(1, (top + page_size - 1) // page_size)
     bt, pool_pages = _assign_pages(gen, ctx, page_size, max_pages, pool_pages)
     B = len(ctx)
-    q = _normal_bf16(gen, (B, num_q_heads, head_dim), q_std)
+    qshape = (B, num_q_heads, head_dim) if num_queries == 1 else (B, num_queries, num_q_heads, head_dim)
+    q = _normal_bf16(gen, qshape, q_std)
     if layout == "PHSD":
         shape = (pool_pages, num_kv_heads, page_size, head_dim)
     else:
@@ -238,8 +250,9 @@ def make_gqa_case(*, context_lens: Sequence[int], num_q_heads: int, num_kv_heads
     k_pool = _normal_bf16(gen, shape)
     v_pool = _normal_bf16(gen, shape)
     if poison:
-        _poison_gqa(k_pool, layout, bt, ctx, page_size, window)
-        _poison_gqa(v_pool, layout, bt, ctx, page_size, window)
+        reach = window + num_queries - 1 if window > 0 else 0
+        _poison_gqa(k_pool, layout, bt, ctx, page_size, reach)
+        _poison_gqa(v_pool, layout, bt, ctx, page_size, reach)
     return GqaCase(q=q, k_pool=k_pool, v_pool=v_pool, block_table=bt,
                    context_lens=torch.tensor(ctx, dtype=torch.int32), num_pages=pool_pages,
                    page_size=page_size, num_kv_heads=num_kv_heads, head_dim=head_dim,

@@ -87,3 +87,35 @@ def mla_unabsorbed(case):
             e = np.exp(s - s.max())
             out[b, h] = (e @ v) / e.sum()
     return out
+
+
+def dense_multi(case, causal: bool):
+    """(out [B,S,Hq,D], lse [B,S,Hq]) in float64 for a multi-query case:
+    query s of sequence b sees keys t <= n - S + s (causal) or t < n, and
+    with a window only the last `window` of them."""
+    K = pool_f64(case.k_pool)
+    V = pool_f64(case.v_pool)
+    q = case.q.to(torch.float64).numpy()
+    bt = case.block_table.numpy()
+    ctx = case.context_lens.numpy()
+    B, S, H, D = q.shape
+    G = H // case.num_kv_heads
+    out = np.zeros((B, S, H, D))
+    lse = np.full((B, S, H), -np.inf)
+    for b in range(B):
+        n = int(ctx[b])
+        for s in range(S):
+            hi = min(n, n - S + s + 1) if causal else n
+            lo = max(0, hi - case.window) if case.window > 0 else 0
+            if hi <= lo:
+                continue
+            t = np.arange(lo, hi)
+            for h in range(H):
+                k = gather_rows(K, case.layout, bt[b], t, case.page_size, h // G)
+                v = gather_rows(V, case.layout, bt[b], t, case.page_size, h // G)
+                sc = case.scale * (k @ q[b, s, h])
+                m = sc.max()
+                e = np.exp(sc - m)
+                out[b, s, h] = (e @ v) / e.sum()
+                lse[b, s, h] = m + np.log(e.sum())
+    return out, lse

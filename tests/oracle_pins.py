@@ -22,6 +22,11 @@ builds with a planted mistake (at least one must fail).
   insert_then_decode   rows knocked out of a pool and inserted again at each
                        sequence's last position give a bit-identical decode
   mla_insert_concat    latent ++ rope land in the 576-wide row in that order
+  multi_single_query   multi-query decode with one query == decode, bit for bit
+  multi_is_shortened   causal query s == decode over the first n - S + 1 + s
+                       keys (with and without a window), bit for bit
+  multi_noncausal      every non-causal query == decode over the whole context
+  multi_bruteforce     multi-query decode == float64 dense causal attention
 """
 from __future__ import annotations
 
@@ -359,6 +364,58 @@ def mla_insert_concat(o):
     assert torch.equal(out[~touched].view(torch.int16), cache[~touched].view(torch.int16))
 
 
+def _multi_case(S, window, seed, ctx=(2, 5, 33, 70)):
+    return make_gqa_case(context_lens=ctx, num_q_heads=4, num_kv_heads=2, head_dim=16,
+                         page_size=8, seed=seed, window=window, num_queries=S)
+
+
+def _single_of(case, s, ctx_shift):
+    one = case.to("cpu")
+    one.q = (case.q if case.q.dim() == 4 else case.q[:, None])[:, s].contiguous()
+    one.context_lens = (case.context_lens - ctx_shift).clamp(min=0).to(torch.int32)
+    return one
+
+
+def multi_single_query(o):
+    for causal in (True, False):
+        case = _multi_case(1, 0, 7130)
+        out, lse = o.decode_multi(case, causal)
+        ref, ref_lse = o.decode(_single_of(case, 0, 0))
+        assert np.array_equal(out[:, 0], ref) and np.array_equal(lse[:, 0], ref_lse)
+
+
+def multi_is_shortened(o):
+    for window in (0, 20):
+        case = _multi_case(3, window, 7131)
+        out, lse = o.decode_multi(case, True)
+        for s in range(3):
+            ref, ref_lse = o.decode(_single_of(case, s, 3 - 1 - s))
+            assert np.array_equal(out[:, s], ref) and np.array_equal(lse[:, s], ref_lse), (window, s)
+
+
+def multi_noncausal(o):
+    case = _multi_case(3, 0, 7132)
+    out, lse = o.decode_multi(case, False)
+    for s in range(3):
+        ref, ref_lse = o.decode(_single_of(case, s, 0))
+        assert np.array_equal(out[:, s], ref) and np.array_equal(lse[:, s], ref_lse)
+
+
+def multi_bruteforce(o):
+    import brute
+    for causal, window in ((True, 0), (True, 6), (False, 0)):
+        case = _multi_case(4, window, 7133, ctx=(1, 3, 9, 40))
+        case_clean = make_gqa_case(context_lens=(1, 3, 9, 40), num_q_heads=4, num_kv_heads=2,
+                                   head_dim=16, page_size=8, seed=7133, window=window,
+                                   num_queries=4, poison=False)
+        ref, ref_lse = brute.dense_multi(case_clean, causal)
+        out, lse = o.decode_multi(case, causal)
+        assert np.abs(out - ref).max() < 1e-12, (causal, window, np.abs(out - ref).max())
+        fin = np.isfinite(ref_lse)
+        assert np.array_equal(fin, np.isfinite(lse))
+        assert np.abs(lse[fin] - ref_lse[fin]).max() < 1e-12
+
+
 PINS = {
     "dense_bruteforce": dense_bruteforce,
     "single_token": single_token,
@@ -373,6 +430,10 @@ PINS = {
     "kv_insert_roundtrip": kv_insert_roundtrip,
     "insert_then_decode": insert_then_decode,
     "mla_insert_concat": mla_insert_concat,
+    "multi_single_query": multi_single_query,
+    "multi_is_shortened": multi_is_shortened,
+    "multi_noncausal": multi_noncausal,
+    "multi_bruteforce": multi_bruteforce,
 }
 
 

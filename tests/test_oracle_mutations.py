@@ -26,6 +26,7 @@ MUTATIONS = {
     10: "split partitions counted from key 0",
     11: "KV insert with page and offset swapped",
     12: "MLA insert with the rope part first",
+    13: "multi-query causal limit one key too far",
 }
 
 
