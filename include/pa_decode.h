@@ -165,6 +165,42 @@ PA_API int pa_decode(const void* q, const void* k_pool, const void* v_pool,
               float scale, int32_t window, void* out, float* lse_out,
               void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * pa_decode_multiquery -- decode with S query tokens per sequence (the verify
+ * step of speculative decoding, or a block of draft queries).
+ *
+ * The S queries of sequence b stand at the last S positions of its context
+ * (context_lens[b] counts them; their K/V rows are already in the pools).
+ * Query s attends to keys t <= context_lens[b] - S + s when causal != 0, to
+ * all keys t < context_lens[b] otherwise; with window > 0 only to the last
+ * `window` of those [pegainfer PR #938, commit message: the b=8 and b=16
+ * verify steps; vllm.cpp kernel matrix, row KERNEL-ATTN-DFLASH-PAGED-BLOCK:
+ * the (1+k) block queries attend over the paged context holding their own
+ * block, under a causal or a non-causal in-block mask].  All S queries of a
+ * KV group share one pass over its K/V rows, as S * (Hq / Hkv) heads.  A
+ * query with no key gives out = 0 and lse = -inf.
+ *
+ * q [batch][S][num_q_heads][head_dim] bf16; out the same shape; lse_out
+ * [batch][S][num_q_heads] fp32 or NULL.  1 <= S <= 16, and S rounded up to a
+ * power of two times num_q_heads / num_kv_heads must be 1, 2, 4, 8 or 16
+ * (head_dim 128) or 1, 2, 4, 8 (head_dim 256).  workspace: at least
+ * pa_decode_multiquery_workspace_size(...) bytes, 256-byte aligned,
+ * clobbered.  S = 1 gives exactly pa_decode.  Other arguments as pa_decode.
+ * ------------------------------------------------------------------------- */
+PA_API int pa_decode_multiquery(const void* q, const void* k_pool, const void* v_pool,
+                                const pa_kv_layout* kv, const int32_t* block_table,
+                                int32_t block_table_stride, const int32_t* context_lens,
+                                int32_t batch, int32_t num_q_heads, int32_t num_queries,
+                                int32_t causal, int32_t max_pages_per_seq, float scale,
+                                int32_t window, void* out, float* lse_out, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace pa_decode_multiquery needs (0 on invalid shapes). */
+PA_API size_t pa_decode_multiquery_workspace_size(int32_t batch, int32_t num_q_heads,
+                                                  int32_t num_kv_heads, int32_t head_dim,
+                                                  int32_t max_pages_per_seq, int32_t page_size,
+                                                  int32_t window, int32_t num_queries);
+
 /* Bytes of workspace pa_decode needs for these shapes (0 on invalid shapes). */
 PA_API size_t pa_decode_workspace_size(int32_t batch, int32_t num_q_heads,
                                 int32_t num_kv_heads, int32_t head_dim,

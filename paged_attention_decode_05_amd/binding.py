@@ -24,7 +24,7 @@ STATUS_NAMES = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_U
 EXPORTS = ("pa_decode", "pa_decode_splitkv", "pa_merge_lse", "pa_decode_workspace_size",
            "pa_decode_partition_size", "mla_absorbed_decode",
            "mla_absorbed_decode_workspace_size", "pa_kv_insert", "mla_cache_insert",
-           "pa_last_error")
+           "pa_decode_multiquery", "pa_decode_multiquery_workspace_size", "pa_last_error")
 
 
 class PaError(RuntimeError):
@@ -64,6 +64,11 @@ def _load() -> C.CDLL:
     lib.mla_absorbed_decode.restype = C.c_int
     lib.mla_absorbed_decode_workspace_size.argtypes = [i32] * 5
     lib.mla_absorbed_decode_workspace_size.restype = C.c_size_t
+    lib.pa_decode_multiquery.argtypes = [vp, vp, vp, kvp, i32p, i32, i32p, i32, i32, i32, i32,
+                                         i32, C.c_float, i32, vp, vp, vp, C.c_size_t, vp]
+    lib.pa_decode_multiquery.restype = C.c_int
+    lib.pa_decode_multiquery_workspace_size.argtypes = [i32] * 8
+    lib.pa_decode_multiquery_workspace_size.restype = C.c_size_t
     i64, i64p = C.c_int64, C.POINTER(C.c_int64)
     lib.pa_kv_insert.argtypes = [vp, vp, i64, i64, vp, vp, kvp, vp, i32, vp]
     lib.pa_kv_insert.restype = C.c_int
@@ -252,4 +257,33 @@ def mla_cache_insert(kv_c, k_pe, kv_cache, cache: KvLayout, slots, stream=None) 
                               _ptr(k_pe, torch.bfloat16, "k_pe"), k_pe.stride(0),
                               _ptr(kv_cache, torch.bfloat16, "kv_cache"), C.byref(cache),
                               _ptr(slots, torch.int64, "slots"), kv_c.shape[0], _stream(stream))
+    _check(rc)
+
+
+def pa_decode_multiquery_workspace_size(batch, num_q_heads, num_kv_heads, head_dim,
+                                        max_pages_per_seq, page_size, window, num_queries) -> int:
+    return int(LIB.pa_decode_multiquery_workspace_size(batch, num_q_heads, num_kv_heads, head_dim,
+                                                       max_pages_per_seq, page_size, window,
+                                                       num_queries))
+
+
+def pa_decode_multiquery(q, k_pool, v_pool, kv: KvLayout, block_table, context_lens, scale: float,
+                         window: int, causal: bool, out, lse_out=None, workspace=None,
+                         max_pages_per_seq=None, stream=None) -> None:
+    """q and out [B, S, Hq, D] bf16 (contiguous); lse_out [B, S, Hq] fp32 or None."""
+    for t, n in ((q, "q"), (block_table, "block_table"), (context_lens, "context_lens"),
+                 (out, "out")):
+        _contig(t, n)
+    B, S, H = q.shape[0], q.shape[1], q.shape[2]
+    maxp = block_table.shape[1] if max_pages_per_seq is None else max_pages_per_seq
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = LIB.pa_decode_multiquery(_ptr(q, torch.bfloat16, "q"), _ptr(k_pool, torch.bfloat16, "k_pool"),
+                                  _ptr(v_pool, torch.bfloat16, "v_pool"), C.byref(kv),
+                                  _ptr(block_table, torch.int32, "block_table"),
+                                  block_table.stride(0),
+                                  _ptr(context_lens, torch.int32, "context_lens"), B, H, S,
+                                  int(bool(causal)), maxp, float(scale), int(window),
+                                  _ptr(out, torch.bfloat16, "out"),
+                                  _ptr(lse_out, torch.float32, "lse_out"), _ptr(workspace),
+                                  ws_bytes, _stream(stream))
     _check(rc)

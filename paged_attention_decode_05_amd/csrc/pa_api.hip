@@ -73,9 +73,15 @@ pa::SplitParams split_params(const void* q, const void* k_pool, const void* v_po
   p.page_bytes = static_cast<uint32_t>(kv->page_stride * 2);
   p.bt_stride = block_table_stride;
   p.num_q_heads = num_q_heads;
+  p.kv_heads = kv->num_kv_heads;
   p.page_size = kv->page_size;
   p.page_shift = ilog2(kv->page_size);
   p.window = window;
+  p.num_queries = 1;
+  p.q_heads = num_q_heads;
+  p.group_shift = ilog2(num_q_heads / kv->num_kv_heads);
+  p.causal = 1;
+  p.reach = window;
   p.partition_size = partition_size;
   p.max_parts = max_partitions;
   p.write_empty = write_empty;
@@ -148,29 +154,39 @@ int32_t pa_decode_partition_size(int32_t batch, int32_t num_q_heads, int32_t num
   return pa::suggest_partition(batch, num_kv_heads, head_dim, max_pages_per_seq, page_size, window);
 }
 
-int pa_decode(const void* q, const void* k_pool, const void* v_pool, const pa_kv_layout* kv,
-              const int32_t* block_table, int32_t block_table_stride,
-              const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
-              int32_t max_pages_per_seq, float scale, int32_t window, void* out,
-              float* lse_out, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// pa_decode with S query tokens per sequence (S = 1: plain decode).
+int decode_impl(const void* q, const void* k_pool, const void* v_pool, const pa_kv_layout* kv,
+                const int32_t* block_table, int32_t block_table_stride,
+                const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                int32_t num_queries, int32_t causal, int32_t max_pages_per_seq, float scale,
+                int32_t window, void* out, float* lse_out, void* workspace,
+                size_t workspace_bytes, void* stream) {
   int rc = pa::check_gqa(q, k_pool, v_pool, kv, block_table, block_table_stride, context_lens,
                          batch, num_q_heads, max_pages_per_seq, scale);
   if (rc) return rc;
   if (!out) return pa::fail(PA_ERR_NULL, "out must not be NULL");
   if (reinterpret_cast<uintptr_t>(out) & 15u)
     return pa::fail(PA_ERR_ALIGN, "out must be 16-byte aligned");
+  const int qpad = pa::queries_padded(num_queries);
+  const int group = num_q_heads / kv->num_kv_heads;
+  if (qpad < 1 || !pa::group_supported(kv->head_dim, qpad * group))
+    return pa::fail(PA_ERR_UNSUPPORTED, "num_queries (rounded up to a power of two) times the "
+                                        "q heads per KV head must be a supported group size");
   pa::DecodePlan plan;
-  if (!pa::plan_decode(batch, num_q_heads, kv->num_kv_heads, kv->head_dim, max_pages_per_seq,
-                       kv->page_size, window, &plan))
+  if (!pa::plan_decode(batch, num_q_heads * qpad, kv->num_kv_heads, kv->head_dim,
+                       max_pages_per_seq, kv->page_size, window, &plan))
     return pa::fail(PA_ERR_SHAPE, "no launch plan for these shapes");
   if (!workspace || workspace_bytes < plan.bytes)
-    return pa::fail(PA_ERR_WORKSPACE, "workspace must hold pa_decode_workspace_size() = " +
-                                          std::to_string(plan.bytes) + " bytes");
+    return pa::fail(PA_ERR_WORKSPACE, "workspace must hold " + std::to_string(plan.bytes) + " bytes");
   if (reinterpret_cast<uintptr_t>(workspace) & 255u)
     return pa::fail(PA_ERR_ALIGN, "workspace must be 256-byte aligned");
   char* ws = static_cast<char*>(workspace);
-  const int group = num_q_heads / kv->num_kv_heads;
-  const int nbmax = pa::balanced_grid(kv->head_dim, group, device_cus(), pa::kMaxBalancedBlocks);
+  const int vgroup = qpad * group;
+  const int nbmax = pa::balanced_grid(kv->head_dim, vgroup, device_cus(), pa::kMaxBalancedBlocks);
   if (nbmax < 1) return pa::fail(PA_ERR_UNSUPPORTED, "no balanced-split kernel for these shapes");
 
   pa::BalancedLayout bl{};
@@ -183,14 +199,61 @@ int pa_decode(const void* q, const void* k_pool, const void* v_pool, const pa_kv
   bl.min_units = pa::kMinUnitsPerBlock;
   bl.rows = plan.rows;
   bl.batch = batch;
+  bl.q_heads = num_q_heads;
+  bl.group_shift = ilog2(group);
+  bl.num_queries = num_queries;
 
-  const pa::SplitParams sp = split_params(q, k_pool, v_pool, kv, block_table, block_table_stride,
-                                          context_lens, num_q_heads, scale, window, 1, 1, nullptr,
-                                          nullptr, nullptr, 0);
+  pa::SplitParams sp = split_params(q, k_pool, v_pool, kv, block_table, block_table_stride,
+                                    context_lens, num_q_heads, scale, window, 1, 1, nullptr,
+                                    nullptr, nullptr, 0);
+  sp.num_q_heads = num_q_heads * num_queries;   // rows of q and out per sequence
+  sp.num_queries = num_queries;
+  sp.causal = causal ? 1 : 0;
+  sp.reach = (window > 0 && causal) ? window + num_queries - 1 : window;
   pa::clear_error();
-  return launch_status(pa::launch_balanced(sp, bl, kv->head_dim, group, nbmax,
+  return launch_status(pa::launch_balanced(sp, bl, kv->head_dim, vgroup, nbmax,
                                            static_cast<hipStream_t>(stream)),
                        "balanced decode");
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_decode(const void* q, const void* k_pool, const void* v_pool, const pa_kv_layout* kv,
+              const int32_t* block_table, int32_t block_table_stride,
+              const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+              int32_t max_pages_per_seq, float scale, int32_t window, void* out,
+              float* lse_out, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(q, k_pool, v_pool, kv, block_table, block_table_stride, context_lens, batch,
+                     num_q_heads, 1, 1, max_pages_per_seq, scale, window, out, lse_out,
+                     workspace, workspace_bytes, stream);
+}
+
+int pa_decode_multiquery(const void* q, const void* k_pool, const void* v_pool,
+                         const pa_kv_layout* kv, const int32_t* block_table,
+                         int32_t block_table_stride, const int32_t* context_lens, int32_t batch,
+                         int32_t num_q_heads, int32_t num_queries, int32_t causal,
+                         int32_t max_pages_per_seq, float scale, int32_t window, void* out,
+                         float* lse_out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_queries < 1 || num_queries > 16)
+    return pa::fail(PA_ERR_SHAPE, "num_queries must be in 1..16");
+  return decode_impl(q, k_pool, v_pool, kv, block_table, block_table_stride, context_lens, batch,
+                     num_q_heads, num_queries, causal, max_pages_per_seq, scale, window, out,
+                     lse_out, workspace, workspace_bytes, stream);
+}
+
+size_t pa_decode_multiquery_workspace_size(int32_t batch, int32_t num_q_heads,
+                                           int32_t num_kv_heads, int32_t head_dim,
+                                           int32_t max_pages_per_seq, int32_t page_size,
+                                           int32_t window, int32_t num_queries) {
+  const int qpad = pa::queries_padded(num_queries);
+  if (qpad < 1 || num_queries > 16) return 0;
+  pa::DecodePlan plan;
+  if (!pa::plan_decode(batch, num_q_heads * qpad, num_kv_heads, head_dim, max_pages_per_seq,
+                       page_size, window, &plan))
+    return 0;
+  return plan.bytes;
 }
 
 const char* pa_last_error(void) { return pa::last_error(); }

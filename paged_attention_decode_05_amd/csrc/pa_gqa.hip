@@ -289,14 +289,41 @@ __device__ __forceinline__ void attend_range(const SplitParams& p, int b, int gk
   const int koff = (lane / g::LQ) * p.token_bytes + 16 * (lane % g::LQ);
   const int voff0 = (lane / g::LV) * p.token_bytes + 16 * (lane % g::LV);
 
+  // Virtual head h of the group is query h >> group_shift, q head
+  // h & (gq - 1); its q and out rows sit hoff(h) rows after row0.  With one
+  // query, hoff(h) = h.  Queries past the last real one (the query count
+  // rounded up to a power of two) repeat it and write no output.
+  const int gq = 1 << p.group_shift;
+  const int64_t row0 = static_cast<int64_t>(b) * p.num_q_heads + static_cast<int64_t>(gk) * gq;
+  auto hoff = [&](int h) -> int64_t {
+    return static_cast<int64_t>(min(h >> p.group_shift, p.num_queries - 1) * p.q_heads +
+                                (h & (gq - 1)));
+  };
+
   // q pieces, pre-permuted per lane: slot h holds head h ^ pi.
   uint4 qv[G][g::NQL];
   {
-    const uint16_t* qb = p.q + (static_cast<int64_t>(b) * p.num_q_heads + gk * G) * D + 8 * jq;
+    const uint16_t* qb = p.q + row0 * D + 8 * jq;
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int s = 0; s < g::NQL; ++s) qv[h][s] = load16(qb + (h ^ pi) * D + s * 8 * g::LQ);
+      for (int s = 0; s < g::NQL; ++s) qv[h][s] = load16(qb + hoff(h ^ pi) * D + s * 8 * g::LQ);
+  }
+
+  // Keys each owned head may see, within [begin, end): query s of a
+  // multi-query row sees up to n - S + s when causal, and a window counts
+  // back from its last key.  With one query this is [begin, end) itself.
+  int lo_h[g::VH], hi_h[g::VH];
+  {
+    const int n = p.context_lens[b];
+#pragma unroll
+    for (int vh = 0; vh < g::VH; ++vh) {
+      const int sq = min((vh ^ pi) >> p.group_shift, p.num_queries - 1);
+      const int hi = p.causal ? min(n, n - p.num_queries + 1 + sq) : n;
+      const int lo = p.window > 0 ? max(0, hi - p.window) : 0;
+      lo_h[vh] = max(lo, begin);
+      hi_h[vh] = min(hi, end);
+    }
   }
 
   float m_own[g::VH], l_own[g::VH];
@@ -339,9 +366,9 @@ __device__ __forceinline__ void attend_range(const SplitParams& p, int b, int gk
       }
       scatter_step<D, G, 0>(v);
       const int t = tchunk + u * g::TQ + rq;
-      const bool live = t >= wk.begin && t < wk.end;
 #pragma unroll
-      for (int vh = 0; vh < g::VH; ++vh) s_own[u][vh] = live ? v[vh] * p.scale_log2 : -INFINITY;
+      for (int vh = 0; vh < g::VH; ++vh)
+        s_own[u][vh] = (t >= lo_h[vh] && t < hi_h[vh]) ? v[vh] * p.scale_log2 : -INFINITY;
     }
 
     // online softmax for the heads this lane owns; the running max of a head
@@ -423,7 +450,9 @@ __device__ __forceinline__ void attend_range(const SplitParams& p, int b, int gk
   }
   __syncthreads();
 
-  // Merge the waves and write the normalised partial, fp32.
+  // Merge the waves and write the normalised partial, fp32.  A head that saw
+  // no key (possible only for the early queries of a multi-query row) gets
+  // o = 0, max -inf, sum 0.
   for (int i = threadIdx.x; i < G * D; i += NT) {
     const int h = i / D;
     const int d = i % D;
@@ -437,13 +466,15 @@ __device__ __forceinline__ void attend_range(const SplitParams& p, int b, int gk
       W += red_l[w][h] * sc;
       o += red_acc[w][h][d] * sc;
     }
+    const bool any = W > 0.0f;
     if (final_out) {
-      final_out[h * D + d] = f32_to_bf16_rne(o / W);
-      if (d == 0 && final_lse) final_lse[h] = M * kLn2 + __logf(W);
+      if ((h >> p.group_shift) >= p.num_queries) continue;   // padding query
+      final_out[hoff(h) * D + d] = f32_to_bf16_rne(any ? o / W : 0.0f);
+      if (d == 0 && final_lse) final_lse[hoff(h)] = any ? M * kLn2 + __logf(W) : -INFINITY;
     } else {
-      out[h * hstride * D + d] = o / W;
+      out[h * hstride * D + d] = any ? o / W : 0.0f;
       if (d == 0) {
-        mx[h * hstride] = M * kLn2;
+        mx[h * hstride] = any ? M * kLn2 : -INFINITY;
         sm[h * hstride] = W;
       }
     }
@@ -542,15 +573,15 @@ __global__ __launch_bounds__(kBlock) void balanced_split_kernel(const SplitParam
   __shared__ int64_t sh_pre;
   __shared__ int sh_b;
   const int i = blockIdx.x;
-  const int hkv = p.num_q_heads / G;
+  const int hkv = p.kv_heads;
   if (threadIdx.x < 64) {
-    const int64_t keys = total_keys(p.context_lens, bl.batch, p.window);
+    const int64_t keys = total_keys(p.context_lens, bl.batch, p.reach);
     const int64_t T = keys * hkv;
     int b = 0;
     int64_t pre = 0;
     if (T > 0) {
       const int nb = used_blocks(T, gridDim.x, bl.min_units);
-      if (i < nb) locate_unit(p.context_lens, bl.batch, p.window, hkv, static_cast<int64_t>(i) * T / nb, b, pre);
+      if (i < nb) locate_unit(p.context_lens, bl.batch, p.reach, hkv, static_cast<int64_t>(i) * T / nb, b, pre);
     }
     if (threadIdx.x == 0) {
       sh_total = T;
@@ -567,9 +598,10 @@ __global__ __launch_bounds__(kBlock) void balanced_split_kernel(const SplitParam
   const int64_t s1 = static_cast<int64_t>(i + 1) * T / nb;
   int b = sh_b;
   int64_t pre = sh_pre;                                  // keys per KV head before sequence b
+  const int gq = 1 << p.group_shift;
   while (b < bl.batch) {
     const int n = p.context_lens[b];
-    const int lo = p.window > 0 ? max(0, n - p.window) : 0;
+    const int lo = p.reach > 0 ? max(0, n - p.reach) : 0;
     const int64_t len = n - lo;
     const int64_t seq0 = pre * hkv;                      // first unit of sequence b
     if (seq0 >= s1) break;
@@ -584,7 +616,7 @@ __global__ __launch_bounds__(kBlock) void balanced_split_kernel(const SplitParam
       // a row that lies inside this block's share gets its final output here
       const bool whole = off >= s0 && off + len <= s1;
       const int64_t slot = static_cast<int64_t>(b * hkv + gk) + i;
-      const int64_t h0 = static_cast<int64_t>(b) * p.num_q_heads + static_cast<int64_t>(gk) * G;
+      const int64_t h0 = static_cast<int64_t>(b) * p.num_q_heads + static_cast<int64_t>(gk) * gq;
       attend_range<D, G, kWaves>(p, b, gk, begin, end, bl.seg_out + slot * G * D,
                                  bl.seg_max + slot * G, bl.seg_sum + slot * G, 1,
                                  whole ? bl.out + h0 * D : nullptr,
@@ -603,9 +635,14 @@ template <int D, int G>
 __device__ __forceinline__ void merge_segments(const BalancedLayout& bl, int64_t slot0, int count,
                                                uint16_t* out, float* lse) {
   constexpr int kBatch = 16;
+  const int gq = 1 << bl.group_shift;
   for (int i = blockIdx.y * kBlock + threadIdx.x; i < G * D; i += kBlock * gridDim.y) {
     const int h = i / D;
     const int d = i % D;
+    // output row of virtual head h (query h >> shift, q head h & (gq - 1));
+    // padding queries past the last real one write nothing
+    if ((h >> bl.group_shift) >= bl.num_queries) continue;
+    const int64_t ho = static_cast<int64_t>((h >> bl.group_shift) * bl.q_heads + (h & (gq - 1)));
     const float* pm = bl.seg_max + slot0 * G + h;
     const float* pl = bl.seg_sum + slot0 * G + h;
     const float* po = bl.seg_out + (slot0 * G + h) * D + d;
@@ -616,6 +653,11 @@ __device__ __forceinline__ void merge_segments(const BalancedLayout& bl, int64_t
       for (int k = 0; k < kBatch; ++k) mk[k] = (k0 + k < count) ? pm[(k0 + k) * G] : -INFINITY;
 #pragma unroll
       for (int k = 0; k < kBatch; ++k) M = fmaxf(M, mk[k]);
+    }
+    if (M == -INFINITY) {          // no piece saw a key for this head
+      out[ho * D + d] = 0;
+      if (d == 0 && lse) lse[ho] = -INFINITY;
+      continue;
     }
     float W = 0.0f, o = 0.0f;
     for (int k0 = 0; k0 < count; k0 += kBatch) {
@@ -631,21 +673,22 @@ __device__ __forceinline__ void merge_segments(const BalancedLayout& bl, int64_t
 #pragma unroll
       for (int k = 0; k < kBatch; ++k) o = fmaf(wk[k], ok[k], o);
     }
-    out[h * D + d] = f32_to_bf16_rne(o / W);
-    if (d == 0 && lse) lse[h] = M + __logf(W);
+    out[ho * D + d] = f32_to_bf16_rne(o / W);
+    if (d == 0 && lse) lse[ho] = M + __logf(W);
   }
 }
 
-// Block (r, y) handles outputs y*256 .. +256 of the G*D of row r = (b, g):
-// rows with no key get zeros and lse -inf, rows that one block covered are
-// already written, the rest are merged here.
+// Block (r, y) handles outputs y*256 .. +256 of the G*D (virtual) heads' dims
+// of row r = (b, g): rows with no key get zeros and lse -inf, rows that one
+// block covered are already written, the rest are merged here.  `window` is
+// the reach of the row's key range.
 template <int D, int G>
 __global__ __launch_bounds__(kBlock) void balanced_merge_kernel(const BalancedLayout bl,
                                                                int num_q_heads, int window,
                                                                int split_grid) {
   __shared__ int64_t sh_total, sh_pre;
   const int r = blockIdx.x;
-  const int hkv = num_q_heads / G;
+  const int hkv = bl.rows / bl.batch;
   const int b = r / hkv;
   const int gk = r - b * hkv;
   if (threadIdx.x < 64) {
@@ -663,11 +706,16 @@ __global__ __launch_bounds__(kBlock) void balanced_merge_kernel(const BalancedLa
   __syncthreads();
   const int64_t T = sh_total;
   const int64_t len = seq_len(bl.context_lens, b, window);
-  const int64_t h0 = static_cast<int64_t>(b) * num_q_heads + static_cast<int64_t>(gk) * G;
+  const int gq = 1 << bl.group_shift;
+  const int64_t h0 = static_cast<int64_t>(b) * num_q_heads + static_cast<int64_t>(gk) * gq;
   if (len == 0) {
-    for (int i = blockIdx.y * kBlock + threadIdx.x; i < G * D; i += kBlock * gridDim.y)
-      bl.out[h0 * D + i] = 0;
-    if (bl.lse && blockIdx.y == 0 && threadIdx.x < G) bl.lse[h0 + threadIdx.x] = -INFINITY;
+    for (int i = blockIdx.y * kBlock + threadIdx.x; i < G * D; i += kBlock * gridDim.y) {
+      const int h = i / D;
+      if ((h >> bl.group_shift) >= bl.num_queries) continue;
+      const int64_t ho = static_cast<int64_t>((h >> bl.group_shift) * bl.q_heads + (h & (gq - 1)));
+      bl.out[(h0 + ho) * D + i % D] = 0;
+      if (bl.lse && i % D == 0) bl.lse[h0 + ho] = -INFINITY;
+    }
     return;
   }
   const int nb = used_blocks(T, split_grid, bl.min_units);
@@ -789,7 +837,7 @@ static hipError_t launch_balanced_dg(const SplitParams& p, const BalancedLayout&
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((balanced_merge_kernel<D, G>), dim3(bl.rows, (G * D + kBlock - 1) / kBlock),
-                     dim3(kBlock), 0, stream, bl, p.num_q_heads, p.window, grid);
+                     dim3(kBlock), 0, stream, bl, p.num_q_heads, p.reach, grid);
   return hipGetLastError();
 }
 

@@ -22,10 +22,23 @@ struct SplitParams {
   int32_t token_bytes;  // token_stride * 2
   uint32_t page_bytes;  // page_stride * 2
   int32_t bt_stride;
-  int32_t num_q_heads;
+  int32_t num_q_heads;  // rows of q and out per sequence: Hq * num_queries
+  int32_t kv_heads;     // Hkv
   int32_t page_size;
   int32_t page_shift;   // log2(page_size)
   int32_t window;
+  // Multi-query decode (S query tokens per sequence, q [b][s][Hq][D]): the
+  // kernel's group G holds S' * Gq virtual heads (S' = S rounded up to a
+  // power of two), virtual head h being query h >> group_shift, q head
+  // (h & (Gq - 1)) of the KV group; queries S .. S'-1 repeat query S - 1 and
+  // write nothing.  Query s sees keys up to n - S + s when causal; `reach` is
+  // the window of the union of the queries' key ranges (window + S - 1 when
+  // causal, else window).
+  int32_t num_queries;
+  int32_t q_heads;      // Hq
+  int32_t group_shift;  // log2(Gq)
+  int32_t causal;
+  int32_t reach;
   int32_t partition_size;
   int32_t max_parts;
   int32_t write_empty;
@@ -56,6 +69,9 @@ struct BalancedLayout {
   int64_t min_units;     // a block owns at least this many units (keys of one KV head)
   int32_t rows;          // batch * num_kv_heads
   int32_t batch;
+  int32_t q_heads;       // Hq (out rows are [b][s][Hq])
+  int32_t group_shift;   // log2(Gq); virtual head h -> query h >> shift, head h & (Gq - 1)
+  int32_t num_queries;   // S; virtual queries >= S write nothing
 };
 
 }  // namespace pa

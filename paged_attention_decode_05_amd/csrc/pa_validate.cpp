@@ -34,6 +34,13 @@ bool group_supported(int32_t head_dim, int32_t group) {
 
 bool page_size_supported(int32_t ps) { return ps == 16 || ps == 32 || ps == 64; }
 
+int32_t queries_padded(int32_t num_queries) {
+  if (num_queries < 1) return 0;
+  int32_t p = 1;
+  while (p < num_queries) p *= 2;
+  return p;
+}
+
 int64_t max_keys(int32_t max_pages_per_seq, int32_t page_size, int32_t window) {
   int64_t k = static_cast<int64_t>(max_pages_per_seq) * page_size;
   if (window > 0 && window < k) k = window;

@@ -21,6 +21,9 @@ bool head_dim_supported(int32_t d);
 bool group_supported(int32_t head_dim, int32_t group);
 bool page_size_supported(int32_t ps);
 
+// Query count of multi-query decode rounded up to a power of two (0 if < 1).
+int32_t queries_padded(int32_t num_queries);
+
 // Largest number of keys one sequence can attend to.
 int64_t max_keys(int32_t max_pages_per_seq, int32_t page_size, int32_t window);
 

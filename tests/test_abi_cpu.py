@@ -187,3 +187,18 @@ def test_mla_cache_insert_rejections():
     assert _mins(ps=56) == PA["SHAPE"]
     assert _mins(pe=FAKE + 4) == PA["ALIGN"]
     assert _mins(n=0) == PA["OK"]
+
+
+def test_multiquery_rejections_and_sizes():
+    kv = _kv()
+    f = pb.LIB.pa_decode_multiquery
+    args = lambda S, heads=8: (FAKE, FAKE, FAKE, C.byref(kv), FAKE, 32, FAKE, 8, heads, S, 1, 32,
+                               0.088, 0, FAKE, None, None, 0, None)
+    assert f(*args(0)) == PA["SHAPE"]
+    assert f(*args(17)) == PA["SHAPE"]
+    assert f(*args(5)) == PA["UNSUPPORTED"]      # 8 padded queries x 4 heads per KV head = 32
+    assert f(*args(4)) == PA["WORKSPACE"]        # 4 x 4 = 16: supported, no workspace given
+    ws = pb.pa_decode_multiquery_workspace_size
+    assert ws(8, 8, 2, 128, 32, 32, 0, 3) == ws(8, 8, 2, 128, 32, 32, 0, 4) > 0
+    assert ws(8, 8, 2, 128, 32, 32, 0, 1) == pb.pa_decode_workspace_size(8, 8, 2, 128, 32, 32, 0)
+    assert ws(8, 8, 2, 128, 32, 32, 0, 0) == 0
