@@ -50,7 +50,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="llama", choices=["tiny", "llama", "d256w", "long", "mla"])
+    ap.add_argument("--workload", default="llama",
+                    choices=["tiny", "llama", "d256w", "long", "mla", "verify", "insert"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run K device-to-device copies of a 1 GiB buffer instead (reference "
@@ -89,6 +90,10 @@ def main() -> int:
         return 0
     if a.workload == "mla":
         return bench_mla(a, torch, pb, wl, dev)
+    if a.workload == "verify":
+        return bench_verify(a, torch, pb, wl, dev)
+    if a.workload == "insert":
+        return bench_insert(a, torch, pb, wl, dev)
     log(f"generating workload {a.workload} (seeded) ...")
     t0 = time.time()
     cases = [wl.NAMED[a.workload](poison=False, seed=wl.SEED_BASE + 100 * i + {
@@ -232,6 +237,97 @@ def _time_calls(torch, stream, step, steps):
     torch.cuda.synchronize()
     ms = [e[0].elapsed_time(e[1]) for e in ev]
     return statistics.fmean(ms), ms
+
+
+def _timed(a, torch, step):
+    stream = torch.cuda.current_stream()
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(a.steps):
+        step(i)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(stop) / a.steps
+    call_mean, call_ms = _time_calls(torch, stream, step, a.steps)
+    return ms_per_step, call_mean, call_ms
+
+
+def _line(a, metric, nbytes, ms_per_step, call_mean, call_ms, config, kernel, extra=None):
+    gbs = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (call_mean * 1e-3) / 1e9
+    res = {"metric": metric, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
+           "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_per_step, 5),
+           "us_per_call": round(ms_per_step * 1e3, 2),
+           "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "f32", "storage_dtype": "bf16",
+           "data": "synthetic", "config": config,
+           "call_us": {"mean": round(call_mean * 1e3, 2),
+                       "p10": round(sorted(call_ms)[len(call_ms) // 10] * 1e3, 2),
+                       "p90": round(sorted(call_ms)[(9 * len(call_ms)) // 10] * 1e3, 2)},
+           "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                        "kernel": kernel, "algorithmic_bytes_per_launch": int(nbytes)},
+           "cpu_baseline": None}
+    if extra:
+        res.update(extra)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def bench_verify(a, torch, pb, wl, dev) -> int:
+    """Speculative-decoding verify step: the llama-shaped bs64 batch with 4
+    causal queries per sequence through pa_decode_multiquery."""
+    S = 4
+    log("generating workload verify (seeded) ...")
+    case = wl.make_gqa_case(context_lens=(), ctx_draw=(512, 8192), batch=64, num_q_heads=32,
+                            num_kv_heads=8, head_dim=128, page_size=32, seed=wl.SEED_BASE + 6,
+                            num_queries=S, poison=False, name="verify")
+    dc = case.to(dev)
+    B, _, H, D = dc.q.shape
+    out = torch.empty_like(dc.q)
+    ws = torch.zeros(pb.pa_decode_multiquery_workspace_size(B, H, 8, D, dc.max_pages, 32, 0, S),
+                     dtype=torch.uint8, device=dev)
+    kv = pb.kv_layout(dc.k_pool, dc.layout)
+
+    def step(i):
+        pb.pa_decode_multiquery(dc.q, dc.k_pool, dc.v_pool, kv, dc.block_table, dc.context_lens,
+                                dc.scale, 0, True, out, None, ws)
+
+    ms, mean, calls = _timed(a, torch, step)
+    return _line(a, "verify-step decode-attn GB/s (4 causal queries per sequence), d128 GQA bs64",
+                 case.kv_bytes(), ms, mean, calls,
+                 {"workload": "llama3-8b-shaped verify step, bs64, 4 causal queries per sequence, "
+                              "32q/8kv heads, d128, page 32, ctx U[512,8192]",
+                  "sum_context": int(case.context_lens.sum()), "num_queries": S},
+                 "pa_decode_multiquery call: balanced_split_kernel<128,16> + merge")
+
+
+def bench_insert(a, torch, pb, wl, dev) -> int:
+    """KV insert of an 8192-token chunk (32q/8kv heads, d128) into the
+    llama-shaped pools at random free slots."""
+    T = 8192
+    log("generating workload insert (seeded) ...")
+    case = wl.llama(poison=False)
+    dc = case.to(dev)
+    g = torch.Generator().manual_seed(wl.SEED_BASE + 7)
+    total = case.num_pages * case.page_size
+    slots = torch.randperm(total, generator=g)[:T].to(torch.int64).to(dev)
+    k_new = torch.randn(T, 8, 128, generator=g).to(torch.bfloat16).to(dev)
+    v_new = torch.randn(T, 8, 128, generator=g).to(torch.bfloat16).to(dev)
+    kv = pb.kv_layout(dc.k_pool, dc.layout)
+
+    def step(i):
+        pb.pa_kv_insert(k_new, v_new, dc.k_pool, dc.v_pool, kv, slots)
+
+    ms, mean, calls = _timed(a, torch, step)
+    nbytes = 2 * (2 * T * 8 * 128 * 2)          # K and V rows read once and written once
+    return _line(a, "KV insert GB/s (rows read + written), 8192 tokens x 8 KV heads x d128",
+                 nbytes, ms, mean, calls,
+                 {"workload": "KV insert of an 8192-token chunk into the llama-shaped pools",
+                  "tokens": T}, "pa_kv_insert call: kv_insert_kernel")
 
 
 def bench_mla(a, torch, pb, wl, dev) -> int:
