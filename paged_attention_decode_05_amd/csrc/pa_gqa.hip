@@ -23,6 +23,7 @@
 #include <hip/hip_runtime.h>
 
 #include "pa_device.h"
+#include "pa_mfma.h"
 #include "pa_params.h"
 
 namespace pa {
@@ -236,23 +237,84 @@ __device__ __forceinline__ void load_v(VRegs<D, G>& vr, const WaveKeys& wk, int 
   }
 }
 
-// Attention of the G q heads of KV head gk of sequence b over keys
-// [begin, end) (begin < end), by the NW waves of the block: wave w takes
-// chunks w, w + NW, ..., keeps its own running state, and the waves are
-// merged at the end.
-// Writes the fp32 partial of head h (0 <= h < G) to out + h*hstride*D,
-// mx[h*hstride] (natural-log max) and sm[h*hstride] (sum) -- or, when
-// `final_out` is set (the range is the row's only one), the bf16 attention
-// output of head h to final_out + h*D and its log-sum-exp to final_lse[h].
+// Virtual head h of a KV group is query h >> group_shift, q head
+// h & (gq - 1); its q and out rows sit head_offset(h) rows after the group's
+// first row.  With one query, head_offset(h) = h.  Queries past the last real
+// one (the query count rounded up to a power of two) repeat it and write no
+// output.
+__device__ __forceinline__ int64_t head_offset(const SplitParams& p, int h) {
+  const int gq = 1 << p.group_shift;
+  return static_cast<int64_t>(min(h >> p.group_shift, p.num_queries - 1) * p.q_heads + (h & (gq - 1)));
+}
+
+// Keys [lo, hi) that head h of sequence b may see, within [begin, end): query
+// s of a multi-query row sees up to n - S + s when causal, and a window
+// counts back from its last key.  With one query this is [begin, end) itself.
+__device__ __forceinline__ void head_bounds(const SplitParams& p, int n, int h, int begin, int end,
+                                            int& lo_h, int& hi_h) {
+  const int sq = min(h >> p.group_shift, p.num_queries - 1);
+  const int hi = p.causal ? min(n, n - p.num_queries + 1 + sq) : n;
+  const int lo = p.window > 0 ? max(0, hi - p.window) : 0;
+  lo_h = max(lo, begin);
+  hi_h = min(hi, end);
+}
+
+// Merge of the NW waves' states of one range and the write of its result.
+// Wave w left, per head h < G, its running max red_m[w][h] (log2 domain, -inf
+// if it saw no key), its sum red_l[w][h] relative to that max and its
+// unnormalised accumulator red_acc[(w*G + h)*D + d].  Writes the fp32 partial
+// of head h to out + h*hstride*D, mx[h*hstride] (natural-log max) and
+// sm[h*hstride] (sum) -- or, when `final_out` is set (the range is the row's
+// only one), the bf16 output of head h to final_out + head_offset(h)*D and
+// its log-sum-exp to final_lse[head_offset(h)].  A head that saw no key
+// (possible only for the early queries of a multi-query row) gets o = 0, max
+// -inf, sum 0.
 template <int D, int G, int NW>
-__device__ __forceinline__ void attend_range(const SplitParams& p, int b, int gk, int begin,
-                                             int end, float* out, float* mx, float* sm,
-                                             int64_t hstride, uint16_t* final_out = nullptr,
-                                             float* final_lse = nullptr) {
+__device__ __forceinline__ void write_range(const SplitParams& p, const float* red_acc,
+                                            const float (*red_m)[G], const float (*red_l)[G],
+                                            float* out, float* mx, float* sm, int64_t hstride,
+                                            uint16_t* final_out, float* final_lse) {
+  for (int i = threadIdx.x; i < G * D; i += 64 * NW) {
+    const int h = i / D;
+    const int d = i % D;
+    float M = red_m[0][h];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, red_m[w][h]);
+    float W = 0.0f, o = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float sc = (red_m[w][h] == -INFINITY) ? 0.0f : fast_exp2(red_m[w][h] - M);
+      W += red_l[w][h] * sc;
+      o += red_acc[(w * G + h) * D + d] * sc;
+    }
+    const bool any = W > 0.0f;
+    if (final_out) {
+      if ((h >> p.group_shift) >= p.num_queries) continue;   // padding query
+      const int64_t ho = head_offset(p, h);
+      final_out[ho * D + d] = f32_to_bf16_rne(any ? o / W : 0.0f);
+      if (d == 0 && final_lse) final_lse[ho] = any ? M * kLn2 + __logf(W) : -INFINITY;
+    } else {
+      out[h * hstride * D + d] = any ? o / W : 0.0f;
+      if (d == 0) {
+        mx[h * hstride] = any ? M * kLn2 : -INFINITY;
+        sm[h * hstride] = W;
+      }
+    }
+  }
+}
+
+// Attention of the G q heads of KV head gk of sequence b over keys
+// [begin, end) (begin < end), by the NW waves of the block, on the vector
+// ALUs: wave w takes chunks w, w + NW, ..., keeps its own running state, and
+// the waves are merged at the end (write_range).
+template <int D, int G, int NW>
+__device__ __forceinline__ void attend_range_valu(const SplitParams& p, int b, int gk, int begin,
+                                                  int end, float* out, float* mx, float* sm,
+                                                  int64_t hstride, uint16_t* final_out,
+                                                  float* final_lse) {
   using g = Geo<D, G>;
   constexpr int CH = g::CH;
 
-  constexpr int NT = 64 * NW;
   __shared__ float red_acc[NW][G][D];
   __shared__ float red_m[NW][G];
   __shared__ float red_l[NW][G];
@@ -289,16 +351,8 @@ __device__ __forceinline__ void attend_range(const SplitParams& p, int b, int gk
   const int koff = (lane / g::LQ) * p.token_bytes + 16 * (lane % g::LQ);
   const int voff0 = (lane / g::LV) * p.token_bytes + 16 * (lane % g::LV);
 
-  // Virtual head h of the group is query h >> group_shift, q head
-  // h & (gq - 1); its q and out rows sit hoff(h) rows after row0.  With one
-  // query, hoff(h) = h.  Queries past the last real one (the query count
-  // rounded up to a power of two) repeat it and write no output.
   const int gq = 1 << p.group_shift;
   const int64_t row0 = static_cast<int64_t>(b) * p.num_q_heads + static_cast<int64_t>(gk) * gq;
-  auto hoff = [&](int h) -> int64_t {
-    return static_cast<int64_t>(min(h >> p.group_shift, p.num_queries - 1) * p.q_heads +
-                                (h & (gq - 1)));
-  };
 
   // q pieces, pre-permuted per lane: slot h holds head h ^ pi.
   uint4 qv[G][g::NQL];
@@ -307,23 +361,15 @@ __device__ __forceinline__ void attend_range(const SplitParams& p, int b, int gk
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int s = 0; s < g::NQL; ++s) qv[h][s] = load16(qb + hoff(h ^ pi) * D + s * 8 * g::LQ);
+      for (int s = 0; s < g::NQL; ++s) qv[h][s] = load16(qb + head_offset(p, h ^ pi) * D + s * 8 * g::LQ);
   }
 
-  // Keys each owned head may see, within [begin, end): query s of a
-  // multi-query row sees up to n - S + s when causal, and a window counts
-  // back from its last key.  With one query this is [begin, end) itself.
+  // keys each owned head may see
   int lo_h[g::VH], hi_h[g::VH];
   {
     const int n = p.context_lens[b];
 #pragma unroll
-    for (int vh = 0; vh < g::VH; ++vh) {
-      const int sq = min((vh ^ pi) >> p.group_shift, p.num_queries - 1);
-      const int hi = p.causal ? min(n, n - p.num_queries + 1 + sq) : n;
-      const int lo = p.window > 0 ? max(0, hi - p.window) : 0;
-      lo_h[vh] = max(lo, begin);
-      hi_h[vh] = min(hi, end);
-    }
+    for (int vh = 0; vh < g::VH; ++vh) head_bounds(p, n, vh ^ pi, begin, end, lo_h[vh], hi_h[vh]);
   }
 
   float m_own[g::VH], l_own[g::VH];
@@ -450,36 +496,231 @@ __device__ __forceinline__ void attend_range(const SplitParams& p, int b, int gk
   }
   __syncthreads();
 
-  // Merge the waves and write the normalised partial, fp32.  A head that saw
-  // no key (possible only for the early queries of a multi-query row) gets
-  // o = 0, max -inf, sum 0.
-  for (int i = threadIdx.x; i < G * D; i += NT) {
-    const int h = i / D;
-    const int d = i % D;
-    float M = red_m[0][h];
+  write_range<D, G, NW>(p, &red_acc[0][0][0], red_m, red_l, out, mx, sm, hstride, final_out,
+                        final_lse);
+  __syncthreads();   // the shared buffers are reused by the block's next range
+}
+
+// ---- matrix-core range routine (wide groups) ------------------------------------
+//
+// For groups of 8 or more (virtual) heads the vector-ALU layout needs G*8
+// accumulators and G q pieces per lane; on MFMA the 16 heads of a tile share
+// one operand column each and a lane holds D/4 accumulators.  Per wave and
+// chunk of 16 keys (always inside one page):
+//   scores  S^T[16 keys x 16 heads] = K[16 x D] . Q^T[D x 16]    (16x16x32, D/32 steps)
+//           A = K rows loaded straight from the page (lane: key c, dims
+//           32ks + 8g .. +8), B = q (lane: head c, same dims), exact bf16
+//           products, fp32 sums; D lane holds keys 4g .. 4g+3 of head c.
+//   softmax per head c over the chunk (max across the 4 lane groups), with a
+//           reference max that moves only when a score passes it by more than
+//           8 (log2 domain): P <= 2^8 and the accumulators are rescaled rarely.
+//   P.V     O[16 heads x D] += P[16 x 16 keys] . V[16 keys x D] (16x16x16)
+//           A = P exactly as the score D layout left it (head c, keys 4g+i),
+//           split into three bf16 terms hi + mid + lo, which represent the fp32
+//           value exactly; B = V columns from the wave's LDS tile (row-major,
+//           rows padded to D + 16 elements) by transposed reads.
+// Heads c >= G (G = 8) get q = 0 and are masked out.  The loads of chunk k+1
+// are issued as soon as chunk k's registers are free: K after the scores, V
+// after its LDS write.
+template <int D, int G>
+struct MfmaGeo {
+  static constexpr int KC = 16;          // keys per chunk
+  static constexpr int KS = D / 32;      // score k-steps
+  static constexpr int NT = D / 16;      // P.V output tiles
+  static constexpr int LV = D / 8;       // lanes per V row in the load layout
+  static constexpr int TV = 64 / LV;     // V rows per load
+  static constexpr int NV = KC / TV;     // V loads per chunk
+  static constexpr int VPAD = D + 16;    // LDS row stride of the V tile (elements)
+  static_assert(G == 8 || G == 16, "MFMA path takes 8 or 16 heads");
+};
+
+template <int D, int G, int NW>
+__device__ __forceinline__ void attend_range_mfma(const SplitParams& p, int b, int gk, int begin,
+                                                  int end, float* out, float* mx, float* sm,
+                                                  int64_t hstride, uint16_t* final_out,
+                                                  float* final_lse) {
+  using mg = MfmaGeo<D, G>;
+  constexpr int KC = mg::KC;
+  constexpr int kTileBytes = NW * KC * mg::VPAD * 2;
+  constexpr int kRedBytes = NW * G * D * 4;
+  // the V tiles of the loop and the wave states of the epilogue share one buffer
+  __shared__ __align__(16) char lds[kTileBytes > kRedBytes ? kTileBytes : kRedBytes];
+  __shared__ float red_m[NW][G];
+  __shared__ float red_l[NW][G];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4;
+  const int c16 = lane & 15;
+  uint16_t (*vt)[mg::VPAD] = reinterpret_cast<uint16_t (*)[mg::VPAD]>(lds + wave * KC * mg::VPAD * 2);
+
+  WaveKeys wk;
+  wk.bt = p.block_table + static_cast<int64_t>(b) * p.bt_stride;
+  wk.begin = begin;
+  wk.end = end;
+  const int c_first = begin / KC;
+  const int c_last = (end - 1) / KC;
+  wk.c0 = c_first + wave;
+  wk.step = NW;
+  wk.nk = (wk.c0 <= c_last) ? (c_last - wk.c0) / NW + 1 : 0;
+  wk.ppc_shift = 0;                // a chunk never spans two pages (page_size >= 16)
+  wk.ptab = 0;
+  wk.group = -1;
+
+  const uint16_t* kbase = p.k + static_cast<int64_t>(gk) * p.head_stride;
+  const uint16_t* vbase = p.v + static_cast<int64_t>(gk) * p.head_stride;
+
+  const int gq = 1 << p.group_shift;
+  const int64_t row0 = static_cast<int64_t>(b) * p.num_q_heads + static_cast<int64_t>(gk) * gq;
+  const bool head_live = c16 < G;
+
+  // B operand of the scores: q of head c16, dims 32ks + 8g .. +8
+  uint4 qb[mg::KS];
+  {
+    const uint16_t* qrow = p.q + (row0 + head_offset(p, head_live ? c16 : 0)) * D + 8 * g;
 #pragma unroll
-    for (int w = 1; w < NW; ++w) M = fmaxf(M, red_m[w][h]);
-    float W = 0.0f, o = 0.0f;
+    for (int ks = 0; ks < mg::KS; ++ks)
+      qb[ks] = head_live ? load16(qrow + 32 * ks) : make_uint4(0, 0, 0, 0);
+  }
+  int lo_h = 0, hi_h = 0;          // no key for a padding head
+  if (head_live) head_bounds(p, p.context_lens[b], c16, begin, end, lo_h, hi_h);
+
+  f32x4_t acc[mg::NT];
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float sc = (red_m[w][h] == -INFINITY) ? 0.0f : fast_exp2(red_m[w][h] - M);
-      W += red_l[w][h] * sc;
-      o += red_acc[w][h][d] * sc;
+  for (int nt = 0; nt < mg::NT; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_ref = -INFINITY;         // per head c16, equal on its 4 lanes
+  float l_sum = 0.0f;              // this lane's share of head c16's sum
+
+  const int koff = c16 * p.token_bytes + 16 * g;
+  const int voff0 = (lane / mg::LV) * p.token_bytes + 16 * (lane % mg::LV);
+  uint4 kr[mg::KS], vr[mg::NV];
+  auto issue_k = [&](int k) {
+    const int t0 = (wk.c0 + k * NW) * KC;
+    const auto rs = tile_rsrc(kbase, page_of<KC>(wk, k, t0, p.page_shift), p.page_bytes, p.tile_bytes);
+    const int soff = (t0 & (p.page_size - 1)) * p.token_bytes;
+    const int voff = koff | dead_bit(t0 + c16, wk.begin, wk.end);
+#pragma unroll
+    for (int ks = 0; ks < mg::KS; ++ks) kr[ks] = tile_load(rs, voff + 64 * ks, soff);
+  };
+  auto issue_v = [&](int k) {
+    const int t0 = (wk.c0 + k * NW) * KC;
+    const auto rs = tile_rsrc(vbase, page_of<KC>(wk, k, t0, p.page_shift), p.page_bytes, p.tile_bytes);
+    const int soff = (t0 & (p.page_size - 1)) * p.token_bytes;
+#pragma unroll
+    for (int j = 0; j < mg::NV; ++j)
+      vr[j] = tile_load(rs, voff0 | dead_bit(t0 + mg::TV * j + lane / mg::LV, wk.begin, wk.end),
+                        soff + mg::TV * j * p.token_bytes);
+  };
+
+  if (wk.nk > 0) {
+    ensure_pages<KC>(wk, 0, lane, p.page_shift);
+    issue_k(0);
+    issue_v(0);
+  }
+  const uint16_t* brow = &vt[4 * g + (c16 >> 2)][4 * (c16 & 3)];
+  for (int k = 0; k < wk.nk; ++k) {
+    const int t0 = (wk.c0 + k * NW) * KC;
+    const bool more = k + 1 < wk.nk;
+    f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < mg::KS; ++ks) sc = mfma(kr[ks], qb[ks], sc);
+    if (more) {
+      ensure_pages<KC>(wk, k + 1, lane, p.page_shift);
+      issue_k(k + 1);
     }
-    const bool any = W > 0.0f;
-    if (final_out) {
-      if ((h >> p.group_shift) >= p.num_queries) continue;   // padding query
-      final_out[hoff(h) * D + d] = f32_to_bf16_rne(any ? o / W : 0.0f);
-      if (d == 0 && final_lse) final_lse[hoff(h)] = any ? M * kLn2 + __logf(W) : -INFINITY;
-    } else {
-      out[h * hstride * D + d] = any ? o / W : 0.0f;
-      if (d == 0) {
-        mx[h * hstride] = any ? M * kLn2 : -INFINITY;
-        sm[h * hstride] = W;
-      }
+
+    // lane holds keys t0 + 4g + i of head c16
+    float s[4];
+    float cm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + 4 * g + i;
+      s[i] = (t >= lo_h && t < hi_h) ? sc[i] * p.scale_log2 : -INFINITY;
+      cm = fmaxf(cm, s[i]);
+    }
+    cm = fmaxf(cm, xor16(cm));
+    cm = fmaxf(cm, xor32(cm));
+    const bool bump = cm > m_ref + 8.0f;
+    if (__builtin_amdgcn_read_exec() & __ballot(bump)) {
+      const float nref = bump ? cm : m_ref;
+      const float alpha = (m_ref == -INFINITY) ? 0.0f : fast_exp2(m_ref - nref);
+      m_ref = nref;
+      l_sum *= alpha;
+      // accumulator rows are heads 4g + i: fetch their factors
+      float ar[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * g + i);
+#pragma unroll
+      for (int nt = 0; nt < mg::NT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[nt][i] *= ar[i];
+    }
+    const float base = (m_ref == -INFINITY) ? 0.0f : m_ref;
+    uint16_t ph[4], pm[4], pl[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float e = fast_exp2(s[i] - base);
+      l_sum += e;
+      split3_bf16(e, ph[i], pm[i], pl[i]);
+    }
+    const uint2 pa_hi = make_uint2(pack_bf16(ph[0], ph[1]), pack_bf16(ph[2], ph[3]));
+    const uint2 pa_mid = make_uint2(pack_bf16(pm[0], pm[1]), pack_bf16(pm[2], pm[3]));
+    const uint2 pa_lo = make_uint2(pack_bf16(pl[0], pl[1]), pack_bf16(pl[2], pl[3]));
+
+    // V rows to the wave's tile, then the next chunk's V loads
+#pragma unroll
+    for (int j = 0; j < mg::NV; ++j)
+      *reinterpret_cast<uint4*>(&vt[mg::TV * j + lane / mg::LV][8 * (lane % mg::LV)]) = vr[j];
+    if (more) issue_v(k + 1);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int nt = 0; nt < mg::NT; ++nt) {
+      const uint2 bv = lds_read_tr(brow + 16 * nt);
+      acc[nt] = mfma16(pa_lo, bv, acc[nt]);
+      acc[nt] = mfma16(pa_mid, bv, acc[nt]);
+      acc[nt] = mfma16(pa_hi, bv, acc[nt]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  }
+
+  // head c16's sum over the 4 lane groups
+  l_sum += xor16(l_sum);
+  l_sum += xor32(l_sum);
+
+  __syncthreads();                 // every wave is done with its V tile
+  float* red_acc = reinterpret_cast<float*>(lds);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * g + i;
+    if (h < G) {
+#pragma unroll
+      for (int nt = 0; nt < mg::NT; ++nt) red_acc[(wave * G + h) * D + 16 * nt + c16] = acc[nt][i];
     }
   }
+  if (g == 0 && head_live) {
+    red_m[wave][c16] = m_ref;
+    red_l[wave][c16] = l_sum;
+  }
+  __syncthreads();
+  write_range<D, G, NW>(p, red_acc, red_m, red_l, out, mx, sm, hstride, final_out, final_lse);
   __syncthreads();   // the shared buffers are reused by the block's next range
+}
+
+// Groups of 8 and 16 heads run on the matrix cores, smaller ones on the
+// vector ALUs.
+template <int D, int G>
+constexpr bool kUseMfma = G >= 8;
+
+template <int D, int G, int NW>
+__device__ __forceinline__ void attend_range(const SplitParams& p, int b, int gk, int begin,
+                                             int end, float* out, float* mx, float* sm,
+                                             int64_t hstride, uint16_t* final_out = nullptr,
+                                             float* final_lse = nullptr) {
+  if constexpr (kUseMfma<D, G>)
+    attend_range_mfma<D, G, NW>(p, b, gk, begin, end, out, mx, sm, hstride, final_out, final_lse);
+  else
+    attend_range_valu<D, G, NW>(p, b, gk, begin, end, out, mx, sm, hstride, final_out, final_lse);
 }
 
 // Fixed partitions: block (j, gk, b) handles keys [lo + j*P, lo + (j+1)*P).

@@ -32,14 +32,10 @@
 
 #include "pa_decode.h"
 #include "pa_device.h"
+#include "pa_mfma.h"
 #include "pa_validate.h"
 
 namespace pa {
-
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
-typedef __attribute__((ext_vector_type(4))) float f32x4_t;
-typedef __attribute__((ext_vector_type(4))) short s16x4_t;
-typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 constexpr int kLat = kMlaLat;      // 512
 constexpr int kRow = kMlaRow;      // 576
@@ -84,37 +80,6 @@ struct MlaParams {
   int32_t min_keys;        // keys per block below which fewer blocks are used
   float scale_log2;
 };
-
-__device__ __forceinline__ uint32_t pack_bf16(uint16_t lo, uint16_t hi) {
-  return static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
-}
-
-__device__ __forceinline__ float bf16_val(uint16_t b) { return u2f(static_cast<uint32_t>(b) << 16); }
-
-// x = hi + mid + lo exactly: hi = bf16(x), mid = bf16(x - hi), lo = x - hi - mid
-// (round to nearest even; each residual is exact in fp32 and the last one
-// has at most 8 significant bits left).
-__device__ __forceinline__ void split3_bf16(float x, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
-  hi = f32_to_bf16_rne(x);
-  const float r = x - bf16_val(hi);
-  mid = f32_to_bf16_rne(r);
-  lo = f32_to_bf16_rne(r - bf16_val(mid));
-}
-
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
-
-__device__ __forceinline__ f32x4_t mfma(uint4 a, uint4 b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
-}
-
-// Transposed 64-bit LDS read (ds_read_b64_tr_b16).  Within each 16-lane
-// group, lane j receives element k (k < 4) of the 4 bf16 that lane 4k + j/4
-// addresses, at position j % 4: with lane a pointing at row a/4, columns
-// 4(a%4) .. +4 of a row-major tile, lane j gets column j of rows 0..3.
-__device__ __forceinline__ uint2 lds_read_tr(const uint16_t* p) {
-  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p));
-  return __builtin_bit_cast(uint2, v);
-}
 
 // ---- 1. absorption: q_abs = q_nope . W_UK[h] on MFMA, split in three; rope copied ---
 //
