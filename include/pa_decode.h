@@ -155,8 +155,9 @@ PA_API int pa_merge_lse(const float* part_out, const float* part_max,
  * out [batch][num_q_heads][head_dim] bf16; lse_out [batch][num_q_heads] fp32
  * (natural log of the softmax denominator, -inf for an empty row) or NULL.
  * workspace: device memory of at least pa_decode_workspace_size(...) bytes,
- * 256-byte aligned, owned by the caller and clobbered by the call (no state
- * is kept between calls).
+ * 256-byte aligned, owned by the caller and clobbered by the call; it needs
+ * no initialisation (every call rewrites what it later reads) and keeps no
+ * state between calls.  Two calls must not share a workspace while both run.
  * ------------------------------------------------------------------------- */
 PA_API int pa_decode(const void* q, const void* k_pool, const void* v_pool,
               const pa_kv_layout* kv, const int32_t* block_table,

@@ -196,6 +196,7 @@ int decode_impl(const void* q, const void* k_pool, const void* v_pool, const pa_
   bl.seg_out = reinterpret_cast<float*>(ws + plan.off_seg_out);
   bl.seg_max = reinterpret_cast<float*>(ws + plan.off_seg_max);
   bl.seg_sum = reinterpret_cast<float*>(ws + plan.off_seg_sum);
+  bl.row_info = reinterpret_cast<int32_t*>(ws + plan.off_row_info);
   bl.min_units = pa::kMinUnitsPerBlock;
   bl.rows = plan.rows;
   bl.batch = batch;

@@ -25,6 +25,7 @@
 #include "pa_device.h"
 #include "pa_mfma.h"
 #include "pa_params.h"
+#include "pa_validate.h"
 
 namespace pa {
 
@@ -260,9 +261,12 @@ __device__ __forceinline__ void head_bounds(const SplitParams& p, int n, int h, 
 }
 
 // Merge of the NW waves' states of one range and the write of its result.
-// Wave w left, per head h < G, its running max red_m[w][h] (log2 domain, -inf
-// if it saw no key), its sum red_l[w][h] relative to that max and its
-// unnormalised accumulator red_acc[(w*G + h)*D + d].  Writes the fp32 partial
+// Wave w left, per head h < G, the reference max red_m[w][h] (log2 domain, -inf
+// if it saw no key) its sum red_l[w][h] and unnormalised accumulator
+// red_acc[(w*G + h)*D + d] are relative to, and the largest score it saw,
+// red_mt[w][h] (>= red_m[w][h]; the same array when the reference is the
+// running max).  Results are expressed relative to the largest score of the
+// range, so the partial's max is that score.  Writes the fp32 partial
 // of head h to out + h*hstride*D, mx[h*hstride] (natural-log max) and
 // sm[h*hstride] (sum) -- or, when `final_out` is set (the range is the row's
 // only one), the bf16 output of head h to final_out + head_offset(h)*D and
@@ -271,30 +275,42 @@ __device__ __forceinline__ void head_bounds(const SplitParams& p, int n, int h, 
 // -inf, sum 0.
 template <int D, int G, int NW>
 __device__ __forceinline__ void write_range(const SplitParams& p, const float* red_acc,
-                                            const float (*red_m)[G], const float (*red_l)[G],
-                                            float* out, float* mx, float* sm, int64_t hstride,
-                                            uint16_t* final_out, float* final_lse) {
-  for (int i = threadIdx.x; i < G * D; i += 64 * NW) {
-    const int h = i / D;
-    const int d = i % D;
-    float M = red_m[0][h];
+                                            const float (*red_m)[G], const float (*red_mt)[G],
+                                            const float (*red_l)[G], float* out, float* mx,
+                                            float* sm, int64_t hstride, uint16_t* final_out,
+                                            float* final_lse) {
+  constexpr int D4 = D / 4;        // a thread takes 4 consecutive dims of one head
+  for (int i = threadIdx.x; i < G * D4; i += 64 * NW) {
+    const int h = i / D4;
+    const int d = (i % D4) * 4;
+    float M = red_mt[0][h];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) M = fmaxf(M, red_m[w][h]);
-    float W = 0.0f, o = 0.0f;
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, red_mt[w][h]);
+    float W = 0.0f;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       const float sc = (red_m[w][h] == -INFINITY) ? 0.0f : fast_exp2(red_m[w][h] - M);
       W += red_l[w][h] * sc;
-      o += red_acc[(w * G + h) * D + d] * sc;
+      const float4 a = *reinterpret_cast<const float4*>(&red_acc[(w * G + h) * D + d]);
+      o.x += a.x * sc;
+      o.y += a.y * sc;
+      o.z += a.z * sc;
+      o.w += a.w * sc;
     }
     const bool any = W > 0.0f;
+    const float inv = any ? 1.0f / W : 0.0f;
     if (final_out) {
       if ((h >> p.group_shift) >= p.num_queries) continue;   // padding query
       const int64_t ho = head_offset(p, h);
-      final_out[ho * D + d] = f32_to_bf16_rne(any ? o / W : 0.0f);
+      uint2 packed;
+      packed.x = pack_bf16(f32_to_bf16_rne(o.x * inv), f32_to_bf16_rne(o.y * inv));
+      packed.y = pack_bf16(f32_to_bf16_rne(o.z * inv), f32_to_bf16_rne(o.w * inv));
+      *reinterpret_cast<uint2*>(final_out + ho * D + d) = packed;
       if (d == 0 && final_lse) final_lse[ho] = any ? M * kLn2 + __logf(W) : -INFINITY;
     } else {
-      out[h * hstride * D + d] = any ? o / W : 0.0f;
+      *reinterpret_cast<float4*>(out + h * hstride * D + d) =
+          make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
       if (d == 0) {
         mx[h * hstride] = any ? M * kLn2 : -INFINITY;
         sm[h * hstride] = W;
@@ -496,8 +512,8 @@ __device__ __forceinline__ void attend_range_valu(const SplitParams& p, int b, i
   }
   __syncthreads();
 
-  write_range<D, G, NW>(p, &red_acc[0][0][0], red_m, red_l, out, mx, sm, hstride, final_out,
-                        final_lse);
+  write_range<D, G, NW>(p, &red_acc[0][0][0], red_m, red_m, red_l, out, mx, sm, hstride,
+                        final_out, final_lse);
   __syncthreads();   // the shared buffers are reused by the block's next range
 }
 
@@ -531,7 +547,7 @@ struct MfmaGeo {
   static constexpr int TV = 64 / LV;     // V rows per load
   static constexpr int NV = KC / TV;     // V loads per chunk
   static constexpr int VPAD = D + 16;    // LDS row stride of the V tile (elements)
-  static_assert(G == 8 || G == 16, "MFMA path takes 8 or 16 heads");
+  static_assert(G >= 1 && G <= 16, "one 16-column MFMA tile holds the group");
 };
 
 template <int D, int G, int NW>
@@ -546,6 +562,7 @@ __device__ __forceinline__ void attend_range_mfma(const SplitParams& p, int b, i
   // the V tiles of the loop and the wave states of the epilogue share one buffer
   __shared__ __align__(16) char lds[kTileBytes > kRedBytes ? kTileBytes : kRedBytes];
   __shared__ float red_m[NW][G];
+  __shared__ float red_mt[NW][G];
   __shared__ float red_l[NW][G];
 
   const int lane = threadIdx.x & 63;
@@ -589,6 +606,7 @@ __device__ __forceinline__ void attend_range_mfma(const SplitParams& p, int b, i
 #pragma unroll
   for (int nt = 0; nt < mg::NT; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_ref = -INFINITY;         // per head c16, equal on its 4 lanes
+  float m_top = -INFINITY;         // largest score of head c16 so far (>= m_ref, < m_ref + 8)
   float l_sum = 0.0f;              // this lane's share of head c16's sum
 
   const int koff = c16 * p.token_bytes + 16 * g;
@@ -640,6 +658,7 @@ __device__ __forceinline__ void attend_range_mfma(const SplitParams& p, int b, i
     }
     cm = fmaxf(cm, xor16(cm));
     cm = fmaxf(cm, xor32(cm));
+    m_top = fmaxf(m_top, cm);
     const bool bump = cm > m_ref + 8.0f;
     if (__builtin_amdgcn_read_exec() & __ballot(bump)) {
       const float nref = bump ? cm : m_ref;
@@ -700,17 +719,23 @@ __device__ __forceinline__ void attend_range_mfma(const SplitParams& p, int b, i
   }
   if (g == 0 && head_live) {
     red_m[wave][c16] = m_ref;
+    red_mt[wave][c16] = m_top;
     red_l[wave][c16] = l_sum;
   }
   __syncthreads();
-  write_range<D, G, NW>(p, red_acc, red_m, red_l, out, mx, sm, hstride, final_out, final_lse);
+  write_range<D, G, NW>(p, red_acc, red_m, red_mt, red_l, out, mx, sm, hstride, final_out,
+                        final_lse);
   __syncthreads();   // the shared buffers are reused by the block's next range
 }
 
-// Groups of 8 and 16 heads run on the matrix cores, smaller ones on the
-// vector ALUs.
+// Groups of 4 to 16 heads run on the matrix cores, 1 and 2 on the vector
+// ALUs (measured on the bs64 GQA-4 decode: 199 us on MFMA against 206 us).
 template <int D, int G>
-constexpr bool kUseMfma = G >= 8;
+constexpr bool kUseMfma = G >= 4;
+
+// Waves per SIMD the compiler must fit the range kernels' registers into.
+template <int D, int G>
+constexpr int kMinWaves = kUseMfma<D, G> ? (D == 128 ? 3 : 2) : 1;
 
 template <int D, int G, int NW>
 __device__ __forceinline__ void attend_range(const SplitParams& p, int b, int gk, int begin,
@@ -725,7 +750,8 @@ __device__ __forceinline__ void attend_range(const SplitParams& p, int b, int gk
 
 // Fixed partitions: block (j, gk, b) handles keys [lo + j*P, lo + (j+1)*P).
 template <int D, int G>
-__global__ __launch_bounds__(kBlock) void split_kernel(const SplitParams p) {
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kMinWaves<D, G>)))
+void split_kernel(const SplitParams p) {
   const int j = blockIdx.x;
   const int gk = blockIdx.y;
   const int b = blockIdx.z;
@@ -763,11 +789,14 @@ __global__ __launch_bounds__(kBlock) void split_kernel(const SplitParams p) {
 // r + i, which is unique (each segment starts at the (r + i)-th boundary of
 // the merged row/block boundary sequence) and makes the slots of one row
 // contiguous, in ascending key order.  A row that lies inside one block's share
-// is written out directly by that block; the others are merged afterwards.
-// Every block, and the merge, derives the split from the context lengths
-// itself (a scan by one wave), so no plan has to be built and read back.  The
-// split points depend on the context lengths of the whole batch and on
-// nothing else (not on where pages live).
+// is written out directly by that block.  Every call rewrites every row's
+// record, (first block << 12) | pieces, from the block holding the row's first
+// piece (0 pieces for a sequence with no key), and the merge kernel combines
+// the pieces of the rows with two or more, in ascending order.  Every block
+// derives the split from the context lengths itself (a scan by one wave), so
+// no plan has to be built and read back.  The split points depend on the
+// context lengths of the whole batch and on nothing else (not on where pages
+// live).
 
 __device__ __forceinline__ int64_t seq_len(const int32_t* ctx, int b, int window) {
   const int n = ctx[b];
@@ -808,13 +837,23 @@ __device__ __forceinline__ void locate_unit(const int32_t* ctx, int batch, int w
 
 
 template <int D, int G>
-__global__ __launch_bounds__(kBlock) void balanced_split_kernel(const SplitParams p,
-                                                                const BalancedLayout bl) {
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kMinWaves<D, G>)))
+void balanced_split_kernel(const SplitParams p, const BalancedLayout bl) {
   __shared__ int64_t sh_total;
   __shared__ int64_t sh_pre;
   __shared__ int sh_b;
   const int i = blockIdx.x;
   const int hkv = p.kv_heads;
+  // sequences with no key: output 0, log-sum-exp -inf (block i takes b = i,
+  // i + grid, ...; the out rows of a sequence are contiguous)
+  for (int b = i; b < bl.batch; b += gridDim.x) {
+    if (p.context_lens[b] > 0) continue;
+    const int64_t r0 = static_cast<int64_t>(b) * p.num_q_heads;
+    for (int j = threadIdx.x; j < p.num_q_heads * D; j += kBlock) bl.out[r0 * D + j] = 0;
+    if (bl.lse)
+      for (int j = threadIdx.x; j < p.num_q_heads; j += kBlock) bl.lse[r0 + j] = -INFINITY;
+    for (int g = threadIdx.x; g < hkv; g += kBlock) bl.row_info[static_cast<int64_t>(b) * hkv + g] = 0;
+  }
   if (threadIdx.x < 64) {
     const int64_t keys = total_keys(p.context_lens, bl.batch, p.reach);
     const int64_t T = keys * hkv;
@@ -856,116 +895,98 @@ __global__ __launch_bounds__(kBlock) void balanced_split_kernel(const SplitParam
       const int end = lo + static_cast<int>(x1 - off);
       // a row that lies inside this block's share gets its final output here
       const bool whole = off >= s0 && off + len <= s1;
-      const int64_t slot = static_cast<int64_t>(b * hkv + gk) + i;
+      const int64_t r = static_cast<int64_t>(b) * hkv + gk;
+      const int64_t slot = r + i;
       const int64_t h0 = static_cast<int64_t>(b) * p.num_q_heads + static_cast<int64_t>(gk) * gq;
       attend_range<D, G, kWaves>(p, b, gk, begin, end, bl.seg_out + slot * G * D,
                                  bl.seg_max + slot * G, bl.seg_sum + slot * G, 1,
                                  whole ? bl.out + h0 * D : nullptr,
                                  (whole && bl.lse) ? bl.lse + h0 : nullptr);
+      // the block holding a row's first piece records where its pieces are:
+      // slots r + i .. r + i + count - 1 (count 1: written here already)
+      if (x0 == off && threadIdx.x == 0)
+        bl.row_info[r] = (i << 12) | (block_of(off + len - 1, T, nb) - i + 1);
     }
     pre += len;
     ++b;
   }
 }
 
-// Merge of the fp32 partials in slots slot0 .. slot0+count-1 (ascending key
-// order) of one row, all G heads, by the whole block; writes the bf16 output
-// of head h to out + h*D and its log-sum-exp to lse[h].  Up to kBatch slots
-// are read in one go (independent loads), longer rows in rounds of kBatch.
-template <int D, int G>
-__device__ __forceinline__ void merge_segments(const BalancedLayout& bl, int64_t slot0, int count,
-                                               uint16_t* out, float* lse) {
-  constexpr int kBatch = 16;
-  const int gq = 1 << bl.group_shift;
-  for (int i = blockIdx.y * kBlock + threadIdx.x; i < G * D; i += kBlock * gridDim.y) {
-    const int h = i / D;
-    const int d = i % D;
-    // output row of virtual head h (query h >> shift, q head h & (gq - 1));
-    // padding queries past the last real one write nothing
-    if ((h >> bl.group_shift) >= bl.num_queries) continue;
-    const int64_t ho = static_cast<int64_t>((h >> bl.group_shift) * bl.q_heads + (h & (gq - 1)));
-    const float* pm = bl.seg_max + slot0 * G + h;
-    const float* pl = bl.seg_sum + slot0 * G + h;
-    const float* po = bl.seg_out + (slot0 * G + h) * D + d;
-    float M = -INFINITY;
-    for (int k0 = 0; k0 < count; k0 += kBatch) {
-      float mk[kBatch];
-#pragma unroll
-      for (int k = 0; k < kBatch; ++k) mk[k] = (k0 + k < count) ? pm[(k0 + k) * G] : -INFINITY;
-#pragma unroll
-      for (int k = 0; k < kBatch; ++k) M = fmaxf(M, mk[k]);
-    }
-    if (M == -INFINITY) {          // no piece saw a key for this head
-      out[ho * D + d] = 0;
-      if (d == 0 && lse) lse[ho] = -INFINITY;
-      continue;
-    }
-    float W = 0.0f, o = 0.0f;
-    for (int k0 = 0; k0 < count; k0 += kBatch) {
-      float wk[kBatch], ok[kBatch];
-#pragma unroll
-      for (int k = 0; k < kBatch; ++k) {
-        const bool in = k0 + k < count;
-        wk[k] = in ? pl[(k0 + k) * G] * __expf(pm[(k0 + k) * G] - M) : 0.0f;
-        ok[k] = in ? po[static_cast<int64_t>(k0 + k) * G * D] : 0.0f;
-      }
-#pragma unroll
-      for (int k = 0; k < kBatch; ++k) W += wk[k];
-#pragma unroll
-      for (int k = 0; k < kBatch; ++k) o = fmaf(wk[k], ok[k], o);
-    }
-    out[ho * D + d] = f32_to_bf16_rne(o / W);
-    if (d == 0 && lse) lse[ho] = M + __logf(W);
-  }
-}
-
-// Block (r, y) handles outputs y*256 .. +256 of the G*D (virtual) heads' dims
-// of row r = (b, g): rows with no key get zeros and lse -inf, rows that one
-// block covered are already written, the rest are merged here.  `window` is
-// the reach of the row's key range.
+// Merge of the cut rows: block (r, y) combines the pieces of row r = (b, g),
+// float4 units y*256 .. +256 of its G*D (virtual) head dims.  All pieces are
+// read in one go (up to kBatch at a time, with a running max across
+// batches), in ascending slot order; rows not cut (whole, or with no key) were
+// written by the split kernel (which rewrites every row's record each call).
 template <int D, int G>
 __global__ __launch_bounds__(kBlock) void balanced_merge_kernel(const BalancedLayout bl,
-                                                               int num_q_heads, int window,
-                                                               int split_grid) {
-  __shared__ int64_t sh_total, sh_pre;
+                                                               int num_q_heads) {
+  constexpr int kBatch = 8;
+  constexpr int D4 = D / 4;
   const int r = blockIdx.x;
+  const int info = bl.row_info[r];
+  const int count = info & 0xfff;
+  const int first = info >> 12;
+  // rows with one piece (or none) are done; the slot range stays inside the
+  // workspace whatever the record holds
+  if (count < 2 || first < 0 || first + count > kMaxBalancedBlocks) return;
+  const int64_t slot0 = r + static_cast<int64_t>(first);
+  const int u = blockIdx.y * kBlock + threadIdx.x;
+  if (u >= G * D4) return;
+  const int h = u / D4;
+  const int d = (u % D4) * 4;
+  // output row of virtual head h (query h >> shift, q head h & (gq - 1));
+  // padding queries past the last real one write nothing
+  if ((h >> bl.group_shift) >= bl.num_queries) return;
+  const int gq = 1 << bl.group_shift;
   const int hkv = bl.rows / bl.batch;
   const int b = r / hkv;
-  const int gk = r - b * hkv;
-  if (threadIdx.x < 64) {
-    const int64_t T = total_keys(bl.context_lens, bl.batch, window) * hkv;
-    int64_t pre = 0;
-    const int lane = threadIdx.x & 63;
-    for (int b0 = 0; b0 < b; b0 += 64)
-      pre += (b0 + lane < b) ? seq_len(bl.context_lens, b0 + lane, window) : 0;
-    pre = wave_sum64(pre);
-    if (threadIdx.x == 0) {
-      sh_total = T;
-      sh_pre = pre;
+  const int64_t h0 = static_cast<int64_t>(b) * num_q_heads + static_cast<int64_t>(r - b * hkv) * gq;
+  const int64_t ho = h0 + (h >> bl.group_shift) * bl.q_heads + (h & (gq - 1));
+  const float* pm = bl.seg_max + slot0 * G + h;
+  const float* pl = bl.seg_sum + slot0 * G + h;
+  const float* po = bl.seg_out + (slot0 * G + h) * D + d;
+  float M = -INFINITY, W = 0.0f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int k0 = 0; k0 < count; k0 += kBatch) {
+    float mk[kBatch], lk[kBatch];
+    float4 ok[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const bool in = k0 + k < count;
+      mk[k] = in ? pm[(k0 + k) * G] : -INFINITY;
+      lk[k] = in ? pl[(k0 + k) * G] : 0.0f;
+      ok[k] = in ? *reinterpret_cast<const float4*>(po + static_cast<int64_t>(k0 + k) * G * D)
+                 : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    float Mn = M;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) Mn = fmaxf(Mn, mk[k]);
+    if (Mn == -INFINITY) continue;            // no piece so far saw a key for this head
+    const float a = __expf(M - Mn);           // 0 while M is -inf
+    W *= a;
+    o.x *= a; o.y *= a; o.z *= a; o.w *= a;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const float w = lk[k] * __expf(mk[k] - Mn);   // 0 for an empty piece (l = 0, m = -inf)
+      W += w;
+      o.x = fmaf(w, ok[k].x, o.x);
+      o.y = fmaf(w, ok[k].y, o.y);
+      o.z = fmaf(w, ok[k].z, o.z);
+      o.w = fmaf(w, ok[k].w, o.w);
+    }
+    M = Mn;
   }
-  __syncthreads();
-  const int64_t T = sh_total;
-  const int64_t len = seq_len(bl.context_lens, b, window);
-  const int gq = 1 << bl.group_shift;
-  const int64_t h0 = static_cast<int64_t>(b) * num_q_heads + static_cast<int64_t>(gk) * gq;
-  if (len == 0) {
-    for (int i = blockIdx.y * kBlock + threadIdx.x; i < G * D; i += kBlock * gridDim.y) {
-      const int h = i / D;
-      if ((h >> bl.group_shift) >= bl.num_queries) continue;
-      const int64_t ho = static_cast<int64_t>((h >> bl.group_shift) * bl.q_heads + (h & (gq - 1)));
-      bl.out[(h0 + ho) * D + i % D] = 0;
-      if (bl.lse && i % D == 0) bl.lse[h0 + ho] = -INFINITY;
-    }
+  uint16_t* dst = bl.out + ho * D + d;
+  if (M == -INFINITY) {                       // no piece saw a key for this head
+    *reinterpret_cast<uint2*>(dst) = make_uint2(0, 0);
+    if (d == 0 && bl.lse) bl.lse[ho] = -INFINITY;
     return;
   }
-  const int nb = used_blocks(T, split_grid, bl.min_units);
-  const int64_t off = sh_pre * hkv + static_cast<int64_t>(gk) * len;
-  const int i0 = block_of(off, T, nb);
-  const int i1 = block_of(off + len - 1, T, nb);
-  if (i1 == i0) return;                       // written by the split kernel
-  merge_segments<D, G>(bl, static_cast<int64_t>(r) + i0, i1 - i0 + 1, bl.out + h0 * D,
-                       bl.lse ? bl.lse + h0 : nullptr);
+  const float inv = 1.0f / W;
+  *reinterpret_cast<uint2*>(dst) =
+      make_uint2(pack_bf16(f32_to_bf16_rne(o.x * inv), f32_to_bf16_rne(o.y * inv)),
+                 pack_bf16(f32_to_bf16_rne(o.z * inv), f32_to_bf16_rne(o.w * inv)));
+  if (d == 0 && bl.lse) bl.lse[ho] = M + __logf(W);
 }
 
 // ---- merge -----------------------------------------------------------------------
@@ -1077,8 +1098,8 @@ static hipError_t launch_balanced_dg(const SplitParams& p, const BalancedLayout&
   hipLaunchKernelGGL((balanced_split_kernel<D, G>), dim3(grid), dim3(kBlock), 0, stream, p, bl);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((balanced_merge_kernel<D, G>), dim3(bl.rows, (G * D + kBlock - 1) / kBlock),
-                     dim3(kBlock), 0, stream, bl, p.num_q_heads, p.reach, grid);
+  hipLaunchKernelGGL((balanced_merge_kernel<D, G>), dim3(bl.rows, (G * D / 4 + kBlock - 1) / kBlock),
+                     dim3(kBlock), 0, stream, bl, p.num_q_heads);
   return hipGetLastError();
 }
 

@@ -66,6 +66,9 @@ struct BalancedLayout {
   float* seg_out;        // [(rows + grid) * G][D]  partial of segment slot s, head h at s*G + h
   float* seg_max;        // [(rows + grid) * G]
   float* seg_sum;
+  // Record of row r, rewritten by every call: (first block << 12) | pieces,
+  // the pieces sitting in slots r + first .. r + first + pieces - 1.
+  int32_t* row_info;     // [rows]
   int64_t min_units;     // a block owns at least this many units (keys of one KV head)
   int32_t rows;          // batch * num_kv_heads
   int32_t batch;

@@ -160,6 +160,7 @@ bool plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32
   plan->off_seg_out = o;    o += round_up(slots * plan->group * head_dim * sizeof(float), 256);
   plan->off_seg_max = o;    o += round_up(slots * plan->group * sizeof(float), 256);
   plan->off_seg_sum = o;    o += round_up(slots * plan->group * sizeof(float), 256);
+  plan->off_row_info = o;   o += round_up(static_cast<size_t>(plan->rows) * sizeof(int32_t), 256);
   plan->bytes = o;
   return true;
 }

@@ -50,7 +50,9 @@ constexpr int64_t kMinUnitsPerBlock = 128;   // keys (of one KV head) below whic
 struct DecodePlan {
   int32_t rows = 0;          // batch * num_kv_heads
   int32_t group = 0;
-  size_t off_seg_out = 0, off_seg_max = 0, off_seg_sum = 0, bytes = 0;
+  size_t off_seg_out = 0, off_seg_max = 0, off_seg_sum = 0;
+  size_t off_row_info = 0;   // one 32-bit record per row
+  size_t bytes = 0;
 };
 bool plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                  int32_t max_pages_per_seq, int32_t page_size, int32_t window, DecodePlan* plan);

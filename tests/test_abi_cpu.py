@@ -93,10 +93,12 @@ def test_workspace_and_partition_plan():
     # suggested two-stage partition: bs64 32q/8kv d128, 256 pages of 32 -> 512 keys
     assert pb.pa_decode_partition_size(64, 32, 8, 128, 256, 32, 0) == 512
     # pa_decode's balanced split: one fp32 partial slot per (row, block) segment,
-    # rows + 2048 slots of G*(D+2) floats
+    # rows + 2048 slots of G*(D+2) floats, and a 4-byte record per row
     need = pb.pa_decode_workspace_size(64, 32, 8, 128, 256, 32, 0)
-    slots = 64 * 8 + 2048
-    assert slots * 4 * 130 * 4 <= need < slots * 4 * 130 * 4 + 1024
+    rows = 64 * 8
+    slots = rows + 2048
+    base = slots * 4 * 130 * 4 + rows * 4
+    assert base <= need < base + 1024
     # a window bounds the keys, hence the partitions
     p = pb.pa_decode_partition_size(32, 16, 2, 256, 512, 32, 4096)
     assert p >= 128 and 4096 % p == 0

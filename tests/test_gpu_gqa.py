@@ -186,6 +186,29 @@ def test_run_to_run_bit_identical():
         assert torch.equal(lse, first_lse)
 
 
+def test_workspace_needs_no_initialisation(oracle):
+    """Rows cut into many pieces (one KV head, long rows), merged by the block
+    that finishes last: a workspace full of random bytes, reused call after
+    call, gives the same bits as a zeroed one, and passes the oracle gate."""
+    from paged_attention_decode_05_amd import binding as pb
+    case = wl.make_gqa_case(context_lens=(0, 1, 5000, 17, 9000, 0, 4096), num_q_heads=8,
+                            num_kv_heads=1, head_dim=128, page_size=16, seed=8610)
+    dc = dev_case(case)
+    B, H, D = dc.q.shape
+    nbytes = pb.pa_decode_workspace_size(B, H, 1, D, dc.max_pages, dc.page_size, dc.window)
+    g = torch.Generator(device="cuda").manual_seed(8611)
+    junk = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda", generator=g)
+    ref, ref_lse = oracle.decode(case)
+    base, base_lse = run_decode(dc)
+    _gate(base, ref, "zeroed workspace")
+    _lse_ok(base_lse, ref_lse, "zeroed workspace")
+    ones = torch.full((nbytes,), 255, dtype=torch.uint8, device="cuda")
+    for ws in (junk, junk, ones, ones):
+        out, lse = run_decode(dc, workspace=ws)
+        assert torch.equal(out.view(torch.int16), base.view(torch.int16))
+        assert torch.equal(lse, base_lse)
+
+
 def test_page_permutation_bit_identical():
     case = wl.make_gqa_case(context_lens=(1, 31, 32, 33, 64, 100, 685, 1000), num_q_heads=8,
                             num_kv_heads=2, head_dim=128, page_size=32, seed=8601, pool_pages=128,
