@@ -88,6 +88,13 @@ class Oracle:
         self.lib.oracle_mla_cache_insert.argtypes = [u16p, C.c_int64, u16p, C.c_int64, u16p, pool,
                                                      i64p, C.c_int32, C.c_int32, C.c_int32]
         self.lib.oracle_mla_cache_insert.restype = C.c_int
+        u8p = C.POINTER(C.c_uint8)
+        self.lib.oracle_e4m3_value.argtypes = [C.c_uint8]
+        self.lib.oracle_e4m3_value.restype = C.c_double
+        self.lib.oracle_pa_decode_fp8.argtypes = [u16p, u8p, u8p, pool, i32p, C.c_int32, i32p,
+                                                  C.c_int32, C.c_int32, C.c_double, C.c_double,
+                                                  C.c_double, C.c_int32, f64p, f64p]
+        self.lib.oracle_pa_decode_fp8.restype = C.c_int
         self.lib.oracle_set_num_threads.argtypes = [C.c_int32]
         self.lib.oracle_max_threads.restype = C.c_int32
         self.lib.oracle_mutation.restype = C.c_int32
@@ -128,6 +135,29 @@ class Oracle:
             bt.shape[1], _ptr(ctx, i32), B, H, float(case.scale), int(w),
             _ptr(out, f64), _ptr(lse, f64))
         self._check(rc, "oracle_pa_decode")
+        return out, lse
+
+    def e4m3_value(self, byte: int) -> float:
+        return float(self.lib.oracle_e4m3_value(int(byte)))
+
+    def decode_fp8(self, case, window: Optional[int] = None):
+        """(out [B,Hq,D], lse [B,Hq]) float64 for a GqaCase with FP8 pools."""
+        assert case.kv_dtype == "fp8"
+        B, H, D = case.batch, case.num_q_heads, case.head_dim
+        q = _bits(case.q)
+        k = np.ascontiguousarray(case.k_pool.cpu().contiguous().numpy(), dtype=np.uint8)
+        v = np.ascontiguousarray(case.v_pool.cpu().contiguous().numpy(), dtype=np.uint8)
+        bt, ctx = _i32(case.block_table), _i32(case.context_lens)
+        out = np.zeros((B, H, D), np.float64)
+        lse = np.zeros((B, H), np.float64)
+        pool = self._pool_of(case)
+        w = case.window if window is None else window
+        u8, u16, i32, f64 = C.c_uint8, C.c_uint16, C.c_int32, C.c_double
+        rc = self.lib.oracle_pa_decode_fp8(
+            _ptr(q, u16), _ptr(k, u8), _ptr(v, u8), C.byref(pool), _ptr(bt, i32), bt.shape[1],
+            _ptr(ctx, i32), B, H, float(case.scale), float(case.k_scale), float(case.v_scale),
+            int(w), _ptr(out, f64), _ptr(lse, f64))
+        self._check(rc, "oracle_pa_decode_fp8")
         return out, lse
 
     def decode_multi(self, case, causal: bool = True, precision: str = "f64"):

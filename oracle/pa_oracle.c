@@ -16,6 +16,8 @@
  *  11 KV insert: page and in-page offset of a slot swapped
  *  12 MLA insert: rope part written first, latent after it
  *  13 multi-query decode: causal limit one key too far
+ *  14 FP8 decode: e4m3 exponent bias read as 8 instead of 7
+ *  15 FP8 decode: the K and V scales swapped
  */
 #include <math.h>
 #include <stdlib.h>
@@ -144,4 +146,110 @@ int oracle_mla_cache_insert(const uint16_t* kv_c, int64_t c_stride, const uint16
 #endif
   }
   return ORACLE_OK;
+}
+
+/* ---- FP8 (OCP E4M3) KV cache ------------------------------------------------
+ *
+ * A quantized pool stores one byte per element; the real value is the byte's
+ * E4M3 value times the pool's scale [vllm.cpp kernel matrix, inventory row
+ * "Quantized KV cache, including FP8 and NVFP4" (the paged path there admits
+ * F32/BF16 only); row KERNEL-KV-CACHE-DSA, the fp8_ds_mla dequant read: an
+ * e4m3 element times its scale].  The pages fix no scale granularity for a
+ * GQA pool; the reading taken is one scale per K pool and one per V pool. */
+
+/* OCP FP8 E4M3 ("e4m3fn"): sign = bit 7, exponent E = bits 6..3 with bias 7,
+ * mantissa M = bits 2..0.  E = 0 is subnormal, M * 2^-9; otherwise
+ * (1 + M/8) * 2^(E-7), except S.1111.111, which is NaN.  There are no
+ * infinities; the largest finite magnitude is 1.75 * 2^8 = 448. */
+double oracle_e4m3_value(uint8_t byte) {
+  const int sign = byte >> 7;
+  const int e = (byte >> 3) & 15;
+  const int m = byte & 7;
+#if ORACLE_MUTATION == 14
+  const int bias = 8; /* planted */
+#else
+  const int bias = 7;
+#endif
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    v = ldexp((double)m, 1 - bias - 3);
+  else
+    v = ldexp(1.0 + m / 8.0, e - bias);
+  return sign ? -v : v;
+}
+
+/* Decode with FP8 pools, float64: K_t = e4m3(k byte) * k_scale, V_t =
+ * e4m3(v byte) * v_scale, then the same two-pass softmax attention as
+ * oracle_pa_decode over keys [lo, n) in ascending order. */
+int oracle_pa_decode_fp8(const uint16_t* q, const uint8_t* k_pool, const uint8_t* v_pool,
+                         const oracle_pool* pool, const int32_t* block_table, int32_t bt_stride,
+                         const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                         double scale, double k_scale, double v_scale, int32_t window,
+                         double* out, double* lse) {
+  if (!q || !k_pool || !v_pool || !pool || !block_table || !context_lens || !out || !lse ||
+      batch < 0 || num_q_heads <= 0 || pool->num_pages <= 0 || pool->page_size <= 0 ||
+      pool->num_kv_heads <= 0 || pool->head_dim <= 0 || num_q_heads % pool->num_kv_heads)
+    return ORACLE_ERR_ARGS;
+#if ORACLE_MUTATION == 15
+  { const double t = k_scale; k_scale = v_scale; v_scale = t; } /* planted */
+#endif
+  const int32_t D = pool->head_dim;
+  const int32_t G = num_q_heads / pool->num_kv_heads;
+  int err = ORACLE_OK;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+  for (int32_t b = 0; b < batch; ++b) {
+    for (int32_t h = 0; h < num_q_heads; ++h) {
+      const int32_t n = context_lens[b];
+      const int32_t lo = (window > 0 && n - window > 0) ? n - window : 0;
+      const int32_t g = h / G;
+      const uint16_t* qr = q + ((int64_t)b * num_q_heads + h) * D;
+      const int32_t* bt = block_table + (int64_t)b * bt_stride;
+      double* o = out + ((int64_t)b * num_q_heads + h) * D;
+      for (int32_t d = 0; d < D; ++d) o[d] = 0.0;
+      const int32_t cnt = n > lo ? n - lo : 0;
+      double* sc = (double*)malloc(sizeof(double) * (size_t)(cnt > 0 ? cnt : 1));
+      if (!sc) {
+#pragma omp atomic write
+        err = ORACLE_ERR_ARGS;
+        continue;
+      }
+      int bad = 0;
+      double m = -INFINITY;
+      for (int32_t i = 0; i < cnt && !bad; ++i) {          /* pass 1: scores, max */
+        const int32_t t = lo + i;
+        const int32_t page = bt[t / pool->page_size];
+        if (page < 0 || page >= pool->num_pages) { bad = 1; break; }
+        const uint8_t* k = k_pool + (int64_t)page * pool->page_stride +
+                           (int64_t)g * pool->head_stride +
+                           (int64_t)(t % pool->page_size) * pool->token_stride;
+        double dot = 0.0;
+        for (int32_t d = 0; d < D; ++d)
+          dot += (double)bf16_to_float(qr[d]) * (oracle_e4m3_value(k[d]) * k_scale);
+        sc[i] = scale * dot;
+        if (sc[i] > m) m = sc[i];
+      }
+      double l = 0.0;
+      for (int32_t i = 0; i < cnt && !bad; ++i) {          /* pass 2: sums */
+        const int32_t t = lo + i;
+        const int32_t page = bt[t / pool->page_size];
+        const uint8_t* v = v_pool + (int64_t)page * pool->page_stride +
+                           (int64_t)g * pool->head_stride +
+                           (int64_t)(t % pool->page_size) * pool->token_stride;
+        const double e = exp(sc[i] - m);
+        l += e;
+        for (int32_t d = 0; d < D; ++d) o[d] += e * (oracle_e4m3_value(v[d]) * v_scale);
+      }
+      free(sc);
+      if (bad) {
+#pragma omp atomic write
+        err = ORACLE_ERR_PAGE;
+        continue;
+      }
+      if (cnt > 0)
+        for (int32_t d = 0; d < D; ++d) o[d] /= l;
+      lse[(int64_t)b * num_q_heads + h] = cnt > 0 ? m + log(l) : -INFINITY;
+    }
+  }
+  return err;
 }

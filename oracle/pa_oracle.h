@@ -125,6 +125,17 @@ ORACLE_DECL_MULTI(_f32)
 ORACLE_DECL_MLA(_f64)
 ORACLE_DECL_MLA(_f32)
 
+/* FP8 KV cache (OCP E4M3 bytes, one scale per pool), float64 only.
+ * oracle_e4m3_value decodes one byte (NaN for S.1111.111).
+ * oracle_pa_decode_fp8: as oracle_pa_decode_f64 with K = e4m3(k) * k_scale
+ * and V = e4m3(v) * v_scale; pool strides are in bytes (= elements). */
+double oracle_e4m3_value(uint8_t byte);
+int oracle_pa_decode_fp8(const uint16_t* q, const uint8_t* k_pool, const uint8_t* v_pool,
+                         const oracle_pool* pool, const int32_t* block_table, int32_t bt_stride,
+                         const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                         double scale, double k_scale, double v_scale, int32_t window,
+                         double* out, double* lse);
+
 /* Thread control for the (b, h) loop; results do not depend on it. */
 void oracle_set_num_threads(int32_t n);
 int32_t oracle_max_threads(void);

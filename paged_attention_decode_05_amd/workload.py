@@ -60,10 +60,19 @@ class GqaCase:
     partition_size: Optional[int] = None
     name: str = "custom"
     seed: int = 0
+    # "bf16" pools, or "fp8": one OCP E4M3 byte per element (uint8 tensors), the
+    # element's value being e4m3(byte) * k_scale (K) or * v_scale (V)
+    kv_dtype: str = "bf16"
+    k_scale: float = 1.0
+    v_scale: float = 1.0
 
     @property
     def batch(self) -> int:
         return int(self.q.shape[0])
+
+    @property
+    def kv_elem_bytes(self) -> int:
+        return 1 if self.kv_dtype == "fp8" else 2
 
     @property
     def num_q_heads(self) -> int:
@@ -97,7 +106,7 @@ class GqaCase:
 
     def kv_bytes(self) -> int:
         """Algorithmic K+V bytes one decode call must read."""
-        return self.kv_read_tokens() * 2 * self.num_kv_heads * self.head_dim * 2
+        return self.kv_read_tokens() * 2 * self.num_kv_heads * self.head_dim * self.kv_elem_bytes
 
     def to(self, device) -> "GqaCase":
         c = GqaCase(**{f: getattr(self, f) for f in self.__dataclass_fields__})
@@ -183,11 +192,23 @@ def _assign_pages(gen, ctx: Sequence[int], page_size: int, max_pages: int,
     return bt, pool_pages
 
 
+# E4M3 bit pattern of NaN (S.1111.111), the canary of an FP8 pool
+FP8_NAN = 0x7F
+
+
+def _normal_fp8(gen: torch.Generator, shape, scale: float) -> torch.Tensor:
+    """Bytes of N(0, 1) / scale cast to OCP E4M3 (torch's round-to-nearest
+    conversion, clamped to the finite range +-448), as a uint8 tensor: the
+    element's value is e4m3(byte) * scale."""
+    x = torch.randn(*shape, generator=gen, dtype=torch.float32).div_(scale).clamp_(-448.0, 448.0)
+    return x.to(torch.float8_e4m3fn).view(torch.uint8)
+
+
 def _poison_gqa(pool: torch.Tensor, layout: str, bt: torch.Tensor, ctx, page_size: int,
                 window: int) -> None:
     """NaN every slot no correct reader touches: unused pages, the tail of each
     sequence's last page, and (with a window) every key older than the window."""
-    nan = float("nan")
+    nan = FP8_NAN if pool.dtype == torch.uint8 else float("nan")
     live = torch.zeros(pool.shape[0], dtype=torch.bool)
     for b, n in enumerate(ctx):
         k = (n + page_size - 1) // page_size
@@ -221,13 +242,15 @@ def make_gqa_case(*, context_lens: Sequence[int], num_q_heads: int, num_kv_heads
                   q_std: float = 1.0, scale: Optional[float] = None, poison: bool = True,
                   partition_size: Optional[int] = None, name: str = "custom",
                   ctx_draw: Optional[tuple] = None, batch: Optional[int] = None,
-                  num_queries: int = 1) -> GqaCase:
+                  num_queries: int = 1, kv_dtype: str = "bf16", k_scale: float = 1.0,
+                  v_scale: float = 1.0) -> GqaCase:
     """Build one GQA decode case.  ``ctx_draw=(lo, hi)`` draws ``batch`` context
     lengths uniformly from the integers lo..hi (inclusive) instead of using
     ``context_lens``.  ``num_queries`` > 1 gives q of shape [B, S, Hq, D] (the
     last S positions of each context), for multi-query decode; the NaN
     canaries then spare the S - 1 keys the earlier queries' windows reach
-    further back."""
+    further back.  ``kv_dtype="fp8"`` draws E4M3 pools whose values times
+    k_scale / v_scale are N(0, 1) samples rounded to E4M3 precision."""
     if layout not in LAYOUTS:
         raise ValueError(layout)
     gen = torch.Generator().manual_seed(int(seed))
@@ -247,8 +270,14 @@ def make_gqa_case(*, context_lens: Sequence[int], num_q_heads: int, num_kv_heads
         shape = (pool_pages, num_kv_heads, page_size, head_dim)
     else:
         shape = (pool_pages, page_size, num_kv_heads, head_dim)
-    k_pool = _normal_bf16(gen, shape)
-    v_pool = _normal_bf16(gen, shape)
+    if kv_dtype == "fp8":
+        k_pool = _normal_fp8(gen, shape, k_scale)
+        v_pool = _normal_fp8(gen, shape, v_scale)
+    elif kv_dtype == "bf16":
+        k_pool = _normal_bf16(gen, shape)
+        v_pool = _normal_bf16(gen, shape)
+    else:
+        raise ValueError(kv_dtype)
     if poison:
         reach = window + num_queries - 1 if window > 0 else 0
         _poison_gqa(k_pool, layout, bt, ctx, page_size, reach)
@@ -257,7 +286,9 @@ def make_gqa_case(*, context_lens: Sequence[int], num_q_heads: int, num_kv_heads
                    context_lens=torch.tensor(ctx, dtype=torch.int32), num_pages=pool_pages,
                    page_size=page_size, num_kv_heads=num_kv_heads, head_dim=head_dim,
                    layout=layout, scale=(1.0 / math.sqrt(head_dim)) if scale is None else scale,
-                   window=window, partition_size=partition_size, name=name, seed=seed)
+                   window=window, partition_size=partition_size, name=name, seed=seed,
+                   kv_dtype=kv_dtype, k_scale=k_scale if kv_dtype == "fp8" else 1.0,
+                   v_scale=v_scale if kv_dtype == "fp8" else 1.0)
 
 
 def make_mla_case(*, context_lens: Sequence[int] = (), num_heads: int, page_size: int, seed: int,

@@ -29,11 +29,20 @@ def key_range(n: int, window: int) -> tuple[int, int]:
     return (max(0, n - window) if window > 0 else 0), n
 
 
+def fp8_pool_f64(pool: torch.Tensor, scale: float) -> np.ndarray:
+    """Values of an E4M3 byte pool times its scale, decoded by torch."""
+    return pool.detach().cpu().contiguous().view(torch.float8_e4m3fn).to(torch.float64).numpy() * scale
+
+
 def dense_attention(case, window=None):
     """(out [B,Hq,D], lse [B,Hq]) in float64 over materialised K/V."""
     w = case.window if window is None else window
-    K = pool_f64(case.k_pool)
-    V = pool_f64(case.v_pool)
+    if getattr(case, "kv_dtype", "bf16") == "fp8":
+        K = fp8_pool_f64(case.k_pool, case.k_scale)
+        V = fp8_pool_f64(case.v_pool, case.v_scale)
+    else:
+        K = pool_f64(case.k_pool)
+        V = pool_f64(case.v_pool)
     q = case.q.to(torch.float64).numpy()
     bt = case.block_table.numpy()
     ctx = case.context_lens.numpy()

@@ -27,6 +27,13 @@ builds with a planted mistake (at least one must fail).
                        keys (with and without a window), bit for bit
   multi_noncausal      every non-causal query == decode over the whole context
   multi_bruteforce     multi-query decode == float64 dense causal attention
+  e4m3_decode          E4M3 byte values: closed forms from the OCP definition,
+                       all 256 bytes == torch.float8_e4m3fn, finite codes
+                       strictly increasing
+  fp8_equals_bf16      FP8 pools with power-of-two scales == the bf16 oracle on
+                       the exactly dequantised pools, bit for bit
+  fp8_bruteforce       FP8 decode == float64 dense attention over K/V decoded
+                       by torch and scaled (scales not powers of two)
 """
 from __future__ import annotations
 
@@ -416,6 +423,59 @@ def multi_bruteforce(o):
         assert np.abs(lse[fin] - ref_lse[fin]).max() < 1e-12
 
 
+def e4m3_decode(o):
+    # closed forms of the OCP E4M3 definition (bias 7, subnormals m * 2^-9)
+    want = {0x00: 0.0, 0x01: 2.0**-9, 0x07: 7 * 2.0**-9, 0x08: 2.0**-6, 0x30: 0.5,
+            0x38: 1.0, 0x3C: 1.5, 0x40: 2.0, 0x77: 240.0, 0x7E: 448.0, 0xB8: -1.0,
+            0xFE: -448.0}
+    for b, v in want.items():
+        assert o.e4m3_value(b) == v, (hex(b), o.e4m3_value(b), v)
+    assert math.copysign(1.0, o.e4m3_value(0x80)) == -1.0 and o.e4m3_value(0x80) == 0.0
+    assert math.isnan(o.e4m3_value(0x7F)) and math.isnan(o.e4m3_value(0xFF))
+    # every byte against torch's decoder
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = np.array([o.e4m3_value(b) for b in range(256)])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(got[fin], ref[fin])
+    assert np.all(np.diff(got[:0x7F]) > 0)
+
+
+def _fp8_case(seed, ks, vs, **kw):
+    base = dict(context_lens=(0, 1, 5, 37, 100), num_q_heads=4, num_kv_heads=2, head_dim=16,
+                page_size=8, window=0)
+    base.update(kw)
+    return make_gqa_case(seed=seed, kv_dtype="fp8", k_scale=ks, v_scale=vs, **base)
+
+
+def fp8_equals_bf16(o):
+    from brute import fp8_pool_f64
+    for layout, window, ks, vs in (("PHSD", 0, 2.0**-6, 2.0**-5), ("PSHD", 30, 2.0**-4, 2.0**-7)):
+        c8 = _fp8_case(7140, ks, vs, layout=layout, window=window)
+        c16 = c8.to("cpu")
+        c16.kv_dtype, c16.k_scale, c16.v_scale = "bf16", 1.0, 1.0
+        c16.k_pool = torch.from_numpy(fp8_pool_f64(c8.k_pool, ks)).to(torch.bfloat16)
+        c16.v_pool = torch.from_numpy(fp8_pool_f64(c8.v_pool, vs)).to(torch.bfloat16)
+        # the dequantised values are exact in bf16 (3 mantissa bits, power-of-two scale)
+        back = torch.from_numpy(fp8_pool_f64(c8.k_pool, ks))
+        assert torch.equal(c16.k_pool.to(torch.float64).nan_to_num(7.0), back.nan_to_num(7.0))
+        out8, lse8 = o.decode_fp8(c8)
+        out16, lse16 = o.decode(c16, "f64")
+        assert np.array_equal(out8, out16) and np.array_equal(lse8, lse16), (layout, window)
+
+
+def fp8_bruteforce(o):
+    for i, (layout, window) in enumerate((("PHSD", 0), ("PSHD", 0), ("PHSD", 40))):
+        c = _fp8_case(7150 + i, 0.0173, 0.0291, layout=layout, window=window, poison=False)
+        ref, ref_lse = dense_attention(c)
+        cp = _fp8_case(7150 + i, 0.0173, 0.0291, layout=layout, window=window)
+        out, lse = o.decode_fp8(cp)
+        assert np.abs(out - ref).max() < F64_TOL, np.abs(out - ref).max()
+        fin = np.isfinite(ref_lse)
+        assert np.array_equal(fin, np.isfinite(lse))
+        assert np.abs(lse[fin] - ref_lse[fin]).max() < F64_TOL
+
+
 PINS = {
     "dense_bruteforce": dense_bruteforce,
     "single_token": single_token,
@@ -434,6 +494,9 @@ PINS = {
     "multi_is_shortened": multi_is_shortened,
     "multi_noncausal": multi_noncausal,
     "multi_bruteforce": multi_bruteforce,
+    "e4m3_decode": e4m3_decode,
+    "fp8_equals_bf16": fp8_equals_bf16,
+    "fp8_bruteforce": fp8_bruteforce,
 }
 
 

@@ -27,6 +27,8 @@ MUTATIONS = {
     11: "KV insert with page and offset swapped",
     12: "MLA insert with the rope part first",
     13: "multi-query causal limit one key too far",
+    14: "E4M3 exponent bias 8",
+    15: "FP8 K and V scales swapped",
 }
 
 
