@@ -51,7 +51,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama",
-                    choices=["tiny", "llama", "d256w", "long", "mla", "verify", "insert"])
+                    choices=["tiny", "llama", "d256w", "long", "mla", "verify", "insert",
+                             "llama_fp8"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run K device-to-device copies of a 1 GiB buffer instead (reference "
@@ -97,7 +98,8 @@ def main() -> int:
     log(f"generating workload {a.workload} (seeded) ...")
     t0 = time.time()
     cases = [wl.NAMED[a.workload](poison=False, seed=wl.SEED_BASE + 100 * i + {
-        "tiny": 1, "llama": 2, "d256w": 3, "long": 4}[a.workload]) for i in range(a.rotate)]
+        "tiny": 1, "llama": 2, "d256w": 3, "long": 4, "llama_fp8": 5}[a.workload])
+        for i in range(a.rotate)]
     dcs = [c.to(dev) for c in cases]
     log(f"  {time.time() - t0:.1f}s; pool pages {cases[0].num_pages}, "
         f"sum ctx {int(cases[0].context_lens.sum())}")
@@ -110,10 +112,16 @@ def main() -> int:
     out = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
     kvl = [pb.kv_layout(d.k_pool, d.layout) for d in dcs]
 
+    fp8 = c0.kv_dtype == "fp8"
+
     def step(i):
         d = dcs[i % len(dcs)]
-        pb.pa_decode(d.q, d.k_pool, d.v_pool, kvl[i % len(dcs)], d.block_table, d.context_lens,
-                     d.scale, d.window, out, None, ws)
+        if fp8:
+            pb.pa_decode_fp8(d.q, d.k_pool, d.v_pool, kvl[i % len(dcs)], d.block_table,
+                             d.context_lens, d.scale, d.k_scale, d.v_scale, d.window, out, None, ws)
+        else:
+            pb.pa_decode(d.q, d.k_pool, d.v_pool, kvl[i % len(dcs)], d.block_table,
+                         d.context_lens, d.scale, d.window, out, None, ws)
 
     stream = torch.cuda.current_stream()
     for i in range(a.warmup):
@@ -133,9 +141,9 @@ def main() -> int:
     gbs = mean_bytes / (ms_per_step * 1e-3) / 1e9
 
     # The dominant work is the balanced split-KV kernel; pa_decode launches it
-    # between a one-block plan kernel and the merge kernel inside one C call,
-    # so the per-launch figure brackets the whole call with HIP events on the
-    # launch stream (an upper bound on the split kernel's own duration).
+    # and the merge kernel inside one C call, so the per-launch figure brackets
+    # the whole call with HIP events on the launch stream (an upper bound on
+    # the split kernel's own duration).
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(a.steps)]
     torch.cuda.synchronize()
@@ -166,14 +174,16 @@ def main() -> int:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "storage_dtype": "bf16",
+        "storage_dtype": "e4m3 (one scale per pool)" if fp8 else "bf16",
         "data": "synthetic",
         "config": {
             "workload": {"llama": "llama3-8b-shaped decode, bs64, 32q/8kv heads, d128, page 32, "
                                   "ctx U[512,8192]",
                          "tiny": "tiny paged decode, 8 seqs, 8q/2kv, d128, page 32",
                          "d256w": "d256 GQA-8 sliding window 4096, bs32",
-                         "long": "long context bs4, ctx 32K-128K, d128"}[a.workload],
+                         "long": "long context bs4, ctx 32K-128K, d128",
+                         "llama_fp8": "llama3-8b-shaped decode over an FP8 (E4M3) KV cache, bs64, "
+                                      "32q/8kv heads, d128, page 32, ctx U[512,8192]"}[a.workload],
             "batch": B, "num_q_heads": H, "num_kv_heads": Hkv, "head_dim": D,
             "page_size": c0.page_size, "window": c0.window,
             "sum_context": int(c0.context_lens.sum()), "pool_pages": c0.num_pages,
@@ -189,8 +199,11 @@ def main() -> int:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": recorded_traffic("pa_decode_llama_bs64") if a.workload == "llama" and a.rotate == 1 else None,
-            "kernel": "pa_decode call: balanced_split_kernel + balanced_merge_kernel",
+            "traffic": (recorded_traffic({"llama": "pa_decode_llama_bs64",
+                                          "llama_fp8": "pa_decode_fp8_llama_bs64"}[a.workload])
+                        if a.workload in ("llama", "llama_fp8") and a.rotate == 1 else None),
+            "kernel": ("pa_decode_fp8" if fp8 else "pa_decode") +
+                      " call: balanced_split_kernel + balanced_merge_kernel",
             "algorithmic_bytes_per_launch": int(mean_bytes),
         },
         "cpu_baseline": cpu,
@@ -415,7 +428,10 @@ def cpu_baseline(case):
     t_all = time.time()
     while len(times) < 3 or (time.time() - t_all < 10 and len(times) < 10):
         t = time.time()
-        o.decode(case, "f64")
+        if case.kv_dtype == "fp8":
+            o.decode_fp8(case)
+        else:
+            o.decode(case, "f64")
         times.append(time.time() - t)
     med = statistics.median(times)
     return {"value": round(case.kv_bytes() / med / 1e9, 3), "unit": "GB/s", "cores": threads,

@@ -196,6 +196,35 @@ PA_API int pa_decode_multiquery(const void* q, const void* k_pool, const void* v
                                 int32_t window, void* out, float* lse_out, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * pa_decode_fp8 -- pa_decode over an FP8 KV cache.
+ *
+ * k_pool and v_pool hold one OCP FP8 E4M3 byte per element (sign, 4-bit
+ * exponent with bias 7, 3-bit mantissa; S.1111.111 is NaN; largest finite
+ * magnitude 448).  The value of a K element is e4m3(byte) * k_scale, of a V
+ * element e4m3(byte) * v_scale: one scale per pool [vllm.cpp kernel matrix,
+ * inventory row "Quantized KV cache, including FP8 and NVFP4"; row
+ * KERNEL-KV-CACHE-DSA, the fp8_ds_mla dequant read: the e4m3 element times
+ * its scale; the per-pool granularity is this library's reading, the pages
+ * fix none for a GQA pool].  The bytes are widened to bf16 in registers
+ * (exact), k_scale is folded into the softmax scale and v_scale into the
+ * output, so the result is attention over the dequantized values, computed
+ * as in pa_decode.  K/V bytes read per call are half those of bf16 pools.
+ *
+ * kv: strides and sizes in elements (= bytes); every K/V row must start on
+ * a 16-byte boundary (strides multiples of 16).  k_scale, v_scale: finite,
+ * > 0.  Every group size pa_decode takes is supported.  workspace: at least
+ * pa_decode_workspace_size(...) bytes for the same shapes, 256-byte aligned,
+ * needs no initialisation.  Other arguments, the split, determinism and
+ * the error codes as pa_decode.
+ * ------------------------------------------------------------------------- */
+PA_API int pa_decode_fp8(const void* q, const void* k_pool, const void* v_pool,
+                         const pa_kv_layout* kv, const int32_t* block_table,
+                         int32_t block_table_stride, const int32_t* context_lens,
+                         int32_t batch, int32_t num_q_heads, int32_t max_pages_per_seq,
+                         float scale, float k_scale, float v_scale, int32_t window, void* out,
+                         float* lse_out, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of workspace pa_decode_multiquery needs (0 on invalid shapes). */
 PA_API size_t pa_decode_multiquery_workspace_size(int32_t batch, int32_t num_q_heads,
                                                   int32_t num_kv_heads, int32_t head_dim,

@@ -24,7 +24,8 @@ STATUS_NAMES = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_U
 EXPORTS = ("pa_decode", "pa_decode_splitkv", "pa_merge_lse", "pa_decode_workspace_size",
            "pa_decode_partition_size", "mla_absorbed_decode",
            "mla_absorbed_decode_workspace_size", "pa_kv_insert", "mla_cache_insert",
-           "pa_decode_multiquery", "pa_decode_multiquery_workspace_size", "pa_last_error")
+           "pa_decode_multiquery", "pa_decode_multiquery_workspace_size", "pa_decode_fp8",
+           "pa_last_error")
 
 
 class PaError(RuntimeError):
@@ -50,6 +51,9 @@ def _load() -> C.CDLL:
     lib.pa_decode.argtypes = [vp, vp, vp, kvp, i32p, i32, i32p, i32, i32, i32, C.c_float, i32, vp,
                               vp, vp, C.c_size_t, vp]
     lib.pa_decode.restype = C.c_int
+    lib.pa_decode_fp8.argtypes = [vp, vp, vp, kvp, i32p, i32, i32p, i32, i32, i32, C.c_float,
+                                  C.c_float, C.c_float, i32, vp, vp, vp, C.c_size_t, vp]
+    lib.pa_decode_fp8.restype = C.c_int
     lib.pa_decode_splitkv.argtypes = [vp, vp, vp, kvp, i32p, i32, i32p, i32, i32, i32, C.c_float,
                                       i32, i32, i32, vp, vp, vp, vp]
     lib.pa_decode_splitkv.restype = C.c_int
@@ -115,8 +119,9 @@ def _contig(t: torch.Tensor, name: str) -> None:
 
 
 def kv_layout(pool: torch.Tensor, layout: str = "PHSD") -> KvLayout:
-    """Descriptor of a bf16 pool tensor: "PHSD" = [page][kv head][slot][dim],
-    "PSHD" = [page][slot][kv head][dim], "PSR" = [page][slot][row] (MLA)."""
+    """Descriptor of a pool tensor (bf16, or uint8 holding E4M3 bytes; strides
+    in elements): "PHSD" = [page][kv head][slot][dim], "PSHD" = [page][slot]
+    [kv head][dim], "PSR" = [page][slot][row] (MLA)."""
     s = pool.stride()
     if layout == "PHSD":
         P, H, S, D = pool.shape
@@ -164,6 +169,26 @@ def pa_decode(q, k_pool, v_pool, kv: KvLayout, block_table, context_lens, scale:
                        int(window), _ptr(out, torch.bfloat16, "out"),
                        _ptr(lse_out, torch.float32, "lse_out"), _ptr(workspace), ws_bytes,
                        _stream(stream))
+    _check(rc)
+
+
+def pa_decode_fp8(q, k_pool, v_pool, kv: KvLayout, block_table, context_lens, scale: float,
+                  k_scale: float, v_scale: float, window: int, out, lse_out=None, workspace=None,
+                  max_pages_per_seq=None, stream=None) -> None:
+    """pa_decode over E4M3 pools (uint8 tensors of the raw bytes)."""
+    for t, n in ((q, "q"), (block_table, "block_table"), (context_lens, "context_lens"),
+                 (out, "out")):
+        _contig(t, n)
+    B, H = q.shape[0], q.shape[1]
+    maxp = block_table.shape[1] if max_pages_per_seq is None else max_pages_per_seq
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = LIB.pa_decode_fp8(_ptr(q, torch.bfloat16, "q"), _ptr(k_pool, torch.uint8, "k_pool"),
+                           _ptr(v_pool, torch.uint8, "v_pool"), C.byref(kv),
+                           _ptr(block_table, torch.int32, "block_table"), block_table.stride(0),
+                           _ptr(context_lens, torch.int32, "context_lens"), B, H, maxp,
+                           float(scale), float(k_scale), float(v_scale), int(window),
+                           _ptr(out, torch.bfloat16, "out"), _ptr(lse_out, torch.float32, "lse_out"),
+                           _ptr(workspace), ws_bytes, _stream(stream))
     _check(rc)
 
 

@@ -23,7 +23,7 @@ SOURCES = ["pa_api.hip", "pa_gqa.hip", "pa_mla.hip", "pa_cache.hip", "pa_validat
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-fvisibility=hidden",
     f"-I{INCLUDE}", f"-I{CSRC}",

@@ -18,8 +18,8 @@ hipError_t launch_split(const SplitParams& p, int head_dim, int group, int batch
                         int num_kv_heads, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, int head_dim, int batch, hipStream_t stream);
 hipError_t launch_balanced(const SplitParams& sp, const BalancedLayout& bl, int head_dim, int group,
-                           int grid, hipStream_t stream);
-int balanced_grid(int head_dim, int group, int num_cus, int max_blocks);
+                           int grid, hipStream_t stream, bool fp8);
+int balanced_grid(int head_dim, int group, int num_cus, int max_blocks, bool fp8);
 
 }  // namespace pa
 
@@ -55,7 +55,8 @@ pa::SplitParams split_params(const void* q, const void* k_pool, const void* v_po
                              int32_t block_table_stride, const int32_t* context_lens,
                              int32_t num_q_heads, float scale, int32_t window,
                              int32_t partition_size, int32_t max_partitions, float* part_out,
-                             float* part_max, float* part_sum, int32_t write_empty) {
+                             float* part_max, float* part_sum, int32_t write_empty,
+                             int32_t elem_bytes = 2) {
   pa::SplitParams p{};
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k_pool);
@@ -68,9 +69,10 @@ pa::SplitParams split_params(const void* q, const void* k_pool, const void* v_po
   p.page_stride = kv->page_stride;
   p.head_stride = kv->head_stride;
   p.token_stride = static_cast<int32_t>(kv->token_stride);
-  p.tile_bytes = static_cast<int32_t>(((kv->page_size - 1) * kv->token_stride + kv->head_dim) * 2);
-  p.token_bytes = static_cast<int32_t>(kv->token_stride * 2);
-  p.page_bytes = static_cast<uint32_t>(kv->page_stride * 2);
+  p.tile_bytes =
+      static_cast<int32_t>(((kv->page_size - 1) * kv->token_stride + kv->head_dim) * elem_bytes);
+  p.token_bytes = static_cast<int32_t>(kv->token_stride * elem_bytes);
+  p.page_bytes = static_cast<uint32_t>(kv->page_stride * elem_bytes);
   p.bt_stride = block_table_stride;
   p.num_q_heads = num_q_heads;
   p.kv_heads = kv->num_kv_heads;
@@ -86,6 +88,7 @@ pa::SplitParams split_params(const void* q, const void* k_pool, const void* v_po
   p.max_parts = max_partitions;
   p.write_empty = write_empty;
   p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  p.out_scale = 1.0f;
   return p;
 }
 
@@ -159,15 +162,22 @@ int32_t pa_decode_partition_size(int32_t batch, int32_t num_q_heads, int32_t num
 namespace {
 
 // pa_decode with S query tokens per sequence (S = 1: plain decode).
+// fp8: K/V pools of OCP E4M3 bytes, values e4m3 * k_scale / v_scale.
 int decode_impl(const void* q, const void* k_pool, const void* v_pool, const pa_kv_layout* kv,
                 const int32_t* block_table, int32_t block_table_stride,
                 const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
                 int32_t num_queries, int32_t causal, int32_t max_pages_per_seq, float scale,
                 int32_t window, void* out, float* lse_out, void* workspace,
-                size_t workspace_bytes, void* stream) {
+                size_t workspace_bytes, void* stream, bool fp8 = false, float k_scale = 1.0f,
+                float v_scale = 1.0f) {
   int rc = pa::check_gqa(q, k_pool, v_pool, kv, block_table, block_table_stride, context_lens,
-                         batch, num_q_heads, max_pages_per_seq, scale);
+                         batch, num_q_heads, max_pages_per_seq, scale, fp8 ? 1 : 2);
   if (rc) return rc;
+  if (fp8 && !(std::isfinite(k_scale) && k_scale > 0.0f && std::isfinite(v_scale) &&
+               v_scale > 0.0f))
+    return pa::fail(PA_ERR_SHAPE, "k_scale and v_scale must be finite and > 0");
+  if (fp8 && !(std::isfinite(scale * k_scale) && scale * k_scale > 0.0f))
+    return pa::fail(PA_ERR_SHAPE, "scale * k_scale must be a finite positive float");
   if (!out) return pa::fail(PA_ERR_NULL, "out must not be NULL");
   if (reinterpret_cast<uintptr_t>(out) & 15u)
     return pa::fail(PA_ERR_ALIGN, "out must be 16-byte aligned");
@@ -186,7 +196,8 @@ int decode_impl(const void* q, const void* k_pool, const void* v_pool, const pa_
     return pa::fail(PA_ERR_ALIGN, "workspace must be 256-byte aligned");
   char* ws = static_cast<char*>(workspace);
   const int vgroup = qpad * group;
-  const int nbmax = pa::balanced_grid(kv->head_dim, vgroup, device_cus(), pa::kMaxBalancedBlocks);
+  const int nbmax =
+      pa::balanced_grid(kv->head_dim, vgroup, device_cus(), pa::kMaxBalancedBlocks, fp8);
   if (nbmax < 1) return pa::fail(PA_ERR_UNSUPPORTED, "no balanced-split kernel for these shapes");
 
   pa::BalancedLayout bl{};
@@ -205,15 +216,16 @@ int decode_impl(const void* q, const void* k_pool, const void* v_pool, const pa_
   bl.num_queries = num_queries;
 
   pa::SplitParams sp = split_params(q, k_pool, v_pool, kv, block_table, block_table_stride,
-                                    context_lens, num_q_heads, scale, window, 1, 1, nullptr,
-                                    nullptr, nullptr, 0);
+                                    context_lens, num_q_heads, fp8 ? scale * k_scale : scale,
+                                    window, 1, 1, nullptr, nullptr, nullptr, 0, fp8 ? 1 : 2);
+  if (fp8) sp.out_scale = v_scale;
   sp.num_q_heads = num_q_heads * num_queries;   // rows of q and out per sequence
   sp.num_queries = num_queries;
   sp.causal = causal ? 1 : 0;
   sp.reach = (window > 0 && causal) ? window + num_queries - 1 : window;
   pa::clear_error();
   return launch_status(pa::launch_balanced(sp, bl, kv->head_dim, vgroup, nbmax,
-                                           static_cast<hipStream_t>(stream)),
+                                           static_cast<hipStream_t>(stream), fp8),
                        "balanced decode");
 }
 
@@ -242,6 +254,17 @@ int pa_decode_multiquery(const void* q, const void* k_pool, const void* v_pool,
   return decode_impl(q, k_pool, v_pool, kv, block_table, block_table_stride, context_lens, batch,
                      num_q_heads, num_queries, causal, max_pages_per_seq, scale, window, out,
                      lse_out, workspace, workspace_bytes, stream);
+}
+
+int pa_decode_fp8(const void* q, const void* k_pool, const void* v_pool, const pa_kv_layout* kv,
+                  const int32_t* block_table, int32_t block_table_stride,
+                  const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                  int32_t max_pages_per_seq, float scale, float k_scale, float v_scale,
+                  int32_t window, void* out, float* lse_out, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  return decode_impl(q, k_pool, v_pool, kv, block_table, block_table_stride, context_lens, batch,
+                     num_q_heads, 1, 1, max_pages_per_seq, scale, window, out, lse_out,
+                     workspace, workspace_bytes, stream, true, k_scale, v_scale);
 }
 
 size_t pa_decode_multiquery_workspace_size(int32_t batch, int32_t num_q_heads,

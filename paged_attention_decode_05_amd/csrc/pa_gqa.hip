@@ -299,7 +299,7 @@ __device__ __forceinline__ void write_range(const SplitParams& p, const float* r
       o.w += a.w * sc;
     }
     const bool any = W > 0.0f;
-    const float inv = any ? 1.0f / W : 0.0f;
+    const float inv = any ? p.out_scale / W : 0.0f;   // out_scale: V pool scale (1 for bf16)
     if (final_out) {
       if ((h >> p.group_shift) >= p.num_queries) continue;   // padding query
       const int64_t ho = head_offset(p, h);
@@ -538,25 +538,55 @@ __device__ __forceinline__ void attend_range_valu(const SplitParams& p, int b, i
 // Heads c >= G (G = 8) get q = 0 and are masked out.  The loads of chunk k+1
 // are issued as soon as chunk k's registers are free: K after the scores, V
 // after its LDS write.
-template <int D, int G>
+//
+// FP8 pools (F8): K and V hold one OCP E4M3 byte per element.  They are
+// converted to bf16 in registers (exact: every E4M3 value is a bf16 value);
+// the per-pool scales are folded into the softmax scale (K) and the output
+// (V) by the host.  A 16-byte K load then covers two score steps: lane g
+// holds dims 64j + 16g .. +16 of its key, the first 8 for step 2j and the
+// last 8 for step 2j+1, and q is loaded with the same dims order (the
+// contraction over dims does not depend on it).  V rows are converted on
+// their way into the LDS tile, which stays bf16.
+template <int D, int G, bool F8 = false>
 struct MfmaGeo {
-  static constexpr int KC = 16;          // keys per chunk
+  // A wave's chunk is SUB tiles of 16 keys (a tile never spans two pages);
+  // their loads are issued together and one softmax update covers them.
+  // Measured on the bs64 decode: two tiles per chunk made the FP8 call slower
+  // (125 against 119.5 us) and the bf16 one spill, so a chunk is one tile.
+  static constexpr int SUB = 1;
+  static constexpr int KC = 16 * SUB;    // keys per chunk
   static constexpr int KS = D / 32;      // score k-steps
   static constexpr int NT = D / 16;      // P.V output tiles
-  static constexpr int LV = D / 8;       // lanes per V row in the load layout
+  static constexpr int EB = F8 ? 1 : 2;  // bytes per pool element
+  static constexpr int NK = KS * EB / 2; // 16-byte K loads per lane and 16-key tile
+  static constexpr int LV = D * EB / 16; // lanes per V row in the load layout (16 B each)
   static constexpr int TV = 64 / LV;     // V rows per load
-  static constexpr int NV = KC / TV;     // V loads per chunk
-  static constexpr int VPAD = D + 16;    // LDS row stride of the V tile (elements)
+  static constexpr int NV = 16 / TV;     // V loads per 16-key tile
+  static constexpr int VD = 16 / EB;     // dims per V lane load
+  static constexpr int VPAD = D + 16;    // LDS row stride of the V tile (bf16 elements)
   static_assert(G >= 1 && G <= 16, "one 16-column MFMA tile holds the group");
 };
 
-template <int D, int G, int NW>
+// 16 E4M3 bytes -> 16 bf16 (exact), bytes 0..7 into lo, 8..15 into hi.
+__device__ __forceinline__ uint32_t fp8x2_bf16(uint32_t w, bool high_word) {
+  return __builtin_bit_cast(uint32_t, high_word ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+                                                : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+}
+__device__ __forceinline__ void fp8x16_bf16(uint4 x, uint4& lo, uint4& hi) {
+  lo = make_uint4(fp8x2_bf16(x.x, false), fp8x2_bf16(x.x, true), fp8x2_bf16(x.y, false),
+                  fp8x2_bf16(x.y, true));
+  hi = make_uint4(fp8x2_bf16(x.z, false), fp8x2_bf16(x.z, true), fp8x2_bf16(x.w, false),
+                  fp8x2_bf16(x.w, true));
+}
+
+template <int D, int G, int NW, bool F8>
 __device__ __forceinline__ void attend_range_mfma(const SplitParams& p, int b, int gk, int begin,
                                                   int end, float* out, float* mx, float* sm,
                                                   int64_t hstride, uint16_t* final_out,
                                                   float* final_lse) {
-  using mg = MfmaGeo<D, G>;
+  using mg = MfmaGeo<D, G, F8>;
   constexpr int KC = mg::KC;
+  constexpr int SUB = mg::SUB;
   constexpr int kTileBytes = NW * KC * mg::VPAD * 2;
   constexpr int kRedBytes = NW * G * D * 4;
   // the V tiles of the loop and the wave states of the epilogue share one buffer
@@ -580,24 +610,31 @@ __device__ __forceinline__ void attend_range_mfma(const SplitParams& p, int b, i
   wk.c0 = c_first + wave;
   wk.step = NW;
   wk.nk = (wk.c0 <= c_last) ? (c_last - wk.c0) / NW + 1 : 0;
-  wk.ppc_shift = 0;                // a chunk never spans two pages (page_size >= 16)
+  // pages per chunk: 1, or 2 when a 32-key chunk meets 16-key pages
+  wk.ppc_shift = (KC > p.page_size) ? (ilog2c(KC) - p.page_shift) : 0;
   wk.ptab = 0;
   wk.group = -1;
 
-  const uint16_t* kbase = p.k + static_cast<int64_t>(gk) * p.head_stride;
-  const uint16_t* vbase = p.v + static_cast<int64_t>(gk) * p.head_stride;
+  // pool bases of KV head gk (head_stride counts pool elements)
+  const uint16_t* kbase = reinterpret_cast<const uint16_t*>(
+      reinterpret_cast<const char*>(p.k) + static_cast<int64_t>(gk) * p.head_stride * mg::EB);
+  const uint16_t* vbase = reinterpret_cast<const uint16_t*>(
+      reinterpret_cast<const char*>(p.v) + static_cast<int64_t>(gk) * p.head_stride * mg::EB);
 
   const int gq = 1 << p.group_shift;
   const int64_t row0 = static_cast<int64_t>(b) * p.num_q_heads + static_cast<int64_t>(gk) * gq;
   const bool head_live = c16 < G;
 
-  // B operand of the scores: q of head c16, dims 32ks + 8g .. +8
+  // B operand of the scores: q of head c16, dims 32ks + 8g .. +8 (bf16 pools)
+  // or 64j + 16g + 8(ks & 1) .. +8 with j = ks / 2 (FP8 pools)
   uint4 qb[mg::KS];
   {
-    const uint16_t* qrow = p.q + (row0 + head_offset(p, head_live ? c16 : 0)) * D + 8 * g;
+    const uint16_t* qrow = p.q + (row0 + head_offset(p, head_live ? c16 : 0)) * D;
 #pragma unroll
-    for (int ks = 0; ks < mg::KS; ++ks)
-      qb[ks] = head_live ? load16(qrow + 32 * ks) : make_uint4(0, 0, 0, 0);
+    for (int ks = 0; ks < mg::KS; ++ks) {
+      const int d0 = F8 ? 64 * (ks >> 1) + 16 * g + 8 * (ks & 1) : 32 * ks + 8 * g;
+      qb[ks] = head_live ? load16(qrow + d0) : make_uint4(0, 0, 0, 0);
+    }
   }
   int lo_h = 0, hi_h = 0;          // no key for a padding head
   if (head_live) head_bounds(p, p.context_lens[b], c16, begin, end, lo_h, hi_h);
@@ -609,25 +646,37 @@ __device__ __forceinline__ void attend_range_mfma(const SplitParams& p, int b, i
   float m_top = -INFINITY;         // largest score of head c16 so far (>= m_ref, < m_ref + 8)
   float l_sum = 0.0f;              // this lane's share of head c16's sum
 
+  // K: lane (g, c16) reads key c16 of each tile, 16 bytes at 64 * i + 16 * g,
+  // straight into the A-operand layout.  (Loading whole rows to LDS instead,
+  // with direct global->LDS loads, and reading the operand back measured
+  // slower on the bs64 decode: 198 against 193 us.)
   const int koff = c16 * p.token_bytes + 16 * g;
   const int voff0 = (lane / mg::LV) * p.token_bytes + 16 * (lane % mg::LV);
-  uint4 kr[mg::KS], vr[mg::NV];
+  uint4 kr[SUB][mg::NK], vr[SUB][mg::NV];
   auto issue_k = [&](int k) {
     const int t0 = (wk.c0 + k * NW) * KC;
-    const auto rs = tile_rsrc(kbase, page_of<KC>(wk, k, t0, p.page_shift), p.page_bytes, p.tile_bytes);
-    const int soff = (t0 & (p.page_size - 1)) * p.token_bytes;
-    const int voff = koff | dead_bit(t0 + c16, wk.begin, wk.end);
 #pragma unroll
-    for (int ks = 0; ks < mg::KS; ++ks) kr[ks] = tile_load(rs, voff + 64 * ks, soff);
+    for (int u = 0; u < SUB; ++u) {
+      const int tu = t0 + 16 * u;
+      const auto rs = tile_rsrc(kbase, page_of<KC>(wk, k, tu, p.page_shift), p.page_bytes, p.tile_bytes);
+      const int soff = (tu & (p.page_size - 1)) * p.token_bytes;
+      const int voff = koff | dead_bit(tu + c16, wk.begin, wk.end);
+#pragma unroll
+      for (int i = 0; i < mg::NK; ++i) kr[u][i] = tile_load(rs, voff + 64 * i, soff);
+    }
   };
   auto issue_v = [&](int k) {
     const int t0 = (wk.c0 + k * NW) * KC;
-    const auto rs = tile_rsrc(vbase, page_of<KC>(wk, k, t0, p.page_shift), p.page_bytes, p.tile_bytes);
-    const int soff = (t0 & (p.page_size - 1)) * p.token_bytes;
 #pragma unroll
-    for (int j = 0; j < mg::NV; ++j)
-      vr[j] = tile_load(rs, voff0 | dead_bit(t0 + mg::TV * j + lane / mg::LV, wk.begin, wk.end),
-                        soff + mg::TV * j * p.token_bytes);
+    for (int u = 0; u < SUB; ++u) {
+      const int tu = t0 + 16 * u;
+      const auto rs = tile_rsrc(vbase, page_of<KC>(wk, k, tu, p.page_shift), p.page_bytes, p.tile_bytes);
+      const int soff = (tu & (p.page_size - 1)) * p.token_bytes;
+#pragma unroll
+      for (int j = 0; j < mg::NV; ++j)
+        vr[u][j] = tile_load(rs, voff0 | dead_bit(tu + mg::TV * j + lane / mg::LV, wk.begin, wk.end),
+                             soff + mg::TV * j * p.token_bytes);
+    }
   };
 
   if (wk.nk > 0) {
@@ -639,22 +688,51 @@ __device__ __forceinline__ void attend_range_mfma(const SplitParams& p, int b, i
   for (int k = 0; k < wk.nk; ++k) {
     const int t0 = (wk.c0 + k * NW) * KC;
     const bool more = k + 1 < wk.nk;
-    f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    f32x4_t sc[SUB];
 #pragma unroll
-    for (int ks = 0; ks < mg::KS; ++ks) sc = mfma(kr[ks], qb[ks], sc);
+    for (int u = 0; u < SUB; ++u) {
+      sc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const uint4* kv = kr[u];
+      if constexpr (F8) {
+#pragma unroll
+        for (int i = 0; i < mg::NK; ++i) {
+          uint4 a0, a1;
+          fp8x16_bf16(kv[i], a0, a1);
+          sc[u] = mfma(a0, qb[2 * i], sc[u]);
+          sc[u] = mfma(a1, qb[2 * i + 1], sc[u]);
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < mg::KS; ++ks) sc[u] = mfma(kv[ks], qb[ks], sc[u]);
+      }
+    }
     if (more) {
       ensure_pages<KC>(wk, k + 1, lane, p.page_shift);
       issue_k(k + 1);
     }
 
-    // lane holds keys t0 + 4g + i of head c16
-    float s[4];
+    // lane holds keys t0 + 16u + 4g + i of head c16; a chunk inside every
+    // live head's key range needs no mask (padding heads' values are unused)
+    float s[SUB][4];
     float cm = -INFINITY;
+    const bool inside = !head_live || (t0 >= lo_h && t0 + KC <= hi_h);
+    if (__builtin_amdgcn_read_exec() == __ballot(inside)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = t0 + 4 * g + i;
-      s[i] = (t >= lo_h && t < hi_h) ? sc[i] * p.scale_log2 : -INFINITY;
-      cm = fmaxf(cm, s[i]);
+      for (int u = 0; u < SUB; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          s[u][i] = sc[u][i] * p.scale_log2;
+          cm = fmaxf(cm, s[u][i]);
+        }
+    } else {
+#pragma unroll
+      for (int u = 0; u < SUB; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = t0 + 16 * u + 4 * g + i;
+          s[u][i] = (t >= lo_h && t < hi_h) ? sc[u][i] * p.scale_log2 : -INFINITY;
+          cm = fmaxf(cm, s[u][i]);
+        }
     }
     cm = fmaxf(cm, xor16(cm));
     cm = fmaxf(cm, xor32(cm));
@@ -675,31 +753,65 @@ __device__ __forceinline__ void attend_range_mfma(const SplitParams& p, int b, i
         for (int i = 0; i < 4; ++i) acc[nt][i] *= ar[i];
     }
     const float base = (m_ref == -INFINITY) ? 0.0f : m_ref;
-    uint16_t ph[4], pm[4], pl[4];
+    uint2 pa_hi[SUB], pa_mid[SUB], pa_lo[SUB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float e = fast_exp2(s[i] - base);
-      l_sum += e;
-      split3_bf16(e, ph[i], pm[i], pl[i]);
+    for (int u = 0; u < SUB; ++u) {
+      float e[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        e[i] = fast_exp2(s[u][i] - base);
+        l_sum += e[i];
+      }
+      split3_bf16x2(e[0], e[1], pa_hi[u].x, pa_mid[u].x, pa_lo[u].x);
+      split3_bf16x2(e[2], e[3], pa_hi[u].y, pa_mid[u].y, pa_lo[u].y);
     }
-    const uint2 pa_hi = make_uint2(pack_bf16(ph[0], ph[1]), pack_bf16(ph[2], ph[3]));
-    const uint2 pa_mid = make_uint2(pack_bf16(pm[0], pm[1]), pack_bf16(pm[2], pm[3]));
-    const uint2 pa_lo = make_uint2(pack_bf16(pl[0], pl[1]), pack_bf16(pl[2], pl[3]));
 
-    // V rows to the wave's tile, then the next chunk's V loads
+    // V rows to the wave's tile (as bf16), then the next chunk's V loads
 #pragma unroll
-    for (int j = 0; j < mg::NV; ++j)
-      *reinterpret_cast<uint4*>(&vt[mg::TV * j + lane / mg::LV][8 * (lane % mg::LV)]) = vr[j];
+    for (int u = 0; u < SUB; ++u)
+#pragma unroll
+      for (int j = 0; j < mg::NV; ++j) {
+        // 16-byte units of the row: a lane's VD dims are units m * VD / 8 ..
+        uint4* row = reinterpret_cast<uint4*>(&vt[16 * u + mg::TV * j + lane / mg::LV][0]);
+        const int m = lane % mg::LV;
+        if constexpr (F8) {
+          // the two 16-byte halves are written in an order that puts the 16
+          // lanes of one write pass on 16 different 4-bank groups
+          uint4 lo, hi;
+          fp8x16_bf16(vr[u][j], lo, hi);
+          const int swap = (mg::LV == 8 ? m : m >> 3) & 1;
+          const uint4 first = make_uint4(swap ? hi.x : lo.x, swap ? hi.y : lo.y,
+                                         swap ? hi.z : lo.z, swap ? hi.w : lo.w);
+          const uint4 second = make_uint4(swap ? lo.x : hi.x, swap ? lo.y : hi.y,
+                                          swap ? lo.z : hi.z, swap ? lo.w : hi.w);
+          row[2 * m + swap] = first;
+          row[2 * m + 1 - swap] = second;
+        } else {
+          row[m] = vr[u][j];
+        }
+      }
     if (more) issue_v(k + 1);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // P.V in groups of 8 output tiles: the group's transposed reads first, then
+    // its MFMAs term-major, so no MFMA waits on the one before it and the
+    // reads' latency is paid once per group
+    constexpr int kGroupTiles = mg::NT < 8 ? mg::NT : 8;
 #pragma unroll
-    for (int nt = 0; nt < mg::NT; ++nt) {
-      const uint2 bv = lds_read_tr(brow + 16 * nt);
-      acc[nt] = mfma16(pa_lo, bv, acc[nt]);
-      acc[nt] = mfma16(pa_mid, bv, acc[nt]);
-      acc[nt] = mfma16(pa_hi, bv, acc[nt]);
-    }
+    for (int u = 0; u < SUB; ++u)
+#pragma unroll
+      for (int n0 = 0; n0 < mg::NT; n0 += kGroupTiles) {
+        uint2 bv[kGroupTiles];
+#pragma unroll
+        for (int n = 0; n < kGroupTiles; ++n)
+          bv[n] = lds_read_tr(brow + 16 * u * mg::VPAD + 16 * (n0 + n));
+#pragma unroll
+        for (int n = 0; n < kGroupTiles; ++n) acc[n0 + n] = mfma16(pa_lo[u], bv[n], acc[n0 + n]);
+#pragma unroll
+        for (int n = 0; n < kGroupTiles; ++n) acc[n0 + n] = mfma16(pa_mid[u], bv[n], acc[n0 + n]);
+#pragma unroll
+        for (int n = 0; n < kGroupTiles; ++n) acc[n0 + n] = mfma16(pa_hi[u], bv[n], acc[n0 + n]);
+      }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   }
 
@@ -734,16 +846,18 @@ template <int D, int G>
 constexpr bool kUseMfma = G >= 4;
 
 // Waves per SIMD the compiler must fit the range kernels' registers into.
-template <int D, int G>
-constexpr int kMinWaves = kUseMfma<D, G> ? (D == 128 ? 3 : 2) : 1;
+template <int D, int G, bool F8 = false>
+constexpr int kMinWaves = (F8 || kUseMfma<D, G>) ? (D == 128 ? 3 : 2) : 1;
 
-template <int D, int G, int NW>
+// FP8 pools always take the matrix-core routine.
+template <int D, int G, int NW, bool F8 = false>
 __device__ __forceinline__ void attend_range(const SplitParams& p, int b, int gk, int begin,
                                              int end, float* out, float* mx, float* sm,
                                              int64_t hstride, uint16_t* final_out = nullptr,
                                              float* final_lse = nullptr) {
-  if constexpr (kUseMfma<D, G>)
-    attend_range_mfma<D, G, NW>(p, b, gk, begin, end, out, mx, sm, hstride, final_out, final_lse);
+  if constexpr (F8 || kUseMfma<D, G>)
+    attend_range_mfma<D, G, NW, F8>(p, b, gk, begin, end, out, mx, sm, hstride, final_out,
+                                    final_lse);
   else
     attend_range_valu<D, G, NW>(p, b, gk, begin, end, out, mx, sm, hstride, final_out, final_lse);
 }
@@ -836,8 +950,8 @@ __device__ __forceinline__ void locate_unit(const int32_t* ctx, int batch, int w
 }
 
 
-template <int D, int G>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kMinWaves<D, G>)))
+template <int D, int G, bool F8>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kMinWaves<D, G, F8>)))
 void balanced_split_kernel(const SplitParams p, const BalancedLayout bl) {
   __shared__ int64_t sh_total;
   __shared__ int64_t sh_pre;
@@ -898,7 +1012,7 @@ void balanced_split_kernel(const SplitParams p, const BalancedLayout bl) {
       const int64_t r = static_cast<int64_t>(b) * hkv + gk;
       const int64_t slot = r + i;
       const int64_t h0 = static_cast<int64_t>(b) * p.num_q_heads + static_cast<int64_t>(gk) * gq;
-      attend_range<D, G, kWaves>(p, b, gk, begin, end, bl.seg_out + slot * G * D,
+      attend_range<D, G, kWaves, F8>(p, b, gk, begin, end, bl.seg_out + slot * G * D,
                                  bl.seg_max + slot * G, bl.seg_sum + slot * G, 1,
                                  whole ? bl.out + h0 * D : nullptr,
                                  (whole && bl.lse) ? bl.lse + h0 : nullptr);
@@ -1092,10 +1206,10 @@ static hipError_t launch_split_dg(const SplitParams& p, int batch, int num_kv_he
   return hipGetLastError();
 }
 
-template <int D, int G>
+template <int D, int G, bool F8>
 static hipError_t launch_balanced_dg(const SplitParams& p, const BalancedLayout& bl, int grid,
                                      hipStream_t stream) {
-  hipLaunchKernelGGL((balanced_split_kernel<D, G>), dim3(grid), dim3(kBlock), 0, stream, p, bl);
+  hipLaunchKernelGGL((balanced_split_kernel<D, G, F8>), dim3(grid), dim3(kBlock), 0, stream, p, bl);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((balanced_merge_kernel<D, G>), dim3(bl.rows, (G * D / 4 + kBlock - 1) / kBlock),
@@ -1103,12 +1217,12 @@ static hipError_t launch_balanced_dg(const SplitParams& p, const BalancedLayout&
   return hipGetLastError();
 }
 
-template <int D, int G>
+template <int D, int G, bool F8>
 static int blocks_per_cu() {
   static int cached = -1;
   if (cached < 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, balanced_split_kernel<D, G>, kBlock, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, balanced_split_kernel<D, G, F8>, kBlock, 0) !=
             hipSuccess || n < 1)
       n = 1;
     cached = n;
@@ -1150,54 +1264,40 @@ hipError_t launch_merge(const MergeParams& p, int head_dim, int batch, hipStream
   return hipGetLastError();
 }
 
-template <int D, int G>
+template <int D, int G, bool F8>
 static int balanced_blocks(int num_cus, int max_blocks) {
-  const int n = blocks_per_cu<D, G>() * num_cus;
+  const int n = blocks_per_cu<D, G, F8>() * num_cus;
   return n < max_blocks ? n : max_blocks;
 }
 
+// Calls f.template operator()<D, G, F8>() for a supported (head_dim, group,
+// fp8) triple; returns `none` otherwise.
+template <typename R, typename F>
+static R dispatch_dg(int head_dim, int group, bool fp8, R none, F&& f) {
+#define PA_CASE(DD, GG)                                                                \
+  if (head_dim == DD && group == GG)                                                   \
+    return fp8 ? f.template operator()<DD, GG, true>() : f.template operator()<DD, GG, false>();
+  PA_CASE(128, 1) PA_CASE(128, 2) PA_CASE(128, 4) PA_CASE(128, 8) PA_CASE(128, 16)
+  PA_CASE(256, 1) PA_CASE(256, 2) PA_CASE(256, 4) PA_CASE(256, 8)
+#undef PA_CASE
+  return none;
+}
+
 // Blocks the balanced split would use on this device (occupancy x CUs, capped).
-int balanced_grid(int head_dim, int group, int num_cus, int max_blocks) {
-  if (head_dim == 128) {
-    switch (group) {
-      case 1: return balanced_blocks<128, 1>(num_cus, max_blocks);
-      case 2: return balanced_blocks<128, 2>(num_cus, max_blocks);
-      case 4: return balanced_blocks<128, 4>(num_cus, max_blocks);
-      case 8: return balanced_blocks<128, 8>(num_cus, max_blocks);
-      case 16: return balanced_blocks<128, 16>(num_cus, max_blocks);
-    }
-  } else if (head_dim == 256) {
-    switch (group) {
-      case 1: return balanced_blocks<256, 1>(num_cus, max_blocks);
-      case 2: return balanced_blocks<256, 2>(num_cus, max_blocks);
-      case 4: return balanced_blocks<256, 4>(num_cus, max_blocks);
-      case 8: return balanced_blocks<256, 8>(num_cus, max_blocks);
-    }
-  }
-  return 0;
+int balanced_grid(int head_dim, int group, int num_cus, int max_blocks, bool fp8) {
+  return dispatch_dg<int>(head_dim, group, fp8, 0, [&]<int D, int G, bool F8>() {
+    return balanced_blocks<D, G, F8>(num_cus, max_blocks);
+  });
 }
 
 // Balanced split, then the merge of the rows several blocks shared: the whole
-// of pa_decode.
+// of pa_decode (bf16 or FP8 pools).
 hipError_t launch_balanced(const SplitParams& sp, const BalancedLayout& bl, int head_dim, int group,
-                           int grid, hipStream_t stream) {
-  if (head_dim == 128) {
-    switch (group) {
-      case 1: return launch_balanced_dg<128, 1>(sp, bl, grid, stream);
-      case 2: return launch_balanced_dg<128, 2>(sp, bl, grid, stream);
-      case 4: return launch_balanced_dg<128, 4>(sp, bl, grid, stream);
-      case 8: return launch_balanced_dg<128, 8>(sp, bl, grid, stream);
-      case 16: return launch_balanced_dg<128, 16>(sp, bl, grid, stream);
-    }
-  } else if (head_dim == 256) {
-    switch (group) {
-      case 1: return launch_balanced_dg<256, 1>(sp, bl, grid, stream);
-      case 2: return launch_balanced_dg<256, 2>(sp, bl, grid, stream);
-      case 4: return launch_balanced_dg<256, 4>(sp, bl, grid, stream);
-      case 8: return launch_balanced_dg<256, 8>(sp, bl, grid, stream);
-    }
-  }
-  return hipErrorInvalidValue;
+                           int grid, hipStream_t stream, bool fp8) {
+  return dispatch_dg<hipError_t>(head_dim, group, fp8, hipErrorInvalidValue,
+                                 [&]<int D, int G, bool F8>() {
+                                   return launch_balanced_dg<D, G, F8>(sp, bl, grid, stream);
+                                 });
 }
 
 }  // namespace pa

@@ -36,6 +36,27 @@ __device__ __forceinline__ void split3_bf16(float x, uint16_t& hi, uint16_t& mid
   lo = f32_to_bf16_rne(r - bf16_val(mid));
 }
 
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2v_t;
+
+// Two fp32 -> two bf16 packed in one dword (low half from a), round to
+// nearest even: one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v_t));
+}
+
+// split3_bf16 for a pair, on the hardware conversion: a = hi + mid + lo in the
+// low halves, b in the high halves, exactly (the same argument: each residual
+// is exact in fp32 and the last has at most 8 significant bits).
+__device__ __forceinline__ void split3_bf16x2(float a, float b, uint32_t& hi, uint32_t& mid,
+                                              uint32_t& lo) {
+  hi = cvt_bf16x2(a, b);
+  const float ra = a - u2f(hi << 16), rb = b - u2f(hi & 0xffff0000u);
+  mid = cvt_bf16x2(ra, rb);
+  lo = cvt_bf16x2(ra - u2f(mid << 16), rb - u2f(mid & 0xffff0000u));
+}
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 // D = A.B + C, 16x16x32, bf16 operands (8 per lane), fp32 accumulation.

@@ -42,7 +42,8 @@ struct SplitParams {
   int32_t partition_size;
   int32_t max_parts;
   int32_t write_empty;
-  float scale_log2;
+  float scale_log2;     // softmax scale * log2(e) (times the K pool scale for FP8 pools)
+  float out_scale;      // factor on every output and partial: the V pool scale (1 for bf16)
 };
 
 struct MergeParams {

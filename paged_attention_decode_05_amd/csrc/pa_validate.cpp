@@ -50,7 +50,7 @@ int64_t max_keys(int32_t max_pages_per_seq, int32_t page_size, int32_t window) {
 int check_gqa(const void* q, const void* k_pool, const void* v_pool, const pa_kv_layout* kv,
               const int32_t* block_table, int32_t block_table_stride,
               const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
-              int32_t max_pages_per_seq, float scale) {
+              int32_t max_pages_per_seq, float scale, int32_t elem_bytes) {
   if (!q || !k_pool || !v_pool || !kv || !block_table || !context_lens)
     return fail(PA_ERR_NULL, "a required pointer (q, k_pool, v_pool, kv, block_table, "
                              "context_lens) is NULL");
@@ -75,8 +75,11 @@ int check_gqa(const void* q, const void* k_pool, const void* v_pool, const pa_kv
     return fail(PA_ERR_UNSUPPORTED, "q heads per KV head must be 1, 2, 4, 8 (or 16 at head_dim 128)");
   if (!page_size_supported(kv->page_size))
     return fail(PA_ERR_UNSUPPORTED, "page_size must be 16, 32 or 64");
-  if (!mult8(kv->page_stride) || !mult8(kv->head_stride) || !mult8(kv->token_stride))
-    return fail(PA_ERR_ALIGN, "kv strides must be positive multiples of 8 elements");
+  const int64_t row_align = 16 / elem_bytes;   // elements per 16 bytes
+  auto mult = [&](int64_t v) { return v > 0 && v % row_align == 0; };
+  if (!mult(kv->page_stride) || !mult(kv->head_stride) || !mult(kv->token_stride))
+    return fail(PA_ERR_ALIGN, "kv strides must be positive multiples of " +
+                                  std::to_string(row_align) + " elements (16 bytes)");
   if (kv->token_stride < kv->head_dim)
     return fail(PA_ERR_SHAPE, "token_stride must be >= head_dim");
   if (static_cast<int64_t>(kv->page_size - 1) * kv->token_stride + kv->head_dim > INT32_MAX / 4)

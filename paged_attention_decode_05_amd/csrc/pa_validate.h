@@ -28,10 +28,12 @@ int32_t queries_padded(int32_t num_queries);
 int64_t max_keys(int32_t max_pages_per_seq, int32_t page_size, int32_t window);
 
 // Checks shared by pa_decode and pa_decode_splitkv.
+// elem_bytes: 2 for bf16 pools, 1 for FP8 (E4M3) pools; pool strides count
+// elements, and every K/V row must start on a 16-byte boundary.
 int check_gqa(const void* q, const void* k_pool, const void* v_pool, const pa_kv_layout* kv,
               const int32_t* block_table, int32_t block_table_stride,
               const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
-              int32_t max_pages_per_seq, float scale);
+              int32_t max_pages_per_seq, float scale, int32_t elem_bytes = 2);
 
 // Checks for explicit split parameters.
 int check_split(int32_t partition_size, int32_t max_partitions, int32_t max_pages_per_seq,

@@ -204,3 +204,19 @@ def test_multiquery_rejections_and_sizes():
     assert ws(8, 8, 2, 128, 32, 32, 0, 3) == ws(8, 8, 2, 128, 32, 32, 0, 4) > 0
     assert ws(8, 8, 2, 128, 32, 32, 0, 1) == pb.pa_decode_workspace_size(8, 8, 2, 128, 32, 32, 0)
     assert ws(8, 8, 2, 128, 32, 32, 0, 0) == 0
+
+
+def test_fp8_rejections():
+    f = pb.LIB.pa_decode_fp8
+    kv8 = _kv(page_stride=2 * 32 * 128, head_stride=32 * 128, token_stride=128)
+    def call(kv=kv8, ks=0.02, vs=0.03, scale=0.088):
+        return f(FAKE, FAKE, FAKE, C.byref(kv), FAKE, 32, FAKE, 8, 8, 32, scale, ks, vs, 0, FAKE,
+                 None, None, 0, None)
+    assert call(kv=_kv(token_stride=136, head_stride=32 * 136, page_stride=2 * 32 * 136)) == PA["ALIGN"]
+    assert call(ks=0.0) == PA["SHAPE"]
+    assert call(vs=float("nan")) == PA["SHAPE"]
+    assert call(ks=1e38, scale=1e3) == PA["SHAPE"]            # scale * k_scale overflows
+    assert call() == PA["WORKSPACE"]                          # valid up to the workspace
+    # bf16 pools need 8-element strides, FP8 pools 16-element ones
+    kv_b = _kv(token_stride=136, head_stride=32 * 136, page_stride=2 * 32 * 136)
+    assert _decode(kv=kv_b) == PA["WORKSPACE"]
