@@ -95,6 +95,11 @@ class Oracle:
                                                   C.c_int32, C.c_int32, C.c_double, C.c_double,
                                                   C.c_double, C.c_int32, f64p, f64p]
         self.lib.oracle_pa_decode_fp8.restype = C.c_int
+        f32p = C.POINTER(C.c_float)
+        self.lib.oracle_pa_decode_f32pool.argtypes = [u16p, f32p, f32p, pool, i32p, C.c_int32,
+                                                      i32p, C.c_int32, C.c_int32, C.c_double,
+                                                      C.c_int32, f64p, f64p]
+        self.lib.oracle_pa_decode_f32pool.restype = C.c_int
         self.lib.oracle_set_num_threads.argtypes = [C.c_int32]
         self.lib.oracle_max_threads.restype = C.c_int32
         self.lib.oracle_mutation.restype = C.c_int32
@@ -158,6 +163,25 @@ class Oracle:
             _ptr(ctx, i32), B, H, float(case.scale), float(case.k_scale), float(case.v_scale),
             int(w), _ptr(out, f64), _ptr(lse, f64))
         self._check(rc, "oracle_pa_decode_fp8")
+        return out, lse
+
+    def decode_f32pool(self, case, window: Optional[int] = None):
+        """(out [B,Hq,D], lse [B,Hq]) float64 for a GqaCase with f32 pools."""
+        assert case.kv_dtype == "f32"
+        B, H, D = case.batch, case.num_q_heads, case.head_dim
+        q = _bits(case.q)
+        k = np.ascontiguousarray(case.k_pool.cpu().contiguous().numpy(), dtype=np.float32)
+        v = np.ascontiguousarray(case.v_pool.cpu().contiguous().numpy(), dtype=np.float32)
+        bt, ctx = _i32(case.block_table), _i32(case.context_lens)
+        out = np.zeros((B, H, D), np.float64)
+        lse = np.zeros((B, H), np.float64)
+        pool = self._pool_of(case)
+        w = case.window if window is None else window
+        u16, f32, i32, f64 = C.c_uint16, C.c_float, C.c_int32, C.c_double
+        rc = self.lib.oracle_pa_decode_f32pool(
+            _ptr(q, u16), _ptr(k, f32), _ptr(v, f32), C.byref(pool), _ptr(bt, i32), bt.shape[1],
+            _ptr(ctx, i32), B, H, float(case.scale), int(w), _ptr(out, f64), _ptr(lse, f64))
+        self._check(rc, "oracle_pa_decode_f32pool")
         return out, lse
 
     def decode_multi(self, case, causal: bool = True, precision: str = "f64"):

@@ -18,6 +18,7 @@
  *  13 multi-query decode: causal limit one key too far
  *  14 FP8 decode: e4m3 exponent bias read as 8 instead of 7
  *  15 FP8 decode: the K and V scales swapped
+ *  16 f32 decode: V rows read one token after K's
  */
 #include <math.h>
 #include <stdlib.h>
@@ -239,6 +240,84 @@ int oracle_pa_decode_fp8(const uint16_t* q, const uint8_t* k_pool, const uint8_t
         const double e = exp(sc[i] - m);
         l += e;
         for (int32_t d = 0; d < D; ++d) o[d] += e * (oracle_e4m3_value(v[d]) * v_scale);
+      }
+      free(sc);
+      if (bad) {
+#pragma omp atomic write
+        err = ORACLE_ERR_PAGE;
+        continue;
+      }
+      if (cnt > 0)
+        for (int32_t d = 0; d < D; ++d) o[d] /= l;
+      lse[(int64_t)b * num_q_heads + h] = cnt > 0 ? m + log(l) : -INFINITY;
+    }
+  }
+  return err;
+}
+
+/* ---- f32 KV cache -----------------------------------------------------------
+ *
+ * Pools of IEEE binary32 elements, read as they are [vllm.cpp PR #425, the
+ * row loader's float instantiation next to the bf16 one; vllm.cpp kernel
+ * matrix, inventory row: the paged path admits F32/BF16].  float64
+ * arithmetic, the same two-pass softmax attention as oracle_pa_decode. */
+int oracle_pa_decode_f32pool(const uint16_t* q, const float* k_pool, const float* v_pool,
+                             const oracle_pool* pool, const int32_t* block_table,
+                             int32_t bt_stride, const int32_t* context_lens, int32_t batch,
+                             int32_t num_q_heads, double scale, int32_t window, double* out,
+                             double* lse) {
+  if (!q || !k_pool || !v_pool || !pool || !block_table || !context_lens || !out || !lse ||
+      batch < 0 || num_q_heads <= 0 || pool->num_pages <= 0 || pool->page_size <= 0 ||
+      pool->num_kv_heads <= 0 || pool->head_dim <= 0 || num_q_heads % pool->num_kv_heads)
+    return ORACLE_ERR_ARGS;
+  const int32_t D = pool->head_dim;
+  const int32_t G = num_q_heads / pool->num_kv_heads;
+  int err = ORACLE_OK;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+  for (int32_t b = 0; b < batch; ++b) {
+    for (int32_t h = 0; h < num_q_heads; ++h) {
+      const int32_t n = context_lens[b];
+      const int32_t lo = (window > 0 && n - window > 0) ? n - window : 0;
+      const int32_t g = h / G;
+      const uint16_t* qr = q + ((int64_t)b * num_q_heads + h) * D;
+      const int32_t* bt = block_table + (int64_t)b * bt_stride;
+      double* o = out + ((int64_t)b * num_q_heads + h) * D;
+      for (int32_t d = 0; d < D; ++d) o[d] = 0.0;
+      const int32_t cnt = n > lo ? n - lo : 0;
+      double* sc = (double*)malloc(sizeof(double) * (size_t)(cnt > 0 ? cnt : 1));
+      if (!sc) {
+#pragma omp atomic write
+        err = ORACLE_ERR_ARGS;
+        continue;
+      }
+      int bad = 0;
+      double m = -INFINITY;
+      for (int32_t i = 0; i < cnt; ++i) {                  /* pass 1: scores, max */
+        const int32_t t = lo + i;
+        const int32_t page = bt[t / pool->page_size];
+        if (page < 0 || page >= pool->num_pages) { bad = 1; break; }
+        const float* k = k_pool + (int64_t)page * pool->page_stride +
+                         (int64_t)g * pool->head_stride +
+                         (int64_t)(t % pool->page_size) * pool->token_stride;
+        double dot = 0.0;
+        for (int32_t d = 0; d < D; ++d) dot += (double)bf16_to_float(qr[d]) * (double)k[d];
+        sc[i] = scale * dot;
+        if (sc[i] > m) m = sc[i];
+      }
+      double l = 0.0;
+      for (int32_t i = 0; i < cnt && !bad; ++i) {          /* pass 2: sums */
+        const int32_t t = lo + i;
+        const int32_t page = bt[t / pool->page_size];
+#if ORACLE_MUTATION == 16
+        const int32_t slot = (t + 1) % pool->page_size; /* planted */
+#else
+        const int32_t slot = t % pool->page_size;
+#endif
+        const float* v = v_pool + (int64_t)page * pool->page_stride +
+                         (int64_t)g * pool->head_stride + (int64_t)slot * pool->token_stride;
+        const double e = exp(sc[i] - m);
+        l += e;
+        for (int32_t d = 0; d < D; ++d) o[d] += e * (double)v[d];
       }
       free(sc);
       if (bad) {

@@ -136,6 +136,14 @@ int oracle_pa_decode_fp8(const uint16_t* q, const uint8_t* k_pool, const uint8_t
                          double scale, double k_scale, double v_scale, int32_t window,
                          double* out, double* lse);
 
+/* f32 KV cache: as oracle_pa_decode_f64 over pools of binary32 elements
+ * (strides in elements). */
+int oracle_pa_decode_f32pool(const uint16_t* q, const float* k_pool, const float* v_pool,
+                             const oracle_pool* pool, const int32_t* block_table,
+                             int32_t bt_stride, const int32_t* context_lens, int32_t batch,
+                             int32_t num_q_heads, double scale, int32_t window, double* out,
+                             double* lse);
+
 /* Thread control for the (b, h) loop; results do not depend on it. */
 void oracle_set_num_threads(int32_t n);
 int32_t oracle_max_threads(void);

@@ -62,8 +62,8 @@ class GqaCase:
     partition_size: Optional[int] = None
     name: str = "custom"
     seed: int = 0
-    # "bf16" pools, or "fp8": one OCP E4M3 byte per element (uint8 tensors), the
-    # element's value being e4m3(byte) * k_scale (K) or * v_scale (V)
+    # "bf16" pools, "f32" pools, or "fp8": one OCP E4M3 byte per element (uint8
+    # tensors), the element's value being e4m3(byte) * k_scale (K) or * v_scale (V)
     kv_dtype: str = "bf16"
     k_scale: float = 1.0
     v_scale: float = 1.0
@@ -74,7 +74,7 @@ class GqaCase:
 
     @property
     def kv_elem_bytes(self) -> int:
-        return 1 if self.kv_dtype == "fp8" else 2
+        return {"fp8": 1, "bf16": 2, "f32": 4}[self.kv_dtype]
 
     @property
     def num_q_heads(self) -> int:
@@ -252,7 +252,8 @@ def make_gqa_case(*, context_lens: Sequence[int], num_q_heads: int, num_kv_heads
     last S positions of each context), for multi-query decode; the NaN
     canaries then spare the S - 1 keys the earlier queries' windows reach
     further back.  ``kv_dtype="fp8"`` draws E4M3 pools whose values times
-    k_scale / v_scale are N(0, 1) samples rounded to E4M3 precision."""
+    k_scale / v_scale are N(0, 1) samples rounded to E4M3 precision;
+    ``kv_dtype="f32"`` draws float32 N(0, 1) pools (full float32 mantissas)."""
     if layout not in LAYOUTS:
         raise ValueError(layout)
     gen = torch.Generator().manual_seed(int(seed))
@@ -278,6 +279,9 @@ def make_gqa_case(*, context_lens: Sequence[int], num_q_heads: int, num_kv_heads
     elif kv_dtype == "bf16":
         k_pool = _normal_bf16(gen, shape)
         v_pool = _normal_bf16(gen, shape)
+    elif kv_dtype == "f32":
+        k_pool = torch.randn(*shape, generator=gen, dtype=torch.float32)
+        v_pool = torch.randn(*shape, generator=gen, dtype=torch.float32)
     else:
         raise ValueError(kv_dtype)
     if poison:

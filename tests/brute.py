@@ -40,6 +40,9 @@ def dense_attention(case, window=None):
     if getattr(case, "kv_dtype", "bf16") == "fp8":
         K = fp8_pool_f64(case.k_pool, case.k_scale)
         V = fp8_pool_f64(case.v_pool, case.v_scale)
+    elif getattr(case, "kv_dtype", "bf16") == "f32":
+        K = case.k_pool.detach().cpu().to(torch.float64).numpy()
+        V = case.v_pool.detach().cpu().to(torch.float64).numpy()
     else:
         K = pool_f64(case.k_pool)
         V = pool_f64(case.v_pool)

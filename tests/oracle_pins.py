@@ -34,6 +34,10 @@ builds with a planted mistake (at least one must fail).
                        the exactly dequantised pools, bit for bit
   fp8_bruteforce       FP8 decode == float64 dense attention over K/V decoded
                        by torch and scaled (scales not powers of two)
+  f32pool_equals_bf16  f32 pools holding bf16 values == the bf16 oracle, bit
+                       for bit
+  f32pool_bruteforce   f32-pool decode == float64 dense attention (full float32
+                       mantissas, windows, both layouts)
 """
 from __future__ import annotations
 
@@ -476,6 +480,38 @@ def fp8_bruteforce(o):
         assert np.abs(lse[fin] - ref_lse[fin]).max() < F64_TOL
 
 
+def _f32_case(seed, **kw):
+    base = dict(context_lens=(0, 1, 5, 37, 100), num_q_heads=4, num_kv_heads=2, head_dim=16,
+                page_size=8, window=0)
+    base.update(kw)
+    return make_gqa_case(seed=seed, kv_dtype="f32", **base)
+
+
+def f32pool_equals_bf16(o):
+    for layout, window in (("PHSD", 0), ("PSHD", 30)):
+        c16 = make_gqa_case(context_lens=(0, 1, 5, 37, 100), num_q_heads=4, num_kv_heads=2,
+                            head_dim=16, page_size=8, seed=7160, layout=layout, window=window)
+        c32 = c16.to("cpu")
+        c32.kv_dtype = "f32"
+        c32.k_pool = c16.k_pool.to(torch.float32)
+        c32.v_pool = c16.v_pool.to(torch.float32)
+        out32, lse32 = o.decode_f32pool(c32)
+        out16, lse16 = o.decode(c16, "f64")
+        assert np.array_equal(out32, out16) and np.array_equal(lse32, lse16), (layout, window)
+
+
+def f32pool_bruteforce(o):
+    for i, (layout, window) in enumerate((("PHSD", 0), ("PSHD", 0), ("PHSD", 40))):
+        c = _f32_case(7170 + i, layout=layout, window=window, poison=False)
+        ref, ref_lse = dense_attention(c)
+        cp = _f32_case(7170 + i, layout=layout, window=window)
+        out, lse = o.decode_f32pool(cp)
+        assert np.abs(out - ref).max() < F64_TOL, np.abs(out - ref).max()
+        fin = np.isfinite(ref_lse)
+        assert np.array_equal(fin, np.isfinite(lse))
+        assert np.abs(lse[fin] - ref_lse[fin]).max() < F64_TOL
+
+
 PINS = {
     "dense_bruteforce": dense_bruteforce,
     "single_token": single_token,
@@ -497,6 +533,8 @@ PINS = {
     "e4m3_decode": e4m3_decode,
     "fp8_equals_bf16": fp8_equals_bf16,
     "fp8_bruteforce": fp8_bruteforce,
+    "f32pool_equals_bf16": f32pool_equals_bf16,
+    "f32pool_bruteforce": f32pool_bruteforce,
 }
 
 

@@ -29,6 +29,7 @@ MUTATIONS = {
     13: "multi-query causal limit one key too far",
     14: "E4M3 exponent bias 8",
     15: "FP8 K and V scales swapped",
+    16: "f32-pool V rows one token late",
 }
 
 
