@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama",
                     choices=["tiny", "llama", "d256w", "long", "mla", "verify", "insert",
-                             "llama_fp8"])
+                             "llama_fp8", "llama_f32"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run K device-to-device copies of a 1 GiB buffer instead (reference "
@@ -98,7 +98,7 @@ def main() -> int:
     log(f"generating workload {a.workload} (seeded) ...")
     t0 = time.time()
     cases = [wl.NAMED[a.workload](poison=False, seed=wl.SEED_BASE + 100 * i + {
-        "tiny": 1, "llama": 2, "d256w": 3, "long": 4, "llama_fp8": 5}[a.workload])
+        "tiny": 1, "llama": 2, "d256w": 3, "long": 4, "llama_fp8": 5, "llama_f32": 6}[a.workload])
         for i in range(a.rotate)]
     dcs = [c.to(dev) for c in cases]
     log(f"  {time.time() - t0:.1f}s; pool pages {cases[0].num_pages}, "
@@ -113,10 +113,14 @@ def main() -> int:
     kvl = [pb.kv_layout(d.k_pool, d.layout) for d in dcs]
 
     fp8 = c0.kv_dtype == "fp8"
+    f32 = c0.kv_dtype == "f32"
 
     def step(i):
         d = dcs[i % len(dcs)]
-        if fp8:
+        if f32:
+            pb.pa_decode_f32(d.q, d.k_pool, d.v_pool, kvl[i % len(dcs)], d.block_table,
+                             d.context_lens, d.scale, d.window, out, None, ws)
+        elif fp8:
             pb.pa_decode_fp8(d.q, d.k_pool, d.v_pool, kvl[i % len(dcs)], d.block_table,
                              d.context_lens, d.scale, d.k_scale, d.v_scale, d.window, out, None, ws)
         else:
@@ -174,7 +178,7 @@ def main() -> int:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "storage_dtype": "e4m3 (one scale per pool)" if fp8 else "bf16",
+        "storage_dtype": "e4m3 (one scale per pool)" if fp8 else ("f32" if f32 else "bf16"),
         "data": "synthetic",
         "config": {
             "workload": {"llama": "llama3-8b-shaped decode, bs64, 32q/8kv heads, d128, page 32, "
@@ -183,6 +187,8 @@ def main() -> int:
                          "d256w": "d256 GQA-8 sliding window 4096, bs32",
                          "long": "long context bs4, ctx 32K-128K, d128",
                          "llama_fp8": "llama3-8b-shaped decode over an FP8 (E4M3) KV cache, bs64, "
+                                      "32q/8kv heads, d128, page 32, ctx U[512,8192]",
+                         "llama_f32": "llama3-8b-shaped decode over an f32 KV cache, bs64, "
                                       "32q/8kv heads, d128, page 32, ctx U[512,8192]"}[a.workload],
             "batch": B, "num_q_heads": H, "num_kv_heads": Hkv, "head_dim": D,
             "page_size": c0.page_size, "window": c0.window,
@@ -202,7 +208,7 @@ def main() -> int:
             "traffic": (recorded_traffic({"llama": "pa_decode_llama_bs64",
                                           "llama_fp8": "pa_decode_fp8_llama_bs64"}[a.workload])
                         if a.workload in ("llama", "llama_fp8") and a.rotate == 1 else None),
-            "kernel": ("pa_decode_fp8" if fp8 else "pa_decode") +
+            "kernel": ("pa_decode_fp8" if fp8 else "pa_decode_f32" if f32 else "pa_decode") +
                       " call: balanced_split_kernel + balanced_merge_kernel",
             "algorithmic_bytes_per_launch": int(mean_bytes),
         },
@@ -430,6 +436,8 @@ def cpu_baseline(case):
         t = time.time()
         if case.kv_dtype == "fp8":
             o.decode_fp8(case)
+        elif case.kv_dtype == "f32":
+            o.decode_f32pool(case)
         else:
             o.decode(case, "f64")
         times.append(time.time() - t)

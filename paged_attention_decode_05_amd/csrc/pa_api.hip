@@ -17,9 +17,10 @@ namespace pa {
 hipError_t launch_split(const SplitParams& p, int head_dim, int group, int batch,
                         int num_kv_heads, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, int head_dim, int batch, hipStream_t stream);
+// kv: pool element type, 0 bf16, 1 FP8 (E4M3), 2 f32
 hipError_t launch_balanced(const SplitParams& sp, const BalancedLayout& bl, int head_dim, int group,
-                           int grid, hipStream_t stream, bool fp8);
-int balanced_grid(int head_dim, int group, int num_cus, int max_blocks, bool fp8);
+                           int grid, hipStream_t stream, int kv);
+int balanced_grid(int head_dim, int group, int num_cus, int max_blocks, int kv);
 
 }  // namespace pa
 
@@ -162,17 +163,22 @@ int32_t pa_decode_partition_size(int32_t batch, int32_t num_q_heads, int32_t num
 namespace {
 
 // pa_decode with S query tokens per sequence (S = 1: plain decode).
-// fp8: K/V pools of OCP E4M3 bytes, values e4m3 * k_scale / v_scale.
+// kv_type: 0 bf16 pools; 1 FP8, OCP E4M3 bytes with values e4m3 * k_scale /
+// v_scale; 2 f32 pools.
 int decode_impl(const void* q, const void* k_pool, const void* v_pool, const pa_kv_layout* kv,
                 const int32_t* block_table, int32_t block_table_stride,
                 const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
                 int32_t num_queries, int32_t causal, int32_t max_pages_per_seq, float scale,
                 int32_t window, void* out, float* lse_out, void* workspace,
-                size_t workspace_bytes, void* stream, bool fp8 = false, float k_scale = 1.0f,
+                size_t workspace_bytes, void* stream, int kv_type = 0, float k_scale = 1.0f,
                 float v_scale = 1.0f) {
+  const bool fp8 = kv_type == 1;
+  const int elem_bytes = kv_type == 1 ? 1 : kv_type == 2 ? 4 : 2;
   int rc = pa::check_gqa(q, k_pool, v_pool, kv, block_table, block_table_stride, context_lens,
-                         batch, num_q_heads, max_pages_per_seq, scale, fp8 ? 1 : 2);
+                         batch, num_q_heads, max_pages_per_seq, scale, elem_bytes);
   if (rc) return rc;
+  if (kv_type == 2 && kv->head_dim > 128)
+    return pa::fail(PA_ERR_UNSUPPORTED, "f32 pools take head_dim 64 or 128");
   if (fp8 && !(std::isfinite(k_scale) && k_scale > 0.0f && std::isfinite(v_scale) &&
                v_scale > 0.0f))
     return pa::fail(PA_ERR_SHAPE, "k_scale and v_scale must be finite and > 0");
@@ -197,7 +203,7 @@ int decode_impl(const void* q, const void* k_pool, const void* v_pool, const pa_
   char* ws = static_cast<char*>(workspace);
   const int vgroup = qpad * group;
   const int nbmax =
-      pa::balanced_grid(kv->head_dim, vgroup, device_cus(), pa::kMaxBalancedBlocks, fp8);
+      pa::balanced_grid(kv->head_dim, vgroup, device_cus(), pa::kMaxBalancedBlocks, kv_type);
   if (nbmax < 1) return pa::fail(PA_ERR_UNSUPPORTED, "no balanced-split kernel for these shapes");
 
   pa::BalancedLayout bl{};
@@ -217,7 +223,7 @@ int decode_impl(const void* q, const void* k_pool, const void* v_pool, const pa_
 
   pa::SplitParams sp = split_params(q, k_pool, v_pool, kv, block_table, block_table_stride,
                                     context_lens, num_q_heads, fp8 ? scale * k_scale : scale,
-                                    window, 1, 1, nullptr, nullptr, nullptr, 0, fp8 ? 1 : 2);
+                                    window, 1, 1, nullptr, nullptr, nullptr, 0, elem_bytes);
   if (fp8) sp.out_scale = v_scale;
   sp.num_q_heads = num_q_heads * num_queries;   // rows of q and out per sequence
   sp.num_queries = num_queries;
@@ -225,7 +231,7 @@ int decode_impl(const void* q, const void* k_pool, const void* v_pool, const pa_
   sp.reach = (window > 0 && causal) ? window + num_queries - 1 : window;
   pa::clear_error();
   return launch_status(pa::launch_balanced(sp, bl, kv->head_dim, vgroup, nbmax,
-                                           static_cast<hipStream_t>(stream), fp8),
+                                           static_cast<hipStream_t>(stream), kv_type),
                        "balanced decode");
 }
 
@@ -264,7 +270,17 @@ int pa_decode_fp8(const void* q, const void* k_pool, const void* v_pool, const p
                   size_t workspace_bytes, void* stream) {
   return decode_impl(q, k_pool, v_pool, kv, block_table, block_table_stride, context_lens, batch,
                      num_q_heads, 1, 1, max_pages_per_seq, scale, window, out, lse_out,
-                     workspace, workspace_bytes, stream, true, k_scale, v_scale);
+                     workspace, workspace_bytes, stream, 1, k_scale, v_scale);
+}
+
+int pa_decode_f32(const void* q, const void* k_pool, const void* v_pool, const pa_kv_layout* kv,
+                  const int32_t* block_table, int32_t block_table_stride,
+                  const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                  int32_t max_pages_per_seq, float scale, int32_t window, void* out,
+                  float* lse_out, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(q, k_pool, v_pool, kv, block_table, block_table_stride, context_lens, batch,
+                     num_q_heads, 1, 1, max_pages_per_seq, scale, window, out, lse_out,
+                     workspace, workspace_bytes, stream, 2);
 }
 
 size_t pa_decode_multiquery_workspace_size(int32_t batch, int32_t num_q_heads,

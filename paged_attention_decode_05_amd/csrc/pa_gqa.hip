@@ -539,6 +539,12 @@ __device__ __forceinline__ void attend_range_valu(const SplitParams& p, int b, i
 // are issued as soon as chunk k's registers are free: K after the scores, V
 // after its LDS write.
 //
+// f32 pools (F32): every K or V element splits exactly into three bf16 terms
+// hi + mid + lo (as P does), so the scores take three MFMAs per step and P.V
+// nine (P's three terms times V's three), all with exact products and fp32
+// sums; V goes through three bf16 LDS tiles, one per term.  A step's 8 dims
+// are two 16-byte loads (dims 32ks + 8g .. +4 and +4 .. +8).
+//
 // FP8 pools (F8): K and V hold one OCP E4M3 byte per element.  They are
 // converted to bf16 in registers (exact: every E4M3 value is a bf16 value);
 // the per-pool scales are folded into the softmax scale (K) and the output
@@ -547,8 +553,13 @@ __device__ __forceinline__ void attend_range_valu(const SplitParams& p, int b, i
 // last 8 for step 2j+1, and q is loaded with the same dims order (the
 // contraction over dims does not depend on it).  V rows are converted on
 // their way into the LDS tile, which stays bf16.
-template <int D, int G, bool F8 = false>
+// Element type of the K/V pools.
+enum : int { kKvBf16 = 0, kKvFp8 = 1, kKvF32 = 2 };
+
+template <int D, int G, int KV = kKvBf16>
 struct MfmaGeo {
+  static constexpr bool F8 = KV == kKvFp8;
+  static constexpr bool F32 = KV == kKvF32;
   // A wave's chunk is SUB tiles of 16 keys (a tile never spans two pages);
   // their loads are issued together and one softmax update covers them.
   // Measured on the bs64 decode: two tiles per chunk made the FP8 call slower
@@ -557,7 +568,7 @@ struct MfmaGeo {
   static constexpr int KC = 16 * SUB;    // keys per chunk
   static constexpr int KS = D / 32;      // score k-steps
   static constexpr int NT = D / 16;      // P.V output tiles
-  static constexpr int EB = F8 ? 1 : 2;  // bytes per pool element
+  static constexpr int EB = F8 ? 1 : F32 ? 4 : 2;   // bytes per pool element
   static constexpr int NK = KS * EB / 2; // 16-byte K loads per lane and 16-key tile
   static constexpr int LV = D * EB / 16; // lanes per V row in the load layout (16 B each)
   static constexpr int TV = 64 / LV;     // V rows per load
@@ -579,15 +590,19 @@ __device__ __forceinline__ void fp8x16_bf16(uint4 x, uint4& lo, uint4& hi) {
                   fp8x2_bf16(x.w, true));
 }
 
-template <int D, int G, int NW, bool F8>
+template <int D, int G, int NW, int KV>
 __device__ __forceinline__ void attend_range_mfma(const SplitParams& p, int b, int gk, int begin,
                                                   int end, float* out, float* mx, float* sm,
                                                   int64_t hstride, uint16_t* final_out,
                                                   float* final_lse) {
-  using mg = MfmaGeo<D, G, F8>;
+  using mg = MfmaGeo<D, G, KV>;
+  constexpr bool F8 = mg::F8;
+  constexpr bool F32 = mg::F32;
   constexpr int KC = mg::KC;
   constexpr int SUB = mg::SUB;
-  constexpr int kTileBytes = NW * KC * mg::VPAD * 2;
+  constexpr int kVTerms = F32 ? 3 : 1;    // bf16 V tiles per wave (hi, mid, lo for f32)
+  constexpr int kVTileBytes = KC * mg::VPAD * 2;
+  constexpr int kTileBytes = NW * kVTerms * kVTileBytes;
   constexpr int kRedBytes = NW * G * D * 4;
   // the V tiles of the loop and the wave states of the epilogue share one buffer
   __shared__ __align__(16) char lds[kTileBytes > kRedBytes ? kTileBytes : kRedBytes];
@@ -599,7 +614,8 @@ __device__ __forceinline__ void attend_range_mfma(const SplitParams& p, int b, i
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;
   const int c16 = lane & 15;
-  uint16_t (*vt)[mg::VPAD] = reinterpret_cast<uint16_t (*)[mg::VPAD]>(lds + wave * KC * mg::VPAD * 2);
+  uint16_t (*vt)[mg::VPAD] =
+      reinterpret_cast<uint16_t (*)[mg::VPAD]>(lds + wave * kVTerms * kVTileBytes);
 
   WaveKeys wk;
   wk.bt = p.block_table + static_cast<int64_t>(b) * p.bt_stride;
@@ -650,7 +666,9 @@ __device__ __forceinline__ void attend_range_mfma(const SplitParams& p, int b, i
   // straight into the A-operand layout.  (Loading whole rows to LDS instead,
   // with direct global->LDS loads, and reading the operand back measured
   // slower on the bs64 decode: 198 against 193 us.)
-  const int koff = c16 * p.token_bytes + 16 * g;
+  const int koff = c16 * p.token_bytes + (F32 ? 32 : 16) * g;
+  // byte offset of K load i within the lane's row share
+  auto kload_off = [](int i) { return F32 ? 128 * (i >> 1) + 16 * (i & 1) : 64 * i; };
   const int voff0 = (lane / mg::LV) * p.token_bytes + 16 * (lane % mg::LV);
   uint4 kr[SUB][mg::NK], vr[SUB][mg::NV];
   auto issue_k = [&](int k) {
@@ -662,7 +680,7 @@ __device__ __forceinline__ void attend_range_mfma(const SplitParams& p, int b, i
       const int soff = (tu & (p.page_size - 1)) * p.token_bytes;
       const int voff = koff | dead_bit(tu + c16, wk.begin, wk.end);
 #pragma unroll
-      for (int i = 0; i < mg::NK; ++i) kr[u][i] = tile_load(rs, voff + 64 * i, soff);
+      for (int i = 0; i < mg::NK; ++i) kr[u][i] = tile_load(rs, voff + kload_off(i), soff);
     }
   };
   auto issue_v = [&](int k) {
@@ -700,6 +718,19 @@ __device__ __forceinline__ void attend_range_mfma(const SplitParams& p, int b, i
           fp8x16_bf16(kv[i], a0, a1);
           sc[u] = mfma(a0, qb[2 * i], sc[u]);
           sc[u] = mfma(a1, qb[2 * i + 1], sc[u]);
+        }
+      } else if constexpr (F32) {
+#pragma unroll
+        for (int ks = 0; ks < mg::KS; ++ks) {
+          const uint4 x0 = kv[2 * ks], x1 = kv[2 * ks + 1];
+          uint4 h, m, l;
+          split3_bf16x2(u2f(x0.x), u2f(x0.y), h.x, m.x, l.x);
+          split3_bf16x2(u2f(x0.z), u2f(x0.w), h.y, m.y, l.y);
+          split3_bf16x2(u2f(x1.x), u2f(x1.y), h.z, m.z, l.z);
+          split3_bf16x2(u2f(x1.z), u2f(x1.w), h.w, m.w, l.w);
+          sc[u] = mfma(l, qb[ks], sc[u]);
+          sc[u] = mfma(m, qb[ks], sc[u]);
+          sc[u] = mfma(h, qb[ks], sc[u]);
         }
       } else {
 #pragma unroll
@@ -774,7 +805,18 @@ __device__ __forceinline__ void attend_range_mfma(const SplitParams& p, int b, i
         // 16-byte units of the row: a lane's VD dims are units m * VD / 8 ..
         uint4* row = reinterpret_cast<uint4*>(&vt[16 * u + mg::TV * j + lane / mg::LV][0]);
         const int m = lane % mg::LV;
-        if constexpr (F8) {
+        if constexpr (F32) {
+          // 4 dims of one key, as three bf16 terms into the three tiles
+          const uint4 x = vr[u][j];
+          uint2 h, mm, l;
+          split3_bf16x2(u2f(x.x), u2f(x.y), h.x, mm.x, l.x);
+          split3_bf16x2(u2f(x.z), u2f(x.w), h.y, mm.y, l.y);
+          const int r = 16 * u + mg::TV * j + lane / mg::LV;
+          char* base = lds + wave * kVTerms * kVTileBytes + r * mg::VPAD * 2 + 8 * m;
+          *reinterpret_cast<uint2*>(base) = h;
+          *reinterpret_cast<uint2*>(base + kVTileBytes) = mm;
+          *reinterpret_cast<uint2*>(base + 2 * kVTileBytes) = l;
+        } else if constexpr (F8) {
           // the two 16-byte halves are written in an order that puts the 16
           // lanes of one write pass on 16 different 4-bank groups
           uint4 lo, hi;
@@ -796,7 +838,28 @@ __device__ __forceinline__ void attend_range_mfma(const SplitParams& p, int b, i
     // P.V in groups of 8 output tiles: the group's transposed reads first, then
     // its MFMAs term-major, so no MFMA waits on the one before it and the
     // reads' latency is paid once per group
-    constexpr int kGroupTiles = mg::NT < 8 ? mg::NT : 8;
+    constexpr int kGroupTiles = F32 ? (mg::NT < 4 ? mg::NT : 4) : (mg::NT < 8 ? mg::NT : 8);
+    if constexpr (F32) {
+      // P's three terms times V's three: nine exact-product MFMAs per tile
+#pragma unroll
+      for (int n0 = 0; n0 < mg::NT; n0 += kGroupTiles) {
+        uint2 bv[3][kGroupTiles];
+#pragma unroll
+        for (int t = 0; t < 3; ++t)
+#pragma unroll
+          for (int n = 0; n < kGroupTiles; ++n)
+            bv[t][n] = lds_read_tr(brow + t * (kVTileBytes / 2) + 16 * (n0 + n));
+#pragma unroll
+        for (int t = 2; t >= 0; --t) {
+#pragma unroll
+          for (int n = 0; n < kGroupTiles; ++n) acc[n0 + n] = mfma16(pa_lo[0], bv[t][n], acc[n0 + n]);
+#pragma unroll
+          for (int n = 0; n < kGroupTiles; ++n) acc[n0 + n] = mfma16(pa_mid[0], bv[t][n], acc[n0 + n]);
+#pragma unroll
+          for (int n = 0; n < kGroupTiles; ++n) acc[n0 + n] = mfma16(pa_hi[0], bv[t][n], acc[n0 + n]);
+        }
+      }
+    } else
 #pragma unroll
     for (int u = 0; u < SUB; ++u)
 #pragma unroll
@@ -841,22 +904,25 @@ __device__ __forceinline__ void attend_range_mfma(const SplitParams& p, int b, i
 }
 
 // Groups of 4 to 16 heads run on the matrix cores, 1 and 2 on the vector
-// ALUs (measured on the bs64 GQA-4 decode: 199 us on MFMA against 206 us).
+// ALUs (measured on the bs64 GQA-4 decode: 199 us on MFMA against 206 us);
+// head_dim 64 always takes the matrix cores.
 template <int D, int G>
-constexpr bool kUseMfma = G >= 4;
+constexpr bool kUseMfma = G >= 4 || D == 64;
 
 // Waves per SIMD the compiler must fit the range kernels' registers into.
-template <int D, int G, bool F8 = false>
-constexpr int kMinWaves = (F8 || kUseMfma<D, G>) ? (D == 128 ? 3 : 2) : 1;
+template <int D, int G, int KV = kKvBf16>
+constexpr int kMinWaves = KV == kKvF32 ? (D == 64 ? 3 : 2)
+                          : (KV != kKvBf16 || kUseMfma<D, G>) ? (D == 64 ? 4 : D == 128 ? 3 : 2)
+                                                              : 1;
 
-// FP8 pools always take the matrix-core routine.
-template <int D, int G, int NW, bool F8 = false>
+// FP8 and f32 pools always take the matrix-core routine.
+template <int D, int G, int NW, int KV = kKvBf16>
 __device__ __forceinline__ void attend_range(const SplitParams& p, int b, int gk, int begin,
                                              int end, float* out, float* mx, float* sm,
                                              int64_t hstride, uint16_t* final_out = nullptr,
                                              float* final_lse = nullptr) {
-  if constexpr (F8 || kUseMfma<D, G>)
-    attend_range_mfma<D, G, NW, F8>(p, b, gk, begin, end, out, mx, sm, hstride, final_out,
+  if constexpr (KV != kKvBf16 || kUseMfma<D, G>)
+    attend_range_mfma<D, G, NW, KV>(p, b, gk, begin, end, out, mx, sm, hstride, final_out,
                                     final_lse);
   else
     attend_range_valu<D, G, NW>(p, b, gk, begin, end, out, mx, sm, hstride, final_out, final_lse);
@@ -950,8 +1016,8 @@ __device__ __forceinline__ void locate_unit(const int32_t* ctx, int batch, int w
 }
 
 
-template <int D, int G, bool F8>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kMinWaves<D, G, F8>)))
+template <int D, int G, int KV>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kMinWaves<D, G, KV>)))
 void balanced_split_kernel(const SplitParams p, const BalancedLayout bl) {
   __shared__ int64_t sh_total;
   __shared__ int64_t sh_pre;
@@ -1012,7 +1078,7 @@ void balanced_split_kernel(const SplitParams p, const BalancedLayout bl) {
       const int64_t r = static_cast<int64_t>(b) * hkv + gk;
       const int64_t slot = r + i;
       const int64_t h0 = static_cast<int64_t>(b) * p.num_q_heads + static_cast<int64_t>(gk) * gq;
-      attend_range<D, G, kWaves, F8>(p, b, gk, begin, end, bl.seg_out + slot * G * D,
+      attend_range<D, G, kWaves, KV>(p, b, gk, begin, end, bl.seg_out + slot * G * D,
                                  bl.seg_max + slot * G, bl.seg_sum + slot * G, 1,
                                  whole ? bl.out + h0 * D : nullptr,
                                  (whole && bl.lse) ? bl.lse + h0 : nullptr);
@@ -1206,10 +1272,10 @@ static hipError_t launch_split_dg(const SplitParams& p, int batch, int num_kv_he
   return hipGetLastError();
 }
 
-template <int D, int G, bool F8>
+template <int D, int G, int KV>
 static hipError_t launch_balanced_dg(const SplitParams& p, const BalancedLayout& bl, int grid,
                                      hipStream_t stream) {
-  hipLaunchKernelGGL((balanced_split_kernel<D, G, F8>), dim3(grid), dim3(kBlock), 0, stream, p, bl);
+  hipLaunchKernelGGL((balanced_split_kernel<D, G, KV>), dim3(grid), dim3(kBlock), 0, stream, p, bl);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((balanced_merge_kernel<D, G>), dim3(bl.rows, (G * D / 4 + kBlock - 1) / kBlock),
@@ -1217,12 +1283,12 @@ static hipError_t launch_balanced_dg(const SplitParams& p, const BalancedLayout&
   return hipGetLastError();
 }
 
-template <int D, int G, bool F8>
+template <int D, int G, int KV>
 static int blocks_per_cu() {
   static int cached = -1;
   if (cached < 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, balanced_split_kernel<D, G, F8>, kBlock, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, balanced_split_kernel<D, G, KV>, kBlock, 0) !=
             hipSuccess || n < 1)
       n = 1;
     cached = n;
@@ -1239,7 +1305,7 @@ static hipError_t launch_split_d(const SplitParams& p, int group, int batch, int
     case 4: return launch_split_dg<D, 4>(p, batch, num_kv_heads, stream);
     case 8: return launch_split_dg<D, 8>(p, batch, num_kv_heads, stream);
     case 16:
-      if constexpr (D == 128) return launch_split_dg<D, 16>(p, batch, num_kv_heads, stream);
+      if constexpr (D <= 128) return launch_split_dg<D, 16>(p, batch, num_kv_heads, stream);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
@@ -1247,6 +1313,7 @@ static hipError_t launch_split_d(const SplitParams& p, int group, int batch, int
 
 hipError_t launch_split(const SplitParams& p, int head_dim, int group, int batch,
                         int num_kv_heads, hipStream_t stream) {
+  if (head_dim == 64) return launch_split_d<64>(p, group, batch, num_kv_heads, stream);
   if (head_dim == 128) return launch_split_d<128>(p, group, batch, num_kv_heads, stream);
   if (head_dim == 256) return launch_split_d<256>(p, group, batch, num_kv_heads, stream);
   return hipErrorInvalidValue;
@@ -1254,7 +1321,9 @@ hipError_t launch_split(const SplitParams& p, int head_dim, int group, int batch
 
 hipError_t launch_merge(const MergeParams& p, int head_dim, int batch, hipStream_t stream) {
   dim3 grid(p.num_q_heads, batch);
-  if (head_dim == 128) {
+  if (head_dim == 64) {
+    hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(kBlock), 0, stream, p);
+  } else if (head_dim == 128) {
     hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(kBlock), 0, stream, p);
   } else if (head_dim == 256) {
     hipLaunchKernelGGL(merge_kernel<256>, grid, dim3(kBlock), 0, stream, p);
@@ -1264,19 +1333,26 @@ hipError_t launch_merge(const MergeParams& p, int head_dim, int batch, hipStream
   return hipGetLastError();
 }
 
-template <int D, int G, bool F8>
+template <int D, int G, int KV>
 static int balanced_blocks(int num_cus, int max_blocks) {
-  const int n = blocks_per_cu<D, G, F8>() * num_cus;
+  const int n = blocks_per_cu<D, G, KV>() * num_cus;
   return n < max_blocks ? n : max_blocks;
 }
 
-// Calls f.template operator()<D, G, F8>() for a supported (head_dim, group,
-// fp8) triple; returns `none` otherwise.
+// Calls f.template operator()<D, G, KV>() for a supported (head_dim, group,
+// pool element type) triple; returns `none` otherwise.  f32 pools stop at
+// head_dim 128 (their K and V registers would not fit two waves per SIMD at 256).
 template <typename R, typename F>
-static R dispatch_dg(int head_dim, int group, bool fp8, R none, F&& f) {
+static R dispatch_dg(int head_dim, int group, int kv, R none, F&& f) {
 #define PA_CASE(DD, GG)                                                                \
-  if (head_dim == DD && group == GG)                                                   \
-    return fp8 ? f.template operator()<DD, GG, true>() : f.template operator()<DD, GG, false>();
+  if (head_dim == DD && group == GG) {                                                 \
+    if (kv == kKvBf16) return f.template operator()<DD, GG, kKvBf16>();                \
+    if (kv == kKvFp8) return f.template operator()<DD, GG, kKvFp8>();                  \
+    if constexpr (DD <= 128)                                                           \
+      if (kv == kKvF32) return f.template operator()<DD, GG, kKvF32>();                \
+    return none;                                                                       \
+  }
+  PA_CASE(64, 1) PA_CASE(64, 2) PA_CASE(64, 4) PA_CASE(64, 8) PA_CASE(64, 16)
   PA_CASE(128, 1) PA_CASE(128, 2) PA_CASE(128, 4) PA_CASE(128, 8) PA_CASE(128, 16)
   PA_CASE(256, 1) PA_CASE(256, 2) PA_CASE(256, 4) PA_CASE(256, 8)
 #undef PA_CASE
@@ -1284,19 +1360,19 @@ static R dispatch_dg(int head_dim, int group, bool fp8, R none, F&& f) {
 }
 
 // Blocks the balanced split would use on this device (occupancy x CUs, capped).
-int balanced_grid(int head_dim, int group, int num_cus, int max_blocks, bool fp8) {
-  return dispatch_dg<int>(head_dim, group, fp8, 0, [&]<int D, int G, bool F8>() {
-    return balanced_blocks<D, G, F8>(num_cus, max_blocks);
+int balanced_grid(int head_dim, int group, int num_cus, int max_blocks, int kv) {
+  return dispatch_dg<int>(head_dim, group, kv, 0, [&]<int D, int G, int KV>() {
+    return balanced_blocks<D, G, KV>(num_cus, max_blocks);
   });
 }
 
 // Balanced split, then the merge of the rows several blocks shared: the whole
-// of pa_decode (bf16 or FP8 pools).
+// of pa_decode (bf16, FP8 or f32 pools).
 hipError_t launch_balanced(const SplitParams& sp, const BalancedLayout& bl, int head_dim, int group,
-                           int grid, hipStream_t stream, bool fp8) {
-  return dispatch_dg<hipError_t>(head_dim, group, fp8, hipErrorInvalidValue,
-                                 [&]<int D, int G, bool F8>() {
-                                   return launch_balanced_dg<D, G, F8>(sp, bl, grid, stream);
+                           int grid, hipStream_t stream, int kv) {
+  return dispatch_dg<hipError_t>(head_dim, group, kv, hipErrorInvalidValue,
+                                 [&]<int D, int G, int KV>() {
+                                   return launch_balanced_dg<D, G, KV>(sp, bl, grid, stream);
                                  });
 }
 

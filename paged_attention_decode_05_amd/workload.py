@@ -24,6 +24,7 @@ unless stated, pool = ceil(1.1 * pages in use) unless stated):
          ctx {32768, 65536, 100000, 131072}, 512-token partitions
   llama_fp8  the llama shape with OCP E4M3 K/V pools, k_scale 0.0173,
          v_scale 0.0291 (values N(0, 1) rounded to E4M3 precision)
+  llama_f32  the llama shape with float32 K/V pools
   mla    16 seqs, 128 heads, q_nope 128 + q_rope 64, 576-wide latent rows in
          64-token pages, ctx ~ U{1024..8192}, W_UK/W_UV ~ N(0, 0.02^2),
          scale 1/sqrt(192)
@@ -362,6 +363,13 @@ def llama_fp8(layout: str = "PHSD", poison: bool = True, seed: int = SEED_BASE +
                          v_scale=0.0291)
 
 
+def llama_f32(layout: str = "PHSD", poison: bool = True, seed: int = SEED_BASE + 6) -> GqaCase:
+    """The llama shape over float32 pools."""
+    return make_gqa_case(context_lens=(), ctx_draw=(512, 8192), batch=64, num_q_heads=32,
+                         num_kv_heads=8, head_dim=128, page_size=32, seed=seed, layout=layout,
+                         poison=poison, name="llama_f32", kv_dtype="f32")
+
+
 def d256w(layout: str = "PHSD", poison: bool = True, seed: int = SEED_BASE + 3) -> GqaCase:
     return make_gqa_case(context_lens=(), ctx_draw=(1024, 16384), batch=32, num_q_heads=16,
                          num_kv_heads=2, head_dim=256, page_size=32, seed=seed, layout=layout,
@@ -380,4 +388,4 @@ def mla(poison: bool = True, seed: int = SEED_BASE + 5) -> MlaCase:
 
 
 NAMED = {"tiny": tiny, "llama": llama, "d256w": d256w, "long": long_ctx, "mla": mla,
-         "llama_fp8": llama_fp8}
+         "llama_fp8": llama_fp8, "llama_f32": llama_f32}

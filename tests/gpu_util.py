@@ -43,6 +43,21 @@ def run_decode_fp8(dc, with_lse=True, workspace=None):
     return out.cpu(), (lse.cpu() if lse is not None else None)
 
 
+def run_decode_f32(dc, with_lse=True, workspace=None):
+    B, H, D = dc.q.shape
+    out = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda") if with_lse else None
+    kv = pb.kv_layout(dc.k_pool, dc.layout)
+    if workspace is None:
+        nbytes = pb.pa_decode_workspace_size(B, H, dc.num_kv_heads, D, dc.max_pages, dc.page_size,
+                                             dc.window)
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    pb.pa_decode_f32(dc.q, dc.k_pool, dc.v_pool, kv, dc.block_table, dc.context_lens, dc.scale,
+                     dc.window, out, lse, workspace)
+    torch.cuda.synchronize()
+    return out.cpu(), (lse.cpu() if lse is not None else None)
+
+
 def max_parts_for(dc, partition_size):
     keys = dc.max_pages * dc.page_size
     if dc.window > 0:

@@ -65,7 +65,7 @@ def test_null_pointers(field, status):
     (dict(scale=0.0), "SHAPE"), (dict(scale=float("nan")), "SHAPE"),
     (dict(scale=float("inf")), "SHAPE"), (dict(bt_stride=16), "SHAPE"),
     (dict(batch=70000), "SHAPE"),
-    (dict(kv=_kv(head_dim=64, token_stride=64, head_stride=32 * 64, page_stride=2 * 32 * 64)),
+    (dict(kv=_kv(head_dim=96, token_stride=96, head_stride=32 * 96, page_stride=2 * 32 * 96)),
      "UNSUPPORTED"),
     (dict(hq=64), "UNSUPPORTED"),                                  # 32 q heads per KV head
     (dict(kv=_kv(page_size=8)), "UNSUPPORTED"),
@@ -220,3 +220,15 @@ def test_fp8_rejections():
     # bf16 pools need 8-element strides, FP8 pools 16-element ones
     kv_b = _kv(token_stride=136, head_stride=32 * 136, page_stride=2 * 32 * 136)
     assert _decode(kv=kv_b) == PA["WORKSPACE"]
+
+
+def test_f32_pool_rejections():
+    f = pb.LIB.pa_decode_f32
+    def call(kv):
+        return f(FAKE, FAKE, FAKE, C.byref(kv), FAKE, 32, FAKE, 8, 8, 32, 0.088, 0, FAKE, None,
+                 None, 0, None)
+    assert call(_kv(head_dim=256, token_stride=256, head_stride=32 * 256,
+                    page_stride=2 * 32 * 256)) == PA["UNSUPPORTED"]
+    assert call(_kv(token_stride=130, head_stride=32 * 130, page_stride=2 * 32 * 130)) == PA["ALIGN"]
+    # 4-element strides are 16-byte rows for f32: valid up to the workspace
+    assert call(_kv(token_stride=132, head_stride=32 * 132, page_stride=2 * 32 * 132)) == PA["WORKSPACE"]

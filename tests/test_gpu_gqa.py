@@ -95,6 +95,7 @@ def test_context_zero_gives_zero_and_neg_inf(oracle):
 
 
 @pytest.mark.parametrize("head_dim,group,kv_heads", [
+    (64, 1, 3), (64, 2, 1), (64, 4, 3), (64, 8, 1), (64, 16, 2),
     (128, 1, 3), (128, 2, 3), (128, 4, 1), (128, 8, 3), (128, 16, 1),
     (256, 1, 3), (256, 2, 1), (256, 4, 3), (256, 8, 1)])
 def test_group_and_head_dim_sweep(oracle, head_dim, group, kv_heads):
@@ -287,3 +288,22 @@ def test_long_full_splitkv_512(oracle):
     _lse_ok(lse, ref_lse, "long")
     out2, _ = run_decode(dc)
     _gate(out2, ref, "long pa_decode")
+
+
+@pytest.mark.parametrize("layout", ["PHSD", "PSHD"])
+def test_head_dim_64_window_and_two_stage(oracle, layout):
+    """head_dim 64 (every group size runs on the matrix cores): a window, 16-key
+    pages, and the fixed-partition split + merge against the same oracle."""
+    case = wl.make_gqa_case(context_lens=(0, 1, 15, 16, 17, 300, 2049), num_q_heads=16,
+                            num_kv_heads=4, head_dim=64, page_size=16, seed=8650, layout=layout,
+                            window=500)
+    ref, ref_lse = oracle.decode(case)
+    dc = dev_case(case)
+    out, lse = run_decode(dc)
+    _gate(out, ref, f"D64 window {layout}")
+    _lse_ok(lse, ref_lse, "D64")
+    mp = max_parts_for(dc, 128)
+    po, pm, ps = run_splitkv(dc, 128, mp)
+    out2, lse2 = run_merge(po, pm, ps, dc.context_lens, 128, case.window)
+    _gate(out2, ref, f"D64 two-stage {layout}")
+    _lse_ok(lse2, ref_lse, "D64 two-stage")
