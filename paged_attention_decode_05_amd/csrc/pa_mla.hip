@@ -206,7 +206,7 @@ __device__ __forceinline__ void mla_locate(const int32_t* ctx, int batch, int64_
 // the accumulators only when a score exceeds it by more than 8 (log2
 // domain), so P stays below 2^8 and rescaling is rare.
 __device__ __forceinline__ void mla_segment(const MlaParams& p, int b, int hg, int begin, int end,
-                                            int64_t slot, uint16_t (*crow)[kRowPad],
+                                            int64_t slot, uint16_t (*crow2)[kTileKeys][kRowPad],
                                             uint16_t (*qlo_s)[kLat + 8]) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -241,10 +241,10 @@ __device__ __forceinline__ void mla_segment(const MlaParams& p, int b, int hg, i
     for (int k = 0; k < kChunks; ++k)
       stage[k] = page >= 0 ? load16(src + 64 * k) : make_uint4(0, 0, 0, 0);
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](uint16_t (*dst)[kRowPad]) {
 #pragma unroll
     for (int k = 0; k < kChunks; ++k)
-      *reinterpret_cast<uint4*>(&crow[skey][(schunk + 8 * k) * 8]) = stage[k];
+      *reinterpret_cast<uint4*>(&dst[skey][(schunk + 8 * k) * 8]) = stage[k];
   };
   const int first_tile = begin / kTileKeys;
   const int last_tile = (end - 1) / kTileKeys;
@@ -274,18 +274,26 @@ __device__ __forceinline__ void mla_segment(const MlaParams& p, int b, int hg, i
   float m_ref = -INFINITY;     // per head c16 (same on the 4 lanes of the head)
   float l_sum = 0.0f;          // this lane's share of the head's denominator
 
+  // Tiles alternate between two LDS buffers: tile k+1 is stored into the
+  // other buffer right after tile k's P.V, so one barrier per tile (at the
+  // top: tile k is complete and the other buffer's readers are done) orders
+  // everything.
+  store_tile(crow2[0]);
   for (int tile = first_tile; tile <= last_tile; ++tile) {
     const int t0 = tile * kTileKeys;
-    __syncthreads();                 // previous tile fully consumed
-    store_tile();
+    uint16_t (*crow)[kRowPad] = crow2[(tile - first_tile) & 1];
+    uint16_t (*cnext)[kRowPad] = crow2[(tile - first_tile + 1) & 1];
     __syncthreads();
     // The next tile's loads are issued inside the score loop, between MFMAs
-    // (waves without heads issue them here).
+    // (waves without heads issue and store them here).
     const bool more = tile < last_tile;
     const int page_now = page_next;
     if (more) page_next = tile + 1 < last_tile ? page_of(t0 + 2 * kTileKeys) : -1;
     if (!active) {
-      if (more) load_tile(t0 + kTileKeys, page_now);
+      if (more) {
+        load_tile(t0 + kTileKeys, page_now);
+        store_tile(cnext);
+      }
       continue;
     }
 
@@ -353,19 +361,17 @@ __device__ __forceinline__ void mla_segment(const MlaParams& p, int b, int hg, i
         for (int i = 0; i < 4; ++i) acc[jt][i] *= ar[i];
     }
     const float base = (m_ref == -INFINITY) ? 0.0f : m_ref;
-    uint16_t ph[8], pm[8], pl[8];
+    float e[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const float e = fast_exp2(pv[k] - base);
-      l_sum += e;
-      split3_bf16(e, ph[k], pm[k], pl[k]);
+      e[k] = fast_exp2(pv[k] - base);
+      l_sum += e[k];
     }
-    const uint4 pa_hi = make_uint4(pack_bf16(ph[0], ph[1]), pack_bf16(ph[2], ph[3]),
-                                   pack_bf16(ph[4], ph[5]), pack_bf16(ph[6], ph[7]));
-    const uint4 pa_mid = make_uint4(pack_bf16(pm[0], pm[1]), pack_bf16(pm[2], pm[3]),
-                                    pack_bf16(pm[4], pm[5]), pack_bf16(pm[6], pm[7]));
-    const uint4 pa_lo = make_uint4(pack_bf16(pl[0], pl[1]), pack_bf16(pl[2], pl[3]),
-                                   pack_bf16(pl[4], pl[5]), pack_bf16(pl[6], pl[7]));
+    uint4 pa_hi, pa_mid, pa_lo;
+    split3_bf16x2(e[0], e[1], pa_hi.x, pa_mid.x, pa_lo.x);
+    split3_bf16x2(e[2], e[3], pa_hi.y, pa_mid.y, pa_lo.y);
+    split3_bf16x2(e[4], e[5], pa_hi.z, pa_mid.z, pa_lo.z);
+    split3_bf16x2(e[6], e[7], pa_hi.w, pa_mid.w, pa_lo.w);
     // O[heads][latent] += P . C over the 32 keys of the tile; lane (g, a)
     // points the transposed reads at the rows of keys key_row(4g + a/4) and
     // 16 + key_row(4g + a/4), columns 16*jt + 4*(a%4).
@@ -394,6 +400,7 @@ __device__ __forceinline__ void mla_segment(const MlaParams& p, int b, int hg, i
       acc[jt + 1] = mfma(pa_hi, bopb, acc[jt + 1]);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if (more) store_tile(cnext);
   }
   if (!active) return;
 
@@ -418,7 +425,7 @@ __device__ __forceinline__ void mla_segment(const MlaParams& p, int b, int hg, i
 }
 
 __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(const MlaParams p) {
-  __shared__ __align__(16) uint16_t crow[kTileKeys][kRowPad];
+  __shared__ __align__(16) uint16_t crow[2][kTileKeys][kRowPad];
   __shared__ __align__(16) uint16_t qlo_s[kGroup][kLat + 8];
   __shared__ int64_t sh[4];
   __shared__ int sh_b;
