@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama",
                     choices=["tiny", "llama", "d256w", "long", "mla", "verify", "insert",
-                             "llama_fp8", "llama_f32"])
+                             "llama_fp8", "llama_f32", "d512"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run K device-to-device copies of a 1 GiB buffer instead (reference "
@@ -98,7 +98,8 @@ def main() -> int:
     log(f"generating workload {a.workload} (seeded) ...")
     t0 = time.time()
     cases = [wl.NAMED[a.workload](poison=False, seed=wl.SEED_BASE + 100 * i + {
-        "tiny": 1, "llama": 2, "d256w": 3, "long": 4, "llama_fp8": 5, "llama_f32": 6}[a.workload])
+        "tiny": 1, "llama": 2, "d256w": 3, "long": 4, "llama_fp8": 5, "llama_f32": 6,
+        "d512": 7}[a.workload])
         for i in range(a.rotate)]
     dcs = [c.to(dev) for c in cases]
     log(f"  {time.time() - t0:.1f}s; pool pages {cases[0].num_pages}, "
@@ -185,6 +186,8 @@ def main() -> int:
                                   "ctx U[512,8192]",
                          "tiny": "tiny paged decode, 8 seqs, 8q/2kv, d128, page 32",
                          "d256w": "d256 GQA-8 sliding window 4096, bs32",
+                         "d512": "head_dim-512 GQA-8 decode, bs64, 16q/2kv heads, page 32, "
+                                 "ctx U[512,8192]",
                          "long": "long context bs4, ctx 32K-128K, d128",
                          "llama_fp8": "llama3-8b-shaped decode over an FP8 (E4M3) KV cache, bs64, "
                                       "32q/8kv heads, d128, page 32, ctx U[512,8192]",

@@ -64,7 +64,9 @@ typedef struct pa_kv_layout {
   int32_t num_pages;
   int32_t page_size;    /* 16, 32 or 64 */
   int32_t num_kv_heads;
-  int32_t head_dim;     /* 64, 128 or 256 (576 for the MLA cache) */
+  int32_t head_dim;     /* 64, 128, 256 or 512 (576 for the MLA cache); 512 is the
+                           global-layer head size of a model that mixes 256 and 512
+                           per layer [vllm.cpp kernel matrix, row KERNEL-ATTN-PAGED] */
   int64_t page_stride;
   int64_t head_stride;
   int64_t token_stride;
@@ -101,8 +103,8 @@ typedef struct pa_kv_layout {
  * Requires partition_size >= 1 and max_partitions * partition_size >= the
  * largest possible attended range (min(window, max_pages_per_seq *
  * page_size) with a window, else max_pages_per_seq * page_size); supported
- * head_dim 64 or 128 with 1/2/4/8/16 q heads per KV head, head_dim 256
- * with 1/2/4/8; page_size 16/32/64.
+ * head_dim 64, 128 or 512 with 1/2/4/8/16 q heads per KV head, head_dim
+ * 256 with 1/2/4/8; page_size 16/32/64.
  * ------------------------------------------------------------------------- */
 PA_API int pa_decode_splitkv(const void* q, const void* k_pool, const void* v_pool,
                       const pa_kv_layout* kv, const int32_t* block_table,
@@ -128,7 +130,7 @@ PA_API int pa_decode_splitkv(const void* q, const void* k_pool, const void* v_po
  * Arguments as written by pa_decode_splitkv with the same partition_size,
  * max_partitions and window; max_partitions must cover every sequence's live
  * partitions (not checked: the context lengths live on the device).  out [batch][num_q_heads][head_dim] bf16;
- * lse_out [batch][num_q_heads] fp32 or NULL.  head_dim 64, 128 or 256.
+ * lse_out [batch][num_q_heads] fp32 or NULL.  head_dim 64, 128, 256 or 512.
  * ------------------------------------------------------------------------- */
 PA_API int pa_merge_lse(const float* part_out, const float* part_max,
                  const float* part_sum, const int32_t* context_lens,
@@ -184,7 +186,7 @@ PA_API int pa_decode(const void* q, const void* k_pool, const void* v_pool,
  * q [batch][S][num_q_heads][head_dim] bf16; out the same shape; lse_out
  * [batch][S][num_q_heads] fp32 or NULL.  1 <= S <= 16, and S rounded up to a
  * power of two times num_q_heads / num_kv_heads must be 1, 2, 4, 8 or 16
- * (head_dim 64, 128) or 1, 2, 4, 8 (head_dim 256).  workspace: at least
+ * (head_dim 64, 128, 512) or 1, 2, 4, 8 (head_dim 256).  workspace: at least
  * pa_decode_multiquery_workspace_size(...) bytes, 256-byte aligned,
  * clobbered.  S = 1 gives exactly pa_decode.  Other arguments as pa_decode.
  * ------------------------------------------------------------------------- */
@@ -232,8 +234,8 @@ PA_API int pa_decode_fp8(const void* q, const void* k_pool, const void* v_pool,
  * loader's float instantiation beside the bf16 one; vllm.cpp kernel matrix,
  * inventory row: the paged path admits F32/BF16].  Every element is split
  * exactly into three bf16 terms on the matrix cores, so the score and P.V
- * products are exact and the sums fp32, as in pa_decode.  head_dim 64 or 128
- * (PA_ERR_UNSUPPORTED for 256); strides in elements, rows on 16-byte
+ * products are exact and the sums fp32, as in pa_decode.  head_dim 64, 128
+ * or 512 (PA_ERR_UNSUPPORTED for 256); strides in elements, rows on 16-byte
  * boundaries (strides multiples of 4).  workspace: at least
  * pa_decode_workspace_size(...) bytes for the same shapes.  Other arguments,
  * the split, determinism and the error codes as pa_decode.

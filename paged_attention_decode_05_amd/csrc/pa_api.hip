@@ -177,8 +177,8 @@ int decode_impl(const void* q, const void* k_pool, const void* v_pool, const pa_
   int rc = pa::check_gqa(q, k_pool, v_pool, kv, block_table, block_table_stride, context_lens,
                          batch, num_q_heads, max_pages_per_seq, scale, elem_bytes);
   if (rc) return rc;
-  if (kv_type == 2 && kv->head_dim > 128)
-    return pa::fail(PA_ERR_UNSUPPORTED, "f32 pools take head_dim 64 or 128");
+  if (kv_type == 2 && kv->head_dim == 256)
+    return pa::fail(PA_ERR_UNSUPPORTED, "f32 pools take head_dim 64, 128 or 512");
   if (fp8 && !(std::isfinite(k_scale) && k_scale > 0.0f && std::isfinite(v_scale) &&
                v_scale > 0.0f))
     return pa::fail(PA_ERR_SHAPE, "k_scale and v_scale must be finite and > 0");

@@ -273,26 +273,33 @@ __device__ __forceinline__ void head_bounds(const SplitParams& p, int n, int h, 
 // its log-sum-exp to final_lse[head_offset(h)].  A head that saw no key
 // (possible only for the early queries of a multi-query row) gets o = 0, max
 // -inf, sum 0.
-template <int D, int G, int NW>
+//
+// With NSL > 1 the waves split the dims instead of the keys (wave w holds dims
+// w*D/NSL .. +D/NSL of every head): they share one state, red_*[0][h], and
+// red_acc is slice-major, [w][h][D/NSL].
+template <int D, int G, int NW, int NSL = 1>
 __device__ __forceinline__ void write_range(const SplitParams& p, const float* red_acc,
                                             const float (*red_m)[G], const float (*red_mt)[G],
                                             const float (*red_l)[G], float* out, float* mx,
                                             float* sm, int64_t hstride, uint16_t* final_out,
                                             float* final_lse) {
   constexpr int D4 = D / 4;        // a thread takes 4 consecutive dims of one head
+  constexpr int NS = NSL > 1 ? 1 : NW;   // wave states to merge
+  constexpr int DW = D / NSL;            // dims of one slice
   for (int i = threadIdx.x; i < G * D4; i += 64 * NW) {
     const int h = i / D4;
     const int d = (i % D4) * 4;
     float M = red_mt[0][h];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) M = fmaxf(M, red_mt[w][h]);
+    for (int w = 1; w < NS; ++w) M = fmaxf(M, red_mt[w][h]);
     float W = 0.0f;
     float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
+    for (int w = 0; w < NS; ++w) {
       const float sc = (red_m[w][h] == -INFINITY) ? 0.0f : fast_exp2(red_m[w][h] - M);
       W += red_l[w][h] * sc;
-      const float4 a = *reinterpret_cast<const float4*>(&red_acc[(w * G + h) * D + d]);
+      const float4 a =
+          *reinterpret_cast<const float4*>(&red_acc[((w + d / DW) * G + h) * DW + d % DW]);
       o.x += a.x * sc;
       o.y += a.y * sc;
       o.z += a.z * sc;
@@ -590,12 +597,22 @@ __device__ __forceinline__ void fp8x16_bf16(uint4 x, uint4& lo, uint4& hi) {
                   fp8x2_bf16(x.w, true));
 }
 
+//
+// head_dim 512 (the global-layer head size of a model that mixes 256 and 512
+// per layer [vllm.cpp kernel matrix, row KERNEL-ATTN-PAGED]) splits the dims
+// instead of the keys: the NW waves walk the same
+// chunks, wave w holding dims 128w .. 128w+127 of K, q, V and the output (the
+// D = 128 geometry per wave).  Their partial scores are summed through LDS in
+// wave order, so every wave has the same scores and the same softmax state,
+// and each writes its own output columns.
 template <int D, int G, int NW, int KV>
 __device__ __forceinline__ void attend_range_mfma(const SplitParams& p, int b, int gk, int begin,
                                                   int end, float* out, float* mx, float* sm,
                                                   int64_t hstride, uint16_t* final_out,
                                                   float* final_lse) {
-  using mg = MfmaGeo<D, G, KV>;
+  constexpr int NSL = D > 256 ? NW : 1;   // dim slices
+  constexpr int DW = D / NSL;             // dims of one wave
+  using mg = MfmaGeo<DW, G, KV>;
   constexpr bool F8 = mg::F8;
   constexpr bool F32 = mg::F32;
   constexpr int KC = mg::KC;
@@ -603,9 +620,11 @@ __device__ __forceinline__ void attend_range_mfma(const SplitParams& p, int b, i
   constexpr int kVTerms = F32 ? 3 : 1;    // bf16 V tiles per wave (hi, mid, lo for f32)
   constexpr int kVTileBytes = KC * mg::VPAD * 2;
   constexpr int kTileBytes = NW * kVTerms * kVTileBytes;
-  constexpr int kRedBytes = NW * G * D * 4;
+  constexpr int kRedBytes = NW * G * DW * 4;
   // the V tiles of the loop and the wave states of the epilogue share one buffer
   __shared__ __align__(16) char lds[kTileBytes > kRedBytes ? kTileBytes : kRedBytes];
+  // partial scores of the dim slices, double-buffered (one barrier per chunk)
+  __shared__ f32x4_t sx[NSL > 1 ? 2 : 1][NSL][64];
   __shared__ float red_m[NW][G];
   __shared__ float red_mt[NW][G];
   __shared__ float red_l[NW][G];
@@ -614,6 +633,7 @@ __device__ __forceinline__ void attend_range_mfma(const SplitParams& p, int b, i
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;
   const int c16 = lane & 15;
+  const int slice = NSL > 1 ? wave : 0;
   uint16_t (*vt)[mg::VPAD] =
       reinterpret_cast<uint16_t (*)[mg::VPAD]>(lds + wave * kVTerms * kVTileBytes);
 
@@ -623,19 +643,21 @@ __device__ __forceinline__ void attend_range_mfma(const SplitParams& p, int b, i
   wk.end = end;
   const int c_first = begin / KC;
   const int c_last = (end - 1) / KC;
-  wk.c0 = c_first + wave;
-  wk.step = NW;
-  wk.nk = (wk.c0 <= c_last) ? (c_last - wk.c0) / NW + 1 : 0;
+  wk.c0 = c_first + (NSL > 1 ? 0 : wave);
+  wk.step = NSL > 1 ? 1 : NW;
+  wk.nk = (wk.c0 <= c_last) ? (c_last - wk.c0) / wk.step + 1 : 0;
   // pages per chunk: 1, or 2 when a 32-key chunk meets 16-key pages
   wk.ppc_shift = (KC > p.page_size) ? (ilog2c(KC) - p.page_shift) : 0;
   wk.ptab = 0;
   wk.group = -1;
 
-  // pool bases of KV head gk (head_stride counts pool elements)
+  // pool bases of KV head gk (head_stride counts pool elements), at the
+  // wave's dim slice
+  const int64_t slice_bytes = static_cast<int64_t>(slice) * DW * mg::EB;
   const uint16_t* kbase = reinterpret_cast<const uint16_t*>(
-      reinterpret_cast<const char*>(p.k) + static_cast<int64_t>(gk) * p.head_stride * mg::EB);
+      reinterpret_cast<const char*>(p.k) + static_cast<int64_t>(gk) * p.head_stride * mg::EB + slice_bytes);
   const uint16_t* vbase = reinterpret_cast<const uint16_t*>(
-      reinterpret_cast<const char*>(p.v) + static_cast<int64_t>(gk) * p.head_stride * mg::EB);
+      reinterpret_cast<const char*>(p.v) + static_cast<int64_t>(gk) * p.head_stride * mg::EB + slice_bytes);
 
   const int gq = 1 << p.group_shift;
   const int64_t row0 = static_cast<int64_t>(b) * p.num_q_heads + static_cast<int64_t>(gk) * gq;
@@ -645,7 +667,7 @@ __device__ __forceinline__ void attend_range_mfma(const SplitParams& p, int b, i
   // or 64j + 16g + 8(ks & 1) .. +8 with j = ks / 2 (FP8 pools)
   uint4 qb[mg::KS];
   {
-    const uint16_t* qrow = p.q + (row0 + head_offset(p, head_live ? c16 : 0)) * D;
+    const uint16_t* qrow = p.q + (row0 + head_offset(p, head_live ? c16 : 0)) * D + slice * DW;
 #pragma unroll
     for (int ks = 0; ks < mg::KS; ++ks) {
       const int d0 = F8 ? 64 * (ks >> 1) + 16 * g + 8 * (ks & 1) : 32 * ks + 8 * g;
@@ -672,7 +694,7 @@ __device__ __forceinline__ void attend_range_mfma(const SplitParams& p, int b, i
   const int voff0 = (lane / mg::LV) * p.token_bytes + 16 * (lane % mg::LV);
   uint4 kr[SUB][mg::NK], vr[SUB][mg::NV];
   auto issue_k = [&](int k) {
-    const int t0 = (wk.c0 + k * NW) * KC;
+    const int t0 = (wk.c0 + k * wk.step) * KC;
 #pragma unroll
     for (int u = 0; u < SUB; ++u) {
       const int tu = t0 + 16 * u;
@@ -684,7 +706,7 @@ __device__ __forceinline__ void attend_range_mfma(const SplitParams& p, int b, i
     }
   };
   auto issue_v = [&](int k) {
-    const int t0 = (wk.c0 + k * NW) * KC;
+    const int t0 = (wk.c0 + k * wk.step) * KC;
 #pragma unroll
     for (int u = 0; u < SUB; ++u) {
       const int tu = t0 + 16 * u;
@@ -704,7 +726,7 @@ __device__ __forceinline__ void attend_range_mfma(const SplitParams& p, int b, i
   }
   const uint16_t* brow = &vt[4 * g + (c16 >> 2)][4 * (c16 & 3)];
   for (int k = 0; k < wk.nk; ++k) {
-    const int t0 = (wk.c0 + k * NW) * KC;
+    const int t0 = (wk.c0 + k * wk.step) * KC;
     const bool more = k + 1 < wk.nk;
     f32x4_t sc[SUB];
 #pragma unroll
@@ -740,6 +762,15 @@ __device__ __forceinline__ void attend_range_mfma(const SplitParams& p, int b, i
     if (more) {
       ensure_pages<KC>(wk, k + 1, lane, p.page_shift);
       issue_k(k + 1);
+    }
+    if constexpr (NSL > 1) {
+      static_assert(SUB == 1, "one score tile per chunk");
+      sx[k & 1][slice][lane] = sc[0];
+      __syncthreads();
+      f32x4_t t = sx[k & 1][0][lane];
+#pragma unroll
+      for (int w = 1; w < NSL; ++w) t += sx[k & 1][w][lane];
+      sc[0] = t;
     }
 
     // lane holds keys t0 + 16u + 4g + i of head c16; a chunk inside every
@@ -889,31 +920,33 @@ __device__ __forceinline__ void attend_range_mfma(const SplitParams& p, int b, i
     const int h = 4 * g + i;
     if (h < G) {
 #pragma unroll
-      for (int nt = 0; nt < mg::NT; ++nt) red_acc[(wave * G + h) * D + 16 * nt + c16] = acc[nt][i];
+      for (int nt = 0; nt < mg::NT; ++nt) red_acc[(wave * G + h) * DW + 16 * nt + c16] = acc[nt][i];
     }
   }
-  if (g == 0 && head_live) {
+  if (g == 0 && head_live && (NSL == 1 || wave == 0)) {
     red_m[wave][c16] = m_ref;
     red_mt[wave][c16] = m_top;
     red_l[wave][c16] = l_sum;
   }
   __syncthreads();
-  write_range<D, G, NW>(p, red_acc, red_m, red_mt, red_l, out, mx, sm, hstride, final_out,
-                        final_lse);
+  write_range<D, G, NW, NSL>(p, red_acc, red_m, red_mt, red_l, out, mx, sm, hstride, final_out,
+                             final_lse);
   __syncthreads();   // the shared buffers are reused by the block's next range
 }
 
 // Groups of 4 to 16 heads run on the matrix cores, 1 and 2 on the vector
 // ALUs (measured on the bs64 GQA-4 decode: 199 us on MFMA against 206 us);
-// head_dim 64 always takes the matrix cores.
+// head_dim 64 and 512 always take the matrix cores.
 template <int D, int G>
-constexpr bool kUseMfma = G >= 4 || D == 64;
+constexpr bool kUseMfma = G >= 4 || D == 64 || D == 512;
 
 // Waves per SIMD the compiler must fit the range kernels' registers into.
+// (head_dim 512 holds the D = 128 registers per wave)
 template <int D, int G, int KV = kKvBf16>
 constexpr int kMinWaves = KV == kKvF32 ? (D == 64 ? 3 : 2)
-                          : (KV != kKvBf16 || kUseMfma<D, G>) ? (D == 64 ? 4 : D == 128 ? 3 : 2)
-                                                              : 1;
+                          : (KV != kKvBf16 || kUseMfma<D, G>)
+                              ? (D == 64 ? 4 : (D == 128 || D == 512) ? 3 : 2)
+                              : 1;
 
 // FP8 and f32 pools always take the matrix-core routine.
 template <int D, int G, int NW, int KV = kKvBf16>
@@ -1305,7 +1338,7 @@ static hipError_t launch_split_d(const SplitParams& p, int group, int batch, int
     case 4: return launch_split_dg<D, 4>(p, batch, num_kv_heads, stream);
     case 8: return launch_split_dg<D, 8>(p, batch, num_kv_heads, stream);
     case 16:
-      if constexpr (D <= 128) return launch_split_dg<D, 16>(p, batch, num_kv_heads, stream);
+      if constexpr (D != 256) return launch_split_dg<D, 16>(p, batch, num_kv_heads, stream);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
@@ -1316,6 +1349,7 @@ hipError_t launch_split(const SplitParams& p, int head_dim, int group, int batch
   if (head_dim == 64) return launch_split_d<64>(p, group, batch, num_kv_heads, stream);
   if (head_dim == 128) return launch_split_d<128>(p, group, batch, num_kv_heads, stream);
   if (head_dim == 256) return launch_split_d<256>(p, group, batch, num_kv_heads, stream);
+  if (head_dim == 512) return launch_split_d<512>(p, group, batch, num_kv_heads, stream);
   return hipErrorInvalidValue;
 }
 
@@ -1327,6 +1361,8 @@ hipError_t launch_merge(const MergeParams& p, int head_dim, int batch, hipStream
     hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(kBlock), 0, stream, p);
   } else if (head_dim == 256) {
     hipLaunchKernelGGL(merge_kernel<256>, grid, dim3(kBlock), 0, stream, p);
+  } else if (head_dim == 512) {
+    hipLaunchKernelGGL(merge_kernel<512>, grid, dim3(kBlock), 0, stream, p);
   } else {
     return hipErrorInvalidValue;
   }
@@ -1340,21 +1376,23 @@ static int balanced_blocks(int num_cus, int max_blocks) {
 }
 
 // Calls f.template operator()<D, G, KV>() for a supported (head_dim, group,
-// pool element type) triple; returns `none` otherwise.  f32 pools stop at
-// head_dim 128 (their K and V registers would not fit two waves per SIMD at 256).
+// pool element type) triple; returns `none` otherwise.  f32 pools skip
+// head_dim 256 (their K and V registers would not fit two waves per SIMD; at
+// 512 a wave holds 128 dims).
 template <typename R, typename F>
 static R dispatch_dg(int head_dim, int group, int kv, R none, F&& f) {
 #define PA_CASE(DD, GG)                                                                \
   if (head_dim == DD && group == GG) {                                                 \
     if (kv == kKvBf16) return f.template operator()<DD, GG, kKvBf16>();                \
     if (kv == kKvFp8) return f.template operator()<DD, GG, kKvFp8>();                  \
-    if constexpr (DD <= 128)                                                           \
+    if constexpr (DD != 256)                                                           \
       if (kv == kKvF32) return f.template operator()<DD, GG, kKvF32>();                \
     return none;                                                                       \
   }
   PA_CASE(64, 1) PA_CASE(64, 2) PA_CASE(64, 4) PA_CASE(64, 8) PA_CASE(64, 16)
   PA_CASE(128, 1) PA_CASE(128, 2) PA_CASE(128, 4) PA_CASE(128, 8) PA_CASE(128, 16)
   PA_CASE(256, 1) PA_CASE(256, 2) PA_CASE(256, 4) PA_CASE(256, 8)
+  PA_CASE(512, 1) PA_CASE(512, 2) PA_CASE(512, 4) PA_CASE(512, 8) PA_CASE(512, 16)
 #undef PA_CASE
   return none;
 }

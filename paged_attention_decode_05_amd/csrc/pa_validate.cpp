@@ -23,13 +23,14 @@ int fail(int status, const std::string& msg) {
 void clear_error() { g_last_error.clear(); }
 const char* last_error() { return g_last_error.c_str(); }
 
-bool head_dim_supported(int32_t d) { return d == 64 || d == 128 || d == 256; }
+bool head_dim_supported(int32_t d) { return d == 64 || d == 128 || d == 256 || d == 512; }
 
 // q heads per KV head built per head_dim: 16 heads at head_dim 256 would need
-// more registers than two waves per SIMD leave, so head_dim 256 stops at 8.
+// more registers than two waves per SIMD leave, so head_dim 256 stops at 8
+// (at 512 each wave holds 128 of the dims).
 bool group_supported(int32_t head_dim, int32_t group) {
   if (group == 1 || group == 2 || group == 4 || group == 8) return true;
-  return group == 16 && head_dim <= 128;
+  return group == 16 && head_dim != 256;
 }
 
 bool page_size_supported(int32_t ps) { return ps == 16 || ps == 32 || ps == 64; }
@@ -69,10 +70,10 @@ int check_gqa(const void* q, const void* k_pool, const void* v_pool, const pa_kv
   if (static_cast<int64_t>(max_pages_per_seq) * kv->page_size > INT32_MAX / 2)
     return fail(PA_ERR_SHAPE, "max_pages_per_seq * page_size is too large");
   if (!head_dim_supported(kv->head_dim))
-    return fail(PA_ERR_UNSUPPORTED, "head_dim must be 64, 128 or 256");
+    return fail(PA_ERR_UNSUPPORTED, "head_dim must be 64, 128, 256 or 512");
   const int32_t group = num_q_heads / kv->num_kv_heads;
   if (!group_supported(kv->head_dim, group))
-    return fail(PA_ERR_UNSUPPORTED, "q heads per KV head must be 1, 2, 4, 8 (or 16 at head_dim 64 or 128)");
+    return fail(PA_ERR_UNSUPPORTED, "q heads per KV head must be 1, 2, 4, 8 (or 16 at head_dim 64, 128 or 512)");
   if (!page_size_supported(kv->page_size))
     return fail(PA_ERR_UNSUPPORTED, "page_size must be 16, 32 or 64");
   const int64_t row_align = 16 / elem_bytes;   // elements per 16 bytes
@@ -126,7 +127,7 @@ int check_merge(const float* part_out, const float* part_max, const float* part_
   if (batch > 65535 || num_q_heads > 65535)
     return fail(PA_ERR_SHAPE, "batch and num_q_heads must be <= 65535 (grid limits)");
   if (!head_dim_supported(head_dim))
-    return fail(PA_ERR_UNSUPPORTED, "head_dim must be 64, 128 or 256");
+    return fail(PA_ERR_UNSUPPORTED, "head_dim must be 64, 128, 256 or 512");
   if (!aligned16(part_out) || !aligned16(out))
     return fail(PA_ERR_ALIGN, "part_out and out must be 16-byte aligned");
   return PA_OK;

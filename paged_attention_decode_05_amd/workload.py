@@ -370,6 +370,14 @@ def llama_f32(layout: str = "PHSD", poison: bool = True, seed: int = SEED_BASE +
                          poison=poison, name="llama_f32", kv_dtype="f32")
 
 
+def d512(layout: str = "PHSD", poison: bool = True, seed: int = SEED_BASE + 7) -> GqaCase:
+    """head_dim 512 (a global-attention layer's head size), 16 q / 2 KV heads:
+    the same K/V bytes per key as the llama shape."""
+    return make_gqa_case(context_lens=(), ctx_draw=(512, 8192), batch=64, num_q_heads=16,
+                         num_kv_heads=2, head_dim=512, page_size=32, seed=seed, layout=layout,
+                         poison=poison, name="d512")
+
+
 def d256w(layout: str = "PHSD", poison: bool = True, seed: int = SEED_BASE + 3) -> GqaCase:
     return make_gqa_case(context_lens=(), ctx_draw=(1024, 16384), batch=32, num_q_heads=16,
                          num_kv_heads=2, head_dim=256, page_size=32, seed=seed, layout=layout,
@@ -388,4 +396,4 @@ def mla(poison: bool = True, seed: int = SEED_BASE + 5) -> MlaCase:
 
 
 NAMED = {"tiny": tiny, "llama": llama, "d256w": d256w, "long": long_ctx, "mla": mla,
-         "llama_fp8": llama_fp8, "llama_f32": llama_f32}
+         "llama_fp8": llama_fp8, "llama_f32": llama_f32, "d512": d512}

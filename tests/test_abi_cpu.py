@@ -83,6 +83,23 @@ def test_decode_rejections(kw, status):
     assert pb.pa_last_error()
 
 
+def test_head_dim_512_accepted():
+    """head_dim 512 takes groups 1-16 (16 is refused only at 256); every such
+    call is valid up to the missing workspace, for bf16 and f32 pools."""
+    kv = _kv(head_dim=512, num_kv_heads=1, token_stride=512, head_stride=32 * 512,
+             page_stride=32 * 512)
+    for hq in (1, 2, 4, 8, 16):
+        assert _decode(kv=kv, hq=hq) == PA["WORKSPACE"], pb.pa_last_error()
+    assert _decode(kv=kv, hq=32) == PA["UNSUPPORTED"]
+    f = pb.LIB.pa_decode_f32
+    assert f(FAKE, FAKE, FAKE, C.byref(kv), FAKE, 32, FAKE, 8, 16, 32, 0.044, 0, FAKE, None,
+             None, 0, None) == PA["WORKSPACE"], pb.pa_last_error()
+    need = pb.pa_decode_workspace_size(8, 16, 1, 512, 32, 32, 0)
+    slots = 8 + 2048
+    base = slots * 16 * 514 * 4 + 8 * 4
+    assert base <= need < base + 1024
+
+
 def test_workspace_alignment_checked_last():
     need = pb.pa_decode_workspace_size(8, 8, 2, 128, 32, 32, 0)
     assert need > 0
