@@ -95,6 +95,17 @@ class Oracle:
                                                   C.c_int32, C.c_int32, C.c_double, C.c_double,
                                                   C.c_double, C.c_int32, f64p, f64p]
         self.lib.oracle_pa_decode_fp8.restype = C.c_int
+        self.lib.oracle_e4m3_encode.argtypes = [C.c_double]
+        self.lib.oracle_e4m3_encode.restype = C.c_uint8
+        self.lib.oracle_mla_cache_insert_fp8.argtypes = [u16p, C.c_int64, u16p, C.c_int64, u8p,
+                                                         pool, i64p, C.c_int32, C.c_int32,
+                                                         C.c_int32]
+        self.lib.oracle_mla_cache_insert_fp8.restype = C.c_int
+        self.lib.oracle_mla_decode_fp8.argtypes = [u16p, u16p, u8p, pool, u16p, u16p, i32p,
+                                                   C.c_int32, i32p, C.c_int32, C.c_int32,
+                                                   C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                                                   C.c_double, f64p, f64p]
+        self.lib.oracle_mla_decode_fp8.restype = C.c_int
         f32p = C.POINTER(C.c_float)
         self.lib.oracle_pa_decode_f32pool.argtypes = [u16p, f32p, f32p, pool, i32p, C.c_int32,
                                                       i32p, C.c_int32, C.c_int32, C.c_double,
@@ -144,6 +155,9 @@ class Oracle:
 
     def e4m3_value(self, byte: int) -> float:
         return float(self.lib.oracle_e4m3_value(int(byte)))
+
+    def e4m3_encode(self, v: float) -> int:
+        return int(self.lib.oracle_e4m3_encode(float(v)))
 
     def decode_fp8(self, case, window: Optional[int] = None):
         """(out [B,Hq,D], lse [B,Hq]) float64 for a GqaCase with FP8 pools."""
@@ -267,6 +281,45 @@ class Oracle:
                                               d_lat, d_rope)
         self._check(rc, "oracle_mla_cache_insert")
         return torch.from_numpy(out.view(np.int16)).view(torch.bfloat16).reshape(cache.shape)
+
+    def mla_cache_insert_fp8(self, kv_c: torch.Tensor, k_pe: torch.Tensor, cache: torch.Tensor,
+                             slots) -> torch.Tensor:
+        """Copy of the FP8 latent cache [P, page, row bytes] (uint8) after
+        quantizing kv_c [T, d_lat] and writing it with k_pe [T, d_rope] (bf16,
+        contiguous) at the slots."""
+        c, pe = _bits(kv_c), _bits(k_pe)
+        out = np.ascontiguousarray(cache.cpu().numpy(), dtype=np.uint8).copy()
+        sl = np.ascontiguousarray(torch.as_tensor(slots).cpu().numpy(), np.int64)
+        T, d_lat = kv_c.shape
+        d_rope = k_pe.shape[1]
+        P, S, R = cache.shape
+        pool = _Pool(P, S, 1, R, S * R, 0, R)
+        u8, u16, i64 = C.c_uint8, C.c_uint16, C.c_int64
+        rc = self.lib.oracle_mla_cache_insert_fp8(_ptr(c, u16), d_lat, _ptr(pe, u16), d_rope,
+                                                  _ptr(out, u8), C.byref(pool), _ptr(sl, i64), T,
+                                                  d_lat, d_rope)
+        self._check(rc, "oracle_mla_cache_insert_fp8")
+        return torch.from_numpy(out)
+
+    def mla_fp8(self, case):
+        """(out [B,H,d_v], lse [B,H]) float64 for an MlaCase with an FP8 cache."""
+        assert case.cache_dtype == "fp8"
+        B, H = case.batch, case.num_heads
+        qn, qr = _bits(case.q_nope), _bits(case.q_rope)
+        cache = np.ascontiguousarray(case.cache.cpu().numpy(), dtype=np.uint8)
+        wuk, wuv = _bits(case.w_uk), _bits(case.w_uv)
+        bt, ctx = _i32(case.block_table), _i32(case.context_lens)
+        P, S, R = case.cache.shape
+        pool = _Pool(case.num_pages, case.page_size, 1, R, S * R, 0, R)
+        out = np.zeros((B, H, case.d_v), np.float64)
+        lse = np.zeros((B, H), np.float64)
+        u8, u16, i32, f64 = C.c_uint8, C.c_uint16, C.c_int32, C.c_double
+        rc = self.lib.oracle_mla_decode_fp8(
+            _ptr(qn, u16), _ptr(qr, u16), _ptr(cache, u8), C.byref(pool), _ptr(wuk, u16),
+            _ptr(wuv, u16), _ptr(bt, i32), bt.shape[1], _ptr(ctx, i32), B, H, case.d_nope,
+            case.d_rope, case.d_lat, case.d_v, float(case.scale), _ptr(out, f64), _ptr(lse, f64))
+        self._check(rc, "oracle_mla_decode_fp8")
+        return out, lse
 
     # ---- absorbed MLA --------------------------------------------------------
     def mla(self, case, precision: str = "f64", want_q_abs: bool = False):

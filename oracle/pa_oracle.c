@@ -19,6 +19,8 @@
  *  14 FP8 decode: e4m3 exponent bias read as 8 instead of 7
  *  15 FP8 decode: the K and V scales swapped
  *  16 f32 decode: V rows read one token after K's
+ *  17 FP8 MLA insert: block exponent floor(log2(absmax / 448)) instead of ceil
+ *  18 FP8 MLA decode: block scale 2^(byte - 128) instead of 2^(byte - 127)
  */
 #include <math.h>
 #include <stdlib.h>
@@ -329,6 +331,194 @@ int oracle_pa_decode_f32pool(const uint16_t* q, const float* k_pool, const float
         for (int32_t d = 0; d < D; ++d) o[d] /= l;
       lse[(int64_t)b * num_q_heads + h] = cnt > 0 ? m + log(l) : -INFINITY;
     }
+  }
+  return err;
+}
+
+/* ---- FP8 MLA latent cache ----------------------------------------------------
+ *
+ * The fp8_ds_mla cache state of the pages [vllm.cpp kernel matrix, row
+ * KERNEL-KV-CACHE-DSA]: the latent is quantized to E4M3 in blocks of 64
+ * elements, each block with one UE8M0 power-of-two scale whose exponent is
+ * ceil(log2(absmax / 448)) (stored as exponent + 127); the rope part stays
+ * bf16; the dequant read is e4m3(byte) * 2^(scale byte - 127).  The pages
+ * apply it to a 448 + 64 latent; here it is applied to the d_lat + d_rope
+ * latent of the MLA path (all d_lat values in blocks of 64), with this row
+ * layout, in bytes:
+ *   [0, d_lat)                        E4M3 latent
+ *   [d_lat, d_lat + 2 d_rope)         rope, bf16 little-endian
+ *   [d_lat + 2 d_rope, + d_lat / 64)  scale bytes, block j at offset j
+ *   then zero bytes up to the row size (pool->head_dim bytes).
+ * Readings where the pages are silent: an all-zero block (absmax 0) and any
+ * block whose exponent falls outside [-126, 127] take the nearest end of that
+ * range, so every scale is a normal float32; the element byte is the E4M3
+ * value nearest x / 2^exponent (|x / 2^exponent| <= 448 by the choice of the
+ * exponent), ties to the even code, sign bit = the sign bit of x. */
+
+#define ORACLE_FP8_BLOCK 64
+
+/* Block exponent: the smallest e with 448 * 2^e >= absmax, clamped. */
+static int fp8_block_exponent(double absmax) {
+  if (absmax == 0.0) return -126;
+#if ORACLE_MUTATION == 17
+  double e = floor(log2(absmax / 448.0)); /* planted */
+#else
+  double e = ceil(log2(absmax / 448.0));
+#endif
+  if (e < -126) e = -126;
+  if (e > 127) e = 127;
+  return (int)e;
+}
+
+/* E4M3 byte nearest to v (|v| <= 448), ties to the even code, by comparing
+ * v with the value of every finite non-negative code. */
+uint8_t oracle_e4m3_encode(double v) {
+  const double a = fabs(v);
+  int best = 0;
+  double best_d = INFINITY;
+  for (int c = 0; c < 127; ++c) {   /* 0x7F is NaN */
+    const double d = fabs(oracle_e4m3_value((uint8_t)c) - a);
+    if (d < best_d || (d == best_d && (c & 1) == 0)) {
+      best = c;
+      best_d = d;
+    }
+  }
+  return (uint8_t)(signbit(v) ? (best | 0x80) : best);
+}
+
+static int mla_fp8_row_ok(const oracle_pool* pool, int32_t d_lat, int32_t d_rope) {
+  return pool && pool->num_kv_heads == 1 && pool->num_pages > 0 && pool->page_size > 0 &&
+         d_lat > 0 && d_lat % ORACLE_FP8_BLOCK == 0 && d_rope >= 0 &&
+         pool->head_dim >= d_lat + 2 * d_rope + d_lat / ORACLE_FP8_BLOCK &&
+         pool->token_stride >= pool->head_dim;
+}
+
+int oracle_mla_cache_insert_fp8(const uint16_t* kv_c, int64_t c_stride, const uint16_t* k_pe,
+                                int64_t pe_stride, uint8_t* cache, const oracle_pool* pool,
+                                const int64_t* slots, int32_t num_tokens, int32_t d_lat,
+                                int32_t d_rope) {
+  if (!kv_c || !k_pe || !cache || !slots || num_tokens < 0 || !mla_fp8_row_ok(pool, d_lat, d_rope))
+    return ORACLE_ERR_ARGS;
+  const int64_t total = (int64_t)pool->num_pages * pool->page_size;
+  const int32_t nblk = d_lat / ORACLE_FP8_BLOCK;
+  for (int32_t i = 0; i < num_tokens; ++i) {
+    const int64_t s = slots[i];
+    if (s < 0 || s >= total) continue;
+    uint8_t* row = cache + (s / pool->page_size) * pool->page_stride +
+                   (s % pool->page_size) * pool->token_stride;
+    const uint16_t* x = kv_c + i * c_stride;
+    for (int32_t j = 0; j < nblk; ++j) {
+      double absmax = 0.0;
+      for (int32_t k = 0; k < ORACLE_FP8_BLOCK; ++k) {
+        const double a = fabs((double)bf16_to_float(x[j * ORACLE_FP8_BLOCK + k]));
+        if (a > absmax) absmax = a;
+      }
+      const int e = fp8_block_exponent(absmax);
+      for (int32_t k = 0; k < ORACLE_FP8_BLOCK; ++k) {
+        const int32_t d = j * ORACLE_FP8_BLOCK + k;
+        double q = ldexp((double)bf16_to_float(x[d]), -e);
+        if (q > 448.0) q = 448.0;   /* only reachable with the planted floor */
+        if (q < -448.0) q = -448.0;
+        row[d] = oracle_e4m3_encode(q);
+      }
+      row[d_lat + 2 * d_rope + j] = (uint8_t)(e + 127);
+    }
+    for (int32_t r = 0; r < d_rope; ++r) {
+      const uint16_t v = k_pe[i * pe_stride + r];
+      row[d_lat + 2 * r] = (uint8_t)(v & 0xff);
+      row[d_lat + 2 * r + 1] = (uint8_t)(v >> 8);
+    }
+    for (int32_t o = d_lat + 2 * d_rope + nblk; o < pool->head_dim; ++o) row[o] = 0;
+  }
+  return ORACLE_OK;
+}
+
+/* Value of element d of a row: the dequantized latent (d < d_lat) or the
+ * bf16 rope part. */
+static double mla_fp8_elem(const uint8_t* row, int32_t d, int32_t d_lat, int32_t d_rope) {
+  if (d < d_lat) {
+    const int sb = row[d_lat + 2 * d_rope + d / ORACLE_FP8_BLOCK];
+#if ORACLE_MUTATION == 18
+    return ldexp(oracle_e4m3_value(row[d]), sb - 128); /* planted */
+#else
+    return ldexp(oracle_e4m3_value(row[d]), sb - 127);
+#endif
+  }
+  const int32_t r = d - d_lat;
+  return (double)bf16_to_float((uint16_t)(row[d_lat + 2 * r] | (row[d_lat + 2 * r + 1] << 8)));
+}
+
+/* Absorbed MLA decode over an FP8 latent cache, float64: every row of a
+ * sequence is dequantized, then the steps of oracle_mla_decode_f64 follow on
+ * the dequantized rows (q_abs, scores over the d_lat + d_rope values, two-pass
+ * softmax, o_lat over the latent values, W_UV). */
+int oracle_mla_decode_fp8(const uint16_t* q_nope, const uint16_t* q_rope, const uint8_t* cache,
+                          const oracle_pool* pool, const uint16_t* w_uk, const uint16_t* w_uv,
+                          const int32_t* block_table, int32_t bt_stride,
+                          const int32_t* context_lens, int32_t batch, int32_t num_heads,
+                          int32_t d_nope, int32_t d_rope, int32_t d_lat, int32_t d_v,
+                          double scale, double* out, double* lse) {
+  if (!q_nope || !q_rope || !cache || !w_uk || !w_uv || !block_table || !context_lens || !out ||
+      batch < 0 || num_heads <= 0 || d_nope <= 0 || d_v <= 0 || !mla_fp8_row_ok(pool, d_lat, d_rope))
+    return ORACLE_ERR_ARGS;
+  const int32_t R = d_lat + d_rope;
+  int err = ORACLE_OK;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int32_t n = context_lens[b];
+    const int32_t* bt = block_table + (int64_t)b * bt_stride;
+    double* rows = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * (size_t)R);
+    if (!rows) return ORACLE_ERR_ARGS;
+    int bad = 0;
+    for (int32_t t = 0; t < n && !bad; ++t) {
+      const int32_t page = bt[t / pool->page_size];
+      if (page < 0 || page >= pool->num_pages) { bad = 1; break; }
+      const uint8_t* row = cache + (int64_t)page * pool->page_stride +
+                           (int64_t)(t % pool->page_size) * pool->token_stride;
+      for (int32_t d = 0; d < R; ++d) rows[(int64_t)t * R + d] = mla_fp8_elem(row, d, d_lat, d_rope);
+    }
+    if (bad) { free(rows); err = ORACLE_ERR_PAGE; continue; }
+#pragma omp parallel for schedule(dynamic)
+    for (int32_t h = 0; h < num_heads; ++h) {
+      const int64_t hr = (int64_t)b * num_heads + h;
+      const uint16_t* qn = q_nope + hr * d_nope;
+      const uint16_t* qr = q_rope + hr * d_rope;
+      double* q_abs = (double*)malloc(sizeof(double) * (size_t)d_lat);
+      double* o_lat = (double*)calloc((size_t)d_lat, sizeof(double));
+      double* s = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+      if (!q_abs || !o_lat || !s) { free(q_abs); free(o_lat); free(s); continue; }
+      for (int32_t j = 0; j < d_lat; ++j) {
+        double acc = 0.0;
+        for (int32_t d = 0; d < d_nope; ++d)
+          acc += (double)bf16_to_float(qn[d]) *
+                 (double)bf16_to_float(w_uk[((int64_t)h * d_nope + d) * d_lat + j]);
+        q_abs[j] = acc;
+      }
+      double m = -INFINITY;
+      for (int32_t t = 0; t < n; ++t) {
+        const double* c = rows + (int64_t)t * R;
+        double dot = 0.0;
+        for (int32_t j = 0; j < d_lat; ++j) dot += q_abs[j] * c[j];
+        for (int32_t r = 0; r < d_rope; ++r) dot += (double)bf16_to_float(qr[r]) * c[d_lat + r];
+        s[t] = scale * dot;
+        if (s[t] > m) m = s[t];
+      }
+      double l = 0.0;
+      for (int32_t t = 0; t < n; ++t) {
+        const double e = exp(s[t] - m);
+        l += e;
+        for (int32_t j = 0; j < d_lat; ++j) o_lat[j] += e * rows[(int64_t)t * R + j];
+      }
+      for (int32_t j = 0; j < d_lat; ++j) o_lat[j] = (n > 0) ? o_lat[j] / l : 0.0;
+      for (int32_t dv = 0; dv < d_v; ++dv) {
+        double acc = 0.0;
+        for (int32_t j = 0; j < d_lat; ++j)
+          acc += (double)bf16_to_float(w_uv[((int64_t)h * d_v + dv) * d_lat + j]) * o_lat[j];
+        out[hr * d_v + dv] = acc;
+      }
+      if (lse) lse[hr] = (n > 0) ? m + log(l) : -INFINITY;
+      free(q_abs); free(o_lat); free(s);
+    }
+    free(rows);
   }
   return err;
 }

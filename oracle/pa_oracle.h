@@ -163,6 +163,26 @@ int oracle_mla_cache_insert(const uint16_t* kv_c, int64_t c_stride, const uint16
                             const int64_t* slots, int32_t num_tokens, int32_t d_lat,
                             int32_t d_rope);
 
+/* FP8 MLA latent cache (E4M3 latent in blocks of 64 with one UE8M0 scale
+ * byte each, bf16 rope); row layout in bytes: [d_lat E4M3][2 d_rope rope]
+ * [d_lat / 64 scale bytes][zeros up to pool->head_dim].  pool strides and
+ * head_dim count bytes; num_kv_heads = 1.
+ * oracle_e4m3_encode: the E4M3 byte nearest to v (|v| <= 448), ties to even.
+ * oracle_mla_cache_insert_fp8: quantizes kv_c rows and copies k_pe into the
+ * rows at the slots (slots outside the pool are skipped).
+ * oracle_mla_decode_fp8: absorbed MLA over the dequantized rows, float64. */
+uint8_t oracle_e4m3_encode(double v);
+int oracle_mla_cache_insert_fp8(const uint16_t* kv_c, int64_t c_stride, const uint16_t* k_pe,
+                                int64_t pe_stride, uint8_t* cache, const oracle_pool* pool,
+                                const int64_t* slots, int32_t num_tokens, int32_t d_lat,
+                                int32_t d_rope);
+int oracle_mla_decode_fp8(const uint16_t* q_nope, const uint16_t* q_rope, const uint8_t* cache,
+                          const oracle_pool* pool, const uint16_t* w_uk, const uint16_t* w_uv,
+                          const int32_t* block_table, int32_t bt_stride,
+                          const int32_t* context_lens, int32_t batch, int32_t num_heads,
+                          int32_t d_nope, int32_t d_rope, int32_t d_lat, int32_t d_v,
+                          double scale, double* out, double* lse);
+
 #ifdef __cplusplus
 }
 #endif

@@ -125,7 +125,8 @@ class GqaCase:
 class MlaCase:
     q_nope: torch.Tensor            # [B, H, d_nope] bf16
     q_rope: torch.Tensor            # [B, H, d_rope] bf16
-    cache: torch.Tensor             # [P, page_size, d_lat + d_rope] bf16
+    cache: torch.Tensor             # [P, page_size, d_lat + d_rope] bf16, or
+                                    # [P, page_size, MLA_FP8_ROW] uint8 (FP8 rows)
     w_uk: torch.Tensor              # [H, d_nope, d_lat] bf16
     w_uv: torch.Tensor              # [H, d_v, d_lat] bf16
     block_table: torch.Tensor       # [B, max_pages] int32
@@ -139,6 +140,7 @@ class MlaCase:
     scale: float
     name: str = "custom"
     seed: int = 0
+    cache_dtype: str = "bf16"       # "bf16" or "fp8"
 
     @property
     def batch(self) -> int:
@@ -153,7 +155,8 @@ class MlaCase:
         return int(self.block_table.shape[1])
 
     def latent_bytes(self) -> int:
-        return int(self.context_lens.sum()) * (self.d_lat + self.d_rope) * 2
+        row = MLA_FP8_ROW if self.cache_dtype == "fp8" else (self.d_lat + self.d_rope) * 2
+        return int(self.context_lens.sum()) * row
 
     def algorithmic_bytes(self) -> int:
         """Latent rows + both weight tensors + q in + out, read/written once."""
@@ -197,6 +200,37 @@ def _assign_pages(gen, ctx: Sequence[int], page_size: int, max_pages: int,
 
 # E4M3 bit pattern of NaN (S.1111.111), the canary of an FP8 pool
 FP8_NAN = 0x7F
+
+# FP8 latent-cache row of the MLA path, in bytes: 512 E4M3 latent values
+# (8 blocks of 64), 64 bf16 rope values, 8 block-scale bytes, 8 zero bytes.
+MLA_FP8_LAT, MLA_FP8_ROPE = 512, 64
+MLA_FP8_SCALES = MLA_FP8_LAT + 2 * MLA_FP8_ROPE          # offset of the scale bytes
+MLA_FP8_ROW = MLA_FP8_SCALES + 16
+
+
+def _fp8_mla_rows(gen: torch.Generator, pages: int, page_size: int) -> torch.Tensor:
+    """Random FP8 latent-cache rows [pages, page_size, MLA_FP8_ROW] uint8:
+    latent bytes are E4M3 codes of N(0, 1) * 112 (torch's conversion, clamped
+    to +-448), scale bytes uniform in 118..121 (block scales 2^-9 .. 2^-6, so
+    the latent values are about N(0, 1) * 0.2 .. 1.75), the rope part bf16
+    normals, the padding zero."""
+    rows = torch.zeros(pages, page_size, MLA_FP8_ROW, dtype=torch.uint8)
+    rows[..., :MLA_FP8_LAT] = _normal_fp8(gen, (pages, page_size, MLA_FP8_LAT), 1.0 / 112.0)
+    rope = _normal_bf16(gen, (pages, page_size, MLA_FP8_ROPE))
+    rows[..., MLA_FP8_LAT:MLA_FP8_SCALES] = rope.view(torch.uint8)
+    rows[..., MLA_FP8_SCALES:MLA_FP8_SCALES + MLA_FP8_LAT // 64] = torch.randint(
+        118, 122, (pages, page_size, MLA_FP8_LAT // 64), generator=gen, dtype=torch.int64).to(torch.uint8)
+    return rows
+
+
+def _poison_fp8_rows(rows: torch.Tensor, sel) -> None:
+    """NaN canaries in FP8 latent rows: E4M3 NaN latent bytes and bf16 NaN
+    rope values (0x7FC0)."""
+    rows[sel + (slice(0, MLA_FP8_LAT),)] = FP8_NAN
+    rope = rows[sel + (slice(MLA_FP8_LAT, MLA_FP8_SCALES),)]
+    rope[..., 0::2] = 0xC0
+    rope[..., 1::2] = 0x7F
+    rows[sel + (slice(MLA_FP8_LAT, MLA_FP8_SCALES),)] = rope
 
 
 def _normal_fp8(gen: torch.Generator, shape, scale: float) -> torch.Tensor:
@@ -303,7 +337,7 @@ def make_mla_case(*, context_lens: Sequence[int] = (), num_heads: int, page_size
                   max_pages: Optional[int] = None, pool_pages: Optional[int] = None,
                   w_std: float = 0.02, scale: Optional[float] = None, poison: bool = True,
                   name: str = "custom", ctx_draw: Optional[tuple] = None,
-                  batch: Optional[int] = None) -> MlaCase:
+                  batch: Optional[int] = None, cache_dtype: str = "bf16") -> MlaCase:
     gen = torch.Generator().manual_seed(int(seed))
     if ctx_draw is not None:
         lo, hi = ctx_draw
@@ -317,7 +351,13 @@ def make_mla_case(*, context_lens: Sequence[int] = (), num_heads: int, page_size
     B = len(ctx)
     q_nope = _normal_bf16(gen, (B, num_heads, d_nope))
     q_rope = _normal_bf16(gen, (B, num_heads, d_rope))
-    cache = _normal_bf16(gen, (pool_pages, page_size, d_lat + d_rope))
+    if cache_dtype == "fp8":
+        assert (d_lat, d_rope) == (MLA_FP8_LAT, MLA_FP8_ROPE)
+        cache = _fp8_mla_rows(gen, pool_pages, page_size)
+    elif cache_dtype == "bf16":
+        cache = _normal_bf16(gen, (pool_pages, page_size, d_lat + d_rope))
+    else:
+        raise ValueError(cache_dtype)
     w_uk = _normal_bf16(gen, (num_heads, d_nope, d_lat), w_std)
     w_uv = _normal_bf16(gen, (num_heads, d_v, d_lat), w_std)
     if poison:
@@ -326,15 +366,22 @@ def make_mla_case(*, context_lens: Sequence[int] = (), num_heads: int, page_size
             k = (n + page_size - 1) // page_size
             if k:
                 live[bt[b, :k].long()] = True
-                cache[int(bt[b, k - 1]), n - (k - 1) * page_size:, :] = float("nan")
-        cache[~live] = float("nan")
+                tail = (int(bt[b, k - 1]), slice(n - (k - 1) * page_size, None))
+                if cache_dtype == "fp8":
+                    _poison_fp8_rows(cache, tail)
+                else:
+                    cache[tail + (slice(None),)] = float("nan")
+        if cache_dtype == "fp8":
+            _poison_fp8_rows(cache, (~live,))
+        else:
+            cache[~live] = float("nan")
     qk_dim = d_nope + d_rope
     return MlaCase(q_nope=q_nope, q_rope=q_rope, cache=cache, w_uk=w_uk, w_uv=w_uv,
                    block_table=bt, context_lens=torch.tensor(ctx, dtype=torch.int32),
                    num_pages=pool_pages, page_size=page_size, d_nope=d_nope, d_rope=d_rope,
                    d_lat=d_lat, d_v=d_v,
                    scale=(1.0 / math.sqrt(qk_dim)) if scale is None else scale,
-                   name=name, seed=seed)
+                   name=name, seed=seed, cache_dtype=cache_dtype)
 
 
 # ---- the five named workloads ------------------------------------------------
@@ -395,5 +442,11 @@ def mla(poison: bool = True, seed: int = SEED_BASE + 5) -> MlaCase:
                          seed=seed, poison=poison, name="mla")
 
 
+def mla_fp8(poison: bool = True, seed: int = SEED_BASE + 8) -> MlaCase:
+    """The mla shape over an FP8 latent cache."""
+    return make_mla_case(ctx_draw=(1024, 8192), batch=16, num_heads=128, page_size=64,
+                         seed=seed, poison=poison, name="mla_fp8", cache_dtype="fp8")
+
+
 NAMED = {"tiny": tiny, "llama": llama, "d256w": d256w, "long": long_ctx, "mla": mla,
-         "llama_fp8": llama_fp8, "llama_f32": llama_f32, "d512": d512}
+         "llama_fp8": llama_fp8, "llama_f32": llama_f32, "d512": d512, "mla_fp8": mla_fp8}

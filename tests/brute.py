@@ -34,6 +34,18 @@ def fp8_pool_f64(pool: torch.Tensor, scale: float) -> np.ndarray:
     return pool.detach().cpu().contiguous().view(torch.float8_e4m3fn).to(torch.float64).numpy() * scale
 
 
+def mla_fp8_rows_f64(rows: torch.Tensor, d_lat: int = 512, d_rope: int = 64) -> np.ndarray:
+    """Values [P, S, d_lat + d_rope] of FP8 latent-cache rows (uint8): the
+    E4M3 latent decoded by torch times 2^(scale byte - 127) of its 64-block,
+    then the bf16 rope part."""
+    r = rows.detach().cpu().contiguous()
+    lat = r[..., :d_lat].contiguous().view(torch.float8_e4m3fn).to(torch.float64)
+    sb = r[..., d_lat + 2 * d_rope:d_lat + 2 * d_rope + d_lat // 64].to(torch.float64)
+    lat = lat * torch.exp2(sb - 127.0).repeat_interleave(64, dim=-1)
+    rope = r[..., d_lat:d_lat + 2 * d_rope].contiguous().view(torch.bfloat16).to(torch.float64)
+    return torch.cat([lat, rope], dim=-1).numpy()
+
+
 def dense_attention(case, window=None):
     """(out [B,Hq,D], lse [B,Hq]) in float64 over materialised K/V."""
     w = case.window if window is None else window

@@ -38,6 +38,15 @@ builds with a planted mistake (at least one must fail).
                        for bit
   f32pool_bruteforce   f32-pool decode == float64 dense attention (full float32
                        mantissas, windows, both layouts)
+  e4m3_encode          E4M3 encoding: hand-computed ties (to the even code),
+                       == torch.float8_e4m3fn's conversion over every midpoint
+                       and a random sweep, decode(encode(v)) == v on every code
+  mla_fp8_insert       FP8 latent rows: each block exponent is the smallest e
+                       with 448 * 2^e >= absmax (exact test), element bytes ==
+                       torch's conversion of x * 2^-e, rope bits, zero padding,
+                       other rows untouched
+  mla_fp8_equals_bf16  MLA over an FP8 cache == the bf16 MLA oracle over the
+                       cache dequantized by torch, bit for bit
 """
 from __future__ import annotations
 
@@ -512,6 +521,92 @@ def f32pool_bruteforce(o):
         assert np.abs(lse[fin] - ref_lse[fin]).max() < F64_TOL
 
 
+def e4m3_encode(o):
+    # hand-computed from the OCP definition: ties go to the even code
+    want = {0.0: 0x00, 1.0: 0x38, 1.0625: 0x38, 1.1875: 0x3A, -3.0: 0xC4, 448.0: 0x7E,
+            440.0: 0x7E, 432.0: 0x7E, 424.0: 0x7D, 2.0**-10: 0x00, 3 * 2.0**-10: 0x02,
+            2.0**-6 - 2.0**-10: 0x08, -(2.0**-9): 0x81, 0.3: 0x2A}
+    for v, b in want.items():
+        assert o.e4m3_encode(v) == b, (v, hex(o.e4m3_encode(v)), hex(b))
+    assert o.e4m3_encode(-0.0) == 0x80
+    # every finite code round-trips
+    for b in range(256):
+        if (b & 0x7F) != 0x7F:
+            assert o.e4m3_encode(o.e4m3_value(b)) == b, hex(b)
+    # against torch's round-to-nearest-even conversion: every midpoint between
+    # neighbouring codes (and its negative) and a random sweep of +-448
+    vals = torch.arange(0x7F, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64)
+    mids = (vals[1:] + vals[:-1]) / 2
+    gen = torch.Generator().manual_seed(7190)
+    sweep = (torch.rand(4000, generator=gen, dtype=torch.float64) * 2 - 1) * 448.0
+    x = torch.cat([mids, -mids, sweep, sweep * 2.0**-8]).to(torch.float32)
+    ref = x.to(torch.float8_e4m3fn).view(torch.uint8).tolist()
+    got = [o.e4m3_encode(float(v)) for v in x.tolist()]
+    bad = [(float(x[i]), got[i], ref[i]) for i in range(len(ref)) if got[i] != ref[i]]
+    assert not bad, bad[:5]
+
+
+def mla_fp8_insert(o):
+    gen = torch.Generator().manual_seed(7200)
+    T, P, S = 24, 4, 8
+    x = torch.randn(T, 512, generator=gen, dtype=torch.float64)
+    # per-block magnitudes from 2^-140 to 2^40; one all-zero block; a block
+    # whose absmax is exactly 448; a block of exact E4M3 ties at scale 1
+    mag = torch.exp2(torch.randint(-140, 41, (T, 8), generator=gen).to(torch.float64))
+    x = x * mag.repeat_interleave(64, dim=1)
+    x[0, 64:128] = 0.0
+    x[1, :64] = 1.0
+    x[1, 0] = 448.0
+    x[2, :64] = torch.tensor([1.0625, 1.1875, -3.0, 2.0**-10, 3 * 2.0**-10, 432.0, 448.0] * 9 + [1.0])
+    kv_c = x.to(torch.bfloat16)
+    k_pe = torch.randn(T, 64, generator=gen).to(torch.bfloat16)
+    cache = torch.randint(0, 256, (P, S, 656), generator=gen, dtype=torch.int64).to(torch.uint8)
+    perm = torch.randperm(P * S, generator=gen)[:T - 2]
+    slots = torch.cat([perm, torch.tensor([-1, P * S])])
+    new = o.mla_cache_insert_fp8(kv_c, k_pe, cache, slots)
+    xs = kv_c.to(torch.float64)
+    touched = set()
+    for i, sl in enumerate(slots.tolist()):
+        if not 0 <= sl < P * S:
+            continue
+        touched.add(sl)
+        row = new[sl // S, sl % S]
+        for j in range(8):
+            blk = xs[i, 64 * j:64 * (j + 1)]
+            e = int(row[640 + j]) - 127
+            a = float(blk.abs().max())
+            if a == 0.0 or a <= 448.0 * 2.0**-126:
+                assert e == -126, (i, j, a, e)
+            else:   # the smallest e with 448 * 2^e >= absmax
+                assert 448.0 * 2.0**(e - 1) < a <= 448.0 * 2.0**e, (i, j, a, e)
+            q = (blk * 2.0**-e).to(torch.float32)
+            ref = q.to(torch.float8_e4m3fn).view(torch.uint8)
+            assert torch.equal(row[64 * j:64 * (j + 1)], ref), (i, j)
+        assert torch.equal(row[512:640], k_pe[i].contiguous().view(torch.uint8))
+        assert int(row[648:].sum()) == 0
+    s0 = int(slots[0])                  # token 0's zero block 1 takes the clamped exponent
+    assert int(new[s0 // S, s0 % S, 641]) == -126 + 127
+    for sl in range(P * S):
+        if sl not in touched:
+            assert torch.equal(new[sl // S, sl % S], cache[sl // S, sl % S]), sl
+
+
+def mla_fp8_equals_bf16(o):
+    from brute import mla_fp8_rows_f64
+    for seed, ctx, page in ((7210, (0, 1, 17, 40), 16), (7211, (63, 64, 65), 64)):
+        c8 = make_mla_case(context_lens=ctx, num_heads=5, page_size=page, seed=seed,
+                           cache_dtype="fp8")
+        deq = torch.from_numpy(mla_fp8_rows_f64(c8.cache))
+        c16 = c8.to("cpu")
+        c16.cache_dtype = "bf16"
+        c16.cache = deq.to(torch.bfloat16)
+        # the dequantized values are exact in bf16 (4 significant bits, power-of-two scale)
+        assert torch.equal(c16.cache.to(torch.float64).nan_to_num(7.0), deq.nan_to_num(7.0))
+        out8, lse8 = o.mla_fp8(c8)
+        out16, lse16, _ = o.mla(c16, "f64")
+        assert np.array_equal(out8, out16) and np.array_equal(lse8, lse16), seed
+
+
 PINS = {
     "dense_bruteforce": dense_bruteforce,
     "single_token": single_token,
@@ -535,6 +630,9 @@ PINS = {
     "fp8_bruteforce": fp8_bruteforce,
     "f32pool_equals_bf16": f32pool_equals_bf16,
     "f32pool_bruteforce": f32pool_bruteforce,
+    "e4m3_encode": e4m3_encode,
+    "mla_fp8_insert": mla_fp8_insert,
+    "mla_fp8_equals_bf16": mla_fp8_equals_bf16,
 }
 
 

@@ -30,6 +30,8 @@ MUTATIONS = {
     14: "E4M3 exponent bias 8",
     15: "FP8 K and V scales swapped",
     16: "f32-pool V rows one token late",
+    17: "FP8 MLA block exponent rounded down",
+    18: "FP8 MLA block scale 2^(byte - 128)",
 }
 
 
