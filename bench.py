@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama",
                     choices=["tiny", "llama", "d256w", "long", "mla", "verify", "insert",
-                             "llama_fp8", "llama_f32", "d512"])
+                             "llama_fp8", "llama_f32", "d512", "mla_fp8"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run K device-to-device copies of a 1 GiB buffer instead (reference "
@@ -89,7 +89,7 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "copies": a.steps}), flush=True)
         return 0
-    if a.workload == "mla":
+    if a.workload in ("mla", "mla_fp8"):
         return bench_mla(a, torch, pb, wl, dev)
     if a.workload == "verify":
         return bench_verify(a, torch, pb, wl, dev)
@@ -353,8 +353,9 @@ def bench_insert(a, torch, pb, wl, dev) -> int:
 
 
 def bench_mla(a, torch, pb, wl, dev) -> int:
-    log("generating workload mla (seeded) ...")
-    case = wl.mla(poison=False)
+    fp8 = a.workload == "mla_fp8"
+    log(f"generating workload {a.workload} (seeded) ...")
+    case = wl.mla_fp8(poison=False) if fp8 else wl.mla(poison=False)
     dc = case.to(dev)
     B, H = case.batch, case.num_heads
     out = torch.empty((B, H, case.d_v), dtype=torch.bfloat16, device=dev)
@@ -362,9 +363,11 @@ def bench_mla(a, torch, pb, wl, dev) -> int:
                      dtype=torch.uint8, device=dev)
     layout = pb.kv_layout(dc.cache, "PSR")
 
+    decode = pb.mla_absorbed_decode_fp8 if fp8 else pb.mla_absorbed_decode
+
     def step(i):
-        pb.mla_absorbed_decode(dc.q_nope, dc.q_rope, dc.cache, layout, dc.w_uk, dc.w_uv,
-                               dc.block_table, dc.context_lens, dc.scale, out, ws)
+        decode(dc.q_nope, dc.q_rope, dc.cache, layout, dc.w_uk, dc.w_uv, dc.block_table,
+               dc.context_lens, dc.scale, out, ws)
 
     stream = torch.cuda.current_stream()
     for i in range(a.warmup):
@@ -392,7 +395,10 @@ def bench_mla(a, torch, pb, wl, dev) -> int:
                              int(os.environ.get("OMP_NUM_THREADS", "16") or 16)))
         o.set_threads(threads)
         t = time.time()
-        o.mla(case, "f64")
+        if fp8:
+            o.mla_fp8(case)
+        else:
+            o.mla(case, "f64")
         sec = time.time() - t
         cpu = {"value": round(nbytes / sec / 1e9, 3), "unit": "GB/s", "cores": threads,
                "kind": "oracle", "sample": f"whole workload ({B} seqs, {keys} keys), float64 "
@@ -403,18 +409,23 @@ def bench_mla(a, torch, pb, wl, dev) -> int:
         "warmup": a.warmup, "ms_per_step": round(ms_per_step, 5),
         "us_per_call": round(ms_per_step * 1e3, 2),
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "storage_dtype": "bf16",
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "storage_dtype": ("e4m3 latent (one power-of-two scale per 64) + bf16 rope, 656 B/token"
+                          if fp8 else "bf16"),
         "data": "synthetic",
-        "config": {"workload": "absorbed MLA decode, bs16, 128 heads, 512+64 latent, page 64, "
-                               "ctx U[1024,8192]", "sum_context": keys,
+        "config": {"workload": ("absorbed MLA decode over an FP8 latent cache, " if fp8 else
+                                "absorbed MLA decode, ") +
+                               "bs16, 128 heads, 512+64 latent, page 64, ctx U[1024,8192]",
+                   "sum_context": keys,
                    "algorithmic_bytes": nbytes, "algorithmic_flops": flops},
         "call_us": {"mean": round(call_mean * 1e3, 2),
                     "p10": round(sorted(call_ms)[len(call_ms) // 10] * 1e3, 2),
                     "p90": round(sorted(call_ms)[(9 * len(call_ms)) // 10] * 1e3, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic("mla_absorbed_decode_bs16_h128"),
-                     "kernel": "mla_absorbed_decode call: absorb + split + merge/W_UV kernels",
+                     "traffic": None if fp8 else recorded_traffic("mla_absorbed_decode_bs16_h128"),
+                     "kernel": ("mla_absorbed_decode_fp8" if fp8 else "mla_absorbed_decode") +
+                               " call: absorb + split + merge/W_UV kernels",
                      "algorithmic_bytes_per_launch": nbytes,
                      "mfma_tflops": round(flops / (call_mean * 1e-3) / 1e12, 2)},
         "cpu_baseline": cpu,

@@ -353,6 +353,52 @@ PA_API int mla_cache_insert(const void* kv_c, int64_t c_stride, const void* k_pe
                             int64_t pe_stride, void* kv_cache, const pa_kv_layout* cache,
                             const int64_t* slots, int32_t num_tokens, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * FP8 MLA latent cache.
+ *
+ * The fp8_ds_mla quantization of the pages [vllm.cpp kernel matrix, row
+ * KERNEL-KV-CACHE-DSA: E4M3 elements in blocks of 64, one UE8M0 power-of-two
+ * scale per block, exponent ceil(log2(absmax / 448)) stored as exponent +
+ * 127, rope in bf16; dequant read e4m3 * 2^(byte - 127)], applied to the
+ * 512 + 64 latent of this library's MLA.  One row per token, 656 bytes:
+ *   [0, 512)    the latent as E4M3 (OCP e4m3fn), block j = elements 64j..64j+63
+ *   [512, 640)  the rope part, 64 bf16
+ *   [640, 648)  scale byte of block j at 640 + j
+ *   [648, 656)  zero
+ * The cache layout has num_kv_heads 1 and head_dim 656, with page_stride and
+ * token_stride in BYTES (positive multiples of 16, token_stride >= 656).
+ * Element value: e4m3(byte) * 2^(scale byte - 127).  Scale bytes are 1..254
+ * as written by mla_cache_insert_fp8; other values are outside the contract.
+ * ------------------------------------------------------------------------- */
+
+/* mla_cache_insert_fp8 -- quantize new tokens' latent rows into the FP8
+ * cache.  Per 64-block of kv_c[i][0:512]: exponent e = the smallest integer
+ * with 448 * 2^e >= max |x| over the block (computed exactly), clamped to
+ * [-126, 127] (an all-zero block takes -126); element byte = the E4M3 value
+ * nearest x * 2^-e, ties to the even code, sign bit from x.  k_pe[i][0:64]
+ * is copied bit for bit.  Sources as for mla_cache_insert (bf16, strides in
+ * elements, multiples of 8, 16-byte aligned); non-finite inputs give
+ * unspecified bytes.  Slots outside the cache are skipped.  Returns PA_OK or
+ * an error code (nothing launched). */
+PA_API int mla_cache_insert_fp8(const void* kv_c, int64_t c_stride, const void* k_pe,
+                                int64_t pe_stride, void* kv_cache, const pa_kv_layout* cache,
+                                const int64_t* slots, int32_t num_tokens, void* stream);
+
+/* mla_absorbed_decode_fp8 -- mla_absorbed_decode over the FP8 latent cache.
+ * Each row is widened to bf16 on the way into the workgroup's shared tile
+ * (exact for every value in bf16's normal range), then the computation is
+ * mla_absorbed_decode's over the dequantized latent and rope.  Latent bytes
+ * read per key: 656 instead of 1152.  Workspace as mla_absorbed_decode
+ * (mla_absorbed_decode_workspace_size with the same shapes); other arguments,
+ * determinism and error codes as mla_absorbed_decode. */
+PA_API int mla_absorbed_decode_fp8(const void* q_nope, const void* q_rope, const void* kv_cache,
+                                   const pa_kv_layout* cache, const void* w_uk, const void* w_uv,
+                                   const int32_t* block_table, int32_t block_table_stride,
+                                   const int32_t* context_lens, int32_t batch, int32_t num_heads,
+                                   int32_t max_pages_per_seq, float scale,
+                                   int32_t partition_size, void* out, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
 /* Text describing the last non-zero status returned on the calling thread
  * ("" if none).  The pointer stays valid until the next call on that thread. */
 PA_API const char* pa_last_error(void);

@@ -25,7 +25,7 @@ EXPORTS = ("pa_decode", "pa_decode_splitkv", "pa_merge_lse", "pa_decode_workspac
            "pa_decode_partition_size", "mla_absorbed_decode",
            "mla_absorbed_decode_workspace_size", "pa_kv_insert", "mla_cache_insert",
            "pa_decode_multiquery", "pa_decode_multiquery_workspace_size", "pa_decode_fp8",
-           "pa_decode_f32", "pa_last_error")
+           "pa_decode_f32", "mla_cache_insert_fp8", "mla_absorbed_decode_fp8", "pa_last_error")
 
 
 class PaError(RuntimeError):
@@ -68,6 +68,8 @@ def _load() -> C.CDLL:
     lib.mla_absorbed_decode.argtypes = [vp, vp, vp, kvp, vp, vp, i32p, i32, i32p, i32, i32, i32,
                                         C.c_float, i32, vp, vp, C.c_size_t, vp]
     lib.mla_absorbed_decode.restype = C.c_int
+    lib.mla_absorbed_decode_fp8.argtypes = list(lib.mla_absorbed_decode.argtypes)
+    lib.mla_absorbed_decode_fp8.restype = C.c_int
     lib.mla_absorbed_decode_workspace_size.argtypes = [i32] * 5
     lib.mla_absorbed_decode_workspace_size.restype = C.c_size_t
     lib.pa_decode_multiquery.argtypes = [vp, vp, vp, kvp, i32p, i32, i32p, i32, i32, i32, i32,
@@ -80,6 +82,8 @@ def _load() -> C.CDLL:
     lib.pa_kv_insert.restype = C.c_int
     lib.mla_cache_insert.argtypes = [vp, i64, vp, i64, vp, kvp, vp, i32, vp]
     lib.mla_cache_insert.restype = C.c_int
+    lib.mla_cache_insert_fp8.argtypes = [vp, i64, vp, i64, vp, kvp, vp, i32, vp]
+    lib.mla_cache_insert_fp8.restype = C.c_int
     lib.pa_last_error.argtypes = []
     lib.pa_last_error.restype = C.c_char_p
     return lib
@@ -249,27 +253,42 @@ def pa_merge_lse(part_out, part_max, part_sum, context_lens, partition_size: int
     _check(rc)
 
 
-def mla_absorbed_decode(q_nope, q_rope, kv_cache, cache: KvLayout, w_uk, w_uv, block_table,
-                        context_lens, scale: float, out, workspace, partition_size: int = 0,
-                        max_pages_per_seq=None, stream=None) -> None:
+def _mla_decode(fn, cache_dtype, q_nope, q_rope, kv_cache, cache, w_uk, w_uv, block_table,
+                context_lens, scale, out, workspace, partition_size, max_pages_per_seq, stream):
     for t, n in ((q_nope, "q_nope"), (q_rope, "q_rope"), (w_uk, "w_uk"), (w_uv, "w_uv"),
                  (block_table, "block_table"), (context_lens, "context_lens"), (out, "out")):
         _contig(t, n)
     B, H = q_nope.shape[0], q_nope.shape[1]
     maxp = block_table.shape[1] if max_pages_per_seq is None else max_pages_per_seq
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    rc = LIB.mla_absorbed_decode(_ptr(q_nope, torch.bfloat16, "q_nope"),
-                                 _ptr(q_rope, torch.bfloat16, "q_rope"),
-                                 _ptr(kv_cache, torch.bfloat16, "kv_cache"), C.byref(cache),
-                                 _ptr(w_uk, torch.bfloat16, "w_uk"),
-                                 _ptr(w_uv, torch.bfloat16, "w_uv"),
-                                 _ptr(block_table, torch.int32, "block_table"),
-                                 block_table.stride(0),
-                                 _ptr(context_lens, torch.int32, "context_lens"), B, H, maxp,
-                                 float(scale), int(partition_size),
-                                 _ptr(out, torch.bfloat16, "out"), _ptr(workspace), ws_bytes,
-                                 _stream(stream))
+    rc = fn(_ptr(q_nope, torch.bfloat16, "q_nope"), _ptr(q_rope, torch.bfloat16, "q_rope"),
+            _ptr(kv_cache, cache_dtype, "kv_cache"), C.byref(cache),
+            _ptr(w_uk, torch.bfloat16, "w_uk"), _ptr(w_uv, torch.bfloat16, "w_uv"),
+            _ptr(block_table, torch.int32, "block_table"), block_table.stride(0),
+            _ptr(context_lens, torch.int32, "context_lens"), B, H, maxp, float(scale),
+            int(partition_size), _ptr(out, torch.bfloat16, "out"), _ptr(workspace), ws_bytes,
+            _stream(stream))
     _check(rc)
+
+
+def mla_absorbed_decode(q_nope, q_rope, kv_cache, cache: KvLayout, w_uk, w_uv, block_table,
+                        context_lens, scale: float, out, workspace, partition_size: int = 0,
+                        max_pages_per_seq=None, stream=None) -> None:
+    _mla_decode(LIB.mla_absorbed_decode, torch.bfloat16, q_nope, q_rope, kv_cache, cache, w_uk,
+                w_uv, block_table, context_lens, scale, out, workspace, partition_size,
+                max_pages_per_seq, stream)
+
+
+MLA_FP8_ROW = 656   # bytes per token of the FP8 latent cache
+
+
+def mla_absorbed_decode_fp8(q_nope, q_rope, kv_cache, cache: KvLayout, w_uk, w_uv, block_table,
+                            context_lens, scale: float, out, workspace, partition_size: int = 0,
+                            max_pages_per_seq=None, stream=None) -> None:
+    """kv_cache: uint8 FP8 latent rows (cache.head_dim 656, strides in bytes)."""
+    _mla_decode(LIB.mla_absorbed_decode_fp8, torch.uint8, q_nope, q_rope, kv_cache, cache, w_uk,
+                w_uv, block_table, context_lens, scale, out, workspace, partition_size,
+                max_pages_per_seq, stream)
 
 
 def _rows(t: torch.Tensor, name: str, ndim: int) -> None:
@@ -304,6 +323,22 @@ def mla_cache_insert(kv_c, k_pe, kv_cache, cache: KvLayout, slots, stream=None) 
                               _ptr(k_pe, torch.bfloat16, "k_pe"), k_pe.stride(0),
                               _ptr(kv_cache, torch.bfloat16, "kv_cache"), C.byref(cache),
                               _ptr(slots, torch.int64, "slots"), kv_c.shape[0], _stream(stream))
+    _check(rc)
+
+
+def mla_cache_insert_fp8(kv_c, k_pe, kv_cache, cache: KvLayout, slots, stream=None) -> None:
+    """As mla_cache_insert, into the FP8 latent cache (uint8 rows of 656
+    bytes; cache strides in bytes)."""
+    _rows(kv_c, "kv_c", 2)
+    _rows(k_pe, "k_pe", 2)
+    if kv_c.shape[0] != k_pe.shape[0]:
+        raise ValueError("kv_c and k_pe must have the same number of rows")
+    _contig(slots, "slots")
+    rc = LIB.mla_cache_insert_fp8(_ptr(kv_c, torch.bfloat16, "kv_c"), kv_c.stride(0),
+                                  _ptr(k_pe, torch.bfloat16, "k_pe"), k_pe.stride(0),
+                                  _ptr(kv_cache, torch.uint8, "kv_cache"), C.byref(cache),
+                                  _ptr(slots, torch.int64, "slots"), kv_c.shape[0],
+                                  _stream(stream))
     _check(rc)
 
 

@@ -25,6 +25,14 @@
 // keys T/2 units apart, i.e. in blocks i and i + nb/2, which the dispatcher
 // places on the same XCD (nb a multiple of 16), so the second read of a
 // cache tile is served by that XCD's L2.
+//
+// FP8 latent cache (mla_absorbed_decode_fp8): rows of 656 bytes hold the
+// latent as E4M3 in blocks of 64 with one power-of-two scale byte per block
+// and the rope part in bf16 [vllm.cpp kernel matrix, row KERNEL-KV-CACHE-DSA:
+// the fp8_ds_mla dequant read, e4m3 * 2^(scale byte - 127), rope bf16].  The
+// staging lanes widen each 16-byte latent chunk to bf16 with the block's
+// scale (v_cvt_scalef32_pk_bf16_fp8, exact for any result in bf16's normal
+// range), so the LDS tile, and everything after it, is the bf16 path's.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -195,6 +203,18 @@ __device__ __forceinline__ void mla_locate(const int32_t* ctx, int batch, int64_
   pre_out = base;
 }
 
+// 16 E4M3 bytes times the power-of-two scale s -> 16 bf16, bytes 0..7 into lo.
+__device__ __forceinline__ uint32_t fp8x2_bf16_scaled(uint32_t w, float s, bool high_word) {
+  return __builtin_bit_cast(uint32_t, high_word ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, s, true)
+                                                : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, s, false));
+}
+__device__ __forceinline__ void fp8x16_bf16_scaled(uint4 x, float s, uint4& lo, uint4& hi) {
+  lo = make_uint4(fp8x2_bf16_scaled(x.x, s, false), fp8x2_bf16_scaled(x.x, s, true),
+                  fp8x2_bf16_scaled(x.y, s, false), fp8x2_bf16_scaled(x.y, s, true));
+  hi = make_uint4(fp8x2_bf16_scaled(x.z, s, false), fp8x2_bf16_scaled(x.z, s, true),
+                  fp8x2_bf16_scaled(x.w, s, false), fp8x2_bf16_scaled(x.w, s, true));
+}
+
 // Attention of the heads of group hg of sequence b over keys [begin, end);
 // writes the normalised partial, its max and its sum to slot.
 // Score D layout: lane l holds S^T[MFMA row 4*(l/16)+i (+16)][head l%16]; MFMA
@@ -205,6 +225,7 @@ __device__ __forceinline__ void mla_locate(const int32_t* ctx, int batch, int64_
 // key-major tile.  The softmax keeps a per-head reference max and rescales
 // the accumulators only when a score exceeds it by more than 8 (log2
 // domain), so P stays below 2^8 and rescaling is rare.
+template <bool F8>
 __device__ __forceinline__ void mla_segment(const MlaParams& p, int b, int hg, int begin, int end,
                                             int64_t slot, uint16_t (*crow2)[kTileKeys][kRowPad],
                                             uint16_t (*qlo_s)[kLat + 8]) {
@@ -224,27 +245,56 @@ __device__ __forceinline__ void mla_segment(const MlaParams& p, int b, int hg, i
   // Staging of one tile: 32 keys x 72 chunks of 16 B.  Wave w stages keys
   // 8w .. 8w+7, lane l key 8w + l/8 and its chunks l%8 + 8k (k < 9), so each
   // lane resolves one page per tile and the chunk offsets are constants.
+  // FP8 rows: lane l loads E4M3 latent chunks l%8 + 8k (k < 4, 16 dims each,
+  // block (l%8)/4 + 2k), rope chunk l%8 and the 8 scale bytes.
   // The page of the next tile's key is fetched one tile ahead.
-  constexpr int kChunks = kRow / 8 / 8;   // 9
+  constexpr int kChunks = F8 ? 5 : kRow / 8 / 8;   // 16-byte loads per lane and tile
   const int skey = wave * 8 + (lane >> 3);
   const int schunk = lane & 7;
   uint4 stage[kChunks];
+  uint2 sbytes = make_uint2(0, 0);   // FP8: the row's block-scale bytes
   auto page_of = [&](int t0) -> int {
     const int t = t0 + skey;
     return (t >= begin && t < end) ? bt[t >> p.page_shift] : -1;
   };
   auto load_tile = [&](int t0, int page) {
-    const uint16_t* src = p.cache + static_cast<int64_t>(max(page, 0)) * p.page_stride +
-                          static_cast<int64_t>((t0 + skey) & (p.page_size - 1)) * p.token_stride +
-                          schunk * 8;
+    if constexpr (F8) {
+      const char* src = reinterpret_cast<const char*>(p.cache) +
+                        static_cast<int64_t>(max(page, 0)) * p.page_stride +
+                        static_cast<int64_t>((t0 + skey) & (p.page_size - 1)) * p.token_stride;
+      const uint16_t* lat = reinterpret_cast<const uint16_t*>(src + 16 * schunk);
 #pragma unroll
-    for (int k = 0; k < kChunks; ++k)
-      stage[k] = page >= 0 ? load16(src + 64 * k) : make_uint4(0, 0, 0, 0);
+      for (int k = 0; k < 4; ++k) stage[k] = page >= 0 ? load16(lat + 64 * k) : make_uint4(0, 0, 0, 0);
+      stage[4] = page >= 0 ? load16(reinterpret_cast<const uint16_t*>(src + kMlaFp8Rope + 16 * schunk))
+                           : make_uint4(0, 0, 0, 0);
+      sbytes = page >= 0 ? *reinterpret_cast<const uint2*>(src + kMlaFp8Scales) : make_uint2(0, 0);
+    } else {
+      const uint16_t* src = p.cache + static_cast<int64_t>(max(page, 0)) * p.page_stride +
+                            static_cast<int64_t>((t0 + skey) & (p.page_size - 1)) * p.token_stride +
+                            schunk * 8;
+#pragma unroll
+      for (int k = 0; k < kChunks; ++k)
+        stage[k] = page >= 0 ? load16(src + 64 * k) : make_uint4(0, 0, 0, 0);
+    }
   };
   auto store_tile = [&](uint16_t (*dst)[kRowPad]) {
+    if constexpr (F8) {
 #pragma unroll
-    for (int k = 0; k < kChunks; ++k)
-      *reinterpret_cast<uint4*>(&dst[skey][(schunk + 8 * k) * 8]) = stage[k];
+      for (int k = 0; k < 4; ++k) {
+        // block (schunk >> 2) + 2k: byte of sbytes.x (k < 2) or sbytes.y
+        const uint32_t word = k < 2 ? sbytes.x : sbytes.y;
+        const uint32_t sb = (word >> (8 * ((schunk >> 2) + 2 * (k & 1)))) & 0xffu;
+        uint4 lo, hi;
+        fp8x16_bf16_scaled(stage[k], u2f(sb << 23), lo, hi);
+        *reinterpret_cast<uint4*>(&dst[skey][16 * (schunk + 8 * k)]) = lo;
+        *reinterpret_cast<uint4*>(&dst[skey][16 * (schunk + 8 * k) + 8]) = hi;
+      }
+      *reinterpret_cast<uint4*>(&dst[skey][kLat + 8 * schunk]) = stage[4];
+    } else {
+#pragma unroll
+      for (int k = 0; k < kChunks; ++k)
+        *reinterpret_cast<uint4*>(&dst[skey][(schunk + 8 * k) * 8]) = stage[k];
+    }
   };
   const int first_tile = begin / kTileKeys;
   const int last_tile = (end - 1) / kTileKeys;
@@ -424,6 +474,7 @@ __device__ __forceinline__ void mla_segment(const MlaParams& p, int b, int hg, i
   }
 }
 
+template <bool F8>
 __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(const MlaParams p) {
   __shared__ __align__(16) uint16_t crow[2][kTileKeys][kRowPad];
   __shared__ __align__(16) uint16_t qlo_s[kGroup][kLat + 8];
@@ -461,7 +512,7 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(const MlaParams 
     const int begin = static_cast<int>(u - row_start);
     const int end = static_cast<int>(min(u1 - row_start, static_cast<int64_t>(n)));
     if (end > begin)
-      mla_segment(p, b, hg, begin, end, static_cast<int64_t>(hg) * p.batch + b + i, crow, qlo_s);
+      mla_segment<F8>(p, b, hg, begin, end, static_cast<int64_t>(hg) * p.batch + b + i, crow, qlo_s);
     u = row_start + n;
     pre += n;
     if (++b == p.batch) {
@@ -658,15 +709,19 @@ size_t mla_absorbed_decode_workspace_size(int32_t batch, int32_t num_heads,
   return plan.bytes;
 }
 
-int mla_absorbed_decode(const void* q_nope, const void* q_rope, const void* kv_cache,
-                        const pa_kv_layout* cache, const void* w_uk, const void* w_uv,
-                        const int32_t* block_table, int32_t block_table_stride,
-                        const int32_t* context_lens, int32_t batch, int32_t num_heads,
-                        int32_t max_pages_per_seq, float scale, int32_t partition_size, void* out,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int mla_decode_impl(const void* q_nope, const void* q_rope, const void* kv_cache,
+                    const pa_kv_layout* cache, const void* w_uk, const void* w_uv,
+                    const int32_t* block_table, int32_t block_table_stride,
+                    const int32_t* context_lens, int32_t batch, int32_t num_heads,
+                    int32_t max_pages_per_seq, float scale, int32_t partition_size, void* out,
+                    void* workspace, size_t workspace_bytes, void* stream, bool fp8) {
   int rc = pa::check_mla(q_nope, q_rope, kv_cache, cache, w_uk, w_uv, block_table,
                          block_table_stride, context_lens, batch, num_heads, max_pages_per_seq,
-                         scale, partition_size, out);
+                         scale, partition_size, out, fp8);
   if (rc) return rc;
   pa::MlaPlan plan;
   if (!pa::plan_mla(batch, num_heads, max_pages_per_seq, cache->page_size, partition_size, &plan))
@@ -722,7 +777,10 @@ int mla_absorbed_decode(const void* q_nope, const void* q_rope, const void* kv_c
                      0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return pa::fail(PA_ERR_LAUNCH, std::string("absorb: ") + hipGetErrorString(e));
-  hipLaunchKernelGGL(pa::mla_split_kernel, dim3(p.split_grid), dim3(pa::kMlaThreads), 0, s, p);
+  if (fp8)
+    hipLaunchKernelGGL(pa::mla_split_kernel<true>, dim3(p.split_grid), dim3(pa::kMlaThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL(pa::mla_split_kernel<false>, dim3(p.split_grid), dim3(pa::kMlaThreads), 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return pa::fail(PA_ERR_LAUNCH, std::string("split: ") + hipGetErrorString(e));
   hipLaunchKernelGGL(pa::mla_merge_uv_kernel,
@@ -731,6 +789,32 @@ int mla_absorbed_decode(const void* q_nope, const void* q_rope, const void* kv_c
   e = hipGetLastError();
   if (e != hipSuccess) return pa::fail(PA_ERR_LAUNCH, std::string("merge: ") + hipGetErrorString(e));
   return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_absorbed_decode(const void* q_nope, const void* q_rope, const void* kv_cache,
+                        const pa_kv_layout* cache, const void* w_uk, const void* w_uv,
+                        const int32_t* block_table, int32_t block_table_stride,
+                        const int32_t* context_lens, int32_t batch, int32_t num_heads,
+                        int32_t max_pages_per_seq, float scale, int32_t partition_size, void* out,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  return mla_decode_impl(q_nope, q_rope, kv_cache, cache, w_uk, w_uv, block_table,
+                         block_table_stride, context_lens, batch, num_heads, max_pages_per_seq,
+                         scale, partition_size, out, workspace, workspace_bytes, stream, false);
+}
+
+int mla_absorbed_decode_fp8(const void* q_nope, const void* q_rope, const void* kv_cache,
+                            const pa_kv_layout* cache, const void* w_uk, const void* w_uv,
+                            const int32_t* block_table, int32_t block_table_stride,
+                            const int32_t* context_lens, int32_t batch, int32_t num_heads,
+                            int32_t max_pages_per_seq, float scale, int32_t partition_size,
+                            void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return mla_decode_impl(q_nope, q_rope, kv_cache, cache, w_uk, w_uv, block_table,
+                         block_table_stride, context_lens, batch, num_heads, max_pages_per_seq,
+                         scale, partition_size, out, workspace, workspace_bytes, stream, true);
 }
 
 }  // extern "C"

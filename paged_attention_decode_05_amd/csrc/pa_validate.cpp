@@ -206,7 +206,8 @@ int check_mla(const void* q_nope, const void* q_rope, const void* kv_cache,
               const pa_kv_layout* cache, const void* w_uk, const void* w_uv,
               const int32_t* block_table, int32_t block_table_stride,
               const int32_t* context_lens, int32_t batch, int32_t num_heads,
-              int32_t max_pages_per_seq, float scale, int32_t partition_size, const void* out) {
+              int32_t max_pages_per_seq, float scale, int32_t partition_size, const void* out,
+              bool fp8) {
   if (!q_nope || !q_rope || !kv_cache || !cache || !w_uk || !w_uv || !block_table ||
       !context_lens || !out)
     return fail(PA_ERR_NULL, "a required pointer is NULL");
@@ -222,18 +223,24 @@ int check_mla(const void* q_nope, const void* q_rope, const void* kv_cache,
     return fail(PA_ERR_SHAPE, "scale must be finite and > 0");
   if (static_cast<int64_t>(max_pages_per_seq) * cache->page_size > INT32_MAX / 2)
     return fail(PA_ERR_SHAPE, "max_pages_per_seq * page_size is too large");
-  if (cache->num_kv_heads != 1 || cache->head_dim != kMlaRow)
-    return fail(PA_ERR_UNSUPPORTED, "MLA cache must have num_kv_heads 1 and head_dim 576");
+  const int32_t row = fp8 ? kMlaFp8Row : kMlaRow;
+  if (cache->num_kv_heads != 1 || cache->head_dim != row)
+    return fail(PA_ERR_UNSUPPORTED, fp8 ? "FP8 MLA cache must have num_kv_heads 1 and head_dim 656 (bytes)"
+                                        : "MLA cache must have num_kv_heads 1 and head_dim 576");
   if (num_heads % kMlaHeadTile)
     return fail(PA_ERR_UNSUPPORTED, "num_heads must be a multiple of 16");
   if (!page_size_supported(cache->page_size))
     return fail(PA_ERR_UNSUPPORTED, "page_size must be 16, 32 or 64");
   if (partition_size < 0 || partition_size % kMlaKeyTile)
     return fail(PA_ERR_SHAPE, "partition_size must be 0 or a positive multiple of 64");
-  if (!mult8(cache->page_stride) || !mult8(cache->token_stride))
-    return fail(PA_ERR_ALIGN, "cache strides must be positive multiples of 8 elements");
-  if (cache->token_stride < kMlaRow)
-    return fail(PA_ERR_SHAPE, "cache token_stride must be >= 576");
+  const int64_t smul = fp8 ? 16 : 8;   // 16 bytes either way
+  if (cache->page_stride <= 0 || cache->page_stride % smul || cache->token_stride <= 0 ||
+      cache->token_stride % smul)
+    return fail(PA_ERR_ALIGN, fp8 ? "FP8 cache strides must be positive multiples of 16 bytes"
+                                  : "cache strides must be positive multiples of 8 elements");
+  if (cache->token_stride < row)
+    return fail(PA_ERR_SHAPE, fp8 ? "FP8 cache token_stride must be >= 656"
+                                  : "cache token_stride must be >= 576");
   if (static_cast<int64_t>(cache->page_size) * cache->token_stride > INT32_MAX / 4)
     return fail(PA_ERR_SHAPE, "cache token_stride too large");
   if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(kv_cache) || !aligned16(w_uk) ||
@@ -271,19 +278,25 @@ int check_kv_insert(const void* k_new, const void* v_new, int64_t src_token_stri
 
 int check_mla_insert(const void* kv_c, int64_t c_stride, const void* k_pe, int64_t pe_stride,
                      const void* kv_cache, const pa_kv_layout* cache, const int64_t* slots,
-                     int32_t num_tokens) {
+                     int32_t num_tokens, bool fp8) {
   if (!kv_c || !k_pe || !kv_cache || !cache || !slots)
     return fail(PA_ERR_NULL, "a required pointer is NULL");
   if (num_tokens < 0) return fail(PA_ERR_SHAPE, "num_tokens must be >= 0");
   if (cache->num_pages < 1 || cache->page_size < 1)
     return fail(PA_ERR_SHAPE, "cache: num_pages and page_size must be >= 1");
-  if (cache->num_kv_heads != 1 || cache->head_dim != kMlaRow)
-    return fail(PA_ERR_UNSUPPORTED, "MLA cache must have num_kv_heads 1 and head_dim 576");
-  if (!mult8(cache->page_stride) || !mult8(cache->token_stride) || !mult8(c_stride) ||
-      !mult8(pe_stride))
-    return fail(PA_ERR_ALIGN, "strides must be positive multiples of 8 elements");
-  if (cache->token_stride < kMlaRow || c_stride < kMlaLat || pe_stride < kMlaRope)
-    return fail(PA_ERR_SHAPE, "token_stride >= 576, c_stride >= 512 and pe_stride >= 64 required");
+  const int32_t row = fp8 ? kMlaFp8Row : kMlaRow;
+  if (cache->num_kv_heads != 1 || cache->head_dim != row)
+    return fail(PA_ERR_UNSUPPORTED, fp8 ? "FP8 MLA cache must have num_kv_heads 1 and head_dim 656 (bytes)"
+                                        : "MLA cache must have num_kv_heads 1 and head_dim 576");
+  const int64_t smul = fp8 ? 16 : 8;   // cache strides: 16 bytes either way
+  if (cache->page_stride <= 0 || cache->page_stride % smul || cache->token_stride <= 0 ||
+      cache->token_stride % smul || !mult8(c_stride) || !mult8(pe_stride))
+    return fail(PA_ERR_ALIGN, fp8 ? "FP8 cache strides must be positive multiples of 16 bytes, "
+                                    "source strides multiples of 8 elements"
+                                  : "strides must be positive multiples of 8 elements");
+  if (cache->token_stride < row || c_stride < kMlaLat || pe_stride < kMlaRope)
+    return fail(PA_ERR_SHAPE, fp8 ? "token_stride >= 656, c_stride >= 512 and pe_stride >= 64 required"
+                                  : "token_stride >= 576, c_stride >= 512 and pe_stride >= 64 required");
   if (!aligned16(kv_c) || !aligned16(k_pe) || !aligned16(kv_cache))
     return fail(PA_ERR_ALIGN, "kv_c, k_pe and kv_cache must be 16-byte aligned");
   return PA_OK;

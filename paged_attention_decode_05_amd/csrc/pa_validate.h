@@ -76,6 +76,12 @@ constexpr int32_t kMlaBlockHeads = 64;           // heads per split-kernel block
 constexpr int32_t kMlaMaxBlocks = 512;           // split blocks at the library's choice (>= CUs)
 constexpr int32_t kMlaMaxExplicitBlocks = 16384; // cap for an explicit partition size
 constexpr int32_t kMlaMinKeys = 128;             // keys per block below which fewer blocks are used
+// FP8 latent-cache row, in bytes: E4M3 latent (blocks of 64, one scale byte
+// each), bf16 rope, the scale bytes, zero padding to a 16-byte multiple.
+constexpr int32_t kMlaFp8Block = 64;
+constexpr int32_t kMlaFp8Rope = kMlaLat;                        // 512
+constexpr int32_t kMlaFp8Scales = kMlaLat + 2 * kMlaRope;       // 640
+constexpr int32_t kMlaFp8Row = kMlaFp8Scales + 16;              // 656
 
 struct MlaPlan {
   int32_t groups = 0;        // ceil(num_heads / 64)
@@ -86,11 +92,14 @@ struct MlaPlan {
 bool plan_mla(int32_t batch, int32_t num_heads, int32_t max_pages_per_seq, int32_t page_size,
               int32_t partition_size, MlaPlan* plan);
 
+// fp8: the cache holds FP8 rows (head_dim kMlaFp8Row, strides in bytes,
+// multiples of 16) instead of bf16 576-wide rows.
 int check_mla(const void* q_nope, const void* q_rope, const void* kv_cache,
               const pa_kv_layout* cache, const void* w_uk, const void* w_uv,
               const int32_t* block_table, int32_t block_table_stride,
               const int32_t* context_lens, int32_t batch, int32_t num_heads,
-              int32_t max_pages_per_seq, float scale, int32_t partition_size, const void* out);
+              int32_t max_pages_per_seq, float scale, int32_t partition_size, const void* out,
+              bool fp8 = false);
 
 int check_kv_insert(const void* k_new, const void* v_new, int64_t src_token_stride,
                     int64_t src_head_stride, const void* k_pool, const void* v_pool,
@@ -98,6 +107,6 @@ int check_kv_insert(const void* k_new, const void* v_new, int64_t src_token_stri
 
 int check_mla_insert(const void* kv_c, int64_t c_stride, const void* k_pe, int64_t pe_stride,
                      const void* kv_cache, const pa_kv_layout* cache, const int64_t* slots,
-                     int32_t num_tokens);
+                     int32_t num_tokens, bool fp8 = false);
 
 }  // namespace pa
