@@ -166,6 +166,33 @@ def test_mla_rejections():
     assert pb.mla_absorbed_decode_workspace_size(16, 100, 128, 64, 0) == 0
 
 
+def test_mla_fp8_rejections():
+    """FP8 latent rows are 656 bytes with byte strides in multiples of 16;
+    the bf16 row size is refused and vice versa."""
+    f8 = pb.KvLayout(1300, 64, 1, 656, 64 * 656, 0, 656)
+
+    def dec(cache, **kw):
+        a = dict(qn=FAKE, out=FAKE)
+        a.update(kw)
+        return pb.LIB.mla_absorbed_decode_fp8(a["qn"], FAKE, FAKE, C.byref(cache), FAKE, FAKE,
+                                              FAKE, 128, FAKE, 16, 128, 128, 0.072, 0, a["out"],
+                                              None, 0, None)
+    assert dec(f8) == PA["WORKSPACE"], pb.pa_last_error()
+    assert dec(f8, qn=None) == PA["NULL"]
+    assert dec(pb.KvLayout(1300, 64, 1, 576, 64 * 576, 0, 576)) == PA["UNSUPPORTED"]
+    assert dec(pb.KvLayout(1300, 64, 1, 656, 64 * 664, 0, 664)) == PA["ALIGN"]   # 664 % 16
+    assert dec(pb.KvLayout(1300, 64, 1, 656, 64 * 672, 0, 672)) == PA["WORKSPACE"]
+    assert _mla(cache=f8) == PA["UNSUPPORTED"]            # the bf16 entry point
+    ins = pb.LIB.mla_cache_insert_fp8
+    assert ins(None, 512, FAKE, 64, FAKE, C.byref(f8), FAKE, 4, None) == PA["NULL"]
+    assert ins(FAKE, 512, FAKE, 64, FAKE, C.byref(f8), FAKE, 0, None) == PA["OK"]
+    assert ins(FAKE, 500, FAKE, 64, FAKE, C.byref(f8), FAKE, 0, None) == PA["ALIGN"]
+    assert ins(FAKE, 512, FAKE, 64, FAKE, C.byref(pb.KvLayout(100, 64, 1, 576, 64 * 576, 0, 576)),
+               FAKE, 0, None) == PA["UNSUPPORTED"]
+    assert ins(FAKE, 512, FAKE, 64, FAKE, C.byref(pb.KvLayout(100, 64, 1, 656, 64 * 640, 0, 640)),
+               FAKE, 0, None) == PA["SHAPE"]             # token_stride < 656
+
+
 def _ins(kv=None, n=4, ts=256, hs=128, **kw):
     kv = kv or _kv()
     a = dict(k=FAKE, v=FAKE, kp=FAKE, vp=FAKE, sl=FAKE)
