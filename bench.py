@@ -209,8 +209,9 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": (recorded_traffic({"llama": "pa_decode_llama_bs64",
-                                          "llama_fp8": "pa_decode_fp8_llama_bs64"}[a.workload])
-                        if a.workload in ("llama", "llama_fp8") and a.rotate == 1 else None),
+                                          "llama_fp8": "pa_decode_fp8_llama_bs64",
+                                          "d512": "pa_decode_d512_bs64"}[a.workload])
+                        if a.workload in ("llama", "llama_fp8", "d512") and a.rotate == 1 else None),
             "kernel": ("pa_decode_fp8" if fp8 else "pa_decode_f32" if f32 else "pa_decode") +
                       " call: balanced_split_kernel + balanced_merge_kernel",
             "algorithmic_bytes_per_launch": int(mean_bytes),
@@ -423,7 +424,8 @@ def bench_mla(a, torch, pb, wl, dev) -> int:
                     "p90": round(sorted(call_ms)[(9 * len(call_ms)) // 10] * 1e3, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None if fp8 else recorded_traffic("mla_absorbed_decode_bs16_h128"),
+                     "traffic": recorded_traffic("mla_absorbed_decode_fp8_bs16_h128" if fp8
+                                                 else "mla_absorbed_decode_bs16_h128"),
                      "kernel": ("mla_absorbed_decode_fp8" if fp8 else "mla_absorbed_decode") +
                                " call: absorb + split + merge/W_UV kernels",
                      "algorithmic_bytes_per_launch": nbytes,
