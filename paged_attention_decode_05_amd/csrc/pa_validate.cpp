@@ -88,9 +88,11 @@ int check_gqa(const void* q, const void* k_pool, const void* v_pool, const pa_kv
   if (static_cast<double>(batch) * kv->num_kv_heads *
           static_cast<double>(max_keys(max_pages_per_seq, kv->page_size, 0)) > 1e15)
     return fail(PA_ERR_SHAPE, "batch * num_kv_heads * max keys is too large");
-  if (kv->page_stride > static_cast<int64_t>(UINT32_MAX / 2) ||
+  // the kernels hold one page's size in bytes in 32 bits
+  if (kv->page_stride * elem_bytes > static_cast<int64_t>(UINT32_MAX) ||
       kv->head_stride > static_cast<int64_t>(UINT32_MAX / 2))
-    return fail(PA_ERR_SHAPE, "page_stride and head_stride must stay below 2^31 elements");
+    return fail(PA_ERR_SHAPE, "page_stride must stay below 2^32 bytes and head_stride below "
+                              "2^31 elements");
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
     return fail(PA_ERR_ALIGN, "q, k_pool and v_pool must be 16-byte aligned");
   return PA_OK;

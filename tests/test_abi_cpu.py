@@ -276,3 +276,6 @@ def test_f32_pool_rejections():
     assert call(_kv(token_stride=130, head_stride=32 * 130, page_stride=2 * 32 * 130)) == PA["ALIGN"]
     # 4-element strides are 16-byte rows for f32: valid up to the workspace
     assert call(_kv(token_stride=132, head_stride=32 * 132, page_stride=2 * 32 * 132)) == PA["WORKSPACE"]
+    # one page must stay below 2^32 bytes: 2^30 f32 elements is 2^32 bytes
+    assert call(_kv(page_stride=2**30)) == PA["SHAPE"]
+    assert call(_kv(page_stride=2**30 - 4)) == PA["WORKSPACE"]
