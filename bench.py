@@ -356,19 +356,23 @@ def bench_insert(a, torch, pb, wl, dev) -> int:
 def bench_mla(a, torch, pb, wl, dev) -> int:
     fp8 = a.workload == "mla_fp8"
     log(f"generating workload {a.workload} (seeded) ...")
-    case = wl.mla_fp8(poison=False) if fp8 else wl.mla(poison=False)
-    dc = case.to(dev)
+    make = wl.mla_fp8 if fp8 else wl.mla
+    base = wl.SEED_BASE + (8 if fp8 else 5)
+    cases = [make(poison=False, seed=base + 100 * i) for i in range(a.rotate)]
+    case = cases[0]
+    dcs = [c.to(dev) for c in cases]
     B, H = case.batch, case.num_heads
     out = torch.empty((B, H, case.d_v), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(pb.mla_absorbed_decode_workspace_size(B, H, case.max_pages, case.page_size, 0),
-                     dtype=torch.uint8, device=dev)
-    layout = pb.kv_layout(dc.cache, "PSR")
+    ws = torch.empty(max(pb.mla_absorbed_decode_workspace_size(B, H, c.max_pages, c.page_size, 0)
+                         for c in cases), dtype=torch.uint8, device=dev)
+    layouts = [pb.kv_layout(d.cache, "PSR") for d in dcs]
 
     decode = pb.mla_absorbed_decode_fp8 if fp8 else pb.mla_absorbed_decode
 
     def step(i):
-        decode(dc.q_nope, dc.q_rope, dc.cache, layout, dc.w_uk, dc.w_uv, dc.block_table,
-               dc.context_lens, dc.scale, out, ws)
+        dc = dcs[i % len(dcs)]
+        decode(dc.q_nope, dc.q_rope, dc.cache, layouts[i % len(dcs)], dc.w_uk, dc.w_uv,
+               dc.block_table, dc.context_lens, dc.scale, out, ws)
 
     stream = torch.cuda.current_stream()
     for i in range(a.warmup):
@@ -382,28 +386,49 @@ def bench_mla(a, torch, pb, wl, dev) -> int:
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(stop) / a.steps
     call_mean, call_ms = _time_calls(torch, stream, step, a.steps)
-    nbytes = case.algorithmic_bytes()
+    def flops_of(c):
+        k = int(c.context_lens.sum())
+        return 2 * B * H * c.d_nope * c.d_lat + 2 * H * k * (c.d_lat + c.d_rope) \
+            + 2 * H * k * c.d_lat + 2 * B * H * c.d_lat * c.d_v
+    # mean over the calls of the timed loops (input set i % rotate)
+    nbytes = int(round(sum(cases[i % len(cases)].algorithmic_bytes() for i in range(a.steps)) / a.steps))
+    flops = int(round(sum(flops_of(cases[i % len(cases)]) for i in range(a.steps)) / a.steps))
     keys = int(case.context_lens.sum())
-    flops = 2 * B * H * case.d_nope * case.d_lat + 2 * H * keys * (case.d_lat + case.d_rope) \
-        + 2 * H * keys * case.d_lat + 2 * B * H * case.d_lat * case.d_v
     gbs = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (call_mean * 1e-3) / 1e9
     cpu = None
     if not a.no_cpu:
         from oracle.oracle import Oracle
         o = Oracle()
-        threads = max(1, min(len(os.sched_getaffinity(0)),
-                             int(os.environ.get("OMP_NUM_THREADS", "16") or 16)))
+        threads = oracle_threads()
+
+        def run(c):
+            if fp8:
+                o.mla_fp8(c)
+            else:
+                o.mla(c, "f64")
+
         o.set_threads(threads)
         t = time.time()
-        if fp8:
-            o.mla_fp8(case)
-        else:
-            o.mla(case, "f64")
+        run(case)
         sec = time.time() - t
-        cpu = {"value": round(nbytes / sec / 1e9, 3), "unit": "GB/s", "cores": threads,
+        # one thread: the first 2 sequences (the oracle's time is linear in the keys)
+        sub = case.to("cpu")
+        sub.q_nope, sub.q_rope = case.q_nope[:2].contiguous(), case.q_rope[:2].contiguous()
+        sub.block_table, sub.context_lens = case.block_table[:2].contiguous(), case.context_lens[:2].contiguous()
+        o.set_threads(1)
+        t = time.time()
+        run(sub)
+        sec1 = time.time() - t
+        o.set_threads(threads)
+        cpu = {"value": round(case.algorithmic_bytes() / sec / 1e9, 3), "unit": "GB/s", "cores": threads,
                "kind": "oracle", "sample": f"whole workload ({B} seqs, {keys} keys), float64 "
-                                           "oracle, one run", "seconds_per_call": round(sec, 3)}
+                                           "oracle, one run", "seconds_per_call": round(sec, 3),
+               "one_core": {"value": round(sub.algorithmic_bytes() / sec1 / 1e9, 3), "unit": "GB/s",
+                            "seconds": round(sec1, 3),
+                            "sample": f"first 2 sequences ({int(sub.context_lens.sum())} keys), "
+                                      "one run, their bytes on the same definition"},
+               "host": host_info()}
     res = {
         "metric": "absorbed-MLA decode µs/call + latent GB/s, bs16 h128",
         "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": a.steps,
@@ -417,7 +442,7 @@ def bench_mla(a, torch, pb, wl, dev) -> int:
         "config": {"workload": ("absorbed MLA decode over an FP8 latent cache, " if fp8 else
                                 "absorbed MLA decode, ") +
                                "bs16, 128 heads, 512+64 latent, page 64, ctx U[1024,8192]",
-                   "sum_context": keys,
+                   "sum_context": keys, "input_sets_rotated": a.rotate,
                    "algorithmic_bytes": nbytes, "algorithmic_flops": flops},
         "call_us": {"mean": round(call_mean * 1e3, 2),
                     "p10": round(sorted(call_ms)[len(call_ms) // 10] * 1e3, 2),
@@ -425,7 +450,8 @@ def bench_mla(a, torch, pb, wl, dev) -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic("mla_absorbed_decode_fp8_bs16_h128" if fp8
-                                                 else "mla_absorbed_decode_bs16_h128"),
+                                                 else "mla_absorbed_decode_bs16_h128")
+                                if a.rotate == 1 else None,
                      "kernel": ("mla_absorbed_decode_fp8" if fp8 else "mla_absorbed_decode") +
                                " call: absorb + split + merge/W_UV kernels",
                      "algorithmic_bytes_per_launch": nbytes,
@@ -436,33 +462,63 @@ def bench_mla(a, torch, pb, wl, dev) -> int:
     return 0
 
 
+def host_info():
+    """CPU model and logical CPU count of the host the bench runs on."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"cpu_model": model, "cpu_count": os.cpu_count()}
+
+
+def oracle_threads():
+    threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    # the GPU box grants 16 host threads per GPU (OMP_NUM_THREADS)
+    return max(1, min(threads, int(os.environ.get("OMP_NUM_THREADS", "16") or 16)))
+
+
 def cpu_baseline(case):
     """The CPU oracle (float64 gate instantiation, unmodified) on the whole
     workload with every host thread, repeated until about 10 s of wall time or
-    3 runs; reports the median on the same byte definition as the GPU."""
+    3 runs; reports the median on the same byte definition as the GPU.  Then
+    one run of the whole workload on one thread."""
     from oracle.oracle import Oracle
     o = Oracle()
-    threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
-    # the GPU box grants 16 host threads per GPU (OMP_NUM_THREADS)
-    threads = max(1, min(threads, int(os.environ.get("OMP_NUM_THREADS", "16") or 16)))
-    o.set_threads(threads)
-    times = []
-    t_all = time.time()
-    while len(times) < 3 or (time.time() - t_all < 10 and len(times) < 10):
-        t = time.time()
+    threads = oracle_threads()
+
+    def run():
         if case.kv_dtype == "fp8":
             o.decode_fp8(case)
         elif case.kv_dtype == "f32":
             o.decode_f32pool(case)
         else:
             o.decode(case, "f64")
+
+    o.set_threads(threads)
+    times = []
+    t_all = time.time()
+    while len(times) < 3 or (time.time() - t_all < 10 and len(times) < 10):
+        t = time.time()
+        run()
         times.append(time.time() - t)
     med = statistics.median(times)
+    o.set_threads(1)
+    t = time.time()
+    run()
+    one = time.time() - t
+    o.set_threads(threads)
     return {"value": round(case.kv_bytes() / med / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"whole workload ({case.batch} seqs, {int(case.context_lens.sum())} keys), "
                       f"float64 oracle, median of {len(times)} runs",
-            "seconds_per_call": round(med, 3)}
+            "seconds_per_call": round(med, 3),
+            "one_core": {"value": round(case.kv_bytes() / one / 1e9, 3), "unit": "GB/s",
+                         "seconds_per_call": round(one, 3), "sample": "whole workload, one run"},
+            "host": host_info()}
 
 
 if __name__ == "__main__":
