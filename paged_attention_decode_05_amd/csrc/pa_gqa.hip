@@ -8,18 +8,24 @@
 // q heads; vllm.cpp kernel matrix, row KERNEL-ATTN-FA2: a split axis across
 // the context fills the machine when batch x heads alone does not].
 //
-// Lane layout (wave64): a K or V row of D bf16 is read as D/8 lanes x 16
-// bytes, so one wave load instruction covers 64*16 B = 1 KB = 64/(D/8)
-// consecutive keys of a contiguous (page, head) tile.  A wave walks aligned
-// chunks of NI such loads (NI*64/(D/8) keys), the four waves of the block
-// taking every fourth chunk of the partition.
+// Two attention routines over a key range, both reading every K/V row with
+// 16-byte lane loads of contiguous (page, head) tiles:
 //
-// Per chunk:  q.k partial dots with v_dot2_f32_bf16 (bf16 products exact,
-// fp32 sums), summed over the D/8 lanes of a row with DPP; online softmax in
-// the log2 domain (scale*log2(e) folded into the score); P stays fp32 and
-// multiplies V widened to fp32.  Each group of D/8 lanes that shares a key
-// slot keeps its own running (max, sum, accumulator); the groups and the four
-// waves are merged once at the end, in a fixed order.
+// attend_range_mfma (groups of 4-16 heads, head_dim 64 and 512, FP8 and f32
+// pools): per 16-key chunk, S^T[16 keys x 16 heads] = K.Q^T and O += P.V on
+// the matrix cores.  bf16 products are exact and sums fp32; P (and f32 pool
+// elements) enter as three exact bf16 terms.  The softmax keeps a lazy
+// per-head reference max in the log2 domain.  Waves take every fourth chunk
+// and are merged once at the end; at head_dim 512 they split the dims of
+// each chunk instead.
+//
+// attend_range_valu (groups of 1 and 2 heads): a K or V row of D bf16 is
+// read as D/8 lanes x 16 bytes, one wave load covering 1 KB of consecutive
+// keys; q.k partial dots with v_dot2_f32_bf16, summed over the D/8 lanes of
+// a row with DPP; P stays fp32 and multiplies V widened to fp32.  Each group
+// of D/8 lanes that shares a key slot keeps its own running (max, sum,
+// accumulator); the groups and the waves are merged once at the end, in a
+// fixed order.
 #include <hip/hip_runtime.h>
 
 #include "pa_device.h"
