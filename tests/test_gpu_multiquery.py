@@ -76,6 +76,15 @@ def test_head_dim_256(oracle):
     _check(oracle, case, True, "d256 S=4")
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_head_dim_64(oracle, causal):
+    """head_dim 64 (matrix-core routine at every group size): 4 queries of
+    GQA-4 fill the 16-column tile; 16-key pages."""
+    case = wl.make_gqa_case(context_lens=(1, 17, 300, 2049), num_q_heads=8, num_kv_heads=2,
+                            head_dim=64, page_size=16, seed=9925, num_queries=4)
+    _check(oracle, case, causal, f"d64 S=4 causal={causal}")
+
+
 def test_context_shorter_than_queries(oracle):
     """ctx 1 and 2 with S = 4: the early causal queries see no key."""
     case = wl.make_gqa_case(context_lens=(1, 2, 4, 9), num_q_heads=8, num_kv_heads=2,
