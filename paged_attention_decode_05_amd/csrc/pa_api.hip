@@ -4,6 +4,7 @@
 // synchronises.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <string>
 
@@ -31,18 +32,19 @@ int launch_status(hipError_t e, const char* what) {
   return pa::fail(PA_ERR_LAUNCH, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (cached per device; threads that race
+// on the first call store the same value).
 int device_cus() {
-  static int cus[64] = {0};
+  static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
       n = 256;
-    cus[dev] = n;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return n;
 }
 
 int ilog2(int v) {

@@ -28,6 +28,8 @@
 // fixed order.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "pa_device.h"
 #include "pa_mfma.h"
 #include "pa_params.h"
@@ -1322,17 +1324,20 @@ static hipError_t launch_balanced_dg(const SplitParams& p, const BalancedLayout&
   return hipGetLastError();
 }
 
+// Resident blocks per CU of the balanced split kernel (a property of the
+// code object, the same on every gfx950 device; threads that race on the
+// first call store the same value).
 template <int D, int G, int KV>
 static int blocks_per_cu() {
-  static int cached = -1;
-  if (cached < 0) {
-    int n = 0;
+  static std::atomic<int> cached{0};
+  int n = cached.load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, balanced_split_kernel<D, G, KV>, kBlock, 0) !=
             hipSuccess || n < 1)
       n = 1;
-    cached = n;
+    cached.store(n, std::memory_order_relaxed);
   }
-  return cached;
+  return n;
 }
 
 template <int D>
