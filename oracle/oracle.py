@@ -10,6 +10,7 @@ are passed as their raw 16-bit patterns) and returns float64 numpy arrays.
 """
 from __future__ import annotations
 
+import copy
 import ctypes as C
 import os
 from typing import Optional
@@ -342,6 +343,38 @@ class Oracle:
             _ptr(qa, f64) if qa is not None else None, _ptr(lse, f64))
         self._check(rc, "oracle_mla_decode")
         return out, lse, qa
+
+
+    # ---- absorbed MLA with S queries per sequence ------------------------------
+    def mla_multi(self, case, causal: bool = True):
+        """(out [B,S,H,d_v], lse [B,S,H]) float64 for an MlaCase whose q_nope /
+        q_rope are [B, S, H, *], bf16 or FP8 cache.
+
+        The S queries of sequence b stand at its last S positions [pegainfer
+        PR #938: plain decode and the speculative verify step run through the
+        same absorbed-MLA kernel; vllm.cpp kernel matrix, row
+        KERNEL-ATTN-DFLASH-PAGED-BLOCK: the (1+k) block queries attend over
+        the paged context that holds their own block, under a causal or a
+        non-causal in-block mask].  Causal: query s sees keys t <= n - S + s,
+        so it is the one-query absorbed decode of its own q over the first
+        max(0, n - S + 1 + s) keys; not causal: over all n keys.  A query with
+        no key gives out = 0, lse = -inf."""
+        S = case.num_queries
+        out = np.zeros((case.batch, S, case.num_heads, case.d_v), np.float64)
+        lse = np.zeros((case.batch, S, case.num_heads), np.float64)
+        n = case.context_lens.to(torch.int64)
+        for s in range(S):
+            one = copy.copy(case)
+            q4n = case.q_nope if case.q_nope.dim() == 4 else case.q_nope[:, None]
+            q4r = case.q_rope if case.q_rope.dim() == 4 else case.q_rope[:, None]
+            one.q_nope, one.q_rope = q4n[:, s].contiguous(), q4r[:, s].contiguous()
+            if causal:
+                one.context_lens = (n - S + 1 + s).clamp(min=0).to(torch.int32)
+            if case.cache_dtype == "fp8":
+                out[:, s], lse[:, s] = self.mla_fp8(one)
+            else:
+                out[:, s], lse[:, s], _ = self.mla(one)
+        return out, lse
 
 
 _DEFAULT: Optional[Oracle] = None

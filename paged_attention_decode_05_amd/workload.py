@@ -123,8 +123,8 @@ class GqaCase:
 
 @dataclass
 class MlaCase:
-    q_nope: torch.Tensor            # [B, H, d_nope] bf16
-    q_rope: torch.Tensor            # [B, H, d_rope] bf16
+    q_nope: torch.Tensor            # [B, H, d_nope] bf16, or [B, S, H, d_nope] (S queries)
+    q_rope: torch.Tensor            # [B, H, d_rope] bf16, or [B, S, H, d_rope]
     cache: torch.Tensor             # [P, page_size, d_lat + d_rope] bf16, or
                                     # [P, page_size, MLA_FP8_ROW] uint8 (FP8 rows)
     w_uk: torch.Tensor              # [H, d_nope, d_lat] bf16
@@ -148,7 +148,11 @@ class MlaCase:
 
     @property
     def num_heads(self) -> int:
-        return int(self.q_nope.shape[1])
+        return int(self.q_nope.shape[-2])
+
+    @property
+    def num_queries(self) -> int:
+        return int(self.q_nope.shape[1]) if self.q_nope.dim() == 4 else 1
 
     @property
     def max_pages(self) -> int:
@@ -162,7 +166,7 @@ class MlaCase:
         """Latent rows + both weight tensors + q in + out, read/written once."""
         w = (self.w_uk.numel() + self.w_uv.numel()) * 2
         q = (self.q_nope.numel() + self.q_rope.numel()) * 2
-        out = self.batch * self.num_heads * self.d_v * 2
+        out = self.batch * self.num_queries * self.num_heads * self.d_v * 2
         return self.latent_bytes() + w + q + out
 
     def to(self, device) -> "MlaCase":
@@ -337,7 +341,11 @@ def make_mla_case(*, context_lens: Sequence[int] = (), num_heads: int, page_size
                   max_pages: Optional[int] = None, pool_pages: Optional[int] = None,
                   w_std: float = 0.02, scale: Optional[float] = None, poison: bool = True,
                   name: str = "custom", ctx_draw: Optional[tuple] = None,
-                  batch: Optional[int] = None, cache_dtype: str = "bf16") -> MlaCase:
+                  batch: Optional[int] = None, cache_dtype: str = "bf16",
+                  num_queries: int = 1) -> MlaCase:
+    """``num_queries`` > 1 gives q_nope / q_rope of shape [B, S, H, *]: the S
+    queries of a sequence stand at its last S positions (its context length
+    counts them)."""
     gen = torch.Generator().manual_seed(int(seed))
     if ctx_draw is not None:
         lo, hi = ctx_draw
@@ -349,8 +357,9 @@ def make_mla_case(*, context_lens: Sequence[int] = (), num_heads: int, page_size
         max_pages = max(1, (top + page_size - 1) // page_size)
     bt, pool_pages = _assign_pages(gen, ctx, page_size, max_pages, pool_pages)
     B = len(ctx)
-    q_nope = _normal_bf16(gen, (B, num_heads, d_nope))
-    q_rope = _normal_bf16(gen, (B, num_heads, d_rope))
+    qs = (B, num_heads) if num_queries == 1 else (B, num_queries, num_heads)
+    q_nope = _normal_bf16(gen, qs + (d_nope,))
+    q_rope = _normal_bf16(gen, qs + (d_rope,))
     if cache_dtype == "fp8":
         assert (d_lat, d_rope) == (MLA_FP8_LAT, MLA_FP8_ROPE)
         cache = _fp8_mla_rows(gen, pool_pages, page_size)
@@ -448,5 +457,14 @@ def mla_fp8(poison: bool = True, seed: int = SEED_BASE + 8) -> MlaCase:
                          seed=seed, poison=poison, name="mla_fp8", cache_dtype="fp8")
 
 
+def mla_verify(poison: bool = True, seed: int = SEED_BASE + 9, cache_dtype: str = "bf16") -> MlaCase:
+    """The mla shape with 4 queries per sequence (one token and three drafts
+    to verify), causal within the block: 512 query heads over each page."""
+    return make_mla_case(ctx_draw=(1024, 8192), batch=16, num_heads=128, page_size=64,
+                         seed=seed, poison=poison, name="mla_verify", num_queries=4,
+                         cache_dtype=cache_dtype)
+
+
 NAMED = {"tiny": tiny, "llama": llama, "d256w": d256w, "long": long_ctx, "mla": mla,
-         "llama_fp8": llama_fp8, "llama_f32": llama_f32, "d512": d512, "mla_fp8": mla_fp8}
+         "llama_fp8": llama_fp8, "llama_f32": llama_f32, "d512": d512, "mla_fp8": mla_fp8,
+         "mla_verify": mla_verify}

@@ -113,6 +113,47 @@ def mla_unabsorbed(case):
     return out
 
 
+def mla_unabsorbed_multi(case, causal: bool):
+    """(out [B,S,H,d_v], lse [B,S,H]) in float64 for an MLA case whose q is
+    [B, S, H, *] (or [B, H, *], S = 1), over a bf16 or FP8 cache, without
+    absorption: per head k_t = [W_UK[h] c_t[:d_lat] ; c_t[d_lat:]] and
+    v_t = W_UV[h] c_t[:d_lat]; query s of sequence b sees keys
+    t <= n - S + s (causal) or t < n."""
+    if case.cache_dtype == "fp8":
+        C = mla_fp8_rows_f64(case.cache, case.d_lat, case.d_rope)
+    else:
+        C = case.cache.detach().cpu().to(torch.float64).numpy()
+    qn = case.q_nope.to(torch.float64).numpy()
+    qr = case.q_rope.to(torch.float64).numpy()
+    if qn.ndim == 3:
+        qn, qr = qn[:, None], qr[:, None]
+    Wuk = case.w_uk.to(torch.float64).numpy()
+    Wuv = case.w_uv.to(torch.float64).numpy()
+    bt = case.block_table.numpy()
+    ctx = case.context_lens.numpy()
+    B, S, H = qn.shape[:3]
+    out = np.zeros((B, S, H, case.d_v))
+    lse = np.full((B, S, H), -np.inf)
+    for b in range(B):
+        n = int(ctx[b])
+        for s in range(S):
+            hi = n - S + s + 1 if causal else n
+            if hi <= 0:
+                continue
+            t = np.arange(hi)
+            rows = C[bt[b][t // case.page_size], t % case.page_size, :]
+            lat, rope = rows[:, :case.d_lat], rows[:, case.d_lat:]
+            for h in range(H):
+                k = np.concatenate([lat @ Wuk[h].T, rope], axis=1)
+                v = lat @ Wuv[h].T
+                sc = case.scale * (k @ np.concatenate([qn[b, s, h], qr[b, s, h]]))
+                m = sc.max()
+                e = np.exp(sc - m)
+                out[b, s, h] = (e @ v) / e.sum()
+                lse[b, s, h] = m + np.log(e.sum())
+    return out, lse
+
+
 def dense_multi(case, causal: bool):
     """(out [B,S,Hq,D], lse [B,S,Hq]) in float64 for a multi-query case:
     query s of sequence b sees keys t <= n - S + s (causal) or t < n, and

@@ -47,6 +47,10 @@ builds with a planted mistake (at least one must fail).
                        other rows untouched
   mla_fp8_equals_bf16  MLA over an FP8 cache == the bf16 MLA oracle over the
                        cache dequantized by torch, bit for bit
+  mla_multi_bruteforce MLA with S queries per sequence (causal and not, bf16
+                       and FP8 caches, contexts shorter than S) == float64
+                       unabsorbed attention with the in-block mask; one query
+                       == the one-query oracle, bit for bit
 """
 from __future__ import annotations
 
@@ -607,6 +611,31 @@ def mla_fp8_equals_bf16(o):
         assert np.array_equal(out8, out16) and np.array_equal(lse8, lse16), seed
 
 
+def mla_multi_bruteforce(o):
+    from brute import mla_unabsorbed_multi
+    for seed, S, ctx, page, dt in ((7220, 3, (0, 1, 2, 3, 17, 40), 16, "bf16"),
+                                   (7221, 4, (2, 63, 64, 65, 130), 64, "fp8"),
+                                   (7222, 2, (1, 33), 32, "bf16")):
+        case = make_mla_case(context_lens=ctx, num_heads=3, page_size=page, seed=seed,
+                             num_queries=S, cache_dtype=dt)
+        for causal in (True, False):
+            out, lse = o.mla_multi(case, causal)
+            ref, ref_lse = mla_unabsorbed_multi(case, causal)
+            assert np.abs(out - ref).max() < 1e-11, (seed, causal, np.abs(out - ref).max())
+            assert np.array_equal(np.isinf(lse), np.isinf(ref_lse)), (seed, causal)
+            fin = np.isfinite(ref_lse)
+            assert np.abs(lse[fin] - ref_lse[fin]).max() < 1e-11, (seed, causal)
+            if causal:      # the mask is load-bearing: the last query differs from the first
+                assert not np.allclose(out[:, 0], out[:, -1])
+    one = make_mla_case(context_lens=(5, 70), num_heads=4, page_size=16, seed=7223)
+    mq = one.to("cpu")
+    mq.q_nope, mq.q_rope = one.q_nope[:, None], one.q_rope[:, None]
+    for causal in (True, False):
+        a, la = o.mla_multi(mq, causal)
+        b, lb, _ = o.mla(one, "f64")
+        assert np.array_equal(a[:, 0], b) and np.array_equal(la[:, 0], lb)
+
+
 PINS = {
     "dense_bruteforce": dense_bruteforce,
     "single_token": single_token,
@@ -633,6 +662,7 @@ PINS = {
     "e4m3_encode": e4m3_encode,
     "mla_fp8_insert": mla_fp8_insert,
     "mla_fp8_equals_bf16": mla_fp8_equals_bf16,
+    "mla_multi_bruteforce": mla_multi_bruteforce,
 }
 
 

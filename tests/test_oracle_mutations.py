@@ -43,3 +43,33 @@ def test_mutation_is_caught(tmp_path, k):
     res = oracle_pins.run_all(o)
     failed = [n for n, r in res.items() if r is not None]
     assert failed, f"mutation {k} ({MUTATIONS[k]}) passed every pin"
+
+
+# Mistakes planted in the Python-level MLA multi-query composition: the
+# method's source with one substitution, bound to the shipped oracle.
+MULTI_MLA_MUTATIONS = {
+    "causal limit one key short": ("(n - S + 1 + s).clamp", "(n - S + s).clamp"),
+    "queries taken in reverse order": ("q4n[:, s]", "q4n[:, S - 1 - s]"),
+    "mask applied when not causal": ("if causal:", "if True:"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MULTI_MLA_MUTATIONS))
+def test_mla_multi_mutation_is_caught(oracle, name):
+    import copy
+    import inspect
+    import textwrap
+    import types
+
+    import numpy as np
+    import torch
+
+    old, new = MULTI_MLA_MUTATIONS[name]
+    src = inspect.getsource(Oracle.mla_multi)
+    assert src.count(old) == 1
+    ns = {"np": np, "torch": torch, "copy": copy}
+    exec(textwrap.dedent(src.replace(old, new)), ns)   # noqa: S102 -- our own source
+    o = copy.copy(oracle)
+    o.mla_multi = types.MethodType(ns["mla_multi"], o)
+    with pytest.raises(AssertionError):
+        oracle_pins.mla_multi_bruteforce(o)
