@@ -38,6 +38,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, 2.5 PFLOP/s
 METRIC = "decode-attn µs/call + KV-read GB/s (% of MI355X HBM peak), d128 GQA bs64"
 
 
@@ -52,7 +53,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama",
                     choices=["tiny", "llama", "d256w", "long", "mla", "verify", "insert",
-                             "llama_fp8", "llama_f32", "d512", "mla_fp8"])
+                             "llama_fp8", "llama_f32", "d512", "mla_fp8", "mla_verify",
+                             "mla_verify_fp8"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run K device-to-device copies of a 1 GiB buffer instead (reference "
@@ -89,7 +91,7 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "copies": a.steps}), flush=True)
         return 0
-    if a.workload in ("mla", "mla_fp8"):
+    if a.workload in ("mla", "mla_fp8", "mla_verify", "mla_verify_fp8"):
         return bench_mla(a, torch, pb, wl, dev)
     if a.workload == "verify":
         return bench_verify(a, torch, pb, wl, dev)
@@ -354,20 +356,32 @@ def bench_insert(a, torch, pb, wl, dev) -> int:
 
 
 def bench_mla(a, torch, pb, wl, dev) -> int:
-    fp8 = a.workload == "mla_fp8"
+    fp8 = a.workload.endswith("_fp8")
+    verify = a.workload.startswith("mla_verify")
     log(f"generating workload {a.workload} (seeded) ...")
-    make = wl.mla_fp8 if fp8 else wl.mla
-    base = wl.SEED_BASE + (8 if fp8 else 5)
+    if verify:
+        def make(poison, seed):
+            return wl.mla_verify(poison=poison, seed=seed, cache_dtype="fp8" if fp8 else "bf16")
+        base = wl.SEED_BASE + 9
+    else:
+        make = wl.mla_fp8 if fp8 else wl.mla
+        base = wl.SEED_BASE + (8 if fp8 else 5)
     cases = [make(poison=False, seed=base + 100 * i) for i in range(a.rotate)]
     case = cases[0]
     dcs = [c.to(dev) for c in cases]
-    B, H = case.batch, case.num_heads
-    out = torch.empty((B, H, case.d_v), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(max(pb.mla_absorbed_decode_workspace_size(B, H, c.max_pages, c.page_size, 0)
+    B, H, S = case.batch, case.num_heads, case.num_queries
+    out = torch.empty(((B, S, H) if verify else (B, H)) + (case.d_v,), dtype=torch.bfloat16,
+                      device=dev)
+    ws = torch.empty(max(pb.mla_absorbed_decode_workspace_size(B, S * H, c.max_pages, c.page_size,
+                                                               0)
                          for c in cases), dtype=torch.uint8, device=dev)
     layouts = [pb.kv_layout(d.cache, "PSR") for d in dcs]
 
-    decode = pb.mla_absorbed_decode_fp8 if fp8 else pb.mla_absorbed_decode
+    if verify:
+        def decode(*args):
+            pb.mla_absorbed_decode_multiquery(*args, causal=True)
+    else:
+        decode = pb.mla_absorbed_decode_fp8 if fp8 else pb.mla_absorbed_decode
 
     def step(i):
         dc = dcs[i % len(dcs)]
@@ -387,9 +401,13 @@ def bench_mla(a, torch, pb, wl, dev) -> int:
     ms_per_step = start.elapsed_time(stop) / a.steps
     call_mean, call_ms = _time_calls(torch, stream, step, a.steps)
     def flops_of(c):
-        k = int(c.context_lens.sum())
-        return 2 * B * H * c.d_nope * c.d_lat + 2 * H * k * (c.d_lat + c.d_rope) \
-            + 2 * H * k * c.d_lat + 2 * B * H * c.d_lat * c.d_v
+        # keys seen per query head, summed: under the causal mask query s of S
+        # sees n - S + 1 + s keys
+        n = c.context_lens.to(torch.int64)
+        k = int(sum((n - S + 1 + s).clamp(min=0).sum() for s in range(S))) if verify \
+            else int(n.sum())
+        return 2 * B * S * H * c.d_nope * c.d_lat + 2 * H * k * (c.d_lat + c.d_rope) \
+            + 2 * H * k * c.d_lat + 2 * B * S * H * c.d_lat * c.d_v
     # mean over the calls of the timed loops (input set i % rotate)
     nbytes = int(round(sum(cases[i % len(cases)].algorithmic_bytes() for i in range(a.steps)) / a.steps))
     flops = int(round(sum(flops_of(cases[i % len(cases)]) for i in range(a.steps)) / a.steps))
@@ -403,7 +421,9 @@ def bench_mla(a, torch, pb, wl, dev) -> int:
         threads = oracle_threads()
 
         def run(c):
-            if fp8:
+            if verify:
+                o.mla_multi(c, True)
+            elif fp8:
                 o.mla_fp8(c)
             else:
                 o.mla(c, "f64")
@@ -429,8 +449,34 @@ def bench_mla(a, torch, pb, wl, dev) -> int:
                             "sample": f"first 2 sequences ({int(sub.context_lens.sum())} keys), "
                                       "one run, their bytes on the same definition"},
                "host": host_info()}
+    mflops = flops / (call_mean * 1e-3) / 1e12
+    if verify:
+        # query heads x keys dominate: the contraction over the latent cache
+        roof = {"bound": "mfma", "achieved": round(mflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(mflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": recorded_traffic("mla_verify_fp8_bs16_s4_h128" if fp8
+                                            else "mla_verify_bs16_s4_h128")
+                if a.rotate == 1 else None,
+                "kernel": ("mla_absorbed_decode_multiquery_fp8" if fp8 else
+                           "mla_absorbed_decode_multiquery") +
+                          " call: absorb + split + merge/W_UV kernels",
+                "algorithmic_flops_per_launch": flops,
+                "hbm_gbs": round(achieved, 1)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": recorded_traffic("mla_absorbed_decode_fp8_bs16_h128" if fp8
+                                            else "mla_absorbed_decode_bs16_h128")
+                if a.rotate == 1 else None,
+                "kernel": ("mla_absorbed_decode_fp8" if fp8 else "mla_absorbed_decode") +
+                          " call: absorb + split + merge/W_UV kernels",
+                "algorithmic_bytes_per_launch": nbytes,
+                "mfma_tflops": round(mflops, 2)}
+    what = ("absorbed MLA verify, 4 causal queries per sequence, " if verify else
+            "absorbed MLA decode, ")
     res = {
-        "metric": "absorbed-MLA decode µs/call + latent GB/s, bs16 h128",
+        "metric": ("absorbed-MLA verify µs/call + TFLOP/s, bs16 S4 h128" if verify else
+                   "absorbed-MLA decode µs/call + latent GB/s, bs16 h128"),
         "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": round(ms_per_step, 5),
         "us_per_call": round(ms_per_step * 1e3, 2),
@@ -439,23 +485,14 @@ def bench_mla(a, torch, pb, wl, dev) -> int:
         "storage_dtype": ("e4m3 latent (one power-of-two scale per 64) + bf16 rope, 656 B/token"
                           if fp8 else "bf16"),
         "data": "synthetic",
-        "config": {"workload": ("absorbed MLA decode over an FP8 latent cache, " if fp8 else
-                                "absorbed MLA decode, ") +
+        "config": {"workload": what + ("over an FP8 latent cache, " if fp8 else "") +
                                "bs16, 128 heads, 512+64 latent, page 64, ctx U[1024,8192]",
                    "sum_context": keys, "input_sets_rotated": a.rotate,
                    "algorithmic_bytes": nbytes, "algorithmic_flops": flops},
         "call_us": {"mean": round(call_mean * 1e3, 2),
                     "p10": round(sorted(call_ms)[len(call_ms) // 10] * 1e3, 2),
                     "p90": round(sorted(call_ms)[(9 * len(call_ms)) // 10] * 1e3, 2)},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic("mla_absorbed_decode_fp8_bs16_h128" if fp8
-                                                 else "mla_absorbed_decode_bs16_h128")
-                                if a.rotate == 1 else None,
-                     "kernel": ("mla_absorbed_decode_fp8" if fp8 else "mla_absorbed_decode") +
-                               " call: absorb + split + merge/W_UV kernels",
-                     "algorithmic_bytes_per_launch": nbytes,
-                     "mfma_tflops": round(flops / (call_mean * 1e-3) / 1e12, 2)},
+        "roofline": roof,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

@@ -281,16 +281,18 @@ PA_API int32_t pa_decode_partition_size(int32_t batch, int32_t num_q_heads,
  *   out[b][h][dv] = bf16( sum_j w_uv[h][dv][j] * o_lat[j] )    (dv < 128)
  * q_abs, the probabilities and o_lat are fp32; they enter the bf16 matrix
  * products as three bf16 terms that sum to the fp32 value exactly, so only
- * fp32 accumulation rounds.  Keys are split into partitions of
- * partition_size (one workgroup per sequence, 64 heads and partition), merged
- * by log-sum-exp in ascending partition order; an empty context gives 0.
- * Deterministic run to run and independent of page placement.
+ * fp32 accumulation rounds.  The keys of every (64-head group, sequence) row,
+ * laid end to end, are cut into equal contiguous ranges, one per workgroup
+ * (about partition_size keys each, or the library's choice for 0); the
+ * pieces of a row are merged by log-sum-exp in ascending order; an empty
+ * context gives 0.  Deterministic run to run and independent of page
+ * placement.
  *
  * q_nope [batch][num_heads][128] bf16; q_rope [batch][num_heads][64] bf16;
  * kv_cache: pool described by *cache (num_kv_heads 1, head_dim 576,
  * page_size 16/32/64, token_stride >= 576 and a multiple of 8);
  * w_uk, w_uv [num_heads][128][512] bf16; out [batch][num_heads][128] bf16.
- * num_heads must be a multiple of 16.  partition_size: keys per split
+ * num_heads must be a multiple of 16.  partition_size: keys per workgroup
  * (multiple of 64, or 0 to let the library choose from host-known shapes).
  * workspace: at least mla_absorbed_decode_workspace_size(...) bytes,
  * 256-byte aligned, clobbered by the call.  Device-side contract as for
@@ -398,6 +400,54 @@ PA_API int mla_absorbed_decode_fp8(const void* q_nope, const void* q_rope, const
                                    int32_t max_pages_per_seq, float scale,
                                    int32_t partition_size, void* out, void* workspace,
                                    size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * mla_absorbed_decode_multiquery -- absorbed MLA with S queries per sequence
+ * (the verify step of speculative decoding).
+ *
+ * The S queries of sequence b stand at the last S positions of its context
+ * (context_lens[b] counts them; their rows are already in the cache).  Query
+ * s attends to keys t <= context_lens[b] - S + s when causal != 0, to all keys
+ * t < context_lens[b] otherwise [pegainfer PR #938: plain decode and the
+ * speculative verify step (the b=8 and b=16 verify launches) run through the
+ * same absorbed-MLA kernel; vllm.cpp kernel matrix, row
+ * KERNEL-ATTN-DFLASH-PAGED-BLOCK: the (1+k) block queries attend over the
+ * paged context holding their own block, under a causal or a non-causal
+ * in-block mask].  Each query is mla_absorbed_decode of its own q_nope and
+ * q_rope; a query with no key gives 0.  The S * num_heads query heads of a
+ * sequence share one pass over its cache rows (head s*num_heads + h uses
+ * W_UK[h] and W_UV[h]), so the cache is read from HBM about once however
+ * large S is.
+ *
+ * q_nope [batch][S][num_heads][128] bf16; q_rope [batch][S][num_heads][64];
+ * out [batch][S][num_heads][128] bf16.  1 <= num_queries = S <= 16.
+ * workspace: at least mla_absorbed_decode_workspace_size(batch,
+ * S * num_heads, max_pages_per_seq, page_size, partition_size) bytes.
+ * S = 1 gives exactly mla_absorbed_decode (causal or not).  Other arguments,
+ * determinism and error codes as mla_absorbed_decode; the _fp8 variant reads
+ * the FP8 latent cache as mla_absorbed_decode_fp8 does.
+ * ------------------------------------------------------------------------- */
+PA_API int mla_absorbed_decode_multiquery(const void* q_nope, const void* q_rope,
+                                          const void* kv_cache, const pa_kv_layout* cache,
+                                          const void* w_uk, const void* w_uv,
+                                          const int32_t* block_table,
+                                          int32_t block_table_stride,
+                                          const int32_t* context_lens, int32_t batch,
+                                          int32_t num_heads, int32_t num_queries, int32_t causal,
+                                          int32_t max_pages_per_seq, float scale,
+                                          int32_t partition_size, void* out, void* workspace,
+                                          size_t workspace_bytes, void* stream);
+PA_API int mla_absorbed_decode_multiquery_fp8(const void* q_nope, const void* q_rope,
+                                              const void* kv_cache, const pa_kv_layout* cache,
+                                              const void* w_uk, const void* w_uv,
+                                              const int32_t* block_table,
+                                              int32_t block_table_stride,
+                                              const int32_t* context_lens, int32_t batch,
+                                              int32_t num_heads, int32_t num_queries,
+                                              int32_t causal, int32_t max_pages_per_seq,
+                                              float scale, int32_t partition_size, void* out,
+                                              void* workspace, size_t workspace_bytes,
+                                              void* stream);
 
 /* Text describing the last non-zero status returned on the calling thread
  * ("" if none).  The pointer stays valid until the next call on that thread. */

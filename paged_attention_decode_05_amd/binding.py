@@ -25,7 +25,9 @@ EXPORTS = ("pa_decode", "pa_decode_splitkv", "pa_merge_lse", "pa_decode_workspac
            "pa_decode_partition_size", "mla_absorbed_decode",
            "mla_absorbed_decode_workspace_size", "pa_kv_insert", "mla_cache_insert",
            "pa_decode_multiquery", "pa_decode_multiquery_workspace_size", "pa_decode_fp8",
-           "pa_decode_f32", "mla_cache_insert_fp8", "mla_absorbed_decode_fp8", "pa_last_error")
+           "pa_decode_f32", "mla_cache_insert_fp8", "mla_absorbed_decode_fp8",
+           "mla_absorbed_decode_multiquery", "mla_absorbed_decode_multiquery_fp8",
+           "pa_last_error")
 
 
 class PaError(RuntimeError):
@@ -70,6 +72,10 @@ def _load() -> C.CDLL:
     lib.mla_absorbed_decode.restype = C.c_int
     lib.mla_absorbed_decode_fp8.argtypes = list(lib.mla_absorbed_decode.argtypes)
     lib.mla_absorbed_decode_fp8.restype = C.c_int
+    for f in (lib.mla_absorbed_decode_multiquery, lib.mla_absorbed_decode_multiquery_fp8):
+        f.argtypes = [vp, vp, vp, kvp, vp, vp, i32p, i32, i32p, i32, i32, i32, i32, i32,
+                      C.c_float, i32, vp, vp, C.c_size_t, vp]
+        f.restype = C.c_int
     lib.mla_absorbed_decode_workspace_size.argtypes = [i32] * 5
     lib.mla_absorbed_decode_workspace_size.restype = C.c_size_t
     lib.pa_decode_multiquery.argtypes = [vp, vp, vp, kvp, i32p, i32, i32p, i32, i32, i32, i32,
@@ -254,18 +260,21 @@ def pa_merge_lse(part_out, part_max, part_sum, context_lens, partition_size: int
 
 
 def _mla_decode(fn, cache_dtype, q_nope, q_rope, kv_cache, cache, w_uk, w_uv, block_table,
-                context_lens, scale, out, workspace, partition_size, max_pages_per_seq, stream):
+                context_lens, scale, out, workspace, partition_size, max_pages_per_seq, stream,
+                queries=None):
+    """queries: None for the one-query entries, else (num_queries, causal)."""
     for t, n in ((q_nope, "q_nope"), (q_rope, "q_rope"), (w_uk, "w_uk"), (w_uv, "w_uv"),
                  (block_table, "block_table"), (context_lens, "context_lens"), (out, "out")):
         _contig(t, n)
-    B, H = q_nope.shape[0], q_nope.shape[1]
+    B, H = q_nope.shape[0], q_nope.shape[-2]
+    extra = () if queries is None else (int(queries[0]), int(bool(queries[1])))
     maxp = block_table.shape[1] if max_pages_per_seq is None else max_pages_per_seq
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = fn(_ptr(q_nope, torch.bfloat16, "q_nope"), _ptr(q_rope, torch.bfloat16, "q_rope"),
             _ptr(kv_cache, cache_dtype, "kv_cache"), C.byref(cache),
             _ptr(w_uk, torch.bfloat16, "w_uk"), _ptr(w_uv, torch.bfloat16, "w_uv"),
             _ptr(block_table, torch.int32, "block_table"), block_table.stride(0),
-            _ptr(context_lens, torch.int32, "context_lens"), B, H, maxp, float(scale),
+            _ptr(context_lens, torch.int32, "context_lens"), B, H, *extra, maxp, float(scale),
             int(partition_size), _ptr(out, torch.bfloat16, "out"), _ptr(workspace), ws_bytes,
             _stream(stream))
     _check(rc)
@@ -289,6 +298,21 @@ def mla_absorbed_decode_fp8(q_nope, q_rope, kv_cache, cache: KvLayout, w_uk, w_u
     _mla_decode(LIB.mla_absorbed_decode_fp8, torch.uint8, q_nope, q_rope, kv_cache, cache, w_uk,
                 w_uv, block_table, context_lens, scale, out, workspace, partition_size,
                 max_pages_per_seq, stream)
+
+
+def mla_absorbed_decode_multiquery(q_nope, q_rope, kv_cache, cache: KvLayout, w_uk, w_uv,
+                                   block_table, context_lens, scale: float, out, workspace,
+                                   causal: bool = True, partition_size: int = 0,
+                                   max_pages_per_seq=None, stream=None) -> None:
+    """q_nope [B, S, H, 128], q_rope [B, S, H, 64], out [B, S, H, 128] bf16
+    (3-D tensors mean S = 1); kv_cache bf16 576-wide rows, or uint8 FP8 rows
+    of MLA_FP8_ROW bytes, which select the _fp8 entry."""
+    S = q_nope.shape[1] if q_nope.dim() == 4 else 1
+    fp8 = kv_cache.dtype == torch.uint8
+    fn = LIB.mla_absorbed_decode_multiquery_fp8 if fp8 else LIB.mla_absorbed_decode_multiquery
+    _mla_decode(fn, torch.uint8 if fp8 else torch.bfloat16, q_nope, q_rope, kv_cache, cache, w_uk,
+                w_uv, block_table, context_lens, scale, out, workspace, partition_size,
+                max_pages_per_seq, stream, queries=(S, causal))
 
 
 def _rows(t: torch.Tensor, name: str, ndim: int) -> None:

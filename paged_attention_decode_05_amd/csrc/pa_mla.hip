@@ -26,6 +26,13 @@
 // places on the same XCD (nb a multiple of 16), so the second read of a
 // cache tile is served by that XCD's L2.
 //
+// S queries per sequence (mla_absorbed_decode_multiquery): query s, head h is
+// query head s*H + h of its sequence, so a sequence has S*H heads in
+// ceil(S*H / 64) groups that share its key range; the absorption treats
+// q_nope [B][S][H][128] as B*S rows of H heads, W_UK[h] / W_UV[h] serve every
+// query, and under the causal in-block mask head s*H + h drops the keys
+// t >= n - S + 1 + s of its sequence.
+//
 // FP8 latent cache (mla_absorbed_decode_fp8): rows of 656 bytes hold the
 // latent as E4M3 in blocks of 64 with one power-of-two scale byte per block
 // and the rope part in bf16 [vllm.cpp kernel matrix, row KERNEL-KV-CACHE-DSA:
@@ -75,12 +82,15 @@ struct MlaParams {
   float* seg_out;          // [slots][64][512] normalised partial o_lat
   float* seg_max;          // [slots][64] natural-log-domain reference max
   float* seg_sum;          // [slots][64] sum of exp(s - max)
-  uint16_t* out;           // [B][H][128]
+  uint16_t* out;           // [B][S][H][128]
   int64_t page_stride;
   int32_t token_stride;
   int32_t bt_stride;
   int32_t batch;
-  int32_t num_heads;
+  int32_t num_heads;       // query heads per sequence: S * H (query s, head h -> s*H + h)
+  int32_t w_heads;         // H, the heads of W_UK / W_UV
+  int32_t num_queries;     // S
+  int32_t abs_rows;        // B * S, the rows of the absorption
   int32_t groups;          // ceil(num_heads / 64)
   int32_t page_size;
   int32_t page_shift;
@@ -91,8 +101,10 @@ struct MlaParams {
 
 // ---- 1. absorption: q_abs = q_nope . W_UK[h] on MFMA, split in three; rope copied ---
 //
-// Block (h, jq, bt): q_abs[b][h][jq*128 .. +128) for the 16 sequences
-// b = 16*bt .. +16, as the product [16 b x 128 d] . [128 d x 128 j] of exact
+// Block (h, jq, bt): q_abs[r][h][jq*128 .. +128) for the 16 query rows
+// r = 16*bt .. +16 (r = b*S + s: q_nope [B][S][H][128] is [B*S][H][128], and
+// row r*H + h of the result is head s*H + h of sequence b, the numbering of
+// the later kernels), as the product [16 r x 128 d] . [128 d x 128 j] of exact
 // bf16 operands (MFMA, fp32 accumulation).  A = q_nope rows straight from
 // memory (8 consecutive d per lane); B = the W_UK[h] tile staged in LDS
 // row-major ([d][j]) and read with transposed reads, which give each lane
@@ -109,7 +121,7 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(const MlaParams p) {
   const int wave = t >> 6;
   const int g = lane >> 4;
   const int c16 = lane & 15;
-  const int nb = min(16, p.batch - b0);
+  const int nb = min(16, p.abs_rows - b0);
   const uint16_t* wsrc = p.w_uk + static_cast<int64_t>(h) * kNope * kLat + jq * 128;
   uint4 wst[8];
 #pragma unroll
@@ -120,7 +132,7 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(const MlaParams p) {
   uint4 qa[kNope / 32];                  // A operand: sequence b0 + c16, d = 32ks + 8g .. +8
 #pragma unroll
   for (int ks = 0; ks < kNope / 32; ++ks)
-    qa[ks] = c16 < nb ? load16(p.q_nope + (static_cast<int64_t>(b0 + c16) * p.num_heads + h) * kNope +
+    qa[ks] = c16 < nb ? load16(p.q_nope + (static_cast<int64_t>(b0 + c16) * p.w_heads + h) * kNope +
                                32 * ks + 8 * g)
                       : make_uint4(0, 0, 0, 0);
 #pragma unroll
@@ -149,7 +161,7 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(const MlaParams p) {
       if (bb < nb) {
         uint16_t hi, mid, lo;
         split3_bf16(c[i], hi, mid, lo);
-        const int64_t row = static_cast<int64_t>(b0 + bb) * p.num_heads + h;
+        const int64_t row = static_cast<int64_t>(b0 + bb) * p.w_heads + h;
         p.q_hi[row * kRow + j] = hi;
         p.q_mid[row * kLat + j] = mid;
         p.q_lo[row * kLat + j] = lo;
@@ -158,7 +170,7 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(const MlaParams p) {
   }
   if (jq == 0 && t < nb * (kRope / 8)) {   // rope part: exact bf16, one term
     const int rb = t / (kRope / 8), rc = t % (kRope / 8);
-    const int64_t row = static_cast<int64_t>(b0 + rb) * p.num_heads + h;
+    const int64_t row = static_cast<int64_t>(b0 + rb) * p.w_heads + h;
     *reinterpret_cast<uint4*>(p.q_hi + row * kRow + kLat + 8 * rc) =
         load16(p.q_rope + row * kRope + 8 * rc);
   }
@@ -225,9 +237,13 @@ __device__ __forceinline__ void fp8x16_bf16_scaled(uint4 x, float s, uint4& lo, 
 // key-major tile.  The softmax keeps a per-head reference max and rescales
 // the accumulators only when a score exceeds it by more than 8 (log2
 // domain), so P stays below 2^8 and rescaling is rare.
-template <bool F8>
-__device__ __forceinline__ void mla_segment(const MlaParams& p, int b, int hg, int begin, int end,
-                                            int64_t slot, uint16_t (*crow2)[kTileKeys][kRowPad],
+// CAUSAL: head s*H + h (query s of S) sees only keys t < n - S + 1 + s; a
+// head with no such key in [begin, end) writes a zero partial with max -inf
+// and sum 0.
+template <bool F8, bool CAUSAL>
+__device__ __forceinline__ void mla_segment(const MlaParams& p, int b, int n, int hg, int begin,
+                                            int end, int64_t slot,
+                                            uint16_t (*crow2)[kTileKeys][kRowPad],
                                             uint16_t (*qlo_s)[kLat + 8]) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -383,12 +399,13 @@ __device__ __forceinline__ void mla_segment(const MlaParams& p, int b, int hg, i
     // lane holds keys t0 + 16*mt + key_row(4g + i) for head c16
     float pv[8];
     float cm = -INFINITY;
+    const int end_h = CAUSAL ? min(end, n - p.num_queries + 1 + (h0 + c16) / p.w_heads) : end;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = t0 + 16 * mt + key_row(4 * g + i);
-        const float v = (t >= begin && t < end) ? sc[mt][i] * p.scale_log2 : -INFINITY;
+        const float v = (t >= begin && t < end_h) ? sc[mt][i] * p.scale_log2 : -INFINITY;
         pv[4 * mt + i] = v;
         cm = fmaxf(cm, v);
       }
@@ -464,7 +481,7 @@ __device__ __forceinline__ void mla_segment(const MlaParams& p, int b, int hg, i
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float* dst = p.seg_out + (srow + 4 * g + i) * kLat;
-    const float inv = 1.0f / lr[i];
+    const float inv = (!CAUSAL || lr[i] > 0.0f) ? 1.0f / lr[i] : 0.0f;
 #pragma unroll
     for (int jt = 0; jt < kLat / 16; ++jt) dst[16 * jt + c16] = acc[jt][i] * inv;
   }
@@ -474,7 +491,7 @@ __device__ __forceinline__ void mla_segment(const MlaParams& p, int b, int hg, i
   }
 }
 
-template <bool F8>
+template <bool F8, bool CAUSAL>
 __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(const MlaParams p) {
   __shared__ __align__(16) uint16_t crow[2][kTileKeys][kRowPad];
   __shared__ __align__(16) uint16_t qlo_s[kGroup][kLat + 8];
@@ -512,7 +529,8 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(const MlaParams 
     const int begin = static_cast<int>(u - row_start);
     const int end = static_cast<int>(min(u1 - row_start, static_cast<int64_t>(n)));
     if (end > begin)
-      mla_segment<F8>(p, b, hg, begin, end, static_cast<int64_t>(hg) * p.batch + b + i, crow, qlo_s);
+      mla_segment<F8, CAUSAL>(p, b, n, hg, begin, end, static_cast<int64_t>(hg) * p.batch + b + i,
+                              crow, qlo_s);
     u = row_start + n;
     pre += n;
     if (++b == p.batch) {
@@ -525,7 +543,8 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(const MlaParams 
 
 // ---- 3. merge of the partials, then out = W_UV[h] . o_lat on MFMA ---------------------
 //
-// Block (h, bt) handles sequences 8*bt .. +8 of head h: row (group hg, b)
+// Block (h, bt, s) handles sequences 8*bt .. +8 of head s*H + h (query s,
+// W_UV[h]; hg below is that head's group): row (group hg, b)
 // was cut into pieces by blocks i0 .. i1 of the split (recomputed here from
 // the context lengths), whose partials sit in slots r + i0 .. r + i1 with
 // r = hg*batch + b.  The max M and the total W = sum l_i e^(m_i - M) of a row
@@ -534,7 +553,7 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(const MlaParams 
 // written to LDS as three bf16 terms; then out[b][dv] = sum_j o_lat[b][j]
 // W_UV[h][dv][j] on MFMA with A = o_lat (rows 8..15 zero) and B = W_UV rows,
 // whose 8 consecutive latent dims per lane are contiguous in memory; wave w
-// computes dv tile w.  An empty context gives 0.
+// computes dv tile w.  An empty context, or a query that sees no key, gives 0.
 constexpr int kMergeThreads = 512;
 constexpr int kMergeRows = 8;
 constexpr int kMergeWts = 64;      // piece weights kept in LDS per row
@@ -547,7 +566,8 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_uv_kernel(const MlaPa
   __shared__ int64_t sh_slot[kMergeRows];
   __shared__ int sh_cnt[kMergeRows];
   __shared__ float sh_m[kMergeRows], sh_iw[kMergeRows];
-  const int h = blockIdx.x;
+  const int hw = blockIdx.x;                       // head of W_UV
+  const int h = blockIdx.z * p.w_heads + hw;       // query head
   const int b0 = blockIdx.y * kMergeRows;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -602,6 +622,7 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_uv_kernel(const MlaPa
     float M = m0;
     for (int k = lane + 64; k < cnt; k += 64) M = fmaxf(M, p.seg_max[(slot + k) * kGroup + hl]);
     M = wave_max(M);
+    if (M == -INFINITY) M = 0.0f;   // no piece saw a key: every weight is 0
     float wk = mine ? l0 * __expf(m0 - M) : 0.0f;
     if (mine) wts[bb][lane] = wk;
     for (int k = lane + 64; k < cnt; k += 64)
@@ -609,7 +630,7 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_uv_kernel(const MlaPa
     const float W = wave_sum(wk);
     if (lane == 0) {
       sh_m[bb] = M;
-      sh_iw[bb] = cnt > 0 ? 1.0f / W : 0.0f;
+      sh_iw[bb] = W > 0.0f ? 1.0f / W : 0.0f;
     }
   }
   __syncthreads();
@@ -660,7 +681,7 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_uv_kernel(const MlaPa
   }
   __syncthreads();
   // out[b][dv]: wave w takes dv tile w; all 16 W_UV loads in flight
-  const uint16_t* wuv = p.w_uv + static_cast<int64_t>(h) * kDv * kLat +
+  const uint16_t* wuv = p.w_uv + static_cast<int64_t>(hw) * kDv * kLat +
                         static_cast<int64_t>(16 * wave + c16) * kLat + 8 * g;
   uint4 bw[kLat / 32];
 #pragma unroll
@@ -718,17 +739,20 @@ int mla_decode_impl(const void* q_nope, const void* q_rope, const void* kv_cache
                     const int32_t* block_table, int32_t block_table_stride,
                     const int32_t* context_lens, int32_t batch, int32_t num_heads,
                     int32_t max_pages_per_seq, float scale, int32_t partition_size, void* out,
-                    void* workspace, size_t workspace_bytes, void* stream, bool fp8) {
+                    void* workspace, size_t workspace_bytes, void* stream, bool fp8,
+                    int32_t num_queries, bool causal) {
   int rc = pa::check_mla(q_nope, q_rope, kv_cache, cache, w_uk, w_uv, block_table,
                          block_table_stride, context_lens, batch, num_heads, max_pages_per_seq,
-                         scale, partition_size, out, fp8);
+                         scale, partition_size, out, fp8, num_queries);
   if (rc) return rc;
+  const int32_t qheads = num_queries * num_heads;   // query heads per sequence
   pa::MlaPlan plan;
-  if (!pa::plan_mla(batch, num_heads, max_pages_per_seq, cache->page_size, partition_size, &plan))
+  if (!pa::plan_mla(batch, qheads, max_pages_per_seq, cache->page_size, partition_size, &plan))
     return pa::fail(PA_ERR_SHAPE, "no launch plan for these shapes");
   if (!workspace || workspace_bytes < plan.bytes)
     return pa::fail(PA_ERR_WORKSPACE, "workspace must hold mla_absorbed_decode_workspace_size() = " +
-                                          std::to_string(plan.bytes) + " bytes");
+                                          std::to_string(plan.bytes) + " bytes (num_heads " +
+                                          std::to_string(qheads) + ")");
   if (reinterpret_cast<uintptr_t>(workspace) & 255u)
     return pa::fail(PA_ERR_ALIGN, "workspace must be 256-byte aligned");
   char* ws = static_cast<char*>(workspace);
@@ -751,7 +775,10 @@ int mla_decode_impl(const void* q_nope, const void* q_rope, const void* kv_cache
   p.token_stride = static_cast<int32_t>(cache->token_stride);
   p.bt_stride = block_table_stride;
   p.batch = batch;
-  p.num_heads = num_heads;
+  p.num_heads = qheads;
+  p.w_heads = num_heads;
+  p.num_queries = num_queries;
+  p.abs_rows = batch * num_queries;
   p.groups = plan.groups;
   p.page_size = cache->page_size;
   int shift = 0;
@@ -772,19 +799,26 @@ int mla_decode_impl(const void* q_nope, const void* q_rope, const void* kv_cache
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   pa::clear_error();
-  const int btiles = (batch + 15) / 16;
+  const int btiles = (p.abs_rows + 15) / 16;
   hipLaunchKernelGGL(pa::mla_absorb_kernel, dim3(num_heads, pa::kMlaLat / 128, btiles), dim3(256),
                      0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return pa::fail(PA_ERR_LAUNCH, std::string("absorb: ") + hipGetErrorString(e));
-  if (fp8)
-    hipLaunchKernelGGL(pa::mla_split_kernel<true>, dim3(p.split_grid), dim3(pa::kMlaThreads), 0, s, p);
+  // one query, or no mask: every head sees the whole context
+  const bool masked = causal && num_queries > 1;
+  const dim3 sg(p.split_grid), st(pa::kMlaThreads);
+  if (fp8 && masked)
+    hipLaunchKernelGGL((pa::mla_split_kernel<true, true>), sg, st, 0, s, p);
+  else if (fp8)
+    hipLaunchKernelGGL((pa::mla_split_kernel<true, false>), sg, st, 0, s, p);
+  else if (masked)
+    hipLaunchKernelGGL((pa::mla_split_kernel<false, true>), sg, st, 0, s, p);
   else
-    hipLaunchKernelGGL(pa::mla_split_kernel<false>, dim3(p.split_grid), dim3(pa::kMlaThreads), 0, s, p);
+    hipLaunchKernelGGL((pa::mla_split_kernel<false, false>), sg, st, 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return pa::fail(PA_ERR_LAUNCH, std::string("split: ") + hipGetErrorString(e));
   hipLaunchKernelGGL(pa::mla_merge_uv_kernel,
-                     dim3(num_heads, (batch + pa::kMergeRows - 1) / pa::kMergeRows),
+                     dim3(num_heads, (batch + pa::kMergeRows - 1) / pa::kMergeRows, num_queries),
                      dim3(pa::kMergeThreads), 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return pa::fail(PA_ERR_LAUNCH, std::string("merge: ") + hipGetErrorString(e));
@@ -803,7 +837,8 @@ int mla_absorbed_decode(const void* q_nope, const void* q_rope, const void* kv_c
                         void* workspace, size_t workspace_bytes, void* stream) {
   return mla_decode_impl(q_nope, q_rope, kv_cache, cache, w_uk, w_uv, block_table,
                          block_table_stride, context_lens, batch, num_heads, max_pages_per_seq,
-                         scale, partition_size, out, workspace, workspace_bytes, stream, false);
+                         scale, partition_size, out, workspace, workspace_bytes, stream, false, 1,
+                         false);
 }
 
 int mla_absorbed_decode_fp8(const void* q_nope, const void* q_rope, const void* kv_cache,
@@ -814,7 +849,36 @@ int mla_absorbed_decode_fp8(const void* q_nope, const void* q_rope, const void* 
                             void* out, void* workspace, size_t workspace_bytes, void* stream) {
   return mla_decode_impl(q_nope, q_rope, kv_cache, cache, w_uk, w_uv, block_table,
                          block_table_stride, context_lens, batch, num_heads, max_pages_per_seq,
-                         scale, partition_size, out, workspace, workspace_bytes, stream, true);
+                         scale, partition_size, out, workspace, workspace_bytes, stream, true, 1,
+                         false);
+}
+
+int mla_absorbed_decode_multiquery(const void* q_nope, const void* q_rope, const void* kv_cache,
+                                   const pa_kv_layout* cache, const void* w_uk, const void* w_uv,
+                                   const int32_t* block_table, int32_t block_table_stride,
+                                   const int32_t* context_lens, int32_t batch, int32_t num_heads,
+                                   int32_t num_queries, int32_t causal, int32_t max_pages_per_seq,
+                                   float scale, int32_t partition_size, void* out, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  return mla_decode_impl(q_nope, q_rope, kv_cache, cache, w_uk, w_uv, block_table,
+                         block_table_stride, context_lens, batch, num_heads, max_pages_per_seq,
+                         scale, partition_size, out, workspace, workspace_bytes, stream, false,
+                         num_queries, causal != 0);
+}
+
+int mla_absorbed_decode_multiquery_fp8(const void* q_nope, const void* q_rope,
+                                       const void* kv_cache, const pa_kv_layout* cache,
+                                       const void* w_uk, const void* w_uv,
+                                       const int32_t* block_table, int32_t block_table_stride,
+                                       const int32_t* context_lens, int32_t batch,
+                                       int32_t num_heads, int32_t num_queries, int32_t causal,
+                                       int32_t max_pages_per_seq, float scale,
+                                       int32_t partition_size, void* out, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  return mla_decode_impl(q_nope, q_rope, kv_cache, cache, w_uk, w_uv, block_table,
+                         block_table_stride, context_lens, batch, num_heads, max_pages_per_seq,
+                         scale, partition_size, out, workspace, workspace_bytes, stream, true,
+                         num_queries, causal != 0);
 }
 
 }  // extern "C"

@@ -209,14 +209,16 @@ int check_mla(const void* q_nope, const void* q_rope, const void* kv_cache,
               const int32_t* block_table, int32_t block_table_stride,
               const int32_t* context_lens, int32_t batch, int32_t num_heads,
               int32_t max_pages_per_seq, float scale, int32_t partition_size, const void* out,
-              bool fp8) {
+              bool fp8, int32_t num_queries) {
   if (!q_nope || !q_rope || !kv_cache || !cache || !w_uk || !w_uv || !block_table ||
       !context_lens || !out)
     return fail(PA_ERR_NULL, "a required pointer is NULL");
   if (batch < 1 || num_heads < 1 || max_pages_per_seq < 1)
     return fail(PA_ERR_SHAPE, "batch, num_heads and max_pages_per_seq must be >= 1");
-  if (batch > 65535 || num_heads > 65535)
-    return fail(PA_ERR_SHAPE, "batch and num_heads must be <= 65535 (grid limits)");
+  if (num_queries < 1 || num_queries > 16)
+    return fail(PA_ERR_SHAPE, "num_queries must be in 1..16");
+  if (batch > 65535 || static_cast<int64_t>(num_heads) * num_queries > 65535)
+    return fail(PA_ERR_SHAPE, "batch and num_heads * num_queries must be <= 65535 (grid limits)");
   if (cache->num_pages < 1 || cache->page_size < 1)
     return fail(PA_ERR_SHAPE, "cache: num_pages and page_size must be >= 1");
   if (block_table_stride < max_pages_per_seq)

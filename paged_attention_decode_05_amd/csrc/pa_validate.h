@@ -93,13 +93,14 @@ bool plan_mla(int32_t batch, int32_t num_heads, int32_t max_pages_per_seq, int32
               int32_t partition_size, MlaPlan* plan);
 
 // fp8: the cache holds FP8 rows (head_dim kMlaFp8Row, strides in bytes,
-// multiples of 16) instead of bf16 576-wide rows.
+// multiples of 16) instead of bf16 576-wide rows.  num_queries: queries per
+// sequence (1..16), each with num_heads heads.
 int check_mla(const void* q_nope, const void* q_rope, const void* kv_cache,
               const pa_kv_layout* cache, const void* w_uk, const void* w_uv,
               const int32_t* block_table, int32_t block_table_stride,
               const int32_t* context_lens, int32_t batch, int32_t num_heads,
               int32_t max_pages_per_seq, float scale, int32_t partition_size, const void* out,
-              bool fp8 = false);
+              bool fp8 = false, int32_t num_queries = 1);
 
 int check_kv_insert(const void* k_new, const void* v_new, int64_t src_token_stride,
                     int64_t src_head_stride, const void* k_pool, const void* v_pool,

@@ -193,6 +193,29 @@ def test_mla_fp8_rejections():
                FAKE, 0, None) == PA["SHAPE"]             # token_stride < 656
 
 
+def test_mla_multiquery_rejections():
+    """num_queries outside 1..16, or a workspace sized for fewer query heads,
+    is refused before any launch; FP8 and bf16 rows go to their own entry."""
+    bf = pb.KvLayout(1300, 64, 1, 576, 64 * 576, 0, 576)
+    f8 = pb.KvLayout(1300, 64, 1, 656, 64 * 656, 0, 656)
+
+    def dec(cache=bf, S=4, causal=1, H=128, ws=0, fn=pb.LIB.mla_absorbed_decode_multiquery):
+        return fn(FAKE, FAKE, FAKE, C.byref(cache), FAKE, FAKE, FAKE, 128, FAKE, 16, H, S, causal,
+                  128, 0.072, 0, FAKE, FAKE if ws else None, ws, None)
+    assert dec() == PA["WORKSPACE"], pb.pa_last_error()
+    assert "512" in pb.pa_last_error()                    # the query heads the size is for
+    assert dec(S=0) == PA["SHAPE"] and dec(S=17) == PA["SHAPE"]
+    assert dec(S=16, H=4096) == PA["SHAPE"]               # 65536 query heads
+    assert dec(H=24) == PA["UNSUPPORTED"]                 # heads not a multiple of 16
+    n1 = pb.mla_absorbed_decode_workspace_size(16, 128, 128, 64, 0)
+    n4 = pb.mla_absorbed_decode_workspace_size(16, 512, 128, 64, 0)
+    assert 0 < n1 < n4
+    assert dec(ws=n1) == PA["WORKSPACE"]
+    assert dec(cache=f8) == PA["UNSUPPORTED"]
+    assert dec(cache=f8, fn=pb.LIB.mla_absorbed_decode_multiquery_fp8) == PA["WORKSPACE"]
+    assert dec(cache=bf, fn=pb.LIB.mla_absorbed_decode_multiquery_fp8) == PA["UNSUPPORTED"]
+
+
 def _ins(kv=None, n=4, ts=256, hs=128, **kw):
     kv = kv or _kv()
     a = dict(k=FAKE, v=FAKE, kp=FAKE, vp=FAKE, sl=FAKE)

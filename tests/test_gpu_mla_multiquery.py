@@ -1,0 +1,166 @@
+"""GPU parity of mla_absorbed_decode_multiquery (S queries per sequence,
+causal in-block mask or none), bf16 and FP8 latent caches, against the CPU
+oracle, through the C ABI.
+
+Gate: oracle.compare (|g - r| <= 2e-2 and <= 2 bf16 ulps, floor 2^-22) on
+the bf16 outputs against the float64 oracle.  Caches carry NaN canaries in
+unused pages and page tails; workspaces start as NaN bytes.  The cases cover
+query-head groups that mix queries (S * H not a multiple of 64), contexts
+shorter than S (queries that see no key), 16 queries, and pieces of the
+split in which some queries see no key.
+"""
+from __future__ import annotations
+
+import pytest
+import torch
+
+from gpu_util import run_mla
+from oracle.compare import compare
+from paged_attention_decode_05_amd import binding as pb
+from paged_attention_decode_05_amd import workload as wl
+
+pytestmark = pytest.mark.gpu
+
+
+def _gate(out, ref, what):
+    rep = compare(out, ref)
+    print(f"[{what}] {rep}", flush=True)
+    assert rep.ok, f"{what}: {rep}"
+
+
+def run_mla_multi(dc, causal, partition_size=0, workspace=None):
+    S = dc.num_queries
+    B, H = dc.batch, dc.num_heads
+    out = torch.full((B, S, H, dc.d_v), float("nan"), dtype=torch.bfloat16, device="cuda")
+    if workspace is None:
+        n = pb.mla_absorbed_decode_workspace_size(B, S * H, dc.max_pages, dc.page_size,
+                                                  partition_size)
+        assert n > 0
+        workspace = torch.full((n,), 0xFF, dtype=torch.uint8, device="cuda")
+    pb.mla_absorbed_decode_multiquery(dc.q_nope, dc.q_rope, dc.cache, pb.kv_layout(dc.cache, "PSR"),
+                                      dc.w_uk, dc.w_uv, dc.block_table, dc.context_lens,
+                                      dc.scale, out, workspace, causal=causal,
+                                      partition_size=partition_size)
+    torch.cuda.synchronize()
+    return out.cpu()
+
+
+def _case(ctx, S, heads, page, seed, dt="bf16"):
+    return wl.make_mla_case(context_lens=ctx, num_heads=heads, page_size=page, seed=seed,
+                            num_queries=S, cache_dtype=dt)
+
+
+@pytest.mark.parametrize("S,heads,page,causal,dt,ctx", [
+    (2, 16, 16, True, "bf16", (0, 1, 2, 3, 17, 100, 700)),
+    (4, 16, 64, True, "bf16", (1, 4, 5, 63, 64, 65, 300)),     # one group of all 4 queries
+    (3, 48, 32, False, "bf16", (1, 40, 129, 1000)),            # 144 heads: a 16-head group
+    (3, 48, 32, True, "bf16", (2, 3, 40, 129, 1000)),
+    (4, 128, 64, True, "bf16", (2, 700, 2049)),                # 8 groups of 64
+    (16, 16, 32, True, "bf16", (1, 15, 16, 17, 40, 500)),      # the most queries
+    (4, 32, 64, True, "fp8", (3, 64, 65, 900)),
+    (2, 64, 16, False, "fp8", (1, 33, 250)),
+])
+def test_matches_oracle(oracle, S, heads, page, causal, dt, ctx):
+    case = _case(ctx, S, heads, page, 9100 + 7 * S + heads + page, dt)
+    ref, _ = oracle.mla_multi(case, causal)
+    _gate(run_mla_multi(case.to("cuda"), causal), ref,
+          f"mla multi S={S} H={heads} page={page} causal={causal} {dt}")
+
+
+def _pieces_with_blind_queries(ctx, S, heads, partition_size, batch_pages_keys):
+    """Number of split pieces that start inside the last S - 1 keys of their
+    row (so some query sees none of their keys), for the split that an explicit
+    partition size gives: the keys of all (group, sequence) rows laid end to
+    end, cut into nb = ceil(T / partition_size) equal ranges (nb below the
+    explicit-size block cap here)."""
+    groups = (S * heads + 63) // 64
+    total = sum(ctx)
+    T = groups * total
+    nb = -(-T // partition_size)
+    assert nb <= -(-groups * len(ctx) * batch_pages_keys // partition_size)
+    starts = {T * i // nb for i in range(nb)}
+    hits, row = 0, 0
+    for _ in range(groups):
+        for n in ctx:
+            hits += sum(1 for u in starts if row + max(0, n - S + 1) <= u < row + n)
+            row += n
+    return hits
+
+
+@pytest.mark.parametrize("partition_size", [64, 128, 1024])
+def test_partition_sizes(oracle, partition_size):
+    S, heads, ctx = 8, 16, (3, 200, 1501, 64, 777)
+    case = _case(ctx, S, heads, 32, 9200 + partition_size)
+    if partition_size == 64:      # the case holds pieces in which some queries see no key
+        assert _pieces_with_blind_queries(ctx, S, heads, 64, case.max_pages * case.page_size) > 0
+    ref, _ = oracle.mla_multi(case, True)
+    _gate(run_mla_multi(case.to("cuda"), True, partition_size), ref,
+          f"mla multi P={partition_size}")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp8"])
+def test_one_query_equals_decode(dt):
+    """S = 1 through the multi-query entry (causal or not) is
+    mla_absorbed_decode / _fp8 bit for bit."""
+    case = wl.make_mla_case(context_lens=(1, 63, 64, 65, 700), num_heads=32, page_size=64,
+                            seed=9300, cache_dtype=dt)
+    dc = case.to("cuda")
+    if dt == "bf16":
+        ref = run_mla(dc)
+    else:
+        B, H = dc.batch, dc.num_heads
+        ref = torch.full((B, H, dc.d_v), float("nan"), dtype=torch.bfloat16, device="cuda")
+        n = pb.mla_absorbed_decode_workspace_size(B, H, dc.max_pages, dc.page_size, 0)
+        ws = torch.full((n,), 0xFF, dtype=torch.uint8, device="cuda")
+        pb.mla_absorbed_decode_fp8(dc.q_nope, dc.q_rope, dc.cache, pb.kv_layout(dc.cache, "PSR"),
+                                   dc.w_uk, dc.w_uv, dc.block_table, dc.context_lens, dc.scale,
+                                   ref, ws)
+        torch.cuda.synchronize()
+        ref = ref.cpu()
+    m = dc.to("cuda")
+    m.q_nope, m.q_rope = dc.q_nope[:, None].contiguous(), dc.q_rope[:, None].contiguous()
+    for causal in (True, False):
+        got = run_mla_multi(m, causal)[:, 0]
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), causal
+
+
+def test_run_to_run_and_workspace_contents():
+    case = _case((5, 300, 2000), 4, 32, 64, 9400).to("cuda")
+    first = run_mla_multi(case, True)
+    n = pb.mla_absorbed_decode_workspace_size(case.batch, 4 * 32, case.max_pages, case.page_size,
+                                              0)
+    junk = torch.full((n,), 0xA5, dtype=torch.uint8, device="cuda")
+    for ws in (None, junk, junk):
+        again = run_mla_multi(case, True, workspace=ws)
+        assert torch.equal(again.view(torch.int16), first.view(torch.int16))
+
+
+def test_rejections():
+    case = _case((5, 9), 2, 16, 16, 9500).to("cuda")
+    B, H = case.batch, case.num_heads
+    ws = torch.zeros(pb.mla_absorbed_decode_workspace_size(B, 2 * H, case.max_pages, 16, 0),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, 2, H, 128), dtype=torch.bfloat16, device="cuda")
+    small = torch.zeros(pb.mla_absorbed_decode_workspace_size(B, H, case.max_pages, 16, 0),
+                        dtype=torch.uint8, device="cuda")
+    with pytest.raises(pb.PaError, match="WORKSPACE"):   # sized for one query, not two
+        pb.mla_absorbed_decode_multiquery(case.q_nope, case.q_rope, case.cache,
+                                          pb.kv_layout(case.cache, "PSR"), case.w_uk, case.w_uv,
+                                          case.block_table, case.context_lens, case.scale, out,
+                                          small)
+    q17 = torch.zeros((B, 17, H, 128), dtype=torch.bfloat16, device="cuda")
+    r17 = torch.zeros((B, 17, H, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(pb.PaError, match="SHAPE"):
+        pb.mla_absorbed_decode_multiquery(q17, r17, case.cache, pb.kv_layout(case.cache, "PSR"),
+                                          case.w_uk, case.w_uv, case.block_table,
+                                          case.context_lens, case.scale, out, ws)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp8"])
+def test_verify_full(oracle, dt):
+    """The verify workload at full size: batch 16, 4 causal queries x 128
+    heads per sequence, ctx U[1024, 8192], page 64."""
+    case = wl.mla_verify(cache_dtype=dt)
+    oracle.set_threads(max(1, min(16, oracle.max_threads())))
+    ref, _ = oracle.mla_multi(case, True)
+    _gate(run_mla_multi(case.to("cuda"), True), ref, f"mla verify bs16 S4 h128 {dt}")
