@@ -101,27 +101,31 @@ struct MlaParams {
 
 // ---- 1. absorption: q_abs = q_nope . W_UK[h] on MFMA, split in three; rope copied ---
 //
-// Block (h, jq, bt): q_abs[r][h][jq*128 .. +128) for the 16 query rows
-// r = 16*bt .. +16 (r = b*S + s: q_nope [B][S][H][128] is [B*S][H][128], and
-// row r*H + h of the result is head s*H + h of sequence b, the numbering of
-// the later kernels), as the product [16 r x 128 d] . [128 d x 128 j] of exact
-// bf16 operands (MFMA, fp32 accumulation).  A = q_nope rows straight from
-// memory (8 consecutive d per lane); B = the W_UK[h] tile staged in LDS
-// row-major ([d][j]) and read with transposed reads, which give each lane
-// 4 consecutive d of one column j.  Wave w computes j tiles 2w and 2w+1.
+// Block (h, jq, bt): q_abs[r][h][jq*128 .. +128) for the query rows
+// r = 64*bt .. +64, in tiles of 16 that share one staged W_UK tile (r = b*S + s:
+// q_nope [B][S][H][128] is [B*S][H][128], and row r*H + h of the result is
+// head s*H + h of sequence b, the numbering of the later kernels).  Each tile
+// is the product [16 r x 128 d] . [128 d x 128 j] of exact bf16 operands
+// (MFMA, fp32 accumulation).  A = q_nope rows straight from memory (8
+// consecutive d per lane); B = the W_UK[h] tile staged in LDS row-major
+// ([d][j]) and read with transposed reads, which give each lane 4
+// consecutive d of one column j.  Wave w computes j tiles 2w and 2w+1.  The
+// three bf16 terms of a tile go through LDS so that each row's 128 columns
+// leave as 16-byte stores.
 constexpr int kWukPad = 128 + 16;  // LDS row stride of the W_UK tile: 72 dwords, conflict-free
+constexpr int kAbsTiles = 4;       // 16-row tiles per absorb block
+constexpr int kAbsOutPad = 128 + 8;
 
 __global__ __launch_bounds__(256) void mla_absorb_kernel(const MlaParams p) {
   __shared__ __align__(16) uint16_t ws[kNope][kWukPad];
+  __shared__ __align__(16) uint16_t os[3][16][kAbsOutPad];   // hi, mid, lo of one tile
   const int h = blockIdx.x;
   const int jq = blockIdx.y;
-  const int b0 = blockIdx.z * 16;
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
   const int g = lane >> 4;
   const int c16 = lane & 15;
-  const int nb = min(16, p.abs_rows - b0);
   const uint16_t* wsrc = p.w_uk + static_cast<int64_t>(h) * kNope * kLat + jq * 128;
   uint4 wst[8];
 #pragma unroll
@@ -129,50 +133,77 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(const MlaParams p) {
     const int c = t + 256 * k;
     wst[k] = load16(wsrc + static_cast<int64_t>(c >> 4) * kLat + (c & 15) * 8);
   }
-  uint4 qa[kNope / 32];                  // A operand: sequence b0 + c16, d = 32ks + 8g .. +8
+  // A operand of a tile: row b0 + c16, d = 32ks + 8g .. +8
+  auto load_a = [&](int b0, int nb, uint4 (&qa)[kNope / 32]) {
 #pragma unroll
-  for (int ks = 0; ks < kNope / 32; ++ks)
-    qa[ks] = c16 < nb ? load16(p.q_nope + (static_cast<int64_t>(b0 + c16) * p.w_heads + h) * kNope +
-                               32 * ks + 8 * g)
-                      : make_uint4(0, 0, 0, 0);
+    for (int ks = 0; ks < kNope / 32; ++ks)
+      qa[ks] = c16 < nb ? load16(p.q_nope + (static_cast<int64_t>(b0 + c16) * p.w_heads + h) * kNope +
+                                 32 * ks + 8 * g)
+                        : make_uint4(0, 0, 0, 0);
+  };
+  const int r0 = blockIdx.z * 16 * kAbsTiles;
+  uint4 qa[kNope / 32];
+  load_a(r0, min(16, p.abs_rows - r0), qa);
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const int c = t + 256 * k;
     *reinterpret_cast<uint4*>(&ws[c >> 4][(c & 15) * 8]) = wst[k];
   }
   __syncthreads();
+  for (int tt = 0; tt < kAbsTiles; ++tt) {
+    const int b0 = r0 + 16 * tt;
+    if (b0 >= p.abs_rows) break;
+    const int nb = min(16, p.abs_rows - b0);
+    uint4 qn[kNope / 32];                // the next tile's A operand, in flight
+    const int b1 = b0 + 16;
+    const bool more = tt + 1 < kAbsTiles && b1 < p.abs_rows;
+    if (more) load_a(b1, min(16, p.abs_rows - b1), qn);
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int nt = 2 * wave + u;
-    f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < 2; ++u) {
+      const int nt = 2 * wave + u;
+      f32x4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < kNope / 32; ++ks) {
-      // lane (g, a) points at rows 32ks + 8g + a/4 (+4), columns 16nt + 4(a%4)
-      const uint16_t* bp = &ws[32 * ks + 8 * g + (c16 >> 2)][16 * nt + 4 * (c16 & 3)];
-      const uint2 k03 = lds_read_tr(bp);
-      const uint2 k47 = lds_read_tr(bp + 4 * kWukPad);
-      c = mfma(qa[ks], make_uint4(k03.x, k03.y, k47.x, k47.y), c);
-    }
-    // D: lane holds q_abs[b0 + 4g + i][jq*128 + 16nt + c16]
-    const int j = jq * 128 + 16 * nt + c16;
+      for (int ks = 0; ks < kNope / 32; ++ks) {
+        // lane (g, a) points at rows 32ks + 8g + a/4 (+4), columns 16nt + 4(a%4)
+        const uint16_t* bp = &ws[32 * ks + 8 * g + (c16 >> 2)][16 * nt + 4 * (c16 & 3)];
+        const uint2 k03 = lds_read_tr(bp);
+        const uint2 k47 = lds_read_tr(bp + 4 * kWukPad);
+        c = mfma(qa[ks], make_uint4(k03.x, k03.y, k47.x, k47.y), c);
+      }
+      // D: lane holds q_abs[b0 + 4g + i][jq*128 + 16nt + c16]
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int bb = 4 * g + i;
-      if (bb < nb) {
+      for (int i = 0; i < 4; ++i) {
         uint16_t hi, mid, lo;
         split3_bf16(c[i], hi, mid, lo);
-        const int64_t row = static_cast<int64_t>(b0 + bb) * p.w_heads + h;
-        p.q_hi[row * kRow + j] = hi;
-        p.q_mid[row * kLat + j] = mid;
-        p.q_lo[row * kLat + j] = lo;
+        os[0][4 * g + i][16 * nt + c16] = hi;
+        os[1][4 * g + i][16 * nt + c16] = mid;
+        os[2][4 * g + i][16 * nt + c16] = lo;
       }
     }
-  }
-  if (jq == 0 && t < nb * (kRope / 8)) {   // rope part: exact bf16, one term
-    const int rb = t / (kRope / 8), rc = t % (kRope / 8);
-    const int64_t row = static_cast<int64_t>(b0 + rb) * p.w_heads + h;
-    *reinterpret_cast<uint4*>(p.q_hi + row * kRow + kLat + 8 * rc) =
-        load16(p.q_rope + row * kRope + 8 * rc);
+    __syncthreads();
+    // 3 terms x 16 rows x 16 chunks of 8 columns, three 16-byte stores per thread
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const int e = t + 256 * k;
+      const int term = e >> 8, bb = (e >> 4) & 15, ch = e & 15;
+      if (bb < nb) {
+        const int64_t row = static_cast<int64_t>(b0 + bb) * p.w_heads + h;
+        uint16_t* dst = term == 0 ? p.q_hi + row * kRow : (term == 1 ? p.q_mid : p.q_lo) + row * kLat;
+        *reinterpret_cast<uint4*>(dst + jq * 128 + 8 * ch) =
+            *reinterpret_cast<const uint4*>(&os[term][bb][8 * ch]);
+      }
+    }
+    __syncthreads();   // os is rewritten by the next tile
+    if (jq == 0 && t < nb * (kRope / 8)) {   // rope part: exact bf16, one term
+      const int rb = t / (kRope / 8), rc = t % (kRope / 8);
+      const int64_t row = static_cast<int64_t>(b0 + rb) * p.w_heads + h;
+      *reinterpret_cast<uint4*>(p.q_hi + row * kRow + kLat + 8 * rc) =
+          load16(p.q_rope + row * kRope + 8 * rc);
+    }
+    if (more) {
+#pragma unroll
+      for (int ks = 0; ks < kNope / 32; ++ks) qa[ks] = qn[ks];
+    }
   }
 }
 
@@ -498,11 +529,11 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(const MlaParams 
   __shared__ int64_t sh[4];
   __shared__ int sh_b;
 
-  const int i = blockIdx.x;
   if (threadIdx.x < 64) {
     const int64_t S = mla_total(p.context_lens, p.batch);
     const int64_t T = S * p.groups;
     const int nb = used_blocks(T, p.split_grid, p.min_keys);
+    const int i = blockIdx.x;
     const int64_t u0 = T * i / nb;
     int b = p.batch;
     int64_t pre = 0;
@@ -516,6 +547,7 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(const MlaParams 
     }
   }
   __syncthreads();
+  const int i = blockIdx.x;
   const int64_t S = sh[0];
   const int64_t u1 = sh[2];
   int64_t u = sh[1];
@@ -543,32 +575,36 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(const MlaParams 
 
 // ---- 3. merge of the partials, then out = W_UV[h] . o_lat on MFMA ---------------------
 //
-// Block (h, bt, s) handles sequences 8*bt .. +8 of head s*H + h (query s,
-// W_UV[h]; hg below is that head's group): row (group hg, b)
-// was cut into pieces by blocks i0 .. i1 of the split (recomputed here from
-// the context lengths), whose partials sit in slots r + i0 .. r + i1 with
-// r = hg*batch + b.  The max M and the total W = sum l_i e^(m_i - M) of a row
-// are wave reductions over its pieces; o_lat is the (l_i e^(m_i - M) / W)-
-// weighted sum of the pieces in ascending i (eight pieces' loads in flight),
-// written to LDS as three bf16 terms; then out[b][dv] = sum_j o_lat[b][j]
-// W_UV[h][dv][j] on MFMA with A = o_lat (rows 8..15 zero) and B = W_UV rows,
-// whose 8 consecutive latent dims per lane are contiguous in memory; wave w
-// computes dv tile w.  An empty context, or a query that sees no key, gives 0.
+// Block (h, bt, s) handles sequences ROWS*bt .. +ROWS (ROWS = 8 or 16) of
+// head s*H + h (query s, W_UV[h]; hg below is that head's group): row
+// (group hg, b) was cut into pieces by blocks i0 .. i1 of the split
+// (recomputed here from the context lengths), whose partials sit in slots
+// r + i0 .. r + i1 with r = hg*batch + b.  The max M and the total
+// W = sum l_i e^(m_i - M) of a row are wave reductions over its pieces; o_lat
+// is the (l_i e^(m_i - M) / W)-weighted sum of the pieces in ascending i
+// (eight pieces' loads in flight), written to LDS as three bf16 terms; then
+// out[b][dv] = sum_j o_lat[b][j] W_UV[h][dv][j] on MFMA with A = o_lat (rows
+// past ROWS zero) and B = W_UV rows, whose 8 consecutive latent dims per lane
+// are contiguous in memory; wave w computes dv tile w.  The W_UV loads are
+// issued first, so they overlap the merge.  An empty context, or a query that
+// sees no key, gives 0.
 constexpr int kMergeThreads = 512;
-constexpr int kMergeRows = 8;
+constexpr int kMergeWaves = kMergeThreads / 64;
 constexpr int kMergeWts = 64;      // piece weights kept in LDS per row
 
+template <int ROWS>
 __global__ __launch_bounds__(kMergeThreads) void mla_merge_uv_kernel(const MlaParams p) {
+  static_assert(ROWS == 8 || ROWS == 16, "rows per block");
   __shared__ __align__(16) uint16_t ohi[16][kLat + 8];
   __shared__ __align__(16) uint16_t omid[16][kLat + 8];
   __shared__ __align__(16) uint16_t olo[16][kLat + 8];
-  __shared__ float wts[kMergeRows][kMergeWts];
-  __shared__ int64_t sh_slot[kMergeRows];
-  __shared__ int sh_cnt[kMergeRows];
-  __shared__ float sh_m[kMergeRows], sh_iw[kMergeRows];
+  __shared__ float wts[ROWS][kMergeWts];
+  __shared__ int64_t sh_slot[ROWS];
+  __shared__ int sh_cnt[ROWS];
+  __shared__ float sh_m[ROWS], sh_iw[ROWS];
   const int hw = blockIdx.x;                       // head of W_UV
   const int h = blockIdx.z * p.w_heads + hw;       // query head
-  const int b0 = blockIdx.y * kMergeRows;
+  const int b0 = blockIdx.y * ROWS;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -576,7 +612,14 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_uv_kernel(const MlaPa
   const int c16 = lane & 15;
   const int hg = h / kGroup;
   const int hl = h % kGroup;
-  const int nrow = min(kMergeRows, p.batch - b0);
+  const int nrow = min(ROWS, p.batch - b0);
+
+  // W_UV[h] rows of dv tile `wave`, all 16 k-steps, in flight from the start
+  const uint16_t* wuv = p.w_uv + static_cast<int64_t>(hw) * kDv * kLat +
+                        static_cast<int64_t>(16 * wave + c16) * kLat + 8 * g;
+  uint4 bw[kLat / 32];
+#pragma unroll
+  for (int ks = 0; ks < kLat / 32; ++ks) bw[ks] = load16(wuv + 32 * ks);
 
   if (tid < 64) {
     const int64_t S = mla_total(p.context_lens, p.batch);
@@ -588,7 +631,7 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_uv_kernel(const MlaPa
     before = wave_sum64(before);
     const int64_t len = (lane < nrow) ? p.context_lens[b0 + lane] : 0;
     const int64_t pre = before + wave_scan64(len) - len;
-    if (lane < kMergeRows) {
+    if (lane < ROWS) {
       int64_t slot = 0;
       int cnt = 0;
       if (lane < nrow && len > 0) {
@@ -602,18 +645,20 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_uv_kernel(const MlaPa
       sh_cnt[lane] = cnt;
     }
   }
-  // rows 8..15 of the MFMA A operand stay zero
-  for (int i = tid; i < kMergeRows * (kLat / 8); i += kMergeThreads) {
-    const int r = kMergeRows + i / (kLat / 8), c8 = (i % (kLat / 8)) * 8;
-    *reinterpret_cast<uint4*>(&ohi[r][c8]) = make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4*>(&omid[r][c8]) = make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4*>(&olo[r][c8]) = make_uint4(0, 0, 0, 0);
+  if constexpr (ROWS < 16) {   // rows ROWS..15 of the MFMA A operand stay zero
+    for (int i = tid; i < (16 - ROWS) * (kLat / 8); i += kMergeThreads) {
+      const int r = ROWS + i / (kLat / 8), c8 = (i % (kLat / 8)) * 8;
+      *reinterpret_cast<uint4*>(&ohi[r][c8]) = make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(&omid[r][c8]) = make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(&olo[r][c8]) = make_uint4(0, 0, 0, 0);
+    }
   }
   __syncthreads();
   // per row: M and W over its pieces, lanes striding over the pieces (max and
-  // sum read together, the first 64 pieces' terms kept); wave w takes row w
-  {
-    const int bb = wave;
+  // sum read together, the first 64 pieces' terms kept); wave w takes rows
+  // w, w + 8
+#pragma unroll
+  for (int bb = wave; bb < ROWS; bb += kMergeWaves) {
     const int cnt = sh_cnt[bb];
     const int64_t slot = sh_slot[bb];
     const bool mine = lane < cnt;
@@ -634,9 +679,10 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_uv_kernel(const MlaPa
     }
   }
   __syncthreads();
-  // o_lat for 8 sequences x 512 dims: wave w takes row w, lane l dims 8l .. 8l+8
-  {
-    const int bb = wave;
+  // o_lat for ROWS sequences x 512 dims: wave w takes rows w, w + 8; lane l
+  // dims 8l .. 8l+8
+#pragma unroll
+  for (int bb = wave; bb < ROWS; bb += kMergeWaves) {
     const int d0 = lane * 8;
     float o[8];
 #pragma unroll
@@ -680,12 +726,7 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_uv_kernel(const MlaPa
                                                          pack_bf16(l8[4], l8[5]), pack_bf16(l8[6], l8[7]));
   }
   __syncthreads();
-  // out[b][dv]: wave w takes dv tile w; all 16 W_UV loads in flight
-  const uint16_t* wuv = p.w_uv + static_cast<int64_t>(hw) * kDv * kLat +
-                        static_cast<int64_t>(16 * wave + c16) * kLat + 8 * g;
-  uint4 bw[kLat / 32];
-#pragma unroll
-  for (int ks = 0; ks < kLat / 32; ++ks) bw[ks] = load16(wuv + 32 * ks);
+  // out[b][dv]: wave w takes dv tile w
   f32x4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < kLat / 32; ++ks) {
@@ -784,6 +825,7 @@ int mla_decode_impl(const void* q_nope, const void* q_rope, const void* kv_cache
   int shift = 0;
   while ((1 << shift) < cache->page_size) ++shift;
   p.page_shift = shift;
+  const int cus = mla_device_cus();
   // Explicit partition size: about that many keys per block.  Library choice:
   // one block per CU (a multiple of 16, so the head groups of a key range
   // share an XCD), each block at least kMlaMinKeys keys.
@@ -791,7 +833,6 @@ int mla_decode_impl(const void* q_nope, const void* q_rope, const void* kv_cache
     p.split_grid = plan.max_blocks;
     p.min_keys = partition_size;
   } else {
-    const int cus = mla_device_cus();
     p.split_grid = std::max(16, std::min(plan.max_blocks, cus / 16 * 16));
     p.min_keys = pa::kMlaMinKeys;
   }
@@ -799,7 +840,7 @@ int mla_decode_impl(const void* q_nope, const void* q_rope, const void* kv_cache
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   pa::clear_error();
-  const int btiles = (p.abs_rows + 15) / 16;
+  const int btiles = (p.abs_rows + 16 * pa::kAbsTiles - 1) / (16 * pa::kAbsTiles);
   hipLaunchKernelGGL(pa::mla_absorb_kernel, dim3(num_heads, pa::kMlaLat / 128, btiles), dim3(256),
                      0, s, p);
   hipError_t e = hipGetLastError();
@@ -817,9 +858,16 @@ int mla_decode_impl(const void* q_nope, const void* q_rope, const void* kv_cache
     hipLaunchKernelGGL((pa::mla_split_kernel<false, false>), sg, st, 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return pa::fail(PA_ERR_LAUNCH, std::string("split: ") + hipGetErrorString(e));
-  hipLaunchKernelGGL(pa::mla_merge_uv_kernel,
-                     dim3(num_heads, (batch + pa::kMergeRows - 1) / pa::kMergeRows, num_queries),
-                     dim3(pa::kMergeThreads), 0, s, p);
+  // 16 sequences per merge block (a full MFMA tile, W_UV read half as often)
+  // when that still gives a block per CU, else 8
+  if (static_cast<int64_t>(num_heads) * num_queries * ((batch + 15) / 16) >= cus)
+    hipLaunchKernelGGL(pa::mla_merge_uv_kernel<16>,
+                       dim3(num_heads, (batch + 15) / 16, num_queries), dim3(pa::kMergeThreads),
+                       0, s, p);
+  else
+    hipLaunchKernelGGL(pa::mla_merge_uv_kernel<8>,
+                       dim3(num_heads, (batch + 7) / 8, num_queries), dim3(pa::kMergeThreads),
+                       0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return pa::fail(PA_ERR_LAUNCH, std::string("merge: ") + hipGetErrorString(e));
   return PA_OK;
