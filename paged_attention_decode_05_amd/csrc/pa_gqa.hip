@@ -613,11 +613,35 @@ __device__ __forceinline__ void fp8x16_bf16(uint4 x, uint4& lo, uint4& hi) {
 // D = 128 geometry per wave).  Their partial scores are summed through LDS in
 // wave order, so every wave has the same scores and the same softmax state,
 // and each writes its own output columns.
+//
+// Issue priority from progress: a SIMD's instruction arbiter prefers its
+// oldest wave, so of the blocks resident on one CU (each owning the same
+// number of keys in the balanced split) the first dispatched pulls ahead,
+// finishes early and leaves its slot idle while the last one is still
+// streaming.  A wave of the balanced split therefore lowers its priority as
+// its block advances (prog = fraction of the block's keys behind it): 3
+// below one half, 2 below three quarters, 1 below nine tenths, then 0.  The
+// leaders yield to the laggards at each step and the blocks of a CU end
+// close together.  Priority changes only the order of issue, never a result.
+__device__ __forceinline__ void progress_priority(float prog, int& cur) {
+  const int lvl = __builtin_amdgcn_readfirstlane(prog < 0.5f ? 3 : prog < 0.75f ? 2 : prog < 0.9f ? 1 : 0);
+  if (lvl == cur) return;
+  cur = lvl;
+  if (lvl == 3) __builtin_amdgcn_s_setprio(3);
+  else if (lvl == 2) __builtin_amdgcn_s_setprio(2);
+  else if (lvl == 1) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
+// prog0, prog_span: the block's progress at `begin` and the share of its
+// keys in [begin, end); prog_span 0 (the fixed partitions) leaves the
+// priority alone.
 template <int D, int G, int NW, int KV>
 __device__ __forceinline__ void attend_range_mfma(const SplitParams& p, int b, int gk, int begin,
                                                   int end, float* out, float* mx, float* sm,
                                                   int64_t hstride, uint16_t* final_out,
-                                                  float* final_lse) {
+                                                  float* final_lse, float prog0 = 0.0f,
+                                                  float prog_span = 0.0f) {
   constexpr int NSL = D > 256 ? NW : 1;   // dim slices
   constexpr int DW = D / NSL;             // dims of one wave
   using mg = MfmaGeo<DW, G, KV>;
@@ -733,7 +757,10 @@ __device__ __forceinline__ void attend_range_mfma(const SplitParams& p, int b, i
     issue_v(0);
   }
   const uint16_t* brow = &vt[4 * g + (c16 >> 2)][4 * (c16 & 3)];
+  int prio = -1;
   for (int k = 0; k < wk.nk; ++k) {
+    if (prog_span > 0.0f)
+      progress_priority(prog0 + prog_span * static_cast<float>(k) / static_cast<float>(wk.nk), prio);
     const int t0 = (wk.c0 + k * wk.step) * KC;
     const bool more = k + 1 < wk.nk;
     f32x4_t sc[SUB];
@@ -961,10 +988,11 @@ template <int D, int G, int NW, int KV = kKvBf16>
 __device__ __forceinline__ void attend_range(const SplitParams& p, int b, int gk, int begin,
                                              int end, float* out, float* mx, float* sm,
                                              int64_t hstride, uint16_t* final_out = nullptr,
-                                             float* final_lse = nullptr) {
+                                             float* final_lse = nullptr, float prog0 = 0.0f,
+                                             float prog_span = 0.0f) {
   if constexpr (KV != kKvBf16 || kUseMfma<D, G>)
     attend_range_mfma<D, G, NW, KV>(p, b, gk, begin, end, out, mx, sm, hstride, final_out,
-                                    final_lse);
+                                    final_lse, prog0, prog_span);
   else
     attend_range_valu<D, G, NW>(p, b, gk, begin, end, out, mx, sm, hstride, final_out, final_lse);
 }
@@ -1122,7 +1150,9 @@ void balanced_split_kernel(const SplitParams p, const BalancedLayout bl) {
       attend_range<D, G, kWaves, KV>(p, b, gk, begin, end, bl.seg_out + slot * G * D,
                                  bl.seg_max + slot * G, bl.seg_sum + slot * G, 1,
                                  whole ? bl.out + h0 * D : nullptr,
-                                 (whole && bl.lse) ? bl.lse + h0 : nullptr);
+                                 (whole && bl.lse) ? bl.lse + h0 : nullptr,
+                                 static_cast<float>(x0 - s0) / static_cast<float>(s1 - s0),
+                                 static_cast<float>(x1 - x0) / static_cast<float>(s1 - s0));
       // the block holding a row's first piece records where its pieces are:
       // slots r + i .. r + i + count - 1 (count 1: written here already)
       if (x0 == off && threadIdx.x == 0)
