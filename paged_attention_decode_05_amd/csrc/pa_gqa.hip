@@ -619,12 +619,19 @@ __device__ __forceinline__ void fp8x16_bf16(uint4 x, uint4& lo, uint4& hi) {
 // number of keys in the balanced split) the first dispatched pulls ahead,
 // finishes early and leaves its slot idle while the last one is still
 // streaming.  A wave of the balanced split therefore lowers its priority as
-// its block advances (prog = fraction of the block's keys behind it): 3
-// below one half, 2 below three quarters, 1 below nine tenths, then 0.  The
-// leaders yield to the laggards at each step and the blocks of a CU end
-// close together.  Priority changes only the order of issue, never a result.
-__device__ __forceinline__ void progress_priority(float prog, int& cur) {
-  const int lvl = __builtin_amdgcn_readfirstlane(prog < 0.5f ? 3 : prog < 0.75f ? 2 : prog < 0.9f ? 1 : 0);
+// its block advances: 3 until the block has passed one half of its keys, 2
+// until three quarters, 1 until nine tenths, then 0.  The leaders yield to
+// the laggards at each step and the blocks of a CU end close together.
+// Priority changes only the order of issue, never a result.  The steps are
+// given as key indices of the range's row, so the loop only compares
+// wave-uniform integers.
+struct PrioKeys {
+  bool on;
+  int t50, t75, t90;   // first key at which the block has passed 1/2, 3/4, 9/10 of its keys
+};
+
+__device__ __forceinline__ void progress_priority(const PrioKeys& pk, int t, int& cur) {
+  const int lvl = 3 - (t >= pk.t50 ? 1 : 0) - (t >= pk.t75 ? 1 : 0) - (t >= pk.t90 ? 1 : 0);
   if (lvl == cur) return;
   cur = lvl;
   if (lvl == 3) __builtin_amdgcn_s_setprio(3);
@@ -633,15 +640,14 @@ __device__ __forceinline__ void progress_priority(float prog, int& cur) {
   else __builtin_amdgcn_s_setprio(0);
 }
 
-// prog0, prog_span: the block's progress at `begin` and the share of its
-// keys in [begin, end); prog_span 0 (the fixed partitions) leaves the
-// priority alone.
+// pk: where the block's progress steps fall (pk.on false, as for the fixed
+// partitions, leaves the priority alone).
 template <int D, int G, int NW, int KV>
 __device__ __forceinline__ void attend_range_mfma(const SplitParams& p, int b, int gk, int begin,
                                                   int end, float* out, float* mx, float* sm,
                                                   int64_t hstride, uint16_t* final_out,
-                                                  float* final_lse, float prog0 = 0.0f,
-                                                  float prog_span = 0.0f) {
+                                                  float* final_lse,
+                                                  const PrioKeys& pk = PrioKeys{false, 0, 0, 0}) {
   constexpr int NSL = D > 256 ? NW : 1;   // dim slices
   constexpr int DW = D / NSL;             // dims of one wave
   using mg = MfmaGeo<DW, G, KV>;
@@ -759,9 +765,8 @@ __device__ __forceinline__ void attend_range_mfma(const SplitParams& p, int b, i
   const uint16_t* brow = &vt[4 * g + (c16 >> 2)][4 * (c16 & 3)];
   int prio = -1;
   for (int k = 0; k < wk.nk; ++k) {
-    if (prog_span > 0.0f)
-      progress_priority(prog0 + prog_span * static_cast<float>(k) / static_cast<float>(wk.nk), prio);
     const int t0 = (wk.c0 + k * wk.step) * KC;
+    if (pk.on) progress_priority(pk, t0, prio);
     const bool more = k + 1 < wk.nk;
     f32x4_t sc[SUB];
 #pragma unroll
@@ -988,11 +993,11 @@ template <int D, int G, int NW, int KV = kKvBf16>
 __device__ __forceinline__ void attend_range(const SplitParams& p, int b, int gk, int begin,
                                              int end, float* out, float* mx, float* sm,
                                              int64_t hstride, uint16_t* final_out = nullptr,
-                                             float* final_lse = nullptr, float prog0 = 0.0f,
-                                             float prog_span = 0.0f) {
+                                             float* final_lse = nullptr,
+                                             const PrioKeys& pk = PrioKeys{false, 0, 0, 0}) {
   if constexpr (KV != kKvBf16 || kUseMfma<D, G>)
     attend_range_mfma<D, G, NW, KV>(p, b, gk, begin, end, out, mx, sm, hstride, final_out,
-                                    final_lse, prog0, prog_span);
+                                    final_lse, pk);
   else
     attend_range_valu<D, G, NW>(p, b, gk, begin, end, out, mx, sm, hstride, final_out, final_lse);
 }
@@ -1147,12 +1152,16 @@ void balanced_split_kernel(const SplitParams p, const BalancedLayout bl) {
       const int64_t r = static_cast<int64_t>(b) * hkv + gk;
       const int64_t slot = r + i;
       const int64_t h0 = static_cast<int64_t>(b) * p.num_q_heads + static_cast<int64_t>(gk) * gq;
+      // key of this row at which the block has passed num/den of its units
+      auto key_at = [&](int num, int den) {
+        const int64_t t = lo + (s0 + (s1 - s0) * num / den - off);
+        return static_cast<int>(t < -(1 << 30) ? -(1 << 30) : t > (1 << 30) ? (1 << 30) : t);
+      };
+      const PrioKeys pk{true, key_at(1, 2), key_at(3, 4), key_at(9, 10)};
       attend_range<D, G, kWaves, KV>(p, b, gk, begin, end, bl.seg_out + slot * G * D,
                                  bl.seg_max + slot * G, bl.seg_sum + slot * G, 1,
                                  whole ? bl.out + h0 * D : nullptr,
-                                 (whole && bl.lse) ? bl.lse + h0 : nullptr,
-                                 static_cast<float>(x0 - s0) / static_cast<float>(s1 - s0),
-                                 static_cast<float>(x1 - x0) / static_cast<float>(s1 - s0));
+                                 (whole && bl.lse) ? bl.lse + h0 : nullptr, pk);
       // the block holding a row's first piece records where its pieces are:
       // slots r + i .. r + i + count - 1 (count 1: written here already)
       if (x0 == off && threadIdx.x == 0)
