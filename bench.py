@@ -54,7 +54,7 @@ def parse():
     ap.add_argument("--workload", default="llama",
                     choices=["tiny", "llama", "d256w", "long", "mla", "verify", "insert",
                              "llama_fp8", "llama_f32", "d512", "mla_fp8", "mla_verify",
-                             "mla_verify_fp8"])
+                             "mla_verify_fp8", "long_splitkv"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run K device-to-device copies of a 1 GiB buffer instead (reference "
@@ -97,6 +97,8 @@ def main() -> int:
         return bench_verify(a, torch, pb, wl, dev)
     if a.workload == "insert":
         return bench_insert(a, torch, pb, wl, dev)
+    if a.workload == "long_splitkv":
+        return bench_splitkv(a, torch, pb, wl, dev)
     log(f"generating workload {a.workload} (seeded) ...")
     t0 = time.time()
     cases = [wl.NAMED[a.workload](poison=False, seed=wl.SEED_BASE + 100 * i + {
@@ -353,6 +355,37 @@ def bench_insert(a, torch, pb, wl, dev) -> int:
                  nbytes, ms, mean, calls,
                  {"workload": "KV insert of an 8192-token chunk into the llama-shaped pools",
                   "tokens": T}, "pa_kv_insert call: kv_insert_kernel")
+
+
+def bench_splitkv(a, torch, pb, wl, dev) -> int:
+    """The long-context workload through the fixed-partition path: 512-key
+    partitions, per-partition (max, sum, partial out) in fp32 from
+    pa_decode_splitkv, then pa_merge_lse in ascending partition order."""
+    P = 512
+    log("generating workload long (seeded) ...")
+    case = wl.long_ctx(poison=False)
+    dc = case.to(dev)
+    B, H, D = case.q.shape
+    maxp = (int(case.context_lens.max()) + P - 1) // P
+    part_out = torch.empty((B, H, maxp, D), dtype=torch.float32, device=dev)
+    part_max = torch.empty((B, H, maxp), dtype=torch.float32, device=dev)
+    part_sum = torch.empty((B, H, maxp), dtype=torch.float32, device=dev)
+    out = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
+    kv = pb.kv_layout(dc.k_pool, dc.layout)
+
+    def step(i):
+        pb.pa_decode_splitkv(dc.q, dc.k_pool, dc.v_pool, kv, dc.block_table, dc.context_lens,
+                             dc.scale, dc.window, P, maxp, part_out, part_max, part_sum)
+        pb.pa_merge_lse(part_out, part_max, part_sum, dc.context_lens, P, dc.window, out)
+
+    ms, mean, calls = _timed(a, torch, step)
+    return _line(a, METRIC, case.kv_bytes(), ms, mean, calls,
+                 {"workload": "long context bs4, ctx 32K-128K, d128, fixed 512-key partitions",
+                  "batch": B, "num_q_heads": H, "num_kv_heads": case.num_kv_heads, "head_dim": D,
+                  "page_size": case.page_size, "sum_context": int(case.context_lens.sum()),
+                  "partition_size": P, "max_partitions": maxp,
+                  "partial_bytes_written": int(part_out.numel() * 4 + 2 * part_max.numel() * 4)},
+                 "pa_decode_splitkv + pa_merge_lse calls: split_kernel + merge_kernel")
 
 
 def bench_mla(a, torch, pb, wl, dev) -> int:
