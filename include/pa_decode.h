@@ -103,8 +103,9 @@ typedef struct pa_kv_layout {
  * Requires partition_size >= 1 and max_partitions * partition_size >= the
  * largest possible attended range (min(window, max_pages_per_seq *
  * page_size) with a window, else max_pages_per_seq * page_size); supported
- * head_dim 64, 128 or 512 with 1/2/4/8/16 q heads per KV head, head_dim
- * 256 with 1/2/4/8; page_size 16/32/64.
+ * head_dim 64, 128, 256 or 512 with 1 to 16 q heads per KV head (a group
+ * that is not a power of two runs on the kernel built for the next one,
+ * its padding heads masked); page_size 16/32/64.
  * ------------------------------------------------------------------------- */
 PA_API int pa_decode_splitkv(const void* q, const void* k_pool, const void* v_pool,
                       const pa_kv_layout* kv, const int32_t* block_table,
@@ -129,8 +130,11 @@ PA_API int pa_decode_splitkv(const void* q, const void* k_pool, const void* v_po
  *
  * Arguments as written by pa_decode_splitkv with the same partition_size,
  * max_partitions and window; max_partitions must cover every sequence's live
- * partitions (not checked: the context lengths live on the device).  out [batch][num_q_heads][head_dim] bf16;
- * lse_out [batch][num_q_heads] fp32 or NULL.  head_dim 64, 128, 256 or 512.
+ * partitions (not checked: the context lengths live on the device).  A row
+ * with more live partitions than that (outside the contract) merges its
+ * first max_partitions and reads nothing past its own partials.
+ * out [batch][num_q_heads][head_dim] bf16; lse_out [batch][num_q_heads]
+ * fp32 or NULL.  head_dim 64, 128, 256 or 512.
  * ------------------------------------------------------------------------- */
 PA_API int pa_merge_lse(const float* part_out, const float* part_max,
                  const float* part_sum, const int32_t* context_lens,
@@ -149,17 +153,24 @@ PA_API int pa_merge_lse(const float* part_out, const float* part_max,
  * KERNEL-ATTN-MLA-SPARSE, W4: split-KV with a fixed, ordered merge].  A row
  * that one range covers is written directly; a row cut by range boundaries
  * gets one partial per piece, merged in ascending order as in pa_merge_lse.
- * The cut points are computed on the device from context_lens, so a row's
- * result may differ in the last bits when other sequences' lengths change;
- * for fixed inputs the result is deterministic run to run and does not
- * depend on where the pages sit in the pool.
+ * The cut points are computed on the device from context_lens and a block
+ * count fixed by the build (resident blocks per compute unit x 256), not by
+ * the device: a row's result may differ in the last bits when other
+ * sequences' lengths change; for fixed inputs the result is deterministic
+ * run to run, the same on every gfx950 device, and does not depend on where
+ * the pages sit in the pool.
  *
+ * Any 1 to 16 q heads per KV head, at head_dim 64, 128, 256 or 512.
  * out [batch][num_q_heads][head_dim] bf16; lse_out [batch][num_q_heads] fp32
  * (natural log of the softmax denominator, -inf for an empty row) or NULL.
  * workspace: device memory of at least pa_decode_workspace_size(...) bytes,
  * 256-byte aligned, owned by the caller and clobbered by the call; it needs
  * no initialisation (every call rewrites what it later reads) and keeps no
  * state between calls.  Two calls must not share a workspace while both run.
+ * workspace NULL (workspace_bytes ignored): no split -- one workgroup per
+ * (sequence, KV head) row writes that row's bf16 output directly, so the
+ * call needs no memory beyond its arguments, at the price of balance: the
+ * longest row sets the time.  Its bits are fixed by the row alone.
  * ------------------------------------------------------------------------- */
 PA_API int pa_decode(const void* q, const void* k_pool, const void* v_pool,
               const pa_kv_layout* kv, const int32_t* block_table,
@@ -184,11 +195,11 @@ PA_API int pa_decode(const void* q, const void* k_pool, const void* v_pool,
  * query with no key gives out = 0 and lse = -inf.
  *
  * q [batch][S][num_q_heads][head_dim] bf16; out the same shape; lse_out
- * [batch][S][num_q_heads] fp32 or NULL.  1 <= S <= 16, and S rounded up to a
- * power of two times num_q_heads / num_kv_heads must be 1, 2, 4, 8 or 16
- * (head_dim 64, 128, 512) or 1, 2, 4, 8 (head_dim 256).  workspace: at least
+ * [batch][S][num_q_heads] fp32 or NULL.  1 <= S <= 16, and S times
+ * num_q_heads / num_kv_heads must be at most 16.  workspace: at least
  * pa_decode_multiquery_workspace_size(...) bytes, 256-byte aligned,
- * clobbered.  S = 1 gives exactly pa_decode.  Other arguments as pa_decode.
+ * clobbered, or NULL as for pa_decode.  S = 1 gives exactly pa_decode.
+ * Other arguments as pa_decode.
  * ------------------------------------------------------------------------- */
 PA_API int pa_decode_multiquery(const void* q, const void* k_pool, const void* v_pool,
                                 const pa_kv_layout* kv, const int32_t* block_table,
@@ -234,8 +245,8 @@ PA_API int pa_decode_fp8(const void* q, const void* k_pool, const void* v_pool,
  * loader's float instantiation beside the bf16 one; vllm.cpp kernel matrix,
  * inventory row: the paged path admits F32/BF16].  Every element is split
  * exactly into three bf16 terms on the matrix cores, so the score and P.V
- * products are exact and the sums fp32, as in pa_decode.  head_dim 64, 128
- * or 512 (PA_ERR_UNSUPPORTED for 256); strides in elements, rows on 16-byte
+ * products are exact and the sums fp32, as in pa_decode.  head_dim 64, 128,
+ * 256 or 512; strides in elements, rows on 16-byte
  * boundaries (strides multiples of 4).  workspace: at least
  * pa_decode_workspace_size(...) bytes for the same shapes.  Other arguments,
  * the split, determinism and the error codes as pa_decode.
@@ -283,10 +294,11 @@ PA_API int32_t pa_decode_partition_size(int32_t batch, int32_t num_q_heads,
  * products as three bf16 terms that sum to the fp32 value exactly, so only
  * fp32 accumulation rounds.  The keys of every (64-head group, sequence) row,
  * laid end to end, are cut into equal contiguous ranges, one per workgroup
- * (about partition_size keys each, or the library's choice for 0); the
- * pieces of a row are merged by log-sum-exp in ascending order; an empty
- * context gives 0.  Deterministic run to run and independent of page
- * placement.
+ * (about partition_size keys each, or for 0 the library's choice, a count
+ * fixed by the build rather than the device); the pieces of a row are
+ * merged by log-sum-exp in ascending order; an empty context gives 0.
+ * Deterministic run to run, the same on every gfx950 device, and
+ * independent of page placement.
  *
  * q_nope [batch][num_heads][128] bf16; q_rope [batch][num_heads][64] bf16;
  * kv_cache: pool described by *cache (num_kv_heads 1, head_dim 576,

@@ -38,10 +38,29 @@ def hipcc() -> str:
 
 
 def build(resource_usage: bool = False, verbose: bool = False, out: str = LIB) -> str:
+    """Compile every source to an object in parallel (no relocatable device
+    code: each source holds its own kernels), then link the shared library."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    objdir = os.path.join(ROOT, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+
+    def compile_one(src: str) -> str:
+        obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+        cmd = [hipcc(), *compile_flags, "-c", os.path.join(CSRC, src), "-o", obj]
+        if resource_usage:
+            cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        return obj
+
+    jobs = max(1, min(len(SOURCES), int(os.environ.get("MAX_JOBS", "8") or 8)))
+    with ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(compile_one, SOURCES))
     tmp = out + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
-    if resource_usage:
-        cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

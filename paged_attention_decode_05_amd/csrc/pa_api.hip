@@ -32,21 +32,6 @@ int launch_status(hipError_t e, const char* what) {
   return pa::fail(PA_ERR_LAUNCH, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-// Compute units of the current device (cached per device; threads that race
-// on the first call store the same value).
-int device_cus() {
-  static std::atomic<int> cus[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int n = cus[dev].load(std::memory_order_relaxed);
-  if (n == 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
-      n = 256;
-    cus[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
-
 int ilog2(int v) {
   int s = 0;
   while ((1 << s) < v) ++s;
@@ -84,7 +69,8 @@ pa::SplitParams split_params(const void* q, const void* k_pool, const void* v_po
   p.window = window;
   p.num_queries = 1;
   p.q_heads = num_q_heads;
-  p.group_shift = ilog2(num_q_heads / kv->num_kv_heads);
+  p.gq = num_q_heads / kv->num_kv_heads;
+  p.vheads = p.gq;
   p.causal = 1;
   p.reach = window;
   p.partition_size = partition_size;
@@ -115,7 +101,7 @@ int pa_decode_splitkv(const void* q, const void* k_pool, const void* v_pool,
                                          context_lens, num_q_heads, scale, window, partition_size,
                                          max_partitions, part_out, part_max, part_sum, 1);
   pa::clear_error();
-  return launch_status(pa::launch_split(p, kv->head_dim, num_q_heads / kv->num_kv_heads, batch,
+  return launch_status(pa::launch_split(p, kv->head_dim, pa::group_padded(p.gq), batch,
                                         kv->num_kv_heads, static_cast<hipStream_t>(stream)),
                        "split kernel");
 }
@@ -147,8 +133,9 @@ size_t pa_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_
                                 int32_t head_dim, int32_t max_pages_per_seq, int32_t page_size,
                                 int32_t window) {
   pa::DecodePlan plan;
-  if (!pa::plan_decode(batch, num_q_heads, num_kv_heads, head_dim, max_pages_per_seq, page_size,
-                       window, &plan))
+  if (num_kv_heads < 1 || num_q_heads < 1 || num_q_heads % num_kv_heads ||
+      !pa::plan_decode(batch, num_kv_heads, num_q_heads / num_kv_heads, head_dim,
+                       max_pages_per_seq, page_size, window, &plan))
     return 0;
   return plan.bytes;
 }
@@ -179,8 +166,6 @@ int decode_impl(const void* q, const void* k_pool, const void* v_pool, const pa_
   int rc = pa::check_gqa(q, k_pool, v_pool, kv, block_table, block_table_stride, context_lens,
                          batch, num_q_heads, max_pages_per_seq, scale, elem_bytes);
   if (rc) return rc;
-  if (kv_type == 2 && kv->head_dim == 256)
-    return pa::fail(PA_ERR_UNSUPPORTED, "f32 pools take head_dim 64, 128 or 512");
   if (fp8 && !(std::isfinite(k_scale) && k_scale > 0.0f && std::isfinite(v_scale) &&
                v_scale > 0.0f))
     return pa::fail(PA_ERR_SHAPE, "k_scale and v_scale must be finite and > 0");
@@ -189,39 +174,44 @@ int decode_impl(const void* q, const void* k_pool, const void* v_pool, const pa_
   if (!out) return pa::fail(PA_ERR_NULL, "out must not be NULL");
   if (reinterpret_cast<uintptr_t>(out) & 15u)
     return pa::fail(PA_ERR_ALIGN, "out must be 16-byte aligned");
-  const int qpad = pa::queries_padded(num_queries);
   const int group = num_q_heads / kv->num_kv_heads;
-  if (qpad < 1 || !pa::group_supported(kv->head_dim, qpad * group))
-    return pa::fail(PA_ERR_UNSUPPORTED, "num_queries (rounded up to a power of two) times the "
-                                        "q heads per KV head must be a supported group size");
+  const int vheads = num_queries * group;   // live heads of one KV group
+  if (vheads > 16)
+    return pa::fail(PA_ERR_UNSUPPORTED, "num_queries times the q heads per KV head must be <= 16");
   pa::DecodePlan plan;
-  if (!pa::plan_decode(batch, num_q_heads * qpad, kv->num_kv_heads, kv->head_dim,
-                       max_pages_per_seq, kv->page_size, window, &plan))
+  if (!pa::plan_decode(batch, kv->num_kv_heads, vheads, kv->head_dim, max_pages_per_seq,
+                       kv->page_size, window, &plan))
     return pa::fail(PA_ERR_SHAPE, "no launch plan for these shapes");
-  if (!workspace || workspace_bytes < plan.bytes)
-    return pa::fail(PA_ERR_WORKSPACE, "workspace must hold " + std::to_string(plan.bytes) + " bytes");
+  // No workspace: one block per (sequence, KV head) row, outputs written
+  // directly.  With one: the balanced split and the merge of cut rows.
+  if (workspace && workspace_bytes < plan.bytes)
+    return pa::fail(PA_ERR_WORKSPACE, "workspace must hold " + std::to_string(plan.bytes) +
+                                          " bytes (or be NULL)");
   if (reinterpret_cast<uintptr_t>(workspace) & 255u)
     return pa::fail(PA_ERR_ALIGN, "workspace must be 256-byte aligned");
   char* ws = static_cast<char*>(workspace);
-  const int vgroup = qpad * group;
-  const int nbmax =
-      pa::balanced_grid(kv->head_dim, vgroup, device_cus(), pa::kMaxBalancedBlocks, kv_type);
+  const int vgroup = plan.group;
+  int nbmax = pa::balanced_grid(kv->head_dim, vgroup, pa::kSplitCUs, pa::kMaxBalancedBlocks, kv_type);
   if (nbmax < 1) return pa::fail(PA_ERR_UNSUPPORTED, "no balanced-split kernel for these shapes");
 
   pa::BalancedLayout bl{};
   bl.context_lens = context_lens;
   bl.out = static_cast<uint16_t*>(out);
   bl.lse = lse_out;
-  bl.seg_out = reinterpret_cast<float*>(ws + plan.off_seg_out);
-  bl.seg_max = reinterpret_cast<float*>(ws + plan.off_seg_max);
-  bl.seg_sum = reinterpret_cast<float*>(ws + plan.off_seg_sum);
-  bl.row_info = reinterpret_cast<int32_t*>(ws + plan.off_row_info);
+  if (ws) {
+    bl.seg_out = reinterpret_cast<float*>(ws + plan.off_seg_out);
+    bl.seg_max = reinterpret_cast<float*>(ws + plan.off_seg_max);
+    bl.seg_sum = reinterpret_cast<float*>(ws + plan.off_seg_sum);
+    bl.row_info = reinterpret_cast<int32_t*>(ws + plan.off_row_info);
+  } else {
+    nbmax = plan.rows < (1 << 20) ? plan.rows : (1 << 20);   // one block per row
+  }
   bl.min_units = pa::kMinUnitsPerBlock;
   bl.rows = plan.rows;
   bl.batch = batch;
   bl.q_heads = num_q_heads;
-  bl.group_shift = ilog2(group);
-  bl.num_queries = num_queries;
+  bl.gq = group;
+  bl.vheads = vheads;
 
   pa::SplitParams sp = split_params(q, k_pool, v_pool, kv, block_table, block_table_stride,
                                     context_lens, num_q_heads, fp8 ? scale * k_scale : scale,
@@ -229,6 +219,7 @@ int decode_impl(const void* q, const void* k_pool, const void* v_pool, const pa_
   if (fp8) sp.out_scale = v_scale;
   sp.num_q_heads = num_q_heads * num_queries;   // rows of q and out per sequence
   sp.num_queries = num_queries;
+  sp.vheads = vheads;
   sp.causal = causal ? 1 : 0;
   sp.reach = (window > 0 && causal) ? window + num_queries - 1 : window;
   pa::clear_error();
@@ -289,11 +280,12 @@ size_t pa_decode_multiquery_workspace_size(int32_t batch, int32_t num_q_heads,
                                            int32_t num_kv_heads, int32_t head_dim,
                                            int32_t max_pages_per_seq, int32_t page_size,
                                            int32_t window, int32_t num_queries) {
-  const int qpad = pa::queries_padded(num_queries);
-  if (qpad < 1 || num_queries > 16) return 0;
+  if (num_queries < 1 || num_queries > 16 || num_kv_heads < 1 || num_q_heads < 1 ||
+      num_q_heads % num_kv_heads)
+    return 0;
   pa::DecodePlan plan;
-  if (!pa::plan_decode(batch, num_q_heads * qpad, num_kv_heads, head_dim, max_pages_per_seq,
-                       page_size, window, &plan))
+  if (!pa::plan_decode(batch, num_kv_heads, num_queries * (num_q_heads / num_kv_heads), head_dim,
+                       max_pages_per_seq, page_size, window, &plan))
     return 0;
   return plan.bytes;
 }

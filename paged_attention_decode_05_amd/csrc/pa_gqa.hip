@@ -246,14 +246,14 @@ __device__ __forceinline__ void load_v(VRegs<D, G>& vr, const WaveKeys& wk, int 
   }
 }
 
-// Virtual head h of a KV group is query h >> group_shift, q head
-// h & (gq - 1); its q and out rows sit head_offset(h) rows after the group's
-// first row.  With one query, head_offset(h) = h.  Queries past the last real
-// one (the query count rounded up to a power of two) repeat it and write no
-// output.
+// Virtual head h of a KV group is query h / gq, q head h % gq; its q and out
+// rows sit head_offset(h) rows after the group's first row.  With one query,
+// head_offset(h) = h.  Padding heads (h >= vheads) alias head 0 for their q
+// loads and write no output.
 __device__ __forceinline__ int64_t head_offset(const SplitParams& p, int h) {
-  const int gq = 1 << p.group_shift;
-  return static_cast<int64_t>(min(h >> p.group_shift, p.num_queries - 1) * p.q_heads + (h & (gq - 1)));
+  const int hh = h < p.vheads ? h : 0;
+  const int s = hh / p.gq;
+  return static_cast<int64_t>(s) * p.q_heads + (hh - s * p.gq);
 }
 
 // Keys [lo, hi) that head h of sequence b may see, within [begin, end): query
@@ -261,7 +261,7 @@ __device__ __forceinline__ int64_t head_offset(const SplitParams& p, int h) {
 // counts back from its last key.  With one query this is [begin, end) itself.
 __device__ __forceinline__ void head_bounds(const SplitParams& p, int n, int h, int begin, int end,
                                             int& lo_h, int& hi_h) {
-  const int sq = min(h >> p.group_shift, p.num_queries - 1);
+  const int sq = (h < p.vheads ? h : 0) / p.gq;
   const int hi = p.causal ? min(n, n - p.num_queries + 1 + sq) : n;
   const int lo = p.window > 0 ? max(0, hi - p.window) : 0;
   lo_h = max(lo, begin);
@@ -297,6 +297,7 @@ __device__ __forceinline__ void write_range(const SplitParams& p, const float* r
   for (int i = threadIdx.x; i < G * D4; i += 64 * NW) {
     const int h = i / D4;
     const int d = (i % D4) * 4;
+    if (h >= p.vheads) continue;     // padding head
     float M = red_mt[0][h];
 #pragma unroll
     for (int w = 1; w < NS; ++w) M = fmaxf(M, red_mt[w][h]);
@@ -316,7 +317,6 @@ __device__ __forceinline__ void write_range(const SplitParams& p, const float* r
     const bool any = W > 0.0f;
     const float inv = any ? p.out_scale / W : 0.0f;   // out_scale: V pool scale (1 for bf16)
     if (final_out) {
-      if ((h >> p.group_shift) >= p.num_queries) continue;   // padding query
       const int64_t ho = head_offset(p, h);
       uint2 packed;
       packed.x = pack_bf16(f32_to_bf16_rne(o.x * inv), f32_to_bf16_rne(o.y * inv));
@@ -382,8 +382,7 @@ __device__ __forceinline__ void attend_range_valu(const SplitParams& p, int b, i
   const int koff = (lane / g::LQ) * p.token_bytes + 16 * (lane % g::LQ);
   const int voff0 = (lane / g::LV) * p.token_bytes + 16 * (lane % g::LV);
 
-  const int gq = 1 << p.group_shift;
-  const int64_t row0 = static_cast<int64_t>(b) * p.num_q_heads + static_cast<int64_t>(gk) * gq;
+  const int64_t row0 = static_cast<int64_t>(b) * p.num_q_heads + static_cast<int64_t>(gk) * p.gq;
 
   // q pieces, pre-permuted per lane: slot h holds head h ^ pi.
   uint4 qv[G][g::NQL];
@@ -550,7 +549,7 @@ __device__ __forceinline__ void attend_range_valu(const SplitParams& p, int b, i
 //           split into three bf16 terms hi + mid + lo, which represent the fp32
 //           value exactly; B = V columns from the wave's LDS tile (row-major,
 //           rows padded to D + 16 elements) by transposed reads.
-// Heads c >= G (G = 8) get q = 0 and are masked out.  The loads of chunk k+1
+// Padding heads (c >= vheads) get q = 0 and write nothing.  The loads of chunk k+1
 // are issued as soon as chunk k's registers are free: K after the scores, V
 // after its LDS write.
 //
@@ -697,9 +696,8 @@ __device__ __forceinline__ void attend_range_mfma(const SplitParams& p, int b, i
   const uint16_t* vbase = reinterpret_cast<const uint16_t*>(
       reinterpret_cast<const char*>(p.v) + static_cast<int64_t>(gk) * p.head_stride * mg::EB + slice_bytes);
 
-  const int gq = 1 << p.group_shift;
-  const int64_t row0 = static_cast<int64_t>(b) * p.num_q_heads + static_cast<int64_t>(gk) * gq;
-  const bool head_live = c16 < G;
+  const int64_t row0 = static_cast<int64_t>(b) * p.num_q_heads + static_cast<int64_t>(gk) * p.gq;
+  const bool head_live = c16 < p.vheads;
 
   // B operand of the scores: q of head c16, dims 32ks + 8g .. +8 (bf16 pools)
   // or 64j + 16g + 8(ks & 1) .. +8 with j = ks / 2 (FP8 pools)
@@ -983,7 +981,7 @@ constexpr bool kUseMfma = G >= 4 || D == 64 || D == 512;
 // Waves per SIMD the compiler must fit the range kernels' registers into.
 // (head_dim 512 holds the D = 128 registers per wave)
 template <int D, int G, int KV = kKvBf16>
-constexpr int kMinWaves = KV == kKvF32 ? (D == 64 ? 3 : 2)
+constexpr int kMinWaves = KV == kKvF32 ? (D == 64 ? 3 : D == 256 ? 1 : 2)
                           : (KV != kKvBf16 || kUseMfma<D, G>)
                               ? (D == 64 ? 4 : (D == 128 || D == 512) ? 3 : 2)
                               : 1;
@@ -1012,15 +1010,15 @@ void split_kernel(const SplitParams p) {
   const int n = p.context_lens[b];
   const int lo = p.window > 0 ? max(0, n - p.window) : 0;
   const int64_t begin64 = static_cast<int64_t>(lo) + static_cast<int64_t>(j) * p.partition_size;
-  const int64_t rowbase = (static_cast<int64_t>(b) * p.num_q_heads + static_cast<int64_t>(gk) * G) *
-                          p.max_parts + j;   // index of (b, h = gk*G, j)
+  const int64_t rowbase = (static_cast<int64_t>(b) * p.num_q_heads + static_cast<int64_t>(gk) * p.gq) *
+                          p.max_parts + j;   // index of (b, h = gk*Gq, j)
   if (begin64 >= n) {
     if (p.write_empty) {
-      for (int i = threadIdx.x; i < G * D; i += kBlock) {
+      for (int i = threadIdx.x; i < p.vheads * D; i += kBlock) {
         const int h = i / D;
         p.part_out[(rowbase + static_cast<int64_t>(h) * p.max_parts) * D + (i % D)] = 0.0f;
       }
-      if (threadIdx.x < G) {
+      if (threadIdx.x < p.vheads) {
         p.part_max[rowbase + static_cast<int64_t>(threadIdx.x) * p.max_parts] = -INFINITY;
         p.part_sum[rowbase + static_cast<int64_t>(threadIdx.x) * p.max_parts] = 0.0f;
       }
@@ -1106,7 +1104,23 @@ void balanced_split_kernel(const SplitParams p, const BalancedLayout bl) {
     for (int j = threadIdx.x; j < p.num_q_heads * D; j += kBlock) bl.out[r0 * D + j] = 0;
     if (bl.lse)
       for (int j = threadIdx.x; j < p.num_q_heads; j += kBlock) bl.lse[r0 + j] = -INFINITY;
-    for (int g = threadIdx.x; g < hkv; g += kBlock) bl.row_info[static_cast<int64_t>(b) * hkv + g] = 0;
+    if (bl.row_info)
+      for (int g = threadIdx.x; g < hkv; g += kBlock) bl.row_info[static_cast<int64_t>(b) * hkv + g] = 0;
+  }
+  if (!bl.seg_out) {
+    // No workspace: block i takes whole rows (b, g) = i, i + grid, ... and
+    // writes their bf16 outputs directly; no partials, no merge.
+    for (int64_t r = i; r < bl.rows; r += gridDim.x) {
+      const int b = static_cast<int>(r / hkv);
+      const int gk = static_cast<int>(r - static_cast<int64_t>(b) * hkv);
+      const int n = p.context_lens[b];
+      if (n <= 0) continue;                                  // written above
+      const int lo = p.reach > 0 ? max(0, n - p.reach) : 0;
+      const int64_t h0 = static_cast<int64_t>(b) * p.num_q_heads + static_cast<int64_t>(gk) * p.gq;
+      attend_range<D, G, kWaves, KV>(p, b, gk, lo, n, nullptr, nullptr, nullptr, 1, bl.out + h0 * D,
+                                     bl.lse ? bl.lse + h0 : nullptr);
+    }
+    return;
   }
   if (threadIdx.x < 64) {
     const int64_t keys = total_keys(p.context_lens, bl.batch, p.reach);
@@ -1132,7 +1146,7 @@ void balanced_split_kernel(const SplitParams p, const BalancedLayout bl) {
   const int64_t s1 = static_cast<int64_t>(i + 1) * T / nb;
   int b = sh_b;
   int64_t pre = sh_pre;                                  // keys per KV head before sequence b
-  const int gq = 1 << p.group_shift;
+  const int gq = p.gq;
   while (b < bl.batch) {
     const int n = p.context_lens[b];
     const int lo = p.reach > 0 ? max(0, n - p.reach) : 0;
@@ -1194,14 +1208,14 @@ __global__ __launch_bounds__(kBlock) void balanced_merge_kernel(const BalancedLa
   if (u >= G * D4) return;
   const int h = u / D4;
   const int d = (u % D4) * 4;
-  // output row of virtual head h (query h >> shift, q head h & (gq - 1));
-  // padding queries past the last real one write nothing
-  if ((h >> bl.group_shift) >= bl.num_queries) return;
-  const int gq = 1 << bl.group_shift;
+  // output row of virtual head h (query h / gq, q head h % gq); padding heads
+  // write nothing
+  if (h >= bl.vheads) return;
+  const int gq = bl.gq;
   const int hkv = bl.rows / bl.batch;
   const int b = r / hkv;
   const int64_t h0 = static_cast<int64_t>(b) * num_q_heads + static_cast<int64_t>(r - b * hkv) * gq;
-  const int64_t ho = h0 + (h >> bl.group_shift) * bl.q_heads + (h & (gq - 1));
+  const int64_t ho = h0 + static_cast<int64_t>(h / gq) * bl.q_heads + (h % gq);
   const float* pm = bl.seg_max + slot0 * G + h;
   const float* pl = bl.seg_sum + slot0 * G + h;
   const float* po = bl.seg_out + (slot0 * G + h) * D + d;
@@ -1333,9 +1347,13 @@ __global__ __launch_bounds__(kBlock) void merge_kernel(const MergeParams p) {
   const int b = blockIdx.y;
   const int n = p.context_lens[b];
   const int lo = p.window > 0 ? max(0, n - p.window) : 0;
-  const int live = (n > lo) ? static_cast<int>((static_cast<int64_t>(n - lo) + p.partition_size - 1) /
-                                               p.partition_size)
-                            : 0;
+  // live partitions, at most max_parts: a context past the partitions'
+  // reach (outside the contract) merges the ones written and reads nothing
+  // beyond its own row
+  const int64_t nlive = (n > lo) ? (static_cast<int64_t>(n - lo) + p.partition_size - 1) /
+                                       p.partition_size
+                                 : 0;
+  const int live = static_cast<int>(nlive < p.max_parts ? nlive : p.max_parts);
   const int64_t row = static_cast<int64_t>(b) * p.num_q_heads + h;
   merge_row<D>(p.part_max + row * p.max_parts, p.part_sum + row * p.max_parts,
                p.part_out + row * p.max_parts * D, 1, live, p.out + row * D,
@@ -1357,7 +1375,7 @@ static hipError_t launch_balanced_dg(const SplitParams& p, const BalancedLayout&
                                      hipStream_t stream) {
   hipLaunchKernelGGL((balanced_split_kernel<D, G, KV>), dim3(grid), dim3(kBlock), 0, stream, p, bl);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !bl.seg_out) return e;   // no workspace: rows were written whole
   hipLaunchKernelGGL((balanced_merge_kernel<D, G>), dim3(bl.rows, (G * D / 4 + kBlock - 1) / kBlock),
                      dim3(kBlock), 0, stream, bl, p.num_q_heads);
   return hipGetLastError();
@@ -1387,9 +1405,7 @@ static hipError_t launch_split_d(const SplitParams& p, int group, int batch, int
     case 2: return launch_split_dg<D, 2>(p, batch, num_kv_heads, stream);
     case 4: return launch_split_dg<D, 4>(p, batch, num_kv_heads, stream);
     case 8: return launch_split_dg<D, 8>(p, batch, num_kv_heads, stream);
-    case 16:
-      if constexpr (D != 256) return launch_split_dg<D, 16>(p, batch, num_kv_heads, stream);
-      return hipErrorInvalidValue;
+    case 16: return launch_split_dg<D, 16>(p, batch, num_kv_heads, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1425,29 +1441,27 @@ static int balanced_blocks(int num_cus, int max_blocks) {
   return n < max_blocks ? n : max_blocks;
 }
 
-// Calls f.template operator()<D, G, KV>() for a supported (head_dim, group,
-// pool element type) triple; returns `none` otherwise.  f32 pools skip
-// head_dim 256 (their K and V registers would not fit two waves per SIMD; at
-// 512 a wave holds 128 dims).
+// Calls f.template operator()<D, G, KV>() for a supported (head_dim, padded
+// group, pool element type) triple; returns `none` otherwise.  (f32 pools at
+// head_dim 256 run one wave per SIMD: their K and V registers do not fit two.)
 template <typename R, typename F>
 static R dispatch_dg(int head_dim, int group, int kv, R none, F&& f) {
 #define PA_CASE(DD, GG)                                                                \
   if (head_dim == DD && group == GG) {                                                 \
     if (kv == kKvBf16) return f.template operator()<DD, GG, kKvBf16>();                \
     if (kv == kKvFp8) return f.template operator()<DD, GG, kKvFp8>();                  \
-    if constexpr (DD != 256)                                                           \
-      if (kv == kKvF32) return f.template operator()<DD, GG, kKvF32>();                \
+    if (kv == kKvF32) return f.template operator()<DD, GG, kKvF32>();                  \
     return none;                                                                       \
   }
   PA_CASE(64, 1) PA_CASE(64, 2) PA_CASE(64, 4) PA_CASE(64, 8) PA_CASE(64, 16)
   PA_CASE(128, 1) PA_CASE(128, 2) PA_CASE(128, 4) PA_CASE(128, 8) PA_CASE(128, 16)
-  PA_CASE(256, 1) PA_CASE(256, 2) PA_CASE(256, 4) PA_CASE(256, 8)
+  PA_CASE(256, 1) PA_CASE(256, 2) PA_CASE(256, 4) PA_CASE(256, 8) PA_CASE(256, 16)
   PA_CASE(512, 1) PA_CASE(512, 2) PA_CASE(512, 4) PA_CASE(512, 8) PA_CASE(512, 16)
 #undef PA_CASE
   return none;
 }
 
-// Blocks the balanced split would use on this device (occupancy x CUs, capped).
+// Blocks the balanced split uses for num_cus compute units (occupancy x CUs, capped).
 int balanced_grid(int head_dim, int group, int num_cus, int max_blocks, int kv) {
   return dispatch_dg<int>(head_dim, group, kv, 0, [&]<int D, int G, int KV>() {
     return balanced_blocks<D, G, KV>(num_cus, max_blocks);

@@ -748,18 +748,6 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_uv_kernel(const MlaPa
 
 }  // namespace pa
 
-namespace {
-
-int mla_device_cus() {
-  int dev = 0, n = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
-    return 256;
-  return n;
-}
-
-}  // namespace
-
 extern "C" {
 
 size_t mla_absorbed_decode_workspace_size(int32_t batch, int32_t num_heads,
@@ -825,7 +813,9 @@ int mla_decode_impl(const void* q_nope, const void* q_rope, const void* kv_cache
   int shift = 0;
   while ((1 << shift) < cache->page_size) ++shift;
   p.page_shift = shift;
-  const int cus = mla_device_cus();
+  // The split's block count is fixed by the build, not the device (so are the
+  // results): kSplitCUs blocks for 256 compute units.
+  const int cus = pa::kSplitCUs;
   // Explicit partition size: about that many keys per block.  Library choice:
   // one block per CU (a multiple of 16, so the head groups of a key range
   // share an XCD), each block at least kMlaMinKeys keys.

@@ -27,16 +27,17 @@ struct SplitParams {
   int32_t page_size;
   int32_t page_shift;   // log2(page_size)
   int32_t window;
-  // Multi-query decode (S query tokens per sequence, q [b][s][Hq][D]): the
-  // kernel's group G holds S' * Gq virtual heads (S' = S rounded up to a
-  // power of two), virtual head h being query h >> group_shift, q head
-  // (h & (Gq - 1)) of the KV group; queries S .. S'-1 repeat query S - 1 and
-  // write nothing.  Query s sees keys up to n - S + s when causal; `reach` is
-  // the window of the union of the queries' key ranges (window + S - 1 when
-  // causal, else window).
+  // Virtual heads of a KV group: S query tokens per sequence (q [b][s][Hq][D])
+  // times Gq = Hq / Hkv q heads give vheads = S * Gq live heads, virtual head
+  // h being query h / Gq, q head h % Gq of the group.  The kernel's group G
+  // (a template argument: 1, 2, 4, 8 or 16) is vheads rounded up; heads
+  // vheads .. G-1 are padding, see no key and write nothing.  Query s sees
+  // keys up to n - S + s when causal; `reach` is the window of the union of
+  // the queries' key ranges (window + S - 1 when causal, else window).
   int32_t num_queries;
   int32_t q_heads;      // Hq
-  int32_t group_shift;  // log2(Gq)
+  int32_t gq;           // Gq, q heads per KV head
+  int32_t vheads;       // S * Gq
   int32_t causal;
   int32_t reach;
   int32_t partition_size;
@@ -74,8 +75,8 @@ struct BalancedLayout {
   int32_t rows;          // batch * num_kv_heads
   int32_t batch;
   int32_t q_heads;       // Hq (out rows are [b][s][Hq])
-  int32_t group_shift;   // log2(Gq); virtual head h -> query h >> shift, head h & (Gq - 1)
-  int32_t num_queries;   // S; virtual queries >= S write nothing
+  int32_t gq;            // Gq; virtual head h -> query h / Gq, head h % Gq
+  int32_t vheads;        // S * Gq; padding heads h >= vheads write nothing
 };
 
 }  // namespace pa

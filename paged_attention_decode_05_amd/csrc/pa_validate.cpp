@@ -25,22 +25,20 @@ const char* last_error() { return g_last_error.c_str(); }
 
 bool head_dim_supported(int32_t d) { return d == 64 || d == 128 || d == 256 || d == 512; }
 
-// q heads per KV head built per head_dim: 16 heads at head_dim 256 would need
-// more registers than two waves per SIMD leave, so head_dim 256 stops at 8
-// (at 512 each wave holds 128 of the dims).
+// Heads per KV group: one 16-column matrix tile holds up to 16 of them at
+// every head_dim.
 bool group_supported(int32_t head_dim, int32_t group) {
-  if (group == 1 || group == 2 || group == 4 || group == 8) return true;
-  return group == 16 && head_dim != 256;
+  return head_dim_supported(head_dim) && group >= 1 && group <= 16;
+}
+
+int32_t group_padded(int32_t heads) {
+  if (heads < 1 || heads > 16) return 0;
+  int32_t g = 1;
+  while (g < heads) g *= 2;
+  return g;
 }
 
 bool page_size_supported(int32_t ps) { return ps == 16 || ps == 32 || ps == 64; }
-
-int32_t queries_padded(int32_t num_queries) {
-  if (num_queries < 1) return 0;
-  int32_t p = 1;
-  while (p < num_queries) p *= 2;
-  return p;
-}
 
 int64_t max_keys(int32_t max_pages_per_seq, int32_t page_size, int32_t window) {
   int64_t k = static_cast<int64_t>(max_pages_per_seq) * page_size;
@@ -73,7 +71,7 @@ int check_gqa(const void* q, const void* k_pool, const void* v_pool, const pa_kv
     return fail(PA_ERR_UNSUPPORTED, "head_dim must be 64, 128, 256 or 512");
   const int32_t group = num_q_heads / kv->num_kv_heads;
   if (!group_supported(kv->head_dim, group))
-    return fail(PA_ERR_UNSUPPORTED, "q heads per KV head must be 1, 2, 4, 8 (or 16 at head_dim 64, 128 or 512)");
+    return fail(PA_ERR_UNSUPPORTED, "q heads per KV head must be 1 .. 16");
   if (!page_size_supported(kv->page_size))
     return fail(PA_ERR_UNSUPPORTED, "page_size must be 16, 32 or 64");
   const int64_t row_align = 16 / elem_bytes;   // elements per 16 bytes
@@ -154,13 +152,14 @@ int32_t suggest_partition(int32_t batch, int32_t num_kv_heads, int32_t head_dim,
   return static_cast<int32_t>(p);
 }
 
-bool plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+bool plan_decode(int32_t batch, int32_t num_kv_heads, int32_t vheads, int32_t head_dim,
                  int32_t max_pages_per_seq, int32_t page_size, int32_t window, DecodePlan* plan) {
-  if (batch < 1 || num_q_heads < 1 || num_kv_heads < 1 || max_pages_per_seq < 1 ||
-      page_size < 1 || !head_dim_supported(head_dim) || num_q_heads % num_kv_heads)
+  if (batch < 1 || num_kv_heads < 1 || max_pages_per_seq < 1 || page_size < 1 ||
+      !head_dim_supported(head_dim) || group_padded(vheads) == 0)
     return false;
+  if (static_cast<int64_t>(batch) * num_kv_heads > (int64_t{1} << 30)) return false;
   plan->rows = batch * num_kv_heads;
-  plan->group = num_q_heads / num_kv_heads;
+  plan->group = group_padded(vheads);
   const size_t slots = static_cast<size_t>(plan->rows) + kMaxBalancedBlocks;
   size_t o = 0;
   plan->off_seg_out = o;    o += round_up(slots * plan->group * head_dim * sizeof(float), 256);

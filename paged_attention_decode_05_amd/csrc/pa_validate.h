@@ -16,13 +16,18 @@ int fail(int status, const std::string& msg);
 void clear_error();
 const char* last_error();
 
-// Supported compile-time shapes.
+// Supported shapes.  Any 1..16 heads per KV group (q heads per KV head,
+// times the queries per sequence for multi-query decode) run on a kernel
+// built for 1, 2, 4, 8 or 16: group_padded() rounds up (0 if out of range).
 bool head_dim_supported(int32_t d);
 bool group_supported(int32_t head_dim, int32_t group);
 bool page_size_supported(int32_t ps);
+int32_t group_padded(int32_t heads);
 
-// Query count of multi-query decode rounded up to a power of two (0 if < 1).
-int32_t queries_padded(int32_t num_queries);
+// Compute units the balanced split is sized for (MI355X has 256): a fixed
+// count, so the cut points, and with them an output's last bits, do not
+// depend on the device the call runs on.
+constexpr int32_t kSplitCUs = 256;
 
 // Largest number of keys one sequence can attend to.
 int64_t max_keys(int32_t max_pages_per_seq, int32_t page_size, int32_t window);
@@ -55,12 +60,13 @@ constexpr int64_t kMinUnitsPerBlock = 32;
 
 struct DecodePlan {
   int32_t rows = 0;          // batch * num_kv_heads
-  int32_t group = 0;
+  int32_t group = 0;         // padded heads per KV group (the kernel's tile)
   size_t off_seg_out = 0, off_seg_max = 0, off_seg_sum = 0;
   size_t off_row_info = 0;   // one 32-bit record per row
   size_t bytes = 0;
 };
-bool plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+// vheads: live heads per KV group (q heads per KV head x queries per sequence).
+bool plan_decode(int32_t batch, int32_t num_kv_heads, int32_t vheads, int32_t head_dim,
                  int32_t max_pages_per_seq, int32_t page_size, int32_t window, DecodePlan* plan);
 
 // Fixed partition size used by pa_decode_partition_size (the two-stage API's

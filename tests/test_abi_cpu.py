@@ -2,7 +2,9 @@
 header declares, and rejects bad arguments on the host before any launch.
 
 No call here is valid enough to reach a kernel launch: every one fails a
-host-side check (the fake device addresses are never dereferenced).
+host-side check (the fake device addresses are never dereferenced).  A call
+that is valid up to its workspace passes a 1-byte one (a NULL workspace is
+a valid mode of the decode entry points, so it would launch).
 """
 from __future__ import annotations
 
@@ -47,7 +49,7 @@ def _kv(**kw):
 
 
 def _decode(kv=None, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, bt_stride=32, ctx=FAKE, batch=8, hq=8,
-            maxp=32, scale=0.088, window=0, out=FAKE, lse=None, ws=None, ws_bytes=0):
+            maxp=32, scale=0.088, window=0, out=FAKE, lse=None, ws=FAKE, ws_bytes=1):
     kv = kv or _kv()
     return pb.LIB.pa_decode(q, k, v, C.byref(kv), bt, bt_stride, ctx, batch, hq, maxp, scale,
                             window, out, lse, ws, ws_bytes, None)
@@ -68,15 +70,15 @@ def test_null_pointers(field, status):
     (dict(kv=_kv(head_dim=96, token_stride=96, head_stride=32 * 96, page_stride=2 * 32 * 96)),
      "UNSUPPORTED"),
     (dict(hq=64), "UNSUPPORTED"),                                  # 32 q heads per KV head
+    (dict(hq=34), "UNSUPPORTED"),                                  # 17 q heads per KV head
     (dict(kv=_kv(page_size=8)), "UNSUPPORTED"),
-    (dict(kv=_kv(head_dim=256, num_kv_heads=1, token_stride=256, head_stride=32 * 256,
-                 page_stride=32 * 256), hq=16), "UNSUPPORTED"),    # 16 per KV head at D=256
     (dict(kv=_kv(token_stride=132)), "ALIGN"),
     (dict(kv=_kv(page_stride=4100)), "ALIGN"),
     (dict(q=FAKE + 8), "ALIGN"), (dict(k=FAKE + 2), "ALIGN"),
     (dict(out=FAKE + 4), "ALIGN"),
     (dict(), "WORKSPACE"),
     (dict(ws=FAKE, ws_bytes=100), "WORKSPACE"),
+    (dict(ws=FAKE + 16, ws_bytes=1 << 30), "ALIGN"),
 ])
 def test_decode_rejections(kw, status):
     assert _decode(**kw) == PA[status], pb.pa_last_error()
@@ -84,8 +86,8 @@ def test_decode_rejections(kw, status):
 
 
 def test_head_dim_512_accepted():
-    """head_dim 512 takes groups 1-16 (16 is refused only at 256); every such
-    call is valid up to the missing workspace, for bf16 and f32 pools."""
+    """head_dim 512 takes groups 1-16; every such call is valid up to the
+    too-small workspace, for bf16 and f32 pools."""
     kv = _kv(head_dim=512, num_kv_heads=1, token_stride=512, head_stride=32 * 512,
              page_stride=32 * 512)
     for hq in (1, 2, 4, 8, 16):
@@ -93,7 +95,22 @@ def test_head_dim_512_accepted():
     assert _decode(kv=kv, hq=32) == PA["UNSUPPORTED"]
     f = pb.LIB.pa_decode_f32
     assert f(FAKE, FAKE, FAKE, C.byref(kv), FAKE, 32, FAKE, 8, 16, 32, 0.044, 0, FAKE, None,
-             None, 0, None) == PA["WORKSPACE"], pb.pa_last_error()
+             FAKE, 1, None) == PA["WORKSPACE"], pb.pa_last_error()
+
+
+@pytest.mark.parametrize("head_dim", [64, 128, 256, 512])
+def test_every_group_1_to_16_accepted(head_dim):
+    """Any 1..16 q heads per KV head runs on the kernel built for the next
+    power of two; the workspace is sized for that padded group."""
+    kv = _kv(head_dim=head_dim, num_kv_heads=1, token_stride=head_dim,
+             head_stride=32 * head_dim, page_stride=32 * head_dim)
+    for g in range(1, 17):
+        assert _decode(kv=kv, hq=g) == PA["WORKSPACE"], (g, pb.pa_last_error())
+        padded = 1 << (g - 1).bit_length()
+        assert pb.pa_decode_workspace_size(8, g, 1, head_dim, 32, 32, 0) == \
+            pb.pa_decode_workspace_size(8, padded, 1, head_dim, 32, 32, 0)
+    assert _decode(kv=kv, hq=17) == PA["UNSUPPORTED"]
+    assert pb.pa_decode_workspace_size(8, 17, 1, head_dim, 32, 32, 0) == 0
     need = pb.pa_decode_workspace_size(8, 16, 1, 512, 32, 32, 0)
     slots = 8 + 2048
     base = slots * 16 * 514 * 4 + 8 * 4
@@ -262,13 +279,15 @@ def test_multiquery_rejections_and_sizes():
     kv = _kv()
     f = pb.LIB.pa_decode_multiquery
     args = lambda S, heads=8: (FAKE, FAKE, FAKE, C.byref(kv), FAKE, 32, FAKE, 8, heads, S, 1, 32,
-                               0.088, 0, FAKE, None, None, 0, None)
+                               0.088, 0, FAKE, None, FAKE, 1, None)
     assert f(*args(0)) == PA["SHAPE"]
     assert f(*args(17)) == PA["SHAPE"]
-    assert f(*args(5)) == PA["UNSUPPORTED"]      # 8 padded queries x 4 heads per KV head = 32
-    assert f(*args(4)) == PA["WORKSPACE"]        # 4 x 4 = 16: supported, no workspace given
+    assert f(*args(5)) == PA["UNSUPPORTED"]      # 5 queries x 4 heads per KV head = 20
+    assert f(*args(4)) == PA["WORKSPACE"]        # 4 x 4 = 16: supported, workspace too small
+    assert f(*args(5, heads=6)) == PA["WORKSPACE"]   # 5 x 3 = 15
     ws = pb.pa_decode_multiquery_workspace_size
     assert ws(8, 8, 2, 128, 32, 32, 0, 3) == ws(8, 8, 2, 128, 32, 32, 0, 4) > 0
+    assert ws(8, 6, 2, 128, 32, 32, 0, 5) == ws(8, 8, 2, 128, 32, 32, 0, 4)
     assert ws(8, 8, 2, 128, 32, 32, 0, 1) == pb.pa_decode_workspace_size(8, 8, 2, 128, 32, 32, 0)
     assert ws(8, 8, 2, 128, 32, 32, 0, 0) == 0
 
@@ -278,7 +297,7 @@ def test_fp8_rejections():
     kv8 = _kv(page_stride=2 * 32 * 128, head_stride=32 * 128, token_stride=128)
     def call(kv=kv8, ks=0.02, vs=0.03, scale=0.088):
         return f(FAKE, FAKE, FAKE, C.byref(kv), FAKE, 32, FAKE, 8, 8, 32, scale, ks, vs, 0, FAKE,
-                 None, None, 0, None)
+                 None, FAKE, 1, None)
     assert call(kv=_kv(token_stride=136, head_stride=32 * 136, page_stride=2 * 32 * 136)) == PA["ALIGN"]
     assert call(ks=0.0) == PA["SHAPE"]
     assert call(vs=float("nan")) == PA["SHAPE"]
@@ -293,9 +312,11 @@ def test_f32_pool_rejections():
     f = pb.LIB.pa_decode_f32
     def call(kv):
         return f(FAKE, FAKE, FAKE, C.byref(kv), FAKE, 32, FAKE, 8, 8, 32, 0.088, 0, FAKE, None,
-                 None, 0, None)
+                 FAKE, 1, None)
     assert call(_kv(head_dim=256, token_stride=256, head_stride=32 * 256,
-                    page_stride=2 * 32 * 256)) == PA["UNSUPPORTED"]
+                    page_stride=2 * 32 * 256)) == PA["WORKSPACE"]
+    assert call(_kv(head_dim=96, token_stride=96, head_stride=32 * 96,
+                    page_stride=2 * 32 * 96)) == PA["UNSUPPORTED"]
     assert call(_kv(token_stride=130, head_stride=32 * 130, page_stride=2 * 32 * 130)) == PA["ALIGN"]
     # 4-element strides are 16-byte rows for f32: valid up to the workspace
     assert call(_kv(token_stride=132, head_stride=32 * 132, page_stride=2 * 32 * 132)) == PA["WORKSPACE"]

@@ -50,7 +50,8 @@ def _case(d, group, hkv=2, page=32, layout="PHSD", window=0, ks=0.0173, vs=0.029
 
 @pytest.mark.parametrize("d,group", [(64, 1), (64, 4), (64, 16),
                                      (128, 1), (128, 2), (128, 4), (128, 8), (128, 16),
-                                     (256, 1), (256, 2), (256, 4), (256, 8)])
+                                     (256, 1), (256, 2), (256, 4), (256, 8), (256, 16),
+                                     (128, 3), (128, 6), (256, 6)])
 def test_group_and_head_dim_sweep(oracle, d, group):
     case = _case(d, group, seed=9900 + d + group)
     ref, ref_lse = oracle.decode_fp8(case)

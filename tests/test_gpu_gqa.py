@@ -97,7 +97,10 @@ def test_context_zero_gives_zero_and_neg_inf(oracle):
 @pytest.mark.parametrize("head_dim,group,kv_heads", [
     (64, 1, 3), (64, 2, 1), (64, 4, 3), (64, 8, 1), (64, 16, 2),
     (128, 1, 3), (128, 2, 3), (128, 4, 1), (128, 8, 3), (128, 16, 1),
-    (256, 1, 3), (256, 2, 1), (256, 4, 3), (256, 8, 1)])
+    (256, 1, 3), (256, 2, 1), (256, 4, 3), (256, 8, 1), (256, 16, 1),
+    # groups that are not a power of two run on the next tile size, padded
+    (64, 3, 2), (128, 3, 2), (128, 5, 1), (128, 6, 2), (128, 7, 1), (128, 12, 1),
+    (256, 6, 2), (256, 3, 1), (256, 12, 1), (512, 6, 1)])
 def test_group_and_head_dim_sweep(oracle, head_dim, group, kv_heads):
     case = wl.make_gqa_case(context_lens=(1, 17, 32, 33, 257, 700), num_q_heads=group * kv_heads,
                             num_kv_heads=kv_heads, head_dim=head_dim, page_size=32,
@@ -150,6 +153,58 @@ def test_splitkv_partials_match_oracle(oracle, partition_size, window):
     out, lse = run_merge(po, pm, ps, dc.context_lens, partition_size, window)
     _gate(out, ref, f"split P={partition_size} W={window}")
     _lse_ok(lse, ref_lse)
+
+
+@pytest.mark.parametrize("group,head_dim", [(3, 128), (6, 256), (12, 64)])
+def test_splitkv_partials_padded_group(oracle, group, head_dim):
+    """Fixed partitions with a group that is not a power of two: the padding
+    heads of the kernel's tile write no partial, so the rows of the next KV
+    group (NaN-filled beforehand) hold exactly the oracle's partials."""
+    case = wl.make_gqa_case(context_lens=(0, 1, 33, 300, 1000), num_q_heads=2 * group,
+                            num_kv_heads=2, head_dim=head_dim, page_size=32,
+                            seed=8450 + group, window=700)
+    dc = dev_case(case)
+    P = 128
+    mp = max_parts_for(dc, P)
+    po, pm, ps = run_splitkv(dc, P, mp)
+    rpo, rpm, rps = oracle.partials(case, P, mp)
+    ok, err = close_f32(pm.cpu().numpy(), rpm, rtol=2e-6, atol=1e-5)
+    assert ok, ("max", err)
+    ok, err = close_f32(ps.cpu().numpy(), rps, rtol=1e-5, atol=1e-6)
+    assert ok, ("sum", err)
+    ok, err = close_f32(po.cpu().numpy(), rpo, rtol=1e-5, atol=1e-5)
+    assert ok, ("out", err)
+    ref, ref_lse = oracle.decode(case)
+    out, lse = run_merge(po, pm, ps, dc.context_lens, P, case.window)
+    _gate(out, ref, f"split G={group} D={head_dim}")
+    _lse_ok(lse, ref_lse)
+
+
+@pytest.mark.parametrize("what,kw", [
+    ("tiny", dict(context_lens=(0, 1, 31, 32, 33, 64, 100, 685, 1000), num_q_heads=8,
+                  num_kv_heads=2, head_dim=128, page_size=32)),
+    ("window d256 G8", dict(context_lens=(1, 33, 700, 5000), num_q_heads=16, num_kv_heads=2,
+                            head_dim=256, page_size=32, window=1000, q_std=0.5)),
+    ("G6 d128 ps16", dict(context_lens=(0, 17, 4000, 250), num_q_heads=12, num_kv_heads=2,
+                          head_dim=128, page_size=16)),
+    ("G2 valu", dict(context_lens=(3, 64, 2000), num_q_heads=4, num_kv_heads=2, head_dim=128,
+                     page_size=64)),
+])
+def test_null_workspace(oracle, what, kw):
+    """A NULL workspace: one block per (sequence, KV head) row, bf16 written
+    directly, no merge; the same gate against the oracle."""
+    from paged_attention_decode_05_amd import binding as pb
+    case = wl.make_gqa_case(seed=8470 + len(what), **kw)
+    dc = dev_case(case)
+    B, H, D = dc.q.shape
+    out = torch.full((B, H, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((B, H), float("nan"), dtype=torch.float32, device="cuda")
+    pb.pa_decode(dc.q, dc.k_pool, dc.v_pool, pb.kv_layout(dc.k_pool, dc.layout), dc.block_table,
+                 dc.context_lens, dc.scale, dc.window, out, lse, None)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.decode(case)
+    _gate(out.cpu(), ref, f"no workspace: {what}")
+    _lse_ok(lse.cpu(), ref_lse, what)
 
 
 def test_merge_on_oracle_partials(oracle):

@@ -70,6 +70,36 @@ def test_causal_window(oracle, window):
     _check(oracle, case, True, f"window={window}")
 
 
+@pytest.mark.parametrize("S,gq", [(3, 3), (5, 3), (2, 5), (3, 1)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_padded_virtual_heads(oracle, S, gq, causal):
+    """S * Gq virtual heads that are not a power of two (9, 15, 10, 3): the
+    tile is padded and the padding heads write nothing (out is NaN-filled
+    beforehand, so a stray write would show)."""
+    case = wl.make_gqa_case(context_lens=(2, 40, 33, 900, 1700), num_q_heads=2 * gq,
+                            num_kv_heads=2, head_dim=128, page_size=32,
+                            seed=9960 + 10 * S + gq, num_queries=S)
+    _check(oracle, case, causal, f"S={S} Gq={gq} causal={causal}")
+
+
+def test_null_workspace_multiquery(oracle):
+    case = wl.make_gqa_case(context_lens=(1, 2, 64, 1000), num_q_heads=8, num_kv_heads=2,
+                            head_dim=128, page_size=16, seed=9970, num_queries=3)
+    ref, ref_lse = oracle.decode_multi(case, True)
+    dc = case.to("cuda")
+    B, S, H, D = dc.q.shape
+    out = torch.full((B, S, H, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((B, S, H), float("nan"), dtype=torch.float32, device="cuda")
+    pb.pa_decode_multiquery(dc.q, dc.k_pool, dc.v_pool, pb.kv_layout(dc.k_pool, dc.layout),
+                            dc.block_table, dc.context_lens, dc.scale, dc.window, True, out,
+                            lse, None)
+    torch.cuda.synchronize()
+    rep = compare(out.cpu(), ref)
+    assert rep.ok, rep
+    g = lse.cpu().numpy().astype(np.float64)
+    assert (np.isfinite(g) == np.isfinite(ref_lse)).all()
+
+
 def test_head_dim_256(oracle):
     case = wl.make_gqa_case(context_lens=(17, 300, 1100), num_q_heads=4, num_kv_heads=2,
                             head_dim=256, page_size=32, seed=9920, num_queries=4)
