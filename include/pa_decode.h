@@ -258,6 +258,29 @@ PA_API int pa_decode_f32(const void* q, const void* k_pool, const void* v_pool,
                          float scale, int32_t window, void* out, float* lse_out,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * pa_decode_noalloc -- pa_decode for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.
+ *
+ * Same arguments and results as pa_decode (bit for bit) without the
+ * workspace: the balanced split's partials and row records live in a
+ * 32 MiB array of the library's own device memory, one per device, set up
+ * on the first call on that device and held until the process ends.  Shapes
+ * whose pa_decode_workspace_size(...) exceeds 32 MiB return
+ * PA_ERR_WORKSPACE (nothing launched).  The call allocates nothing.  Every
+ * call on one device shares that device's array: calls that may overlap in
+ * time on one device (other streams, other threads) race and must be
+ * serialised by the caller.  The array needs no initialisation: each call
+ * rewrites what it later reads.
+ * ------------------------------------------------------------------------- */
+PA_API int pa_decode_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                             const pa_kv_layout* kv, const int32_t* block_table,
+                             int32_t block_table_stride, const int32_t* context_lens,
+                             int32_t batch, int32_t num_q_heads, int32_t max_pages_per_seq,
+                             float scale, int32_t window, void* out, float* lse_out,
+                             void* stream);
+
 /* Bytes of workspace pa_decode_multiquery needs (0 on invalid shapes). */
 PA_API size_t pa_decode_multiquery_workspace_size(int32_t batch, int32_t num_q_heads,
                                                   int32_t num_kv_heads, int32_t head_dim,

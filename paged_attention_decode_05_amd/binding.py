@@ -27,7 +27,7 @@ EXPORTS = ("pa_decode", "pa_decode_splitkv", "pa_merge_lse", "pa_decode_workspac
            "pa_decode_multiquery", "pa_decode_multiquery_workspace_size", "pa_decode_fp8",
            "pa_decode_f32", "mla_cache_insert_fp8", "mla_absorbed_decode_fp8",
            "mla_absorbed_decode_multiquery", "mla_absorbed_decode_multiquery_fp8",
-           "pa_last_error")
+           "pa_decode_noalloc", "pa_last_error")
 
 
 class PaError(RuntimeError):
@@ -56,6 +56,9 @@ def _load() -> C.CDLL:
     lib.pa_decode_fp8.argtypes = [vp, vp, vp, kvp, i32p, i32, i32p, i32, i32, i32, C.c_float,
                                   C.c_float, C.c_float, i32, vp, vp, vp, C.c_size_t, vp]
     lib.pa_decode_fp8.restype = C.c_int
+    lib.pa_decode_noalloc.argtypes = [vp, vp, vp, kvp, i32p, i32, i32p, i32, i32, i32, C.c_float,
+                                      i32, vp, vp, vp]
+    lib.pa_decode_noalloc.restype = C.c_int
     lib.pa_decode_f32.argtypes = lib.pa_decode.argtypes
     lib.pa_decode_f32.restype = C.c_int
     lib.pa_decode_splitkv.argtypes = [vp, vp, vp, kvp, i32p, i32, i32p, i32, i32, i32, C.c_float,
@@ -181,6 +184,25 @@ def pa_decode(q, k_pool, v_pool, kv: KvLayout, block_table, context_lens, scale:
                        int(window), _ptr(out, torch.bfloat16, "out"),
                        _ptr(lse_out, torch.float32, "lse_out"), _ptr(workspace), ws_bytes,
                        _stream(stream))
+    _check(rc)
+
+
+def pa_decode_noalloc(q, k_pool, v_pool, kv: KvLayout, block_table, context_lens, scale: float,
+                      window: int, out, lse_out=None, max_pages_per_seq=None,
+                      stream=None) -> None:
+    """pa_decode with the library's own device scratch instead of a workspace."""
+    for t, n in ((q, "q"), (block_table, "block_table"), (context_lens, "context_lens"),
+                 (out, "out")):
+        _contig(t, n)
+    B, H = q.shape[0], q.shape[1]
+    maxp = block_table.shape[1] if max_pages_per_seq is None else max_pages_per_seq
+    rc = LIB.pa_decode_noalloc(_ptr(q, torch.bfloat16, "q"), _ptr(k_pool, torch.bfloat16, "k_pool"),
+                               _ptr(v_pool, torch.bfloat16, "v_pool"), C.byref(kv),
+                               _ptr(block_table, torch.int32, "block_table"),
+                               block_table.stride(0),
+                               _ptr(context_lens, torch.int32, "context_lens"), B, H, maxp,
+                               float(scale), int(window), _ptr(out, torch.bfloat16, "out"),
+                               _ptr(lse_out, torch.float32, "lse_out"), _stream(stream))
     _check(rc)
 
 

@@ -6,6 +6,7 @@
 
 #include <atomic>
 #include <cmath>
+#include <mutex>
 #include <string>
 
 #include "pa_decode.h"
@@ -291,5 +292,72 @@ size_t pa_decode_multiquery_workspace_size(int32_t batch, int32_t num_q_heads,
 }
 
 const char* pa_last_error(void) { return pa::last_error(); }
+
+}  // extern "C"
+
+// ---- pa_decode_noalloc: the workspace in a library-owned device array ------------
+//
+// For callers that cannot allocate.  `scratch` holds pa_decode's partials
+// and row records; every gfx950 device the library runs on gets its own copy
+// when the code object loads there, kept until the process ends.  Host code
+// never uses the array's name as an address: its device address is looked up
+// once per device with hipGetSymbolAddress and kept in scratch_dev[].
+namespace {
+
+constexpr size_t kScratchBytes = size_t{32} << 20;   // 32 MiB per device
+__device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_dev[kMaxDevices];
+
+// Device address of `scratch` on the current device (nullptr and an error
+// message on failure).
+void* scratch_address(std::string& err) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    err = std::string("hipGetDevice: ") + (e != hipSuccess ? hipGetErrorString(e) : "device index out of range");
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_dev[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      err = std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e);
+      return nullptr;
+    }
+    scratch_dev[dev] = ptr;
+  }
+  return scratch_dev[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_decode_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                      const pa_kv_layout* kv, const int32_t* block_table,
+                      int32_t block_table_stride, const int32_t* context_lens, int32_t batch,
+                      int32_t num_q_heads, int32_t max_pages_per_seq, float scale, int32_t window,
+                      void* out, float* lse_out, void* stream) {
+  int rc = pa::check_gqa(q, k_pool, v_pool, kv, block_table, block_table_stride, context_lens,
+                         batch, num_q_heads, max_pages_per_seq, scale);
+  if (rc) return rc;
+  const size_t need = pa_decode_workspace_size(batch, num_q_heads, kv->num_kv_heads, kv->head_dim,
+                                               max_pages_per_seq, kv->page_size, window);
+  if (need == 0) return pa::fail(PA_ERR_SHAPE, "no launch plan for these shapes");
+  if (need > kScratchBytes)
+    return pa::fail(PA_ERR_WORKSPACE, "these shapes need " + std::to_string(need) +
+                                          " bytes of scratch; pa_decode_noalloc holds " +
+                                          std::to_string(kScratchBytes));
+  std::string err;
+  void* ws = scratch_address(err);
+  if (!ws) return pa::fail(PA_ERR_LAUNCH, err);
+  return decode_impl(q, k_pool, v_pool, kv, block_table, block_table_stride, context_lens, batch,
+                     num_q_heads, 1, 1, max_pages_per_seq, scale, window, out, lse_out, ws,
+                     kScratchBytes, stream);
+}
 
 }  // extern "C"

@@ -323,3 +323,19 @@ def test_f32_pool_rejections():
     # one page must stay below 2^32 bytes: 2^30 f32 elements is 2^32 bytes
     assert call(_kv(page_stride=2**30)) == PA["SHAPE"]
     assert call(_kv(page_stride=2**30 - 4)) == PA["WORKSPACE"]
+
+
+def test_noalloc_host_checks():
+    """pa_decode_noalloc validates like pa_decode, and refuses shapes whose
+    plan exceeds its 32 MiB scratch before touching the device."""
+    f = pb.LIB.pa_decode_noalloc
+    kv = _kv()
+    assert f(None, FAKE, FAKE, C.byref(kv), FAKE, 32, FAKE, 8, 8, 32, 0.088, 0, FAKE, None,
+             None) == PA["NULL"]
+    assert f(FAKE, FAKE, FAKE, C.byref(kv), FAKE, 32, FAKE, 8, 7, 32, 0.088, 0, FAKE, None,
+             None) == PA["SHAPE"]
+    big = pb.KvLayout(64, 32, 8, 512, 8 * 32 * 512, 32 * 512, 512)
+    assert pb.pa_decode_workspace_size(4096, 128, 8, 512, 64, 32, 0) > 32 << 20
+    assert f(FAKE, FAKE, FAKE, C.byref(big), FAKE, 64, FAKE, 4096, 128, 64, 0.05, 0, FAKE, None,
+             None) == PA["WORKSPACE"]
+    assert "scratch" in pb.pa_last_error()
