@@ -327,7 +327,8 @@ PA_API int32_t pa_decode_partition_size(int32_t batch, int32_t num_q_heads,
  * kv_cache: pool described by *cache (num_kv_heads 1, head_dim 576,
  * page_size 16/32/64, token_stride >= 576 and a multiple of 8);
  * w_uk, w_uv [num_heads][128][512] bf16; out [batch][num_heads][128] bf16.
- * num_heads must be a multiple of 16.  partition_size: keys per workgroup
+ * Any num_heads >= 1 (heads past the last 32-head tile are masked).
+ * partition_size: keys per workgroup
  * (multiple of 64, or 0 to let the library choose from host-known shapes).
  * workspace: at least mla_absorbed_decode_workspace_size(...) bytes,
  * 256-byte aligned, clobbered by the call.  Device-side contract as for

@@ -6,6 +6,9 @@
 //   16x16x32:  A lane holds A[c][8g .. 8g+7],  B lane holds B[8g .. 8g+7][c]
 //   16x16x16:  A lane holds A[c][4g .. 4g+3],  B lane holds B[4g .. 4g+3][c]
 //   both:      D lane holds D[4g .. 4g+3][c]
+// 32x32x16 (h = lane / 32, c = lane % 32; confirmed by an in-bounds probe):
+//   A lane holds A[c][8h .. 8h+7],  B lane holds B[8h .. 8h+7][c],
+//   D element i (0..15) of a lane is D[8(i / 4) + 4h + i % 4][c]
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -62,6 +65,13 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_ca
 // D = A.B + C, 16x16x32, bf16 operands (8 per lane), fp32 accumulation.
 __device__ __forceinline__ f32x4_t mfma(uint4 a, uint4 b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+
+// D = A.B + C, 32x32x16, bf16 operands (8 per lane), fp32 accumulation.
+__device__ __forceinline__ f32x16_t mfma32(uint4 a, uint4 b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
 // D = A.B + C, 16x16x16, bf16 operands (4 per lane), fp32 accumulation.

@@ -10,21 +10,20 @@
 //   out[dv]   = sum_j W_UV[h][dv][j] o_lat[j]                      (merge + W_UV kernel)
 //
 // The two 576/512-deep contractions over the latent cache run on MFMA
-// (v_mfma_f32_16x16x32_bf16): per 32-key tile, S^T[32 keys x 16 heads] =
-// C[32 x 576] . Q^T, and O[16 heads x 512] += P[16 x 32 keys] . C[32 x 512].
-// The cache and W_UV are exact bf16; each fp32 operand (q_abs, P, o_lat)
-// enters as three bf16 terms hi + mid + lo, which represent an fp32 value
-// exactly (3 x 8 significant bits), so the MFMAs multiply the fp32 operands
-// exactly and only the fp32 accumulation rounds, at three MFMAs instead of one.
+// (v_mfma_f32_32x32x16_bf16): per 32-key tile and 32-head column block,
+// S^T[32 keys x 32 heads] = C[32 x 576] . Q^T, and O[32 heads x 512] += P[32 x
+// 32 keys] . C[32 x 512].  The cache and W_UV are exact bf16; each fp32 operand
+// (q_abs, P, o_lat) enters as three bf16 terms hi + mid + lo, which represent
+// an fp32 value exactly (3 x 8 significant bits), so the MFMAs multiply the
+// fp32 operands exactly and only the fp32 accumulation rounds, at three MFMAs
+// instead of one.
 //
-// Work split: heads form groups of 64 (one block = 4 waves x 16 heads); a
-// row is (head group, sequence), ordered group-major.  The keys of all rows,
-// laid end to end (T = groups * sum of context lengths), are cut into nb
-// equal contiguous ranges, one per block; a block writes one partial per row
-// piece it covers.  Group-major order puts the two head groups of the same
-// keys T/2 units apart, i.e. in blocks i and i + nb/2, which the dispatcher
-// places on the same XCD (nb a multiple of 16), so the second read of a
-// cache tile is served by that XCD's L2.
+// Work split: heads form groups of 64 (one block = 4 waves: two wave pairs of
+// 32 heads, the two waves of a pair splitting the latent dims); a row is
+// (head group, sequence), ordered group-major.  The keys of all rows, laid end
+// to end (T = groups * sum of context lengths), are cut into nb equal
+// contiguous ranges, one per block; a block writes one partial per row piece
+// it covers.
 //
 // S queries per sequence (mla_absorbed_decode_multiquery): query s, head h is
 // query head s*H + h of its sequence, so a sequence has S*H heads in
@@ -44,6 +43,7 @@
 
 #include <algorithm>
 #include <string>
+#include <type_traits>
 
 #include "pa_decode.h"
 #include "pa_device.h"
@@ -57,15 +57,11 @@ constexpr int kRow = kMlaRow;      // 576
 constexpr int kNope = kMlaNope;    // 128
 constexpr int kRope = kMlaRope;    // 64
 constexpr int kDv = kMlaDv;        // 128
-constexpr int kKS = kRow / 32;     // 18 k-steps of the score MFMA
-constexpr int kKSL = kLat / 32;    // 16 of them over the latent part
 constexpr int kTileKeys = 32;      // keys per LDS tile
-constexpr int kHeadsPerWave = 16;
-constexpr int kMlaWaves = 4;
-constexpr int kGroup = kHeadsPerWave * kMlaWaves;   // heads per block
+constexpr int kMlaWaves = 4;       // two wave pairs of 32 heads
+constexpr int kGroup = 64;         // heads per block
 constexpr int kMlaThreads = 64 * kMlaWaves;
-constexpr int kRowPad = kRow + 16; // LDS row stride (elements) of a cache tile row: 296 dwords,
-                                   // conflict-free for the score and transposed reads
+constexpr int kMlaDeadBit = 0x40000000;   // OR-ed into a dead key's offset: past any page
 static_assert(kGroup == kMlaBlockHeads, "head group size");
 
 struct MlaParams {
@@ -209,13 +205,6 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(const MlaParams p) {
 
 // ---- 2. split attention over the latent cache ----------------------------------------
 
-// Tile row of the key that MFMA row m (0..15) of a 16-key half handles.  The
-// transposed P.V reads of one 16-lane group touch the rows of m = 4g .. 4g+3;
-// mapping them to rows 2i + (g&1) + 8(g>>1) (four rows two apart) puts the
-// four 32-byte pieces in disjoint LDS banks (rows are 292 dwords apart),
-// and keeps the score operand reads of rows m = 0..7 conflict-free.
-__device__ __forceinline__ int key_row(int m) { return 2 * (m & 3) + ((m >> 2) & 1) + 8 * (m >> 3); }
-
 // Sum of the context lengths.  Called by a whole wave.
 __device__ __forceinline__ int64_t mla_total(const int32_t* ctx, int batch) {
   const int lane = threadIdx.x & 63;
@@ -258,74 +247,210 @@ __device__ __forceinline__ void fp8x16_bf16_scaled(uint4 x, float s, uint4& lo, 
                   fp8x2_bf16_scaled(x.w, s, false), fp8x2_bf16_scaled(x.w, s, true));
 }
 
+// Split-kernel geometry.  A block's 64-head group is two wave pairs; pair w/2
+// takes heads 32 (w/2) .. +32 (one 32x32 MFMA column block), and within a pair
+// wave half d = w % 2 holds latent dims 256d .. 256d+255 and rope dims
+// 512 + 32d .. +32 of q and of the output accumulators.
+constexpr int kPairHeads = 32;
+constexpr int kHalfLat = kLat / 2;                       // 256
+constexpr int kHalfRope = kRope / 2;                     // 32
+constexpr int kLatSteps = kHalfLat / 16;                 // 16 score k-steps (32x32x16)
+constexpr int kRopeSteps = kHalfRope / 16;               // 2
+constexpr int kDimTiles = kHalfLat / 32;                 // 8 P.V output tiles of 32 dims
+constexpr int kRowChunks = kRow / 8;                     // 72 16-byte chunks per 576-wide row
+constexpr int kTileElems = kTileKeys * kRow;             // one LDS tile, bf16 elements
+constexpr int kWaveLoads = kTileElems * 2 / 1024 / kMlaWaves;   // 9 one-KB wave loads per tile
+constexpr int kTileBufs = 3;
+
+// LDS position (in 16-byte chunks) of chunk c of tile row r: rows of 72
+// chunks back to back, c's low three bits XOR-ed with swz(r).  The 8 rows a
+// score read serves per LDS cycle get 8 distinct swz values, and the 4 rows
+// x 2 chunks of a 16-lane transposed read get 8 distinct bank groups (even
+// swz for rows 0-3 of an 8-row block, odd for rows 4-7), so both read forms
+// run without bank conflicts (32 banks of 4 bytes; measured).
+__device__ __forceinline__ int swz(int r) { return 2 * (r & 3) + ((r >> 2) & 1); }
+
+// Value of lane l ^ 32 combined with this lane's: v_permlane32_swap exchanges
+// the two 32-lane halves of a register pair (a VALU operation, no LDS).
+__device__ __forceinline__ float xhalf(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
+  // lanes 0-31 receive lane l + 32 in r[1], lanes 32-63 lane l - 32 in r[0]
+  return u2f((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+// Keeps x computed at this point: an empty asm that reads it.
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(uint32_t& x) { asm volatile("" : "+v"(x)); }
+
+// x *= f for an accumulator element held in an AGPR, through one temporary
+// VGPR: the rare rescale of the 128 accumulators then needs no VGPR copy of
+// them (VALU instructions cannot read AGPRs).
+__device__ __forceinline__ void scale_in_agpr(float& x, float f) {
+  float t;
+  asm volatile(
+      "v_accvgpr_read_b32 %1, %0\n\t"
+      "v_mul_f32 %1, %1, %2\n\t"
+      "v_accvgpr_write_b32 %0, %1"
+      : "+a"(x), "=&v"(t)
+      : "v"(f));
+}
+
+struct MlaSplitLds {
+  uint16_t tile[kTileBufs][kTileElems];
+  f32x4_t xs[2][kMlaWaves][4][64];   // partial scores of each wave, double-buffered
+};
+
 // Attention of the heads of group hg of sequence b over keys [begin, end);
 // writes the normalised partial, its max and its sum to slot.
-// Score D layout: lane l holds S^T[MFMA row 4*(l/16)+i (+16)][head l%16]; MFMA
-// row m of each 16-key half is tile row key_row(m).  Those 8 values are
-// exactly the A operand of P.V for head l%16 when the P.V k-slots 8g..8g+7
-// are taken as the keys of rows {4g..4g+3, 16+4g..16+4g+3}; the B operand
-// (those keys, 16 latent columns) comes from two transposed LDS reads of the
-// key-major tile.  The softmax keeps a per-head reference max and rescales
-// the accumulators only when a score exceeds it by more than 8 (log2
-// domain), so P stays below 2^8 and rescaling is rare.
+//
+// Per 32-key tile t0 .. t0+31, wave (pair, half):
+//   scores   S^T[32 keys x 32 heads] over the wave's dims on
+//            v_mfma_f32_32x32x16_bf16: A = cache rows from LDS (lane c: key c,
+//            8 dims), B = q (lane: head c, 8 dims), 16 latent k-steps x 3 q
+//            terms + 2 rope k-steps.  The two halves of a pair trade partials
+//            through LDS and add them: a + b = b + a exactly, so both hold the
+//            same scores bit for bit, and the same softmax state.
+//   softmax  D element i of lane l is key t0 + 8(i/4) + 4(l/32) + i%4 of head
+//            l%32; lazy reference max (moves when passed by more than 8 in the
+//            log2 domain, P <= 2^8), P split in three bf16 terms.
+//   P.V      O[32 heads x 256 dims] += P[32 x 32 keys] . C[32 keys x 256]: 8 dim
+//            tiles x 2 k-steps x 3 P terms.  The P registers are the A operand
+//            as they stand when k-slot 8h + j of k-step kk is taken as key
+//            16kk + 4h + j (j < 4) or 16kk + 8 + 4h + (j - 4); the B operand is
+//            two transposed LDS reads (ds_read_b64_tr_b16) of those key rows.
+// Pipeline: iteration it computes the scores of tile it and the softmax and
+// P.V of tile it-1; tile it+1 is loaded during iteration it straight from
+// global memory into its LDS buffer (buffer_load ... lds, whose buffer range
+// turns dead keys into zeros), three tiles resident; one barrier per
+// iteration orders the tile loads, the partial-score exchange and the reuse
+// of buffers.  FP8 rows are widened in registers and stored at the end of
+// the iteration instead.
 // CAUSAL: head s*H + h (query s of S) sees only keys t < n - S + 1 + s; a
 // head with no such key in [begin, end) writes a zero partial with max -inf
 // and sum 0.
 template <bool F8, bool CAUSAL>
 __device__ __forceinline__ void mla_segment(const MlaParams& p, int b, int n, int hg, int begin,
-                                            int end, int64_t slot,
-                                            uint16_t (*crow2)[kTileKeys][kRowPad],
-                                            uint16_t (*qlo_s)[kLat + 8]) {
+                                            int end, int64_t slot, MlaSplitLds& sm) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int g = lane >> 4;
-  const int c16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = wave >> 1;
+  const int half = wave & 1;
+  const int c = lane & 31;
+  const int hh = lane >> 5;
   const int hb = hg * kGroup;
   const int nh = min(kGroup, p.num_heads - hb);
-  const int h0 = hb + wave * kHeadsPerWave;
-  const bool active = wave * kHeadsPerWave < nh;   // waves past the last head only stage tiles
+  const bool active = pair * kPairHeads < nh;      // pairs past the last head only load tiles
+  const int h0 = hb + pair * kPairHeads;
+  const bool head_ok = pair * kPairHeads + c < nh;
   const int32_t* bt = p.block_table + static_cast<int64_t>(b) * p.bt_stride;
 
-  __syncthreads();   // the previous segment is done with qlo_s and crow
+  __syncthreads();   // the previous segment is done with the tiles and partials
 
-  // Staging of one tile: 32 keys x 72 chunks of 16 B.  Wave w stages keys
-  // 8w .. 8w+7, lane l key 8w + l/8 and its chunks l%8 + 8k (k < 9), so each
-  // lane resolves one page per tile and the chunk offsets are constants.
-  // FP8 rows: lane l loads E4M3 latent chunks l%8 + 8k (k < 4, 16 dims each,
-  // block (l%8)/4 + 2k), rope chunk l%8 and the 8 scale bytes.
-  // The page of the next tile's key is fetched one tile ahead.
-  constexpr int kChunks = F8 ? 5 : kRow / 8 / 8;   // 16-byte loads per lane and tile
-  const int skey = wave * 8 + (lane >> 3);
-  const int schunk = lane & 7;
-  uint4 stage[kChunks];
-  uint2 sbytes = make_uint2(0, 0);   // FP8: the row's block-scale bytes
-  auto page_of = [&](int t0) -> int {
-    const int t = t0 + skey;
-    return (t >= begin && t < end) ? bt[t >> p.page_shift] : -1;
+  const int first_tile = begin / kTileKeys;
+  const int ntiles = (end - 1) / kTileKeys - first_tile + 1;
+  const int token_bytes = p.token_stride * (F8 ? 1 : 2);
+
+  // ---- page table: lane l holds the physical page of logical page pbase + l ----
+  // (entries past the segment's last page read as 0; reloaded when a tile
+  // reaches beyond the 64 pages held, so no tile load waits on the table)
+  const int plast = (end - 1) >> p.page_shift;
+  int pbase = (first_tile * kTileKeys) >> p.page_shift;
+  auto load_ptab = [&](int base) {
+    const int pi = base + lane;
+    return pi <= plast ? bt[pi] : 0;
   };
-  auto load_tile = [&](int t0, int page) {
-    if constexpr (F8) {
-      const char* src = reinterpret_cast<const char*>(p.cache) +
-                        static_cast<int64_t>(max(page, 0)) * p.page_stride +
-                        static_cast<int64_t>((t0 + skey) & (p.page_size - 1)) * p.token_stride;
-      const uint16_t* lat = reinterpret_cast<const uint16_t*>(src + 16 * schunk);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) stage[k] = page >= 0 ? load16(lat + 64 * k) : make_uint4(0, 0, 0, 0);
-      stage[4] = page >= 0 ? load16(reinterpret_cast<const uint16_t*>(src + kMlaFp8Rope + 16 * schunk))
-                           : make_uint4(0, 0, 0, 0);
-      sbytes = page >= 0 ? *reinterpret_cast<const uint2*>(src + kMlaFp8Scales) : make_uint2(0, 0);
-    } else {
-      const uint16_t* src = p.cache + static_cast<int64_t>(max(page, 0)) * p.page_stride +
-                            static_cast<int64_t>((t0 + skey) & (p.page_size - 1)) * p.token_stride +
-                            schunk * 8;
-#pragma unroll
-      for (int k = 0; k < kChunks; ++k)
-        stage[k] = page >= 0 ? load16(src + 64 * k) : make_uint4(0, 0, 0, 0);
+  int ptab = load_ptab(pbase);
+  auto ensure_ptab = [&](int t0) {     // wave-uniform
+    if ((((t0 + kTileKeys - 1) >> p.page_shift) - pbase) >= 64) {
+      pbase = t0 >> p.page_shift;
+      ptab = load_ptab(pbase);
     }
   };
-  auto store_tile = [&](uint16_t (*dst)[kRowPad]) {
+
+  // ---- tile loads ----
+  // bf16 rows: wave load u = 9w + j (j < 9) fills LDS chunks 64u .. 64u+63 of
+  // the tile; lane i brings the chunk that belongs at position 64u + i.  Waves
+  // 0 and 1 fill rows 0..15, waves 2 and 3 rows 16..31, so each wave reads one
+  // page (16-key pages included) through that page's buffer range.
+  // chunk offsets of this lane's loads within its half-tile (tile-independent)
+  const int hf = wave >> 1;
+  int lvoff[kWaveLoads];
+#pragma unroll
+  for (int j = 0; j < kWaveLoads; ++j) {
+    const int pos = 64 * (kWaveLoads * wave + j) + lane;
+    const int r = pos / kRowChunks;
+    lvoff[j] = (r - 16 * hf) * token_bytes + 16 * ((pos - r * kRowChunks) ^ swz(r));
+  }
+  // One tile's loads: set up (page, buffer range, dead-key offsets) once,
+  // then load j of 9, issued between the MFMAs of the score k-steps.
+  struct TileLoad {
+    __amdgpu_buffer_rsrc_t rs;
+    int soff, buf;
+  } tl_next;
+  auto setup_tile = [&](int it) {
+    const int t0 = (first_tile + it) * kTileKeys;
+    ensure_ptab(t0);
+    const int k0 = t0 + 16 * hf;
+    const int page = __builtin_amdgcn_readlane(ptab, (k0 >> p.page_shift) - pbase);
+    const char* pg = reinterpret_cast<const char*>(p.cache) +
+                     static_cast<int64_t>(page) * p.page_stride * 2;
+    tl_next.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(pg), static_cast<short>(0),
+                                                   (p.page_size - 1) * token_bytes + kRow * 2,
+                                                   0x00020000);
+    tl_next.soff = (k0 & (p.page_size - 1)) * token_bytes;
+    tl_next.buf = it % kTileBufs;
+    if (!(k0 >= begin && k0 + 16 <= end)) {   // wave-uniform: an edge tile
+#pragma unroll
+      for (int j = 0; j < kWaveLoads; ++j) {
+        const int key = t0 + (64 * (kWaveLoads * wave + j) + lane) / kRowChunks;
+        lvoff[j] = (lvoff[j] & ~kMlaDeadBit) | ((key >= begin && key < end) ? 0 : kMlaDeadBit);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kWaveLoads; ++j) lvoff[j] &= ~kMlaDeadBit;
+    }
+  };
+  auto load_part = [&](int j) {
+    const int u = kWaveLoads * wave + j;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        tl_next.rs, (__attribute__((address_space(3))) void*)(&sm.tile[tl_next.buf][512 * u]), 16,
+        lvoff[j], tl_next.soff, 0, 0);
+  };
+  auto issue_tile = [&](int it) {
+    setup_tile(it);
+#pragma unroll
+    for (int j = 0; j < kWaveLoads; ++j) load_part(j);
+  };
+  // FP8 rows, staged in registers: lane l takes key 8w + l/8 and its latent
+  // E4M3 chunks l%8 + 8k (k < 4, 16 dims each), rope chunk l%8 and the
+  // row's 8 scale bytes; dead keys stage zeros.
+  const int skey = wave * 8 + (lane >> 3);
+  const int schunk = lane & 7;
+  uint4 stage[F8 ? 5 : 1];
+  uint2 sbytes = make_uint2(0, 0);
+  auto stage_tile = [&](int it) {
     if constexpr (F8) {
+      const int t0 = (first_tile + it) * kTileKeys;
+      ensure_ptab(t0);
+      const int t = t0 + skey;
+      const bool live = t >= begin && t < end;
+      const int page = __shfl(ptab, (t >> p.page_shift) - pbase);
+      const char* src = reinterpret_cast<const char*>(p.cache) +
+                        static_cast<int64_t>(page) * p.page_stride +
+                        static_cast<int64_t>(t & (p.page_size - 1)) * p.token_stride;
+      const uint16_t* lat = reinterpret_cast<const uint16_t*>(src + 16 * schunk);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) stage[k] = live ? load16(lat + 64 * k) : make_uint4(0, 0, 0, 0);
+      stage[4] = live ? load16(reinterpret_cast<const uint16_t*>(src + kMlaFp8Rope + 16 * schunk))
+                      : make_uint4(0, 0, 0, 0);
+      sbytes = live ? *reinterpret_cast<const uint2*>(src + kMlaFp8Scales) : make_uint2(0, 0);
+    }
+  };
+  auto store_tile = [&](int buf) {
+    if constexpr (F8) {
+      uint4* row = reinterpret_cast<uint4*>(&sm.tile[buf][skey * kRow]);
+      const int sw = swz(skey);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         // block (schunk >> 2) + 2k: byte of sbytes.x (k < 2) or sbytes.y
@@ -333,199 +458,292 @@ __device__ __forceinline__ void mla_segment(const MlaParams& p, int b, int n, in
         const uint32_t sb = (word >> (8 * ((schunk >> 2) + 2 * (k & 1)))) & 0xffu;
         uint4 lo, hi;
         fp8x16_bf16_scaled(stage[k], u2f(sb << 23), lo, hi);
-        *reinterpret_cast<uint4*>(&dst[skey][16 * (schunk + 8 * k)]) = lo;
-        *reinterpret_cast<uint4*>(&dst[skey][16 * (schunk + 8 * k) + 8]) = hi;
+        const int c0 = 2 * (schunk + 8 * k);
+        row[c0 ^ sw] = lo;
+        row[(c0 + 1) ^ sw] = hi;
       }
-      *reinterpret_cast<uint4*>(&dst[skey][kLat + 8 * schunk]) = stage[4];
-    } else {
-#pragma unroll
-      for (int k = 0; k < kChunks; ++k)
-        *reinterpret_cast<uint4*>(&dst[skey][(schunk + 8 * k) * 8]) = stage[k];
+      row[(kLat / 8 + schunk) ^ sw] = stage[4];
     }
   };
-  const int first_tile = begin / kTileKeys;
-  const int last_tile = (end - 1) / kTileKeys;
-  load_tile(first_tile * kTileKeys, page_of(first_tile * kTileKeys));
-  int page_next = first_tile < last_tile ? page_of((first_tile + 1) * kTileKeys) : -1;
 
-  // Q^T operand for all 18 k-steps: head h0 + c16, dims 32*ks + 8g .. +8;
-  // hi (18 steps) and mid (16 latent steps) in registers, lo in LDS, where
-  // each 1 KB row is one direct global->LDS load of the wave (64 lanes x 16 B).
-  uint4 qh[kKS], qm[kKSL];
-  if (active) {
-    const int64_t hrow = static_cast<int64_t>(b) * p.num_heads + h0 + c16;
+  // ---- q: B operand of the scores, head h0 + c, dims of this wave's half ----
+  uint4 qh[kLatSteps + kRopeSteps], qm[kLatSteps], ql[kLatSteps];
+  {
+    const int64_t hrow = static_cast<int64_t>(b) * p.num_heads + h0 + c;
+    const uint16_t* qhi = p.q_hi + hrow * kRow + kHalfLat * half + 8 * hh;
+    const uint16_t* qmid = p.q_mid + hrow * kLat + kHalfLat * half + 8 * hh;
+    const uint16_t* qlo = p.q_lo + hrow * kLat + kHalfLat * half + 8 * hh;
+    const uint16_t* qrope = p.q_hi + hrow * kRow + kLat + kHalfRope * half + 8 * hh;
+    const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
-    for (int ks = 0; ks < kKS; ++ks) qh[ks] = load16(p.q_hi + hrow * kRow + 32 * ks + 8 * g);
+    for (int ks = 0; ks < kLatSteps; ++ks) {
+      qh[ks] = head_ok ? load16(qhi + 16 * ks) : z;
+      qm[ks] = head_ok ? load16(qmid + 16 * ks) : z;
+      ql[ks] = head_ok ? load16(qlo + 16 * ks) : z;
+    }
 #pragma unroll
-    for (int ks = 0; ks < kKSL; ++ks) qm[ks] = load16(p.q_mid + hrow * kLat + 32 * ks + 8 * g);
+    for (int ks = 0; ks < kRopeSteps; ++ks) qh[kLatSteps + ks] = head_ok ? load16(qrope + 16 * ks) : z;
   }
-  for (int r = wave; r < nh; r += kMlaWaves)
-    __builtin_amdgcn_global_load_lds(
-        (const __attribute__((address_space(1))) void*)(p.q_lo + (static_cast<int64_t>(b) * p.num_heads + hb + r) * kLat + 8 * lane),
-        (__attribute__((address_space(3))) void*)(&qlo_s[r][0]), 16, 0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  f32x4_t acc[kLat / 16];
+  // ---- per-lane LDS addresses (bytes within a tile) ----
+  // score A operand: row c, chunk 32*half + 2ks + hh (latent), 64 + 4*half + 2ks + hh (rope)
+  int sa[4], sr[kRopeSteps];
+  {
+    const int sw = swz(c);
 #pragma unroll
-  for (int jt = 0; jt < kLat / 16; ++jt) acc[jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_ref = -INFINITY;     // per head c16 (same on the 4 lanes of the head)
-  float l_sum = 0.0f;          // this lane's share of the head's denominator
+    for (int r = 0; r < 4; ++r) sa[r] = 16 * (c * kRowChunks + ((32 * half + 2 * r + hh) ^ sw));
+#pragma unroll
+    for (int ks = 0; ks < kRopeSteps; ++ks)
+      sr[ks] = 16 * (c * kRowChunks + ((kLat / 8 + 4 * half + 2 * ks + hh) ^ sw));
+  }
+  // P.V B operand: 16-lane group g = lane/16 reads rows 16kk + 4hh + a/4 (and
+  // + 8), dims 256*half + 32dt + 16(g & 1) + 4(a & 3), a = lane % 16
+  int tb[2];
+  {
+    const int a = lane & 15;
+    const int r = 4 * hh + (a >> 2);
+    const int sw = swz(r);
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      tb[q] = 16 * (r * kRowChunks + ((32 * half + 4 * q + 2 * ((lane >> 4) & 1) + ((a & 3) >> 1)) ^ sw)) +
+              8 * (a & 1);
+  }
 
-  // Tiles alternate between two LDS buffers: tile k+1 is stored into the
-  // other buffer right after tile k's P.V, so one barrier per tile (at the
-  // top: tile k is complete and the other buffer's readers are done) orders
-  // everything.
-  store_tile(crow2[0]);
-  for (int tile = first_tile; tile <= last_tile; ++tile) {
-    const int t0 = tile * kTileKeys;
-    uint16_t (*crow)[kRowPad] = crow2[(tile - first_tile) & 1];
-    uint16_t (*cnext)[kRowPad] = crow2[(tile - first_tile + 1) & 1];
+  f32x16_t acc[kDimTiles];
+#pragma unroll
+  for (int dt = 0; dt < kDimTiles; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[dt][i] = 0.0f;
+  float m_ref = -INFINITY;     // head c, the same on lanes c and c + 32 and on both halves
+  float l_sum = 0.0f;          // this lane's share of head c's denominator
+  const int end_h = CAUSAL ? min(end, n - p.num_queries + 1 + (h0 + c) / p.w_heads) : end;
+  f32x16_t s_mine;             // this wave's partial scores of the previous tile
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s_mine[i] = 0.0f;
+
+  auto next_tile = [&](int it) {   // load tile it (if any) into its buffer in one go
+    if (it < ntiles) {
+      if constexpr (F8) stage_tile(it);
+      else issue_tile(it);
+    }
+  };
+  auto tile_ready = [&](int it) {  // tile it is in LDS for every wave
+    if constexpr (F8) {
+      if (it < ntiles) store_tile(it % kTileBufs);
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
     __syncthreads();
-    // The next tile's loads are issued inside the score loop, between MFMAs
-    // (waves without heads issue and store them here).
-    const bool more = tile < last_tile;
-    const int page_now = page_next;
-    if (more) page_next = tile + 1 < last_tile ? page_of(t0 + 2 * kTileKeys) : -1;
-    if (!active) {
-      if (more) {
-        load_tile(t0 + kTileKeys, page_now);
-        store_tile(cnext);
-      }
-      continue;
-    }
+  };
 
-    // scores S^T for keys t0 .. t0+31 (two 16-key M tiles), heads h0 .. h0+15.
-    // The LDS operands of step ks+1 are read while the MFMAs of step ks run;
-    // the scheduling barriers keep the compiler from hoisting all 18 steps'
-    // reads (which would need ~200 more registers).
-    f32x4_t sc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
-    const uint16_t* arow0 = &crow[key_row(c16)][8 * g];
-    const uint16_t* arow1 = &crow[16 + key_row(c16)][8 * g];
-    const uint16_t* lrow = &qlo_s[wave * kHeadsPerWave + c16][8 * g];
-    uint4 a0 = *reinterpret_cast<const uint4*>(arow0);
-    uint4 a1 = *reinterpret_cast<const uint4*>(arow1);
-    uint4 qlv = *reinterpret_cast<const uint4*>(lrow);
-#pragma unroll
-    for (int ks = 0; ks < kKS; ++ks) {
-      uint4 n0 = a0, n1 = a1, nl = qlv;
-      if (ks + 1 < kKS) {
-        n0 = *reinterpret_cast<const uint4*>(arow0 + 32 * (ks + 1));
-        n1 = *reinterpret_cast<const uint4*>(arow1 + 32 * (ks + 1));
-        if (ks + 1 < kKSL) nl = *reinterpret_cast<const uint4*>(lrow + 32 * (ks + 1));
-      }
-      if (ks < kKSL) {
-        sc[0] = mfma(a0, qlv, sc[0]);
-        sc[1] = mfma(a1, qlv, sc[1]);
-        sc[0] = mfma(a0, qm[ks], sc[0]);
-        sc[1] = mfma(a1, qm[ks], sc[1]);
-      }
-      sc[0] = mfma(a0, qh[ks], sc[0]);
-      sc[1] = mfma(a1, qh[ks], sc[1]);
-      if (ks == 2 && more) load_tile(t0 + kTileKeys, page_now);
-      a0 = n0;
-      a1 = n1;
-      qlv = nl;
-      __builtin_amdgcn_sched_barrier(0);
+  // Iteration it: the score MFMAs of tile it run with the softmax of tile
+  // it-1 (VALU) placed between them in slices, one slice per k-step; then
+  // the P.V MFMAs of tile it-1, with the exchange write of tile it's partial
+  // scores.  SC / SM: whether there is a tile it / a tile it-1.
+  auto iteration = [&](int it, auto sc_on, auto sm_on) {
+    constexpr bool SC = decltype(sc_on)::value;
+    constexpr bool SM = decltype(sm_on)::value;
+    tile_ready(it);
+    // tile it+1: FP8 rows are staged now; bf16 rows go straight to LDS, one
+    // load per score k-step
+    const bool more = it + 1 < ntiles;
+    if constexpr (F8) {
+      if (more) stage_tile(it + 1);
+    } else if constexpr (!SC) {
+      if (more) issue_tile(it + 1);
+    } else {
+      if (more) setup_tile(it + 1);
     }
-    // lane holds keys t0 + 16*mt + key_row(4g + i) for head c16
-    float pv[8];
-    float cm = -INFINITY;
-    const int end_h = CAUSAL ? min(end, n - p.num_queries + 1 + (h0 + c16) / p.w_heads) : end;
+    // softmax state of tile it-1
+    f32x4_t px[4];
+    if constexpr (SM) {
+      const f32x4_t* src = &sm.xs[(it - 1) & 1][wave ^ 1][0][lane];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+      for (int q = 0; q < 4; ++q) px[q] = src[64 * q];
+    }
+    float v[16];
+    float cm = -INFINITY, nref = m_ref, alpha = 1.0f, base = 0.0f, lpart = 0.0f;
+    bool bump = false;
+    uint4 ph[2], pm[2], pl[2];
+    const int t0p = (first_tile + it - 1) * kTileKeys;
+    auto softmax_slice = [&](int k) {
+      // each slice ends with its results pinned (an empty asm that reads
+      // them), so the optimiser cannot sink the work towards its later uses
+      if (k == 0) {           // full scores: this half plus the partner's
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = t0 + 16 * mt + key_row(4 * g + i);
-        const float v = (t >= begin && t < end_h) ? sc[mt][i] * p.scale_log2 : -INFINITY;
-        pv[4 * mt + i] = v;
-        cm = fmaxf(cm, v);
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[4 * q + e] = s_mine[4 * q + e] + px[q][e];
+            pin(v[4 * q + e]);
+          }
+      } else if (k == 1 || k == 2) {   // scale and mask (keys outside [begin, end_h))
+        const int lo = begin - t0p, hi = end_h - t0p;
+#pragma unroll
+        for (int i = 8 * (k - 1); i < 8 * k; ++i) {
+          const int r = 8 * (i >> 2) + 4 * hh + (i & 3);
+          v[i] = (r >= lo && r < hi) ? v[i] * p.scale_log2 : -INFINITY;
+          pin(v[i]);
+        }
+      } else if (k == 3) {    // per-head max over the 32 keys
+#pragma unroll
+        for (int i = 0; i < 16; ++i) cm = fmaxf(cm, v[i]);
+        cm = fmaxf(cm, xhalf(cm));
+        pin(cm);
+      } else if (k == 4) {    // reference max (moves when passed by more than 8)
+        bump = cm > m_ref + 8.0f;
+        nref = bump ? cm : m_ref;
+        alpha = (m_ref == -INFINITY) ? 0.0f : fast_exp2(m_ref - nref);
+        base = (nref == -INFINITY) ? 0.0f : nref;
+        pin(nref);
+        pin(alpha);
+        pin(base);
+      } else if (k >= 5 && k <= 8) {
+#pragma unroll
+        for (int i = 4 * (k - 5); i < 4 * (k - 4); ++i) {
+          v[i] = fast_exp2(v[i] - base);
+          lpart += v[i];
+          pin(v[i]);
+        }
+        pin(lpart);
+      } else if (k >= 9 && k <= 12) {   // P in three bf16 terms, two pairs per slice
+        const int kk = (k - 9) >> 1, q0 = ((k - 9) & 1) * 2;
+#pragma unroll
+        for (int q = q0; q < q0 + 2; ++q) {
+          uint32_t hi2, mi2, lo2;
+          split3_bf16x2(v[8 * kk + 2 * q], v[8 * kk + 2 * q + 1], hi2, mi2, lo2);
+          pin(hi2);
+          pin(mi2);
+          pin(lo2);
+          if (q == 0) { ph[kk].x = hi2; pm[kk].x = mi2; pl[kk].x = lo2; }
+          if (q == 1) { ph[kk].y = hi2; pm[kk].y = mi2; pl[kk].y = lo2; }
+          if (q == 2) { ph[kk].z = hi2; pm[kk].z = mi2; pl[kk].z = lo2; }
+          if (q == 3) { ph[kk].w = hi2; pm[kk].w = mi2; pl[kk].w = lo2; }
+        }
       }
-    cm = fmaxf(cm, xor16(cm));
-    cm = fmaxf(cm, xor32(cm));
-    // move the reference max when a score passes it by more than 8
-    const bool bump = cm > m_ref + 8.0f;
-    if (__builtin_amdgcn_read_exec() & __ballot(bump)) {
-      const float nref = bump ? cm : m_ref;
-      const float alpha = (m_ref == -INFINITY) ? 0.0f : fast_exp2(m_ref - nref);
+    };
+    // scores of tile it, softmax slices of tile it-1 between the k-steps
+    f32x16_t sc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sc[i] = 0.0f;
+    if constexpr (SC) {
+      // the operand of k-step ks is read two steps ahead; the softmax slices
+      // start two steps in, once the partner's partial scores have arrived
+      const char* tl = reinterpret_cast<const char*>(&sm.tile[it % kTileBufs][0]);
+      auto aread = [&](int ks) {
+        return ks < kLatSteps ? *reinterpret_cast<const uint4*>(tl + sa[ks & 3] + 128 * (ks >> 2))
+                              : *reinterpret_cast<const uint4*>(tl + sr[ks - kLatSteps]);
+      };
+      uint4 a0 = aread(0), a1 = aread(1);
+#pragma unroll
+      for (int ks = 0; ks < kLatSteps + kRopeSteps; ++ks) {
+        uint4 a2 = a1;
+        if (ks + 2 < kLatSteps + kRopeSteps) a2 = aread(ks + 2);
+        if (ks < kLatSteps) {
+          sc = mfma32(a0, ql[ks], sc);
+          sc = mfma32(a0, qm[ks], sc);
+        }
+        sc = mfma32(a0, qh[ks], sc);
+        if constexpr (SM)
+          if (ks >= 2) softmax_slice(ks - 2);
+        if constexpr (!F8)
+          if (ks < kWaveLoads && more) load_part(ks);
+        a0 = a1;
+        a1 = a2;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 13; ++k) softmax_slice(k);
+    }
+    if constexpr (SM) {
+      // the rare rescale of the accumulators (heads whose reference moved)
+      l_sum = l_sum * alpha + lpart;
       m_ref = nref;
-      l_sum *= alpha;
-      // accumulator rows are heads 4g + i: fetch their factors
-      float ar[4];
+      if (__builtin_amdgcn_read_exec() & __ballot(bump)) {
+        // accumulator element i of a lane is head 8(i/4) + 4hh + i%4
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * g + i);
+        for (int i = 0; i < 16; ++i) {
+          const float ar = __shfl(alpha, 8 * (i >> 2) + 4 * hh + (i & 3));
 #pragma unroll
-      for (int jt = 0; jt < kLat / 16; ++jt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[jt][i] *= ar[i];
-    }
-    const float base = (m_ref == -INFINITY) ? 0.0f : m_ref;
-    float e[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      e[k] = fast_exp2(pv[k] - base);
-      l_sum += e[k];
-    }
-    uint4 pa_hi, pa_mid, pa_lo;
-    split3_bf16x2(e[0], e[1], pa_hi.x, pa_mid.x, pa_lo.x);
-    split3_bf16x2(e[2], e[3], pa_hi.y, pa_mid.y, pa_lo.y);
-    split3_bf16x2(e[4], e[5], pa_hi.z, pa_mid.z, pa_lo.z);
-    split3_bf16x2(e[6], e[7], pa_hi.w, pa_mid.w, pa_lo.w);
-    // O[heads][latent] += P . C over the 32 keys of the tile; lane (g, a)
-    // points the transposed reads at the rows of keys key_row(4g + a/4) and
-    // 16 + key_row(4g + a/4), columns 16*jt + 4*(a%4).
-    const int krow = key_row(4 * g + (c16 >> 2));
-    const uint16_t* brow0 = &crow[krow][4 * (c16 & 3)];
-    const uint16_t* brow1 = &crow[16 + krow][4 * (c16 & 3)];
-    // Two N-tiles per step, the next pair's transposed reads in flight, the
-    // MFMAs of the pair interleaved so no MFMA waits on the one before it.
-    uint2 ka0 = lds_read_tr(brow0), ka1 = lds_read_tr(brow1);
-    uint2 kb0 = lds_read_tr(brow0 + 16), kb1 = lds_read_tr(brow1 + 16);
-#pragma unroll
-    for (int jt = 0; jt < kLat / 16; jt += 2) {
-      const uint4 bopa = make_uint4(ka0.x, ka0.y, ka1.x, ka1.y);
-      const uint4 bopb = make_uint4(kb0.x, kb0.y, kb1.x, kb1.y);
-      if (jt + 2 < kLat / 16) {
-        ka0 = lds_read_tr(brow0 + 16 * (jt + 2));
-        ka1 = lds_read_tr(brow1 + 16 * (jt + 2));
-        kb0 = lds_read_tr(brow0 + 16 * (jt + 3));
-        kb1 = lds_read_tr(brow1 + 16 * (jt + 3));
+          for (int dt = 0; dt < kDimTiles; ++dt) {
+            float x = acc[dt][i];
+            scale_in_agpr(x, ar);
+            acc[dt][i] = x;
+          }
+        }
       }
-      acc[jt] = mfma(pa_lo, bopa, acc[jt]);
-      acc[jt + 1] = mfma(pa_lo, bopb, acc[jt + 1]);
-      acc[jt] = mfma(pa_mid, bopa, acc[jt]);
-      acc[jt + 1] = mfma(pa_mid, bopb, acc[jt + 1]);
-      acc[jt] = mfma(pa_hi, bopa, acc[jt]);
-      acc[jt + 1] = mfma(pa_hi, bopb, acc[jt + 1]);
-      __builtin_amdgcn_sched_barrier(0);
+      // P.V of tile it-1: the B operands of dim tile dt+1 are read while dt's
+      // MFMAs run; the exchange write of tile it's scores goes in after dt 0
+      const char* tvb = reinterpret_cast<const char*>(&sm.tile[(it - 1) % kTileBufs][0]);
+      auto bread = [&](int dt, int kk) {
+        const char* p0 = tvb + tb[dt & 1] + 128 * (dt >> 1) + 16 * kk * kRowChunks * 16;
+        const uint2 b0 = lds_read_tr(reinterpret_cast<const uint16_t*>(p0));
+        const uint2 b1 = lds_read_tr(reinterpret_cast<const uint16_t*>(p0 + 8 * kRowChunks * 16));
+        return make_uint4(b0.x, b0.y, b1.x, b1.y);
+      };
+      uint4 b0 = bread(0, 0), b1 = bread(0, 1);
+#pragma unroll
+      for (int dt = 0; dt < kDimTiles; ++dt) {
+        uint4 n0 = b0, n1 = b1;
+        if (dt + 1 < kDimTiles) {
+          n0 = bread(dt + 1, 0);
+          n1 = bread(dt + 1, 1);
+        }
+        acc[dt] = mfma32(pl[0], b0, acc[dt]);
+        acc[dt] = mfma32(pl[1], b1, acc[dt]);
+        acc[dt] = mfma32(pm[0], b0, acc[dt]);
+        acc[dt] = mfma32(pm[1], b1, acc[dt]);
+        acc[dt] = mfma32(ph[0], b0, acc[dt]);
+        acc[dt] = mfma32(ph[1], b1, acc[dt]);
+        if (SC && dt == 0) {
+          f32x4_t* dst = &sm.xs[it & 1][wave][0][lane];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) dst[64 * q] = f32x4_t{sc[4 * q], sc[4 * q + 1], sc[4 * q + 2], sc[4 * q + 3]};
+        }
+        b0 = n0;
+        b1 = n1;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else if constexpr (SC) {
+      f32x4_t* dst = &sm.xs[it & 1][wave][0][lane];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dst[64 * q] = f32x4_t{sc[4 * q], sc[4 * q + 1], sc[4 * q + 2], sc[4 * q + 3]};
     }
-    if (more) store_tile(cnext);
-  }
+    if constexpr (SC) s_mine = sc;
+  };
+
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  next_tile(0);
+  iteration(0, T_{}, F_{});
+  for (int it = 1; it < ntiles; ++it) iteration(it, T_{}, T_{});
+  iteration(ntiles, F_{}, T_{});
   if (!active) return;
 
-  // denominators: lanes of one head (c16) across the 4 key groups
-  l_sum += xor16(l_sum);
-  l_sum += xor32(l_sum);
-  float lr[4];
+  // denominators: head c's sum over lanes c and c + 32; accumulator element
+  // i is head 8(i/4) + 4hh + i%4
+  const float l_tot = l_sum + xhalf(l_sum);
+  const int64_t srow = slot * kGroup + pair * kPairHeads;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) lr[i] = __shfl(l_sum, 4 * g + i);
-  const int64_t srow = slot * kGroup + wave * kHeadsPerWave;
+  for (int i = 0; i < 16; ++i) {
+    const int hr = 8 * (i >> 2) + 4 * hh + (i & 3);
+    const float lr = __shfl(l_tot, hr);
+    const float inv = (!CAUSAL || lr > 0.0f) ? 1.0f / lr : 0.0f;
+    float* dst = p.seg_out + (srow + hr) * kLat + kHalfLat * half + c;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float* dst = p.seg_out + (srow + 4 * g + i) * kLat;
-    const float inv = (!CAUSAL || lr[i] > 0.0f) ? 1.0f / lr[i] : 0.0f;
-#pragma unroll
-    for (int jt = 0; jt < kLat / 16; ++jt) dst[16 * jt + c16] = acc[jt][i] * inv;
+    for (int dt = 0; dt < kDimTiles; ++dt) dst[32 * dt] = acc[dt][i] * inv;
   }
-  if (g == 0) {
-    p.seg_max[srow + c16] = m_ref * kLn2;
-    p.seg_sum[srow + c16] = l_sum;
+  if (half == 0 && hh == 0) {
+    p.seg_max[srow + c] = m_ref * kLn2;
+    p.seg_sum[srow + c] = l_tot;
   }
 }
 
 template <bool F8, bool CAUSAL>
-__global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(const MlaParams p) {
-  __shared__ __align__(16) uint16_t crow[2][kTileKeys][kRowPad];
-  __shared__ __align__(16) uint16_t qlo_s[kGroup][kLat + 8];
+__global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(1)))
+void mla_split_kernel(const MlaParams p) {
+  __shared__ MlaSplitLds sm;
   __shared__ int64_t sh[4];
   __shared__ int sh_b;
 
@@ -562,7 +780,7 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(const MlaParams 
     const int end = static_cast<int>(min(u1 - row_start, static_cast<int64_t>(n)));
     if (end > begin)
       mla_segment<F8, CAUSAL>(p, b, n, hg, begin, end, static_cast<int64_t>(hg) * p.batch + b + i,
-                              crow, qlo_s);
+                              sm);
     u = row_start + n;
     pre += n;
     if (++b == p.batch) {

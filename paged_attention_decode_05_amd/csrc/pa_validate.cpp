@@ -178,7 +178,7 @@ bool plan_decode(int32_t batch, int32_t num_kv_heads, int32_t vheads, int32_t he
 // keys in all, capped); 0 leaves it to the library (one block per CU).
 bool plan_mla(int32_t batch, int32_t num_heads, int32_t max_pages_per_seq, int32_t page_size,
               int32_t partition_size, MlaPlan* plan) {
-  if (batch < 1 || num_heads < 1 || num_heads % kMlaHeadTile || max_pages_per_seq < 1 ||
+  if (batch < 1 || num_heads < 1 || max_pages_per_seq < 1 ||
       !page_size_supported(page_size) || partition_size < 0 || partition_size % kMlaKeyTile)
     return false;
   const int64_t keys = static_cast<int64_t>(max_pages_per_seq) * page_size;
@@ -230,8 +230,6 @@ int check_mla(const void* q_nope, const void* q_rope, const void* kv_cache,
   if (cache->num_kv_heads != 1 || cache->head_dim != row)
     return fail(PA_ERR_UNSUPPORTED, fp8 ? "FP8 MLA cache must have num_kv_heads 1 and head_dim 656 (bytes)"
                                         : "MLA cache must have num_kv_heads 1 and head_dim 576");
-  if (num_heads % kMlaHeadTile)
-    return fail(PA_ERR_UNSUPPORTED, "num_heads must be a multiple of 16");
   if (!page_size_supported(cache->page_size))
     return fail(PA_ERR_UNSUPPORTED, "page_size must be 16, 32 or 64");
   if (partition_size < 0 || partition_size % kMlaKeyTile)

@@ -80,7 +80,6 @@ constexpr int32_t kMlaRope = 64;
 constexpr int32_t kMlaLat = 512;
 constexpr int32_t kMlaRow = kMlaLat + kMlaRope;  // 576
 constexpr int32_t kMlaDv = 128;
-constexpr int32_t kMlaHeadTile = 16;             // heads per MFMA tile
 constexpr int32_t kMlaKeyTile = 64;              // partition sizes are multiples of this
 constexpr int32_t kMlaBlockHeads = 64;           // heads per split-kernel block (a head group)
 constexpr int32_t kMlaMaxBlocks = 512;           // split blocks at the library's choice (>= CUs)

@@ -40,9 +40,11 @@ def test_small_mixed_lengths(oracle):
     _gate(run_mla(case.to("cuda")), ref, "mla small")
 
 
-@pytest.mark.parametrize("heads", [16, 32, 48, 80, 128])
+@pytest.mark.parametrize("heads", [1, 3, 16, 17, 32, 33, 48, 80, 100, 128])
 def test_head_counts(oracle, heads):
-    """Head counts that fill 1..4 waves of a 64-head block and spill into a second block."""
+    """Head counts that fill part of a 32-head wave-pair tile, one or both pairs
+    of a 64-head block, and spill into a second block (1, 3 and 17 as in the
+    test discipline of the kernel matrix's sparse-MLA row)."""
     case = _case((5, 129, 700), heads=heads, page_size=32, seed=9100 + heads)
     ref, _, _ = oracle.mla(case)
     _gate(run_mla(case.to("cuda")), ref, f"mla heads={heads}")
