@@ -27,7 +27,7 @@ EXPORTS = ("pa_decode", "pa_decode_splitkv", "pa_merge_lse", "pa_decode_workspac
            "pa_decode_multiquery", "pa_decode_multiquery_workspace_size", "pa_decode_fp8",
            "pa_decode_f32", "mla_cache_insert_fp8", "mla_absorbed_decode_fp8",
            "mla_absorbed_decode_multiquery", "mla_absorbed_decode_multiquery_fp8",
-           "pa_decode_noalloc", "pa_last_error")
+           "pa_decode_noalloc", "pa_profile_next", "pa_last_error")
 
 
 class PaError(RuntimeError):
@@ -93,12 +93,20 @@ def _load() -> C.CDLL:
     lib.mla_cache_insert.restype = C.c_int
     lib.mla_cache_insert_fp8.argtypes = [vp, i64, vp, i64, vp, kvp, vp, i32, vp]
     lib.mla_cache_insert_fp8.restype = C.c_int
+    lib.pa_profile_next.argtypes = [vp, vp]
+    lib.pa_profile_next.restype = None
     lib.pa_last_error.argtypes = []
     lib.pa_last_error.restype = C.c_char_p
     return lib
 
 
 LIB = _load()
+
+
+def pa_profile_next(start_event: Optional[int], stop_event: Optional[int]) -> None:
+    """Arm the next call on this thread to record two hipEvent_t handles around
+    its dominant kernel (see include/pa_decode.h)."""
+    LIB.pa_profile_next(start_event, stop_event)
 
 
 def pa_last_error() -> str:

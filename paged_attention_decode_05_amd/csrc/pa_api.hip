@@ -13,8 +13,11 @@
 #include "pa_validate.h"
 
 #include "pa_params.h"
+#include "pa_profile.h"
 
 namespace pa {
+
+thread_local ProfileHook g_profile;
 
 hipError_t launch_split(const SplitParams& p, int head_dim, int group, int batch,
                         int num_kv_heads, hipStream_t stream);
@@ -292,6 +295,11 @@ size_t pa_decode_multiquery_workspace_size(int32_t batch, int32_t num_q_heads,
 }
 
 const char* pa_last_error(void) { return pa::last_error(); }
+
+void pa_profile_next(void* start_event, void* stop_event) {
+  pa::g_profile.start = static_cast<hipEvent_t>(start_event);
+  pa::g_profile.stop = static_cast<hipEvent_t>(stop_event);
+}
 
 }  // extern "C"
 

@@ -33,6 +33,7 @@
 #include "pa_device.h"
 #include "pa_mfma.h"
 #include "pa_params.h"
+#include "pa_profile.h"
 #include "pa_validate.h"
 
 namespace pa {
@@ -1366,14 +1367,18 @@ template <int D, int G>
 static hipError_t launch_split_dg(const SplitParams& p, int batch, int num_kv_heads,
                                   hipStream_t stream) {
   dim3 grid(p.max_parts, num_kv_heads, batch);
+  profile_begin(stream);
   hipLaunchKernelGGL((split_kernel<D, G>), grid, dim3(kBlock), 0, stream, p);
+  profile_end(stream);
   return hipGetLastError();
 }
 
 template <int D, int G, int KV>
 static hipError_t launch_balanced_dg(const SplitParams& p, const BalancedLayout& bl, int grid,
                                      hipStream_t stream) {
+  profile_begin(stream);
   hipLaunchKernelGGL((balanced_split_kernel<D, G, KV>), dim3(grid), dim3(kBlock), 0, stream, p, bl);
+  profile_end(stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !bl.seg_out) return e;   // no workspace: rows were written whole
   hipLaunchKernelGGL((balanced_merge_kernel<D, G>), dim3(bl.rows, (G * D / 4 + kBlock - 1) / kBlock),
@@ -1421,6 +1426,7 @@ hipError_t launch_split(const SplitParams& p, int head_dim, int group, int batch
 
 hipError_t launch_merge(const MergeParams& p, int head_dim, int batch, hipStream_t stream) {
   dim3 grid(p.num_q_heads, batch);
+  profile_begin(stream);
   if (head_dim == 64) {
     hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(kBlock), 0, stream, p);
   } else if (head_dim == 128) {
@@ -1430,8 +1436,10 @@ hipError_t launch_merge(const MergeParams& p, int head_dim, int batch, hipStream
   } else if (head_dim == 512) {
     hipLaunchKernelGGL(merge_kernel<512>, grid, dim3(kBlock), 0, stream, p);
   } else {
+    profile_end(stream);
     return hipErrorInvalidValue;
   }
+  profile_end(stream);
   return hipGetLastError();
 }
 
