@@ -89,4 +89,18 @@ __device__ __forceinline__ uint2 lds_read_tr(const uint16_t* p) {
   return __builtin_bit_cast(uint2, v);
 }
 
+// Byte address of p (which points into LDS) in the LDS aperture.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)(p)));
+}
+
+// lds_read_tr at an LDS byte address: written as base + constant, the
+// constant goes into the instruction's offset field instead of costing an
+// address add per read.
+__device__ __forceinline__ uint2 lds_read_tr_at(uint32_t addr) {
+  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)(addr));
+  return __builtin_bit_cast(uint2, v);
+}
+
 }  // namespace pa

@@ -567,6 +567,8 @@ __device__ __forceinline__ void mla_segment(const MlaParams& p, int b, int n, in
     bool bump = false;
     uint4 ph[2], pm[2], pl[2];
     const int t0p = (first_tile + it - 1) * kTileKeys;
+    const bool inner = __builtin_amdgcn_read_exec() ==
+                       __ballot(t0p >= begin && t0p + kTileKeys <= end_h);
     auto softmax_slice = [&](int k) {
       // each slice ends with its results pinned (an empty asm that reads
       // them), so the optimiser cannot sink the work towards its later uses
@@ -579,12 +581,20 @@ __device__ __forceinline__ void mla_segment(const MlaParams& p, int b, int n, in
             pin(v[4 * q + e]);
           }
       } else if (k == 1 || k == 2) {   // scale and mask (keys outside [begin, end_h))
-        const int lo = begin - t0p, hi = end_h - t0p;
+        if (inner) {                     // wave-uniform: no key of the tile is masked
 #pragma unroll
-        for (int i = 8 * (k - 1); i < 8 * k; ++i) {
-          const int r = 8 * (i >> 2) + 4 * hh + (i & 3);
-          v[i] = (r >= lo && r < hi) ? v[i] * p.scale_log2 : -INFINITY;
-          pin(v[i]);
+          for (int i = 8 * (k - 1); i < 8 * k; ++i) {
+            v[i] *= p.scale_log2;
+            pin(v[i]);
+          }
+        } else {
+          const int lo = begin - t0p, hi = end_h - t0p;
+#pragma unroll
+          for (int i = 8 * (k - 1); i < 8 * k; ++i) {
+            const int r = 8 * (i >> 2) + 4 * hh + (i & 3);
+            v[i] = (r >= lo && r < hi) ? v[i] * p.scale_log2 : -INFINITY;
+            pin(v[i]);
+          }
         }
       } else if (k == 3) {    // per-head max over the 32 keys
 #pragma unroll
@@ -676,11 +686,12 @@ __device__ __forceinline__ void mla_segment(const MlaParams& p, int b, int n, in
       }
       // P.V of tile it-1: the B operands of dim tile dt+1 are read while dt's
       // MFMAs run; the exchange write of tile it's scores goes in after dt 0
-      const char* tvb = reinterpret_cast<const char*>(&sm.tile[(it - 1) % kTileBufs][0]);
+      const uint32_t tvb = lds_addr(&sm.tile[(it - 1) % kTileBufs][0]);
+      const uint32_t tv0 = tvb + tb[0], tv1 = tvb + tb[1];
       auto bread = [&](int dt, int kk) {
-        const char* p0 = tvb + tb[dt & 1] + 128 * (dt >> 1) + 16 * kk * kRowChunks * 16;
-        const uint2 b0 = lds_read_tr(reinterpret_cast<const uint16_t*>(p0));
-        const uint2 b1 = lds_read_tr(reinterpret_cast<const uint16_t*>(p0 + 8 * kRowChunks * 16));
+        const uint32_t a0 = ((dt & 1) ? tv1 : tv0) + 128 * (dt >> 1) + 16 * kk * kRowChunks * 16;
+        const uint2 b0 = lds_read_tr_at(a0);
+        const uint2 b1 = lds_read_tr_at(a0 + 8 * kRowChunks * 16);
         return make_uint4(b0.x, b0.y, b1.x, b1.y);
       };
       uint4 b0 = bread(0, 0), b1 = bread(0, 1);
@@ -691,6 +702,8 @@ __device__ __forceinline__ void mla_segment(const MlaParams& p, int b, int n, in
           n0 = bread(dt + 1, 0);
           n1 = bread(dt + 1, 1);
         }
+        // the reads stay ahead of this tile's six MFMAs, which hide their latency
+        __builtin_amdgcn_sched_barrier(0);
         acc[dt] = mfma32(pl[0], b0, acc[dt]);
         acc[dt] = mfma32(pl[1], b1, acc[dt]);
         acc[dt] = mfma32(pm[0], b0, acc[dt]);
