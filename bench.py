@@ -17,8 +17,9 @@ value        algorithmic bytes per call / (timed region / K)        (GB/s, 1e9 B
 roofline     one definition for every workload: the algorithmic bytes (or, for the
              MFMA-bound MLA split kernel, flops) of one call divided by the mean
              duration of that call's dominant kernel, which the library times with
-             two HIP events it records on the launch stream right around that
-             kernel (pa_profile_next); averaged over K calls.  `traffic` is the HBM
+             two HIP events attached to that kernel's launch (pa_profile_next:
+             hipExtLaunchKernelGGL stamps them as the kernel starts and ends, the
+             clock of a rocprofv3 kernel trace); averaged over K calls.  `traffic` is the HBM
              byte count of that kernel from the rocprofv3 FETCH_SIZE / WRITE_SIZE
              summary under profiles/, or null when the kernel sources changed
              since the counters were taken.
@@ -176,8 +177,8 @@ def roofline(t: Timing, kernel: str, profile: str | None, rotate: int, nbytes=No
              "algorithmic_bytes_per_launch": int(nbytes)}
     r.update({"kernel": kernel, "kernel_us": round(t.kern_mean * 1e3, 2),
               "definition": "algorithmic work of one call / mean duration of its dominant kernel "
-                            "(HIP events recorded by the library around that kernel's launch, "
-                            "on the launch stream)"})
+                            "(HIP events attached by the library to that kernel's launch, "
+                            "stamped as it starts and ends on the launch stream)"})
     return r
 
 
@@ -331,8 +332,9 @@ def bench_gqa(a, torch, pb, wl, dev) -> int:
     kname = f"balanced_split_kernel<{D}, {1 << (H // Hkv - 1).bit_length()}, {c0.kv_dtype}>"
     roof = roofline(t, f"{entry}: {kname}",
                     {"llama": "pa_decode_llama_bs64", "llama_fp8": "pa_decode_fp8_llama_bs64",
-                     "d512": "pa_decode_d512_bs64", "d256w": "pa_decode_d256w_bs32",
-                     "long": "pa_decode_long_bs4", "tiny": "pa_decode_tiny"}.get(a.workload),
+                     "llama_f32": "pa_decode_f32_llama_bs64", "d512": "pa_decode_d512_bs64",
+                     "d256w": "pa_decode_d256w_bs32", "long": "pa_decode_long_bs4",
+                     "tiny": "pa_decode_tiny"}.get(a.workload),
                     a.rotate, nbytes=nbytes)
     parity = cpu = None
     if not a.no_cpu:
@@ -416,7 +418,7 @@ def bench_insert(a, torch, pb, wl, dev) -> int:
 
     t = Timing(torch, pb, a, step)
     nbytes = 2 * (2 * T * 8 * 128 * 2)          # K and V rows read once and written once
-    roof = roofline(t, "pa_kv_insert: kv_insert_kernel", None, a.rotate, nbytes=nbytes)
+    roof = roofline(t, "pa_kv_insert: kv_insert_kernel", "pa_kv_insert_8192", a.rotate, nbytes=nbytes)
     return line(a, "KV insert GB/s (rows read + written), 8192 tokens x 8 KV heads x d128",
                 nbytes, t, {"workload": "KV insert of an 8192-token chunk into the llama-shaped "
                                         "pools", "tokens": T}, roof, dtype="u16 copy")

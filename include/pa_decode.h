@@ -486,16 +486,17 @@ PA_API int mla_absorbed_decode_multiquery_fp8(const void* q_nope, const void* q_
                                               void* stream);
 
 /* Measurement hook.  Arms the calling thread so that its next entry-point
- * call records start_event on its stream right before launching that call's
- * dominant kernel, and stop_event right after it: the split kernel of the
- * pa_decode family and of pa_decode_splitkv, the merge kernel of
- * pa_merge_lse, the split kernel of the absorbed-MLA entry points, the copy
- * kernel of pa_kv_insert.  The hook is then disarmed; a call that fails
+ * call launches that call's dominant kernel with start_event and stop_event
+ * attached to the launch itself (hipExtLaunchKernelGGL), so that they are
+ * stamped on its stream when the kernel starts and when it ends: the split
+ * kernel of the pa_decode family and of pa_decode_splitkv, the merge kernel
+ * of pa_merge_lse, the split kernel of the absorbed-MLA entry points, the
+ * copy kernel of pa_kv_insert.  The hook is then disarmed; a call that fails
  * validation launches nothing and leaves it armed.  The events are
- * hipEvent_t values owned by the caller (NULL cancels).  Nothing else about
- * the call changes; it exists so a benchmark can time that kernel alone, live,
- * with the events of the stream it runs on [measurement of a kernel against
- * its roofline: the duration of its own launches]. */
+ * hipEvent_t values owned by the caller, created with timing enabled (NULL
+ * cancels).  Nothing else about the call changes; it exists so a benchmark
+ * can time that kernel alone, live, on the stream it runs on [measurement of
+ * a kernel against its roofline: the duration of its own launches]. */
 PA_API void pa_profile_next(void* start_event, void* stop_event);
 
 /* Text describing the last non-zero status returned on the calling thread

@@ -227,10 +227,8 @@ int pa_kv_insert(const void* k_new, const void* v_new, int64_t src_token_stride,
   const int64_t threads = static_cast<int64_t>(num_tokens) * 2 * p.chunks_per_tensor;
   const int64_t blocks = (threads + pa::kCopyThreads - 1) / pa::kCopyThreads;
   pa::clear_error();
-  pa::profile_begin(static_cast<hipStream_t>(stream));
-  hipLaunchKernelGGL(pa::kv_insert_kernel, dim3(static_cast<unsigned>(blocks)),
-                     dim3(pa::kCopyThreads), 0, static_cast<hipStream_t>(stream), p);
-  pa::profile_end(static_cast<hipStream_t>(stream));
+  pa::launch_profiled(pa::kv_insert_kernel, dim3(static_cast<unsigned>(blocks)),
+                      dim3(pa::kCopyThreads), 0, static_cast<hipStream_t>(stream), p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return pa::fail(PA_ERR_LAUNCH, std::string("kv insert: ") + hipGetErrorString(e));
   return PA_OK;

@@ -1367,18 +1367,14 @@ template <int D, int G>
 static hipError_t launch_split_dg(const SplitParams& p, int batch, int num_kv_heads,
                                   hipStream_t stream) {
   dim3 grid(p.max_parts, num_kv_heads, batch);
-  profile_begin(stream);
-  hipLaunchKernelGGL((split_kernel<D, G>), grid, dim3(kBlock), 0, stream, p);
-  profile_end(stream);
+  launch_profiled(split_kernel<D, G>, grid, dim3(kBlock), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int D, int G, int KV>
 static hipError_t launch_balanced_dg(const SplitParams& p, const BalancedLayout& bl, int grid,
                                      hipStream_t stream) {
-  profile_begin(stream);
-  hipLaunchKernelGGL((balanced_split_kernel<D, G, KV>), dim3(grid), dim3(kBlock), 0, stream, p, bl);
-  profile_end(stream);
+  launch_profiled(balanced_split_kernel<D, G, KV>, dim3(grid), dim3(kBlock), 0, stream, p, bl);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !bl.seg_out) return e;   // no workspace: rows were written whole
   hipLaunchKernelGGL((balanced_merge_kernel<D, G>), dim3(bl.rows, (G * D / 4 + kBlock - 1) / kBlock),
@@ -1426,20 +1422,17 @@ hipError_t launch_split(const SplitParams& p, int head_dim, int group, int batch
 
 hipError_t launch_merge(const MergeParams& p, int head_dim, int batch, hipStream_t stream) {
   dim3 grid(p.num_q_heads, batch);
-  profile_begin(stream);
   if (head_dim == 64) {
-    hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(kBlock), 0, stream, p);
+    launch_profiled(merge_kernel<64>, grid, dim3(kBlock), 0, stream, p);
   } else if (head_dim == 128) {
-    hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(kBlock), 0, stream, p);
+    launch_profiled(merge_kernel<128>, grid, dim3(kBlock), 0, stream, p);
   } else if (head_dim == 256) {
-    hipLaunchKernelGGL(merge_kernel<256>, grid, dim3(kBlock), 0, stream, p);
+    launch_profiled(merge_kernel<256>, grid, dim3(kBlock), 0, stream, p);
   } else if (head_dim == 512) {
-    hipLaunchKernelGGL(merge_kernel<512>, grid, dim3(kBlock), 0, stream, p);
+    launch_profiled(merge_kernel<512>, grid, dim3(kBlock), 0, stream, p);
   } else {
-    profile_end(stream);
     return hipErrorInvalidValue;
   }
-  profile_end(stream);
   return hipGetLastError();
 }
 

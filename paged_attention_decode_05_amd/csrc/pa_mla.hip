@@ -1070,16 +1070,14 @@ int mla_decode_impl(const void* q_nope, const void* q_rope, const void* kv_cache
   // one query, or no mask: every head sees the whole context
   const bool masked = causal && num_queries > 1;
   const dim3 sg(p.split_grid), st(pa::kMlaThreads);
-  pa::profile_begin(s);
   if (fp8 && masked)
-    hipLaunchKernelGGL((pa::mla_split_kernel<true, true>), sg, st, 0, s, p);
+    pa::launch_profiled(pa::mla_split_kernel<true, true>, sg, st, 0, s, p);
   else if (fp8)
-    hipLaunchKernelGGL((pa::mla_split_kernel<true, false>), sg, st, 0, s, p);
+    pa::launch_profiled(pa::mla_split_kernel<true, false>, sg, st, 0, s, p);
   else if (masked)
-    hipLaunchKernelGGL((pa::mla_split_kernel<false, true>), sg, st, 0, s, p);
+    pa::launch_profiled(pa::mla_split_kernel<false, true>, sg, st, 0, s, p);
   else
-    hipLaunchKernelGGL((pa::mla_split_kernel<false, false>), sg, st, 0, s, p);
-  pa::profile_end(s);
+    pa::launch_profiled(pa::mla_split_kernel<false, false>, sg, st, 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return pa::fail(PA_ERR_LAUNCH, std::string("split: ") + hipGetErrorString(e));
   // 16 sequences per merge block (a full MFMA tile, W_UV read half as often)
