@@ -315,11 +315,15 @@ PA_API int32_t pa_decode_partition_size(int32_t batch, int32_t num_q_heads,
  *   out[b][h][dv] = bf16( sum_j w_uv[h][dv][j] * o_lat[j] )    (dv < 128)
  * q_abs, the probabilities and o_lat are fp32; they enter the bf16 matrix
  * products as three bf16 terms that sum to the fp32 value exactly, so only
- * fp32 accumulation rounds.  The keys of every (64-head group, sequence) row,
- * laid end to end, are cut into equal contiguous ranges, one per workgroup
- * (about partition_size keys each, or for 0 the library's choice, a count
- * fixed by the build rather than the device); the pieces of a row are
- * merged by log-sum-exp in ascending order; an empty context gives 0.
+ * fp32 accumulation rounds.  Each (64-head group, sequence) row is cut into
+ * pieces of whole 32-key tiles, one per workgroup, in one of two ways chosen
+ * from the context lengths alone: every row into its own near-equal pieces,
+ * the fewest tiles per piece that fit the grid (at most partition_size keys
+ * each when that is given), or, when rows are too few for even pieces, the
+ * keys of all rows laid end to end and cut into equal contiguous ranges (the
+ * library's choice only; a grid fixed by the shapes and the build rather
+ * than the device).  The pieces of a row are merged by log-sum-exp in
+ * ascending order; an empty context gives 0.
  * Deterministic run to run, the same on every gfx950 device, and
  * independent of page placement.
  *
@@ -328,8 +332,9 @@ PA_API int32_t pa_decode_partition_size(int32_t batch, int32_t num_q_heads,
  * page_size 16/32/64, token_stride >= 576 and a multiple of 8);
  * w_uk, w_uv [num_heads][128][512] bf16; out [batch][num_heads][128] bf16.
  * Any num_heads >= 1 (heads past the last 32-head tile are masked).
- * partition_size: keys per workgroup
- * (multiple of 64, or 0 to let the library choose from host-known shapes).
+ * partition_size: most keys per piece of a row (multiple of 64; pieces grow
+ * when a call would need more than 16384 of them), or 0 to let the library
+ * choose.
  * workspace: at least mla_absorbed_decode_workspace_size(...) bytes,
  * 256-byte aligned, clobbered by the call.  Device-side contract as for
  * pa_decode: 0 <= context_lens[b] <= max_pages_per_seq * page_size and the

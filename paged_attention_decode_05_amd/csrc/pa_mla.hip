@@ -58,7 +58,7 @@ constexpr int kRow = kMlaRow;      // 576
 constexpr int kNope = kMlaNope;    // 128
 constexpr int kRope = kMlaRope;    // 64
 constexpr int kDv = kMlaDv;        // 128
-constexpr int kTileKeys = 32;      // keys per LDS tile
+constexpr int kTileKeys = kMlaTileKeys;   // keys per LDS tile
 constexpr int kMlaWaves = 4;       // two wave pairs of 32 heads
 constexpr int kGroup = 64;         // heads per block
 constexpr int kMlaThreads = 64 * kMlaWaves;
@@ -91,8 +91,9 @@ struct MlaParams {
   int32_t groups;          // ceil(num_heads / 64)
   int32_t page_size;
   int32_t page_shift;
-  int32_t split_grid;      // blocks launched for the split kernel
-  int32_t min_keys;        // keys per block below which fewer blocks are used
+  int32_t split_grid;      // blocks launched for the split kernel (and partial slots)
+  int32_t min_tiles;       // fewest 32-key tiles a piece of a row is given
+  int32_t explicit_size;   // the caller fixed the piece size (min_tiles tiles)
   float scale_log2;
 };
 
@@ -206,6 +207,88 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(const MlaParams p) {
 
 // ---- 2. split attention over the latent cache ----------------------------------------
 
+// Two ways to cut the work of the split kernel, chosen per call from the
+// context lengths alone (deterministic, the same on every device), both
+// merged by log-sum-exp in ascending key order:
+//
+// Pieces of rows: row (group hg, sequence b) of T_b = ceil(ctx_b / 32) tiles
+// is cut into n_b = ceil(T_b / L) pieces, piece j taking tiles
+// [j T_b / n_b, (j+1) T_b / n_b), the same for every group.  Group hg's
+// pieces are blocks (and partial slots) hg*N .. hg*N + N - 1, sequence b's
+// from the prefix sum of n_{b' < b}, with N = sum_b n_b rounded up to a
+// multiple of 8 (the groups' pieces of one key range then sit on one XCD).
+// L is the least tile count >= lmin whose pieces fit in nb blocks.  Every
+// block owns one range of one row: no block pays for a second row's start
+// (q loads, a drained and refilled tile pipeline, a second partial), which
+// costs about as much as three or four tiles.
+//
+// The key line: the keys of all rows laid end to end (group-major), cut into
+// equal ranges, one per block, so a block may cover the end of one row and
+// the start of the next; segment (row r, block i) writes slot r + i.  Taken
+// at the library's choice when rows are too few for even pieces (the largest
+// piece more than kMlaRowSlack tiles above the mean), as in a multi-query
+// verify whose many head groups leave two or three blocks per row.
+constexpr int kMlaRowSlack = 3;
+
+struct MlaSplit {
+  bool rows;   // pieces of rows, else the key line
+  int L;       // pieces of rows: tiles per piece, at most
+  int N;       // pieces of rows: blocks per head group (0: no key anywhere)
+  int64_t S;   // key line: keys per group (sum of the context lengths)
+  int nb;      // key line: blocks used
+};
+
+__device__ __forceinline__ int mla_tiles(const int32_t* ctx, int b) { return (ctx[b] + 31) >> 5; }
+
+// explicit: the caller fixed the piece size (lmin tiles): pieces of rows.
+__device__ __forceinline__ MlaSplit mla_plan(const int32_t* ctx, int batch, int groups, int lmin,
+                                             int nb, bool explicit_size) {
+  const int lane = threadIdx.x & 63;
+  int64_t tiles = 0, keys = 0;
+  int tmax = 0;
+  for (int b0 = 0; b0 < batch; b0 += 64) {
+    const int t = (b0 + lane < batch) ? mla_tiles(ctx, b0 + lane) : 0;
+    keys += (b0 + lane < batch) ? ctx[b0 + lane] : 0;
+    tiles += t;
+    tmax = max(tmax, t);
+  }
+  tiles = wave_sum64(tiles);
+  keys = wave_sum64(keys);
+  tmax = static_cast<int>(wave_max(static_cast<float>(tmax)));   // exact below 2^24
+  auto pieces = [&](int L) {          // blocks per head group for L tiles per piece
+    int64_t n = 0;
+    for (int b0 = 0; b0 < batch; b0 += 64)
+      n += (b0 + lane < batch) ? (mla_tiles(ctx, b0 + lane) + L - 1) / L : 0;
+    return (wave_sum64(n) + 7) / 8 * 8;
+  };
+  auto fits = [&](int L) { return groups * pieces(L) <= nb; };
+  int lo = static_cast<int>(max<int64_t>(lmin, (groups * tiles + nb - 1) / nb));
+  int L = lo;
+  if (tmax > 0 && !fits(lo)) {        // gallop, then bisect: fits(lo) false, fits(hi) true
+    int step = max(1, lo / 8);
+    int hi = lo + step;
+    while (hi < tmax && !fits(hi)) {
+      lo = hi;
+      step *= 2;
+      hi = lo + step;
+    }
+    if (hi >= tmax) hi = tmax;        // one piece per row fits (the host sizes the grid so)
+    while (hi - lo > 1) {
+      const int mid = lo + (hi - lo) / 2;
+      if (fits(mid)) hi = mid;
+      else lo = mid;
+    }
+    L = hi;
+  }
+  MlaSplit sp{true, L, tmax > 0 ? static_cast<int>(pieces(L)) : 0, keys, 0};
+  const int64_t mean = (groups * tiles + nb - 1) / nb;
+  if (!explicit_size && L > mean + kMlaRowSlack) {
+    sp.rows = false;
+    sp.nb = used_blocks(groups * keys, nb, int64_t{kMlaMinKeys});
+  }
+  return sp;
+}
+
 // Sum of the context lengths.  Called by a whole wave.
 __device__ __forceinline__ int64_t mla_total(const int32_t* ctx, int batch) {
   const int lane = threadIdx.x & 63;
@@ -228,6 +311,29 @@ __device__ __forceinline__ void mla_locate(const int32_t* ctx, int batch, int64_
       const int l = __ffsll(static_cast<unsigned long long>(hit)) - 1;
       b_out = b0 + l;
       pre_out = base + __shfl(incl, l) - __shfl(len, l);
+      return;
+    }
+    base += __shfl(incl, 63);
+  }
+  b_out = batch;
+  pre_out = base;
+}
+
+
+// Sequence b whose pieces hold piece k (0 <= k < sum_b n_b) of a head group,
+// and the pieces before b.  Called by a whole wave; b = batch past the last.
+__device__ __forceinline__ void mla_piece_row(const int32_t* ctx, int batch, int L, int k, int& b_out,
+                                              int& pre_out) {
+  const int lane = threadIdx.x & 63;
+  int base = 0;
+  for (int b0 = 0; b0 < batch; b0 += 64) {
+    const int n = (b0 + lane < batch) ? (mla_tiles(ctx, b0 + lane) + L - 1) / L : 0;
+    const int incl = static_cast<int>(wave_scan64(n));
+    const uint64_t hit = __ballot(base + incl > k);
+    if (hit) {
+      const int l = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+      b_out = b0 + l;
+      pre_out = base + __shfl(incl, l) - __shfl(n, l);
       return;
     }
     base += __shfl(incl, 63);
@@ -759,48 +865,75 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(1))
 void mla_split_kernel(const MlaParams p) {
   __shared__ MlaSplitLds sm;
   __shared__ int64_t sh[4];
-  __shared__ int sh_b;
-
+  __shared__ int sh_b, sh_rows;
+  const int i = blockIdx.x;
   if (threadIdx.x < 64) {
-    const int64_t S = mla_total(p.context_lens, p.batch);
-    const int64_t T = S * p.groups;
-    const int nb = used_blocks(T, p.split_grid, p.min_keys);
-    const int i = blockIdx.x;
-    const int64_t u0 = T * i / nb;
+    const MlaSplit sp = mla_plan(p.context_lens, p.batch, p.groups, p.min_tiles, p.split_grid,
+                                 p.explicit_size);
     int b = p.batch;
-    int64_t pre = 0;
-    if (i < nb && S > 0) mla_locate(p.context_lens, p.batch, u0 % S, b, pre);
+    if (sp.rows) {                            // piece j of row (hg, b): tiles [j T / n, (j+1) T / n)
+      const int hg = sp.N > 0 ? i / sp.N : p.groups;
+      int pre = 0;
+      if (hg < p.groups) mla_piece_row(p.context_lens, p.batch, sp.L, i - hg * sp.N, b, pre);
+      if (threadIdx.x == 0) {
+        sh[0] = b < p.batch ? hg : p.groups;  // past the last piece: nothing to do
+        if (b < p.batch) {
+          const int T = mla_tiles(p.context_lens, b), nj = (T + sp.L - 1) / sp.L;
+          const int j = i - hg * sp.N - pre;
+          sh[1] = static_cast<int64_t>(j) * T / nj;
+          sh[2] = static_cast<int64_t>(j + 1) * T / nj;
+        }
+      }
+    } else {                                  // units [i T / nb, (i+1) T / nb) of the key line
+      const int64_t T = sp.S * p.groups;
+      const int64_t u0 = T * i / sp.nb;
+      int64_t pre = 0;
+      if (i < sp.nb && sp.S > 0) mla_locate(p.context_lens, p.batch, u0 % sp.S, b, pre);
+      if (threadIdx.x == 0) {
+        sh[0] = sp.S;
+        sh[1] = (i < sp.nb) ? u0 : 0;
+        sh[2] = (i < sp.nb) ? T * (i + 1) / sp.nb : 0;
+        sh[3] = pre;
+      }
+    }
     if (threadIdx.x == 0) {
-      sh[0] = S;
-      sh[1] = (i < nb) ? u0 : 0;
-      sh[2] = (i < nb) ? T * (i + 1) / nb : 0;
-      sh[3] = pre;
       sh_b = b;
+      sh_rows = sp.rows;
     }
   }
   __syncthreads();
-  const int i = blockIdx.x;
-  const int64_t S = sh[0];
-  const int64_t u1 = sh[2];
-  int64_t u = sh[1];
-  if (u >= u1) return;
-  int hg = static_cast<int>(u / S);
+  // the block's segments (one for a piece of a row), one mla_segment call site
+  const bool rows = sh_rows;
   int b = sh_b;
-  int64_t pre = sh[3];
+  int hg = rows ? static_cast<int>(sh[0]) : 0;
+  const int64_t S = rows ? 0 : sh[0];
+  int64_t u = rows ? 0 : sh[1], u1 = rows ? 1 : sh[2], pre = rows ? 0 : sh[3];
+  if (rows ? hg >= p.groups : u >= u1) return;
+  if (!rows) hg = static_cast<int>(u / S);
   while (u < u1) {
-    const int64_t row_start = hg * S + pre;
     const int n = p.context_lens[b];
-    const int begin = static_cast<int>(u - row_start);
-    const int end = static_cast<int>(min(u1 - row_start, static_cast<int64_t>(n)));
-    if (end > begin)
-      mla_segment<F8, CAUSAL>(p, b, n, hg, begin, end, static_cast<int64_t>(hg) * p.batch + b + i,
-                              sm);
-    u = row_start + n;
-    pre += n;
-    if (++b == p.batch) {
-      b = 0;
-      pre = 0;
-      ++hg;
+    int begin, end;
+    int64_t slot;
+    if (rows) {
+      begin = kTileKeys * static_cast<int>(sh[1]);
+      end = min(n, kTileKeys * static_cast<int>(sh[2]));
+      slot = i;
+      u = u1;
+    } else {                                  // the key line, row by row
+      const int64_t row_start = hg * S + pre;
+      begin = static_cast<int>(u - row_start);
+      end = static_cast<int>(min(u1 - row_start, static_cast<int64_t>(n)));
+      slot = static_cast<int64_t>(hg) * p.batch + b + i;
+      u = row_start + n;
+    }
+    if (end > begin) mla_segment<F8, CAUSAL>(p, b, n, hg, begin, end, slot, sm);
+    if (!rows) {
+      pre += n;
+      if (++b == p.batch) {
+        b = 0;
+        pre = 0;
+        ++hg;
+      }
     }
   }
 }
@@ -854,22 +987,28 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_uv_kernel(const MlaPa
   for (int ks = 0; ks < kLat / 32; ++ks) bw[ks] = load16(wuv + 32 * ks);
 
   if (tid < 64) {
-    const int64_t S = mla_total(p.context_lens, p.batch);
-    const int64_t T = S * p.groups;
-    const int nb = used_blocks(T, p.split_grid, p.min_keys);
-    // keys of the sequences before b0, then the prefix within the tile
+    const MlaSplit sp = mla_plan(p.context_lens, p.batch, p.groups, p.min_tiles, p.split_grid,
+                                 p.explicit_size);
+    // pieces (or keys) of the sequences before b0, then the prefix within the tile
+    auto amount = [&](int b) -> int64_t {
+      return sp.rows ? (mla_tiles(p.context_lens, b) + sp.L - 1) / sp.L : p.context_lens[b];
+    };
     int64_t before = 0;
-    for (int c0 = 0; c0 < b0; c0 += 64) before += (c0 + lane < b0) ? p.context_lens[c0 + lane] : 0;
+    for (int c0 = 0; c0 < b0; c0 += 64) before += (c0 + lane < b0) ? amount(c0 + lane) : 0;
     before = wave_sum64(before);
-    const int64_t len = (lane < nrow) ? p.context_lens[b0 + lane] : 0;
-    const int64_t pre = before + wave_scan64(len) - len;
+    const int64_t a = (lane < nrow) ? amount(b0 + lane) : 0;
+    const int64_t pre = before + wave_scan64(a) - a;
     if (lane < ROWS) {
       int64_t slot = 0;
       int cnt = 0;
-      if (lane < nrow && len > 0) {
-        const int64_t start = hg * S + pre;
-        const int i0 = block_of(start, T, nb);
-        const int i1 = block_of(start + len - 1, T, nb);
+      if (sp.rows) {                           // slots hg*N + pre .. + n_b - 1
+        slot = static_cast<int64_t>(hg) * sp.N + pre;
+        cnt = static_cast<int>(a);
+      } else if (lane < nrow && a > 0) {       // blocks i0 .. i1 cut the row; slots r + i
+        const int64_t T = sp.S * p.groups;
+        const int64_t start = hg * sp.S + pre;
+        const int i0 = block_of(start, T, sp.nb);
+        const int i1 = block_of(start + a - 1, T, sp.nb);
         slot = static_cast<int64_t>(hg) * p.batch + b0 + lane + i0;
         cnt = i1 - i0 + 1;
       }
@@ -1045,19 +1184,14 @@ int mla_decode_impl(const void* q_nope, const void* q_rope, const void* kv_cache
   int shift = 0;
   while ((1 << shift) < cache->page_size) ++shift;
   p.page_shift = shift;
-  // The split's block count is fixed by the build, not the device (so are the
-  // results): kSplitCUs blocks for 256 compute units.
+  // The split's grid is fixed by the shapes and the build, not the device (so
+  // are the results): plan.max_blocks blocks, kSplitCUs (one per compute unit
+  // of MI355X) for the library's choice; each piece gets at least
+  // partition_size keys, or kMlaMinKeys for the library's choice.
   const int cus = pa::kSplitCUs;
-  // Explicit partition size: about that many keys per block.  Library choice:
-  // one block per CU (a multiple of 16, so the head groups of a key range
-  // share an XCD), each block at least kMlaMinKeys keys.
-  if (partition_size > 0) {
-    p.split_grid = plan.max_blocks;
-    p.min_keys = partition_size;
-  } else {
-    p.split_grid = std::max(16, std::min(plan.max_blocks, cus / 16 * 16));
-    p.min_keys = pa::kMlaMinKeys;
-  }
+  p.split_grid = plan.max_blocks;
+  p.min_tiles = (partition_size > 0 ? partition_size : pa::kMlaMinKeys) / pa::kMlaTileKeys;
+  p.explicit_size = partition_size > 0;
   p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
 
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -183,14 +183,15 @@ bool plan_mla(int32_t batch, int32_t num_heads, int32_t max_pages_per_seq, int32
     return false;
   const int64_t keys = static_cast<int64_t>(max_pages_per_seq) * page_size;
   plan->groups = static_cast<int32_t>(ceil_div(num_heads, kMlaBlockHeads));
-  if (partition_size > 0) {
-    const int64_t most = ceil_div(plan->groups * static_cast<int64_t>(batch) * keys, partition_size);
-    plan->max_blocks = static_cast<int32_t>(std::min<int64_t>(std::max<int64_t>(most, 1),
-                                                              kMlaMaxExplicitBlocks));
-  } else {
-    plan->max_blocks = kMlaMaxBlocks;
-  }
+  // every (group, sequence) row needs a block of its own (rows of a group
+  // padded to a multiple of 8)
+  const int64_t rows8 = plan->groups * round_up(static_cast<size_t>(batch), 8);
+  const int64_t most = partition_size > 0 ? rows8 * ceil_div(keys, partition_size) : kSplitCUs;
+  const int64_t cap = partition_size > 0 ? kMlaMaxExplicitBlocks : kSplitCUs;
+  if (rows8 > (int64_t{1} << 30)) return false;
+  plan->max_blocks = static_cast<int32_t>(std::max<int64_t>(rows8, std::min<int64_t>(most, cap)));
   const size_t bh = static_cast<size_t>(batch) * num_heads;
+  // one partial per block, or per (row, block) segment of the key line
   const size_t slots = static_cast<size_t>(plan->groups) * batch + plan->max_blocks;
   size_t o = 0;
   plan->off_qhi = o;      o += round_up(bh * kMlaRow * sizeof(uint16_t), 256);   // q_abs|q_rope, hi

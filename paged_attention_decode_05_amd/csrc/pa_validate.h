@@ -81,10 +81,10 @@ constexpr int32_t kMlaLat = 512;
 constexpr int32_t kMlaRow = kMlaLat + kMlaRope;  // 576
 constexpr int32_t kMlaDv = 128;
 constexpr int32_t kMlaKeyTile = 64;              // partition sizes are multiples of this
+constexpr int32_t kMlaTileKeys = 32;             // keys per LDS tile of the split kernel
 constexpr int32_t kMlaBlockHeads = 64;           // heads per split-kernel block (a head group)
-constexpr int32_t kMlaMaxBlocks = 512;           // split blocks at the library's choice (>= CUs)
 constexpr int32_t kMlaMaxExplicitBlocks = 16384; // cap for an explicit partition size
-constexpr int32_t kMlaMinKeys = 128;             // keys per block below which fewer blocks are used
+constexpr int32_t kMlaMinKeys = 128;             // fewest keys per piece at the library's choice
 // FP8 latent-cache row, in bytes: E4M3 latent (blocks of 64, one scale byte
 // each), bf16 rope, the scale bytes, zero padding to a 16-byte multiple.
 constexpr int32_t kMlaFp8Block = 64;
@@ -94,7 +94,7 @@ constexpr int32_t kMlaFp8Row = kMlaFp8Scales + 16;              // 656
 
 struct MlaPlan {
   int32_t groups = 0;        // ceil(num_heads / 64)
-  int32_t max_blocks = 0;    // split-kernel blocks the workspace has partial slots for
+  int32_t max_blocks = 0;    // split-kernel blocks launched, one partial slot each
   size_t off_qhi = 0, off_qmid = 0, off_qlo = 0;
   size_t off_seg_out = 0, off_seg_max = 0, off_seg_sum = 0, bytes = 0;
 };

@@ -70,20 +70,20 @@ def test_matches_oracle(oracle, S, heads, page, causal, dt, ctx):
 def _pieces_with_blind_queries(ctx, S, heads, partition_size, batch_pages_keys):
     """Number of split pieces that start inside the last S - 1 keys of their
     row (so some query sees none of their keys), for the split that an explicit
-    partition size gives: the keys of all (group, sequence) rows laid end to
-    end, cut into nb = ceil(T / partition_size) equal ranges (nb below the
-    explicit-size block cap here)."""
+    partition size gives when its blocks fit the grid: row (group, sequence)
+    of T = ceil(n / 32) tiles cut into p = ceil(T / (partition_size / 32))
+    pieces, piece j starting at tile j * T // p."""
     groups = (S * heads + 63) // 64
-    total = sum(ctx)
-    T = groups * total
-    nb = -(-T // partition_size)
-    assert nb <= -(-groups * len(ctx) * batch_pages_keys // partition_size)
-    starts = {T * i // nb for i in range(nb)}
-    hits, row = 0, 0
+    L = partition_size // 32
+    rows8 = groups * -(-len(ctx) // 8) * 8
+    cap = max(rows8, min(rows8 * -(-batch_pages_keys // partition_size), 16384))
+    assert groups * -(-sum(-(-(-(-n // 32)) // L) for n in ctx) // 8) * 8 <= cap
+    hits = 0
     for _ in range(groups):
         for n in ctx:
-            hits += sum(1 for u in starts if row + max(0, n - S + 1) <= u < row + n)
-            row += n
+            T = -(-n // 32)
+            p = -(-T // L)
+            hits += sum(1 for j in range(p) if max(0, n - S + 1) <= 32 * (j * T // p) < n)
     return hits
 
 
