@@ -793,7 +793,11 @@ __device__ __forceinline__ void mla_segment(const MlaParams& p, int b, int n, in
       // P.V of tile it-1: the B operands of dim tile dt+1 are read while dt's
       // MFMAs run; the exchange write of tile it's scores goes in after dt 0
       const uint32_t tvb = lds_addr(&sm.tile[(it - 1) % kTileBufs][0]);
-      const uint32_t tv0 = tvb + tb[0], tv1 = tvb + tb[1];
+      uint32_t tv0 = tvb + tb[0], tv1 = tvb + tb[1];
+      // the two bases are fixed here, so each read is base + constant and the
+      // constant goes into the instruction's offset field
+      pin(tv0);
+      pin(tv1);
       auto bread = [&](int dt, int kk) {
         const uint32_t a0 = ((dt & 1) ? tv1 : tv0) + 128 * (dt >> 1) + 16 * kk * kRowChunks * 16;
         const uint2 b0 = lds_read_tr_at(a0);
