@@ -256,10 +256,10 @@ __device__ __forceinline__ MlaSplit mla_plan(const int32_t* ctx, int batch, int 
   keys = wave_sum64(keys);
   tmax = static_cast<int>(wave_max(static_cast<float>(tmax)));   // exact below 2^24
   auto pieces = [&](int L) {          // blocks per head group for L tiles per piece
-    int64_t n = 0;
+    float n = 0.0f;                    // counts below 2^24: the float sum is exact
     for (int b0 = 0; b0 < batch; b0 += 64)
-      n += (b0 + lane < batch) ? (mla_tiles(ctx, b0 + lane) + L - 1) / L : 0;
-    return (wave_sum64(n) + 7) / 8 * 8;
+      n += (b0 + lane < batch) ? static_cast<float>((mla_tiles(ctx, b0 + lane) + L - 1) / L) : 0.0f;
+    return (static_cast<int64_t>(wave_sum(n)) + 7) / 8 * 8;
   };
   auto fits = [&](int L) { return groups * pieces(L) <= nb; };
   int lo = static_cast<int>(max<int64_t>(lmin, (groups * tiles + nb - 1) / nb));
