@@ -97,6 +97,19 @@ struct MlaParams {
   float scale_log2;
 };
 
+// q_abs (three bf16 terms) and q_rope in the workspace, in the split kernel's
+// operand order: for sequence b, 32-head tile ht (heads 32ht .. +32 of the
+// S*H heads), half d of the dims and k-step ks, the 16-byte pieces of the 64
+// lanes back to back.  Lane c + 32hh holds head 32ht + c, dims 256d + 16ks +
+// 8hh .. +8 of the latent part (ks < 16) or, in the hi term only, rope dims
+// 32d + 16(ks - 16) + 8hh .. +8 (ks = 16, 17).  Each q load of the split
+// kernel then reads 1 KB in one piece.  Offset of a piece in 16-byte chunks:
+constexpr int kQHiSteps = kMlaLat / 32 + kMlaRope / 32;   // 18: latent and rope k-steps
+constexpr int kQLoSteps = kMlaLat / 32;                   // 16
+__device__ __forceinline__ int64_t q_piece(int64_t tile, int half, int ks, int lane, int steps) {
+  return ((tile * 2 + half) * steps + ks) * 64 + lane;
+}
+
 // ---- 1. absorption: q_abs = q_nope . W_UK[h] on MFMA, split in three; rope copied ---
 //
 // Block (h, jq, bt): q_abs[r][h][jq*128 .. +128) for the query rows
@@ -180,23 +193,33 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(const MlaParams p) {
     }
     __syncthreads();
     // 3 terms x 16 rows x 16 chunks of 8 columns, three 16-byte stores per thread
+    // (q row r = b S + s, head h: head s H + h of sequence b)
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
       const int e = t + 256 * k;
       const int term = e >> 8, bb = (e >> 4) & 15, ch = e & 15;
       if (bb < nb) {
-        const int64_t row = static_cast<int64_t>(b0 + bb) * p.w_heads + h;
-        uint16_t* dst = term == 0 ? p.q_hi + row * kRow : (term == 1 ? p.q_mid : p.q_lo) + row * kLat;
-        *reinterpret_cast<uint4*>(dst + jq * 128 + 8 * ch) =
-            *reinterpret_cast<const uint4*>(&os[term][bb][8 * ch]);
+        const int r = b0 + bb, sb = r / p.num_queries;
+        const int vh = (r - sb * p.num_queries) * p.w_heads + h;
+        const int j = jq * 128 + 8 * ch;            // latent dims j .. j+7
+        const int64_t tile = static_cast<int64_t>(sb) * ((p.num_heads + 31) >> 5) + (vh >> 5);
+        const int64_t at = q_piece(tile, j >> 8, (j & 255) >> 4, (vh & 31) + 32 * ((j >> 3) & 1),
+                                   term == 0 ? kQHiSteps : kQLoSteps);
+        uint16_t* dst = term == 0 ? p.q_hi : (term == 1 ? p.q_mid : p.q_lo);
+        *reinterpret_cast<uint4*>(dst + 8 * at) = *reinterpret_cast<const uint4*>(&os[term][bb][8 * ch]);
       }
     }
     __syncthreads();   // os is rewritten by the next tile
     if (jq == 0 && t < nb * (kRope / 8)) {   // rope part: exact bf16, one term
       const int rb = t / (kRope / 8), rc = t % (kRope / 8);
-      const int64_t row = static_cast<int64_t>(b0 + rb) * p.w_heads + h;
-      *reinterpret_cast<uint4*>(p.q_hi + row * kRow + kLat + 8 * rc) =
-          load16(p.q_rope + row * kRope + 8 * rc);
+      const int r = b0 + rb, sb = r / p.num_queries;
+      const int vh = (r - sb * p.num_queries) * p.w_heads + h;
+      const int64_t row = static_cast<int64_t>(r) * p.w_heads + h;
+      const int jr = 8 * rc;                       // rope dims jr .. jr+7
+      const int64_t tile = static_cast<int64_t>(sb) * ((p.num_heads + 31) >> 5) + (vh >> 5);
+      const int64_t at = q_piece(tile, jr >> 5, kQLoSteps + ((jr & 31) >> 4),
+                                 (vh & 31) + 32 * ((jr >> 3) & 1), kQHiSteps);
+      *reinterpret_cast<uint4*>(p.q_hi + 8 * at) = load16(p.q_rope + row * kRope + 8 * rc);
     }
     if (more) {
 #pragma unroll
@@ -255,9 +278,13 @@ __device__ __forceinline__ MlaSplit mla_plan(const int32_t* ctx, int batch, int 
   tiles = wave_sum64(tiles);
   keys = wave_sum64(keys);
   tmax = static_cast<int>(wave_max(static_cast<float>(tmax)));   // exact below 2^24
+  // the first 64 rows' tile counts stay in a register: the search below
+  // evaluates pieces() a dozen times, and a pass over the lengths in memory
+  // would put a dependent global load in each
+  const int t_first = lane < batch ? mla_tiles(ctx, lane) : 0;
   auto pieces = [&](int L) {          // blocks per head group for L tiles per piece
-    float n = 0.0f;                    // counts below 2^24: the float sum is exact
-    for (int b0 = 0; b0 < batch; b0 += 64)
+    float n = static_cast<float>((t_first + L - 1) / L);   // counts below 2^24: the float sum is exact
+    for (int b0 = 64; b0 < batch; b0 += 64)
       n += (b0 + lane < batch) ? static_cast<float>((mla_tiles(ctx, b0 + lane) + L - 1) / L) : 0.0f;
     return (static_cast<int64_t>(wave_sum(n)) + 7) / 8 * 8;
   };
@@ -574,22 +601,23 @@ __device__ __forceinline__ void mla_segment(const MlaParams& p, int b, int n, in
   };
 
   // ---- q: B operand of the scores, head h0 + c, dims of this wave's half ----
+  // (the workspace holds them in this order: each load is 1 KB in one piece)
   uint4 qh[kLatSteps + kRopeSteps], qm[kLatSteps], ql[kLatSteps];
   {
-    const int64_t hrow = static_cast<int64_t>(b) * p.num_heads + h0 + c;
-    const uint16_t* qhi = p.q_hi + hrow * kRow + kHalfLat * half + 8 * hh;
-    const uint16_t* qmid = p.q_mid + hrow * kLat + kHalfLat * half + 8 * hh;
-    const uint16_t* qlo = p.q_lo + hrow * kLat + kHalfLat * half + 8 * hh;
-    const uint16_t* qrope = p.q_hi + hrow * kRow + kLat + kHalfRope * half + 8 * hh;
+    static_assert(kQHiSteps == kLatSteps + kRopeSteps && kQLoSteps == kLatSteps, "q layout");
+    const int64_t tile = static_cast<int64_t>(b) * ((p.num_heads + 31) >> 5) + (h0 >> 5);
+    const uint16_t* qhi = p.q_hi + 8 * q_piece(tile, half, 0, lane, kQHiSteps);
+    const uint16_t* qmid = p.q_mid + 8 * q_piece(tile, half, 0, lane, kQLoSteps);
+    const uint16_t* qlo = p.q_lo + 8 * q_piece(tile, half, 0, lane, kQLoSteps);
     const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int ks = 0; ks < kLatSteps; ++ks) {
-      qh[ks] = head_ok ? load16(qhi + 16 * ks) : z;
-      qm[ks] = head_ok ? load16(qmid + 16 * ks) : z;
-      ql[ks] = head_ok ? load16(qlo + 16 * ks) : z;
+      qh[ks] = head_ok ? load16(qhi + 512 * ks) : z;
+      qm[ks] = head_ok ? load16(qmid + 512 * ks) : z;
+      ql[ks] = head_ok ? load16(qlo + 512 * ks) : z;
     }
 #pragma unroll
-    for (int ks = 0; ks < kRopeSteps; ++ks) qh[kLatSteps + ks] = head_ok ? load16(qrope + 16 * ks) : z;
+    for (int ks = kLatSteps; ks < kLatSteps + kRopeSteps; ++ks) qh[ks] = head_ok ? load16(qhi + 512 * ks) : z;
   }
 
   // ---- per-lane LDS addresses (bytes within a tile) ----
@@ -876,16 +904,26 @@ void mla_split_kernel(const MlaParams p) {
                                  p.explicit_size);
     int b = p.batch;
     if (sp.rows) {                            // piece j of row (hg, b): tiles [j T / n, (j+1) T / n)
-      const int hg = sp.N > 0 ? i / sp.N : p.groups;
+      // Work unit k = (piece k / groups, head group k % groups), taken in an
+      // XCD-aware order: the hardware deals consecutive blocks to the 8 XCDs
+      // in turn, so block i takes unit (i % 8) (grid / 8) + i / 8 and each
+      // XCD runs a run of consecutive units.  The head groups of a piece (one
+      // set of latent tiles) and the pieces of a row (one set of q rows) then
+      // meet in one L2.  The partial slot stays hg N + piece.
+      const int nbk = p.split_grid;
+      const int k = (nbk & 7) == 0 ? (i & 7) * (nbk >> 3) + (i >> 3) : i;
+      const int piece = k / p.groups;
+      const int hg = piece < sp.N ? k - piece * p.groups : p.groups;
       int pre = 0;
-      if (hg < p.groups) mla_piece_row(p.context_lens, p.batch, sp.L, i - hg * sp.N, b, pre);
+      if (hg < p.groups) mla_piece_row(p.context_lens, p.batch, sp.L, piece, b, pre);
       if (threadIdx.x == 0) {
         sh[0] = b < p.batch ? hg : p.groups;  // past the last piece: nothing to do
         if (b < p.batch) {
           const int T = mla_tiles(p.context_lens, b), nj = (T + sp.L - 1) / sp.L;
-          const int j = i - hg * sp.N - pre;
+          const int j = piece - pre;
           sh[1] = static_cast<int64_t>(j) * T / nj;
           sh[2] = static_cast<int64_t>(j + 1) * T / nj;
+          sh[3] = static_cast<int64_t>(hg) * sp.N + piece;
         }
       }
     } else {                                  // units [i T / nb, (i+1) T / nb) of the key line
@@ -921,7 +959,7 @@ void mla_split_kernel(const MlaParams p) {
     if (rows) {
       begin = kTileKeys * static_cast<int>(sh[1]);
       end = min(n, kTileKeys * static_cast<int>(sh[2]));
-      slot = i;
+      slot = sh[3];
       u = u1;
     } else {                                  // the key line, row by row
       const int64_t row_start = hg * S + pre;

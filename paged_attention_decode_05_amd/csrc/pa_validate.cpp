@@ -190,7 +190,8 @@ bool plan_mla(int32_t batch, int32_t num_heads, int32_t max_pages_per_seq, int32
   const int64_t cap = partition_size > 0 ? kMlaMaxExplicitBlocks : kSplitCUs;
   if (rows8 > (int64_t{1} << 30)) return false;
   plan->max_blocks = static_cast<int32_t>(std::max<int64_t>(rows8, std::min<int64_t>(most, cap)));
-  const size_t bh = static_cast<size_t>(batch) * num_heads;
+  // q_abs in 32-head tiles (the split kernel's operand layout), heads padded
+  const size_t bh = static_cast<size_t>(batch) * round_up(static_cast<size_t>(num_heads), 32);
   // one partial per block, or per (row, block) segment of the key line
   const size_t slots = static_cast<size_t>(plan->groups) * batch + plan->max_blocks;
   size_t o = 0;

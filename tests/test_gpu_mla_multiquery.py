@@ -141,9 +141,9 @@ def test_rejections():
     ws = torch.zeros(pb.mla_absorbed_decode_workspace_size(B, 2 * H, case.max_pages, 16, 0),
                      dtype=torch.uint8, device="cuda")
     out = torch.empty((B, 2, H, 128), dtype=torch.bfloat16, device="cuda")
-    small = torch.zeros(pb.mla_absorbed_decode_workspace_size(B, H, case.max_pages, 16, 0),
-                        dtype=torch.uint8, device="cuda")
-    with pytest.raises(pb.PaError, match="WORKSPACE"):   # sized for one query, not two
+    need = pb.mla_absorbed_decode_workspace_size(B, 2 * H, case.max_pages, 16, 0)
+    small = torch.zeros(need - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(pb.PaError, match="WORKSPACE"):   # 256 bytes short of two queries' need
         pb.mla_absorbed_decode_multiquery(case.q_nope, case.q_rope, case.cache,
                                           pb.kv_layout(case.cache, "PSR"), case.w_uk, case.w_uv,
                                           case.block_table, case.context_lens, case.scale, out,
