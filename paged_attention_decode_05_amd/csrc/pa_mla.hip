@@ -65,6 +65,8 @@ constexpr int kMlaThreads = 64 * kMlaWaves;
 constexpr int kMlaDeadBit = 0x40000000;   // OR-ed into a dead key's offset: past any page
 static_assert(kGroup == kMlaBlockHeads, "head group size");
 
+struct MlaSplit;
+
 struct MlaParams {
   const uint16_t* q_nope;
   const uint16_t* q_rope;
@@ -73,12 +75,13 @@ struct MlaParams {
   const uint16_t* w_uv;
   const int32_t* block_table;
   const int32_t* context_lens;
-  uint16_t* q_hi;          // [B][H][576]  q_abs | q_rope
-  uint16_t* q_mid;         // [B][H][512]  second and third terms of q_abs
+  uint16_t* q_hi;          // q_abs | q_rope, first terms (the split kernel's operand order)
+  uint16_t* q_mid;         // second and third terms of q_abs
   uint16_t* q_lo;
   float* seg_out;          // [slots][64][512] normalised partial o_lat
   float* seg_max;          // [slots][64] natural-log-domain reference max
   float* seg_sum;          // [slots][64] sum of exp(s - max)
+  MlaSplit* split_plan;    // the split plan, written by the absorb kernel
   uint16_t* out;           // [B][S][H][128]
   int64_t page_stride;
   int32_t token_stride;
@@ -127,7 +130,15 @@ constexpr int kWukPad = 128 + 16;  // LDS row stride of the W_UK tile: 72 dwords
 constexpr int kAbsTiles = 4;       // 16-row tiles per absorb block
 constexpr int kAbsOutPad = 128 + 8;
 
+__device__ void mla_write_plan(const MlaParams& p);
+
+// One more slice of blocks (x = H) holds the block that plans the split
+// kernel's work once per call (the split and merge kernels read the plan).
 __global__ __launch_bounds__(256) void mla_absorb_kernel(const MlaParams p) {
+  if (blockIdx.x == p.w_heads) {
+    if (blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x < 64) mla_write_plan(p);
+    return;
+  }
   __shared__ __align__(16) uint16_t ws[kNope][kWukPad];
   __shared__ __align__(16) uint16_t os[3][16][kAbsOutPad];   // hi, mid, lo of one tile
   const int h = blockIdx.x;
@@ -316,6 +327,14 @@ __device__ __forceinline__ MlaSplit mla_plan(const int32_t* ctx, int batch, int 
   return sp;
 }
 
+// The split plan of this call, written once to the workspace.  Called by a
+// whole wave.
+__device__ void mla_write_plan(const MlaParams& p) {
+  const MlaSplit sp = mla_plan(p.context_lens, p.batch, p.groups, p.min_tiles, p.split_grid,
+                               p.explicit_size);
+  if ((threadIdx.x & 63) == 0) *p.split_plan = sp;
+}
+
 // Sum of the context lengths.  Called by a whole wave.
 __device__ __forceinline__ int64_t mla_total(const int32_t* ctx, int batch) {
   const int lane = threadIdx.x & 63;
@@ -326,12 +345,13 @@ __device__ __forceinline__ int64_t mla_total(const int32_t* ctx, int batch) {
 
 // Sequence b holding key y (0 <= y < S) of a group's key line, and the keys
 // before it.  Called by a whole wave.
-__device__ __forceinline__ void mla_locate(const int32_t* ctx, int batch, int64_t y, int& b_out,
-                                           int64_t& pre_out) {
+// c_first: this lane's context length among the first 64 (0 past the batch).
+__device__ __forceinline__ void mla_locate(const int32_t* ctx, int batch, int64_t y, int c_first,
+                                           int& b_out, int64_t& pre_out) {
   const int lane = threadIdx.x & 63;
   int64_t base = 0;
   for (int b0 = 0; b0 < batch; b0 += 64) {
-    const int64_t len = (b0 + lane < batch) ? ctx[b0 + lane] : 0;
+    const int64_t len = b0 == 0 ? c_first : ((b0 + lane < batch) ? ctx[b0 + lane] : 0);
     const int64_t incl = wave_scan64(len);
     const uint64_t hit = __ballot(base + incl > y);
     if (hit) {
@@ -349,12 +369,14 @@ __device__ __forceinline__ void mla_locate(const int32_t* ctx, int batch, int64_
 
 // Sequence b whose pieces hold piece k (0 <= k < sum_b n_b) of a head group,
 // and the pieces before b.  Called by a whole wave; b = batch past the last.
-__device__ __forceinline__ void mla_piece_row(const int32_t* ctx, int batch, int L, int k, int& b_out,
-                                              int& pre_out) {
+// c_first: this lane's context length among the first 64 (0 past the batch).
+__device__ __forceinline__ void mla_piece_row(const int32_t* ctx, int batch, int L, int k,
+                                              int c_first, int& b_out, int& pre_out) {
   const int lane = threadIdx.x & 63;
   int base = 0;
   for (int b0 = 0; b0 < batch; b0 += 64) {
-    const int n = (b0 + lane < batch) ? (mla_tiles(ctx, b0 + lane) + L - 1) / L : 0;
+    const int t = b0 == 0 ? (c_first + 31) >> 5 : ((b0 + lane < batch) ? mla_tiles(ctx, b0 + lane) : 0);
+    const int n = (t + L - 1) / L;
     const int incl = static_cast<int>(wave_scan64(n));
     const uint64_t hit = __ballot(base + incl > k);
     if (hit) {
@@ -897,11 +919,13 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(1))
 void mla_split_kernel(const MlaParams p) {
   __shared__ MlaSplitLds sm;
   __shared__ int64_t sh[4];
-  __shared__ int sh_b, sh_rows;
+  __shared__ int sh_b, sh_rows, sh_n;
   const int i = blockIdx.x;
   if (threadIdx.x < 64) {
-    const MlaSplit sp = mla_plan(p.context_lens, p.batch, p.groups, p.min_tiles, p.split_grid,
-                                 p.explicit_size);
+    // the first 64 context lengths, loaded beside the plan, so the searches
+    // below and the row's length wait for no further load
+    const int c_first = static_cast<int>(threadIdx.x) < p.batch ? p.context_lens[threadIdx.x] : 0;
+    const MlaSplit sp = *p.split_plan;
     int b = p.batch;
     if (sp.rows) {                            // piece j of row (hg, b): tiles [j T / n, (j+1) T / n)
       // Work unit k = (piece k / groups, head group k % groups), taken in an
@@ -915,11 +939,13 @@ void mla_split_kernel(const MlaParams p) {
       const int piece = k / p.groups;
       const int hg = piece < sp.N ? k - piece * p.groups : p.groups;
       int pre = 0;
-      if (hg < p.groups) mla_piece_row(p.context_lens, p.batch, sp.L, piece, b, pre);
+      if (hg < p.groups) mla_piece_row(p.context_lens, p.batch, sp.L, piece, c_first, b, pre);
+      const int nlen = b < 64 ? __shfl(c_first, b) : (b < p.batch ? p.context_lens[b] : 0);
       if (threadIdx.x == 0) {
         sh[0] = b < p.batch ? hg : p.groups;  // past the last piece: nothing to do
+        sh_n = nlen;
         if (b < p.batch) {
-          const int T = mla_tiles(p.context_lens, b), nj = (T + sp.L - 1) / sp.L;
+          const int T = (nlen + 31) >> 5, nj = (T + sp.L - 1) / sp.L;
           const int j = piece - pre;
           sh[1] = static_cast<int64_t>(j) * T / nj;
           sh[2] = static_cast<int64_t>(j + 1) * T / nj;
@@ -930,7 +956,7 @@ void mla_split_kernel(const MlaParams p) {
       const int64_t T = sp.S * p.groups;
       const int64_t u0 = T * i / sp.nb;
       int64_t pre = 0;
-      if (i < sp.nb && sp.S > 0) mla_locate(p.context_lens, p.batch, u0 % sp.S, b, pre);
+      if (i < sp.nb && sp.S > 0) mla_locate(p.context_lens, p.batch, u0 % sp.S, c_first, b, pre);
       if (threadIdx.x == 0) {
         sh[0] = sp.S;
         sh[1] = (i < sp.nb) ? u0 : 0;
@@ -952,8 +978,9 @@ void mla_split_kernel(const MlaParams p) {
   int64_t u = rows ? 0 : sh[1], u1 = rows ? 1 : sh[2], pre = rows ? 0 : sh[3];
   if (rows ? hg >= p.groups : u >= u1) return;
   if (!rows) hg = static_cast<int>(u / S);
+  const int n_row = sh_n;
   while (u < u1) {
-    const int n = p.context_lens[b];
+    const int n = rows ? n_row : p.context_lens[b];
     int begin, end;
     int64_t slot;
     if (rows) {
@@ -1029,8 +1056,7 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_uv_kernel(const MlaPa
   for (int ks = 0; ks < kLat / 32; ++ks) bw[ks] = load16(wuv + 32 * ks);
 
   if (tid < 64) {
-    const MlaSplit sp = mla_plan(p.context_lens, p.batch, p.groups, p.min_tiles, p.split_grid,
-                                 p.explicit_size);
+    const MlaSplit sp = *p.split_plan;
     // pieces (or keys) of the sequences before b0, then the prefix within the tile
     auto amount = [&](int b) -> int64_t {
       return sp.rows ? (mla_tiles(p.context_lens, b) + sp.L - 1) / sp.L : p.context_lens[b];
@@ -1212,6 +1238,7 @@ int mla_decode_impl(const void* q_nope, const void* q_rope, const void* kv_cache
   p.seg_out = reinterpret_cast<float*>(ws + plan.off_seg_out);
   p.seg_max = reinterpret_cast<float*>(ws + plan.off_seg_max);
   p.seg_sum = reinterpret_cast<float*>(ws + plan.off_seg_sum);
+  p.split_plan = reinterpret_cast<pa::MlaSplit*>(ws + plan.off_split_plan);
   p.out = static_cast<uint16_t*>(out);
   p.page_stride = cache->page_stride;
   p.token_stride = static_cast<int32_t>(cache->token_stride);
@@ -1239,7 +1266,7 @@ int mla_decode_impl(const void* q_nope, const void* q_rope, const void* kv_cache
   hipStream_t s = static_cast<hipStream_t>(stream);
   pa::clear_error();
   const int btiles = (p.abs_rows + 16 * pa::kAbsTiles - 1) / (16 * pa::kAbsTiles);
-  hipLaunchKernelGGL(pa::mla_absorb_kernel, dim3(num_heads, pa::kMlaLat / 128, btiles), dim3(256),
+  hipLaunchKernelGGL(pa::mla_absorb_kernel, dim3(num_heads + 1, pa::kMlaLat / 128, btiles), dim3(256),
                      0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return pa::fail(PA_ERR_LAUNCH, std::string("absorb: ") + hipGetErrorString(e));
