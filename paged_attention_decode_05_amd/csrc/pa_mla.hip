@@ -701,22 +701,35 @@ __device__ __forceinline__ void mla_segment(const MlaParams& p, int b, int n, in
     constexpr bool SC = decltype(sc_on)::value;
     constexpr bool SM = decltype(sm_on)::value;
     tile_ready(it);
-    // tile it+1: FP8 rows are staged now; bf16 rows go straight to LDS, one
-    // load per score k-step
+    // tile it+1: FP8 rows are staged now (their loads first); bf16 rows go
+    // straight to LDS, one load per score k-step
     const bool more = it + 1 < ntiles;
-    if constexpr (F8) {
+    if constexpr (F8)
       if (more) stage_tile(it + 1);
-    } else if constexpr (!SC) {
-      if (more) issue_tile(it + 1);
-    } else {
-      if (more) setup_tile(it + 1);
+    // LDS reads next: the first two score operands of tile it and the
+    // partner's partial scores of tile it-1, so that the bf16 tile's set-up
+    // (branches, each closing the compiler's scheduling region) runs while
+    // they are in flight
+    const char* tl = reinterpret_cast<const char*>(&sm.tile[it % kTileBufs][0]);
+    auto aread = [&](int ks) {
+      return ks < kLatSteps ? *reinterpret_cast<const uint4*>(tl + sa[ks & 3] + 128 * (ks >> 2))
+                            : *reinterpret_cast<const uint4*>(tl + sr[ks - kLatSteps]);
+    };
+    uint4 a0 = make_uint4(0, 0, 0, 0), a1 = a0;
+    if constexpr (SC) {
+      a0 = aread(0);
+      a1 = aread(1);
     }
-    // softmax state of tile it-1
-    f32x4_t px[4];
+    f32x4_t px[4];   // softmax state of tile it-1
     if constexpr (SM) {
       const f32x4_t* src = &sm.xs[(it - 1) & 1][wave ^ 1][0][lane];
 #pragma unroll
       for (int q = 0; q < 4; ++q) px[q] = src[64 * q];
+    }
+    if constexpr (!F8 && !SC) {
+      if (more) issue_tile(it + 1);
+    } else if constexpr (!F8) {
+      if (more) setup_tile(it + 1);
     }
     float v[16];
     float cm = -INFINITY, nref = m_ref, alpha = 1.0f, base = 0.0f, lpart = 0.0f;
@@ -796,12 +809,6 @@ __device__ __forceinline__ void mla_segment(const MlaParams& p, int b, int n, in
     if constexpr (SC) {
       // the operand of k-step ks is read two steps ahead; the softmax slices
       // start two steps in, once the partner's partial scores have arrived
-      const char* tl = reinterpret_cast<const char*>(&sm.tile[it % kTileBufs][0]);
-      auto aread = [&](int ks) {
-        return ks < kLatSteps ? *reinterpret_cast<const uint4*>(tl + sa[ks & 3] + 128 * (ks >> 2))
-                              : *reinterpret_cast<const uint4*>(tl + sr[ks - kLatSteps]);
-      };
-      uint4 a0 = aread(0), a1 = aread(1);
 #pragma unroll
       for (int ks = 0; ks < kLatSteps + kRopeSteps; ++ks) {
         uint4 a2 = a1;
@@ -824,10 +831,14 @@ __device__ __forceinline__ void mla_segment(const MlaParams& p, int b, int n, in
       for (int k = 0; k < 13; ++k) softmax_slice(k);
     }
     if constexpr (SM) {
-      // the rare rescale of the accumulators (heads whose reference moved)
+      // the rare rescale of the accumulators (heads whose reference moved).
+      // A head whose reference moves from -inf has seen no key, so its
+      // accumulators are still exactly 0 and need none: the first tile of a
+      // range, where every head's reference moves, skips it.
+      const bool rescale = bump && m_ref != -INFINITY;
       l_sum = l_sum * alpha + lpart;
       m_ref = nref;
-      if (__builtin_amdgcn_read_exec() & __ballot(bump)) {
+      if (__builtin_amdgcn_read_exec() & __ballot(rescale)) {
         // accumulator element i of a lane is head 8(i/4) + 4hh + i%4
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
