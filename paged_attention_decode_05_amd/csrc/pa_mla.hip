@@ -103,14 +103,16 @@ struct MlaParams {
 // q_abs (three bf16 terms) and q_rope in the workspace, in the split kernel's
 // operand order: for sequence b, 32-head tile ht (heads 32ht .. +32 of the
 // S*H heads), half d of the dims and k-step ks, the 16-byte pieces of the 64
-// lanes back to back.  Lane c + 32hh holds head 32ht + c, dims 256d + 16ks +
-// 8hh .. +8 of the latent part (ks < 16) or, in the hi term only, rope dims
-// 32d + 16(ks - 16) + 8hh .. +8 (ks = 16, 17).  Each q load of the split
-// kernel then reads 1 KB in one piece.  Offset of a piece in 16-byte chunks:
+// lanes in one 1 KB run.  Lane c + 32hh holds head 32ht + c, dims 256d + 16ks
+// + 8hh .. +8 of the latent part (ks < 16) or, in the hi term only, rope dims
+// 32d + 16(ks - 16) + 8hh .. +8 (ks = 16, 17), and sits at position 2c + hh
+// of the run.  Each q load of the split kernel then reads one 1 KB run, and
+// the absorption writes each head's two pieces of a run as 32 contiguous
+// bytes.  Offset of a piece in 16-byte chunks (pos = 2c + hh):
 constexpr int kQHiSteps = kMlaLat / 32 + kMlaRope / 32;   // 18: latent and rope k-steps
 constexpr int kQLoSteps = kMlaLat / 32;                   // 16
-__device__ __forceinline__ int64_t q_piece(int64_t tile, int half, int ks, int lane, int steps) {
-  return ((tile * 2 + half) * steps + ks) * 64 + lane;
+__device__ __forceinline__ int64_t q_piece(int64_t tile, int half, int ks, int pos, int steps) {
+  return ((tile * 2 + half) * steps + ks) * 64 + pos;
 }
 
 // ---- 1. absorption: q_abs = q_nope . W_UK[h] on MFMA, split in three; rope copied ---
@@ -214,7 +216,7 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(const MlaParams p) {
         const int vh = (r - sb * p.num_queries) * p.w_heads + h;
         const int j = jq * 128 + 8 * ch;            // latent dims j .. j+7
         const int64_t tile = static_cast<int64_t>(sb) * ((p.num_heads + 31) >> 5) + (vh >> 5);
-        const int64_t at = q_piece(tile, j >> 8, (j & 255) >> 4, (vh & 31) + 32 * ((j >> 3) & 1),
+        const int64_t at = q_piece(tile, j >> 8, (j & 255) >> 4, 2 * (vh & 31) + ((j >> 3) & 1),
                                    term == 0 ? kQHiSteps : kQLoSteps);
         uint16_t* dst = term == 0 ? p.q_hi : (term == 1 ? p.q_mid : p.q_lo);
         *reinterpret_cast<uint4*>(dst + 8 * at) = *reinterpret_cast<const uint4*>(&os[term][bb][8 * ch]);
@@ -229,7 +231,7 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(const MlaParams p) {
       const int jr = 8 * rc;                       // rope dims jr .. jr+7
       const int64_t tile = static_cast<int64_t>(sb) * ((p.num_heads + 31) >> 5) + (vh >> 5);
       const int64_t at = q_piece(tile, jr >> 5, kQLoSteps + ((jr & 31) >> 4),
-                                 (vh & 31) + 32 * ((jr >> 3) & 1), kQHiSteps);
+                                 2 * (vh & 31) + ((jr >> 3) & 1), kQHiSteps);
       *reinterpret_cast<uint4*>(p.q_hi + 8 * at) = load16(p.q_rope + row * kRope + 8 * rc);
     }
     if (more) {
@@ -628,9 +630,10 @@ __device__ __forceinline__ void mla_segment(const MlaParams& p, int b, int n, in
   {
     static_assert(kQHiSteps == kLatSteps + kRopeSteps && kQLoSteps == kLatSteps, "q layout");
     const int64_t tile = static_cast<int64_t>(b) * ((p.num_heads + 31) >> 5) + (h0 >> 5);
-    const uint16_t* qhi = p.q_hi + 8 * q_piece(tile, half, 0, lane, kQHiSteps);
-    const uint16_t* qmid = p.q_mid + 8 * q_piece(tile, half, 0, lane, kQLoSteps);
-    const uint16_t* qlo = p.q_lo + 8 * q_piece(tile, half, 0, lane, kQLoSteps);
+    const int pos = 2 * c + hh;
+    const uint16_t* qhi = p.q_hi + 8 * q_piece(tile, half, 0, pos, kQHiSteps);
+    const uint16_t* qmid = p.q_mid + 8 * q_piece(tile, half, 0, pos, kQLoSteps);
+    const uint16_t* qlo = p.q_lo + 8 * q_piece(tile, half, 0, pos, kQLoSteps);
     const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int ks = 0; ks < kLatSteps; ++ks) {
