@@ -67,6 +67,14 @@ static_assert(kGroup == kMlaBlockHeads, "head group size");
 
 struct MlaSplit;
 
+// The partial slots of one (head group, sequence) row: slot .. slot + cnt - 1,
+// in ascending key order.
+struct MlaRowSlots {
+  int64_t slot;
+  int32_t cnt;
+  int32_t pad;
+};
+
 struct MlaParams {
   const uint16_t* q_nope;
   const uint16_t* q_rope;
@@ -82,6 +90,7 @@ struct MlaParams {
   float* seg_max;          // [slots][64] natural-log-domain reference max
   float* seg_sum;          // [slots][64] sum of exp(s - max)
   MlaSplit* split_plan;    // the split plan, written by the absorb kernel
+  MlaRowSlots* row_slots;  // [groups][batch], written with it
   uint16_t* out;           // [B][S][H][128]
   int64_t page_stride;
   int32_t token_stride;
@@ -334,7 +343,36 @@ __device__ __forceinline__ MlaSplit mla_plan(const int32_t* ctx, int batch, int 
 __device__ void mla_write_plan(const MlaParams& p) {
   const MlaSplit sp = mla_plan(p.context_lens, p.batch, p.groups, p.min_tiles, p.split_grid,
                                p.explicit_size);
-  if ((threadIdx.x & 63) == 0) *p.split_plan = sp;
+  const int lane = threadIdx.x & 63;
+  if (lane == 0) *p.split_plan = sp;
+  // each row's partial slots: pieces of rows, slots hg N + (pieces before b)
+  // .. + n_b - 1; the key line, slots hg B + b + i for the blocks i0 .. i1
+  // whose ranges cut the row
+  int64_t before = 0;
+  for (int b0 = 0; b0 < p.batch; b0 += 64) {
+    const int b = b0 + lane;
+    const int n = b < p.batch ? p.context_lens[b] : 0;
+    const int64_t a = sp.rows ? ((n + 31) / 32 + sp.L - 1) / sp.L : n;
+    const int64_t pre = before + wave_scan64(a) - a;
+    before += wave_sum64(a);
+    if (b < p.batch) {
+      for (int hg = 0; hg < p.groups; ++hg) {
+        MlaRowSlots r{0, 0, 0};
+        if (sp.rows) {
+          r.slot = static_cast<int64_t>(hg) * sp.N + pre;
+          r.cnt = static_cast<int32_t>(a);
+        } else if (a > 0) {
+          const int64_t T = sp.S * p.groups;
+          const int64_t start = hg * sp.S + pre;
+          const int i0 = block_of(start, T, sp.nb);
+          const int i1 = block_of(start + a - 1, T, sp.nb);
+          r.slot = static_cast<int64_t>(hg) * p.batch + b + i0;
+          r.cnt = i1 - i0 + 1;
+        }
+        p.row_slots[static_cast<int64_t>(hg) * p.batch + b] = r;
+      }
+    }
+  }
 }
 
 // Sum of the context lengths.  Called by a whole wave.
@@ -1025,10 +1063,10 @@ void mla_split_kernel(const MlaParams p) {
 //
 // Block (h, bt, s) handles sequences ROWS*bt .. +ROWS (ROWS = 8 or 16) of
 // head s*H + h (query s, W_UV[h]; hg below is that head's group): row
-// (group hg, b) was cut into pieces by blocks i0 .. i1 of the split
-// (recomputed here from the context lengths), whose partials sit in slots
-// r + i0 .. r + i1 with r = hg*batch + b.  The max M and the total
-// W = sum l_i e^(m_i - M) of a row are wave reductions over its pieces; o_lat
+// (group hg, b) was cut into pieces whose partials sit in the slots the
+// absorb kernel's plan block listed for it, in ascending key order.  The max
+// M and the total W = sum l_i e^(m_i - M) of a row are wave reductions over
+// its pieces, loaded together with the first eight pieces' partials; o_lat
 // is the (l_i e^(m_i - M) / W)-weighted sum of the pieces in ascending i
 // (eight pieces' loads in flight), written to LDS as three bf16 terms; then
 // out[b][dv] = sum_j o_lat[b][j] W_UV[h][dv][j] on MFMA with A = o_lat (rows
@@ -1038,7 +1076,6 @@ void mla_split_kernel(const MlaParams p) {
 // sees no key, gives 0.
 constexpr int kMergeThreads = 512;
 constexpr int kMergeWaves = kMergeThreads / 64;
-constexpr int kMergeWts = 64;      // piece weights kept in LDS per row
 
 template <int ROWS>
 __global__ __launch_bounds__(kMergeThreads) void mla_merge_uv_kernel(const MlaParams p) {
@@ -1046,10 +1083,6 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_uv_kernel(const MlaPa
   __shared__ __align__(16) uint16_t ohi[16][kLat + 8];
   __shared__ __align__(16) uint16_t omid[16][kLat + 8];
   __shared__ __align__(16) uint16_t olo[16][kLat + 8];
-  __shared__ float wts[ROWS][kMergeWts];
-  __shared__ int64_t sh_slot[ROWS];
-  __shared__ int sh_cnt[ROWS];
-  __shared__ float sh_m[ROWS], sh_iw[ROWS];
   const int hw = blockIdx.x;                       // head of W_UV
   const int h = blockIdx.z * p.w_heads + hw;       // query head
   const int b0 = blockIdx.y * ROWS;
@@ -1069,35 +1102,6 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_uv_kernel(const MlaPa
 #pragma unroll
   for (int ks = 0; ks < kLat / 32; ++ks) bw[ks] = load16(wuv + 32 * ks);
 
-  if (tid < 64) {
-    const MlaSplit sp = *p.split_plan;
-    // pieces (or keys) of the sequences before b0, then the prefix within the tile
-    auto amount = [&](int b) -> int64_t {
-      return sp.rows ? (mla_tiles(p.context_lens, b) + sp.L - 1) / sp.L : p.context_lens[b];
-    };
-    int64_t before = 0;
-    for (int c0 = 0; c0 < b0; c0 += 64) before += (c0 + lane < b0) ? amount(c0 + lane) : 0;
-    before = wave_sum64(before);
-    const int64_t a = (lane < nrow) ? amount(b0 + lane) : 0;
-    const int64_t pre = before + wave_scan64(a) - a;
-    if (lane < ROWS) {
-      int64_t slot = 0;
-      int cnt = 0;
-      if (sp.rows) {                           // slots hg*N + pre .. + n_b - 1
-        slot = static_cast<int64_t>(hg) * sp.N + pre;
-        cnt = static_cast<int>(a);
-      } else if (lane < nrow && a > 0) {       // blocks i0 .. i1 cut the row; slots r + i
-        const int64_t T = sp.S * p.groups;
-        const int64_t start = hg * sp.S + pre;
-        const int i0 = block_of(start, T, sp.nb);
-        const int i1 = block_of(start + a - 1, T, sp.nb);
-        slot = static_cast<int64_t>(hg) * p.batch + b0 + lane + i0;
-        cnt = i1 - i0 + 1;
-      }
-      sh_slot[lane] = slot;
-      sh_cnt[lane] = cnt;
-    }
-  }
   if constexpr (ROWS < 16) {   // rows ROWS..15 of the MFMA A operand stay zero
     for (int i = tid; i < (16 - ROWS) * (kLat / 8); i += kMergeThreads) {
       const int r = ROWS + i / (kLat / 8), c8 = (i % (kLat / 8)) * 8;
@@ -1106,14 +1110,27 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_uv_kernel(const MlaPa
       *reinterpret_cast<uint4*>(&olo[r][c8]) = make_uint4(0, 0, 0, 0);
     }
   }
-  __syncthreads();
-  // per row: M and W over its pieces, lanes striding over the pieces (max and
-  // sum read together, the first 64 pieces' terms kept); wave w takes rows
-  // w, w + 8
+  // per row (wave w takes rows w, w + 8): its pieces' maxima and sums and the
+  // first eight pieces' partials are loaded together; then M, W and the
+  // weighted sum of the partials in ascending piece order (the weights of
+  // the first 64 pieces from the lanes that computed them)
 #pragma unroll
   for (int bb = wave; bb < ROWS; bb += kMergeWaves) {
-    const int cnt = sh_cnt[bb];
-    const int64_t slot = sh_slot[bb];
+    const MlaRowSlots ri = bb < nrow ? p.row_slots[static_cast<int64_t>(hg) * p.batch + b0 + bb]
+                                     : MlaRowSlots{0, 0, 0};
+    const int cnt = ri.cnt;
+    const int64_t slot = ri.slot;
+    const int d0 = lane * 8;
+    float4 v[8][2];
+    auto load_group = [&](int k0) {   // pieces k0 .. k0+7 (the last repeated past cnt)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t srow = (slot + min(k0 + u, cnt - 1)) * kGroup + hl;
+        v[u][0] = *reinterpret_cast<const float4*>(p.seg_out + srow * kLat + d0);
+        v[u][1] = *reinterpret_cast<const float4*>(p.seg_out + srow * kLat + d0 + 4);
+      }
+    };
+    if (cnt > 0) load_group(0);
     const bool mine = lane < cnt;
     const float m0 = mine ? p.seg_max[(slot + lane) * kGroup + hl] : -INFINITY;
     const float l0 = mine ? p.seg_sum[(slot + lane) * kGroup + hl] : 0.0f;
@@ -1121,42 +1138,23 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_uv_kernel(const MlaPa
     for (int k = lane + 64; k < cnt; k += 64) M = fmaxf(M, p.seg_max[(slot + k) * kGroup + hl]);
     M = wave_max(M);
     if (M == -INFINITY) M = 0.0f;   // no piece saw a key: every weight is 0
-    float wk = mine ? l0 * __expf(m0 - M) : 0.0f;
-    if (mine) wts[bb][lane] = wk;
+    const float w_mine = mine ? l0 * __expf(m0 - M) : 0.0f;
+    float wk = w_mine;
     for (int k = lane + 64; k < cnt; k += 64)
       wk += p.seg_sum[(slot + k) * kGroup + hl] * __expf(p.seg_max[(slot + k) * kGroup + hl] - M);
     const float W = wave_sum(wk);
-    if (lane == 0) {
-      sh_m[bb] = M;
-      sh_iw[bb] = W > 0.0f ? 1.0f / W : 0.0f;
-    }
-  }
-  __syncthreads();
-  // o_lat for ROWS sequences x 512 dims: wave w takes rows w, w + 8; lane l
-  // dims 8l .. 8l+8
-#pragma unroll
-  for (int bb = wave; bb < ROWS; bb += kMergeWaves) {
-    const int d0 = lane * 8;
+    const float iw = W > 0.0f ? 1.0f / W : 0.0f;
     float o[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = 0.0f;
-    const int cnt = sh_cnt[bb];
-    const int64_t slot = sh_slot[bb];
-    const float M = sh_m[bb], iw = sh_iw[bb];
     for (int k0 = 0; k0 < cnt; k0 += 8) {
-      float4 v[8][2];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int64_t srow = (slot + min(k0 + u, cnt - 1)) * kGroup + hl;
-        v[u][0] = *reinterpret_cast<const float4*>(p.seg_out + srow * kLat + d0);
-        v[u][1] = *reinterpret_cast<const float4*>(p.seg_out + srow * kLat + d0 + 4);
-      }
+      if (k0 > 0) load_group(k0);
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int k = k0 + u;
         const int64_t srow = (slot + min(k, cnt - 1)) * kGroup + hl;
-        const float w = k < cnt ? (k < kMergeWts ? wts[bb][k]
-                                                 : p.seg_sum[srow] * __expf(p.seg_max[srow] - M)) * iw
+        const float w = k < cnt ? (k < 64 ? __shfl(w_mine, k)
+                                          : p.seg_sum[srow] * __expf(p.seg_max[srow] - M)) * iw
                                 : 0.0f;
         o[0] = fmaf(w, v[u][0].x, o[0]);
         o[1] = fmaf(w, v[u][0].y, o[1]);
@@ -1253,6 +1251,7 @@ int mla_decode_impl(const void* q_nope, const void* q_rope, const void* kv_cache
   p.seg_max = reinterpret_cast<float*>(ws + plan.off_seg_max);
   p.seg_sum = reinterpret_cast<float*>(ws + plan.off_seg_sum);
   p.split_plan = reinterpret_cast<pa::MlaSplit*>(ws + plan.off_split_plan);
+  p.row_slots = reinterpret_cast<pa::MlaRowSlots*>(ws + plan.off_row_slots);
   p.out = static_cast<uint16_t*>(out);
   p.page_stride = cache->page_stride;
   p.token_stride = static_cast<int32_t>(cache->token_stride);

@@ -202,6 +202,7 @@ bool plan_mla(int32_t batch, int32_t num_heads, int32_t max_pages_per_seq, int32
   plan->off_seg_max = o;  o += round_up(slots * kMlaBlockHeads * sizeof(float), 256);
   plan->off_seg_sum = o;  o += round_up(slots * kMlaBlockHeads * sizeof(float), 256);
   plan->off_split_plan = o;  o += 256;   // the split plan, computed once per call
+  plan->off_row_slots = o;   o += round_up(static_cast<size_t>(plan->groups) * batch * 16, 256);   // per row: first slot, pieces
   plan->bytes = o;
   return true;
 }

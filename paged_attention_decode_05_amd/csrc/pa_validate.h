@@ -96,7 +96,8 @@ struct MlaPlan {
   int32_t groups = 0;        // ceil(num_heads / 64)
   int32_t max_blocks = 0;    // split-kernel blocks launched, one partial slot each
   size_t off_qhi = 0, off_qmid = 0, off_qlo = 0;
-  size_t off_seg_out = 0, off_seg_max = 0, off_seg_sum = 0, off_split_plan = 0, bytes = 0;
+  size_t off_seg_out = 0, off_seg_max = 0, off_seg_sum = 0, off_split_plan = 0, off_row_slots = 0;
+  size_t bytes = 0;
 };
 bool plan_mla(int32_t batch, int32_t num_heads, int32_t max_pages_per_seq, int32_t page_size,
               int32_t partition_size, MlaPlan* plan);
