@@ -67,6 +67,19 @@ def test_partition_sizes(oracle, partition_size):
           f"mla P={partition_size}")
 
 
+@pytest.mark.parametrize("partition_size", [0, 128])
+def test_batch_past_64(oracle, partition_size):
+    """100 sequences of seeded lengths 0 .. 400: the split's plan, row search
+    and row-slot list go past the first 64 sequences (whose lengths a wave
+    holds in registers) into the ones read from memory."""
+    rng = np.random.default_rng(9800)
+    ctx = tuple(int(x) for x in rng.integers(0, 401, size=100))
+    case = _case(ctx, heads=16, page_size=16, seed=9801)
+    ref, _, _ = oracle.mla(case)
+    _gate(run_mla(case.to("cuda"), partition_size=partition_size), ref,
+          f"mla batch=100 P={partition_size}")
+
+
 def test_empty_context_gives_zero(oracle):
     case = _case((0, 10, 0, 70), heads=16, page_size=16, seed=9400)
     ref, _, _ = oracle.mla(case)

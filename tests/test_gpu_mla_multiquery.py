@@ -11,6 +11,7 @@ split in which some queries see no key.
 """
 from __future__ import annotations
 
+import numpy as np
 import pytest
 import torch
 
@@ -122,6 +123,16 @@ def test_one_query_equals_decode(dt):
     for causal in (True, False):
         got = run_mla_multi(m, causal)[:, 0]
         assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), causal
+
+
+def test_verify_batch_past_64(oracle):
+    """70 sequences, 2 causal queries of 64 heads (two head groups): the key
+    line cut of the verify step with sequences past the first 64."""
+    rng = np.random.default_rng(9810)
+    ctx = tuple(int(x) for x in rng.integers(1, 300, size=70))
+    case = _case(ctx, 2, 64, 16, 9811)
+    ref, _ = oracle.mla_multi(case, True)
+    _gate(run_mla_multi(case.to("cuda"), True), ref, "mla verify batch=70")
 
 
 def test_run_to_run_and_workspace_contents():
