@@ -86,7 +86,7 @@ struct MlaParams {
   uint16_t* q_hi;          // q_abs | q_rope, first terms (the split kernel's operand order)
   uint16_t* q_mid;         // second and third terms of q_abs
   uint16_t* q_lo;
-  float* seg_out;          // [slots][64][512] normalised partial o_lat
+  float* seg_out;          // [slots][64][512] partial o_lat, unnormalised: sum of P V
   float* seg_max;          // [slots][64] natural-log-domain reference max
   float* seg_sum;          // [slots][64] sum of exp(s - max)
   MlaSplit* split_plan;    // the split plan, written by the absorb kernel
@@ -497,7 +497,8 @@ struct MlaSplitLds {
 };
 
 // Attention of the heads of group hg of sequence b over keys [begin, end);
-// writes the normalised partial, its max and its sum to slot.
+// writes the unnormalised partial (sum over the keys of P V, P = e^(s - max)),
+// its max and its sum to slot.
 //
 // Per 32-key tile t0 .. t0+31, wave (pair, half):
 //   scores   S^T[32 keys x 32 heads] over the wave's dims on
@@ -951,14 +952,14 @@ __device__ __forceinline__ void mla_segment(const MlaParams& p, int b, int n, in
   // i is head 8(i/4) + 4hh + i%4
   const float l_tot = l_sum + xhalf(l_sum);
   const int64_t srow = slot * kGroup + pair * kPairHeads;
+  // the accumulators leave as they are (the stores take them from the
+  // AGPRs); the merge weighs each piece by e^(m - M) / W
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int hr = 8 * (i >> 2) + 4 * hh + (i & 3);
-    const float lr = __shfl(l_tot, hr);
-    const float inv = (!CAUSAL || lr > 0.0f) ? 1.0f / lr : 0.0f;
     float* dst = p.seg_out + (srow + hr) * kLat + kHalfLat * half + c;
 #pragma unroll
-    for (int dt = 0; dt < kDimTiles; ++dt) dst[32 * dt] = acc[dt][i] * inv;
+    for (int dt = 0; dt < kDimTiles; ++dt) dst[32 * dt] = acc[dt][i];
   }
   if (half == 0 && hh == 0) {
     p.seg_max[srow + c] = m_ref * kLn2;
@@ -1067,8 +1068,9 @@ void mla_split_kernel(const MlaParams p) {
 // absorb kernel's plan block listed for it, in ascending key order.  The max
 // M and the total W = sum l_i e^(m_i - M) of a row are wave reductions over
 // its pieces, loaded together with the first eight pieces' partials; o_lat
-// is the (l_i e^(m_i - M) / W)-weighted sum of the pieces in ascending i
-// (eight pieces' loads in flight), written to LDS as three bf16 terms; then
+// is the (e^(m_i - M) / W)-weighted sum of the pieces' unnormalised partials
+// in ascending i (eight pieces' loads in flight), written to LDS as three
+// bf16 terms; then
 // out[b][dv] = sum_j o_lat[b][j] W_UV[h][dv][j] on MFMA with A = o_lat (rows
 // past ROWS zero) and B = W_UV rows, whose 8 consecutive latent dims per lane
 // are contiguous in memory; wave w computes dv tile w.  The W_UV loads are
@@ -1138,8 +1140,8 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_uv_kernel(const MlaPa
     for (int k = lane + 64; k < cnt; k += 64) M = fmaxf(M, p.seg_max[(slot + k) * kGroup + hl]);
     M = wave_max(M);
     if (M == -INFINITY) M = 0.0f;   // no piece saw a key: every weight is 0
-    const float w_mine = mine ? l0 * __expf(m0 - M) : 0.0f;
-    float wk = w_mine;
+    const float e_mine = mine ? __expf(m0 - M) : 0.0f;   // a piece's weight before 1/W
+    float wk = l0 * e_mine;
     for (int k = lane + 64; k < cnt; k += 64)
       wk += p.seg_sum[(slot + k) * kGroup + hl] * __expf(p.seg_max[(slot + k) * kGroup + hl] - M);
     const float W = wave_sum(wk);
@@ -1153,8 +1155,7 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_uv_kernel(const MlaPa
       for (int u = 0; u < 8; ++u) {
         const int k = k0 + u;
         const int64_t srow = (slot + min(k, cnt - 1)) * kGroup + hl;
-        const float w = k < cnt ? (k < 64 ? __shfl(w_mine, k)
-                                          : p.seg_sum[srow] * __expf(p.seg_max[srow] - M)) * iw
+        const float w = k < cnt ? (k < 64 ? __shfl(e_mine, k) : __expf(p.seg_max[srow] - M)) * iw
                                 : 0.0f;
         o[0] = fmaf(w, v[u][0].x, o[0]);
         o[1] = fmaf(w, v[u][0].y, o[1]);
