@@ -211,6 +211,7 @@ int decode_impl(const void* q, const void* k_pool, const void* v_pool, const pa_
     nbmax = plan.rows < (1 << 20) ? plan.rows : (1 << 20);   // one block per row
   }
   bl.min_units = pa::kMinUnitsPerBlock;
+  bl.row_cost = pa::kRowCostUnits;
   bl.rows = plan.rows;
   bl.batch = batch;
   bl.q_heads = num_q_heads;

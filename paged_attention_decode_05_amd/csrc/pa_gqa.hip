@@ -1059,21 +1059,30 @@ __device__ __forceinline__ int64_t seq_len(const int32_t* ctx, int b, int window
 
 
 // Keys (per KV head) of all sequences: sum_b len_b.  Called by a whole wave.
-__device__ __forceinline__ int64_t total_keys(const int32_t* ctx, int batch, int window) {
+// Units of one row of sequence b on the key line: its keys, after `cost`
+// units that stand for the row's prologue (none for a row with no key).
+__device__ __forceinline__ int64_t row_span(const int32_t* ctx, int b, int window, int cost) {
+  const int64_t len = seq_len(ctx, b, window);
+  return len > 0 ? len + cost : 0;
+}
+
+__device__ __forceinline__ int64_t total_units(const int32_t* ctx, int batch, int window, int cost) {
   const int lane = threadIdx.x & 63;
   int64_t s = 0;
-  for (int b0 = 0; b0 < batch; b0 += 64) s += (b0 + lane < batch) ? seq_len(ctx, b0 + lane, window) : 0;
+  for (int b0 = 0; b0 < batch; b0 += 64)
+    s += (b0 + lane < batch) ? row_span(ctx, b0 + lane, window, cost) : 0;
   return wave_sum64(s);
 }
 
-// Sequence b that holds unit x (0 <= x < T) and the keys before it, pre_b =
-// sum_{b' < b} len_b'.  Called by a whole wave; all lanes get the result.
-__device__ __forceinline__ void locate_unit(const int32_t* ctx, int batch, int window, int hkv,
-                                            int64_t x, int& b_out, int64_t& pre_out) {
+// Sequence b that holds unit x (0 <= x < T) and the units of one row before
+// it, pre_b = sum_{b' < b} span_b'.  Called by a whole wave; all lanes get
+// the result.
+__device__ __forceinline__ void locate_unit(const int32_t* ctx, int batch, int window, int cost,
+                                            int hkv, int64_t x, int& b_out, int64_t& pre_out) {
   const int lane = threadIdx.x & 63;
   int64_t base = 0;
   for (int b0 = 0; b0 < batch; b0 += 64) {
-    const int64_t len = (b0 + lane < batch) ? seq_len(ctx, b0 + lane, window) : 0;
+    const int64_t len = (b0 + lane < batch) ? row_span(ctx, b0 + lane, window, cost) : 0;
     const int64_t incl = wave_scan64(len);
     const uint64_t hit = __ballot(hkv * (base + incl) > x);
     if (hit) {
@@ -1124,13 +1133,14 @@ void balanced_split_kernel(const SplitParams p, const BalancedLayout bl) {
     return;
   }
   if (threadIdx.x < 64) {
-    const int64_t keys = total_keys(p.context_lens, bl.batch, p.reach);
-    const int64_t T = keys * hkv;
+    const int64_t T = total_units(p.context_lens, bl.batch, p.reach, bl.row_cost) * hkv;
     int b = 0;
     int64_t pre = 0;
     if (T > 0) {
       const int nb = used_blocks(T, gridDim.x, bl.min_units);
-      if (i < nb) locate_unit(p.context_lens, bl.batch, p.reach, hkv, static_cast<int64_t>(i) * T / nb, b, pre);
+      if (i < nb)
+        locate_unit(p.context_lens, bl.batch, p.reach, bl.row_cost, hkv,
+                    static_cast<int64_t>(i) * T / nb, b, pre);
     }
     if (threadIdx.x == 0) {
       sh_total = T;
@@ -1146,30 +1156,36 @@ void balanced_split_kernel(const SplitParams p, const BalancedLayout bl) {
   const int64_t s0 = static_cast<int64_t>(i) * T / nb;
   const int64_t s1 = static_cast<int64_t>(i + 1) * T / nb;
   int b = sh_b;
-  int64_t pre = sh_pre;                                  // keys per KV head before sequence b
+  int64_t pre = sh_pre;                                  // units of one row before sequence b
   const int gq = p.gq;
+  const int cost = bl.row_cost;
   while (b < bl.batch) {
     const int n = p.context_lens[b];
     const int lo = p.reach > 0 ? max(0, n - p.reach) : 0;
     const int64_t len = n - lo;
+    const int64_t span = len > 0 ? len + cost : 0;
     const int64_t seq0 = pre * hkv;                      // first unit of sequence b
     if (seq0 >= s1) break;
     for (int gk = 0; gk < hkv && len > 0; ++gk) {
-      const int64_t off = seq0 + static_cast<int64_t>(gk) * len;   // first unit of row (b, gk)
-      if (off >= s1) break;
-      const int64_t x0 = s0 > off ? s0 : off;
-      const int64_t x1 = (s1 < off + len) ? s1 : off + len;
+      // row (b, gk): units off .. off + cost stand for its prologue, its keys
+      // lo .. n are units k0 = off + cost .. k0 + len; a block whose share
+      // holds none of its keys leaves it alone
+      const int64_t off = seq0 + static_cast<int64_t>(gk) * span;
+      const int64_t k0 = off + cost;
+      if (k0 >= s1) break;
+      const int64_t x0 = s0 > k0 ? s0 : k0;
+      const int64_t x1 = (s1 < k0 + len) ? s1 : k0 + len;
       if (x1 <= x0) continue;
-      const int begin = lo + static_cast<int>(x0 - off);
-      const int end = lo + static_cast<int>(x1 - off);
-      // a row that lies inside this block's share gets its final output here
-      const bool whole = off >= s0 && off + len <= s1;
+      const int begin = lo + static_cast<int>(x0 - k0);
+      const int end = lo + static_cast<int>(x1 - k0);
+      // a row whose keys lie inside this block's share gets its final output here
+      const bool whole = k0 >= s0 && k0 + len <= s1;
       const int64_t r = static_cast<int64_t>(b) * hkv + gk;
       const int64_t slot = r + i;
       const int64_t h0 = static_cast<int64_t>(b) * p.num_q_heads + static_cast<int64_t>(gk) * gq;
       // key of this row at which the block has passed num/den of its units
       auto key_at = [&](int num, int den) {
-        const int64_t t = lo + (s0 + (s1 - s0) * num / den - off);
+        const int64_t t = lo + (s0 + (s1 - s0) * num / den - k0);
         return static_cast<int>(t < -(1 << 30) ? -(1 << 30) : t > (1 << 30) ? (1 << 30) : t);
       };
       const PrioKeys pk{true, key_at(1, 2), key_at(3, 4), key_at(9, 10)};
@@ -1179,10 +1195,10 @@ void balanced_split_kernel(const SplitParams p, const BalancedLayout bl) {
                                  (whole && bl.lse) ? bl.lse + h0 : nullptr, pk);
       // the block holding a row's first piece records where its pieces are:
       // slots r + i .. r + i + count - 1 (count 1: written here already)
-      if (x0 == off && threadIdx.x == 0)
-        bl.row_info[r] = (i << 12) | (block_of(off + len - 1, T, nb) - i + 1);
+      if (x0 == k0 && threadIdx.x == 0)
+        bl.row_info[r] = (i << 12) | (block_of(k0 + len - 1, T, nb) - i + 1);
     }
-    pre += len;
+    pre += span;
     ++b;
   }
 }

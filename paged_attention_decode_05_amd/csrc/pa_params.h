@@ -72,6 +72,7 @@ struct BalancedLayout {
   // the pieces sitting in slots r + first .. r + first + pieces - 1.
   int32_t* row_info;     // [rows]
   int64_t min_units;     // a block owns at least this many units (keys of one KV head)
+  int32_t row_cost;      // units charged to a row's start (its prologue), before its keys
   int32_t rows;          // batch * num_kv_heads
   int32_t batch;
   int32_t q_heads;       // Hq (out rows are [b][s][Hq])

@@ -57,6 +57,9 @@ constexpr int32_t kMaxBalancedBlocks = 2048;
 // 64, 17.8 at 32, 21.5 at 16 (more pieces to merge); larger calls fill every
 // block well above it.
 constexpr int64_t kMinUnitsPerBlock = 32;
+// Units of the balanced key line that stand for a row's prologue, charged
+// before its keys, so a block whose share starts several rows gets fewer keys.
+constexpr int32_t kRowCostUnits = 128;
 
 struct DecodePlan {
   int32_t rows = 0;          // batch * num_kv_heads
