@@ -274,12 +274,16 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(const MlaParams p) {
 // piece more than kMlaRowSlack tiles above the mean), as in a multi-query
 // verify whose many head groups leave two or three blocks per row.
 constexpr int kMlaRowSlack = 3;
+// Key line: units before each row's keys that stand for its prologue (q
+// terms, the tile pipeline's refill, one more partial), so a block whose
+// range starts several rows gets fewer keys.
+constexpr int kMlaRowCost = 64;
 
 struct MlaSplit {
   bool rows;   // pieces of rows, else the key line
   int L;       // pieces of rows: tiles per piece, at most
   int N;       // pieces of rows: blocks per head group (0: no key anywhere)
-  int64_t S;   // key line: keys per group (sum of the context lengths)
+  int64_t S;   // key line: units per group (each row's keys after kMlaRowCost units)
   int nb;      // key line: blocks used
 };
 
@@ -293,7 +297,8 @@ __device__ __forceinline__ MlaSplit mla_plan(const int32_t* ctx, int batch, int 
   int tmax = 0;
   for (int b0 = 0; b0 < batch; b0 += 64) {
     const int t = (b0 + lane < batch) ? mla_tiles(ctx, b0 + lane) : 0;
-    keys += (b0 + lane < batch) ? ctx[b0 + lane] : 0;
+    const int n = (b0 + lane < batch) ? ctx[b0 + lane] : 0;
+    keys += n > 0 ? n + kMlaRowCost : 0;   // units of the key line
     tiles += t;
     tmax = max(tmax, t);
   }
@@ -352,7 +357,8 @@ __device__ void mla_write_plan(const MlaParams& p) {
   for (int b0 = 0; b0 < p.batch; b0 += 64) {
     const int b = b0 + lane;
     const int n = b < p.batch ? p.context_lens[b] : 0;
-    const int64_t a = sp.rows ? ((n + 31) / 32 + sp.L - 1) / sp.L : n;
+    // pieces of the row, or its units on the key line
+    const int64_t a = sp.rows ? ((n + 31) / 32 + sp.L - 1) / sp.L : (n > 0 ? n + kMlaRowCost : 0);
     const int64_t pre = before + wave_scan64(a) - a;
     before += wave_sum64(a);
     if (b < p.batch) {
@@ -361,11 +367,11 @@ __device__ void mla_write_plan(const MlaParams& p) {
         if (sp.rows) {
           r.slot = static_cast<int64_t>(hg) * sp.N + pre;
           r.cnt = static_cast<int32_t>(a);
-        } else if (a > 0) {
+        } else if (n > 0) {
           const int64_t T = sp.S * p.groups;
-          const int64_t start = hg * sp.S + pre;
+          const int64_t start = hg * sp.S + pre + kMlaRowCost;   // the row's first key
           const int i0 = block_of(start, T, sp.nb);
-          const int i1 = block_of(start + a - 1, T, sp.nb);
+          const int i1 = block_of(start + n - 1, T, sp.nb);
           r.slot = static_cast<int64_t>(hg) * p.batch + b + i0;
           r.cnt = i1 - i0 + 1;
         }
@@ -391,7 +397,8 @@ __device__ __forceinline__ void mla_locate(const int32_t* ctx, int batch, int64_
   const int lane = threadIdx.x & 63;
   int64_t base = 0;
   for (int b0 = 0; b0 < batch; b0 += 64) {
-    const int64_t len = b0 == 0 ? c_first : ((b0 + lane < batch) ? ctx[b0 + lane] : 0);
+    const int64_t n = b0 == 0 ? c_first : ((b0 + lane < batch) ? ctx[b0 + lane] : 0);
+    const int64_t len = n > 0 ? n + kMlaRowCost : 0;   // the row's units
     const int64_t incl = wave_scan64(len);
     const uint64_t hit = __ballot(base + incl > y);
     if (hit) {
@@ -1043,14 +1050,15 @@ void mla_split_kernel(const MlaParams p) {
       u = u1;
     } else {                                  // the key line, row by row
       const int64_t row_start = hg * S + pre;
-      begin = static_cast<int>(u - row_start);
-      end = static_cast<int>(min(u1 - row_start, static_cast<int64_t>(n)));
+      const int64_t k0 = row_start + (n > 0 ? kMlaRowCost : 0);   // the row's first key
+      begin = static_cast<int>(max(u, k0) - k0);
+      end = static_cast<int>(min(u1 - k0, static_cast<int64_t>(n)));
       slot = static_cast<int64_t>(hg) * p.batch + b + i;
-      u = row_start + n;
+      u = k0 + n;
     }
     if (end > begin) mla_segment<F8, CAUSAL>(p, b, n, hg, begin, end, slot, sm);
     if (!rows) {
-      pre += n;
+      pre += n > 0 ? n + kMlaRowCost : 0;
       if (++b == p.batch) {
         b = 0;
         pre = 0;
