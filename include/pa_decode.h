@@ -147,9 +147,10 @@ PA_API int pa_merge_lse(const float* part_out, const float* part_max,
  * pa_merge_lse define, with a balanced split instead of fixed partitions.
  *
  * The attended keys of the whole batch, counted once per KV head (rows
- * (b, kv head) laid end to end), are cut into equal contiguous ranges, one
- * per workgroup, so every workgroup reads the same number of K/V bytes
- * whatever the length mix [vllm.cpp kernel matrix, row
+ * (b, kv head) laid end to end, each preceded by a fixed number of units
+ * that stand for the cost of starting it), are cut into equal contiguous
+ * ranges, one per workgroup, so every workgroup has the same work whatever
+ * the length mix [vllm.cpp kernel matrix, row
  * KERNEL-ATTN-MLA-SPARSE, W4: split-KV with a fixed, ordered merge].  A row
  * that one range covers is written directly; a row cut by range boundaries
  * gets one partial per piece, merged in ascending order as in pa_merge_lse.
@@ -320,7 +321,8 @@ PA_API int32_t pa_decode_partition_size(int32_t batch, int32_t num_q_heads,
  * from the context lengths alone: every row into its own near-equal pieces,
  * the fewest tiles per piece that fit the grid (at most partition_size keys
  * each when that is given), or, when rows are too few for even pieces, the
- * keys of all rows laid end to end and cut into equal contiguous ranges (the
+ * keys of all rows laid end to end (each after a fixed number of units for
+ * the cost of starting it) and cut into equal contiguous ranges (the
  * library's choice only; a grid fixed by the shapes and the build rather
  * than the device).  The pieces of a row are merged by log-sum-exp in
  * ascending order; an empty context gives 0.
