@@ -381,14 +381,6 @@ __device__ void mla_write_plan(const MlaParams& p) {
   }
 }
 
-// Sum of the context lengths.  Called by a whole wave.
-__device__ __forceinline__ int64_t mla_total(const int32_t* ctx, int batch) {
-  const int lane = threadIdx.x & 63;
-  int64_t s = 0;
-  for (int b0 = 0; b0 < batch; b0 += 64) s += (b0 + lane < batch) ? ctx[b0 + lane] : 0;
-  return wave_sum64(s);
-}
-
 // Sequence b holding key y (0 <= y < S) of a group's key line, and the keys
 // before it.  Called by a whole wave.
 // c_first: this lane's context length among the first 64 (0 past the batch).
