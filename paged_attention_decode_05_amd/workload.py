@@ -451,8 +451,9 @@ def mla(poison: bool = True, seed: int = SEED_BASE + 5) -> MlaCase:
                          seed=seed, poison=poison, name="mla")
 
 
-def mla_fp8(poison: bool = True, seed: int = SEED_BASE + 8) -> MlaCase:
-    """The mla shape over an FP8 latent cache."""
+def mla_fp8(poison: bool = True, seed: int = SEED_BASE + 5) -> MlaCase:
+    """The mla workload (same seed: the same context lengths, q, weights and
+    block tables) over an FP8 latent cache."""
     return make_mla_case(ctx_draw=(1024, 8192), batch=16, num_heads=128, page_size=64,
                          seed=seed, poison=poison, name="mla_fp8", cache_dtype="fp8")
 
