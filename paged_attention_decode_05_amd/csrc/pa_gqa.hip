@@ -1001,13 +1001,84 @@ __device__ __forceinline__ void attend_range(const SplitParams& p, int b, int gk
     attend_range_valu<D, G, NW>(p, b, gk, begin, end, out, mx, sm, hstride, final_out, final_lse);
 }
 
-// Fixed partitions: block (j, gk, b) handles keys [lo + j*P, lo + (j+1)*P).
+// Called by a whole wave, with count(b) items in each of the hkv rows of
+// sequence b: the sum of count(b) over the sequences, and the sequence
+// holding item x of the rows laid end to end (with the items of one row
+// before that sequence).
+template <typename F>
+__device__ __forceinline__ int64_t wave_items(int batch, F count) {
+  const int lane = threadIdx.x & 63;
+  int64_t s = 0;
+  for (int b0 = 0; b0 < batch; b0 += 64) s += (b0 + lane < batch) ? count(b0 + lane) : 0;
+  return wave_sum64(s);
+}
+
+template <typename F>
+__device__ __forceinline__ void wave_find_item(int batch, int hkv, int64_t x, F count, int& b_out,
+                                               int64_t& pre_out) {
+  const int lane = threadIdx.x & 63;
+  int64_t base = 0;
+  for (int b0 = 0; b0 < batch; b0 += 64) {
+    const int64_t len = (b0 + lane < batch) ? count(b0 + lane) : 0;
+    const int64_t incl = wave_scan64(len);
+    const uint64_t hit = __ballot(hkv * (base + incl) > x);
+    if (hit) {
+      const int l = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+      b_out = b0 + l;
+      pre_out = base + __shfl(incl, l) - __shfl(len, l);
+      return;
+    }
+    base += __shfl(incl, 63);
+  }
+  b_out = batch;
+  pre_out = base;
+}
+
+// Fixed partitions: one block per (partition j, KV head gk, sequence b),
+// handling keys [lo + j*P, lo + (j+1)*P).  Blocks are dispatched in the order
+// of the 1-D grid: block i takes the i-th partition with a key, in row-major
+// order over (b, gk) and ascending j, or, past the last of those, the empty
+// partitions in the same order.  So every partition with keys starts before
+// any empty one, and the empty ones fill the slots that the last partitions
+// with keys leave idle.
 template <int D, int G>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kMinWaves<D, G>)))
-void split_kernel(const SplitParams p) {
-  const int j = blockIdx.x;
-  const int gk = blockIdx.y;
-  const int b = blockIdx.z;
+void split_kernel(const SplitParams p, int batch) {
+  __shared__ int sh_item[3];
+  if (threadIdx.x < 64) {
+    const int hkv = p.kv_heads;
+    const int P = p.partition_size;
+    auto live_of = [&](int bb) -> int64_t {   // partitions j < max_parts with a key
+      const int nn = p.context_lens[bb];
+      const int64_t len = nn - (p.window > 0 ? max(0, nn - p.window) : 0);
+      return len > 0 ? min(static_cast<int64_t>(p.max_parts), (len + P - 1) / P) : 0;
+    };
+    auto dead_of = [&](int bb) -> int64_t { return p.max_parts - live_of(bb); };
+    const int64_t W = wave_items(batch, live_of) * hkv;
+    const int64_t i = blockIdx.x;
+    int bb;
+    int64_t pre, off, cnt, first;
+    if (i < W) {
+      wave_find_item(batch, hkv, i, live_of, bb, pre);
+      cnt = live_of(bb);
+      off = i - pre * hkv;
+      first = 0;
+    } else {
+      wave_find_item(batch, hkv, i - W, dead_of, bb, pre);
+      cnt = dead_of(bb);
+      off = i - W - pre * hkv;
+      first = live_of(bb);
+    }
+    if (threadIdx.x == 0) {
+      sh_item[0] = static_cast<int>(first + off % cnt);
+      sh_item[1] = static_cast<int>(off / cnt);
+      sh_item[2] = bb;
+    }
+  }
+  __syncthreads();
+  const int j = sh_item[0];
+  const int gk = sh_item[1];
+  const int b = sh_item[2];
   const int n = p.context_lens[b];
   const int lo = p.window > 0 ? max(0, n - p.window) : 0;
   const int64_t begin64 = static_cast<int64_t>(lo) + static_cast<int64_t>(j) * p.partition_size;
@@ -1382,8 +1453,8 @@ __global__ __launch_bounds__(kBlock) void merge_kernel(const MergeParams p) {
 template <int D, int G>
 static hipError_t launch_split_dg(const SplitParams& p, int batch, int num_kv_heads,
                                   hipStream_t stream) {
-  dim3 grid(p.max_parts, num_kv_heads, batch);
-  launch_profiled(split_kernel<D, G>, grid, dim3(kBlock), 0, stream, p);
+  const dim3 grid(static_cast<uint32_t>(p.max_parts) * num_kv_heads * batch);
+  launch_profiled(split_kernel<D, G>, grid, dim3(kBlock), 0, stream, p, batch);
   return hipGetLastError();
 }
 
