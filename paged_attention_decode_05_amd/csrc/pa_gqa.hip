@@ -1365,11 +1365,19 @@ struct FixedSlots {      // partition j at row*max_parts + j
 // ascending k within each of the block's partition groups, the groups added
 // in fixed order.  `stride` is the distance between consecutive partials in
 // elements of m/l (times D for o).
+// One block merges dims [slice*D/DS, (slice+1)*D/DS) of a row, DS = D/32
+// blocks per row: TPR = 8 threads cover the slice (4 dims each), and the 32
+// groups of them take partitions grp, grp + 32, ... in ascending order, the
+// groups' sums then added in ascending group order.
+template <int D>
+constexpr int kMergeSlices = D / 32;
+
 template <int D>
 __device__ __forceinline__ void merge_row(const float* pm, const float* pl, const float* po,
-                                          int64_t stride, int count, uint16_t* out, float* lse) {
-  constexpr int TPR = D / 4;                  // threads per row (float4 each)
-  constexpr int NGRP = kBlock / TPR;          // partition groups per block
+                                          int64_t stride, int count, uint16_t* out, float* lse,
+                                          int slice) {
+  constexpr int TPR = D / 4 / kMergeSlices<D>;   // threads per row slice (float4 each)
+  constexpr int NGRP = kBlock / TPR;             // partition groups per block
   __shared__ float red[kWaves];
   __shared__ float4 part[NGRP][TPR];
 
@@ -1382,8 +1390,8 @@ __device__ __forceinline__ void merge_row(const float* pm, const float* pl, cons
   __syncthreads();
 
   if (count == 0 || M == -INFINITY) {
-    for (int d = threadIdx.x; d < D; d += kBlock) out[d] = 0;
-    if (lse && threadIdx.x == 0) *lse = -INFINITY;
+    for (int d = threadIdx.x; d < D / kMergeSlices<D>; d += kBlock) out[slice * (D / kMergeSlices<D>) + d] = 0;
+    if (lse && slice == 0 && threadIdx.x == 0) *lse = -INFINITY;
     return;
   }
   float W = 0.0f;
@@ -1398,26 +1406,38 @@ __device__ __forceinline__ void merge_row(const float* pm, const float* pl, cons
   W = (red[0] + red[1]) + (red[2] + red[3]);
 
   const int grp = threadIdx.x / TPR;
-  const int d4 = threadIdx.x % TPR;
+  const int d4 = slice * TPR + threadIdx.x % TPR;   // float4 of the row
+  // partitions grp, grp + NGRP, ... in ascending order, U of them loaded
+  // together (a partition without a key has weight 0 and o = 0)
+  constexpr int U = 8;
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int jj = grp; jj < count; jj += NGRP) {
-    const float mj = pm[jj * stride];
-    const float lj = pl[jj * stride];
-    if (mj == -INFINITY || lj == 0.0f) continue;
-    const float w = lj * __expf(mj - M) / W;
-    const float4 o = reinterpret_cast<const float4*>(po + jj * stride * D)[d4];
-    a.x = fmaf(w, o.x, a.x);
-    a.y = fmaf(w, o.y, a.y);
-    a.z = fmaf(w, o.z, a.z);
-    a.w = fmaf(w, o.w, a.w);
+  for (int j0 = grp; j0 < count; j0 += U * NGRP) {
+    float w[U];
+    float4 o[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int jj = j0 + u * NGRP;
+      const bool in = jj < count;
+      const float mj = in ? pm[jj * stride] : -INFINITY;
+      const float lj = in ? pl[jj * stride] : 0.0f;
+      o[u] = in ? reinterpret_cast<const float4*>(po + jj * stride * D)[d4] : make_float4(0.f, 0.f, 0.f, 0.f);
+      w[u] = (mj == -INFINITY || lj == 0.0f) ? 0.0f : lj * __expf(mj - M) / W;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      a.x = fmaf(w[u], o[u].x, a.x);
+      a.y = fmaf(w[u], o[u].y, a.y);
+      a.z = fmaf(w[u], o[u].z, a.z);
+      a.w = fmaf(w[u], o[u].w, a.w);
+    }
   }
-  part[grp][d4] = a;
+  part[grp][threadIdx.x % TPR] = a;
   __syncthreads();
   if (grp == 0) {
-    float4 t = part[0][d4];
+    float4 t = part[0][threadIdx.x];
 #pragma unroll
     for (int q = 1; q < NGRP; ++q) {
-      const float4 u = part[q][d4];
+      const float4 u = part[q][threadIdx.x];
       t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
     }
     uint2 packed;
@@ -1425,7 +1445,7 @@ __device__ __forceinline__ void merge_row(const float* pm, const float* pl, cons
     packed.y = static_cast<uint32_t>(f32_to_bf16_rne(t.z)) | (static_cast<uint32_t>(f32_to_bf16_rne(t.w)) << 16);
     reinterpret_cast<uint2*>(out)[d4] = packed;
   }
-  if (lse && threadIdx.x == 0) *lse = M + __logf(W);
+  if (lse && slice == 0 && threadIdx.x == 0) *lse = M + __logf(W);
 }
 
 // Fixed partitions: live partitions j < ceil((ctx - lo) / P).
@@ -1445,7 +1465,7 @@ __global__ __launch_bounds__(kBlock) void merge_kernel(const MergeParams p) {
   const int64_t row = static_cast<int64_t>(b) * p.num_q_heads + h;
   merge_row<D>(p.part_max + row * p.max_parts, p.part_sum + row * p.max_parts,
                p.part_out + row * p.max_parts * D, 1, live, p.out + row * D,
-               p.lse ? p.lse + row : nullptr);
+               p.lse ? p.lse + row : nullptr, blockIdx.z);
 }
 
 // ---- launchers -----------------------------------------------------------------
@@ -1508,7 +1528,7 @@ hipError_t launch_split(const SplitParams& p, int head_dim, int group, int batch
 }
 
 hipError_t launch_merge(const MergeParams& p, int head_dim, int batch, hipStream_t stream) {
-  dim3 grid(p.num_q_heads, batch);
+  dim3 grid(p.num_q_heads, batch, head_dim / 32);   // kMergeSlices<head_dim>
   if (head_dim == 64) {
     launch_profiled(merge_kernel<64>, grid, dim3(kBlock), 0, stream, p);
   } else if (head_dim == 128) {
