@@ -119,10 +119,13 @@ PA_API int pa_decode_splitkv(const void* q, const void* k_pool, const void* v_po
 /* ---------------------------------------------------------------------------
  * pa_merge_lse -- stage 2: log-sum-exp merge of split partials.
  *
- * For each (b, h), over the live partitions j < ceil((ctx - lo) / P) in
- * ascending j:  M = max_j m_j,  w_j = l_j exp(m_j - M),  W = sum_j w_j,
+ * For each (b, h), over the live partitions j < ceil((ctx - lo) / P):
+ *   M = max_j m_j,  w_j = l_j exp(m_j - M),  W = sum_j w_j,
  *   out[b][h][:] = bf16( sum_j (w_j / W) part_out[j][:] ),
  *   lse_out[b][h] = M + ln W.
+ * The weighted sum is taken in one fixed order (for each g < 32 the
+ * partitions j = g, g + 32, ... in ascending j, then the 32 group sums in
+ * ascending g), so the result is the same on every call.
  * Empty partitions (m_j = -inf) weigh nothing; no live partition, or all
  * empty, gives out = 0 and lse = -inf [vllm.cpp kernel matrix, row
  * KERNEL-ATTN-MLA-SPARSE, W5: merge of attention states with both -inf edge
