@@ -330,7 +330,9 @@ PA_API int32_t pa_decode_partition_size(int32_t batch, int32_t num_q_heads,
  * than the device).  The pieces of a row are merged by log-sum-exp in
  * ascending order; an empty context gives 0.
  * Deterministic run to run, the same on every gfx950 device, and
- * independent of page placement.
+ * independent of page placement.  The pieces are cut from the context
+ * lengths of the whole batch, so a row's result may differ in the last bits
+ * when other sequences' lengths change.
  *
  * q_nope [batch][num_heads][128] bf16; q_rope [batch][num_heads][64] bf16;
  * kv_cache: pool described by *cache (num_kv_heads 1, head_dim 576,
