@@ -155,6 +155,33 @@ def test_splitkv_partials_match_oracle(oracle, partition_size, window):
     _lse_ok(lse, ref_lse)
 
 
+@pytest.mark.parametrize("partition_size,window", [(64, 0), (100, 0), (48, 90)])
+def test_splitkv_batch_past_64(oracle, partition_size, window):
+    """More than 64 sequences, some with no key: the fixed grid's blocks find
+    their partition with a scan of the context lengths 64 sequences at a time,
+    partitions with keys first, then the empty ones."""
+    rng = np.random.default_rng(9900 + partition_size + window)
+    ctx = rng.integers(0, 700, size=100)
+    ctx[rng.choice(100, size=9, replace=False)] = 0
+    case = wl.make_gqa_case(context_lens=tuple(int(c) for c in ctx), num_q_heads=8,
+                            num_kv_heads=2, head_dim=128, page_size=32,
+                            seed=9950 + partition_size, window=window)
+    dc = dev_case(case)
+    mp = max_parts_for(dc, partition_size)
+    po, pm, ps = run_splitkv(dc, partition_size, mp)
+    rpo, rpm, rps = oracle.partials(case, partition_size, mp)
+    ok, err = close_f32(pm.cpu().numpy(), rpm, rtol=2e-6, atol=1e-5)
+    assert ok, ("max", err)
+    ok, err = close_f32(ps.cpu().numpy(), rps, rtol=1e-5, atol=1e-6)
+    assert ok, ("sum", err)
+    ok, err = close_f32(po.cpu().numpy(), rpo, rtol=1e-5, atol=1e-5)
+    assert ok, ("out", err)
+    ref, ref_lse = oracle.decode(case)
+    out, lse = run_merge(po, pm, ps, dc.context_lens, partition_size, window)
+    _gate(out, ref, f"split B=100 P={partition_size} W={window}")
+    _lse_ok(lse, ref_lse)
+
+
 @pytest.mark.parametrize("group,head_dim", [(3, 128), (6, 256), (12, 64)])
 def test_splitkv_partials_padded_group(oracle, group, head_dim):
     """Fixed partitions with a group that is not a power of two: the padding
