@@ -1073,9 +1073,11 @@ void mla_split_kernel(const MlaParams p) {
 // bf16 terms; then
 // out[b][dv] = sum_j o_lat[b][j] W_UV[h][dv][j] on MFMA with A = o_lat (rows
 // past ROWS zero) and B = W_UV rows, whose 8 consecutive latent dims per lane
-// are contiguous in memory; wave w computes dv tile w.  The W_UV loads are
-// issued first, so they overlap the merge.  An empty context, or a query that
-// sees no key, gives 0.
+// are contiguous in memory; wave w computes dv tile w.  With 8 rows the W_UV
+// loads are issued first, so they overlap the merge; with 16 (the verify
+// step's grids, two blocks or more per CU) they follow it, which keeps the
+// kernel within the registers of two resident blocks per CU.  An empty
+// context, or a query that sees no key, gives 0.
 constexpr int kMergeThreads = 512;
 constexpr int kMergeWaves = kMergeThreads / 64;
 
@@ -1101,8 +1103,11 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_uv_kernel(const MlaPa
   const uint16_t* wuv = p.w_uv + static_cast<int64_t>(hw) * kDv * kLat +
                         static_cast<int64_t>(16 * wave + c16) * kLat + 8 * g;
   uint4 bw[kLat / 32];
+  auto load_wuv = [&]() {
 #pragma unroll
-  for (int ks = 0; ks < kLat / 32; ++ks) bw[ks] = load16(wuv + 32 * ks);
+    for (int ks = 0; ks < kLat / 32; ++ks) bw[ks] = load16(wuv + 32 * ks);
+  };
+  if constexpr (ROWS < 16) load_wuv();   // 16 rows: after the merge (registers for 2 blocks per CU)
 
   if constexpr (ROWS < 16) {   // rows ROWS..15 of the MFMA A operand stay zero
     for (int i = tid; i < (16 - ROWS) * (kLat / 8); i += kMergeThreads) {
@@ -1177,6 +1182,7 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_uv_kernel(const MlaPa
     *reinterpret_cast<uint4*>(&olo[bb][d0]) = make_uint4(pack_bf16(l8[0], l8[1]), pack_bf16(l8[2], l8[3]),
                                                          pack_bf16(l8[4], l8[5]), pack_bf16(l8[6], l8[7]));
   }
+  if constexpr (ROWS == 16) load_wuv();
   __syncthreads();
   // out[b][dv]: wave w takes dv tile w
   f32x4_t c = {0.f, 0.f, 0.f, 0.f};
