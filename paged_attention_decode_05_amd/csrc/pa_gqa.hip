@@ -1036,7 +1036,9 @@ __device__ __forceinline__ void wave_find_item(int batch, int hkv, int64_t x, F 
 
 // Fixed partitions: one block per (partition j, KV head gk, sequence b),
 // handling keys [lo + j*P, lo + (j+1)*P).  Blocks are dispatched in the order
-// of the 1-D grid: block i takes the i-th partition with a key, in row-major
+// of their linear index i = blockIdx.y * gridDim.x + blockIdx.x (a 2-D grid
+// only past 65,536 blocks; indices past the last block exit at once): block i
+// takes the i-th partition with a key, in row-major
 // order over (b, gk) and ascending j, or, past the last of those, the empty
 // partitions in the same order.  So every partition with keys starts before
 // any empty one, and the empty ones fill the slots that the last partitions
@@ -1045,6 +1047,8 @@ template <int D, int G>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kMinWaves<D, G>)))
 void split_kernel(const SplitParams p, int batch) {
   __shared__ int sh_item[3];
+  const int64_t i = static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x;
+  if (i >= static_cast<int64_t>(p.max_parts) * p.kv_heads * batch) return;   // whole block
   if (threadIdx.x < 64) {
     const int hkv = p.kv_heads;
     const int P = p.partition_size;
@@ -1055,7 +1059,6 @@ void split_kernel(const SplitParams p, int batch) {
     };
     auto dead_of = [&](int bb) -> int64_t { return p.max_parts - live_of(bb); };
     const int64_t W = wave_items(batch, live_of) * hkv;
-    const int64_t i = blockIdx.x;
     int bb;
     int64_t pre, off, cnt, first;
     if (i < W) {
@@ -1473,7 +1476,11 @@ __global__ __launch_bounds__(kBlock) void merge_kernel(const MergeParams p) {
 template <int D, int G>
 static hipError_t launch_split_dg(const SplitParams& p, int batch, int num_kv_heads,
                                   hipStream_t stream) {
-  const dim3 grid(static_cast<uint32_t>(p.max_parts) * num_kv_heads * batch);
+  const int64_t blocks = static_cast<int64_t>(p.max_parts) * num_kv_heads * batch;
+  const int64_t gx = blocks < 65536 ? blocks : 65536;
+  const int64_t gy = (blocks + gx - 1) / gx;
+  if (gy > 65535) return hipErrorInvalidConfiguration;
+  const dim3 grid(static_cast<uint32_t>(gx), static_cast<uint32_t>(gy));
   launch_profiled(split_kernel<D, G>, grid, dim3(kBlock), 0, stream, p, batch);
   return hipGetLastError();
 }

@@ -182,6 +182,33 @@ def test_splitkv_batch_past_64(oracle, partition_size, window):
     _lse_ok(lse, ref_lse)
 
 
+def test_splitkv_grid_past_65536_blocks(oracle):
+    """Small partitions over a wide batch: max_parts x KV heads x batch is
+    past 65,536 blocks, so the fixed grid folds its linear block index into
+    two grid dimensions."""
+    rng = np.random.default_rng(9990)
+    ctx = rng.integers(0, 2100, size=64)
+    ctx[:2] = (2100, 0)
+    case = wl.make_gqa_case(context_lens=tuple(int(c) for c in ctx), num_q_heads=32,
+                            num_kv_heads=8, head_dim=128, page_size=32, seed=9991)
+    dc = dev_case(case)
+    P = 16
+    mp = max_parts_for(dc, P)
+    assert mp * 8 * 64 > 65536
+    po, pm, ps = run_splitkv(dc, P, mp)
+    rpo, rpm, rps = oracle.partials(case, P, mp)
+    ok, err = close_f32(pm.cpu().numpy(), rpm, rtol=2e-6, atol=1e-5)
+    assert ok, ("max", err)
+    ok, err = close_f32(ps.cpu().numpy(), rps, rtol=1e-5, atol=1e-6)
+    assert ok, ("sum", err)
+    ok, err = close_f32(po.cpu().numpy(), rpo, rtol=1e-5, atol=1e-5)
+    assert ok, ("out", err)
+    ref, ref_lse = oracle.decode(case)
+    out, lse = run_merge(po, pm, ps, dc.context_lens, P, 0)
+    _gate(out, ref, "split P=16 over 67K blocks")
+    _lse_ok(lse, ref_lse)
+
+
 @pytest.mark.parametrize("group,head_dim", [(3, 128), (6, 256), (12, 64)])
 def test_splitkv_partials_padded_group(oracle, group, head_dim):
     """Fixed partitions with a group that is not a power of two: the padding
