@@ -1172,9 +1172,24 @@ __device__ __forceinline__ void locate_unit(const int32_t* ctx, int batch, int w
 }
 
 
+// Waves per block of the balanced split.  Where a wave's state is large (G*D
+// of 2048 floats or more, bf16 pools on the matrix cores: head_dim 256 groups
+// of 8 and 16, head_dim 128 groups of 16), one block holds all the waves a CU
+// keeps (4 x the waves per SIMD): half or a third as many ranges, so fewer
+// prologues, epilogue merges of the waves' states and cut rows (d256w window
+// decode 57.2 -> 53.7 us, bs64 4-query verify 211.7 -> 200.4 us).  Elsewhere
+// 4-wave blocks measured faster (bs64 decode 188 against 192 us, FP8 107
+// against 123 us).
 template <int D, int G, int KV>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kMinWaves<D, G, KV>)))
+constexpr int kBalWaves = (KV == kKvBf16 && kUseMfma<D, G> && D <= 256 && G * D >= 2048)
+                              ? 4 * kMinWaves<D, G, KV>
+                              : kWaves;
+
+template <int D, int G, int KV>
+__global__ __attribute__((amdgpu_flat_work_group_size(1, 64 * kBalWaves<D, G, KV>)))
+__attribute__((amdgpu_waves_per_eu(kMinWaves<D, G, KV>)))
 void balanced_split_kernel(const SplitParams p, const BalancedLayout bl) {
+  constexpr int NWB = kBalWaves<D, G, KV>;
   __shared__ int64_t sh_total;
   __shared__ int64_t sh_pre;
   __shared__ int sh_b;
@@ -1185,11 +1200,11 @@ void balanced_split_kernel(const SplitParams p, const BalancedLayout bl) {
   for (int b = i; b < bl.batch; b += gridDim.x) {
     if (p.context_lens[b] > 0) continue;
     const int64_t r0 = static_cast<int64_t>(b) * p.num_q_heads;
-    for (int j = threadIdx.x; j < p.num_q_heads * D; j += kBlock) bl.out[r0 * D + j] = 0;
+    for (int j = threadIdx.x; j < p.num_q_heads * D; j += 64 * NWB) bl.out[r0 * D + j] = 0;
     if (bl.lse)
-      for (int j = threadIdx.x; j < p.num_q_heads; j += kBlock) bl.lse[r0 + j] = -INFINITY;
+      for (int j = threadIdx.x; j < p.num_q_heads; j += 64 * NWB) bl.lse[r0 + j] = -INFINITY;
     if (bl.row_info)
-      for (int g = threadIdx.x; g < hkv; g += kBlock) bl.row_info[static_cast<int64_t>(b) * hkv + g] = 0;
+      for (int g = threadIdx.x; g < hkv; g += 64 * NWB) bl.row_info[static_cast<int64_t>(b) * hkv + g] = 0;
   }
   if (!bl.seg_out) {
     // No workspace: block i takes whole rows (b, g) = i, i + grid, ... and
@@ -1201,7 +1216,7 @@ void balanced_split_kernel(const SplitParams p, const BalancedLayout bl) {
       if (n <= 0) continue;                                  // written above
       const int lo = p.reach > 0 ? max(0, n - p.reach) : 0;
       const int64_t h0 = static_cast<int64_t>(b) * p.num_q_heads + static_cast<int64_t>(gk) * p.gq;
-      attend_range<D, G, kWaves, KV>(p, b, gk, lo, n, nullptr, nullptr, nullptr, 1, bl.out + h0 * D,
+      attend_range<D, G, NWB, KV>(p, b, gk, lo, n, nullptr, nullptr, nullptr, 1, bl.out + h0 * D,
                                      bl.lse ? bl.lse + h0 : nullptr);
     }
     return;
@@ -1263,7 +1278,7 @@ void balanced_split_kernel(const SplitParams p, const BalancedLayout bl) {
         return static_cast<int>(t < -(1 << 30) ? -(1 << 30) : t > (1 << 30) ? (1 << 30) : t);
       };
       const PrioKeys pk{true, key_at(1, 2), key_at(3, 4), key_at(9, 10)};
-      attend_range<D, G, kWaves, KV>(p, b, gk, begin, end, bl.seg_out + slot * G * D,
+      attend_range<D, G, NWB, KV>(p, b, gk, begin, end, bl.seg_out + slot * G * D,
                                  bl.seg_max + slot * G, bl.seg_sum + slot * G, 1,
                                  whole ? bl.out + h0 * D : nullptr,
                                  (whole && bl.lse) ? bl.lse + h0 : nullptr, pk);
@@ -1488,7 +1503,8 @@ static hipError_t launch_split_dg(const SplitParams& p, int batch, int num_kv_he
 template <int D, int G, int KV>
 static hipError_t launch_balanced_dg(const SplitParams& p, const BalancedLayout& bl, int grid,
                                      hipStream_t stream) {
-  launch_profiled(balanced_split_kernel<D, G, KV>, dim3(grid), dim3(kBlock), 0, stream, p, bl);
+  launch_profiled(balanced_split_kernel<D, G, KV>, dim3(grid), dim3(64 * kBalWaves<D, G, KV>), 0, stream, p,
+                  bl);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !bl.seg_out) return e;   // no workspace: rows were written whole
   hipLaunchKernelGGL((balanced_merge_kernel<D, G>), dim3(bl.rows, (G * D / 4 + kBlock - 1) / kBlock),
@@ -1504,7 +1520,8 @@ static int blocks_per_cu() {
   static std::atomic<int> cached{0};
   int n = cached.load(std::memory_order_relaxed);
   if (n == 0) {
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, balanced_split_kernel<D, G, KV>, kBlock, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, balanced_split_kernel<D, G, KV>,
+                                                     64 * kBalWaves<D, G, KV>, 0) !=
             hipSuccess || n < 1)
       n = 1;
     cached.store(n, std::memory_order_relaxed);
