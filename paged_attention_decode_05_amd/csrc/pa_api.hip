@@ -26,6 +26,7 @@ hipError_t launch_merge(const MergeParams& p, int head_dim, int batch, hipStream
 hipError_t launch_balanced(const SplitParams& sp, const BalancedLayout& bl, int head_dim, int group,
                            int grid, hipStream_t stream, int kv);
 int balanced_grid(int head_dim, int group, int num_cus, int max_blocks, int kv);
+int balanced_row_cost(int head_dim, int group, int kv);
 
 }  // namespace pa
 
@@ -211,7 +212,7 @@ int decode_impl(const void* q, const void* k_pool, const void* v_pool, const pa_
     nbmax = plan.rows < (1 << 20) ? plan.rows : (1 << 20);   // one block per row
   }
   bl.min_units = pa::kMinUnitsPerBlock;
-  bl.row_cost = pa::kRowCostUnits;
+  bl.row_cost = pa::balanced_row_cost(kv->head_dim, vgroup, kv_type);
   bl.rows = plan.rows;
   bl.batch = batch;
   bl.q_heads = num_q_heads;

@@ -1600,6 +1600,16 @@ int balanced_grid(int head_dim, int group, int num_cus, int max_blocks, int kv) 
   });
 }
 
+// Units charged for starting a row: kRowCostUnits for 4-wave blocks, twice
+// that for the blocks that hold all the waves of a CU (bs64 4-query verify,
+// 12-wave blocks: 194.5 us at 256 against 202.1 at 128 and 195.4 at 384;
+// d256w, 8-wave blocks: 53.5 us at 128 and 256).
+int balanced_row_cost(int head_dim, int group, int kv) {
+  return dispatch_dg<int>(head_dim, group, kv, kRowCostUnits, [&]<int D, int G, int KV>() {
+    return kBalWaves<D, G, KV> > kWaves ? 2 * kRowCostUnits : kRowCostUnits;
+  });
+}
+
 // Balanced split, then the merge of the rows several blocks shared: the whole
 // of pa_decode (bf16, FP8 or f32 pools).
 hipError_t launch_balanced(const SplitParams& sp, const BalancedLayout& bl, int head_dim, int group,

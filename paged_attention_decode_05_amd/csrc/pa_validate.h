@@ -58,7 +58,9 @@ constexpr int32_t kMaxBalancedBlocks = 2048;
 // block well above it.
 constexpr int64_t kMinUnitsPerBlock = 32;
 // Units of the balanced key line that stand for a row's prologue, charged
-// before its keys, so a block whose share starts several rows gets fewer keys.
+// before its keys, so a block whose share starts several rows gets fewer keys
+// (for 4-wave blocks; a block of all the waves of a CU streams its keys faster
+// and is charged twice as many, see balanced_row_cost).
 constexpr int32_t kRowCostUnits = 128;
 
 struct DecodePlan {
