@@ -38,26 +38,42 @@ struct KvInsertParams {
   int32_t chunks_per_tensor;  // num_kv_heads * head_dim / 8
 };
 
-// Thread x: token x / (2 * chunks_per_tensor); within it, K chunks first,
+// Item x: token x / (2 * chunks_per_tensor); within it, K chunks first,
 // then V chunks; chunk c of a tensor is head c / chunks_per_head, dims
-// 8 * (c % chunks_per_head) .. +8.
+// 8 * (c % chunks_per_head) .. +8.  A thread moves the kInsertItems items
+// t, t + T, t + 2T, ... (T threads in the grid): their slot reads, then their
+// row loads, then their stores, so each thread has that many copies in
+// flight while consecutive threads still touch consecutive chunks.
+constexpr int kInsertItems = 4;
+
 __global__ __launch_bounds__(kCopyThreads) void kv_insert_kernel(const KvInsertParams p) {
-  const int64_t x = static_cast<int64_t>(blockIdx.x) * kCopyThreads + threadIdx.x;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kCopyThreads + threadIdx.x;
+  const int64_t T = static_cast<int64_t>(gridDim.x) * kCopyThreads;
   const int64_t per_token = 2 * static_cast<int64_t>(p.chunks_per_tensor);
-  if (x >= p.num_tokens * per_token) return;
-  const int64_t i = x / per_token;
-  int c = static_cast<int>(x - i * per_token);
-  const bool is_v = c >= p.chunks_per_tensor;
-  if (is_v) c -= p.chunks_per_tensor;
-  const int64_t s = p.slots[i];
-  if (s < 0 || s >= p.total_slots) return;
-  const int h = c / p.chunks_per_head;
-  const int d = 8 * (c - h * p.chunks_per_head);
-  const int64_t page = s / p.page_size, off = s - page * p.page_size;
-  const int64_t src = i * p.src_token_stride + h * p.src_head_stride + d;
-  const int64_t dst = page * p.page_stride + h * p.head_stride + off * p.token_stride + d;
-  const uint4 v = load16((is_v ? p.v_new : p.k_new) + src);
-  *reinterpret_cast<uint4*>((is_v ? p.v_pool : p.k_pool) + dst) = v;
+  const int64_t items = p.num_tokens * per_token;
+  int64_t dst[kInsertItems];
+  bool to_v[kInsertItems], live[kInsertItems];
+  uint4 v[kInsertItems];
+#pragma unroll
+  for (int k = 0; k < kInsertItems; ++k) {
+    const int64_t x = t + k * T;
+    const int64_t i = x / per_token;
+    int c = static_cast<int>(x - i * per_token);
+    const bool is_v = c >= p.chunks_per_tensor;
+    if (is_v) c -= p.chunks_per_tensor;
+    const int64_t s = x < items ? p.slots[i] : -1;
+    live[k] = s >= 0 && s < p.total_slots;
+    to_v[k] = is_v;
+    const int h = c / p.chunks_per_head;
+    const int d = 8 * (c - h * p.chunks_per_head);
+    const int64_t page = s / p.page_size, off = s - page * p.page_size;
+    dst[k] = page * p.page_stride + h * p.head_stride + off * p.token_stride + d;
+    const int64_t src = i * p.src_token_stride + h * p.src_head_stride + d;
+    v[k] = live[k] ? load16((is_v ? p.v_new : p.k_new) + src) : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int k = 0; k < kInsertItems; ++k)
+    if (live[k]) *reinterpret_cast<uint4*>((to_v[k] ? p.v_pool : p.k_pool) + dst[k]) = v[k];
 }
 
 struct MlaInsertParams {
@@ -224,8 +240,9 @@ int pa_kv_insert(const void* k_new, const void* v_new, int64_t src_token_stride,
   p.page_size = kv->page_size;
   p.chunks_per_head = kv->head_dim / 8;
   p.chunks_per_tensor = kv->num_kv_heads * (kv->head_dim / 8);
-  const int64_t threads = static_cast<int64_t>(num_tokens) * 2 * p.chunks_per_tensor;
-  const int64_t blocks = (threads + pa::kCopyThreads - 1) / pa::kCopyThreads;
+  const int64_t items = static_cast<int64_t>(num_tokens) * 2 * p.chunks_per_tensor;
+  const int64_t per_block = static_cast<int64_t>(pa::kCopyThreads) * pa::kInsertItems;
+  const int64_t blocks = (items + per_block - 1) / per_block;
   pa::clear_error();
   pa::launch_profiled(pa::kv_insert_kernel, dim3(static_cast<unsigned>(blocks)),
                       dim3(pa::kCopyThreads), 0, static_cast<hipStream_t>(stream), p);
