@@ -4,10 +4,11 @@
 // Token i goes to the flat slot s = slots[i] = page * page_size + offset
 // [vllm.cpp kernel matrix, row KERNEL-KV-CACHE: KV insert into the paged
 // cache; the MLA cache write concatenates the latent and rope projections
-// into the 576-wide row; both are exact copies].  One thread moves one
-// 16-byte chunk (8 bf16) from the source row to the cache row; the flat
-// thread index runs over (token, chunk), so a launch covers any number of
-// tokens with full 16-byte accesses.  Slots outside [0, num_pages *
+// into the 576-wide row; both are exact copies].  The copies move 16-byte
+// chunks (8 bf16) from the source row to the cache row, indexed by a flat
+// (token, chunk) item number, so a launch covers any number of tokens with
+// full 16-byte accesses (the K/V insert moves four items per thread, the
+// latent write one).  Slots outside [0, num_pages *
 // page_size) -- negative ones mark padding -- are skipped, so no slot value
 // can make the kernel write outside the pool.
 #include <hip/hip_runtime.h>
