@@ -44,6 +44,27 @@ def test_noalloc_matches_pa_decode_two_calls(oracle):
         assert rep.ok, rep
 
 
+def test_noalloc_full_cu_blocks_two_calls(oracle):
+    """head_dim 256, groups of 8: the balanced split's blocks hold all the
+    waves of a CU; two calls in a row, the second smaller."""
+    big = wl.make_gqa_case(context_lens=(), ctx_draw=(1024, 6000), batch=12, num_q_heads=16,
+                           num_kv_heads=2, head_dim=256, page_size=32, seed=8810, window=4096,
+                           q_std=0.5)
+    small = wl.make_gqa_case(context_lens=(0, 1, 257, 3000, 90), num_q_heads=16, num_kv_heads=2,
+                             head_dim=256, page_size=32, seed=8811, window=4096, q_std=0.5)
+    for case in (big, small):
+        print(f"case D=256 batch={case.batch}", flush=True)
+        dc = case.to("cuda")
+        out, lse = _noalloc(dc)
+        ref_out, ref_lse = run_decode(dc)
+        assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
+        assert torch.equal(lse, ref_lse)
+        want, _ = oracle.decode(case)
+        rep = compare(out, want)
+        print(f"[noalloc D=256 batch={case.batch}] {rep}", flush=True)
+        assert rep.ok, rep
+
+
 def test_noalloc_rejects_shapes_past_its_scratch():
     """A plan larger than the 32 MiB array is refused on the host."""
     kv = pb.KvLayout(64, 32, 8, 512, 8 * 32 * 512, 32 * 512, 512)
