@@ -1600,13 +1600,17 @@ int balanced_grid(int head_dim, int group, int num_cus, int max_blocks, int kv) 
   });
 }
 
-// Units charged for starting a row: kRowCostUnits for 4-wave blocks, twice
-// that for the blocks that hold all the waves of a CU (bs64 4-query verify,
-// 12-wave blocks: 194.5 us at 256 against 202.1 at 128 and 195.4 at 384;
-// d256w, 8-wave blocks: 53.5 us at 128 and 256).
+// Units charged for starting a row: kRowCostUnits for 4-wave blocks (half
+// that over bf16 pools), twice that for the blocks that hold all the waves of
+// a CU.  bs64 4-query verify, 12-wave blocks: 194.5 us at 256 against 202.1 at
+// 128 and 195.4 at 384; d256w, 8-wave blocks: 53.5 us at 128 and 256; bs64
+// decode, bf16: 187.5-187.8 us at 64 against 188.6-188.7 at 128 (long
+// contexts 0.3 us and the tiny call 0.4 us slower at 64); FP8 pools keep 128
+// (106.5 against 108.5 us at 64).
 int balanced_row_cost(int head_dim, int group, int kv) {
   return dispatch_dg<int>(head_dim, group, kv, kRowCostUnits, [&]<int D, int G, int KV>() {
-    return kBalWaves<D, G, KV> > kWaves ? 2 * kRowCostUnits : kRowCostUnits;
+    if (kBalWaves<D, G, KV> > kWaves) return 2 * kRowCostUnits;
+    return KV == kKvBf16 ? kRowCostUnits / 2 : kRowCostUnits;
   });
 }
 

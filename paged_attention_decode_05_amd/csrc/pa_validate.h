@@ -59,8 +59,9 @@ constexpr int32_t kMaxBalancedBlocks = 2048;
 constexpr int64_t kMinUnitsPerBlock = 32;
 // Units of the balanced key line that stand for a row's prologue, charged
 // before its keys, so a block whose share starts several rows gets fewer keys
-// (for 4-wave blocks; a block of all the waves of a CU streams its keys faster
-// and is charged twice as many, see balanced_row_cost).
+// (for 4-wave blocks over FP8 and f32 pools; balanced_row_cost halves it for
+// bf16 pools and doubles it for a block of all the waves of a CU, which
+// streams its keys faster).
 constexpr int32_t kRowCostUnits = 128;
 
 struct DecodePlan {
