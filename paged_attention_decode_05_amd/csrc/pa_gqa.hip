@@ -1089,9 +1089,9 @@ void split_kernel(const SplitParams p, int batch) {
                           p.max_parts + j;   // index of (b, h = gk*Gq, j)
   if (begin64 >= n) {
     if (p.write_empty) {
-      for (int i = threadIdx.x; i < p.vheads * D; i += kBlock) {
-        const int h = i / D;
-        p.part_out[(rowbase + static_cast<int64_t>(h) * p.max_parts) * D + (i % D)] = 0.0f;
+      for (int e = threadIdx.x; e < p.vheads * D; e += kBlock) {
+        const int h = e / D;
+        p.part_out[(rowbase + static_cast<int64_t>(h) * p.max_parts) * D + (e % D)] = 0.0f;
       }
       if (threadIdx.x < p.vheads) {
         p.part_max[rowbase + static_cast<int64_t>(threadIdx.x) * p.max_parts] = -INFINITY;
